@@ -1,0 +1,204 @@
+"""Python binding of the C ABI in ``include/csa.h`` (``libcsa.so``, built in-tree).
+
+Argument marshalling only: each function takes torch tensors that already live on
+the GPU, passes their device pointers, sizes and the current HIP stream to the C
+entry point of the same name, and raises ``CSAError`` on a non-zero status.  All
+arithmetic runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, importing this module raises.
+
+Tensor dtypes: fp32 -> CSA_F32, bfloat16 -> CSA_BF16, uint8 or float8_e4m3fn codes
+-> CSA_FP8_E4M3.  Workspaces are sized with the library's own queries and, when
+the caller passes none, allocated with torch (device memory plumbing).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
+          4: "CSA_ERR_HIP"}
+
+EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
+           "csa_index_score", "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
+           "csa_attn_workspace_size", "csa_sparse_attn", "hca_dense_attn")
+
+
+class CSAError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m compressed_sparse_kv_amd.build` "
+                          "(hipcc, gfx950).  There is no fallback path.")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    i64 = ctypes.c_int64
+    sig = {
+        "csa_status_string": ([i], ctypes.c_char_p),
+        "csa_version": ([], i),
+        "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
+        "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
+        "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
+        "csa_topk_workspace_size": ([i, i, i], sz),
+        "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
+        "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
+        "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
+        "csa_sparse_attn": ([vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise CSAError(fn, st, _lib.csa_status_string(st).decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return CSA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _ws(nbytes: int, ws, device):
+    if nbytes == 0:
+        return ws, (0 if ws is None else ws.numel() * ws.element_size())
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 1
+# ---------------------------------------------------------------------------------------
+
+def compress_workspace_size(B, T, m, c, overlap, has_prev) -> int:
+    return int(_lib.csa_compress_workspace_size(B, T, m, c, int(overlap), int(has_prev)))
+
+
+def csa_compress(hidden, hidden_prev, w_proj, bias, *, overlap: bool, m: int, c: int, d_rope: int,
+                 rope_theta: float, rms_eps: float, p0: int, out, out_scale=None, ws=None, stream=None):
+    """hidden [B,T,d], hidden_prev [B,m,d] or None, w_proj [S*c, d], bias [S/2,m,c] fp32,
+    out [B,T/m,c] (fp32 / bf16 / uint8 codes with out_scale [B,T/m])."""
+    _dev(hidden, hidden_prev, w_proj, bias, out, out_scale)
+    B, T, d = hidden.shape
+    ws, wsb = _ws(compress_workspace_size(B, T, m, c, overlap, hidden_prev is not None), ws, hidden.device)
+    _check("csa_compress", _lib.csa_compress(
+        _p(hidden), _p(hidden_prev), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), B, T, d, m, c,
+        d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale), _dtype(out),
+        _p(ws), wsb, _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 2
+# ---------------------------------------------------------------------------------------
+
+def csa_index_score(q, q_scale, w, k, k_scale, q_pos, *, m: int, scores, stream=None):
+    """q [B,S,H_I,d_I], k [B,Nc,d_I] (fp8 codes + scales, or fp32 with scales None),
+    w [B,S,H_I], q_pos [B,S] int64 -> scores [B,S,Nc] fp32."""
+    _dev(q, q_scale, w, k, k_scale, q_pos, scores)
+    B, S, H, D = q.shape
+    Nc = k.shape[1]
+    _check("csa_index_score", _lib.csa_index_score(
+        _p(q), _p(q_scale), _p(w), _p(k), _p(k_scale), _dtype(q), _p(q_pos), B, S, H, D, Nc, m,
+        _p(scores), _stream(stream)))
+    return scores
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 3
+# ---------------------------------------------------------------------------------------
+
+def topk_workspace_size(rows, Nc, k) -> int:
+    return int(_lib.csa_topk_workspace_size(rows, Nc, k))
+
+
+def csa_topk(scores, k: int, idx, *, ws=None, algo: int = 0, stream=None):
+    """scores [B,S,Nc] fp32 -> idx [B,S,k] int32."""
+    _dev(scores, idx, ws)
+    B, S, Nc = scores.shape
+    ws, wsb = _ws(topk_workspace_size(B * S, Nc, k), ws, scores.device)
+    _check("csa_topk", _lib.csa_topk_algo(_p(scores), B, S, Nc, k, _p(idx), _p(ws), wsb, algo,
+                                          _stream(stream)))
+    return idx
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 4
+# ---------------------------------------------------------------------------------------
+
+def attn_workspace_size(B, S, H, c, max_rows, dtype) -> int:
+    return int(_lib.csa_attn_workspace_size(B, S, H, c, max_rows, dtype))
+
+
+def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, ws=None, stream=None):
+    """q [B,S,H,c], kv_comp [B,Nc,c], idx [B,S,k] int32, swa [B,Ls,c], sink [H] fp32."""
+    _dev(q, kv_comp, idx, swa, sink, out, lse, ws)
+    B, S, H, c = q.shape
+    Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q)
+    ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
+    _check("csa_sparse_attn", _lib.csa_sparse_attn(
+        _p(q), _p(kv_comp), _p(idx), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
+        _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+    return out
+
+
+def hca_dense_attn(q, kv_comp, q_pos, swa, sink, *, m: int, W: int, out, lse=None, scale=None, ws=None,
+                   stream=None):
+    """q [B,S,H,c], kv_comp [B,Nc,c], q_pos [B,S] int64, swa [B,Ls,c], sink [H] fp32."""
+    _dev(q, kv_comp, q_pos, swa, sink, out, lse, ws)
+    B, S, H, c = q.shape
+    Nc, Ls = kv_comp.shape[1], swa.shape[1]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q)
+    ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + Nc, dt), ws, q.device)
+    _check("hca_dense_attn", _lib.hca_dense_attn(
+        _p(q), _p(kv_comp), _p(q_pos), m, _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, Ls, W,
+        _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+    return out

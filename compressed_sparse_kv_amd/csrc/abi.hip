@@ -1,0 +1,156 @@
+// C entry points: argument validation, then dispatch to the stage launchers.
+// Every check runs on the host before anything is enqueued (see include/csa.h).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace csa {
+int launch_index_score(const void*, const float*, const float*, const void*, const float*, int, const int64_t*, int,
+                       int, int, int, int, int, float*, hipStream_t);
+int launch_topk(const float*, int, int, int, int32_t*, void*, size_t, int, hipStream_t);
+size_t topk_workspace_bytes(int, int, int);
+int launch_attention(bool, const void*, const void*, const int32_t*, const int64_t*, int, const void*, const float*,
+                     int, float, int, int, int, int, int, int, int, int, void*, float*, void*, size_t, hipStream_t);
+size_t attn_workspace_bytes(int, int, int, int, int, int);
+int launch_compress(const void*, const void*, int, const void*, const float*, int, int, int, int, int, int, int,
+                    float, float, int64_t, void*, float*, int, void*, hipStream_t);
+size_t compress_workspace_bytes(int, int, int, int, int, int);
+}  // namespace csa
+
+using namespace csa;
+
+#define CSA_REQUIRE(cond) \
+  do {                    \
+    if (!(cond)) return CSA_ERR_INVALID_ARG; \
+  } while (0)
+
+static hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARG: return "CSA_ERR_INVALID_ARG: an argument is out of range or a required pointer is NULL";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: no kernel for this dtype/shape combination";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace smaller than the size query returned";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    default: return "unknown csa_status";
+  }
+}
+
+int csa_version(void) { return 100; }
+
+// ---- stage 1 ------------------------------------------------------------------------
+size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev) {
+  if (B <= 0 || T <= 0 || m <= 0 || c <= 0) return 0;
+  return compress_workspace_bytes(B, T, m, c, overlap, has_prev);
+}
+
+int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, const void* w_proj, const float* bias,
+                 int overlap, int B, int T, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
+                 int64_t p0, void* out, float* out_scale, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(hidden && w_proj && bias && out);
+  CSA_REQUIRE(overlap == 0 || overlap == 1);
+  CSA_REQUIRE(B > 0 && T > 0 && d > 0 && m > 0 && c > 0);
+  CSA_REQUIRE(T % m == 0 && p0 >= 0 && p0 % m == 0);
+  CSA_REQUIRE(c % 2 == 0 && c <= 1024 && d_rope >= 0 && d_rope <= c && d_rope % 2 == 0);
+  CSA_REQUIRE(rms_eps >= 0.0f && rope_theta > 0.0f);
+  CSA_REQUIRE(!(overlap && p0 > 0 && hidden_prev == nullptr));
+  CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
+  CSA_REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_FP8_E4M3);
+  CSA_REQUIRE(out_dtype != CSA_FP8_E4M3 || out_scale != nullptr);
+  if (in_dtype == CSA_BF16 && d % 64 != 0) return CSA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * (T + m) * 4 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
+  const int has_prev = hidden_prev != nullptr;
+  if (ws == nullptr || ws_bytes < compress_workspace_bytes(B, T, m, c, overlap, has_prev)) return CSA_ERR_WORKSPACE;
+  return launch_compress(hidden, hidden_prev, in_dtype, w_proj, bias, overlap, B, T, d, m, c, d_rope, rope_theta,
+                         rms_eps, p0, out, out_scale, out_dtype, ws, as_stream(stream));
+}
+
+// ---- stage 2 ------------------------------------------------------------------------
+int csa_index_score(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
+                    int dtype, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc, int m, float* scores,
+                    void* stream) {
+  CSA_REQUIRE(q && w && k && q_pos && scores);
+  CSA_REQUIRE(B > 0 && S > 0 && H_I > 0 && d_I > 0 && Nc > 0 && m > 0);
+  CSA_REQUIRE(static_cast<int64_t>(B) * S * Nc < (int64_t{1} << 40));
+  if (dtype == CSA_FP8_E4M3) {
+    CSA_REQUIRE(q_scale && k_scale);
+    if (H_I != 64 || d_I != 128) return CSA_ERR_UNSUPPORTED;
+  } else if (dtype == CSA_F32) {
+    CSA_REQUIRE(q_scale == nullptr && k_scale == nullptr);
+    if (H_I > 64 || d_I > 256) return CSA_ERR_UNSUPPORTED;
+  } else {
+    return CSA_ERR_INVALID_ARG;
+  }
+  return launch_index_score(q, q_scale, w, k, k_scale, dtype, q_pos, B, S, H_I, d_I, Nc, m, scores,
+                            as_stream(stream));
+}
+
+// ---- stage 3 ------------------------------------------------------------------------
+size_t csa_topk_workspace_size(int rows, int Nc, int k) {
+  if (rows <= 0 || Nc <= 0 || k <= 0) return 0;
+  return topk_workspace_bytes(rows, Nc, k);
+}
+
+int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                  int algo, void* stream) {
+  CSA_REQUIRE(scores && idx);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && k >= 1 && k <= 2048);
+  CSA_REQUIRE(algo >= 0 && algo <= 2);
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
+  if (ws != nullptr && ws_bytes < topk_workspace_bytes(static_cast<int>(rows), Nc, k)) return CSA_ERR_WORKSPACE;
+  if (algo == 2 && ws == nullptr) return CSA_ERR_WORKSPACE;
+  return launch_topk(scores, static_cast<int>(rows), Nc, k, idx, ws, ws_bytes, algo, as_stream(stream));
+}
+
+int csa_topk(const float* scores, int B, int S, int Nc, int k, int32_t* idx, void* ws, size_t ws_bytes,
+             void* stream) {
+  return csa_topk_algo(scores, B, S, Nc, k, idx, ws, ws_bytes, 0, stream);
+}
+
+// ---- stage 4 ------------------------------------------------------------------------
+size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dtype) {
+  if (B <= 0 || S <= 0 || H <= 0 || c <= 0 || max_rows <= 0) return 0;
+  return attn_workspace_bytes(B, S, H, c, max_rows, dtype);
+}
+
+static int check_attn(const void* q, const void* kv, const void* swa, const float* sink, int dtype, float scale,
+                      int B, int S, int H, int c, int Nc, int Ls, int W, const void* out) {
+  CSA_REQUIRE(q && kv && swa && sink && out);
+  CSA_REQUIRE(B > 0 && S > 0 && H > 0 && c > 0 && Nc > 0 && W > 0 && Ls >= S);
+  CSA_REQUIRE(scale > 0.0f);
+  CSA_REQUIRE(static_cast<int64_t>(B) * S < (int64_t{1} << 31));
+  if (dtype == CSA_BF16) {
+    if (H != 64 || c != 512) return CSA_ERR_UNSUPPORTED;
+  } else if (dtype == CSA_F32) {
+    if (H > 64 || c > 512) return CSA_ERR_UNSUPPORTED;
+  } else {
+    return CSA_ERR_INVALID_ARG;
+  }
+  return CSA_OK;
+}
+
+int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, const void* swa, const float* sink,
+                    int dtype, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W, void* out,
+                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(idx && k >= 1 && k <= 65536);
+  return launch_attention(false, q, kv_comp, idx, nullptr, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
+                          lse, ws, ws_bytes, as_stream(stream));
+}
+
+int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m, const void* swa, const float* sink,
+                   int dtype, float scale, int B, int S, int H, int c, int Nc, int Ls, int W, void* out, float* lse,
+                   void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(q_pos && m > 0);
+  return launch_attention(true, q, kv_comp, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W, out,
+                          lse, ws, ws_bytes, as_stream(stream));
+}
+
+}  // extern "C"

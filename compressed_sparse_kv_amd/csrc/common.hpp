@@ -1,0 +1,92 @@
+// Device helpers shared by the CSA/HCA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+constexpr int kWave = 64;
+
+// ---- vector types used as MFMA operands --------------------------------------------
+typedef int v8i __attribute__((ext_vector_type(8)));          // 32 fp8 codes
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));        // 8 bf16 bit patterns
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// D(16x16, fp32) += A(16x128 e4m3) * B(128x16 e4m3).  Lane l holds row/column l%16 of
+// A/B and one 32-byte group (l/16) of the reduction index in both operands, so the
+// product pairs the same k-slots on both sides whatever the hardware order inside a group.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x32 bf16) * B(32x16 bf16); lane l: row/col l%16, k-group l/16.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8s& a, const v8s& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// ---- bfloat16 -------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---- OCP e4m3fn encode: round to nearest even, saturate to +-448, NaN -> 0x7f --------
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint8_t sign = static_cast<uint8_t>((u >> 24) & 0x80u);
+  const float a = fabsf(v);
+  if (a != a) return 0x7f;
+  if (a >= 448.0f) return sign | 0x7e;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of step 2^-9
+    const int q = static_cast<int>(rintf(a * 512.0f));   // 0..8; 8 is the smallest normal
+    return sign | static_cast<uint8_t>(q);
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7ffffu + ((ua >> 20) & 1u);        // keep 3 mantissa bits, ties to even
+  const int e = static_cast<int>((ua >> 23) & 0xffu) - 127 + 7;
+  const uint32_t mnt = (ua >> 20) & 7u;
+  return sign | static_cast<uint8_t>((e << 3) | mnt);
+}
+
+// ---- order-preserving keys for selection -----------------------------------------
+// Larger float -> larger key.  -inf and NaN (not candidates) map to 0; -0 and +0
+// share the key of +0.  Every candidate key is >= 0x00800000.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u || u == 0xff800000u) return 0u;
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- wave helpers ------------------------------------------------------------------
+__device__ __forceinline__ float wave_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ unsigned lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+__host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace csa
+
+// ---- host-side launch checking -------------------------------------------------------
+#define CSA_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return CSA_ERR_HIP; \
+  } while (0)

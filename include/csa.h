@@ -1,0 +1,192 @@
+/*
+ * csa.h - C ABI of the CSA / HCA attention hot path (DeepSeek-V4 compressed sparse
+ * attention) for AMD Instinct MI355X (gfx950).
+ *
+ * Five stages, each one asynchronous call on a caller-given HIP stream:
+ *   csa_compress     overlapping (CSA) or single-stream (HCA) block compressor
+ *   csa_index_score  lightning-indexer scores under causal block visibility
+ *   csa_topk         per-query top-k selection of compressed entries
+ *   csa_sparse_attn  shared-KV MQA over [SWA window || selected entries || sink]
+ *   hca_dense_attn   shared-KV MQA over [SWA window || every visible entry || sink]
+ *
+ * Sources (web pages, cited by title and section):
+ *   [HCA-CSA]  zdszero.github.io "hca_csa"
+ *   [KV-COMP]  jerry609.github.io "DeepSeek-V4 的 KV 压缩：从删 token 误解到预算检索"
+ *   [V4-CSA2]  yuyanqi.com "DeepSeek-V4 CSA/HCA 与 DeepSeek-V4.1 CSA2"
+ *   [ATTN-CMP] blog.javazero.top "DeepSeek 注意力结构对比"
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is DEVICE memory owned by the caller; tensors are dense
+ *     row-major in the shape given.  Inputs and outputs must not alias.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     only enqueue work; they never synchronise and never allocate device memory.
+ *     Scratch memory comes from the caller's `ws` buffer, sized by the matching
+ *     *_workspace_size() query; ws may be NULL when that size is 0.
+ *   - The library keeps no state between calls: calls on different streams with
+ *     different buffers may run concurrently.  Two calls that share a workspace
+ *     buffer must be ordered by the caller.
+ *   - Return value: CSA_OK when the work was enqueued.  Argument errors are
+ *     detected before anything is launched (CSA_ERR_INVALID_ARG for bad values,
+ *     CSA_ERR_UNSUPPORTED for a valid shape this build has no kernel for,
+ *     CSA_ERR_WORKSPACE when ws_bytes is too small); CSA_ERR_HIP reports a
+ *     launch failure from the HIP runtime.  Errors that happen while kernels run
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - bf16 = bfloat16 bit patterns (uint16); fp8 = OCP e4m3fn codes (uint8) with an
+ *     fp32 scale per row (real value = decode(code) * scale).
+ */
+#ifndef CSA_MI355X_H
+#define CSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARG = 1,
+  CSA_ERR_UNSUPPORTED = 2,
+  CSA_ERR_WORKSPACE = 3,
+  CSA_ERR_HIP = 4
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* csa_status_string(int status);
+
+/* ABI version: 10000 * major + 100 * minor + patch. */
+int csa_version(void);
+
+/* ------------------------------------------------------------------------------
+ * Stage 1: block compressor.
+ * [HCA-CSA] "CSA 的重叠窗口" (overlapping window) and "HCA：同一个算子，关掉重叠"
+ * (single stream); [KV-COMP] section 9.2 (learned gated pooling).
+ *
+ * Every token h_t of the chunk is projected to contents C and gate logits Z.
+ * Entry i of the chunk is, channel by channel, a softmax-weighted sum over its
+ * slots: with overlap the m a-slots of block i (logit Z^a + B^a, value C^a) and the
+ * m b-slots of block i-1 (logit Z^b + B^b, value C^b); without overlap the m slots
+ * of block i.  The pooled vector u_i goes through RMSNorm (unit gain) and RoPE on
+ * its last d_rope channels at position p0 + m*i (the block's first token):
+ *     out_i = RoPE(u_i / sqrt(mean(u_i^2) + rms_eps)).
+ *
+ *   hidden      [B, T, d]  in_dtype (CSA_F32 or CSA_BF16): tokens at positions p0 .. p0+T-1
+ *   hidden_prev [B, m, d]  in_dtype: the m tokens before p0 (only their b-stream is used,
+ *               for entry 0); NULL means there is no previous block: entry 0's b-slots
+ *               are padding (logit -inf, content 0).  overlap=1 with p0 > 0 requires it.
+ *   w_proj      [S*c, d]   in_dtype, "out x in" layout (proj = hidden @ w_proj^T):
+ *               overlap=1: S = 4 stream blocks (C^a | Z^a | C^b | Z^b);
+ *               overlap=0: S = 2 (C | Z).
+ *   bias        [S/2, m, c] fp32 position bias: (B^a, B^b) or (B).
+ *   Requires T % m == 0, p0 % m == 0, p0 >= 0, 0 <= d_rope <= c, d_rope and c even,
+ *   c <= 1024.
+ *   out         [B, T/m, c]  out_dtype: CSA_F32 or CSA_BF16 (RNE), or CSA_FP8_E4M3 codes
+ *               with out_scale [B, T/m] fp32 = amax/448 of the row (RNE, saturating;
+ *               an all-zero row gets scale 0 and zero codes).  out_scale is ignored
+ *               for the other output types.
+ *   ws          >= csa_compress_workspace_size(...) bytes (holds the projection).
+ * ------------------------------------------------------------------------------ */
+size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev);
+
+int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
+                 const void* w_proj, const float* bias, int overlap,
+                 int B, int T, int d, int m, int c, int d_rope, float rope_theta,
+                 float rms_eps, int64_t p0,
+                 void* out, float* out_scale, int out_dtype,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Stage 2: lightning-indexer scores.
+ * [HCA-CSA] "CSA：轻压缩 + 稀疏选择" (indexer equations); [KV-COMP] sections 9.4, 9.8.
+ *
+ *   scores[b,s,j] = sum_h w[b,s,h] * ReLU(qI[b,s,h,:] . KI[b,j,:])   for j < n_vis(b,s)
+ *                 = -inf                                              otherwise,
+ *   n_vis(b,s) = min(Nc, floor((q_pos[b,s] + 1) / m))  (entry j ends at token m*j+m-1).
+ * No softmax and no 1/sqrt(d_I) factor.
+ *
+ * dtype CSA_FP8_E4M3: q [B,S,H_I,d_I] and k [B,Nc,d_I] are e4m3fn codes, q_scale
+ *   [B,S,H_I] and k_scale [B,Nc] their per-row fp32 scales, which must be finite and
+ *   >= 0 (amax/448 by construction).  Kernels for H_I = 64, d_I = 128.
+ * dtype CSA_F32: q, k are fp32; q_scale and k_scale must be NULL.  Any H_I <= 64,
+ *   d_I <= 256.
+ *   w      [B,S,H_I] fp32 head weights;  q_pos [B,S] int64 absolute positions (>= 0).
+ *   scores [B,S,Nc] fp32 output.
+ * ------------------------------------------------------------------------------ */
+int csa_index_score(const void* q, const float* q_scale, const float* w,
+                    const void* k, const float* k_scale, int dtype,
+                    const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc, int m,
+                    float* scores, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Stage 3: top-k selection.  [KV-COMP] sections 9.4 (S_t = TopK_k of the scores)
+ * and 9.8 (invisible entries carry -inf and come out as -1).
+ *
+ *   scores [rows = B*S, Nc] fp32.  Candidates are the entries whose score is not
+ *   -inf and not NaN (+0 and -0 compare equal).  Each row gets the indices of its
+ *   min(k, n_cand) largest candidate scores, ties going to the lower index, written
+ *   in ascending index order and padded with -1:  idx [rows, k] int32.
+ *   1 <= k <= 2048.
+ *   ws: NULL, or >= csa_topk_workspace_size(rows, Nc, k) bytes.  With ws, rows that
+ *   are few and long are split over several workgroups; without it every row is
+ *   handled by one workgroup.  The result is the same either way.
+ * ------------------------------------------------------------------------------ */
+size_t csa_topk_workspace_size(int rows, int Nc, int k);
+
+int csa_topk(const float* scores, int B, int S, int Nc, int k, int32_t* idx,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* csa_topk with the schedule forced: algo 0 = automatic, 1 = one workgroup per row,
+ * 2 = several workgroups per row (needs ws).  For tuning and tests; same result. */
+int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx,
+                  void* ws, size_t ws_bytes, int algo, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Stage 4a: CSA core attention.  [HCA-CSA] "设计：近处看原文，远处看摘要" (one softmax
+ * over [q K^swa || q K^comp || s_h], values [V^swa || V^comp || 0], K = V shared by
+ * all heads); [KV-COMP] sections 9.5-9.6 (window indices concatenated with the
+ * selected compressed indices).
+ *
+ * For query (b,s) and head h, with E = its window rows followed by the rows
+ * kv_comp[b, j] for every j in idx[b,s,:] that is not -1:
+ *     l_e = scale * (q[b,s,h,:] . kv_e)
+ *     M   = max(sink[h], max_e l_e),  den = exp(sink[h] - M) + sum_e exp(l_e - M)
+ *     out[b,s,h,:] = sum_e exp(l_e - M) * kv_e / den,   lse[b,s,h] = M + log(den).
+ * The sink enters the denominator only (unscaled).
+ *
+ *   q      [B,S,H,c]   dtype (CSA_BF16: H = 64, c = 512;  CSA_F32: H <= 64, c <= 512)
+ *   kv_comp[B,Nc,c]    dtype;   idx [B,S,k] int32 in [-1, Nc), no duplicates.
+ *   swa    [B,Ls,c]    dtype: raw KV of the Ls positions ending at the last query.
+ *          Query s (of S consecutive queries) uses rows
+ *          max(0, s+Ls-S-W+1) .. s+Ls-S  (positions t-W+1 .. t); requires Ls >= S.
+ *   sink   [H] fp32;  scale > 0 (normally 1/sqrt(c)).
+ *   out    [B,S,H,c]   dtype;  lse [B,S,H] fp32 natural log, or NULL.
+ *   ws >= csa_attn_workspace_size(...) bytes (split partial results).
+ * ------------------------------------------------------------------------------ */
+size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dtype);
+
+int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
+                    const void* swa, const float* sink, int dtype, float scale,
+                    int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Stage 4b: HCA core attention.  [HCA-CSA] "HCA：重压缩 + 全量" (no indexer: every
+ * completed, visible compressed entry plus the window and the sink); [KV-COMP]
+ * section 9.8 (entry j visible iff t >= m*j + m - 1).
+ *
+ * Same as csa_sparse_attn with the remote set of query (b,s) being the entries
+ * j < min(Nc, floor((q_pos[b,s] + 1) / m)).  q_pos [B,S] int64, consecutive
+ * positions within a sequence.  The workspace query takes max_rows = W + Nc.
+ * ------------------------------------------------------------------------------ */
+int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m,
+                   const void* swa, const float* sink, int dtype, float scale,
+                   int B, int S, int H, int c, int Nc, int Ls, int W,
+                   void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_MI355X_H */

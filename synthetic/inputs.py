@@ -269,3 +269,53 @@ def score_rows(seed: int, rows: int, n: int, kind: str = "gauss", n_vis=None) ->
         nv = np.broadcast_to(np.asarray(n_vis), (rows,))
         s[np.arange(n)[None, :] >= nv[:, None]] = -np.inf
     return s
+
+
+# ---------------------------------------------------------------------------
+# Small stage-level workloads for the parity tests
+# ---------------------------------------------------------------------------
+
+def indexer_inputs(seed: int, B: int, S: int, Nc: int, H_I: int = 64, d_I: int = 128) -> dict:
+    """FP8 indexer inputs: K rows unit-RMS, q Gaussian, w = N(0,1)/sqrt(d_I*H_I)."""
+    rs = _streams(seed, 3)
+    a = {}
+    a["kI_fp8"], a["kI_scale"] = to_fp8_rows(unit_rms_rows(rs[0], (B, Nc, d_I)))
+    a["qI_fp8"], a["qI_scale"] = to_fp8_rows(gaussian(rs[1], (B, S, H_I, d_I)))
+    a["w"] = gaussian(rs[2], (B, S, H_I), sigma=1.0 / np.sqrt(d_I * H_I))
+    return a
+
+
+def attention_inputs(seed: int, B: int, S: int, Nc: int, Ls: int, H: int = 64, c: int = 512) -> dict:
+    """bf16 attention inputs: unit-RMS KV and window rows, unit-RMS queries, N(0,1) sink."""
+    rs = _streams(seed, 4)
+    return {
+        "kv_comp_bf16": unit_rms_rows_bf16(rs[0], (B, Nc, c)),
+        "swa_bf16": to_bf16_bits(unit_rms_rows(rs[1], (B, Ls, c))),
+        "q_bf16": to_bf16_bits(unit_rms_rows(rs[2], (B, S, H, c))),
+        "sink": gaussian(rs[3], (H,)),
+    }
+
+
+def random_selection(seed: int, B: int, S: int, Nc: int, k: int, n_valid) -> np.ndarray:
+    """idx [B,S,k] int32: n_valid[b,s] distinct entries in ascending order, then -1."""
+    rng = _streams(seed, 1)[0]
+    idx = np.full((B, S, k), -1, np.int32)
+    nv = np.broadcast_to(np.asarray(n_valid), (B, S))
+    for b in range(B):
+        for s in range(S):
+            n = int(min(nv[b, s], k, Nc))
+            idx[b, s, :n] = np.sort(rng.choice(Nc, size=n, replace=False))
+    return idx
+
+
+def compressor_inputs(seed: int, B: int, T: int, d: int, m: int, c: int, overlap: bool, sigma_w: float,
+                      with_prev: bool) -> dict:
+    """hidden N(0,1) bf16 (plus the m previous tokens), W [d, S*c] and bias N(0, sigma_w)."""
+    rs = _streams(seed, 4)
+    ns = 4 if overlap else 2
+    a = {"hidden_bf16": to_bf16_bits(gaussian(rs[0], (B, T, d)))}
+    if with_prev:
+        a["hidden_prev_bf16"] = to_bf16_bits(gaussian(rs[1], (B, m, d)))
+    a["W_bf16"] = to_bf16_bits(gaussian(rs[2], (d, ns * c), sigma_w))
+    a["bias"] = gaussian(rs[3], (ns // 2, m, c), sigma_w)
+    return a

@@ -1,0 +1,115 @@
+"""Comparison rules between the HIP path and the oracle (test infrastructure).
+
+* fp32 outputs: max |gpu - oracle| <= 1e-5;  bf16 attention outputs: <= 2e-3.
+* bf16 compressed KV: within one bf16 spacing of the oracle's value (its rounding
+  step, taken at the oracle's magnitude).
+* FP8 codes: the row scale within 1e-5 relative; every code decodes to within half an
+  e4m3 step (plus 1e-5 relative) of the oracle's value, and codes may differ from the
+  oracle's own rounding only where the oracle's scaled value sits within 1e-4
+  relative of a rounding midpoint.
+* top-k: identical index sets except among entries whose oracle score is within
+  1e-5 relative of the oracle's k-th score (ties the two precisions may order
+  differently); same count, ascending order and -1 padding.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import csa_oracle as O
+
+TOL_F32 = 1e-5
+TOL_BF16_ATTN = 2e-3
+
+
+# ---- device transfer (plumbing) ----------------------------------------------------------
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 device tensor -> uint16 bit patterns on the host."""
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_f64(bits: np.ndarray) -> np.ndarray:
+    return O.bf16_bits_to_f64(bits)
+
+
+# ---- rules -----------------------------------------------------------------------------
+
+def assert_close(gpu, ref, tol, what=""):
+    gpu = np.asarray(gpu, np.float64); ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    both_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
+    err = np.where(both_inf, 0.0, np.abs(gpu - ref))
+    err = np.where(np.isnan(err), np.inf, err)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max abs error {worst:.3e} > {tol:.1e} at {np.unravel_index(np.argmax(err), err.shape)}"
+    return worst
+
+
+def bf16_spacing(x: np.ndarray) -> np.ndarray:
+    ax = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(ax, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def assert_bf16_within_one_step(gpu_bits: np.ndarray, ref: np.ndarray, what=""):
+    g = bf16_f64(gpu_bits)
+    err = np.abs(g - ref)
+    lim = bf16_spacing(ref)
+    bad = err > lim
+    assert not bad.any(), f"{what}: {int(bad.sum())} values beyond one bf16 step; worst ratio {float((err / lim).max()):.3f}"
+    return float((err / lim).max())
+
+
+def e4m3_step(v: np.ndarray) -> np.ndarray:
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (e - 3)
+
+
+def assert_fp8_rows(codes_g: np.ndarray, scale_g: np.ndarray, ref: np.ndarray, what=""):
+    codes_o, scale_o = O.quantize_rows_e4m3(ref)
+    rel = np.abs(scale_g.astype(np.float64) - scale_o) / np.maximum(scale_o, 1e-30)
+    assert rel.max() <= 1e-5, f"{what}: scale mismatch {rel.max():.2e}"
+    v = ref / np.maximum(scale_o.astype(np.float64), 1e-30)[..., None]
+    dec = O.e4m3fn_to_f64(codes_g) * scale_g.astype(np.float64)[..., None]
+    lim = (0.5 * e4m3_step(v) * (1 + 1e-5) + 1e-5 * np.abs(v)) * scale_o[..., None]
+    assert np.all(np.abs(dec - ref) <= lim), f"{what}: decoded FP8 farther than half a step"
+    diff = codes_g != codes_o
+    if diff.any():
+        step = e4m3_step(v[diff])
+        frac = np.abs(v[diff]) / step
+        dist = np.abs(frac - (np.floor(frac) + 0.5)) * step / np.maximum(np.abs(v[diff]), 1e-30)
+        assert np.all(dist <= 1e-4), f"{what}: {int(diff.sum())} codes differ away from a rounding midpoint"
+    return int(diff.sum())
+
+
+def assert_topk_equal(idx_g: np.ndarray, idx_o: np.ndarray, scores_o: np.ndarray, k: int, what="",
+                      rel=1e-5, exact=False):
+    idx_g = np.asarray(idx_g).reshape(-1, k)
+    idx_o = np.asarray(idx_o).reshape(-1, k)
+    sc = np.asarray(scores_o, np.float64).reshape(idx_o.shape[0], -1)
+    for r in range(idx_o.shape[0]):
+        g, o = idx_g[r], idx_o[r]
+        ng, no = int((g >= 0).sum()), int((o >= 0).sum())
+        assert ng == no, f"{what} row {r}: {ng} selected vs {no}"
+        assert np.all(g[ng:] == -1) and np.all(np.diff(g[:ng]) > 0), f"{what} row {r}: not ascending / padded"
+        if exact:
+            assert np.array_equal(g, o), f"{what} row {r}: index sets differ"
+            continue
+        sg, so = set(g[:ng].tolist()), set(o[:no].tolist())
+        if sg == so:
+            continue
+        kth = sc[r, o[:no]].min()
+        for j in sg ^ so:
+            assert abs(sc[r, j] - kth) <= rel * abs(kth), \
+                f"{what} row {r}: entry {j} (score {sc[r, j]}) differs, k-th score {kth}"

@@ -1,0 +1,87 @@
+"""The C ABI library loads and exports every symbol include/csa.h declares; host-side
+argument checks return their status without touching a GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+LIB = os.path.join(ROOT, "compressed_sparse_kv_amd", "libcsa.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    assert os.path.exists(LIB), "libcsa.so not built"
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert {"csa_compress", "csa_index_score", "csa_topk", "csa_sparse_attn", "hca_dense_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_declared_symbol():
+    from compressed_sparse_kv_amd import binding
+    assert set(declared_functions()) == set(binding.EXPORTS)
+
+
+def test_status_strings_and_version():
+    from compressed_sparse_kv_amd import binding
+    lib = binding.lib()
+    assert lib.csa_version() >= 100
+    for st in range(5):
+        assert lib.csa_status_string(st)
+    assert b"unknown" in lib.csa_status_string(99)
+
+
+def test_invalid_arguments_are_rejected_before_launch():
+    from compressed_sparse_kv_amd import binding
+    lib = binding.lib()
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced: the checks fail first
+    # null pointers
+    assert lib.csa_index_score(None, None, None, None, None, 2, None, 1, 1, 64, 128, 10, 4, None, None) == 1
+    # unsupported FP8 head shape
+    assert lib.csa_index_score(fake, fake, fake, fake, fake, 2, fake, 1, 1, 32, 128, 10, 4, fake, None) == 2
+    # fp32 path must not get scales
+    assert lib.csa_index_score(fake, fake, fake, fake, None, 0, fake, 1, 1, 4, 32, 10, 4, fake, None) == 1
+    # top-k: k out of range, bad algo, algo 2 without workspace
+    assert lib.csa_topk(fake, 1, 1, 10, 0, fake, None, 0, None) == 1
+    assert lib.csa_topk(fake, 1, 1, 10, 4096, fake, None, 0, None) == 1
+    assert lib.csa_topk_algo(fake, 1, 1, 10, 4, fake, None, 0, 7, None) == 1
+    assert lib.csa_topk_algo(fake, 1, 1, 10, 4, fake, None, 0, 2, None) == 3
+    # top-k: workspace given but too small
+    assert lib.csa_topk(fake, 4, 1, 100000, 512, fake, fake, 16, None) == 3
+    # compressor: T not a multiple of m, p0 > 0 with overlap and no previous block, bf16 d % 64
+    args = dict(hidden=fake, prev=None, dt=0, w=fake, bias=fake, ov=1, B=1, T=10, d=64, m=4, c=8, dr=4)
+    call = lambda **kw: lib.csa_compress(kw["hidden"], kw["prev"], kw["dt"], kw["w"], kw["bias"], kw["ov"],
+                                         kw["B"], kw["T"], kw["d"], kw["m"], kw["c"], kw["dr"], 1e4, 1e-6,
+                                         kw.get("p0", 0), fake, None, 0, fake, 1 << 30, None)
+    assert call(**args) == 1
+    assert call(**{**args, "T": 8, "p0": 4}) == 1
+    assert call(**{**args, "T": 8, "dt": 1, "d": 96}) == 2
+    # compressor workspace too small
+    assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0,
+                            fake, 8, None) == 3
+    # attention: Ls < S, unsupported bf16 shape, non-positive scale
+    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
+                               fake, None, None, 0, None) == 1
+    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128,
+                               fake, None, None, 0, None) == 2
+    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128,
+                              fake, None, None, 0, None) == 1
+
+
+def test_workspace_queries():
+    from compressed_sparse_kv_amd import binding as b
+    assert b.compress_workspace_size(1, 8192, 4, 512, True, True) == (8192 + 4) * 2048 * 4
+    assert b.compress_workspace_size(1, 8192, 4, 128, False, False) == 8192 * 256 * 4
+    assert b.topk_workspace_size(32, 32768, 512) > 0
+    assert b.attn_workspace_size(64, 1, 64, 512, 8320, 1) > 0          # split rows need partials
+    assert b.attn_workspace_size(1, 1, 8, 64, 160, 0) == 8 * 66 * 4    # fp32 path: one partial

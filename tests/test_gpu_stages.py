@@ -1,0 +1,223 @@
+"""Stage-by-stage parity of the HIP library against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail, plus the
+method's edge cases.  Every call goes through the C ABI (compressed_sparse_kv_amd.binding)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from synthetic import inputs as I
+from tests.parity import (TOL_BF16_ATTN, TOL_F32, assert_bf16_within_one_step, assert_close,
+                          assert_fp8_rows, assert_topk_equal, bf16_f64, dev, dev_bf16, host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------------------
+# Tiny fp32 layer, end to end: compress (main + indexer) -> scores -> top-k -> attention
+# ---------------------------------------------------------------------------------------
+
+def test_tiny_layer_chain_fp32(lib):
+    sh = I.TINY
+    a = I.tiny_inputs()
+    kw = dict(overlap=True, m=sh.m, d_rope=sh.d_rope, rope_theta=sh.rope_theta, rms_eps=1e-6, p0=0)
+    # oracle chain
+    kv_o = O.csa_compress(a["hidden"], a["W_comp"], a["B_comp"], c=sh.c, **kw)
+    kI_o = O.csa_compress(a["hidden"], a["W_icomp"], a["B_icomp"], c=sh.d_I, **kw)
+    sc_o = O.index_scores(a["qI"], a["w"], kI_o, a["q_pos"], sh.m)
+    idx_o = O.topk_indices(sc_o, sh.k)
+    o_o, lse_o = O.sparse_attention(a["q"], kv_o, idx_o, a["swa"], a["sink"], 1 / math.sqrt(sh.c), a["q_pos"], sh.W)
+    # GPU chain
+    hid = dev(a["hidden"])
+    kv = torch.empty(1, sh.N // sh.m, sh.c, device="cuda")
+    kI = torch.empty(1, sh.N // sh.m, sh.d_I, device="cuda")
+    lib.csa_compress(hid, None, dev(a["W_comp"].T), dev(a["B_comp"]), c=sh.c, out=kv, **kw)
+    lib.csa_compress(hid, None, dev(a["W_icomp"].T), dev(a["B_icomp"]), c=sh.d_I, out=kI, **kw)
+    qpos = dev(a["q_pos"])
+    sc = torch.empty(1, 1, sh.N // sh.m, device="cuda")
+    lib.csa_index_score(dev(a["qI"]), None, dev(a["w"]), kI, None, qpos, m=sh.m, scores=sc)
+    idx = torch.empty(1, 1, sh.k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(sc, sh.k, idx)
+    out = torch.empty(1, 1, sh.H, sh.c, device="cuda")
+    lse = torch.empty(1, 1, sh.H, device="cuda")
+    lib.csa_sparse_attn(dev(a["q"]), kv, idx, dev(a["swa"]), dev(a["sink"]), W=sh.W, out=out, lse=lse)
+    # the attention stage again, fed the oracle's indices and entries
+    out2 = torch.empty_like(out)
+    lib.csa_sparse_attn(dev(a["q"]), dev(kv_o.astype(np.float32)), dev(idx_o.astype(np.int32)), dev(a["swa"]),
+                        dev(a["sink"]), W=sh.W, out=out2)
+    torch.cuda.synchronize()
+    assert_close(kv.cpu().numpy(), kv_o, TOL_F32, "compressed KV")
+    assert_close(kI.cpu().numpy(), kI_o, TOL_F32, "indexer K")
+    assert_close(sc.cpu().numpy(), sc_o, TOL_F32, "index scores")
+    assert_topk_equal(idx.cpu().numpy(), idx_o, sc_o, sh.k, "top-k")
+    assert_close(out2.cpu().numpy(), o_o, TOL_F32, "attention (oracle indices)")
+    if np.array_equal(idx.cpu().numpy(), idx_o):
+        assert_close(out.cpu().numpy(), o_o, TOL_F32, "attention (end to end)")
+        assert_close(lse.cpu().numpy(), lse_o, TOL_F32, "lse")
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 2: FP8 index scores (decode kernel for S <= 4, prefill kernel above)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,Nc", [(2, 1, 1000), (3, 3, 257), (2, 37, 1000), (1, 130, 700)])
+def test_index_score_fp8(lib, B, S, Nc):
+    a = I.indexer_inputs(11 + S, B, S, Nc)
+    m = 4
+    # positions: the last query sees every entry in sequence 0; fewer elsewhere (causal edge)
+    pos = np.zeros((B, S), np.int64)
+    for b in range(B):
+        t_last = 4 * Nc - 1 - b * 37 - (0 if b == 0 else 1)
+        pos[b] = t_last - (S - 1) + np.arange(S)
+    pos = np.maximum(pos, 0)
+    sc = torch.empty(B, S, Nc, device="cuda")
+    lib.csa_index_score(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"]),
+                        dev(pos), m=m, scores=sc)
+    ref = O.index_scores(O.dequant_rows(a["qI_fp8"], a["qI_scale"]), a["w"],
+                         O.dequant_rows(a["kI_fp8"], a["kI_scale"]), pos, m)
+    torch.cuda.synchronize()
+    assert_close(sc.cpu().numpy(), ref, TOL_F32, "fp8 index scores")
+
+
+def test_index_score_fp8_nothing_visible(lib):
+    a = I.indexer_inputs(5, 1, 2, 300)
+    pos = np.array([[0, 2]], np.int64)                  # t < m - 1: no complete block yet
+    sc = torch.empty(1, 2, 300, device="cuda")
+    lib.csa_index_score(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"]),
+                        dev(pos), m=4, scores=sc)
+    assert torch.all(sc == -math.inf)
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 3: top-k, bit-exact on identical fp32 inputs
+# ---------------------------------------------------------------------------------------
+
+TOPK_CASES = [
+    # rows, Nc, k, kind, algo
+    (8, 1000, 32, "gauss", 1),
+    (6, 1000, 1, "ties", 1),
+    (4, 5000, 2048, "gauss", 1),
+    (5, 3000, 64, "const", 1),
+    (5, 3000, 64, "mixed", 1),
+    (3, 32768, 512, "gauss", 1),
+    (3, 32768, 512, "gauss", 2),
+    (3, 32768, 512, "ties", 2),
+    (2, 40000, 1024, "gauss", 1),
+    (2, 40000, 1024, "mixed", 2),
+    (2, 70000, 1024, "const", 2),
+]
+
+
+@pytest.mark.parametrize("rows,Nc,k,kind,algo", TOPK_CASES)
+def test_topk_exact(lib, rows, Nc, k, kind, algo):
+    rng = np.random.default_rng(rows * 7 + Nc + k)
+    n_vis = rng.integers(0, Nc + 1, rows)
+    n_vis[0] = Nc
+    if rows > 2:
+        n_vis[1] = 0                                   # nothing visible: all -1
+        n_vis[2] = min(Nc, max(1, k // 2))             # fewer candidates than k
+    s = I.score_rows(rows + Nc, rows, Nc, kind, n_vis)
+    idx = torch.empty(1, rows, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(dev(s[None]), k, idx, algo=algo)
+    ref = O.topk_indices(s, k)
+    torch.cuda.synchronize()
+    assert_topk_equal(idx.cpu().numpy(), ref, s, k, f"top-k {kind}", exact=True)
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 4: bf16 attention (CSA sparse and HCA dense)
+# ---------------------------------------------------------------------------------------
+
+def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=None):
+    Ls = S + W - 1
+    a = I.attention_inputs(seed, B, S, Nc, Ls)
+    if q_pos is None:
+        q_pos = np.tile(10 ** 6 - S + 1 + np.arange(S), (B, 1)).astype(np.int64)
+    q_f = bf16_f64(a["q_bf16"]); kv_f = bf16_f64(a["kv_comp_bf16"]); swa_f = bf16_f64(a["swa_bf16"])
+    out = torch.empty(B, S, 64, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, S, 64, device="cuda")
+    if dense:
+        lib.hca_dense_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(q_pos), dev_bf16(a["swa_bf16"]),
+                           dev(a["sink"]), m=m, W=W, out=out, lse=lse)
+        o_ref, l_ref = O.dense_attention(q_f, kv_f, q_pos, m, swa_f, a["sink"], 1 / math.sqrt(512), W)
+    else:
+        idx = I.random_selection(seed, B, S, Nc, k, n_valid)
+        lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(idx), dev_bf16(a["swa_bf16"]),
+                            dev(a["sink"]), W=W, out=out, lse=lse)
+        o_ref, l_ref = O.sparse_attention(q_f, kv_f, idx, swa_f, a["sink"], 1 / math.sqrt(512), q_pos, W)
+    torch.cuda.synchronize()
+    assert_close(bf16_f64(host_bits(out)), o_ref, TOL_BF16_ATTN, "attention output")
+    assert_close(lse.cpu().numpy(), l_ref, TOL_F32, "lse")
+
+
+def test_sparse_attn_decode_split_rows(lib):
+    # 3 queries -> several workgroups per query (LSE merge); idx with -1 padding
+    _attn_case(lib, B=3, S=1, Nc=2000, k=512, W=128, seed=1, n_valid=np.array([[512], [300], [0]]))
+
+
+def test_sparse_attn_prefill_windows(lib):
+    # consecutive queries, each with its own sliding window; many queries -> one workgroup per query
+    _attn_case(lib, B=2, S=40, Nc=900, k=64, W=128, seed=2, n_valid=64)
+
+
+def test_sparse_attn_many_queries_single_split(lib):
+    _attn_case(lib, B=8, S=64, Nc=600, k=96, W=128, seed=3, n_valid=90)
+
+
+def test_hca_dense_attn(lib):
+    # sequence 0 sees all 300 entries, sequence 1 only the first 200 (causal bound)
+    q_pos = np.array([[128 * 300 - 1], [128 * 200 + 126]], np.int64)
+    _attn_case(lib, B=2, S=1, Nc=300, k=0, W=128, seed=4, n_valid=0, dense=True, q_pos=q_pos)
+
+
+def test_hca_dense_attn_prefill_rows(lib):
+    S = 24
+    q_pos = np.tile(128 * 40 - S + np.arange(S), (1, 1)).astype(np.int64)   # crosses an entry boundary
+    _attn_case(lib, B=1, S=S, Nc=64, k=0, W=128, seed=5, n_valid=0, dense=True, q_pos=q_pos)
+
+
+def test_attention_sink_only_limit(lib):
+    a = I.attention_inputs(6, 1, 1, 100, 128)
+    idx = I.random_selection(6, 1, 1, 100, 32, 32)
+    out = torch.empty(1, 1, 64, 512, dtype=torch.bfloat16, device="cuda")
+    lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(idx), dev_bf16(a["swa_bf16"]),
+                        dev(np.full(64, 1e4, np.float32)), W=128, out=out)
+    assert torch.all(out.float().abs() == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# Stage 1: compressor (bf16 MFMA projection)
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("overlap,m,c,T,with_prev,out_kind", [
+    (True, 4, 512, 256, True, "bf16"),
+    (True, 4, 128, 200, True, "fp8"),
+    (True, 4, 512, 64, False, "bf16"),
+    (False, 128, 512, 512, False, "bf16"),
+])
+def test_compress_bf16(lib, overlap, m, c, T, with_prev, out_kind):
+    B, d = 2, 256
+    a = I.compressor_inputs(20 + m + c, B, T, d, m, c, overlap, 0.05, with_prev)
+    p0 = 4096 if with_prev else 0
+    kw = dict(overlap=overlap, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6, p0=p0)
+    hp = a.get("hidden_prev_bf16")
+    ref = O.csa_compress(bf16_f64(a["hidden_bf16"]), bf16_f64(a["W_bf16"]), a["bias"],
+                         hidden_prev=None if hp is None else bf16_f64(hp), **kw)
+    Wt = np.ascontiguousarray(a["W_bf16"].T)
+    n = T // m
+    if out_kind == "bf16":
+        out = torch.empty(B, n, c, dtype=torch.bfloat16, device="cuda")
+        lib.csa_compress(dev_bf16(a["hidden_bf16"]), None if hp is None else dev_bf16(hp), dev_bf16(Wt),
+                         dev(a["bias"]), out=out, **kw)
+        torch.cuda.synchronize()
+        assert_bf16_within_one_step(host_bits(out), ref, "compressed KV (bf16)")
+    else:
+        out = torch.empty(B, n, c, dtype=torch.uint8, device="cuda")
+        sc = torch.empty(B, n, device="cuda")
+        lib.csa_compress(dev_bf16(a["hidden_bf16"]), None if hp is None else dev_bf16(hp), dev_bf16(Wt),
+                         dev(a["bias"]), out=out, out_scale=sc, **kw)
+        torch.cuda.synchronize()
+        assert_fp8_rows(out.cpu().numpy(), sc.cpu().numpy(), ref, "indexer K (fp8)")
