@@ -1,0 +1,236 @@
+"""Throughput of the CSA decode hot path on one MI355X (plus the prefill indexer).
+
+One step = one CSA decode step of the V4-Flash-shaped workload (batch 32, 128K
+context, 32768 compressed entries per sequence, 64 indexer heads x 128 FP8, top-512,
+64 query heads x 512 bf16, 128-token window, per-head sink): lightning-indexer scores
+-> top-k -> sparse shared-KV attention, all through the C ABI.  Inputs are resident in
+HBM before timing; the step rotates over several independent input sets (together
+larger than the 256 MB Infinity Cache) so the indexer keys stream from HBM.
+
+Prints one JSON line (see the keys below).  `roofline` is for the dominant kernel
+(the indexer), timed with HIP events on the stream it runs on.  `cpu_baseline` is the
+CPU oracle on a bounded sample of the same workload.  `prefill_indexer` times the
+indexer over a prefill chunk (8192 queries x 34816 entries) against the matrix peaks.
+
+    python bench.py [--steps K] [--warmup W] [--sets N] [--no-cpu-baseline] [--no-prefill]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA decode tokens/s + HBM GB/s @128K ctx; prefill indexer TFLOPS (% roofline)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense MFMA
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    return p.parse_args()
+
+
+def index_score_bytes(B, S, Nc, H_I, d_I):
+    """Algorithmic HBM bytes of one indexer launch (decode: every visible key once)."""
+    per_query = Nc * (d_I + 4) + 4 * Nc + H_I * (d_I + 4 + 4) + 8   # keys+scales, scores, q+scale+w, pos
+    return B * S * per_query
+
+
+def decode_step_bytes(sh):
+    """Compulsory bytes of one decode step (the score/index round trip between stages excluded)."""
+    B = sh.B
+    keys = B * sh.n_c * (sh.d_I + 4)
+    gathered = B * (sh.k + sh.W) * sh.c * 2
+    q_and_o = 2 * B * sh.H * sh.c * 2
+    small = B * (sh.H_I * (sh.d_I + 8) + sh.k * 4 + 8) + sh.H * 4
+    return keys + gathered + q_and_o + small
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the multi-GPU sharding is described "
+                                   "in DESIGN.md and not launched", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    from compressed_sparse_kv_amd import binding as L
+    from synthetic import inputs as I
+
+    torch.cuda.set_device(0)
+    sh = I.FLASH_DECODE
+    dev = torch.device("cuda")
+
+    def up(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    def up_bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.time()
+    host_sets, sets = [], []
+    for i in range(args.sets):
+        a = I.decode_inputs(sh, seed=sh.seed + 100 * i).arrays
+        host_sets.append(a)
+        sets.append({
+            "kv": up_bf16(a["kv_comp_bf16"]), "swa": up_bf16(a["swa_bf16"]), "q": up_bf16(a["q_bf16"]),
+            "sink": up(a["sink"]), "pos": up(a["q_pos"]), "k8": up(a["kI_fp8"]), "ks": up(a["kI_scale"]),
+            "q8": up(a["qI_fp8"]), "qs": up(a["qI_scale"]), "w": up(a["w"]),
+        })
+    t_gen = time.time() - t_gen
+
+    B, Nc, k = sh.B, sh.n_c, sh.k
+    scores = torch.empty(B, 1, Nc, device=dev)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
+    tk_ws = torch.empty(L.topk_workspace_size(B, Nc, k), dtype=torch.uint8, device=dev)
+    at_ws_n = L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)
+    at_ws = torch.empty(max(at_ws_n, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record(stream)
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        if ev is not None:
+            ev[1].record(stream)
+        L.csa_topk(scores, k, idx, ws=tk_ws)
+        if ev is not None:
+            ev[2].record(stream)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps between two synchronisations
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel durations (separate pass with events between the stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dur = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    us = dur.mean(axis=0) * 1e3
+
+    isb = index_score_bytes(B, 1, Nc, sh.H_I, sh.d_I)
+    achieved = isb / (us[0] * 1e-6) / 1e9
+    step_bytes = decode_step_bytes(sh)
+    result = {
+        "metric": METRIC,
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-storage/bf16-mfma",
+        "data": "synthetic",
+        "config": {"workload": sh.name, "batch": B, "context_tokens": sh.t + 1, "ratio_m": sh.m,
+                   "entries": Nc, "top_k": k, "heads": sh.H, "head_dim": sh.c, "indexer_heads": sh.H_I,
+                   "indexer_dim": sh.d_I, "window": sh.W, "input_sets": args.sets},
+        "hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_bytes": step_bytes,
+        "kernels_us": {"csa_index_score": us[0], "csa_topk": us[1], "csa_sparse_attn": us[2]},
+        "roofline": {"kernel": "index_score_fp8_decode", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "bytes_per_launch": isb, "traffic": None},
+        "input_generation_s": t_gen,
+    }
+
+    if not args.no_prefill:
+        result["prefill_indexer"] = bench_prefill_indexer(torch, L, I, dev)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(host_sets, sh)
+
+    print(json.dumps(result))
+
+
+def bench_prefill_indexer(torch, L, I, dev, reps=10):
+    """Indexer over one prefill chunk: 8192 queries (positions 131072..139263) x 34816 entries."""
+    sh = I.PREFILL
+    n = sh.ctx // sh.m + sh.S // sh.m
+    a = I.indexer_inputs(sh.seed, 1, sh.S, n)
+    pos = (sh.ctx + np.arange(sh.S, dtype=np.int64))[None]
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q8, qs, w, k8, ks, qp = up(a["qI_fp8"]), up(a["qI_scale"]), up(a["w"]), up(a["kI_fp8"]), up(a["kI_scale"]), up(pos)
+    scores = torch.empty(1, sh.S, n, device=dev)
+    for _ in range(2):
+        L.csa_index_score(q8, qs, w, k8, ks, qp, m=sh.m, scores=scores)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.csa_index_score(q8, qs, w, k8, ks, qp, m=sh.m, scores=scores)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nvis = np.minimum(n, (pos[0] + 1) // sh.m)
+    flops = float(np.sum(nvis)) * sh.H_I * sh.d_I * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": "csa_prefill_chunk8192_ctx128k_indexer", "ms": ms, "causal_flops": flops,
+            "tflops": tflops, "frac_fp8_peak": tflops / FP8_PEAK_TFLOPS,
+            "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS,
+            "note": "contraction on bf16 MFMA (exact e4m3->bf16); FP8 MFMA accumulation misses the 1e-5 bound"}
+
+
+def cpu_baseline(host_sets, sh):
+    """The CPU oracle, as it stands, on every query of the rotated input sets."""
+    import math
+    from oracle import csa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t = time.time()
+    nq = 0
+    for a in host_sets:
+        qI = O.dequant_rows(a["qI_fp8"], a["qI_scale"])
+        for b in range(sh.B):
+            KI = O.dequant_rows(a["kI_fp8"][b:b + 1], a["kI_scale"][b:b + 1])
+            sc = O.index_scores(qI[b:b + 1], a["w"][b:b + 1], KI, a["q_pos"][b:b + 1], sh.m)
+            idx = O.topk_indices(sc, sh.k)
+            O.sparse_attention(O.bf16_bits_to_f64(a["q_bf16"][b:b + 1]),
+                               O.bf16_bits_to_f64(a["kv_comp_bf16"][b:b + 1]), idx,
+                               O.bf16_bits_to_f64(a["swa_bf16"][b:b + 1]), a["sink"], 1 / math.sqrt(sh.c),
+                               a["q_pos"][b:b + 1], sh.W)
+            nq += 1
+    el = time.time() - t
+    return {"value": nq / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nq} decode queries ({len(host_sets)} input sets x batch {sh.B}): "
+                      f"scores over {sh.n_c} entries, top-{sh.k}, attention over {sh.k}+{sh.W} rows; "
+                      f"{el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -12,12 +12,18 @@
 // bf16 kernel (H = 64 heads, c = 512).  A workgroup (4 waves, 16 heads each) owns one
 // query and a contiguous range of row chunks, so every gathered KV row is read from HBM
 // once for all 64 heads.  Per chunk of kRows rows:
-//   1. the rows are staged in LDS (row stride 1040 B, bank-conflict free for both reads);
+//   1. the rows are staged in LDS, row stride 1072 B (rows shift by 12 banks: the 16
+//      rows of a 16-byte operand read and the 4 rows of a transposed read never share
+//      a bank);
 //   2. S^T = KV_chunk . Q^T on MFMA (A = rows from LDS, B = the wave's Q in registers);
 //      the output layout of S^T (lane: head l%16, rows 4*(l/16)+i) is exactly the
 //      A-operand layout P needs below, so P never leaves registers;
 //   3. online softmax in the log2 domain (running max and sum per head);
-//   4. O += P . V on MFMA with V read from the same LDS rows (K = V).
+//   4. O += P . V on MFMA with V read from the same LDS rows (K = V) through the LDS
+//      transpose read ds_read_b64_tr_b16: in each 16-lane group, output lane i' slot j'
+//      receives input lane 4j'+i'/4 slot i'%4, so lanes 4j'..4j'+3 reading 16 columns of
+//      row R(j') hand every lane its column of 4 rows.  P enters as a bf16 hi + lo pair
+//      (two MFMAs on one V operand) so it keeps ~16 bits.
 // Several workgroups may split one query's rows; they write (m, l, O) partials and
 // attn_merge combines them with the sink (LSE merge).
 #include <algorithm>
@@ -29,7 +35,7 @@ namespace csa {
 constexpr int kAH = 64;
 constexpr int kAC = 512;
 constexpr int kRows = 32;
-constexpr int kRowStride = kAC * 2 + 16;          // bytes
+constexpr int kRowStride = kAC * 2 + 48;          // bytes
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -157,13 +163,17 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     const float alpha = exp2f(m_run - m_use);          // 0 when m_run = -inf
+    // P = P_hi + P_lo, both bf16: the two products with V keep P to ~16 bits, so the
+    // weights carry no bf16 rounding into the output (only its final rounding remains)
     float psum = 0.0f;
-    v8s pa;
+    v8s pa, pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float p = exp2f(sv[j] - m_use);
       psum += p;
-      pa[j] = static_cast<short>(f32_to_bf16(p));
+      const uint16_t hi = f32_to_bf16(p);
+      pa[j] = static_cast<short>(hi);
+      pb[j] = static_cast<short>(f32_to_bf16(p - bf16_to_f32(hi)));
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
@@ -177,17 +187,15 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i] *= ah[i];
     }
-    // ---- O += P . V, V rows read column-wise from LDS
-    const uint16_t* vl = reinterpret_cast<const uint16_t*>(rows_lds);
+    // ---- O += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
+    const uint8_t* vt = rows_lds + (4 * g + ((l & 15) >> 2)) * kRowStride + 8 * (l & 3);
 #pragma unroll
     for (int t = 0; t < kAC / 16; ++t) {
-      v8s vb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = 16 * (j >> 2) + 4 * g + (j & 3);
-        vb[j] = static_cast<short>(vl[row * (kRowStride / 2) + 16 * t + (l & 15)]);
-      }
+      const v4s v0 = lds_read_tr16(vt + 32 * t);
+      const v4s v1 = lds_read_tr16(vt + 32 * t + 16 * kRowStride);
+      const v8s vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       o[t] = mfma_bf16_16x16x32(pa, vb, o[t]);
+      o[t] = mfma_bf16_16x16x32(pb, vb, o[t]);
     }
     __syncthreads();
     if (more) swrite();
@@ -235,34 +243,51 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   }
 }
 
-// Combines the split partials of one query with the sink.  Grid: B*S, block 256.
+// Combines the split partials with the sink.  One wave per (query, head); lane l owns
+// columns 8l .. 8l+7 (c = 512) or a strided share of them, loads of every split in flight
+// together.  Grid: ceil(B*S*H / 4) blocks of 256 threads.
 template <typename OutT>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
-                                                  const float* __restrict__ sink, int nsplit, int H, int c,
+                                                  const float* __restrict__ sink, int nsplit, int H, int c, int nqh,
                                                   OutT* __restrict__ out, float* __restrict__ lse) {
-  const size_t qi = blockIdx.x;
-  for (int h = threadIdx.x / 64; h < H; h += blockDim.x / 64) {
-    const int lane = threadIdx.x & 63;
-    const float sink2 = sink[h] * kLog2e;
-    float M = sink2;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_ml[((qi * nsplit + i) * H + h) * 2]);
-    float den = M == -INFINITY ? 0.0f : exp2f(sink2 - M);
+  const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (qh >= nqh) return;
+  const int lane = threadIdx.x & 63;
+  const size_t qi = qh / H;
+  const int h = qh % H;
+  const float sink2 = sink[h] * kLog2e;
+  float M = sink2;
+  for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_ml[((qi * nsplit + i) * H + h) * 2]);
+  float den = M == -INFINITY ? 0.0f : exp2f(sink2 - M);
+  for (int i = 0; i < nsplit; ++i) {
+    const float mi = part_ml[((qi * nsplit + i) * H + h) * 2];
+    if (mi != -INFINITY) den += part_ml[((qi * nsplit + i) * H + h) * 2 + 1] * exp2f(mi - M);
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  for (int c0 = 8 * lane; c0 < c; c0 += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < nsplit; ++i) {
       const float mi = part_ml[((qi * nsplit + i) * H + h) * 2];
-      if (mi != -INFINITY) den += part_ml[((qi * nsplit + i) * H + h) * 2 + 1] * exp2f(mi - M);
-    }
-    for (int col = lane; col < c; col += 64) {
-      float acc = 0.0f;
-      for (int i = 0; i < nsplit; ++i) {
-        const float mi = part_ml[((qi * nsplit + i) * H + h) * 2];
-        if (mi != -INFINITY) acc += part_o[((qi * nsplit + i) * H + h) * c + col] * exp2f(mi - M);
+      const float wgt = mi == -INFINITY ? 0.0f : exp2f(mi - M);
+      const float* src = part_o + ((qi * nsplit + i) * H + h) * c + c0;
+      if (c0 + 8 <= c) {
+        const float4 x0 = reinterpret_cast<const float4*>(src)[0];
+        const float4 x1 = reinterpret_cast<const float4*>(src)[1];
+        acc[0] = fmaf(wgt, x0.x, acc[0]); acc[1] = fmaf(wgt, x0.y, acc[1]);
+        acc[2] = fmaf(wgt, x0.z, acc[2]); acc[3] = fmaf(wgt, x0.w, acc[3]);
+        acc[4] = fmaf(wgt, x1.x, acc[4]); acc[5] = fmaf(wgt, x1.y, acc[5]);
+        acc[6] = fmaf(wgt, x1.z, acc[6]); acc[7] = fmaf(wgt, x1.w, acc[7]);
+      } else {
+        for (int j = 0; j < 8 && c0 + j < c; ++j) acc[j] = fmaf(wgt, src[j], acc[j]);
       }
-      const float v = den > 0.0f ? acc / den : 0.0f;
-      if constexpr (sizeof(OutT) == 2) out[(qi * H + h) * c + col] = f32_to_bf16(v);
-      else out[(qi * H + h) * c + col] = v;
     }
-    if (lse && lane == 0) lse[qi * H + h] = (M == -INFINITY || den <= 0.0f) ? -INFINITY : (M + log2f(den)) * kLn2;
+    OutT* dst = out + (qi * H + h) * c + c0;
+    for (int j = 0; j < 8 && c0 + j < c; ++j) {
+      if constexpr (sizeof(OutT) == 2) dst[j] = f32_to_bf16(acc[j] * inv);
+      else dst[j] = acc[j] * inv;
+    }
   }
+  if (lse && lane == 0) lse[qi * H + h] = (M == -INFINITY || den <= 0.0f) ? -INFINITY : (M + log2f(den)) * kLn2;
 }
 
 // ------------------------------------------------------------------------------------
@@ -346,12 +371,13 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
 }
 
-// Splits used by the bf16 kernel for a query with up to max_rows rows.
+// Splits of one query's rows over workgroups (bf16 kernel).  Enough workgroups to cover
+// the 256 compute units, but every split keeps >= 128 rows: a split's partial result
+// (64 x 512 fp32 = 128 KiB) must stay small next to the rows it reads (1 KiB each).
 int attn_nsplit(int nq, int max_rows) {
-  const int chunks = cdiv(max_rows, kRows);
-  const int by_rows = cdiv(max_rows, 256);           // keep >= ~256 rows per split
-  const int by_fill = cdiv(512, nq);                 // aim for ~512 workgroups
-  return std::max(1, std::min(chunks, std::min(by_rows, by_fill)));
+  const int by_fill = cdiv(256, nq);
+  const int by_rows = max_rows / 128;
+  return std::max(1, std::min(by_fill, by_rows));
 }
 
 size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype) {
@@ -391,8 +417,8 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(256), 0, st, a);
     CSA_LAUNCH_CHECK();
     if (ns > 1) {
-      hipLaunchKernelGGL(attn_merge<uint16_t>, dim3(nq), dim3(256), 0, st, a.part_o, a.part_ml, sink, ns, H, c,
-                         static_cast<uint16_t*>(out), lse);
+      hipLaunchKernelGGL(attn_merge<uint16_t>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, a.part_o, a.part_ml, sink,
+                         ns, H, c, nq * H, static_cast<uint16_t*>(out), lse);
       CSA_LAUNCH_CHECK();
     }
     return CSA_OK;
@@ -410,8 +436,8 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
                        static_cast<const float*>(kv), idx, q_pos, static_cast<const float*>(swa), scale_log2, S, H, c,
                        Nc, k, Ls, W, m, part_o, part_ml);
   CSA_LAUNCH_CHECK();
-  hipLaunchKernelGGL(attn_merge<float>, dim3(nq), dim3(256), 0, st, part_o, part_ml, sink, 1, H, c,
-                     static_cast<float*>(out), lse);
+  hipLaunchKernelGGL(attn_merge<float>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, part_o, part_ml, sink, 1, H, c,
+                     nq * H, static_cast<float*>(out), lse);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

@@ -15,6 +15,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));          // 32 fp8 codes
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));        // 8 bf16 bit patterns
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));        // 4 bf16 bit patterns
 
 // D(16x16, fp32) += A(16x128 e4m3) * B(128x16 e4m3).  Lane l holds row/column l%16 of
 // A/B and one 32-byte group (l/16) of the reduction index in both operands, so the
@@ -27,6 +28,14 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, co
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8s& a, const v8s& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
                                                  __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  In each 16-lane group, output lane i' slot j'
+// receives input lane 4j' + i'/4 slot i'%4 (each input lane names 4 consecutive 16-bit
+// values at its address).
+__device__ __forceinline__ v4s lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
 }
 
 // ---- bfloat16 -------------------------------------------------------------------------

@@ -5,22 +5,50 @@
 // [HCA-CSA] section "CSA：轻压缩 + 稀疏选择" (indexer equations); [KV-COMP] sections 9.4
 // (score = sum over heads of w * ReLU(q . z)) and 9.8 (entry j visible once t >= m*j+m-1).
 //
-// FP8 path.  With q = dec(q8)*sq and K = dec(k8)*sk and non-negative scales,
+// FP8 inputs.  With q = dec(q8)*sq and K = dec(k8)*sk and non-negative scales,
 //   w * ReLU(sq*sk*dot) = sk * (w*sq) * ReLU(dot),   dot = dec(q8) . dec(k8),
-// so the MFMA contracts the raw codes (exact products, fp32 accumulation), each head's
-// partial is weighted by w' = w*sq after the ReLU, and the row scale sk multiplies once.
+// so the matrix unit contracts the decoded codes, each head's partial is weighted by
+// w' = w*sq after the ReLU, and the row scale sk multiplies once.
 //
-// MFMA mapping (v_mfma_f32_16x16x128_f8f6f4): M = 16 heads, N = 16 entries, K = d_I = 128
-// in one instruction.  Output lane l of a 16x16 tile holds heads 4*(l/16)+i of entry l%16;
-// a lane therefore weights-and-sums 16 heads of the 64 locally, and three cross-lane
-// exchanges finish the head sum for 4 entry blocks at once (a reduce-scatter that leaves
-// lane l holding entry e0+l of a 64-entry group, so stores are coalesced).
+// Precision.  The e4m3 codes stay the storage format (128 B + 4 B per entry) but the
+// contraction runs on bf16 MFMA (v_mfma_f32_16x16x32_bf16): e4m3 -> bf16 is exact
+// (v_cvt_scalef32_pk_bf16_fp8, scale 1), bf16 x bf16 products are exact in fp32 and the
+// bf16 unit accumulates at fp32 precision.  The gfx950 FP8 MFMA forms keep only about
+// 12 bits below the largest product of each 32-element block, about 1e-4 relative on
+// these dot products, which would not meet the 1e-5 bound on the fp32 scores.
+//
+// MFMA mapping: M = 16 heads, N = 16 entries, K = d_I = 128 in four 32-wide steps.
+// Lane l owns bytes 32*(l/16) .. +31 of its head's / entry's row and feeds them to the
+// four steps 8 at a time (the same k-slots on both operands, so the pairing is exact).
+// Output lane l of a 16x16 tile holds heads 4*(l/16)+i of entry l%16; a lane weights and
+// sums 16 heads of the 64 locally, and three cross-lane exchanges finish the head sum for
+// 4 entry blocks at once (a reduce-scatter leaving lane l with entry e0+l of a 64-entry
+// group, so stores are coalesced).
 #include "common.hpp"
 
 namespace csa {
 
-constexpr int kIH = 64;    // indexer heads handled by the FP8 kernels
-constexpr int kID = 128;   // indexer head dim handled by the FP8 kernels
+constexpr int kIH = 64;    // indexer heads handled by the FP8-input kernels
+constexpr int kID = 128;   // indexer head dim handled by the FP8-input kernels
+
+// 32 e4m3 codes (8 dwords) -> 32 bf16 (4 MFMA operands of 8 values each), exactly.
+__device__ __forceinline__ void e4m3x32_to_bf16(const v8i& c, v8s out[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<unsigned>(c[2 * ks]), 1.0f, false);
+    const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<unsigned>(c[2 * ks]), 1.0f, true);
+    const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<unsigned>(c[2 * ks + 1]), 1.0f, false);
+    const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<unsigned>(c[2 * ks + 1]), 1.0f, true);
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    v4i w;
+    w[0] = __builtin_bit_cast(int, p0);
+    w[1] = __builtin_bit_cast(int, p1);
+    w[2] = __builtin_bit_cast(int, p2);
+    w[3] = __builtin_bit_cast(int, p3);
+    out[ks] = __builtin_bit_cast(v8s, w);
+  }
+}
 
 // p[nb] = partial head-sum of entry (lane&15) of block nb over this lane's heads.
 // Returns, in lane l, the full sum for entry 16*(l>>4) + (l&15) = l of the 4 blocks.
@@ -37,27 +65,28 @@ __device__ __forceinline__ float reduce_scatter4(const float p[4]) {
 }
 
 // Weighted ReLU head-sum of one 16-entry block against the 4 head blocks of one query.
-__device__ __forceinline__ float head_sum(const v8i a[4], const v8i& bk, const float wv[16]) {
+__device__ __forceinline__ float head_sum(const v8s a[4][4], const v8s bk[4], const float wv[16]) {
   float acc = 0.0f;
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     v4f d = {0.f, 0.f, 0.f, 0.f};
-    d = mfma_fp8_16x16x128(a[hb], bk, d);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) d = mfma_bf16_16x16x32(a[hb][ks], bk[ks], d);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = fmaf(wv[hb * 4 + i], fmaxf(d[i], 0.0f), acc);
   }
   return acc;
 }
 
-// Loads the A operand (64 heads x 128 codes of one query) and its head weights w*sq.
+// A operand (64 heads x 128 codes of one query, as bf16) and its head weights w*sq.
 __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const float* __restrict__ qs,
-                                           const float* __restrict__ w, size_t row, v8i a[4],
+                                           const float* __restrict__ w, size_t row, v8s a[4][4],
                                            float wv[16]) {
   const int l = static_cast<int>(lane_id());
   const uint8_t* qr = q8 + row * (kIH * kID);
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb)
-    a[hb] = *reinterpret_cast<const v8i*>(qr + (16 * hb + (l & 15)) * kID + 32 * (l >> 4));
+    e4m3x32_to_bf16(*reinterpret_cast<const v8i*>(qr + (16 * hb + (l & 15)) * kID + 32 * (l >> 4)), a[hb]);
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
@@ -69,9 +98,9 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 
 // ------------------------------------------------------------------------------------
 // Decode: few queries per sequence.  Each wave streams 64-entry groups of its sequence's
-// K straight from HBM into MFMA operand registers (one 128-byte row = one cache line,
-// read by 4 lanes x 32 bytes); the next group's loads are in flight while the current
-// group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
+// K straight from HBM into registers (one 128-byte row = one cache line, read by 4 lanes
+// x 32 bytes), converts them and multiplies; the next group's loads are in flight while
+// the current group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
 // ------------------------------------------------------------------------------------
 constexpr int kDecGroups = 4;                         // 64-entry groups per wave
 constexpr int kDecEntWG = 4 * 64 * kDecGroups;        // entries per workgroup
@@ -87,7 +116,7 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
   const int64_t t = q_pos[row];
   const int nvis = static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m));
 
-  v8i a[4];
+  v8s a[4][4];
   float wv[16];
   load_query(q8, qs, w, row, a, wv);
 
@@ -97,29 +126,33 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
 
   // group gi of this wave covers entries e0 = base + 64*(gi*4 + wave) .. +63
   const int base = blockIdx.x * kDecEntWG;
-  auto load_group = [&](int e0, v8i bk[4]) {
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int e = min(e0 + 16 * nb + (l & 15), Nc - 1);
-      bk[nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e) * kID + 32 * (l >> 4));
-    }
-  };
-
   v8i cur[4], nxt[4];
+#define CSA_DEC_LOAD(e0_, dst)                                                                      \
+  do {                                                                                              \
+    _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                              \
+      const int e_ = min((e0_) + 16 * nb + (l & 15), Nc - 1);                                       \
+      dst[nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e_) * kID + 32 * (l >> 4));  \
+    }                                                                                               \
+  } while (0)
+
   int e0 = base + 64 * wave;
-  if (e0 < Nc && e0 < nvis) load_group(e0, cur);
-#pragma unroll 1
+  if (e0 < Nc && e0 < nvis) CSA_DEC_LOAD(e0, cur);
+#pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
     e0 = base + 64 * (gi * 4 + wave);
     if (e0 >= Nc) break;
     const int e1 = e0 + 256;
     const bool more = gi + 1 < kDecGroups && e1 < Nc && e1 < nvis;
-    if (more) load_group(e1, nxt);
+    if (more) CSA_DEC_LOAD(e1, nxt);
     const int e = e0 + l;
     if (e0 < nvis) {
       float p[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) p[nb] = head_sum(a, cur[nb], wv);
+      for (int nb = 0; nb < 4; ++nb) {
+        v8s bk[4];
+        e4m3x32_to_bf16(cur[nb], bk);
+        p[nb] = head_sum(a, bk, wv);
+      }
       const float v = reduce_scatter4(p);
       if (e < Nc) out[e] = e < nvis ? v * ksb[e] : -INFINITY;
     } else if (e < Nc) {
@@ -130,21 +163,24 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
       for (int nb = 0; nb < 4; ++nb) cur[nb] = nxt[nb];
     }
   }
+#undef CSA_DEC_LOAD
 }
 
 // ------------------------------------------------------------------------------------
-// Prefill: many queries per sequence.  A workgroup owns kPfQ queries (2 per wave, A
-// operands resident in registers) and walks the entry axis in tiles of kPfTile entries
-// staged in LDS (row stride 144 B: the 16 rows one MFMA operand read touches fall in
-// distinct banks).  Tiles beyond every query's visible range are written as -inf
-// without touching K.  Grid: (ceil(S / kPfQ), B).
+// Prefill: many queries per sequence.  A workgroup of 8 waves owns kPfQ = 8 queries (one
+// per wave, A operands resident in registers) and walks the entry axis in tiles of
+// kPfTile entries: each tile is read once from memory as e4m3, converted to bf16 once by
+// the loading threads, and staged in LDS (row stride 272 B: the 16 rows one operand read
+// touches fall in distinct banks).  Tiles beyond every query's visible range are written
+// as -inf without touching K.  Grid: (ceil(S / kPfQ), B).
 // ------------------------------------------------------------------------------------
-constexpr int kPfQW = 2;                 // queries per wave
-constexpr int kPfQ = 4 * kPfQW;          // queries per workgroup
-constexpr int kPfTile = 64;              // entries per LDS tile
-constexpr int kPfStride = kID + 16;      // LDS row stride in bytes
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfQ = kPfWaves;            // one query per wave
+constexpr int kPfTile = 64;               // entries per LDS tile
+constexpr int kPfStride = 2 * kID + 16;   // LDS row stride in bytes (bf16 rows)
 
-__global__ __launch_bounds__(256) void index_score_fp8_prefill(
+__global__ __launch_bounds__(kPfThreads) void index_score_fp8_prefill(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
     int S, int Nc, int m, float* __restrict__ scores) {
@@ -154,85 +190,82 @@ __global__ __launch_bounds__(256) void index_score_fp8_prefill(
   const int l = static_cast<int>(lane_id());
   const int wave = threadIdx.x >> 6;
   const int tid = threadIdx.x;
+  const int g = l >> 4;
 
-  // this wave's queries (clamped duplicates of the last one are computed, never stored)
-  v8i a[kPfQW][4];
-  float wv[kPfQW][16];
-  int nvis[kPfQW];
-  int qrow[kPfQW];
-  bool qlive[kPfQW];
-#pragma unroll
-  for (int j = 0; j < kPfQW; ++j) {
-    const int s = s0 + wave * kPfQW + j;
-    qlive[j] = s < S;
-    const size_t row = static_cast<size_t>(b) * S + min(s, S - 1);
-    qrow[j] = static_cast<int>(row);
-    load_query(q8, qs, w, row, a[j], wv[j]);
-    const int64_t t = q_pos[row];
-    nvis[j] = static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m));
-  }
+  // this wave's query (a clamped duplicate of the last one is computed, never stored)
+  const int s = s0 + wave;
+  const bool qlive = s < S;
+  const size_t qrow = static_cast<size_t>(b) * S + min(s, S - 1);
+  v8s a[4][4];
+  float wv[16];
+  load_query(q8, qs, w, qrow, a, wv);
+  const int nvis = static_cast<int>(min(static_cast<int64_t>(Nc), (q_pos[qrow] + 1) / m));
   // the workgroup's visible bound (max over its queries) decides which tiles are computed
   int wg_vis = 0;
-  for (int s = s0; s < min(S, s0 + kPfQ); ++s) {
-    const int64_t t = q_pos[static_cast<size_t>(b) * S + s];
+  for (int j = s0; j < min(S, s0 + kPfQ); ++j) {
+    const int64_t t = q_pos[static_cast<size_t>(b) * S + j];
     wg_vis = max(wg_vis, static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m)));
   }
 
   const uint8_t* kb = k8 + static_cast<size_t>(b) * Nc * kID;
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
+  float* out = scores + qrow * Nc;
   const int ntiles_vis = cdiv(wg_vis, kPfTile);
   const int ntiles = cdiv(Nc, kPfTile);
 
-  // cooperative tile load: thread t copies 32 bytes of entry t/4
-  const int le = tid >> 2, lb = 32 * (tid & 3);
-  auto gload = [&](int ti, uint4& x0, uint4& x1) {
-    const int e = min(ti * kPfTile + le, Nc - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(kb + static_cast<size_t>(e) * kID + lb);
-    x0 = src[0];
-    x1 = src[1];
-  };
-  auto swrite = [&](int buf, const uint4& x0, const uint4& x1) {
-    uint4* dst = reinterpret_cast<uint4*>(&tile[buf][le * kPfStride + lb]);
-    dst[0] = x0;
-    dst[1] = x1;
-  };
+  // cooperative tile load: thread t converts codes 16*(t%8) .. +15 of entry t/8
+  const int le = tid >> 3, lb = 16 * (tid & 7);
+  uint4 raw;
+#define CSA_PF_GLOAD(ti)                                                                    \
+  do {                                                                                      \
+    const int e_ = min((ti) * kPfTile + le, Nc - 1);                                        \
+    raw = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(e_) * kID + lb);         \
+  } while (0)
+#define CSA_PF_SWRITE(buf)                                                                  \
+  do {                                                                                      \
+    typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));                               \
+    const unsigned wd_[4] = {raw.x, raw.y, raw.z, raw.w};                                   \
+    unsigned cv_[8];                                                                        \
+    _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) {                                      \
+      cv_[2 * q_] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd_[q_], 1.0f, false)); \
+      cv_[2 * q_ + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd_[q_], 1.0f, true)); \
+    }                                                                                       \
+    uint4* dst_ = reinterpret_cast<uint4*>(&tile[buf][le * kPfStride + 2 * lb]);            \
+    dst_[0] = make_uint4(cv_[0], cv_[1], cv_[2], cv_[3]);                                   \
+    dst_[1] = make_uint4(cv_[4], cv_[5], cv_[6], cv_[7]);                                   \
+  } while (0)
 
-  uint4 x0, x1;
   if (ntiles_vis > 0) {
-    gload(0, x0, x1);
-    swrite(0, x0, x1);
+    CSA_PF_GLOAD(0);
+    CSA_PF_SWRITE(0);
   }
   __syncthreads();
 #pragma unroll 1
   for (int ti = 0; ti < ntiles_vis; ++ti) {
     const int buf = ti & 1;
     const bool more = ti + 1 < ntiles_vis;
-    if (more) gload(ti + 1, x0, x1);
-    const int e0 = ti * kPfTile;
-    v8i bk[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bk[nb] = *reinterpret_cast<const v8i*>(&tile[buf][(16 * nb + (l & 15)) * kPfStride + 32 * (l >> 4)]);
-    const int e = e0 + l;
+    if (more) CSA_PF_GLOAD(ti + 1);
+    const int e = ti * kPfTile + l;
     const float sk = e < Nc ? ksb[e] : 0.0f;
+    float p[4];
 #pragma unroll
-    for (int j = 0; j < kPfQW; ++j) {
-      float p[4];
+    for (int nb = 0; nb < 4; ++nb) {
+      v8s bk[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) p[nb] = head_sum(a[j], bk[nb], wv[j]);
-      const float v = reduce_scatter4(p);
-      if (qlive[j] && e < Nc) scores[static_cast<size_t>(qrow[j]) * Nc + e] = e < nvis[j] ? v * sk : -INFINITY;
+      for (int k4 = 0; k4 < 4; ++k4)
+        bk[k4] = *reinterpret_cast<const v8s*>(&tile[buf][(16 * nb + (l & 15)) * kPfStride + 64 * g + 16 * k4]);
+      p[nb] = head_sum(a, bk, wv);
     }
-    if (more) swrite(buf ^ 1, x0, x1);
+    const float v = reduce_scatter4(p);
+    if (qlive && e < Nc) out[e] = e < nvis ? v * sk : -INFINITY;
+    if (more) CSA_PF_SWRITE(buf ^ 1);
     __syncthreads();
   }
+#undef CSA_PF_GLOAD
+#undef CSA_PF_SWRITE
   // tiles no query of this workgroup can see
-  for (int ti = ntiles_vis; ti < ntiles; ++ti) {
-    const int e = ti * kPfTile + l;
-#pragma unroll
-    for (int j = 0; j < kPfQW; ++j)
-      if (qlive[j] && e < Nc) scores[static_cast<size_t>(qrow[j]) * Nc + e] = -INFINITY;
-  }
+  if (qlive)
+    for (int e = ntiles_vis * kPfTile + l; e < Nc; e += 64) out[e] = -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------
@@ -276,7 +309,7 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
                          k_scale, q_pos, S, Nc, m, scores);
     } else {
       dim3 grid(cdiv(S, kPfQ), B);
-      hipLaunchKernelGGL(index_score_fp8_prefill, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(index_score_fp8_prefill, grid, dim3(kPfThreads), 0, st,
                          static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k),
                          k_scale, q_pos, S, Nc, m, scores);
     }

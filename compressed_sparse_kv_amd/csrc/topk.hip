@@ -423,7 +423,9 @@ size_t topk_workspace_bytes(int rows, int Nc, int k) {
 // algo: 0 = automatic, 1 = one workgroup per row, 2 = several workgroups per row
 int launch_topk(const float* scores, int rows, int Nc, int k, int32_t* idx, void* ws, size_t ws_bytes,
                 int algo, hipStream_t st) {
-  if (algo == 0) algo = (rows < 96 && Nc >= 16384) ? 2 : 1;
+  // several workgroups per row only when a row does not fit in LDS and rows are too few
+  // to fill the chip (the 1M-context decode shape)
+  if (algo == 0) algo = (rows < 64 && Nc > kTkLdsKeys) ? 2 : 1;
   if (algo == 2 && (ws == nullptr || ws_bytes < topk_workspace_bytes(rows, Nc, k))) algo = 1;
   if (algo == 1) {
     if (Nc <= kTkLdsKeys) {

@@ -74,15 +74,46 @@ def unit_rms_rows(rng, shape) -> np.ndarray:
     return x
 
 
-def unit_rms_rows_bf16(rng, shape, chunk_rows=1 << 20) -> np.ndarray:
-    """Same distribution, produced in slabs straight to bf16 bits (bounded host memory)."""
+_CHUNK_ROWS = 8192
+
+
+def _chunked(rng, lead: int, fn, outs):
+    """Fills row slabs of `outs` (arrays with `lead` rows) with fn(child_rng, r0, r1).
+
+    Slab i always draws from child stream i (seeded from `rng`), so the result does not
+    depend on how many threads run the slabs."""
+    import concurrent.futures as cf
+    import os
+    nch = (lead + _CHUNK_ROWS - 1) // _CHUNK_ROWS
+    seeds = rng.integers(0, 2 ** 63 - 1, size=nch)
+
+    def work(i):
+        r0, r1 = i * _CHUNK_ROWS, min(lead, (i + 1) * _CHUNK_ROWS)
+        res = fn(np.random.default_rng(int(seeds[i])), r1 - r0)
+        for o, v in zip(outs, res):
+            o[r0:r1] = v
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1))) as ex:
+        list(ex.map(work, range(nch)))
+
+
+def unit_rms_rows_bf16(rng, shape) -> np.ndarray:
+    """Unit-RMS Gaussian rows produced slab by slab straight to bf16 bits."""
     lead = int(np.prod(shape[:-1]))
     c = shape[-1]
     out = np.empty((lead, c), dtype=np.uint16)
-    for r0 in range(0, lead, chunk_rows):
-        r1 = min(lead, r0 + chunk_rows)
-        out[r0:r1] = to_bf16_bits(unit_rms_rows(rng, (r1 - r0, c)))
+    _chunked(rng, lead, lambda r, n: (to_bf16_bits(unit_rms_rows(r, (n, c))),), (out,))
     return out.reshape(shape)
+
+
+def unit_rms_rows_fp8(rng, shape) -> tuple[np.ndarray, np.ndarray]:
+    """Unit-RMS Gaussian rows as e4m3 codes with their per-row scale, slab by slab."""
+    lead = int(np.prod(shape[:-1]))
+    c = shape[-1]
+    codes = np.empty((lead, c), dtype=np.uint8)
+    scale = np.empty((lead,), dtype=np.float32)
+    _chunked(rng, lead, lambda r, n: to_fp8_rows(unit_rms_rows(r, (n, c))), (codes, scale))
+    return codes.reshape(shape), scale.reshape(shape[:-1])
 
 
 # ---------------------------------------------------------------------------
@@ -134,11 +165,7 @@ def decode_inputs(sh: DecodeShape, seed: int | None = None, with_indexer: bool =
     a["sink"] = gaussian(rs[3], (sh.H,))
     a["q_pos"] = np.full((sh.B, 1), sh.t, dtype=np.int64)
     if with_indexer:
-        kI = np.empty((sh.B, sh.n_c, sh.d_I), np.uint8)
-        kIs = np.empty((sh.B, sh.n_c), np.float32)
-        for b in range(sh.B):                                     # per sequence: bounded memory
-            kI[b], kIs[b] = to_fp8_rows(unit_rms_rows(rs[4], (sh.n_c, sh.d_I)))
-        a["kI_fp8"], a["kI_scale"] = kI, kIs
+        a["kI_fp8"], a["kI_scale"] = unit_rms_rows_fp8(rs[4], (sh.B, sh.n_c, sh.d_I))
         a["qI_fp8"], a["qI_scale"] = to_fp8_rows(gaussian(rs[5], (sh.B, 1, sh.H_I, sh.d_I)))
         a["w"] = gaussian(rs[6], (sh.B, 1, sh.H_I), sigma=1.0 / np.sqrt(sh.d_I * sh.H_I))
     return DecodeInputs(sh, a)
@@ -188,7 +215,7 @@ def prefill_inputs(sh: PrefillShape = PREFILL, seed: int | None = None) -> dict:
     a["W_idx_bf16"] = to_bf16_bits(gaussian(rs[3], (sh.d, 4 * sh.d_I), sh.sigma_w))
     a["B_idx"] = gaussian(rs[4], (2, sh.m, sh.d_I), sh.sigma_w)
     a["kv_ctx_bf16"] = unit_rms_rows_bf16(rs[5], (1, n_ctx, sh.c))
-    a["kI_ctx_fp8"], a["kI_ctx_scale"] = to_fp8_rows(unit_rms_rows(rs[6], (1, n_ctx, sh.d_I)))
+    a["kI_ctx_fp8"], a["kI_ctx_scale"] = unit_rms_rows_fp8(rs[6], (1, n_ctx, sh.d_I))
     a["q_bf16"] = unit_rms_rows_bf16(rs[7], (1, sh.S, sh.H, sh.c))
     a["qI_fp8"], a["qI_scale"] = to_fp8_rows(gaussian(rs[8], (1, sh.S, sh.H_I, sh.d_I)))
     a["w"] = gaussian(rs[9], (1, sh.S, sh.H_I), sigma=1.0 / np.sqrt(sh.d_I * sh.H_I))
@@ -279,7 +306,7 @@ def indexer_inputs(seed: int, B: int, S: int, Nc: int, H_I: int = 64, d_I: int =
     """FP8 indexer inputs: K rows unit-RMS, q Gaussian, w = N(0,1)/sqrt(d_I*H_I)."""
     rs = _streams(seed, 3)
     a = {}
-    a["kI_fp8"], a["kI_scale"] = to_fp8_rows(unit_rms_rows(rs[0], (B, Nc, d_I)))
+    a["kI_fp8"], a["kI_scale"] = unit_rms_rows_fp8(rs[0], (B, Nc, d_I))
     a["qI_fp8"], a["qI_scale"] = to_fp8_rows(gaussian(rs[1], (B, S, H_I, d_I)))
     a["w"] = gaussian(rs[2], (B, S, H_I), sigma=1.0 / np.sqrt(d_I * H_I))
     return a

@@ -1,6 +1,8 @@
 """Comparison rules between the HIP path and the oracle (test infrastructure).
 
-* fp32 outputs: max |gpu - oracle| <= 1e-5;  bf16 attention outputs: <= 2e-3.
+* fp32 outputs: max |gpu - oracle| <= 1e-5;  bf16 attention outputs: <= 2e-3, except
+  where the exact value has magnitude >= 0.5: there a bf16 number cannot be trusted to
+  lie within 2e-3 of it (the rounding step is 2^-8 .. ) and one bf16 step is allowed.
 * bf16 compressed KV: within one bf16 spacing of the oracle's value (its rounding
   step, taken at the oracle's magnitude).
 * FP8 codes: the row scale within 1e-5 relative; every code decodes to within half an
@@ -44,14 +46,28 @@ def bf16_f64(bits: np.ndarray) -> np.ndarray:
 
 # ---- rules -----------------------------------------------------------------------------
 
+def assert_bf16_output(gpu, ref, what=""):
+    """bf16 outputs: |gpu - oracle| <= max(2e-3, one bf16 step at the oracle's value)."""
+    ref = np.asarray(ref, np.float64)
+    tol = np.maximum(TOL_BF16_ATTN, np.where(np.abs(ref) >= 0.5, bf16_spacing(ref), 0.0))
+    err = np.abs(np.asarray(gpu, np.float64) - ref)
+    if np.any(err > tol):
+        i = np.unravel_index(np.argmax(err / tol), err.shape)
+        raise AssertionError(f"{what}: error {err[i]:.3e} > {tol[i]:.1e} at {i}: gpu {gpu[i]!r} oracle {ref[i]!r}")
+    return float(err.max())
+
+
 def assert_close(gpu, ref, tol, what=""):
     gpu = np.asarray(gpu, np.float64); ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     both_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
-    err = np.where(both_inf, 0.0, np.abs(gpu - ref))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_inf, 0.0, np.abs(gpu - ref))
     err = np.where(np.isnan(err), np.inf, err)
     worst = float(err.max()) if err.size else 0.0
-    assert worst <= tol, f"{what}: max abs error {worst:.3e} > {tol:.1e} at {np.unravel_index(np.argmax(err), err.shape)}"
+    if worst > tol:
+        i = np.unravel_index(np.argmax(err), err.shape)
+        raise AssertionError(f"{what}: max abs error {worst:.3e} > {tol:.1e} at {i}: gpu {gpu[i]!r} oracle {ref[i]!r}")
     return worst
 
 
@@ -62,11 +78,18 @@ def bf16_spacing(x: np.ndarray) -> np.ndarray:
 
 
 def assert_bf16_within_one_step(gpu_bits: np.ndarray, ref: np.ndarray, what=""):
+    """|gpu - oracle| <= one bf16 step at the oracle's value + the fp32 allowance 1e-5.
+
+    The kernel rounds its own fp32 result to bf16; that result differs from the oracle's
+    by fp32 rounding noise, which near zero can exceed a (tiny) bf16 step."""
     g = bf16_f64(gpu_bits)
     err = np.abs(g - ref)
-    lim = bf16_spacing(ref)
+    lim = bf16_spacing(ref) + TOL_F32
     bad = err > lim
-    assert not bad.any(), f"{what}: {int(bad.sum())} values beyond one bf16 step; worst ratio {float((err / lim).max()):.3f}"
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / lim), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} values beyond one bf16 step + 1e-5; worst at {i}: "
+                             f"gpu {g[i]!r} oracle {ref[i]!r}")
     return float((err / lim).max())
 
 

@@ -10,7 +10,7 @@ import torch
 
 from oracle import csa_oracle as O
 from synthetic import inputs as I
-from tests.parity import (TOL_BF16_ATTN, TOL_F32, assert_bf16_within_one_step, assert_close,
+from tests.parity import (TOL_BF16_ATTN, TOL_F32, assert_bf16_output, assert_bf16_within_one_step, assert_close,
                           assert_fp8_rows, assert_topk_equal, bf16_f64, dev, dev_bf16, host_bits)
 
 pytestmark = pytest.mark.gpu
@@ -149,7 +149,7 @@ def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=Non
                             dev(a["sink"]), W=W, out=out, lse=lse)
         o_ref, l_ref = O.sparse_attention(q_f, kv_f, idx, swa_f, a["sink"], 1 / math.sqrt(512), q_pos, W)
     torch.cuda.synchronize()
-    assert_close(bf16_f64(host_bits(out)), o_ref, TOL_BF16_ATTN, "attention output")
+    assert_bf16_output(bf16_f64(host_bits(out)), o_ref, "attention output")
     assert_close(lse.cpu().numpy(), l_ref, TOL_F32, "lse")
 
 
