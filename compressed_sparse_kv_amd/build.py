@@ -30,9 +30,16 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Per-file device code generation options.  The indexer keeps its MFMA accumulators in
+# ordinary VGPRs (its epilogue reads every result with VALU instructions, which would
+# otherwise need one accvgpr move per value); attention keeps the AGPR form for its
+# 128 output accumulators.
+PER_FILE = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> tuple[str, str]:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *PER_FILE.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -9,6 +9,7 @@ int launch_index_score(const void*, const float*, const float*, const void*, con
                        int, int, int, int, int, float*, hipStream_t);
 int launch_topk(const float*, int, int, int, int32_t*, void*, size_t, int, hipStream_t);
 size_t topk_workspace_bytes(int, int, int);
+bool topk_supported(int, int, bool);
 int launch_attention(bool, const void*, const void*, const int32_t*, const int64_t*, int, const void*, const float*,
                      int, float, int, int, int, int, int, int, int, int, void*, float*, void*, size_t, hipStream_t);
 size_t attn_workspace_bytes(int, int, int, int, int, int);
@@ -101,8 +102,9 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
   CSA_REQUIRE(algo >= 0 && algo <= 2);
   const int64_t rows = static_cast<int64_t>(B) * S;
   CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
+  if (!topk_supported(Nc, k, true)) return CSA_ERR_UNSUPPORTED;
   if (ws != nullptr && ws_bytes < topk_workspace_bytes(static_cast<int>(rows), Nc, k)) return CSA_ERR_WORKSPACE;
-  if (algo == 2 && ws == nullptr) return CSA_ERR_WORKSPACE;
+  if (ws == nullptr && (algo == 2 || !topk_supported(Nc, k, false))) return CSA_ERR_WORKSPACE;
   return launch_topk(scores, static_cast<int>(rows), Nc, k, idx, ws, ws_bytes, algo, as_stream(stream));
 }
 

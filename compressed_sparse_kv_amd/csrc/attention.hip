@@ -35,6 +35,7 @@ namespace csa {
 constexpr int kAH = 64;
 constexpr int kAC = 512;
 constexpr int kRows = 32;
+constexpr int kMaxSplitSlots = 4096;              // selected entries staged per workgroup
 constexpr int kRowStride = kAC * 2 + 48;          // bytes
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -66,6 +67,7 @@ template <bool kDense>
 __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t rows_lds[kRows * kRowStride];
   __shared__ int valid_lds[kRows];
+  __shared__ int sel_lds[kMaxSplitSlots];
   const int qi = blockIdx.y;
   const int split = blockIdx.x;
   const int b = qi / a.S, s = qi % a.S;
@@ -83,13 +85,22 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
 
   const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
-  const int32_t* idxq = kDense ? nullptr : a.idx + static_cast<size_t>(qi) * a.k;
+  // CSA: this split's selected entries, staged once in LDS so the row loads of a chunk
+  // can be issued back to back (no index load between them)
+  const int slot0 = ch0 * kRows;
+  if (!kDense) {
+    const int32_t* idxq = a.idx + static_cast<size_t>(qi) * a.k;
+    const int r0 = max(0, slot0 - n_swa);
+    const int r1 = min(a.k, ch1 * kRows - n_swa);
+    for (int r = r0 + static_cast<int>(threadIdx.x); r < r1; r += 256) sel_lds[r - r0] = idxq[r];
+    __syncthreads();
+  }
   // slot -> row pointer, nullptr for padding / an absent (-1) index
   auto slot_row = [&](int slot) -> const uint16_t* {
     if (slot >= n_slots) return nullptr;
     if (slot < n_swa) return swab + static_cast<size_t>(w_lo + slot) * kAC;
     const int r = slot - n_swa;
-    const int j = kDense ? r : idxq[r];
+    const int j = kDense ? r : sel_lds[r - max(0, slot0 - n_swa)];
     if (j < 0 || j >= a.Nc) return nullptr;
     return kvb + static_cast<size_t>(j) * kAC;
   };
@@ -377,7 +388,8 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
 int attn_nsplit(int nq, int max_rows) {
   const int by_fill = cdiv(256, nq);
   const int by_rows = max_rows / 128;
-  return std::max(1, std::min(by_fill, by_rows));
+  const int by_lds = cdiv(max_rows, kMaxSplitSlots);  // a split's selection fits its LDS table
+  return std::max(by_lds, std::max(1, std::min(by_fill, by_rows)));
 }
 
 size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype) {
@@ -406,7 +418,7 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     a.scale_log2 = scale_log2;
     a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
     a.nsplit = ns;
-    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
+    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);   // <= kMaxSplitSlots / kRows by attn_nsplit
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     float* wsf = static_cast<float*>(ws);

@@ -64,18 +64,25 @@ __device__ __forceinline__ float reduce_scatter4(const float p[4]) {
   return keep + wave_xor(send, 16);
 }
 
+// ReLU as one instruction: med3(x, 0, 3e38) (fmaxf would also emit a NaN-quieting max).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
+
 // Weighted ReLU head-sum of one 16-entry block against the 4 head blocks of one query.
-__device__ __forceinline__ float head_sum(const v8s a[4][4], const v8s bk[4], const float wv[16]) {
-  float acc = 0.0f;
+// Each head block is a chain of 4 MFMAs followed by its 16 VALU epilogue operations; the
+// epilogue of block hb overlaps the MFMA chain of block hb+1 (MFMA and VALU co-issue),
+// and each head block sums into its own accumulator.
+__device__ __forceinline__ float head_sum1(const v8s a[4][4], const v8s b[4], const float wv[16]) {
+  float s[4];
 #pragma unroll
   for (int hb = 0; hb < 4; ++hb) {
     v4f d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) d = mfma_bf16_16x16x32(a[hb][ks], bk[ks], d);
+    for (int ks = 0; ks < 4; ++ks) d = mfma_bf16_16x16x32(a[hb][ks], b[ks], d);
+    s[hb] = wv[hb * 4] * relu(d[0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = fmaf(wv[hb * 4 + i], fmaxf(d[i], 0.0f), acc);
+    for (int i = 1; i < 4; ++i) s[hb] = fmaf(wv[hb * 4 + i], relu(d[i]), s[hb]);
   }
-  return acc;
+  return (s[0] + s[1]) + (s[2] + s[3]);
 }
 
 // A operand (64 heads x 128 codes of one query, as bf16) and its head weights w*sq.
@@ -102,7 +109,7 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 // x 32 bytes), converts them and multiplies; the next group's loads are in flight while
 // the current group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
 // ------------------------------------------------------------------------------------
-constexpr int kDecGroups = 4;                         // 64-entry groups per wave
+constexpr int kDecGroups = 8;                         // 64-entry groups per wave
 constexpr int kDecEntWG = 4 * 64 * kDecGroups;        // entries per workgroup
 
 __global__ __launch_bounds__(256) void index_score_fp8_decode(
@@ -116,51 +123,48 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
   const int64_t t = q_pos[row];
   const int nvis = static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m));
 
-  v8s a[4][4];
-  float wv[16];
-  load_query(q8, qs, w, row, a, wv);
-
   const uint8_t* kb = k8 + static_cast<size_t>(b) * Nc * kID;
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
   float* out = scores + row * Nc;
 
-  // group gi of this wave covers entries e0 = base + 64*(gi*4 + wave) .. +63
+  // group gi of this wave covers entries base + 64*(gi*4 + wave) .. +63; the keys of
+  // the next two groups are in flight while a group is multiplied
   const int base = blockIdx.x * kDecEntWG;
-  v8i cur[4], nxt[4];
-#define CSA_DEC_LOAD(e0_, dst)                                                                      \
+  auto group_e0 = [&](int gi) { return base + 64 * (gi * 4 + wave); };
+  auto group_live = [&](int gi) { const int e0 = group_e0(gi); return e0 < Nc && e0 < nvis; };
+  v8i ring[3][4];
+#define CSA_DEC_LOAD(gi_)                                                                           \
   do {                                                                                              \
     _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                              \
-      const int e_ = min((e0_) + 16 * nb + (l & 15), Nc - 1);                                       \
-      dst[nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e_) * kID + 32 * (l >> 4));  \
+      const int e_ = min(group_e0(gi_) + 16 * nb + (l & 15), Nc - 1);                               \
+      ring[(gi_) % 3][nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e_) * kID + 32 * (l >> 4)); \
     }                                                                                               \
   } while (0)
+  if (group_live(0)) CSA_DEC_LOAD(0);
+  if (group_live(1)) CSA_DEC_LOAD(1);
 
-  int e0 = base + 64 * wave;
-  if (e0 < Nc && e0 < nvis) CSA_DEC_LOAD(e0, cur);
+  v8s a[4][4];
+  float wv[16];
+  load_query(q8, qs, w, row, a, wv);
+
 #pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
-    e0 = base + 64 * (gi * 4 + wave);
+    const int e0 = group_e0(gi);
     if (e0 >= Nc) break;
-    const int e1 = e0 + 256;
-    const bool more = gi + 1 < kDecGroups && e1 < Nc && e1 < nvis;
-    if (more) CSA_DEC_LOAD(e1, nxt);
+    if (gi + 2 < kDecGroups && group_live(gi + 2)) CSA_DEC_LOAD(gi + 2);
     const int e = e0 + l;
     if (e0 < nvis) {
       float p[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         v8s bk[4];
-        e4m3x32_to_bf16(cur[nb], bk);
-        p[nb] = head_sum(a, bk, wv);
+        e4m3x32_to_bf16(ring[gi % 3][nb], bk);
+        p[nb] = head_sum1(a, bk, wv);
       }
       const float v = reduce_scatter4(p);
       if (e < Nc) out[e] = e < nvis ? v * ksb[e] : -INFINITY;
     } else if (e < Nc) {
       out[e] = -INFINITY;
-    }
-    if (more) {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) cur[nb] = nxt[nb];
     }
   }
 #undef CSA_DEC_LOAD
@@ -180,7 +184,7 @@ constexpr int kPfQ = kPfWaves;            // one query per wave
 constexpr int kPfTile = 64;               // entries per LDS tile
 constexpr int kPfStride = 2 * kID + 16;   // LDS row stride in bytes (bf16 rows)
 
-__global__ __launch_bounds__(kPfThreads) void index_score_fp8_prefill(
+__global__ __launch_bounds__(kPfThreads, 4) void index_score_fp8_prefill(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
     int S, int Nc, int m, float* __restrict__ scores) {
@@ -223,7 +227,6 @@ __global__ __launch_bounds__(kPfThreads) void index_score_fp8_prefill(
   } while (0)
 #define CSA_PF_SWRITE(buf)                                                                  \
   do {                                                                                      \
-    typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));                               \
     const unsigned wd_[4] = {raw.x, raw.y, raw.z, raw.w};                                   \
     unsigned cv_[8];                                                                        \
     _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) {                                      \
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kPfThreads) void index_score_fp8_prefill(
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4)
         bk[k4] = *reinterpret_cast<const v8s*>(&tile[buf][(16 * nb + (l & 15)) * kPfStride + 64 * g + 16 * k4]);
-      p[nb] = head_sum(a, bk, wv);
+      p[nb] = head_sum1(a, bk, wv);
     }
     const float v = reduce_scatter4(p);
     if (qlive && e < Nc) out[e] = e < nvis ? v * sk : -INFINITY;

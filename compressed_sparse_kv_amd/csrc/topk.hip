@@ -5,450 +5,578 @@
 // [KV-COMP] sections 9.4 (S_t = TopK_k of the indexer scores) and 9.8 (invisible entries
 // are -inf before the selection and -1 after it).
 //
-// Scores become order-preserving 32-bit keys (score_key).  A radix select over three
-// digits (11, 11, 10 bits) finds the key T of the kk-th largest candidate and how many
-// keys equal to T must be taken (need_eq).  The selection is then {key > T} plus the
-// first need_eq entries with key == T in index order.
+// Scores become order-preserving 32-bit keys (score_key); the order used throughout is
+// (key descending, position ascending), a total order, and positions are laid out in
+// ascending index order, so "the kk first elements in this order" is exactly the
+// required selection.  One workgroup of 1024 threads selects over a set of up to
+// kTkMaxChunks * 4096 keys held in registers (4 consecutive positions per thread and
+// 4096-position chunk):
+//   1. candidate count and min/max of the candidate values (block reduction);
+//   2. histogram over 2048 equal-width bins of [min, max]  (bin = trunc((x-min)*scale),
+//      monotone in x because every rounding step is);
+//   3. the bin b holding the kk-th element; elements in higher bins are taken, elements
+//      in b go to an LDS candidate list;
+//   4. the candidates are ranked against each other in the total order, which finds the
+//      pivot: the kk-th element (T, posT);
+//   5. an element is taken iff it precedes or equals the pivot, and an ordered compaction
+//      (per-wave counts, one scan) writes the taken indices in position order.
+// When equal-width bins cannot separate the values (all equal, infinities, or more
+// than kTkCandCap elements in bin b), steps 2-4 become an exact radix select over the
+// three key digits (11, 11, 10 bits) followed by a tie rank among keys equal to T.
 //
-// Two schedules:
-//  * one workgroup per row (1024 threads): the row's keys sit in LDS when they fit
-//    (Nc <= kTkLdsKeys), otherwise each pass re-reads the scores; the output is written
-//    in index order by a ballot compaction, so it needs no sort;
-//  * few long rows: G workgroups per row build the first-digit histogram and collect
-//    the entries above / inside the threshold bin; one workgroup per row then finishes
-//    the select on the (small) candidate set and sorts the <= k chosen indices.
+// Schedules:
+//   * one workgroup per row when the row fits one workgroup's registers;
+//   * G segments per row: one workgroup per segment writes its local top-k as (key,
+//     index) pairs in index order, then one workgroup per row selects the global top-k
+//     among the G*k pairs.  The union of the local top-k sets holds the global top-k
+//     (same total order), so the result is identical.
+#include <algorithm>
+#include <cmath>
+
 #include "common.hpp"
 
 namespace csa {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kTkLdsKeys = 36864;                 // 144 KiB of keys
-constexpr int kTkBins = 2048;
+constexpr int kTkChunk = 4 * kTkThreads;       // positions per register chunk
+constexpr int kTkMaxChunks = 9;                // 36864 keys per workgroup
+constexpr int kTkMaxSet = kTkMaxChunks * kTkChunk;
+constexpr int kTkBins = 1024;                  // equal-width bins of the fast path
+constexpr int kTkPB = kTkBins / kWave;
+constexpr int kTkHistWords = 2048 + 4 * 64;    // largest padded histogram (11-bit digit)
+constexpr int kTkCandCap = 1024;
+
 // radix digits, most significant first: bits 31..21, 20..10, 9..0
 __host__ __device__ constexpr inline int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __host__ __device__ constexpr inline int digit_bins(int pass) { return pass < 2 ? 2048 : 1024; }
 
-// ---- block-wide helpers for 1024 threads ---------------------------------------------
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = static_cast<int>(lane_id());
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(v, o, kWave);
-    if (l >= o) v += y;
-  }
-  return v;
-}
-
-struct TkShared {
-  uint32_t hist[kTkBins];
-  int wtot[kTkWaves];
-  int wgt[kTkWaves];
-  int weq[kTkWaves];
-  int bin;
-  int above;
-  int ncand;
+struct alignas(16) TkShared {
+  uint32_t hist[kTkHistWords];
+  uint32_t ckey[kTkCandCap];
+  int32_t cpos[kTkCandCap];
+  int cell_nz[kTkMaxChunks * kTkWaves];   // candidates per (chunk, wave)
+  int cell[kTkMaxChunks * kTkWaves];      // taken elements per (chunk, wave) above bin b / > T
+  int cell_eq[kTkMaxChunks * kTkWaves];   // exact path: keys equal to T per (chunk, wave)
+  uint32_t red_lo[kTkWaves], red_hi[kTkWaves];   // smallest and largest candidate key per wave
+  int ncand, posT;
+  uint32_t T;
 };
 
-// Given hist[0..nbins) and `remain` (>= 1, <= total), finds the bin b such that
-// (#keys in bins > b) < remain <= (#keys in bins >= b).  Writes sh.bin, sh.above.
-// Needs 1024 threads and nbins <= 2048.
-__device__ void find_threshold_bin(TkShared& sh, int nbins, int remain) {
-  const int tid = threadIdx.x, w = tid >> 6;
-  // thread t owns the bins at descending positions r = 2t, 2t+1 (bin = nbins-1-r)
-  int c0 = 0, c1 = 0;
-  const int r0 = 2 * tid, r1 = 2 * tid + 1;
-  if (r0 < nbins) c0 = static_cast<int>(sh.hist[nbins - 1 - r0]);
-  if (r1 < nbins) c1 = static_cast<int>(sh.hist[nbins - 1 - r1]);
-  const int incl = wave_incl_scan(c0 + c1);
-  if (lane_id() == 63) sh.wtot[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += sh.wtot[i];
-  const int p1 = before + incl;          // keys in bins at positions <= r1
-  const int p0 = p1 - c1;                // keys in bins at positions <= r0
-  const int pm = p0 - c0;                // keys in bins at positions < r0
-  if (r0 < nbins && pm < remain && remain <= p0) { sh.bin = nbins - 1 - r0; sh.above = pm; }
-  if (r1 < nbins && p0 < remain && remain <= p1) { sh.bin = nbins - 1 - r1; sh.above = p0; }
-  __syncthreads();
+// Wave64 inclusive prefix sum by DPP: row shifts 1, 2, 4, 8 scan each 16-lane row, then
+// row broadcasts of lanes 15 and 31 carry the row totals forward.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
 }
 
-// Radix select over all keys of a row held either in LDS (keys != nullptr) or re-read
-// from `scores`.  Returns T and need_eq (keys == T to take); kk >= 1.
-template <typename KeyAt>
-__device__ void radix_select(TkShared& sh, KeyAt key_at, int n, int kk, uint32_t& T, int& need_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  int remain = kk;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = digit_shift(pass), nbins = digit_bins(pass);
-    for (int i = tid; i < nbins; i += kTkThreads) sh.hist[i] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += kTkThreads) {
-      const uint32_t key = key_at(j);
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    find_threshold_bin(sh, nbins, remain);
-    prefix |= static_cast<uint32_t>(sh.bin) << shift;
-    mask |= static_cast<uint32_t>(nbins - 1) << shift;
-    remain -= sh.above;
-    __syncthreads();
-  }
-  T = prefix;
-  need_eq = remain;
+// Wave64 maximum (the same DPP pattern; 0 is the identity).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  const int x = static_cast<int>(v);
+  int m = x;
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x111, 0xf, 0xf, false))));
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x112, 0xf, 0xf, false))));
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x114, 0xf, 0xf, false))));
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x118, 0xf, 0xf, false))));
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x142, 0xa, 0xf, false))));
+  m = static_cast<int>(max(static_cast<uint32_t>(m), static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, m, 0x143, 0xc, 0xf, false))));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(m, 63));
 }
 
-// Writes the selection {key > T} + first need_eq of {key == T} in index order, then -1s.
-template <typename KeyAt>
-__device__ void ordered_compaction(TkShared& sh, KeyAt key_at, int n, int k, int kk, uint32_t T,
-                                   int need_eq, int32_t* __restrict__ out) {
-  const int tid = threadIdx.x, w = tid >> 6;
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6); }
+
+// Candidate value of a non-zero key (inverse of score_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Histograms have 64 * PB bins stored with 4 padding words after every PB bins, so
+// that 64 lanes reading PB consecutive bins each hit distinct LDS banks.
+template <int PB>
+__device__ __forceinline__ int hist_slot(int bin) { return bin + 4 * (bin / PB); }
+
+// Threshold search run by every wave on its own over the complete histogram (no
+// barrier): with 1 <= remain <= total, returns the bin b with
+// (#keys in bins > b) < remain <= (#keys in bins >= b) and sets above = #keys in bins > b.
+template <int PB>
+__device__ __forceinline__ int wave_threshold_bin(const uint32_t* hist, int remain, int& above) {
+  constexpr int nbins = kWave * PB;
   const int l = static_cast<int>(lane_id());
-  const int span = cdiv(cdiv(n, kTkWaves), kWave) * kWave;      // contiguous range per wave
-  const int j0 = w * span, j1 = min(n, j0 + span);
-  int gt = 0, eq = 0;
-  for (int j = j0 + l; j - l < j1; j += kWave) {
-    const uint32_t key = j < j1 ? key_at(j) : 0u;
-    gt += __popcll(__ballot(key > T));
-    eq += __popcll(__ballot(key == T && key != 0u));
+  // lane l sums group l counted from the top: bins nbins - PB*(l+1) .. nbins - 1 - PB*l
+  const uint32_t* g = hist + hist_slot<PB>(nbins - PB * (l + 1));
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < PB; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(g + i);
+    sum += static_cast<int>(v.x + v.y + v.z + v.w);
   }
-  if (l == 0) { sh.wgt[w] = gt; sh.weq[w] = eq; }
-  __syncthreads();
-  int eq_run = 0, pos = 0;
-  for (int i = 0; i < w; ++i) {
-    const int take = max(0, min(need_eq - eq_run, sh.weq[i]));
-    pos += sh.wgt[i] + take;
-    eq_run += sh.weq[i];
-  }
-  for (int j = j0 + l; j - l < j1; j += kWave) {
-    const uint32_t key = j < j1 ? key_at(j) : 0u;
-    const uint64_t em = __ballot(key == T && key != 0u);
-    const bool sel = key > T || (key == T && key != 0u && eq_run + lanes_below(em) < need_eq);
-    const uint64_t sm = __ballot(sel);
-    if (sel) out[pos + lanes_below(sm)] = j;
-    pos += __popcll(sm);
-    eq_run += __popcll(em);
-  }
-  for (int p = kk + tid; p < k; p += kTkThreads) out[p] = -1;
+  const int incl = wave_incl_scan(sum);
+  const int L = __ffsll(static_cast<long long>(__ballot(incl >= remain))) - 1;
+  const int before = __builtin_amdgcn_readlane(incl - sum, L);
+  // inside group L, lane j < PB takes the j-th bin from the top
+  const int c = l < PB ? static_cast<int>(hist[hist_slot<PB>(nbins - 1 - (PB * L + l))]) : 0;
+  const int incl2 = wave_incl_scan(c);
+  const int J = __ffsll(static_cast<long long>(__ballot(l < PB && before + incl2 >= remain))) - 1;
+  above = before + __builtin_amdgcn_readlane(incl2 - c, J);
+  return nbins - 1 - (PB * L + J);
 }
 
-__device__ int count_candidates(TkShared& sh, int local) {
-  const int w = threadIdx.x >> 6;
-  const int s = wave_sum_int(local);
-  if (lane_id() == 0) sh.wtot[w] = s;
-  __syncthreads();
-  int tot = 0;
-  for (int i = 0; i < kTkWaves; ++i) tot += sh.wtot[i];
-  __syncthreads();
-  return tot;
+// (chunk, wave) cell of a position, and the first position of a cell
+__device__ __forceinline__ int cell_of(int pos) { return (pos >> 12) * kTkWaves + ((pos & (kTkChunk - 1)) >> 8); }
+
+// Exclusive prefix sums over the cells (chunk, wave) order, computed by every wave:
+// returns the sum over the cells before cell (u, w) for each chunk u.
+template <int NU>
+__device__ __forceinline__ void cells_before(const int* cells, int w, int (&out)[NU]) {
+  constexpr int kCells = NU * kTkWaves;
+  constexpr int kJ = (kCells + kWave - 1) / kWave;
+  const int l = static_cast<int>(lane_id());
+  int cexcl[kJ], cbase[kJ];
+  int run = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {        // cell 64*j + lane in register j
+    const int c = kWave * j + l;
+    const int v = c < kCells ? cells[c] : 0;
+    const int incl = wave_incl_scan(v);
+    cexcl[j] = incl - v;
+    cbase[j] = run;
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u)          // cell u*16 + w: register u/4, lane 16*(u%4) + w
+    out[u] = cbase[u >> 2] + __builtin_amdgcn_readlane(cexcl[u >> 2], 16 * (u & 3) + w);
 }
 
-// One workgroup per row.  kInLds: the row's keys are cached in LDS.
-template <bool kInLds>
+// Selection over the keys of one set held in registers: key[u][s] is the key of position
+// 4096*u + 4*threadIdx.x + s (0 = not a candidate).  Returns kk = min(k, #candidates);
+// sets bit 4u+s of `taken` for the taken elements and obase[u] to the output slot of
+// this thread's first taken element of chunk u (taken elements fill slots 0..kk-1 in
+// position order).
+template <int NU>
+__device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][4], int k, uint64_t& taken, int (&obase)[NU]) {
+  const int tid = threadIdx.x, w = wave_index();
+  const int l = static_cast<int>(lane_id());
+  // ---- 1. candidates per cell and the key range
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t kv = key[u][s];
+      cnt += __popcll(__ballot(kv != 0u));
+      if (kv != 0u) {
+        kmin = min(kmin, kv);
+        kmax = max(kmax, kv);
+      }
+    }
+    if (l == 0) sh.cell_nz[u * kTkWaves + w] = cnt;
+  }
+  for (int i = tid; i < kTkHistWords; i += kTkThreads) sh.hist[i] = 0;
+  if (tid == 0) sh.ncand = 0;
+  kmax = wave_max_u32(kmax);
+  kmin = ~wave_max_u32(~kmin);
+  if (l == 0) { sh.red_lo[w] = kmin; sh.red_hi[w] = kmax; }
+  __syncthreads();                                                    // barrier 1
+  int total = 0;
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kTkWaves; ++i) {
+    kmin = min(kmin, sh.red_lo[i]);
+    kmax = max(kmax, sh.red_hi[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NU * kTkWaves; ++i) total += sh.cell_nz[i];
+  const int kk = __builtin_amdgcn_readfirstlane(min(k, total));
+  taken = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) obase[u] = 0;
+  if (kk == 0) return 0;
+
+  uint32_t T = 0u;
+  int posT = -1;                 // pivot; (0, -1) takes every candidate
+  int sel_before[NU];            // taken candidates of bin b before each of this wave's cells
+  int eq_before[NU];             // exact path: keys == T before each of this wave's cells
+  bool exact = false;
+  int need_eq = 0;
+  const int* cells = sh.cell_nz;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) { sel_before[u] = 0; eq_before[u] = 0; }
+  if (kk < total) {
+    const float lo = key_value(kmin);
+    const float range = key_value(kmax) - lo;
+    const float scale = static_cast<float>(kTkBins) / range;
+    bool ok = range > 0.0f && range <= 3.0e38f && scale <= 3.0e38f;
+    int b = 0, remain = 0;
+    if (ok) {
+      // ---- 2. histogram over equal-width bins of [min, max]
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (key[u][s] != 0u) {
+            const int bn = min(kTkBins - 1, static_cast<int>((key_value(key[u][s]) - lo) * scale));
+            atomicAdd(&sh.hist[hist_slot<kTkPB>(bn)], 1u);
+          }
+      __syncthreads();                                                // barrier 2
+      int above;
+      b = wave_threshold_bin<kTkPB>(sh.hist, kk, above);
+      remain = kk - above;
+      ok = static_cast<int>(sh.hist[hist_slot<kTkPB>(b)]) <= kTkCandCap;
+    }
+    if (ok) {
+      // ---- 3. higher bins are taken (counted per cell); bin b goes to the list
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int g = 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t kv = key[u][s];
+          const int bn = kv != 0u ? min(kTkBins - 1, static_cast<int>((key_value(kv) - lo) * scale)) : -1;
+          g += __popcll(__ballot(bn > b));
+          const uint64_t m = __ballot(bn == b);
+          if (m != 0) {
+            int base = 0;
+            const int leader = __ffsll(static_cast<long long>(m)) - 1;
+            if (l == leader) base = atomicAdd(&sh.ncand, __popcll(m));
+            base = __builtin_amdgcn_readlane(base, leader);
+            if (bn == b) {
+              const int p = base + lanes_below(m);
+              sh.ckey[p] = kv;
+              sh.cpos[p] = kTkChunk * u + 4 * tid + s;
+            }
+          }
+        }
+        if (l == 0) sh.cell[u * kTkWaves + w] = g;
+      }
+      __syncthreads();                                                // barrier 3
+      cells = sh.cell;
+      // ---- 4. rank the candidates; the remain-th is the pivot
+      const int nc = __builtin_amdgcn_readfirstlane(sh.ncand);
+      if (nc <= kWave) {
+        // every wave ranks the list itself: candidate l in lane l, the others by readlane
+        const uint32_t ki = l < nc ? sh.ckey[l] : 0u;
+        const int pi = l < nc ? sh.cpos[l] : 0;
+        int r = 0;
+        for (int j = 0; j < nc; ++j) {
+          const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), j));
+          const int pj = __builtin_amdgcn_readlane(pi, j);
+          r += (kj > ki || (kj == ki && pj < pi)) ? 1 : 0;
+        }
+        const bool sel = l < nc && r < remain;
+        const int lp = __ffsll(static_cast<long long>(__ballot(l < nc && r == remain - 1))) - 1;
+        T = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), lp));
+        posT = __builtin_amdgcn_readlane(pi, lp);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          sel_before[u] = __popcll(__ballot(sel && pi < kTkChunk * u + 256 * w));
+      } else {
+        for (int i = tid; i < nc; i += kTkThreads) {
+          const uint32_t ki = sh.ckey[i];
+          const int pi = sh.cpos[i];
+          int r = 0;
+          for (int j = 0; j < nc; ++j) {
+            const uint32_t kj = sh.ckey[j];
+            r += (kj > ki || (kj == ki && sh.cpos[j] < pi)) ? 1 : 0;
+          }
+          if (r < remain) atomicAdd(&sh.cell[cell_of(pi)], 1);
+          if (r == remain - 1) { sh.T = ki; sh.posT = pi; }
+        }
+        __syncthreads();
+        T = sh.T;
+        posT = sh.posT;
+      }
+    } else {
+      // ---- exact radix select over the three key digits
+      uint32_t prefix = 0, mask = 0;
+      int rem = kk;
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = digit_shift(pass), nbins = digit_bins(pass);
+        __syncthreads();
+        for (int i = tid; i < kTkHistWords; i += kTkThreads) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const uint32_t kv = key[u][s];
+            if (kv != 0u && (kv & mask) == prefix) {
+              const int d = static_cast<int>((kv >> shift) & (nbins - 1));
+              atomicAdd(&sh.hist[nbins == 2048 ? hist_slot<32>(d) : hist_slot<16>(d)], 1u);
+            }
+          }
+        __syncthreads();
+        int above, bb;
+        if (nbins == 2048) bb = wave_threshold_bin<32>(sh.hist, rem, above);
+        else bb = wave_threshold_bin<16>(sh.hist, rem, above);
+        prefix |= static_cast<uint32_t>(bb) << shift;
+        mask |= static_cast<uint32_t>(nbins - 1) << shift;
+        rem -= above;
+      }
+      T = prefix;
+      need_eq = rem;
+      exact = true;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int g = 0, e = 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          g += __popcll(__ballot(key[u][s] > T));
+          e += __popcll(__ballot(key[u][s] == T));
+        }
+        if (l == 0) { sh.cell[u * kTkWaves + w] = g; sh.cell_eq[u * kTkWaves + w] = e; }
+      }
+      __syncthreads();
+      cells = sh.cell;
+      cells_before<NU>(sh.cell_eq, w, eq_before);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) sel_before[u] = min(need_eq, eq_before[u]);
+    }
+  }
+  // ---- 5. output slots: cells before this one, then lanes before this one
+  int base[NU];
+  cells_before<NU>(cells, w, base);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int c = 0;
+    if (exact) {
+      int e = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) e += key[u][s] == T ? 1 : 0;
+      int r = eq_before[u] + wave_incl_scan(e) - e;        // rank among keys == T
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t kv = key[u][s];
+        bool t = kv > T;
+        if (kv == T) t = r++ < need_eq;
+        if (t) { taken |= 1ull << (4 * u + s); ++c; }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t kv = key[u][s];
+        const int pos = kTkChunk * u + 4 * tid + s;
+        if (kv > T || (kv == T && pos <= posT)) { taken |= 1ull << (4 * u + s); ++c; }
+      }
+    }
+    obase[u] = base[u] + sel_before[u] + wave_incl_scan(c) - c;
+  }
+  return kk;
+}
+
+// Loads positions [0, n) of a score row as keys into registers (key 0 beyond n).
+template <int NU>
+__device__ __forceinline__ void load_score_keys(uint32_t (&key)[NU][4], const float* __restrict__ s, int n) {
+  const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;
+  float4 v[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int p = kTkChunk * u + 4 * static_cast<int>(threadIdx.x);
+    if (vec && p + 3 < n) {
+      v[u] = *reinterpret_cast<const float4*>(s + p);
+    } else {
+      v[u].x = p < n ? s[p] : -INFINITY;
+      v[u].y = p + 1 < n ? s[p + 1] : -INFINITY;
+      v[u].z = p + 2 < n ? s[p + 2] : -INFINITY;
+      v[u].w = p + 3 < n ? s[p + 3] : -INFINITY;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    key[u][0] = score_key(v[u].x);
+    key[u][1] = score_key(v[u].y);
+    key[u][2] = score_key(v[u].z);
+    key[u][3] = score_key(v[u].w);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// One workgroup per row (Nc <= NU * 4096).
+// ---------------------------------------------------------------------------------------
+template <int NU>
 __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict__ scores, int Nc, int k,
                                                         int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t lkeys[];
   __shared__ TkShared sh;
   const size_t row = blockIdx.x;
-  const float* sr = scores + row * Nc;
+  uint32_t key[NU][4];
+  load_score_keys<NU>(key, scores + row * Nc, Nc);
+  uint64_t taken;
+  int obase[NU];
+  const int kk = select_regs<NU>(sh, key, k, taken, obase);
   int32_t* out = idx + row * k;
-  int local = 0;
-  for (int j = threadIdx.x; j < Nc; j += kTkThreads) {
-    const uint32_t key = score_key(sr[j]);
-    if (kInLds) lkeys[j] = key;
-    local += key != 0u;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int o = obase[u];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if ((taken >> (4 * u + s)) & 1ull) out[o++] = kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s;
   }
-  const int ncand = count_candidates(sh, local);
-  const int kk = min(k, ncand);
-  auto key_at = [&](int j) -> uint32_t { return kInLds ? lkeys[j] : score_key(sr[j]); };
-  if (kk == 0) {
-    for (int p = threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
-    return;
-  }
-  uint32_t T;
-  int need_eq;
-  radix_select(sh, key_at, Nc, kk, T, need_eq);
-  ordered_compaction(sh, key_at, Nc, k, kk, T, need_eq, out);
+  for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
-// Multi-workgroup schedule for few long rows.
-// Workspace per row: hist[2048] u32 | counters[4] (ncand, ngt, ncand_bin, pad) |
-//                    gt[k] i32 | cand_key[cap] u32 | cand_idx[cap] i32
+// Segmented schedule.  Workspace cand[rows][G][k] of (key, index) pairs, key 0 = empty,
+// each segment's pairs in ascending index order.  Grid (rows, G).
 // ---------------------------------------------------------------------------------------
-constexpr int kMwThreads = 256;
-constexpr int kMwCap = 8192;                  // threshold-bin candidates kept per row
-constexpr int kMwSegment = 4096;              // scores per workgroup in the parallel passes
-
-struct MwRow {
-  uint32_t* hist;
-  int* counters;
-  int32_t* gt;
-  uint32_t* ckey;
-  int32_t* cidx;
-};
-
-__host__ __device__ inline size_t mw_row_words(int k) { return kTkBins + 4 + k + 2 * kMwCap; }
-
-__device__ inline MwRow mw_row(uint32_t* ws, int k, size_t row) {
-  uint32_t* base = ws + row * mw_row_words(k);
-  MwRow r;
-  r.hist = base;
-  r.counters = reinterpret_cast<int*>(base + kTkBins);
-  r.gt = reinterpret_cast<int32_t*>(base + kTkBins + 4);
-  r.ckey = base + kTkBins + 4 + k;
-  r.cidx = reinterpret_cast<int32_t*>(base + kTkBins + 4 + k + kMwCap);
-  return r;
-}
-
-__global__ void topk_mw_clear(uint32_t* __restrict__ ws, int k, int rows) {
-  const size_t words = kTkBins + 4;
-  for (size_t i = blockIdx.x * blockDim.x + threadIdx.x; i < rows * words; i += gridDim.x * blockDim.x) {
-    const size_t r = i / words, o = i % words;
-    ws[r * mw_row_words(k) + o] = 0u;
-  }
-}
-
-__global__ __launch_bounds__(kMwThreads) void topk_mw_hist(const float* __restrict__ scores, int Nc, int k,
-                                                           uint32_t* __restrict__ ws) {
-  __shared__ uint32_t h[kTkBins];
-  __shared__ int wcnt[kMwThreads / kWave];
-  const size_t row = blockIdx.y;
-  const MwRow R = mw_row(ws, k, row);
-  const float* sr = scores + row * Nc;
-  for (int i = threadIdx.x; i < kTkBins; i += kMwThreads) h[i] = 0u;
-  __syncthreads();
-  const int j0 = blockIdx.x * kMwSegment, j1 = min(Nc, j0 + kMwSegment);
-  int local = 0;
-  for (int j = j0 + threadIdx.x; j < j1; j += kMwThreads) {
-    const uint32_t key = score_key(sr[j]);
-    if (key != 0u) {
-      atomicAdd(&h[key >> 21], 1u);
-      ++local;
-    }
-  }
-  local = wave_sum_int(local);
-  if (lane_id() == 0) wcnt[threadIdx.x >> 6] = local;
-  __syncthreads();
-  for (int i = threadIdx.x; i < kTkBins; i += kMwThreads)
-    if (h[i]) atomicAdd(&R.hist[i], h[i]);
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int i = 0; i < kMwThreads / kWave; ++i) tot += wcnt[i];
-    if (tot) atomicAdd(&R.counters[0], tot);
-  }
-}
-
-// First-digit threshold bin of a row from its global histogram (256 threads).
-__device__ void mw_threshold(const MwRow& R, int k, uint32_t* lh, int* scratch, int& bin, int& above, int& kk) {
-  const int ncand = R.counters[0];
-  kk = min(k, ncand);
-  for (int i = threadIdx.x; i < kTkBins; i += kMwThreads) lh[i] = R.hist[i];
-  __syncthreads();
-  // thread t owns 8 bins at descending positions 8t .. 8t+7
-  int c[8], tot = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { c[i] = static_cast<int>(lh[kTkBins - 1 - (8 * threadIdx.x + i)]); tot += c[i]; }
-  const int incl = wave_incl_scan(tot);
-  const int w = threadIdx.x >> 6;
-  if (lane_id() == 63) scratch[w] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += scratch[i];
-  int run = before + incl - tot;
-  if (kk > 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (run < kk && kk <= run + c[i]) { scratch[4] = kTkBins - 1 - (8 * threadIdx.x + i); scratch[5] = run; }
-      run += c[i];
-    }
-  }
-  __syncthreads();
-  bin = kk > 0 ? scratch[4] : 0;
-  above = kk > 0 ? scratch[5] : 0;
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kMwThreads) void topk_mw_filter(const float* __restrict__ scores, int Nc, int k,
-                                                             uint32_t* __restrict__ ws) {
-  __shared__ uint32_t lh[kTkBins];
-  __shared__ int scratch[8];
-  const size_t row = blockIdx.y;
-  const MwRow R = mw_row(ws, k, row);
-  int bin, above, kk;
-  mw_threshold(R, k, lh, scratch, bin, above, kk);
-  if (kk == 0) return;
-  const float* sr = scores + row * Nc;
-  const int j0 = blockIdx.x * kMwSegment, j1 = min(Nc, j0 + kMwSegment);
-  for (int jb = j0; jb < j1; jb += kMwThreads) {
-    const int j = jb + threadIdx.x;
-    const uint32_t key = j < j1 ? score_key(sr[j]) : 0u;
-    const int d = static_cast<int>(key >> 21);
-    const bool is_gt = key != 0u && d > bin;
-    const bool is_c = key != 0u && d == bin;
-    const uint64_t gm = __ballot(is_gt), cm = __ballot(is_c);
-    int gbase = 0, cbase = 0;
-    if (lane_id() == 0) {
-      if (gm) gbase = atomicAdd(&R.counters[1], __popcll(gm));
-      if (cm) cbase = atomicAdd(&R.counters[2], __popcll(cm));
-    }
-    gbase = __shfl(gbase, 0, kWave);
-    cbase = __shfl(cbase, 0, kWave);
-    if (is_gt) R.gt[gbase + lanes_below(gm)] = j;               // < kk entries in total
-    if (is_c) {
-      const int p = cbase + lanes_below(cm);
-      if (p < kMwCap) { R.ckey[p] = key; R.cidx[p] = j; }
-    }
-  }
-}
-
-// Ascending bitonic sort of n (power of two, <= 2*blockDim... any n <= buffer) int32 values
-// in LDS; entries past `valid` must hold INT_MAX.
-__device__ void bitonic_sort_lds(int32_t* v, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const int32_t a = v[lo], b = v[hi];
-        if ((a > b) == up) { v[lo] = b; v[hi] = a; }
-      }
-    }
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kTkThreads) void topk_mw_final(const float* __restrict__ scores, int Nc, int k,
-                                                            uint32_t* __restrict__ ws, int32_t* __restrict__ idx) {
+template <int NU>
+__global__ __launch_bounds__(kTkThreads) void topk_segments(const float* __restrict__ scores, int Nc, int k,
+                                                            int seg, uint2* __restrict__ cand) {
   __shared__ TkShared sh;
-  __shared__ uint32_t ckey[kMwCap];
-  __shared__ int32_t cidx[kMwCap];
-  __shared__ int32_t selv[2 * kTkThreads];
-  __shared__ int nsel, neq;
   const size_t row = blockIdx.x;
-  const MwRow R = mw_row(ws, k, row);
-  int32_t* out = idx + row * k;
-  const int ncand = R.counters[0];
-  const int kk = min(k, ncand);
-  if (kk == 0) {
-    for (int p = threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
-    return;
-  }
-  const int nc = R.counters[2];
-  const float* sr = scores + row * Nc;
-  if (nc > kMwCap) {
-    // threshold bin too crowded for the candidate buffer: finish this row the slow way
-    auto key_at = [&](int j) -> uint32_t { return score_key(sr[j]); };
-    uint32_t T;
-    int need_eq;
-    radix_select(sh, key_at, Nc, kk, T, need_eq);
-    ordered_compaction(sh, key_at, Nc, k, kk, T, need_eq, out);
-    return;
-  }
-  const int ngt = R.counters[1];
-  for (int i = threadIdx.x; i < nc; i += kTkThreads) { ckey[i] = R.ckey[i]; cidx[i] = R.cidx[i]; }
-  __syncthreads();
-  // remaining digits (passes 2 and 3) over the candidates; their top digit is shared
-  const int remain1 = kk - ngt;
-  uint32_t T = ckey[0] & 0xffe00000u;   // placeholder when remain1 == 0 (no candidate taken)
-  int need_eq = 0;
-  if (remain1 > 0) {
-    uint32_t prefix = ckey[0] & 0xffe00000u, mask = 0xffe00000u;
-    int remain = remain1;
-    for (int pass = 1; pass < 3; ++pass) {
-      const int shift = digit_shift(pass), nbins = digit_bins(pass);
-      for (int i = threadIdx.x; i < nbins; i += kTkThreads) sh.hist[i] = 0;
-      __syncthreads();
-      for (int j = threadIdx.x; j < nc; j += kTkThreads) {
-        const uint32_t key = ckey[j];
-        if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nbins - 1)], 1u);
+  const int G = gridDim.y, g = blockIdx.y;
+  const int j0 = g * seg;
+  const int n = max(0, min(seg, Nc - j0));
+  const float* sr = scores + row * Nc + min(j0, Nc);
+  uint32_t key[NU][4];
+  load_score_keys<NU>(key, sr, n);
+  uint64_t taken;
+  int obase[NU];
+  const int kk = select_regs<NU>(sh, key, k, taken, obase);
+  uint2* out = cand + (row * G + g) * static_cast<size_t>(k);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int o = obase[u];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if ((taken >> (4 * u + s)) & 1ull) {      // the key is read again (cached) to keep registers low
+        const int p = kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s;
+        out[o++] = make_uint2(score_key(sr[p]), static_cast<uint32_t>(j0 + p));
       }
-      __syncthreads();
-      find_threshold_bin(sh, nbins, remain);
-      prefix |= static_cast<uint32_t>(sh.bin) << shift;
-      mask |= static_cast<uint32_t>(nbins - 1) << shift;
-      remain -= sh.above;
-      __syncthreads();
-    }
-    T = prefix;
-    need_eq = remain;
   }
-  // gather: every gt entry, candidates with key > T, and the need_eq lowest-index key == T
-  if (threadIdx.x == 0) { nsel = 0; neq = 0; }
-  __syncthreads();
-  for (int i = threadIdx.x; i < ngt; i += kTkThreads) selv[atomicAdd(&nsel, 1)] = R.gt[i];
-  for (int i = threadIdx.x; i < nc; i += kTkThreads) {
-    if (remain1 > 0 && ckey[i] > T) selv[atomicAdd(&nsel, 1)] = cidx[i];
-  }
-  __syncthreads();
-  // equal-key candidates, sorted by index, reuse the candidate key buffer as int storage
-  int32_t* eqv = reinterpret_cast<int32_t*>(ckey);
-  __shared__ int32_t eqtmp[kMwCap];
-  if (remain1 > 0) {
-    for (int i = threadIdx.x; i < nc; i += kTkThreads)
-      if (ckey[i] == T) eqtmp[atomicAdd(&neq, 1)] = cidx[i];
-    __syncthreads();
-    int n2 = 1;
-    while (n2 < neq) n2 <<= 1;
-    for (int i = threadIdx.x; i < n2; i += kTkThreads) eqv[i] = i < neq ? eqtmp[i] : 0x7fffffff;
-    bitonic_sort_lds(eqv, n2);
-    const int base = nsel;
-    for (int i = threadIdx.x; i < need_eq; i += kTkThreads) selv[base + i] = eqv[i];
-    __syncthreads();
-    if (threadIdx.x == 0) nsel = base + need_eq;
-  }
-  __syncthreads();
-  int n2 = 1;
-  while (n2 < kk) n2 <<= 1;
-  for (int i = nsel + threadIdx.x; i < n2; i += kTkThreads) selv[i] = 0x7fffffff;
-  bitonic_sort_lds(selv, n2);
-  for (int p = threadIdx.x; p < k; p += kTkThreads) out[p] = p < kk ? selv[p] : -1;
+  for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = make_uint2(0u, 0u);
 }
+
+// One workgroup per row over the n = G*k pairs of its segments (n <= NU * 4096).  Only
+// the keys are held in registers; the indices of the taken pairs are read again.
+template <int NU>
+__global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict__ cand, int n, int k,
+                                                         int32_t* __restrict__ idx) {
+  __shared__ TkShared sh;
+  const size_t row = blockIdx.x;
+  const uint2* c = cand + row * static_cast<size_t>(n);
+  const bool vec = (reinterpret_cast<uintptr_t>(c) & 15u) == 0;
+  uint32_t key[NU][4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int p = kTkChunk * u + 4 * static_cast<int>(threadIdx.x);
+    if (vec && p + 3 < n) {
+      const uint4 a = *reinterpret_cast<const uint4*>(c + p);
+      const uint4 b = *reinterpret_cast<const uint4*>(c + p + 2);
+      key[u][0] = a.x;
+      key[u][1] = a.z;
+      key[u][2] = b.x;
+      key[u][3] = b.z;
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) key[u][s] = p + s < n ? c[p + s].x : 0u;
+    }
+  }
+  uint64_t taken;
+  int obase[NU];
+  const int kk = select_regs<NU>(sh, key, k, taken, obase);
+  int32_t* out = idx + row * k;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    int o = obase[u];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if ((taken >> (4 * u + s)) & 1ull)
+        out[o++] = static_cast<int32_t>(c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s].y);
+  }
+  for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
+}
+
+// ---------------------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------------------
+// Register chunks per workgroup for a set of n keys: 1, 2, 4 or 9.
+static int chunks_for(int n) {
+  const int c = cdiv(std::max(n, 1), kTkChunk);
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : kTkMaxChunks;
+}
+
+// Segments per row: about sqrt(Nc / k), which balances the segment and merge work, with
+// every segment and the G*k merged pairs within one workgroup.  0 = no valid split.
+int topk_segments_per_row(int Nc, int k) {
+  const int g_max = kTkMaxSet / k;
+  const int g_min = cdiv(Nc, kTkMaxSet);
+  if (g_max < 2 || g_min > g_max) return 0;
+  int G = static_cast<int>(std::lround(std::sqrt(static_cast<double>(Nc) / k)));
+  G = std::max(G, cdiv(Nc, 4 * kTkChunk));     // segments of <= 16384 keys where possible
+  return std::min(g_max, std::max(std::max(G, g_min), 2));
+}
+
+static int topk_seg_len(int Nc, int G) { return 4 * cdiv(cdiv(Nc, G), 4); }
 
 size_t topk_workspace_bytes(int rows, int Nc, int k) {
-  (void)Nc;
-  return static_cast<size_t>(rows) * mw_row_words(k) * sizeof(uint32_t);
+  const int G = topk_segments_per_row(Nc, k);
+  return G < 2 ? 0 : static_cast<size_t>(rows) * G * k * sizeof(uint2);
 }
 
-// algo: 0 = automatic, 1 = one workgroup per row, 2 = several workgroups per row
+// Whether a shape can run: with a workspace (any split allowed) or without one (the
+// row must fit one workgroup).
+bool topk_supported(int Nc, int k, bool with_ws) {
+  if (Nc <= kTkMaxSet) return true;
+  return with_ws && topk_segments_per_row(Nc, k) >= 2;
+}
+
+template <int NU>
+static void launch_rows(const float* scores, int rows, int Nc, int k, int32_t* idx, hipStream_t st) {
+  hipLaunchKernelGGL(topk_rows<NU>, dim3(rows), dim3(kTkThreads), 0, st, scores, Nc, k, idx);
+}
+template <int NU>
+static void launch_segments(const float* scores, int rows, int G, int Nc, int k, int seg, uint2* cand,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(topk_segments<NU>, dim3(rows, G), dim3(kTkThreads), 0, st, scores, Nc, k, seg, cand);
+}
+template <int NU>
+static void launch_merge(const uint2* cand, int rows, int n, int k, int32_t* idx, hipStream_t st) {
+  hipLaunchKernelGGL(topk_merge<NU>, dim3(rows), dim3(kTkThreads), 0, st, cand, n, k, idx);
+}
+
+// algo: 0 = automatic, 1 = one workgroup per row, 2 = segments + merge.  The caller has
+// checked topk_supported() and the workspace size.
 int launch_topk(const float* scores, int rows, int Nc, int k, int32_t* idx, void* ws, size_t ws_bytes,
                 int algo, hipStream_t st) {
-  // several workgroups per row only when a row does not fit in LDS and rows are too few
-  // to fill the chip (the 1M-context decode shape)
-  if (algo == 0) algo = (rows < 64 && Nc > kTkLdsKeys) ? 2 : 1;
-  if (algo == 2 && (ws == nullptr || ws_bytes < topk_workspace_bytes(rows, Nc, k))) algo = 1;
+  const int G = topk_segments_per_row(Nc, k);
+  const bool seg_ok = G >= 2 && ws != nullptr && ws_bytes >= topk_workspace_bytes(rows, Nc, k);
+  const bool rows_ok = Nc <= kTkMaxSet;
+  if (algo == 0) algo = (seg_ok && (!rows_ok || rows < 128)) ? 2 : 1;
+  if (algo == 2 && !seg_ok) algo = 1;
+  if (algo == 1 && !rows_ok) algo = 2;
+  if (algo == 2 && !seg_ok) return CSA_ERR_WORKSPACE;
   if (algo == 1) {
-    if (Nc <= kTkLdsKeys) {
-      static bool attr_set = false;
-      if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_rows<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(uint32_t) * kTkLdsKeys);
-        attr_set = true;
-      }
-      hipLaunchKernelGGL(topk_rows<true>, dim3(rows), dim3(kTkThreads), sizeof(uint32_t) * Nc, st,
-                         scores, Nc, k, idx);
-    } else {
-      hipLaunchKernelGGL(topk_rows<false>, dim3(rows), dim3(kTkThreads), 0, st, scores, Nc, k, idx);
+    switch (chunks_for(Nc)) {
+      case 1: launch_rows<1>(scores, rows, Nc, k, idx, st); break;
+      case 2: launch_rows<2>(scores, rows, Nc, k, idx, st); break;
+      case 4: launch_rows<4>(scores, rows, Nc, k, idx, st); break;
+      default: launch_rows<kTkMaxChunks>(scores, rows, Nc, k, idx, st); break;
     }
     CSA_LAUNCH_CHECK();
     return CSA_OK;
   }
-  uint32_t* w = static_cast<uint32_t*>(ws);
-  const int segs = cdiv(Nc, kMwSegment);
-  hipLaunchKernelGGL(topk_mw_clear, dim3(cdiv(rows * (kTkBins + 4), 256)), dim3(256), 0, st, w, k, rows);
-  hipLaunchKernelGGL(topk_mw_hist, dim3(segs, rows), dim3(kMwThreads), 0, st, scores, Nc, k, w);
-  hipLaunchKernelGGL(topk_mw_filter, dim3(segs, rows), dim3(kMwThreads), 0, st, scores, Nc, k, w);
-  hipLaunchKernelGGL(topk_mw_final, dim3(rows), dim3(kTkThreads), 0, st, scores, Nc, k, w, idx);
+  const int seg = topk_seg_len(Nc, G);
+  uint2* cand = static_cast<uint2*>(ws);
+  switch (chunks_for(seg)) {
+    case 1: launch_segments<1>(scores, rows, G, Nc, k, seg, cand, st); break;
+    case 2: launch_segments<2>(scores, rows, G, Nc, k, seg, cand, st); break;
+    case 4: launch_segments<4>(scores, rows, G, Nc, k, seg, cand, st); break;
+    default: launch_segments<kTkMaxChunks>(scores, rows, G, Nc, k, seg, cand, st); break;
+  }
+  CSA_LAUNCH_CHECK();
+  const int n = G * k;
+  switch (chunks_for(n)) {
+    case 1: launch_merge<1>(cand, rows, n, k, idx, st); break;
+    case 2: launch_merge<2>(cand, rows, n, k, idx, st); break;
+    case 4: launch_merge<4>(cand, rows, n, k, idx, st); break;
+    default: launch_merge<kTkMaxChunks>(cand, rows, n, k, idx, st); break;
+  }
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

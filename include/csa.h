@@ -130,8 +130,10 @@ int csa_index_score(const void* q, const float* q_scale, const float* w,
  *   in ascending index order and padded with -1:  idx [rows, k] int32.
  *   1 <= k <= 2048.
  *   ws: NULL, or >= csa_topk_workspace_size(rows, Nc, k) bytes.  With ws, rows that
- *   are few and long are split over several workgroups; without it every row is
- *   handled by one workgroup.  The result is the same either way.
+ *   are few or long are split over several workgroups; without it every row is
+ *   handled by one workgroup, which holds at most 36864 scores (longer rows without
+ *   ws: CSA_ERR_WORKSPACE).  The result is the same either way.  Rows longer than
+ *   36864 * floor(36864 / k) entries: CSA_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------ */
 size_t csa_topk_workspace_size(int rows, int Nc, int k);
 

@@ -275,7 +275,9 @@ def score_rows(seed: int, rows: int, n: int, kind: str = "gauss", n_vis=None) ->
     """fp32 score rows with -inf beyond n_vis[r] (the invisible entries).
 
     kind: "gauss" (continuous), "ties" (few distinct values), "const" (all equal),
-    "mixed" (Gaussian with a block of exact duplicates of one value).
+    "mixed" (Gaussian with a block of exact duplicates of one value),
+    "narrow" (uniform in [1, 1.25): every score shares its sign, exponent and top two
+    mantissa bits).
     """
     rng = _streams(seed, 1)[0]
     if kind == "gauss":
@@ -290,6 +292,9 @@ def score_rows(seed: int, rows: int, n: int, kind: str = "gauss", n_vis=None) ->
         s[dup] = np.float32(1.25)
         s[rng.random((rows, n)) < 0.01] = -0.0
         s[rng.random((rows, n)) < 0.01] = 0.0
+    elif kind == "narrow":
+        s = (1.0 + 0.25 * rng.random((rows, n), dtype=np.float32)).astype(np.float32)
+        s = np.minimum(s, np.float32(np.nextafter(np.float32(1.25), np.float32(0))))
     else:
         raise ValueError(kind)
     if n_vis is not None:

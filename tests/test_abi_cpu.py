@@ -56,8 +56,11 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.csa_topk(fake, 1, 1, 10, 4096, fake, None, 0, None) == 1
     assert lib.csa_topk_algo(fake, 1, 1, 10, 4, fake, None, 0, 7, None) == 1
     assert lib.csa_topk_algo(fake, 1, 1, 10, 4, fake, None, 0, 2, None) == 3
-    # top-k: workspace given but too small
+    # top-k: workspace given but too small; a row longer than one workgroup holds, no workspace
     assert lib.csa_topk(fake, 4, 1, 100000, 512, fake, fake, 16, None) == 3
+    assert lib.csa_topk(fake, 4, 1, 36865, 512, fake, None, 0, None) == 3
+    # top-k: a row too long for one level of segments
+    assert lib.csa_topk(fake, 1, 1, 36864 * 18 + 1, 2048, fake, fake, 1 << 40, None) == 2
     # compressor: T not a multiple of m, p0 > 0 with overlap and no previous block, bf16 d % 64
     args = dict(hidden=fake, prev=None, dt=0, w=fake, bias=fake, ov=1, B=1, T=10, d=64, m=4, c=8, dr=4)
     call = lambda **kw: lib.csa_compress(kw["hidden"], kw["prev"], kw["dt"], kw["w"], kw["bias"], kw["ov"],

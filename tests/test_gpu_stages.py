@@ -108,6 +108,15 @@ TOPK_CASES = [
     (2, 40000, 1024, "gauss", 1),
     (2, 40000, 1024, "mixed", 2),
     (2, 70000, 1024, "const", 2),
+    (3, 32768, 512, "narrow", 1),
+    (3, 32768, 512, "narrow", 2),
+    (2, 70000, 2048, "gauss", 2),
+    (2, 262144, 1024, "gauss", 0),
+    (2, 262144, 1024, "narrow", 2),
+    (300, 2000, 512, "mixed", 0),
+    (64, 36864, 512, "gauss", 1),
+    (3, 16000, 100, "ties", 1),
+    (3, 9000, 2048, "narrow", 1),
 ]
 
 
