@@ -30,11 +30,12 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-# Per-file device code generation options.  The indexer keeps its MFMA accumulators in
-# ordinary VGPRs (its epilogue reads every result with VALU instructions, which would
-# otherwise need one accvgpr move per value); attention keeps the AGPR form for its
-# 128 output accumulators.
-PER_FILE = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file device code generation options.  The indexer and the attention keep their
+# MFMA accumulators in ordinary VGPRs: their epilogues (and the attention's rescale of
+# the output rows) read results with VALU instructions, which would otherwise need one
+# accvgpr move per value.
+PER_FILE = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> tuple[str, str]:

@@ -9,23 +9,32 @@
 // kernel gathers only the rows the indices name).  CSA: remote rows = kv_comp[idx];
 // HCA ("HCA：重压缩 + 全量"): remote rows = every visible entry.
 //
-// bf16 kernel (H = 64 heads, c = 512).  A workgroup (4 waves, 16 heads each) owns one
-// query and a contiguous range of row chunks, so every gathered KV row is read from HBM
-// once for all 64 heads.  Per chunk of kRows rows:
-//   1. the rows are staged in LDS, row stride 1072 B (rows shift by 12 banks: the 16
-//      rows of a 16-byte operand read and the 4 rows of a transposed read never share
-//      a bank);
-//   2. S^T = KV_chunk . Q^T on MFMA (A = rows from LDS, B = the wave's Q in registers);
-//      the output layout of S^T (lane: head l%16, rows 4*(l/16)+i) is exactly the
-//      A-operand layout P needs below, so P never leaves registers;
-//   3. online softmax in the log2 domain (running max and sum per head);
-//   4. O += P . V on MFMA with V read from the same LDS rows (K = V) through the LDS
-//      transpose read ds_read_b64_tr_b16: in each 16-lane group, output lane i' slot j'
-//      receives input lane 4j'+i'/4 slot i'%4, so lanes 4j'..4j'+3 reading 16 columns of
-//      row R(j') hand every lane its column of 4 rows.  P enters as a bf16 hi + lo pair
-//      (two MFMAs on one V operand) so it keeps ~16 bits.
-// Several workgroups may split one query's rows; they write (m, l, O) partials and
-// attn_merge combines them with the sink (LSE merge).
+// bf16 kernel (H = 64 heads, c = 512).  A workgroup owns one query, a group of 16 heads
+// and a contiguous range of 32-row chunks of its row set; its 4 waves split the 512
+// channels into quarters.  Per chunk:
+//   1. the 32 rows sit in one of two LDS slots; each wave loads 8 of them (16 bytes per
+//      lane per row) into one of two register sets two chunks ahead and writes a set to
+//      its slot after the chunk before it is done, so two chunks are in flight while one
+//      is computed.  (Direct global->LDS loads measured at about half the gather rate
+//      of register loads here.)  Row stride 1072 B (rows shift by 12 banks: 16 rows of a
+//      16-byte operand read and the 4 rows of a transposed read never share a bank);
+//   2. every wave computes its quarter's share of S^T = KV_chunk . Q^T on MFMA (A = rows
+//      from LDS, B = its Q quarter in registers); the 4 shares are summed through LDS
+//      (fixed order, so all waves hold the identical S^T);
+//   3. online softmax in the log2 domain with a lazy reference: the running maximum is
+//      only moved (and O rescaled) when a chunk exceeds it by more than 2^8, which leaves
+//      the result unchanged (numerator and denominator share the reference);
+//   4. O_quarter += P . V on MFMA with V read from the same LDS rows (K = V) through
+//      ds_read_b64_tr_b16: in each 16-lane group, output lane i' slot j' receives input
+//      lane 4j'+i'/4 slot i'%4, so lanes 4j'..4j'+3 reading 16 columns of row R(j') hand
+//      every lane its column of 4 rows.  The S^T output layout (lane: head l%16, rows
+//      4*(l/16)+i and 16+4*(l/16)+i) is the A-operand layout of P under the matching
+//      k-slot order, so P never leaves registers.  P enters as a bf16 hi + lo pair (two
+//      MFMAs on one V operand) so it keeps ~16 bits.
+// A row set split over several workgroups writes (m, l, O) partials that attn_merge
+// combines with the sink (LSE merge).  Workgroups are numbered so that all workgroups
+// of one query land on the same XCD (consecutive workgroup ids go round-robin over the
+// 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
 
 #include "common.hpp"
@@ -34,11 +43,31 @@ namespace csa {
 
 constexpr int kAH = 64;
 constexpr int kAC = 512;
-constexpr int kRows = 32;
-constexpr int kMaxSplitSlots = 4096;              // selected entries staged per workgroup
-constexpr int kRowStride = kAC * 2 + 48;          // bytes
+constexpr int kHG = 16;                             // heads per workgroup
+constexpr int kNHG = kAH / kHG;
+constexpr int kQuarter = kAC / 4;                   // channels per wave
+constexpr int kRows = 32;                           // rows per chunk
+constexpr int kRing = 2;                            // chunks resident in LDS
+constexpr int kRowStride = kAC * 2 + 48;            // bytes
+constexpr int kChunkBytes = kRows * kRowStride;
+constexpr int kMaxSplitChunks = 72;                 // chunks of row addresses tabled per workgroup
+constexpr int kAttnLdsFixed = kRing * kChunkBytes + 4 * kWave * 8 * 4 + kRing * 4 * 4;
+constexpr int kAttnLdsMax = kAttnLdsFixed + kMaxSplitChunks * kRows * 8;
+constexpr float kLazy = 8.0f;                       // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Source of the rows that are absent (index -1, padding): every chunk is the same eight
+// loads per wave, so the compiler's count of loads in flight is the same on every path.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kAC];
+
+
+// Workgroup barrier without a memory fence: the row loads still in flight (later chunks)
+// are not waited for; LDS writes of this wave are waited for explicitly.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);               // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -48,12 +77,12 @@ struct AttnArgs {
   const uint16_t* swa;
   const float* sink;
   float scale_log2;          // scale * log2(e)
-  int S, Nc, k, Ls, W, m;
+  int nq, S, Nc, k, Ls, W, m;
   int nsplit, chunks_per_split;
   uint16_t* out;
   float* lse;
   float* part_o;             // [B*S, nsplit, H, c] fp32, unnormalised
-  float* part_ml;            // [B*S, nsplit, H, 2]: running max (log2 units), sum
+  float* part_ml;            // [B*S, nsplit, H, 2]: reference max (log2 units), sum
 };
 
 // Window rows of query s: [w_lo, w_hi] of the sequence's swa tensor.
@@ -64,14 +93,22 @@ __device__ __forceinline__ void window_rows(int s, int S, int Ls, int W, int& w_
 }
 
 template <bool kDense>
-__global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t rows_lds[kRows * kRowStride];
-  __shared__ int valid_lds[kRows];
-  __shared__ int sel_lds[kMaxSplitSlots];
-  const int qi = blockIdx.y;
-  const int split = blockIdx.x;
+__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ring = smem;
+  float* sx = reinterpret_cast<float*>(smem + kRing * kChunkBytes);        // [wave][lane][8]
+  int* validw = reinterpret_cast<int*>(sx + 4 * kWave * 8);                // [ring slot][wave]: 8-row masks
+  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kRing * 4);     // this split's row addresses
+
+  // ---- workgroup -> (query, head group, split); one query's workgroups share an XCD
+  const int units = kNHG * a.nsplit;
+  const int xcd = blockIdx.x & 7, t8 = blockIdx.x >> 3;
+  const int u = t8 % units;
+  const int qi = (t8 / units) * 8 + xcd;
+  if (qi >= a.nq) return;
+  const int hg = u % kNHG, split = u / kNHG;
   const int b = qi / a.S, s = qi % a.S;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int l = static_cast<int>(lane_id());
   const int g = l >> 4;
 
@@ -85,172 +122,248 @@ __global__ __launch_bounds__(256) void attn_bf16(AttnArgs a) {
 
   const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
-  // CSA: this split's selected entries, staged once in LDS so the row loads of a chunk
-  // can be issued back to back (no index load between them)
-  const int slot0 = ch0 * kRows;
-  if (!kDense) {
-    const int32_t* idxq = a.idx + static_cast<size_t>(qi) * a.k;
-    const int r0 = max(0, slot0 - n_swa);
-    const int r1 = min(a.k, ch1 * kRows - n_swa);
-    for (int r = r0 + static_cast<int>(threadIdx.x); r < r1; r += 256) sel_lds[r - r0] = idxq[r];
+  const int32_t* idxq = kDense ? nullptr : a.idx + static_cast<size_t>(qi) * a.k;
+
+  // Q quarter of the 16 heads as the B operand: lane l holds head 16*hg + l%16,
+  // channels 128*wave + 32*ks + 8*g .. +7
+  v8s qb[kQuarter / 32];
+  {
+    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + kQuarter * wave;
+#pragma unroll
+    for (int ks = 0; ks < kQuarter / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
+  }
+  // Q complete before any row load: otherwise the compiler's wait for Q inside the loop
+  // (on a path where no row load follows) becomes a wait for all rows in flight
+  __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
+
+  // The address of every row of the split (window row, selected or visible entry, or
+  // the zero row for absent ones), computed once by all threads.
+  {
+    const int nsl = (ch1 - ch0) * kRows;
+    for (int e = static_cast<int>(threadIdx.x); e < nsl; e += 256) {
+      const int slot = ch0 * kRows + e;
+      const uint16_t* p = g_zero_row;
+      if (slot < n_swa) {
+        p = swab + static_cast<size_t>(w_lo + slot) * kAC;
+      } else if (slot < n_slots) {
+        const int j = kDense ? slot - n_swa : idxq[slot - n_swa];
+        if (j >= 0 && j < a.Nc) p = kvb + static_cast<size_t>(j) * kAC;
+      }
+      rowptr[e] = reinterpret_cast<uint64_t>(p);
+    }
     __syncthreads();
   }
-  // slot -> row pointer, nullptr for padding / an absent (-1) index
-  auto slot_row = [&](int slot) -> const uint16_t* {
-    if (slot >= n_slots) return nullptr;
-    if (slot < n_swa) return swab + static_cast<size_t>(w_lo + slot) * kAC;
-    const int r = slot - n_swa;
-    const int j = kDense ? r : sel_lds[r - max(0, slot0 - n_swa)];
-    if (j < 0 || j >= a.Nc) return nullptr;
-    return kvb + static_cast<size_t>(j) * kAC;
-  };
+  const uint64_t zero_row = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g_zero_row));
 
-  // staging: round r moves chunk row 4*r + wave, 16 bytes per lane
-  uint4 stage[kRows / 4];
-  int stage_ok[kRows / 4];
-  auto gload = [&](int ch) {
-#pragma unroll
-    for (int r = 0; r < kRows / 4; ++r) {
-      const uint16_t* p = slot_row(ch * kRows + 4 * r + wave);
-      stage_ok[r] = p != nullptr;
-      stage[r] = p ? reinterpret_cast<const uint4*>(p)[l] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto swrite = [&]() {
-#pragma unroll
-    for (int r = 0; r < kRows / 4; ++r) {
-      const int row = 4 * r + wave;
-      *reinterpret_cast<uint4*>(&rows_lds[row * kRowStride + 16 * l]) = stage[r];
-      if (l == 0) valid_lds[row] = stage_ok[r];
-    }
-  };
+  // The wave's 8 rows of chunk CH (the zero row for chunks past the split): addresses from
+  // the table with four 16-byte LDS reads, then one 16-byte load per lane per row.
+#define CSA_ATT_LOAD1(ST, VM, R, PTR)                                                   \
+  do {                                                                                 \
+    const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
+                        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(PTR)));   \
+    (VM) |= (p_ != zero_row ? 1u : 0u) << (R);                                         \
+    ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_)[l];     \
+  } while (0)
+#define CSA_ATT_LOAD(CH, ST, VM)                                                        \
+  do {                                                                                 \
+    uint64_t q_[8];                                                                    \
+    if ((CH) < ch1) {                                                                  \
+      const uint64_t* t_ = rowptr + ((CH) - ch0) * kRows + 8 * wave;                   \
+      const ulonglong2 a_ = reinterpret_cast<const ulonglong2*>(t_)[0];                 \
+      const ulonglong2 b_ = reinterpret_cast<const ulonglong2*>(t_)[1];                 \
+      const ulonglong2 c_ = reinterpret_cast<const ulonglong2*>(t_)[2];                 \
+      const ulonglong2 d_ = reinterpret_cast<const ulonglong2*>(t_)[3];                 \
+      q_[0] = a_.x; q_[1] = a_.y; q_[2] = b_.x; q_[3] = b_.y;                          \
+      q_[4] = c_.x; q_[5] = c_.y; q_[6] = d_.x; q_[7] = d_.y;                          \
+    } else {                                                                           \
+      q_[0] = q_[1] = q_[2] = q_[3] = q_[4] = q_[5] = q_[6] = q_[7] = zero_row;        \
+    }                                                                                  \
+    (VM) = 0;                                                                          \
+    CSA_ATT_LOAD1(ST, VM, 0, q_[0]); CSA_ATT_LOAD1(ST, VM, 1, q_[1]);                  \
+    CSA_ATT_LOAD1(ST, VM, 2, q_[2]); CSA_ATT_LOAD1(ST, VM, 3, q_[3]);                  \
+    CSA_ATT_LOAD1(ST, VM, 4, q_[4]); CSA_ATT_LOAD1(ST, VM, 5, q_[5]);                  \
+    CSA_ATT_LOAD1(ST, VM, 6, q_[6]); CSA_ATT_LOAD1(ST, VM, 7, q_[7]);                  \
+  } while (0)
+#define CSA_ATT_STORE1(BUF, ST, R) \
+  *reinterpret_cast<v4u*>((BUF) + (8 * wave + (R)) * kRowStride + 16 * l) = ST##R
+#define CSA_ATT_STORE(CH, ST, VM)                                                       \
+  do {                                                                                 \
+    uint8_t* buf_ = ring + ((CH) & 1) * kChunkBytes;                                   \
+    CSA_ATT_STORE1(buf_, ST, 0); CSA_ATT_STORE1(buf_, ST, 1);                          \
+    CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                          \
+    CSA_ATT_STORE1(buf_, ST, 4); CSA_ATT_STORE1(buf_, ST, 5);                          \
+    CSA_ATT_STORE1(buf_, ST, 6); CSA_ATT_STORE1(buf_, ST, 7);                          \
+    if (l == 0) validw[((CH) & 1) * 4 + wave] = static_cast<int>(VM);                   \
+  } while (0)
 
-  // Q of this wave's 16 heads as the B operand of S^T = KV . Q^T: lane l holds head
-  // 16*wave + l%16, channels 32*ks + 8*g .. +7
-  v8s qb[kAC / 32];
-  {
-    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + 16 * wave + (l & 15)) * kAC;
+  v4f o[kQuarter / 16];
 #pragma unroll
-    for (int ks = 0; ks < kAC / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
-  }
-
-  v4f o[kAC / 16];
-#pragma unroll
-  for (int t = 0; t < kAC / 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // per head l%16 (log2 units)
+  for (int t = 0; t < kQuarter / 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;   // per head l%16 (log2 units)
   float l_run = 0.0f;        // this lane's share of the per-head sum
+  float* sxw = sx + (wave * kWave + l) * 8;
 
-  if (ch0 < ch1) {
-    gload(ch0);
-    swrite();
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int ch = ch0; ch < ch1; ++ch) {
-    const bool more = ch + 1 < ch1;
-    if (more) gload(ch + 1);
-
-    // ---- S^T for 32 rows x 16 heads
+  // one chunk: S^T share, exchange, softmax, P.V (the chunk is in LDS slot ch & 1)
+  auto compute = [&](int ch) __attribute__((always_inline)) {
+    const uint8_t* buf = ring + (ch & 1) * kChunkBytes;
+    // ---- this wave's share of S^T (32 rows x 16 heads) over its channel quarter
     v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < kAC / 32; ++ks) {
+    for (int ks = 0; ks < kQuarter / 32; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const v8s av = *reinterpret_cast<const v8s*>(&rows_lds[(16 * rb + (l & 15)) * kRowStride + 64 * ks + 16 * g]);
+        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 2 * kQuarter * wave +
+                                                     64 * ks + 16 * g);
         st[rb] = mfma_bf16_16x16x32(av, qb[ks], st[rb]);
       }
     }
-    // ---- online softmax; slot j <-> chunk row rho(j) = 16*(j/4) + 4*g + j%4
+    *reinterpret_cast<v4f*>(sxw) = st[0];
+    *reinterpret_cast<v4f*>(sxw + 4) = st[1];
+    barrier_lds();
     float sv[8];
-    float cmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {                     // fixed order: identical sums in every wave
+      const float* src = sx + (w * kWave + l) * 8;
+      const v4f x0 = *reinterpret_cast<const v4f*>(src);
+      const v4f x1 = *reinterpret_cast<const v4f*>(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] += x0[i];
+        sv[4 + i] += x1[i];
+      }
+    }
+    // ---- online softmax; slot j <-> chunk row 16*(j/4) + 4*g + j%4
+    uint32_t vmask;
+    {
+      const int4 vw = *reinterpret_cast<const int4*>(validw + (ch & 1) * 4);
+      vmask = static_cast<uint32_t>(vw.x) | (static_cast<uint32_t>(vw.y) << 8) | (static_cast<uint32_t>(vw.z) << 16) |
+              (static_cast<uint32_t>(vw.w) << 24);
+    }
+    float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 16 * (j >> 2) + 4 * g + (j & 3);
-      sv[j] = valid_lds[row] ? st[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
-      cmax = fmaxf(cmax, sv[j]);
+      sv[j] = (vmask >> row) & 1u ? sv[j] * a.scale_log2 : -INFINITY;
+      lmax = fmaxf(lmax, sv[j]);
     }
-    cmax = fmaxf(cmax, wave_xor(cmax, 16));
-    cmax = fmaxf(cmax, wave_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);          // 0 when m_run = -inf
-    // P = P_hi + P_lo, both bf16: the two products with V keep P to ~16 bits, so the
-    // weights carry no bf16 rounding into the output (only its final rounding remains)
-    float psum = 0.0f;
-    v8s pa, pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = exp2f(sv[j] - m_use);
-      psum += p;
-      const uint16_t hi = f32_to_bf16(p);
-      pa[j] = static_cast<short>(hi);
-      pb[j] = static_cast<short>(f32_to_bf16(p - bf16_to_f32(hi)));
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // rescale O rows (heads 4*g+i) when any head's max moved
-    if (__ballot(alpha != 1.0f)) {
+    // the reference moves only when some logit exceeds it by more than kLazy; then the
+    // per-head maximum over the 4 lane groups is taken
+    if (__ballot(lmax > m_ref + kLazy)) {
+      float cmax = fmaxf(lmax, wave_xor(lmax, 16));
+      cmax = fmaxf(cmax, wave_xor(cmax, 32));
+      const bool move = cmax > m_ref + kLazy;
+      const float m_new = move ? cmax : m_ref;
+      const float alpha = move ? exp2f(m_ref - m_new) : 1.0f;      // 0 when m_ref = -inf
+      l_run *= alpha;
+      m_ref = m_new;
       float ah[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ah[i] = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
-      for (int t = 0; t < kAC / 16; ++t)
+      for (int t = 0; t < kQuarter / 16; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i] *= ah[i];
     }
-    // ---- O += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
-    const uint8_t* vt = rows_lds + (4 * g + ((l & 15) >> 2)) * kRowStride + 8 * (l & 3);
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+    // P = P_hi + P_lo, both bf16: the two products with V keep P to ~16 bits
+    float psum = 0.0f;
+    v8s pa, pb;
 #pragma unroll
-    for (int t = 0; t < kAC / 16; ++t) {
+    for (int j = 0; j < 8; j += 2) {
+      typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      // v_exp_f32: results below 2^-126 flush to 0, far below the >= 1 of the chunk's top weight
+      const v2f p = {__builtin_amdgcn_exp2f(sv[j] - m_use), __builtin_amdgcn_exp2f(sv[j + 1] - m_use)};
+      psum += p[0] + p[1];
+      const v2bf hi = __builtin_convertvector(p, v2bf);
+      const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+      const v2f r = {p[0] - __uint_as_float(hb << 16), p[1] - __uint_as_float(hb & 0xffff0000u)};
+      const uint32_t lb = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, v2bf));
+      pa[j] = static_cast<short>(hb & 0xffffu);
+      pa[j + 1] = static_cast<short>(hb >> 16);
+      pb[j] = static_cast<short>(lb & 0xffffu);
+      pb[j + 1] = static_cast<short>(lb >> 16);
+    }
+    l_run += psum;
+    // ---- O_quarter += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
+    const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * kQuarter * wave + 8 * (l & 3);
+#pragma unroll
+    for (int t = 0; t < kQuarter / 16; ++t) {
       const v4s v0 = lds_read_tr16(vt + 32 * t);
       const v4s v1 = lds_read_tr16(vt + 32 * t + 16 * kRowStride);
       const v8s vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       o[t] = mfma_bf16_16x16x32(pa, vb, o[t]);
       o[t] = mfma_bf16_16x16x32(pb, vb, o[t]);
     }
-    __syncthreads();
-    if (more) swrite();
-    __syncthreads();
+  };
+
+  v4u stA0, stA1, stA2, stA3, stA4, stA5, stA6, stA7;
+  v4u stB0, stB1, stB2, stB3, stB4, stB5, stB6, stB7;
+  uint32_t vA = 0, vB = 0;
+  // Every chunk step issues its eight loads, also past the split's end (zero row), so the
+  // count of loads in flight is the same on every path and the compiler's waits before
+  // each store only cover the set being stored.
+  CSA_ATT_LOAD(ch0, stA, vA);
+  CSA_ATT_LOAD(ch0 + 1, stB, vB);
+  if (ch0 < ch1) CSA_ATT_STORE(ch0, stA, vA);
+  CSA_ATT_LOAD(ch0 + 2, stA, vA);
+#pragma unroll 1
+  for (int ch = ch0; ch < ch1; ch += 2) {
+    barrier_lds();                                  // chunk ch in slot ch&1; slot of ch-1 free
+    compute(ch);
+    if (ch + 1 < ch1) CSA_ATT_STORE(ch + 1, stB, vB);
+    CSA_ATT_LOAD(ch + 3, stB, vB);
+    if (ch + 1 >= ch1) break;
+    barrier_lds();
+    compute(ch + 1);
+    if (ch + 2 < ch1) CSA_ATT_STORE(ch + 2, stA, vA);
+    CSA_ATT_LOAD(ch + 4, stA, vA);
   }
+#undef CSA_ATT_LOAD1
+#undef CSA_ATT_LOAD
+#undef CSA_ATT_STORE1
+#undef CSA_ATT_STORE
 
   // ---- finish: per-head totals
   float l_tot = l_run + wave_xor(l_run, 16);
   l_tot += wave_xor(l_tot, 32);
-  const int head_l = 16 * wave + (l & 15);            // head whose statistics this lane holds
+  const int head_l = kHG * hg + (l & 15);             // head whose statistics this lane holds
+  const int col0 = kQuarter * wave + (l & 15);
   if (a.nsplit == 1) {
     const float sink2 = a.sink[head_l] * kLog2e;
-    const float M = fmaxf(m_run, sink2);
+    const float M = fmaxf(m_ref, sink2);
     float f, lse2;
     if (M == -INFINITY) {
       f = 0.0f;
       lse2 = -INFINITY;
     } else {
-      const float em = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+      const float em = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - M);
       const float den = l_tot * em + exp2f(sink2 - M);
       f = den > 0.0f ? em / den : 0.0f;
       lse2 = M + log2f(den);
     }
-    if (a.lse && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
+    if (a.lse && wave == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
     float fh[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
-    uint16_t* ob = a.out + static_cast<size_t>(qi) * kAH * kAC;
+    uint16_t* ob = a.out + (static_cast<size_t>(qi) * kAH + kHG * hg) * kAC;
 #pragma unroll
-    for (int t = 0; t < kAC / 16; ++t)
+    for (int t = 0; t < kQuarter / 16; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ob[(16 * wave + 4 * g + i) * kAC + 16 * t + (l & 15)] = f32_to_bf16(o[t][i] * fh[i]);
+      for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(o[t][i] * fh[i]);
   } else {
     const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
-    if (g == 0) {
-      a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_run;
+    if (wave == 0 && g == 0) {
+      a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_ref;
       a.part_ml[(pbase * kAH + head_l) * 2 + 1] = l_tot;
     }
-    float* po = a.part_o + pbase * kAH * kAC;
+    float* po = a.part_o + (pbase * kAH + kHG * hg) * kAC;
 #pragma unroll
-    for (int t = 0; t < kAC / 16; ++t)
+    for (int t = 0; t < kQuarter / 16; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[(16 * wave + 4 * g + i) * kAC + 16 * t + (l & 15)] = o[t][i];
+      for (int i = 0; i < 4; ++i) po[(4 * g + i) * kAC + col0 + 16 * t] = o[t][i];
   }
 }
 
@@ -267,6 +380,54 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
   const size_t qi = qh / H;
   const int h = qh % H;
   const float sink2 = sink[h] * kLog2e;
+  if (c == kAC && nsplit <= 8) {
+    // every load of the (query, head) in flight at once: lane l owns channels 8l .. 8l+7,
+    // lane i < nsplit holds split i's (m, l)
+    float4 x[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nsplit) {
+        const float4* src = reinterpret_cast<const float4*>(part_o + ((qi * nsplit + i) * H + h) * kAC + 8 * lane);
+        x[i][0] = src[0];
+        x[i][1] = src[1];
+      }
+    }
+    const float mi = lane < nsplit ? part_ml[((qi * nsplit + lane) * H + h) * 2] : -INFINITY;
+    const float li = lane < nsplit ? part_ml[((qi * nsplit + lane) * H + h) * 2 + 1] : 0.0f;
+    float M = sink2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nsplit) M = fmaxf(M, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mi), i)));
+    const float wl = (M == -INFINITY || mi == -INFINITY) ? 0.0f : exp2f(mi - M);
+    float den = M == -INFINITY ? 0.0f : exp2f(sink2 - M);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nsplit) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
+        den += w * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, li), i));
+        acc[0] = fmaf(w, x[i][0].x, acc[0]); acc[1] = fmaf(w, x[i][0].y, acc[1]);
+        acc[2] = fmaf(w, x[i][0].z, acc[2]); acc[3] = fmaf(w, x[i][0].w, acc[3]);
+        acc[4] = fmaf(w, x[i][1].x, acc[4]); acc[5] = fmaf(w, x[i][1].y, acc[5]);
+        acc[6] = fmaf(w, x[i][1].z, acc[6]); acc[7] = fmaf(w, x[i][1].w, acc[7]);
+      }
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    OutT* dst = out + (qi * H + h) * kAC + 8 * lane;
+    if constexpr (sizeof(OutT) == 2) {
+      uint32_t pk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[j] = static_cast<uint32_t>(f32_to_bf16(acc[2 * j] * inv)) |
+                (static_cast<uint32_t>(f32_to_bf16(acc[2 * j + 1] * inv)) << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = acc[j] * inv;
+    }
+    if (lse && lane == 0) lse[qi * H + h] = (M == -INFINITY || den <= 0.0f) ? -INFINITY : (M + log2f(den)) * kLn2;
+    return;
+  }
   float M = sink2;
   for (int i = 0; i < nsplit; ++i) M = fmaxf(M, part_ml[((qi * nsplit + i) * H + h) * 2]);
   float den = M == -INFINITY ? 0.0f : exp2f(sink2 - M);
@@ -382,13 +543,14 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
 }
 
-// Splits of one query's rows over workgroups (bf16 kernel).  Enough workgroups to cover
-// the 256 compute units, but every split keeps >= 128 rows: a split's partial result
-// (64 x 512 fp32 = 128 KiB) must stay small next to the rows it reads (1 KiB each).
+// Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (4 head
+// groups x splits per query) to give every compute unit two, but every split keeps >= 4
+// chunks (128 rows): a split's partial result (16 heads x 512 fp32 = 32 KiB) must stay
+// small next to the rows it reads (1 KiB each).
 int attn_nsplit(int nq, int max_rows) {
-  const int by_fill = cdiv(256, nq);
-  const int by_rows = max_rows / 128;
-  const int by_lds = cdiv(max_rows, kMaxSplitSlots);  // a split's selection fits its LDS table
+  const int by_fill = cdiv(512, kNHG * nq);
+  const int by_rows = cdiv(max_rows, kRows) / 4;
+  const int by_lds = cdiv(cdiv(max_rows, kRows), kMaxSplitChunks);   // a split's row table fits LDS
   return std::max(by_lds, std::max(1, std::min(by_fill, by_rows)));
 }
 
@@ -416,17 +578,26 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     a.swa = static_cast<const uint16_t*>(swa);
     a.sink = sink;
     a.scale_log2 = scale_log2;
-    a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
+    a.nq = nq; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
     a.nsplit = ns;
-    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);   // <= kMaxSplitSlots / kRows by attn_nsplit
+    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     float* wsf = static_cast<float*>(ws);
     a.part_o = wsf;
     a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * H * c : nullptr;
-    dim3 grid(ns, nq);
-    if (dense) hipLaunchKernelGGL(attn_bf16<true>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(256), 0, st, a);
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
+      attr = true;
+    }
+    const dim3 grid(cdiv(nq, 8) * 8 * kNHG * ns);
+    const int lds = kAttnLdsFixed + a.chunks_per_split * kRows * 8;
+    if (dense) hipLaunchKernelGGL(attn_bf16<true>, grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(256), lds, st, a);
     CSA_LAUNCH_CHECK();
     if (ns > 1) {
       hipLaunchKernelGGL(attn_merge<uint16_t>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, a.part_o, a.part_ml, sink,

@@ -16,6 +16,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));        // 8 bf16 bit patterns
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));        // 4 bf16 bit patterns
+typedef unsigned v4u __attribute__((ext_vector_type(4)));     // 16 raw bytes
 
 // D(16x16, fp32) += A(16x128 e4m3) * B(128x16 e4m3).  Lane l holds row/column l%16 of
 // A/B and one 32-byte group (l/16) of the reduction index in both operands, so the
