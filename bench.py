@@ -42,6 +42,11 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) made "
+                        "with --calibrate-copy into the committed traffic summary")
     return p.parse_args()
 
 
@@ -61,11 +66,69 @@ def decode_step_bytes(sh):
     return keys + gathered + q_and_o + small
 
 
+COPY_BYTES = 256 << 20
+
+
+def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """Writes profiles/index_score_fp8_decode_flash_decode_b32_traffic.txt from the counter
+    CSVs: each counter of the indexer is scaled by what the same counter reads for the
+    plain device copy of COPY_BYTES (read and written once)."""
+    import csv
+    import glob
+    import hashlib
+
+    def per_kernel(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def pick(vals, key):
+        rows = [v for k, v in vals.items() if key in k]
+        if not rows:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        return rows[0]
+
+    fv, wv = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy_f = max(pick(fv, "copyBuffer"))            # KiB, the one large copy
+    copy_w = max(pick(wv, "copyBuffer"))
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    idx_f = pick(fv, "index_score_fp8_decode")
+    idx_w = pick(wv, "index_score_fp8_decode")
+    fetch = sum(idx_f) / len(idx_f) * 1024.0 * f_scale
+    write = sum(idx_w) / len(idx_w) * 1024.0 * w_scale
+    src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", "index_score.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    out = os.path.join(ROOT, "profiles", "index_score_fp8_decode_flash_decode_b32_traffic.txt")
+    with open(out, "w") as fo:
+        fo.write("# HBM traffic of index_score_fp8_decode, V4-Flash decode (B=32, 32768 entries), from\n")
+        fo.write("# rocprofv3 counters; each counter scaled by its reading for a plain 256 MiB device copy.\n")
+        fo.write(f"# fetch run: {cmd_fetch}\n# write run: {cmd_write}\n")
+        fo.write(f"copy_fetch_kib = {copy_f:.1f}\ncopy_write_kib = {copy_w:.1f}\n")
+        fo.write(f"fetch_scale = {f_scale:.4f}\nwrite_scale = {w_scale:.4f}\n")
+        fo.write(f"index_fetch_kib_per_dispatch = {sum(idx_f) / len(idx_f):.1f}  (n={len(idx_f)})\n")
+        fo.write(f"index_write_kib_per_dispatch = {sum(idx_w) / len(idx_w):.1f}  (n={len(idx_w)})\n")
+        fo.write(f"traffic_fetch_bytes = {fetch:.0f}\ntraffic_write_bytes = {write:.0f}\n")
+        fo.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
+        fo.write(f"algorithmic_bytes_per_launch = {index_score_bytes(32, 1, 32768, 64, 128)}\n")
+        fo.write(f"source_sha256 = {sha}\n")
+    print(open(out).read())
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        base = "rocprofv3 --pmc {} --output-format csv -d <dir> -o run -- python3 bench.py --steps 5 --warmup 2 " \
+               "--no-prefill --no-cpu-baseline --calibrate-copy"
+        summarize_counters(*args.summarize_counters, base.format("FETCH_SIZE"), base.format("WRITE_SIZE"))
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; the multi-GPU sharding is described "
-                                   "in DESIGN.md and not launched", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the CSA hot path here runs on one GPU; sharding over several GPUs "
+                                   "is not launched", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     from compressed_sparse_kv_amd import binding as L
@@ -119,6 +182,12 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.calibrate_copy:
+        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     # timed region: exactly K steps between two synchronisations
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -138,8 +207,22 @@ def main():
     dur = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
     us = dur.mean(axis=0) * 1e3
 
+    # dominant kernel alone: back-to-back launches (rotating input sets) between two
+    # events on its stream, so the average matches a kernel trace of the same run
+    n_rl = max(args.steps, 20)
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    for i in range(n_rl):
+        s = sets[i % len(sets)]
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    is_us = r0.elapsed_time(r1) / n_rl * 1e3
+
     isb = index_score_bytes(B, 1, Nc, sh.H_I, sh.d_I)
-    achieved = isb / (us[0] * 1e-6) / 1e9
+    achieved = isb / (is_us * 1e-6) / 1e9
     step_bytes = decode_step_bytes(sh)
     result = {
         "metric": METRIC,
@@ -162,7 +245,8 @@ def main():
         "kernels_us": {"csa_index_score": us[0], "csa_topk": us[1], "csa_sparse_attn": us[2]},
         "roofline": {"kernel": "index_score_fp8_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "bytes_per_launch": isb, "traffic": None},
+                     "bytes_per_launch": isb, "avg_launch_us": is_us,
+                     "traffic": measured_traffic("index_score.hip", "index_score_fp8_decode")},
         "input_generation_s": t_gen,
     }
 
@@ -173,6 +257,26 @@ def main():
         result["cpu_baseline"] = cpu_baseline(host_sets, sh)
 
     print(json.dumps(result))
+
+
+def measured_traffic(source, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    kernel's source has changed since the counters were taken (the summary records the
+    sha256 of the source file it measured)."""
+    import hashlib
+    summary = os.path.join(ROOT, "profiles", f"{kernel}_flash_decode_b32_traffic.txt")
+    src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", source)
+    if not (os.path.exists(summary) and os.path.exists(src)):
+        return None
+    fields = {}
+    for line in open(summary):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def bench_prefill_indexer(torch, L, I, dev, reps=10):

@@ -27,7 +27,7 @@
  *     buffer must be ordered by the caller.
  *   - Return value: CSA_OK when the work was enqueued.  Argument errors are
  *     detected before anything is launched (CSA_ERR_INVALID_ARG for bad values,
- *     CSA_ERR_UNSUPPORTED for a valid shape this build has no kernel for,
+ *     CSA_ERR_UNSUPPORTED for a valid shape the library has no kernel for,
  *     CSA_ERR_WORKSPACE when ws_bytes is too small); CSA_ERR_HIP reports a
  *     launch failure from the HIP runtime.  Errors that happen while kernels run
  *     surface at the caller's next synchronisation, as for any HIP kernel.
