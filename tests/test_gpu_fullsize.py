@@ -1,0 +1,158 @@
+"""Parity at the full workload sizes, in the launch configuration the bench times.
+
+Every stage runs on the whole batch through the C ABI exactly as in a decode / prefill
+step; the oracle then checks sampled outputs (queries, entries) one by one, and the
+integer stage (top-k) is checked on every row against the oracle's selection over the
+GPU's own scores (bit-exact), besides the tie-tolerant check against oracle scores."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from synthetic import inputs as I
+from tests.parity import (TOL_F32, assert_bf16_output, assert_bf16_within_one_step, assert_close, assert_fp8_rows,
+                          assert_topk_equal, bf16_f64, dev, dev_bf16, host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_chain(lib, sh, a):
+    """index score -> top-k -> sparse attention for one decode step of the whole batch."""
+    B, Nc, k = sh.B, sh.n_c, sh.k
+    scores = torch.empty(B, 1, Nc, device="cuda")
+    lib.csa_index_score(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"]),
+                        dev(a["q_pos"]), m=sh.m, scores=scores)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(scores, k, idx)
+    out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, 1, sh.H, device="cuda")
+    lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), idx, dev_bf16(a["swa_bf16"]),
+                        dev(a["sink"]), W=sh.W, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), idx.cpu().numpy(), out, lse.cpu().numpy()
+
+
+def _check_decode(sh, a, scores, idx, out, lse, sample):
+    k = sh.k
+    # top-k, every row: bit-exact against the oracle's selection over the GPU's scores
+    assert_topk_equal(idx, O.topk_indices(scores, k), scores, k, "top-k of GPU scores (all rows)", exact=True)
+    out_bits = host_bits(out)
+    for b in sample:
+        sl = slice(b, b + 1)
+        qI = O.dequant_rows(a["qI_fp8"][sl], a["qI_scale"][sl])
+        KI = O.dequant_rows(a["kI_fp8"][sl], a["kI_scale"][sl])
+        sc_o = O.index_scores(qI, a["w"][sl], KI, a["q_pos"][sl], sh.m)
+        assert_close(scores[sl], sc_o, TOL_F32, f"index scores, sequence {b}")
+        assert_topk_equal(idx[sl], O.topk_indices(sc_o, k), sc_o, k, f"top-k vs oracle scores, sequence {b}")
+        o_o, lse_o = O.sparse_attention(bf16_f64(a["q_bf16"][sl]), bf16_f64(a["kv_comp_bf16"][sl]), idx[sl],
+                                        bf16_f64(a["swa_bf16"][sl]), a["sink"], 1 / math.sqrt(sh.c),
+                                        a["q_pos"][sl], sh.W)
+        assert_bf16_output(bf16_f64(out_bits[sl]), o_o, f"attention, sequence {b}")
+        assert_close(lse[sl], lse_o, TOL_F32, f"lse, sequence {b}")
+
+
+def test_flash_decode_full(lib):
+    sh = I.FLASH_DECODE
+    a = I.decode_inputs(sh).arrays
+    scores, idx, out, lse = _decode_chain(lib, sh, a)
+    _check_decode(sh, a, scores, idx, out, lse, sample=[0, 13, 31])
+
+
+def test_pro_decode_full(lib):
+    sh = I.PRO_DECODE
+    a = I.decode_inputs(sh).arrays
+    scores, idx, out, lse = _decode_chain(lib, sh, a)
+    _check_decode(sh, a, scores, idx, out, lse, sample=[0, 3])
+
+
+def test_hca_decode_full(lib):
+    sh = I.HCA_DECODE
+    a = I.decode_inputs(sh, with_indexer=False).arrays
+    out = torch.empty(sh.B, 1, sh.H, sh.c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(sh.B, 1, sh.H, device="cuda")
+    lib.hca_dense_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(a["q_pos"]), dev_bf16(a["swa_bf16"]),
+                       dev(a["sink"]), m=sh.m, W=sh.W, out=out, lse=lse)
+    torch.cuda.synchronize()
+    out_bits, lse = host_bits(out), lse.cpu().numpy()
+    for b in (0, 37, 63):
+        sl = slice(b, b + 1)
+        o_o, lse_o = O.dense_attention(bf16_f64(a["q_bf16"][sl]), bf16_f64(a["kv_comp_bf16"][sl]), a["q_pos"][sl],
+                                       sh.m, bf16_f64(a["swa_bf16"][sl]), a["sink"], 1 / math.sqrt(sh.c), sh.W)
+        assert_bf16_output(bf16_f64(out_bits[sl]), o_o, f"HCA attention, sequence {b}")
+        assert_close(lse[sl], lse_o, TOL_F32, f"HCA lse, sequence {b}")
+
+
+def test_prefill_chunk_full(lib):
+    sh = I.PREFILL
+    a = I.prefill_inputs(sh)
+    n_ctx, n_new = sh.ctx // sh.m, sh.S // sh.m
+    Nc = n_ctx + n_new
+    kw = dict(overlap=True, m=sh.m, d_rope=sh.d_rope, rope_theta=sh.rope_theta, rms_eps=1e-6, p0=sh.ctx)
+    # ---- compressor: main KV (bf16) and indexer K (FP8 + row scale) for the chunk's entries
+    hid, prev = dev_bf16(a["hidden_bf16"]), dev_bf16(a["hidden_prev_bf16"])
+    kv = torch.empty(1, Nc, sh.c, dtype=torch.bfloat16, device="cuda")
+    kv[:, :n_ctx].copy_(dev_bf16(a["kv_ctx_bf16"]))
+    kI = torch.empty(1, Nc, sh.d_I, dtype=torch.uint8, device="cuda")
+    kI[:, :n_ctx].copy_(dev(a["kI_ctx_fp8"]))
+    kIs = torch.empty(1, Nc, device="cuda")
+    kIs[:, :n_ctx].copy_(dev(a["kI_ctx_scale"]))
+    lib.csa_compress(hid, prev, dev_bf16(np.ascontiguousarray(a["W_main_bf16"].T)), dev(a["B_main"]), c=sh.c,
+                     out=kv[:, n_ctx:], **kw)
+    kI_new = torch.empty(1, n_new, sh.d_I, dtype=torch.uint8, device="cuda")
+    kIs_new = torch.empty(1, n_new, device="cuda")
+    lib.csa_compress(hid, prev, dev_bf16(np.ascontiguousarray(a["W_idx_bf16"].T)), dev(a["B_idx"]), c=sh.d_I,
+                     out=kI_new, out_scale=kIs_new, **kw)
+    kI[:, n_ctx:].copy_(kI_new)
+    kIs[:, n_ctx:].copy_(kIs_new)
+    # ---- index scores for all 8192 queries, top-k, attention
+    qpos = dev(a["q_pos"])
+    scores = torch.empty(1, sh.S, Nc, device="cuda")
+    lib.csa_index_score(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), kI, kIs, qpos, m=sh.m, scores=scores)
+    idx = torch.empty(1, sh.S, sh.k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(scores, sh.k, idx)
+    out = torch.empty(1, sh.S, sh.H, sh.c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(1, sh.S, sh.H, device="cuda")
+    lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), kv, idx, dev_bf16(a["swa_bf16"]), dev(a["sink"]), W=sh.W, out=out,
+                        lse=lse)
+    torch.cuda.synchronize()
+
+    # compressor: sampled entries of the chunk (entry i pools block i and block i-1)
+    hid_all = np.concatenate([a["hidden_prev_bf16"], a["hidden_bf16"]], axis=1)      # rows of blocks -1 .. S/m-1
+    kv_new = host_bits(kv[:, n_ctx:])
+    kI_codes, kI_sc = kI_new.cpu().numpy(), kIs_new.cpu().numpy()
+    for e in (0, 1, 777, n_new - 1):
+        blk = bf16_f64(hid_all[:, sh.m * (e + 1): sh.m * (e + 2)])
+        blk_prev = bf16_f64(hid_all[:, sh.m * e: sh.m * (e + 1)])
+        pos = sh.ctx + sh.m * e
+        kw_e = dict(kw, p0=pos)
+        ref = O.csa_compress(blk, bf16_f64(a["W_main_bf16"]), a["B_main"], c=sh.c, hidden_prev=blk_prev, **kw_e)
+        assert_bf16_within_one_step(kv_new[:, e:e + 1], ref, f"compressed KV, entry {n_ctx + e}")
+        ref_i = O.csa_compress(blk, bf16_f64(a["W_idx_bf16"]), a["B_idx"], c=sh.d_I, hidden_prev=blk_prev, **kw_e)
+        assert_fp8_rows(kI_codes[:, e:e + 1], kI_sc[:, e:e + 1], ref_i, f"indexer K, entry {n_ctx + e}")
+
+    # scores / top-k / attention for sampled queries (on the GPU's K, which is checked above)
+    sc = scores.cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    out_bits, lse_h = host_bits(out), lse.cpu().numpy()
+    KI = O.dequant_rows(kI.cpu().numpy(), kIs.cpu().numpy())
+    kv_h = host_bits(kv)
+    for s in (0, 1, 4095, sh.S - 1):
+        ss = slice(s, s + 1)
+        qI = O.dequant_rows(a["qI_fp8"][:, ss], a["qI_scale"][:, ss])
+        sc_o = O.index_scores(qI, a["w"][:, ss], KI, a["q_pos"][:, ss], sh.m)
+        assert_close(sc[:, ss], sc_o, TOL_F32, f"prefill scores, query {s}")
+        assert_topk_equal(idx_h[:, ss], O.topk_indices(sc[:, ss], sh.k), sc[:, ss], sh.k,
+                          f"prefill top-k of GPU scores, query {s}", exact=True)
+        assert_topk_equal(idx_h[:, ss], O.topk_indices(sc_o, sh.k), sc_o, sh.k, f"prefill top-k, query {s}")
+        sel = idx_h[0, s]
+        rows = sorted({int(j) for j in sel if j >= 0})
+        kv_sel = np.zeros((1, Nc, sh.c))
+        kv_sel[0, rows] = bf16_f64(kv_h[0, rows])
+        o_o, lse_o = O.sparse_attention(bf16_f64(a["q_bf16"][:, ss]), kv_sel, idx_h[:, ss],
+                                        bf16_f64(a["swa_bf16"][:, s: s + sh.W]), a["sink"], 1 / math.sqrt(sh.c),
+                                        a["q_pos"][:, ss], sh.W)
+        assert_bf16_output(bf16_f64(out_bits[:, ss]), o_o, f"prefill attention, query {s}")
+        assert_close(lse_h[:, ss], lse_o, TOL_F32, f"prefill lse, query {s}")
