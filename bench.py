@@ -7,12 +7,16 @@ context, 32768 compressed entries per sequence, 64 indexer heads x 128 FP8, top-
 HBM before timing; the step rotates over several independent input sets (together
 larger than the 256 MB Infinity Cache) so the indexer keys stream from HBM.
 
+The step is captured once per input set into a HIP graph (torch.cuda.CUDAGraph) and the
+timed region replays K of them; `ms_per_step_eager` is the same K steps launched one
+library call at a time.
+
 Prints one JSON line (see the keys below).  `roofline` is for the dominant kernel
 (the indexer), timed with HIP events on the stream it runs on.  `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload.  `prefill_indexer` times the
 indexer over a prefill chunk (8192 queries x 34816 entries) against the matrix peaks.
 
-    python bench.py [--steps K] [--warmup W] [--sets N] [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--steps K] [--warmup W] [--sets N] [--eager] [--no-cpu-baseline] [--no-prefill]
 """
 
 from __future__ import annotations
@@ -42,6 +46,7 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -188,7 +193,7 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-    # timed region: exactly K steps between two synchronisations
+    # eager: exactly K steps between two synchronisations, one library call per stage
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -197,7 +202,28 @@ def main():
         step(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+    ms_eager = t0.elapsed_time(t1) / args.steps
+
+    # graph: each input set's step captured once (same calls, same buffers) and replayed;
+    # the timed region is again exactly K steps between two synchronisations
+    ms_graph = None
+    if not args.eager:
+        graphs = []
+        for i in range(len(sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(len(sets)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            graphs[i % len(sets)].replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = t0.elapsed_time(t1) / args.steps
+    ms_per_step = ms_eager if ms_graph is None else ms_graph
 
     # per-kernel durations (separate pass with events between the stages)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -232,6 +258,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "timing": "graph replay of the captured step" if ms_graph is not None else "eager launches",
+        "ms_per_step_eager": ms_eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

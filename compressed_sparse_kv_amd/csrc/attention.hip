@@ -9,18 +9,18 @@
 // kernel gathers only the rows the indices name).  CSA: remote rows = kv_comp[idx];
 // HCA ("HCA：重压缩 + 全量"): remote rows = every visible entry.
 //
-// bf16 kernel (H = 64 heads, c = 512).  A workgroup owns one query, a group of 16 heads
-// and a contiguous range of 32-row chunks of its row set; its 4 waves split the 512
-// channels into quarters.  Per chunk:
-//   1. the 32 rows sit in one of two LDS slots; each wave loads 8 of them (16 bytes per
+// bf16 kernel (H = 64 heads, c = 512).  A workgroup owns one query, two groups of 16 heads
+// and a contiguous range of 32-row chunks of its row set; its 8 waves are (head group,
+// channel quarter) pairs, so each row read from memory serves 32 heads.  Per chunk:
+//   1. the 32 rows sit in one of two LDS slots; each wave loads 4 of them (16 bytes per
 //      lane per row) into one of two register sets two chunks ahead and writes a set to
 //      its slot after the chunk before it is done, so two chunks are in flight while one
 //      is computed.  (Direct global->LDS loads measured at about half the gather rate
 //      of register loads here.)  Row stride 1072 B (rows shift by 12 banks: 16 rows of a
 //      16-byte operand read and the 4 rows of a transposed read never share a bank);
-//   2. every wave computes its quarter's share of S^T = KV_chunk . Q^T on MFMA (A = rows
-//      from LDS, B = its Q quarter in registers); the 4 shares are summed through LDS
-//      (fixed order, so all waves hold the identical S^T);
+//   2. every wave computes its quarter's share of S^T = KV_chunk . Q^T for its 16 heads on
+//      MFMA (A = rows from LDS, B = its Q quarter in registers); the 4 shares of a head
+//      group are summed through LDS (fixed order, so its 4 waves hold the identical S^T);
 //   3. online softmax in the log2 domain with a lazy reference: the running maximum is
 //      only moved (and O rescaled) when a chunk exceeds it by more than 2^8, which leaves
 //      the result unchanged (numerator and denominator share the reference);
@@ -45,13 +45,19 @@ constexpr int kAH = 64;
 constexpr int kAC = 512;
 constexpr int kHG = 16;                             // heads per workgroup
 constexpr int kNHG = kAH / kHG;
+constexpr int kWGHG = 2;                            // head groups per workgroup
+constexpr int kNPair = kNHG / kWGHG;                // workgroups per (query, split)
+constexpr int kAttnWaves = 4 * kWGHG;               // 4 channel quarters per head group
+constexpr int kAttnThreads = kAttnWaves * 64;
+constexpr int kRowsPerWave = 32 / kAttnWaves;       // rows of a chunk each wave loads
+static_assert(kRowsPerWave == 4, "the row staging macros move 4 rows per wave");
 constexpr int kQuarter = kAC / 4;                   // channels per wave
 constexpr int kRows = 32;                           // rows per chunk
 constexpr int kRing = 2;                            // chunks resident in LDS
 constexpr int kRowStride = kAC * 2 + 48;            // bytes
 constexpr int kChunkBytes = kRows * kRowStride;
 constexpr int kMaxSplitChunks = 72;                 // chunks of row addresses tabled per workgroup
-constexpr int kAttnLdsFixed = kRing * kChunkBytes + 4 * kWave * 8 * 4 + kRing * 4 * 4;
+constexpr int kAttnLdsFixed = kRing * kChunkBytes + kAttnWaves * kWave * 8 * 4 + kRing * kAttnWaves * 4;
 constexpr int kAttnLdsMax = kAttnLdsFixed + kMaxSplitChunks * kRows * 8;
 constexpr float kLazy = 8.0f;                       // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
@@ -93,22 +99,24 @@ __device__ __forceinline__ void window_rows(int s, int S, int Ls, int W, int& w_
 }
 
 template <bool kDense>
-__global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* ring = smem;
   float* sx = reinterpret_cast<float*>(smem + kRing * kChunkBytes);        // [wave][lane][8]
-  int* validw = reinterpret_cast<int*>(sx + 4 * kWave * 8);                // [ring slot][wave]: 8-row masks
-  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kRing * 4);     // this split's row addresses
+  int* validw = reinterpret_cast<int*>(sx + kAttnWaves * kWave * 8);       // [ring slot][wave]: row masks
+  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kRing * kAttnWaves);   // this split's row addresses
 
   // ---- workgroup -> (query, head group, split); one query's workgroups share an XCD
-  const int units = kNHG * a.nsplit;
+  const int units = kNPair * a.nsplit;
   const int xcd = blockIdx.x & 7, t8 = blockIdx.x >> 3;
   const int u = t8 % units;
   const int qi = (t8 / units) * 8 + xcd;
   if (qi >= a.nq) return;
-  const int hg = u % kNHG, split = u / kNHG;
+  const int hp = u % kNPair, split = u / kNPair;
   const int b = qi / a.S, s = qi % a.S;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int hg = kWGHG * hp + (wave >> 2);            // this wave's head group
+  const int quarter = wave & 3;                       // this wave's channel quarter
   const int l = static_cast<int>(lane_id());
   const int g = l >> 4;
 
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
   // channels 128*wave + 32*ks + 8*g .. +7
   v8s qb[kQuarter / 32];
   {
-    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + kQuarter * wave;
+    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + kQuarter * quarter;
 #pragma unroll
     for (int ks = 0; ks < kQuarter / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
   }
@@ -140,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
   // the zero row for absent ones), computed once by all threads.
   {
     const int nsl = (ch1 - ch0) * kRows;
-    for (int e = static_cast<int>(threadIdx.x); e < nsl; e += 256) {
+    for (int e = static_cast<int>(threadIdx.x); e < nsl; e += kAttnThreads) {
       const int slot = ch0 * kRows + e;
       const uint16_t* p = g_zero_row;
       if (slot < n_swa) {
@@ -155,8 +163,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
   }
   const uint64_t zero_row = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g_zero_row));
 
-  // The wave's 8 rows of chunk CH (the zero row for chunks past the split): addresses from
-  // the table with four 16-byte LDS reads, then one 16-byte load per lane per row.
+  // The wave's 4 rows of chunk CH (the zero row for chunks past the split): addresses from
+  // the table with two 16-byte LDS reads, then one 16-byte load per lane per row.
 #define CSA_ATT_LOAD1(ST, VM, R, PTR)                                                   \
   do {                                                                                 \
     const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
@@ -166,34 +174,27 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
   } while (0)
 #define CSA_ATT_LOAD(CH, ST, VM)                                                        \
   do {                                                                                 \
-    uint64_t q_[8];                                                                    \
+    uint64_t q_[4];                                                                    \
     if ((CH) < ch1) {                                                                  \
-      const uint64_t* t_ = rowptr + ((CH) - ch0) * kRows + 8 * wave;                   \
+      const uint64_t* t_ = rowptr + ((CH) - ch0) * kRows + kRowsPerWave * wave;        \
       const ulonglong2 a_ = reinterpret_cast<const ulonglong2*>(t_)[0];                 \
       const ulonglong2 b_ = reinterpret_cast<const ulonglong2*>(t_)[1];                 \
-      const ulonglong2 c_ = reinterpret_cast<const ulonglong2*>(t_)[2];                 \
-      const ulonglong2 d_ = reinterpret_cast<const ulonglong2*>(t_)[3];                 \
       q_[0] = a_.x; q_[1] = a_.y; q_[2] = b_.x; q_[3] = b_.y;                          \
-      q_[4] = c_.x; q_[5] = c_.y; q_[6] = d_.x; q_[7] = d_.y;                          \
     } else {                                                                           \
-      q_[0] = q_[1] = q_[2] = q_[3] = q_[4] = q_[5] = q_[6] = q_[7] = zero_row;        \
+      q_[0] = q_[1] = q_[2] = q_[3] = zero_row;                                        \
     }                                                                                  \
     (VM) = 0;                                                                          \
     CSA_ATT_LOAD1(ST, VM, 0, q_[0]); CSA_ATT_LOAD1(ST, VM, 1, q_[1]);                  \
     CSA_ATT_LOAD1(ST, VM, 2, q_[2]); CSA_ATT_LOAD1(ST, VM, 3, q_[3]);                  \
-    CSA_ATT_LOAD1(ST, VM, 4, q_[4]); CSA_ATT_LOAD1(ST, VM, 5, q_[5]);                  \
-    CSA_ATT_LOAD1(ST, VM, 6, q_[6]); CSA_ATT_LOAD1(ST, VM, 7, q_[7]);                  \
   } while (0)
 #define CSA_ATT_STORE1(BUF, ST, R) \
-  *reinterpret_cast<v4u*>((BUF) + (8 * wave + (R)) * kRowStride + 16 * l) = ST##R
+  *reinterpret_cast<v4u*>((BUF) + (kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R
 #define CSA_ATT_STORE(CH, ST, VM)                                                       \
   do {                                                                                 \
     uint8_t* buf_ = ring + ((CH) & 1) * kChunkBytes;                                   \
     CSA_ATT_STORE1(buf_, ST, 0); CSA_ATT_STORE1(buf_, ST, 1);                          \
     CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                          \
-    CSA_ATT_STORE1(buf_, ST, 4); CSA_ATT_STORE1(buf_, ST, 5);                          \
-    CSA_ATT_STORE1(buf_, ST, 6); CSA_ATT_STORE1(buf_, ST, 7);                          \
-    if (l == 0) validw[((CH) & 1) * 4 + wave] = static_cast<int>(VM);                   \
+    if (l == 0) validw[((CH) & 1) * kAttnWaves + wave] = static_cast<int>(VM);         \
   } while (0)
 
   v4f o[kQuarter / 16];
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
     for (int ks = 0; ks < kQuarter / 32; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 2 * kQuarter * wave +
+        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 2 * kQuarter * quarter +
                                                      64 * ks + 16 * g);
         st[rb] = mfma_bf16_16x16x32(av, qb[ks], st[rb]);
       }
@@ -224,8 +225,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) sv[j] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {                     // fixed order: identical sums in every wave
-      const float* src = sx + (w * kWave + l) * 8;
+    for (int w = 0; w < 4; ++w) {                     // fixed order: identical sums in the group's waves
+      const float* src = sx + ((wave & ~3) + w) * kWave * 8 + l * 8;
       const v4f x0 = *reinterpret_cast<const v4f*>(src);
       const v4f x1 = *reinterpret_cast<const v4f*>(src + 4);
 #pragma unroll
@@ -237,9 +238,12 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
     // ---- online softmax; slot j <-> chunk row 16*(j/4) + 4*g + j%4
     uint32_t vmask;
     {
-      const int4 vw = *reinterpret_cast<const int4*>(validw + (ch & 1) * 4);
-      vmask = static_cast<uint32_t>(vw.x) | (static_cast<uint32_t>(vw.y) << 8) | (static_cast<uint32_t>(vw.z) << 16) |
-              (static_cast<uint32_t>(vw.w) << 24);
+      const int4 v0 = *reinterpret_cast<const int4*>(validw + (ch & 1) * kAttnWaves);
+      const int4 v1 = *reinterpret_cast<const int4*>(validw + (ch & 1) * kAttnWaves + 4);
+      vmask = static_cast<uint32_t>(v0.x) | (static_cast<uint32_t>(v0.y) << 4) | (static_cast<uint32_t>(v0.z) << 8) |
+              (static_cast<uint32_t>(v0.w) << 12) | (static_cast<uint32_t>(v1.x) << 16) |
+              (static_cast<uint32_t>(v1.y) << 20) | (static_cast<uint32_t>(v1.z) << 24) |
+              (static_cast<uint32_t>(v1.w) << 28);
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
     }
     l_run += psum;
     // ---- O_quarter += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
-    const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * kQuarter * wave + 8 * (l & 3);
+    const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * kQuarter * quarter + 8 * (l & 3);
 #pragma unroll
     for (int t = 0; t < kQuarter / 16; ++t) {
       const v4s v0 = lds_read_tr16(vt + 32 * t);
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
     }
   };
 
-  v4u stA0, stA1, stA2, stA3, stA4, stA5, stA6, stA7;
-  v4u stB0, stB1, stB2, stB3, stB4, stB5, stB6, stB7;
+  v4u stA0, stA1, stA2, stA3;
+  v4u stB0, stB1, stB2, stB3;
   uint32_t vA = 0, vB = 0;
   // Every chunk step issues its eight loads, also past the split's end (zero row), so the
   // count of loads in flight is the same on every path and the compiler's waits before
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
   float l_tot = l_run + wave_xor(l_run, 16);
   l_tot += wave_xor(l_tot, 32);
   const int head_l = kHG * hg + (l & 15);             // head whose statistics this lane holds
-  const int col0 = kQuarter * wave + (l & 15);
+  const int col0 = kQuarter * quarter + (l & 15);
   if (a.nsplit == 1) {
     const float sink2 = a.sink[head_l] * kLog2e;
     const float M = fmaxf(m_ref, sink2);
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
       f = den > 0.0f ? em / den : 0.0f;
       lse2 = M + log2f(den);
     }
-    if (a.lse && wave == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
+    if (a.lse && quarter == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
     float fh[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16(AttnArgs a) {
       for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(o[t][i] * fh[i]);
   } else {
     const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
-    if (wave == 0 && g == 0) {
+    if (quarter == 0 && g == 0) {
       a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_ref;
       a.part_ml[(pbase * kAH + head_l) * 2 + 1] = l_tot;
     }
@@ -543,12 +547,12 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
 }
 
-// Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (4 head
-// groups x splits per query) to give every compute unit two, but every split keeps >= 4
-// chunks (128 rows): a split's partial result (16 heads x 512 fp32 = 32 KiB) must stay
+// Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (2 head-group
+// pairs x splits per query) to give every compute unit one, but every split keeps >= 4
+// chunks (128 rows): a split's partial result (32 heads x 512 fp32 = 64 KiB) must stay
 // small next to the rows it reads (1 KiB each).
 int attn_nsplit(int nq, int max_rows) {
-  const int by_fill = cdiv(512, kNHG * nq);
+  const int by_fill = cdiv(256, kNPair * nq);
   const int by_rows = cdiv(max_rows, kRows) / 4;
   const int by_lds = cdiv(cdiv(max_rows, kRows), kMaxSplitChunks);   // a split's row table fits LDS
   return std::max(by_lds, std::max(1, std::min(by_fill, by_rows)));
@@ -594,10 +598,10 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
                                 hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
       attr = true;
     }
-    const dim3 grid(cdiv(nq, 8) * 8 * kNHG * ns);
+    const dim3 grid(cdiv(nq, 8) * 8 * kNPair * ns);
     const int lds = kAttnLdsFixed + a.chunks_per_split * kRows * 8;
-    if (dense) hipLaunchKernelGGL(attn_bf16<true>, grid, dim3(256), lds, st, a);
-    else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(256), lds, st, a);
+    if (dense) hipLaunchKernelGGL(attn_bf16<true>, grid, dim3(kAttnThreads), lds, st, a);
+    else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(kAttnThreads), lds, st, a);
     CSA_LAUNCH_CHECK();
     if (ns > 1) {
       hipLaunchKernelGGL(attn_merge<uint16_t>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, a.part_o, a.part_ml, sink,

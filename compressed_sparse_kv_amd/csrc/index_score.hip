@@ -133,12 +133,14 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
   auto group_e0 = [&](int gi) { return base + 64 * (gi * 4 + wave); };
   auto group_live = [&](int gi) { const int e0 = group_e0(gi); return e0 < Nc && e0 < nvis; };
   v8i ring[3][4];
+  float sring[3];            // row scale of entry e0 + l, fetched with the group's keys
 #define CSA_DEC_LOAD(gi_)                                                                           \
   do {                                                                                              \
     _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                              \
       const int e_ = min(group_e0(gi_) + 16 * nb + (l & 15), Nc - 1);                               \
       ring[(gi_) % 3][nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e_) * kID + 32 * (l >> 4)); \
     }                                                                                               \
+    sring[(gi_) % 3] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                         \
   } while (0)
   if (group_live(0)) CSA_DEC_LOAD(0);
   if (group_live(1)) CSA_DEC_LOAD(1);
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
         p[nb] = head_sum1(a, bk, wv);
       }
       const float v = reduce_scatter4(p);
-      if (e < Nc) out[e] = e < nvis ? v * ksb[e] : -INFINITY;
+      if (e < Nc) out[e] = e < nvis ? v * sring[gi % 3] : -INFINITY;
     } else if (e < Nc) {
       out[e] = -INFINITY;
     }
@@ -238,8 +240,11 @@ __global__ __launch_bounds__(kPfThreads, 4) void index_score_fp8_prefill(
     dst_[1] = make_uint4(cv_[4], cv_[5], cv_[6], cv_[7]);                                   \
   } while (0)
 
+  // row scales travel one tile ahead of their use, like the codes
+  float sk_next = 0.0f;
   if (ntiles_vis > 0) {
     CSA_PF_GLOAD(0);
+    sk_next = ksb[min(l, Nc - 1)];
     CSA_PF_SWRITE(0);
   }
   __syncthreads();
@@ -247,9 +252,12 @@ __global__ __launch_bounds__(kPfThreads, 4) void index_score_fp8_prefill(
   for (int ti = 0; ti < ntiles_vis; ++ti) {
     const int buf = ti & 1;
     const bool more = ti + 1 < ntiles_vis;
-    if (more) CSA_PF_GLOAD(ti + 1);
+    const float sk = sk_next;
+    if (more) {
+      CSA_PF_GLOAD(ti + 1);
+      sk_next = ksb[min((ti + 1) * kPfTile + l, Nc - 1)];
+    }
     const int e = ti * kPfTile + l;
-    const float sk = e < Nc ? ksb[e] : 0.0f;
     float p[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {

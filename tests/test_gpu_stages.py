@@ -230,3 +230,44 @@ def test_compress_bf16(lib, overlap, m, c, T, with_prev, out_kind):
                          dev(a["bias"]), out=out, out_scale=sc, **kw)
         torch.cuda.synchronize()
         assert_fp8_rows(out.cpu().numpy(), sc.cpu().numpy(), ref, "indexer K (fp8)")
+
+
+# ---------------------------------------------------------------------------------------
+# The decode chain captured in a HIP graph: every replay equals the eager result
+# ---------------------------------------------------------------------------------------
+
+def test_decode_chain_graph_replay(lib):
+    B, Nc, k, m, W = 4, 5000, 256, 4, 128
+    a = I.indexer_inputs(41, B, 1, Nc)
+    at = I.attention_inputs(42, B, 1, Nc, W)
+    qpos = dev(np.full((B, 1), 4 * Nc + 3, np.int64))
+    q8, qs, w, k8, ks = dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"])
+    q, kv, swa, sink = dev_bf16(at["q_bf16"]), dev_bf16(at["kv_comp_bf16"]), dev_bf16(at["swa_bf16"]), dev(at["sink"])
+    scores = torch.empty(B, 1, Nc, device="cuda")
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, 1, 64, 512, dtype=torch.bfloat16, device="cuda")
+    tk_ws = torch.empty(max(1, lib.topk_workspace_size(B, Nc, k)), dtype=torch.uint8, device="cuda")
+    at_ws = torch.empty(max(1, lib.attn_workspace_size(B, 1, 64, 512, W + k, lib.CSA_BF16)), dtype=torch.uint8,
+                        device="cuda")
+
+    def step():
+        lib.csa_index_score(q8, qs, w, k8, ks, qpos, m=m, scores=scores)
+        lib.csa_topk(scores, k, idx, ws=tk_ws)
+        lib.csa_sparse_attn(q, kv, idx, swa, sink, W=W, out=out, ws=at_ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (scores.clone(), idx.clone(), out.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        scores.fill_(7.0)
+        idx.fill_(-7)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores, ref[0]), f"scores differ on replay {r}"
+        assert torch.equal(idx, ref[1]), f"indices differ on replay {r}"
+        assert torch.equal(out, ref[2]), f"attention differs on replay {r}"
