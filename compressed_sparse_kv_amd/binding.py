@@ -26,7 +26,8 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "C
           4: "CSA_ERR_HIP"}
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
-           "csa_index_score", "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
+           "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
+           "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "hca_dense_attn")
 
 
@@ -49,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
+        "csa_index_topk_workspace_size": ([i, i, i, i], sz),
+        "csa_index_topk": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
@@ -147,6 +150,30 @@ def csa_index_score(q, q_scale, w, k, k_scale, q_pos, *, m: int, scores, stream=
         _p(q), _p(q_scale), _p(w), _p(k), _p(k_scale), _dtype(q), _p(q_pos), B, S, H, D, Nc, m,
         _p(scores), _stream(stream)))
     return scores
+
+
+# ---------------------------------------------------------------------------------------
+# Stages 2 + 3 in one call
+# ---------------------------------------------------------------------------------------
+
+def index_topk_workspace_size(B, S, Nc, k) -> int:
+    return int(_lib.csa_index_topk_workspace_size(B, S, Nc, k))
+
+
+def csa_index_topk(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, k: int, idx, scores=None, ws=None,
+                   stream=None):
+    """FP8 q [B,S,64,128] + q_scale [B,S,64], w [B,S,64], k_codes [B,Nc,128] + k_scale [B,Nc],
+    q_pos [B,S] -> idx [B,S,k] int32 (and scores [B,S,Nc] fp32 when given)."""
+    _dev(q, q_scale, w, k_codes, k_scale, q_pos, idx, scores, ws)
+    B, S, H, D = q.shape
+    Nc = k_codes.shape[1]
+    need = index_topk_workspace_size(B, S, Nc, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check("csa_index_topk", _lib.csa_index_topk(
+        _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores), _p(idx),
+        _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return idx
 
 
 # ---------------------------------------------------------------------------------------

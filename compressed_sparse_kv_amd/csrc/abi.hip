@@ -16,6 +16,10 @@ size_t attn_workspace_bytes(int, int, int, int, int, int);
 int launch_compress(const void*, const void*, int, const void*, const float*, int, int, int, int, int, int, int,
                     float, float, int64_t, void*, float*, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
+bool index_topk_fused_ok(int, int, int);
+int index_topk_segments(int);
+int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
+                      int, int, int, float*, int32_t*, void*, hipStream_t);
 }  // namespace csa
 
 using namespace csa;
@@ -87,6 +91,42 @@ int csa_index_score(const void* q, const float* q_scale, const float* w, const v
   }
   return launch_index_score(q, q_scale, w, k, k_scale, dtype, q_pos, B, S, H_I, d_I, Nc, m, scores,
                             as_stream(stream));
+}
+
+// ---- stages 2 + 3 -------------------------------------------------------------------
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t csa_index_topk_workspace_size(int B, int S, int Nc, int k) {
+  if (B <= 0 || S <= 0 || Nc <= 0 || k <= 0) return 0;
+  const size_t rows = static_cast<size_t>(B) * S;
+  if (index_topk_fused_ok(S, Nc, k)) return rows * index_topk_segments(Nc) * k * sizeof(uint2);
+  return align256(rows * Nc * sizeof(float)) + topk_workspace_bytes(static_cast<int>(rows), Nc, k);
+}
+
+int csa_index_topk(const void* q, const float* q_scale, const float* w, const void* k_codes, const float* k_scale,
+                   const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc, int m, int k, float* scores,
+                   int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(q && q_scale && w && k_codes && k_scale && q_pos && idx);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0 && k >= 1 && k <= 2048);
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
+  if (H_I != 64 || d_I != 128) return CSA_ERR_UNSUPPORTED;
+  if (!topk_supported(Nc, k, true)) return CSA_ERR_UNSUPPORTED;
+  if (ws == nullptr || ws_bytes < csa_index_topk_workspace_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
+  if (index_topk_fused_ok(S, Nc, k))
+    return launch_index_topk(q, q_scale, w, k_codes, k_scale, q_pos, B, S, Nc, m, k, scores, idx, ws,
+                             as_stream(stream));
+  // other shapes: the two stages one after the other, scores in the workspace when not given
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  float* sc = scores;
+  if (sc == nullptr) sc = reinterpret_cast<float*>(wsb);
+  wsb += align256(static_cast<size_t>(rows) * Nc * sizeof(float));
+  const size_t tk_bytes = topk_workspace_bytes(static_cast<int>(rows), Nc, k);
+  int st = launch_index_score(q, q_scale, w, k_codes, k_scale, CSA_FP8_E4M3, q_pos, B, S, H_I, d_I, Nc, m, sc,
+                              as_stream(stream));
+  if (st != CSA_OK) return st;
+  return launch_topk(sc, static_cast<int>(rows), Nc, k, idx, tk_bytes ? wsb : nullptr, tk_bytes, 0,
+                     as_stream(stream));
 }
 
 // ---- stage 3 ------------------------------------------------------------------------

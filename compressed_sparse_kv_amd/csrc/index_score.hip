@@ -25,6 +25,7 @@
 // 4 entry blocks at once (a reduce-scatter leaving lane l with entry e0+l of a 64-entry
 // group, so stores are coalesced).
 #include "common.hpp"
+#include "select.hpp"
 
 namespace csa {
 
@@ -106,16 +107,23 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 // ------------------------------------------------------------------------------------
 // Decode: few queries per sequence.  Each wave streams 64-entry groups of its sequence's
 // K straight from HBM into registers (one 128-byte row = one cache line, read by 4 lanes
-// x 32 bytes), converts them and multiplies; the next group's loads are in flight while
-// the current group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
+// x 32 bytes), converts them and multiplies; the keys (and row scales) of the next two
+// groups are in flight while a group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
+//
+// kTopk: the workgroup also selects the top-k of its kDecEntWG scores (select_regs over
+// the scores' order-preserving keys, [KV-COMP] section 9.4) and writes them as (key,
+// entry) pairs in entry order to cand[row][blockIdx.x][k] (key 0 = empty slot); the union
+// of these local selections holds the row's top-k, which topk_merge finishes.  Scores are
+// then written only when `scores` is not null.
 // ------------------------------------------------------------------------------------
 constexpr int kDecGroups = 8;                         // 64-entry groups per wave
 constexpr int kDecEntWG = 4 * 64 * kDecGroups;        // entries per workgroup
 
+template <bool kTopk>
 __global__ __launch_bounds__(256) void index_score_fp8_decode(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
-    int S, int Nc, int m, float* __restrict__ scores) {
+    int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand) {
   const size_t row = blockIdx.y;
   const int b = static_cast<int>(row / S);
   const int l = static_cast<int>(lane_id());
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
 
   const uint8_t* kb = k8 + static_cast<size_t>(b) * Nc * kID;
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
-  float* out = scores + row * Nc;
+  float* out = scores ? scores + row * Nc : nullptr;
 
   // group gi of this wave covers entries base + 64*(gi*4 + wave) .. +63; the keys of
   // the next two groups are in flight while a group is multiplied
@@ -149,12 +157,14 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
   float wv[16];
   load_query(q8, qs, w, row, a, wv);
 
+  __shared__ uint32_t kst[kTopk ? kDecEntWG : 1];       // keys of the workgroup's entries
 #pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
     const int e0 = group_e0(gi);
-    if (e0 >= Nc) break;
+    if (!kTopk && e0 >= Nc) break;
     if (gi + 2 < kDecGroups && group_live(gi + 2)) CSA_DEC_LOAD(gi + 2);
     const int e = e0 + l;
+    uint32_t key = 0u;
     if (e0 < nvis) {
       float p[4];
 #pragma unroll
@@ -163,13 +173,31 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
         e4m3x32_to_bf16(ring[gi % 3][nb], bk);
         p[nb] = head_sum1(a, bk, wv);
       }
-      const float v = reduce_scatter4(p);
-      if (e < Nc) out[e] = e < nvis ? v * sring[gi % 3] : -INFINITY;
-    } else if (e < Nc) {
+      const float v = reduce_scatter4(p) * sring[gi % 3];
+      if (out && e < Nc) out[e] = e < nvis ? v : -INFINITY;
+      if (e < nvis) key = score_key(v);
+    } else if (out && e < Nc) {
       out[e] = -INFINITY;
     }
+    if (kTopk) kst[64 * (gi * 4 + wave) + l] = key;
   }
 #undef CSA_DEC_LOAD
+  if (kTopk) {
+    __shared__ TkShared sh;
+    __syncthreads();
+    uint32_t key[1][8];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) key[0][s2] = kst[8 * threadIdx.x + s2];
+    uint64_t taken;
+    int obase[1];
+    const int kk = select_regs<256, 8, 1>(sh, key, ktop, taken, obase);
+    uint2* dst = cand + (row * gridDim.x + blockIdx.x) * static_cast<size_t>(ktop);
+    int o = obase[0];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      if ((taken >> s2) & 1ull) dst[o++] = make_uint2(key[0][s2], static_cast<uint32_t>(base + 8 * threadIdx.x + s2));
+    for (int p = kk + static_cast<int>(threadIdx.x); p < ktop; p += 256) dst[p] = make_uint2(0u, 0u);
+  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -315,9 +343,9 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
   if (dtype == CSA_FP8_E4M3) {
     if (S <= 4) {
       dim3 grid(cdiv(Nc, kDecEntWG), B * S);
-      hipLaunchKernelGGL(index_score_fp8_decode, grid, dim3(256), 0, st,
+      hipLaunchKernelGGL(index_score_fp8_decode<false>, grid, dim3(256), 0, st,
                          static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k),
-                         k_scale, q_pos, S, Nc, m, scores);
+                         k_scale, q_pos, S, Nc, m, scores, 0, nullptr);
     } else {
       dim3 grid(cdiv(S, kPfQ), B);
       hipLaunchKernelGGL(index_score_fp8_prefill, grid, dim3(kPfThreads), 0, st,
@@ -332,6 +360,29 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
   }
   CSA_LAUNCH_CHECK();
   return CSA_OK;
+}
+
+// Scores and per-segment top-k in one pass (decode shapes, FP8, H_I = 64, d_I = 128), then
+// the per-row merge: idx = the k largest of each row, as csa_topk would return.
+int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st);
+int topk_merge_supported(int G, int k);
+
+int index_topk_segments(int Nc) { return cdiv(Nc, kDecEntWG); }
+
+bool index_topk_fused_ok(int S, int Nc, int k) {
+  return S <= 4 && k <= kDecEntWG && topk_merge_supported(index_topk_segments(Nc), k);
+}
+
+int launch_index_topk(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
+                      const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, int32_t* idx,
+                      void* ws, hipStream_t st) {
+  const int G = index_topk_segments(Nc);
+  uint2* cand = static_cast<uint2*>(ws);
+  dim3 grid(G, B * S);
+  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(256), 0, st, static_cast<const uint8_t*>(q), q_scale,
+                     w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc, m, scores, ktop, cand);
+  CSA_LAUNCH_CHECK();
+  return launch_topk_merge(cand, B * S, G, ktop, idx, st);
 }
 
 }  // namespace csa

@@ -121,6 +121,25 @@ int csa_index_score(const void* q, const float* q_scale, const float* w,
                     float* scores, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * Stages 2 and 3 in one call (FP8 inputs, H_I = 64, d_I = 128): the index scores of
+ * csa_index_score and the selection of csa_topk, identical results.  For decode shapes
+ * (S <= 4, ceil(Nc / 2048) * k <= 36864) the scoring pass also selects the top-k of each
+ * 2048-entry segment while the scores are in registers, and one merge pass finishes the
+ * rows ([KV-COMP] section 9.4: the union of segment top-k sets holds the row's top-k);
+ * other shapes run the two stages back to back.
+ *   Arguments as csa_index_score and csa_topk (k = top-k, 1 <= k <= 2048);
+ *   scores [B,S,Nc] fp32 or NULL (then not written, except in the workspace);
+ *   idx [B,S,k] int32 output;
+ *   ws >= csa_index_topk_workspace_size(B, S, Nc, k) bytes (required, never NULL).
+ * ------------------------------------------------------------------------------ */
+size_t csa_index_topk_workspace_size(int B, int S, int Nc, int k);
+
+int csa_index_topk(const void* q, const float* q_scale, const float* w,
+                   const void* k_codes, const float* k_scale, const int64_t* q_pos,
+                   int B, int S, int H_I, int d_I, int Nc, int m, int k,
+                   float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 3: top-k selection.  [KV-COMP] sections 9.4 (S_t = TopK_k of the scores)
  * and 9.8 (invisible entries carry -inf and come out as -1).
  *

@@ -271,3 +271,37 @@ def test_decode_chain_graph_replay(lib):
         assert torch.equal(scores, ref[0]), f"scores differ on replay {r}"
         assert torch.equal(idx, ref[1]), f"indices differ on replay {r}"
         assert torch.equal(out, ref[2]), f"attention differs on replay {r}"
+
+
+# ---------------------------------------------------------------------------------------
+# Stages 2 + 3 in one call: identical to csa_index_score followed by csa_topk
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,Nc,k,t,with_scores", [
+    (3, 1, 32768, 512, 4 * 32768 - 1, True),       # decode, fused path
+    (2, 1, 5000, 256, 4 * 5000 + 7, False),        # ragged last segment, no score output
+    (2, 2, 9000, 300, 4 * 2500 + 2, True),         # causal limit inside the row, 2 queries
+    (1, 1, 3000, 2048, 4 * 3000 - 1, True),        # k above the visible count
+    (2, 8, 3000, 128, 4 * 3000 + 40, True),        # prefill shape: the two stages back to back
+    (1, 1, 262144, 1024, 4 * 262144 - 1, False),   # Pro shape: too many segment candidates, back to back
+])
+def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
+    a = I.indexer_inputs(B * 1000 + Nc + k, B, S, Nc)
+    pos = (t - S + 1 + np.arange(S, dtype=np.int64))[None].repeat(B, 0)
+    args = (dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"]), dev(pos))
+    sc_ref = torch.empty(B, S, Nc, device="cuda")
+    lib.csa_index_score(*args[:5], args[5], m=4, scores=sc_ref)
+    idx_ref = torch.empty(B, S, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(sc_ref, k, idx_ref)
+    idx = torch.empty(B, S, k, dtype=torch.int32, device="cuda")
+    sc = torch.empty(B, S, Nc, device="cuda") if with_scores else None
+    lib.csa_index_topk(*args, m=4, k=k, idx=idx, scores=sc)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref), "fused top-k differs from csa_index_score + csa_topk"
+    if with_scores:
+        assert torch.equal(sc, sc_ref), "fused scores differ from csa_index_score"
+    # and against the oracle, on the first query
+    qI = O.dequant_rows(a["qI_fp8"][:1, :1], a["qI_scale"][:1, :1])
+    KI = O.dequant_rows(a["kI_fp8"][:1], a["kI_scale"][:1])
+    sc_o = O.index_scores(qI, a["w"][:1, :1], KI, pos[:1, :1], 4)
+    assert_topk_equal(idx[:1, :1].cpu().numpy(), O.topk_indices(sc_o, k), sc_o, k, "fused top-k vs oracle")
