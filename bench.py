@@ -46,6 +46,7 @@ def parse():
     p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-other", action="store_true", help="skip the Pro / HCA decode and compressor lines")
     p.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
@@ -280,6 +281,10 @@ def main():
 
     if not args.no_prefill:
         result["prefill_indexer"] = bench_prefill_indexer(torch, L, I, dev)
+    if not args.no_other:
+        result["pro_decode"] = bench_csa_decode(torch, L, I, dev, I.PRO_DECODE, n_sets=2)
+        result["hca_decode"] = bench_hca_decode(torch, L, I, dev)
+        result["prefill_compressor"] = bench_prefill_compressor(torch, L, I, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_sets, sh)
@@ -305,6 +310,96 @@ def measured_traffic(source, kernel):
     if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def _timed(torch, fn, reps):
+    fn(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_csa_decode(torch, L, I, dev, sh, n_sets=2, reps=20):
+    """One CSA decode step (scores -> top-k -> attention) of another decode shape."""
+    sets = []
+    for i in range(n_sets):
+        a = I.decode_inputs(sh, seed=sh.seed + 100 * i).arrays
+        up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        upb = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        sets.append({"kv": upb(a["kv_comp_bf16"]), "swa": upb(a["swa_bf16"]), "q": upb(a["q_bf16"]),
+                     "sink": up(a["sink"]), "pos": up(a["q_pos"]), "k8": up(a["kI_fp8"]), "ks": up(a["kI_scale"]),
+                     "q8": up(a["qI_fp8"]), "qs": up(a["qI_scale"]), "w": up(a["w"])})
+        del a
+    B, Nc, k = sh.B, sh.n_c, sh.k
+    scores = torch.empty(B, 1, Nc, device=dev)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+    out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
+    tk_ws = torch.empty(max(1, L.topk_workspace_size(B, Nc, k)), dtype=torch.uint8, device=dev)
+    at_ws = torch.empty(max(1, L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)), dtype=torch.uint8,
+                        device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        L.csa_topk(scores, k, idx, ws=tk_ws)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+
+    ms = _timed(torch, step, reps)
+    byts = decode_step_bytes(sh)
+    return {"workload": sh.name, "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms, "step_bytes": byts,
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "input_sets": n_sets}
+
+
+def bench_hca_decode(torch, L, I, dev, reps=20):
+    """HCA decode: dense attention of 64 queries over 8192 compressed entries (1M context) + window."""
+    sh = I.HCA_DECODE
+    a = I.decode_inputs(sh, with_indexer=False).arrays
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    upb = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    kv, swa, q, sink, pos = upb(a["kv_comp_bf16"]), upb(a["swa_bf16"]), upb(a["q_bf16"]), up(a["sink"]), up(a["q_pos"])
+    del a
+    out = torch.empty(sh.B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, L.attn_workspace_size(sh.B, 1, sh.H, sh.c, sh.W + sh.n_c, L.CSA_BF16)), dtype=torch.uint8,
+                     device=dev)
+    ms = _timed(torch, lambda i: L.hca_dense_attn(q, kv, pos, swa, sink, m=sh.m, W=sh.W, out=out, ws=ws), reps)
+    byts = sh.B * (sh.n_c + sh.W) * sh.c * 2 + 2 * sh.B * sh.H * sh.c * 2 + sh.H * 4 + sh.B * 8
+    flops = 4.0 * sh.B * sh.H * (sh.n_c + sh.W) * sh.c
+    return {"workload": sh.name, "tokens_per_s": sh.B / (ms * 1e-3), "ms_per_step": ms, "bytes": byts,
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def bench_prefill_compressor(torch, L, I, dev, reps=5):
+    """Compressor over one prefill chunk: 8192 new tokens (+4 from the previous block), d = 5120,
+    main KV (c = 512, bf16 out) and indexer K (c = 128, FP8 out)."""
+    sh = I.PREFILL
+    a = I.prefill_inputs(sh)
+    upb = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    hid, prev = upb(a["hidden_bf16"]), upb(a["hidden_prev_bf16"])
+    Wm, Wi = upb(np.ascontiguousarray(a["W_main_bf16"].T)), upb(np.ascontiguousarray(a["W_idx_bf16"].T))
+    Bm, Bi = up(a["B_main"]), up(a["B_idx"])
+    del a
+    n = sh.S // sh.m
+    kv = torch.empty(1, n, sh.c, dtype=torch.bfloat16, device=dev)
+    kI = torch.empty(1, n, sh.d_I, dtype=torch.uint8, device=dev)
+    kIs = torch.empty(1, n, device=dev)
+    kw = dict(overlap=True, m=sh.m, d_rope=sh.d_rope, rope_theta=sh.rope_theta, rms_eps=1e-6, p0=sh.ctx)
+    ws = torch.empty(L.compress_workspace_size(1, sh.S, sh.m, sh.c, True, True), dtype=torch.uint8, device=dev)
+    ms_m = _timed(torch, lambda i: L.csa_compress(hid, prev, Wm, Bm, c=sh.c, out=kv, ws=ws, **kw), reps)
+    ms_i = _timed(torch, lambda i: L.csa_compress(hid, prev, Wi, Bi, c=sh.d_I, out=kI, out_scale=kIs, ws=ws, **kw),
+                  reps)
+    rows = sh.S + sh.m
+    f_m, f_i = 2.0 * rows * sh.d * 4 * sh.c, 2.0 * rows * sh.d * 4 * sh.d_I
+    return {"workload": "csa_prefill_chunk8192_d5120_compressor", "main_ms": ms_m, "indexer_ms": ms_i,
+            "main_tflops": f_m / (ms_m * 1e-3) / 1e12, "indexer_tflops": f_i / (ms_i * 1e-3) / 1e12,
+            "main_frac_bf16_peak": f_m / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "indexer_frac_bf16_peak": f_i / (ms_i * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
 
 
 def bench_prefill_indexer(torch, L, I, dev, reps=10):

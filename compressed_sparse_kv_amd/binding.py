@@ -56,7 +56,7 @@ def _load() -> ctypes.CDLL:
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
         "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
-        "csa_sparse_attn": ([vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
         "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
     }
     for name, (args, res) in sig.items():
@@ -202,16 +202,18 @@ def attn_workspace_size(B, S, H, c, max_rows, dtype) -> int:
     return int(_lib.csa_attn_workspace_size(B, S, H, c, max_rows, dtype))
 
 
-def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, ws=None, stream=None):
-    """q [B,S,H,c], kv_comp [B,Nc,c], idx [B,S,k] int32, swa [B,Ls,c], sink [H] fp32."""
-    _dev(q, kv_comp, idx, swa, sink, out, lse, ws)
+def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None, ws=None,
+                    stream=None):
+    """q [B,S,H,c], kv_comp [B,Nc,c], idx [B,S,k] int32, swa [B,Ls,c], sink [H] fp32;
+    q_pos [B,S] int64 (optional) leaves out window rows of negative positions."""
+    _dev(q, kv_comp, idx, swa, sink, out, lse, ws, q_pos)
     B, S, H, c = q.shape
     Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     dt = _dtype(q)
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_sparse_attn", _lib.csa_sparse_attn(
-        _p(q), _p(kv_comp), _p(idx), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
+        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
         _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
     return out
 

@@ -30,6 +30,7 @@ using namespace csa;
   } while (0)
 
 static hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 extern "C" {
 
@@ -68,6 +69,7 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, cons
   if (in_dtype == CSA_BF16 && d % 64 != 0) return CSA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * (T + m) * 4 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
   const int has_prev = hidden_prev != nullptr;
+  CSA_REQUIRE(aligned16(ws));
   if (ws == nullptr || ws_bytes < compress_workspace_bytes(B, T, m, c, overlap, has_prev)) return CSA_ERR_WORKSPACE;
   return launch_compress(hidden, hidden_prev, in_dtype, w_proj, bias, overlap, B, T, d, m, c, d_rope, rope_theta,
                          rms_eps, p0, out, out_scale, out_dtype, ws, as_stream(stream));
@@ -112,6 +114,7 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w, const vo
   CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
   if (H_I != 64 || d_I != 128) return CSA_ERR_UNSUPPORTED;
   if (!topk_supported(Nc, k, true)) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(ws));
   if (ws == nullptr || ws_bytes < csa_index_topk_workspace_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
   if (index_topk_fused_ok(S, Nc, k))
     return launch_index_topk(q, q_scale, w, k_codes, k_scale, q_pos, B, S, Nc, m, k, scores, idx, ws,
@@ -143,6 +146,7 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
   const int64_t rows = static_cast<int64_t>(B) * S;
   CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
   if (!topk_supported(Nc, k, true)) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(ws));
   if (ws != nullptr && ws_bytes < topk_workspace_bytes(static_cast<int>(rows), Nc, k)) return CSA_ERR_WORKSPACE;
   if (ws == nullptr && (algo == 2 || !topk_supported(Nc, k, false))) return CSA_ERR_WORKSPACE;
   return launch_topk(scores, static_cast<int>(rows), Nc, k, idx, ws, ws_bytes, algo, as_stream(stream));
@@ -175,13 +179,14 @@ static int check_attn(const void* q, const void* kv, const void* swa, const floa
   return CSA_OK;
 }
 
-int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, const void* swa, const float* sink,
-                    int dtype, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W, void* out,
-                    float* lse, void* ws, size_t ws_bytes, void* stream) {
+int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos, const void* swa,
+                    const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(idx && k >= 1 && k <= 65536);
-  return launch_attention(false, q, kv_comp, idx, nullptr, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
+  CSA_REQUIRE(aligned16(ws));
+  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
                           lse, ws, ws_bytes, as_stream(stream));
 }
 
@@ -191,6 +196,7 @@ int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int
   const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(q_pos && m > 0);
+  CSA_REQUIRE(aligned16(ws));
   return launch_attention(true, q, kv_comp, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W, out,
                           lse, ws, ws_bytes, as_stream(stream));
 }

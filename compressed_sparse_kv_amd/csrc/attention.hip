@@ -9,119 +9,95 @@
 // kernel gathers only the rows the indices name).  CSA: remote rows = kv_comp[idx];
 // HCA ("HCA：重压缩 + 全量"): remote rows = every visible entry.
 //
-// bf16 kernel (H = 64 heads, c = 512).  A workgroup owns one query, two groups of 16 heads
-// and a contiguous range of 32-row chunks of its row set; its 8 waves are (head group,
-// channel quarter) pairs, so each row read from memory serves 32 heads.  Per chunk:
-//   1. the 32 rows sit in one of two LDS slots; each wave loads 4 of them (16 bytes per
-//      lane per row) into one of two register sets two chunks ahead and writes a set to
-//      its slot after the chunk before it is done, so two chunks are in flight while one
-//      is computed.  (Direct global->LDS loads measured at about half the gather rate
-//      of register loads here.)  Row stride 1072 B (rows shift by 12 banks: 16 rows of a
-//      16-byte operand read and the 4 rows of a transposed read never share a bank);
-//   2. every wave computes its quarter's share of S^T = KV_chunk . Q^T for its 16 heads on
-//      MFMA (A = rows from LDS, B = its Q quarter in registers); the 4 shares of a head
-//      group are summed through LDS (fixed order, so its 4 waves hold the identical S^T);
+// bf16 kernel (H = 64 heads, c = 512).  A workgroup owns one query, some groups of 16
+// heads and a contiguous range of 32-row chunks of its row set; its 8 waves are (head
+// group, channel part) pairs.  Two shapes: channel quarters (2 head groups per workgroup,
+// two workgroups per query: more workgroups for few queries) and channel halves (all 4
+// head groups in one workgroup, so each row read from memory serves all 64 heads: for
+// many queries or long row sets).  Per chunk:
+//   1. the 32 rows sit in one of three LDS slots; each wave loads 4 of them (16 bytes per
+//      lane per row) into one of two register sets four chunks ahead of the chunk being
+//      finished and writes a set to its slot two chunks ahead.  (Direct global->LDS
+//      loads measured at about half the gather rate of register loads here.)  Row
+//      stride 1056 B: rows shift by 8 banks, so the 8 rows that 32 lanes of a
+//      transposed read touch never share a bank (measured: 1/5 of the conflict cycles
+//      of a 12-bank shift);
+//   2. every wave computes its part's share of S^T = KV_chunk . Q^T for its 16 heads on
+//      MFMA (A = rows from LDS, B = its Q part in registers); the shares of a head group
+//      are summed through LDS (fixed order, so its waves hold the identical S^T).  The
+//      shares of chunk c+1 are formed in the same step as chunk c is finished (two
+//      exchange buffers), so one barrier per chunk orders everything;
 //   3. online softmax in the log2 domain with a lazy reference: the running maximum is
 //      only moved (and O rescaled) when a chunk exceeds it by more than 2^8, which leaves
 //      the result unchanged (numerator and denominator share the reference);
-//   4. O_quarter += P . V on MFMA with V read from the same LDS rows (K = V) through
+//   4. O_part += P . V on MFMA with V read from the same LDS rows (K = V) through
 //      ds_read_b64_tr_b16: in each 16-lane group, output lane i' slot j' receives input
 //      lane 4j'+i'/4 slot i'%4, so lanes 4j'..4j'+3 reading 16 columns of row R(j') hand
 //      every lane its column of 4 rows.  The S^T output layout (lane: head l%16, rows
 //      4*(l/16)+i and 16+4*(l/16)+i) is the A-operand layout of P under the matching
 //      k-slot order, so P never leaves registers.  P enters as a bf16 hi + lo pair (two
 //      MFMAs on one V operand) so it keeps ~16 bits.
-// A row set split over several workgroups writes (m, l, O) partials that attn_merge
+// A row set split over several workgroups writes (m, l, O) partials that attn_merge_tiles
 // combines with the sink (LSE merge).  Workgroups are numbered so that all workgroups
 // of one query land on the same XCD (consecutive workgroup ids go round-robin over the
 // 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
 
-#include "common.hpp"
+#include "attention_common.hpp"
 
 namespace csa {
 
-constexpr int kAH = 64;
-constexpr int kAC = 512;
-constexpr int kHG = 16;                             // heads per workgroup
-constexpr int kNHG = kAH / kHG;
-constexpr int kWGHG = 2;                            // head groups per workgroup
-constexpr int kNPair = kNHG / kWGHG;                // workgroups per (query, split)
-constexpr int kAttnWaves = 4 * kWGHG;               // 4 channel quarters per head group
+constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kRowsPerWave = 32 / kAttnWaves;       // rows of a chunk each wave loads
 static_assert(kRowsPerWave == 4, "the row staging macros move 4 rows per wave");
-constexpr int kQuarter = kAC / 4;                   // channels per wave
-constexpr int kRows = 32;                           // rows per chunk
-constexpr int kRing = 2;                            // chunks resident in LDS
-constexpr int kRowStride = kAC * 2 + 48;            // bytes
-constexpr int kChunkBytes = kRows * kRowStride;
-constexpr int kMaxSplitChunks = 72;                 // chunks of row addresses tabled per workgroup
-constexpr int kAttnLdsFixed = kRing * kChunkBytes + kAttnWaves * kWave * 8 * 4 + kRing * kAttnWaves * 4;
-constexpr int kAttnLdsMax = kAttnLdsFixed + kMaxSplitChunks * kRows * 8;
-constexpr float kLazy = 8.0f;                       // log2 units
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
-// Source of the rows that are absent (index -1, padding): every chunk is the same eight
-// loads per wave, so the compiler's count of loads in flight is the same on every path.
-__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kAC];
-
-
-// Workgroup barrier without a memory fence: the row loads still in flight (later chunks)
-// are not waited for; LDS writes of this wave are waited for explicitly.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);               // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
-struct AttnArgs {
-  const uint16_t* q;
-  const uint16_t* kv;
-  const int32_t* idx;
-  const int64_t* q_pos;
-  const uint16_t* swa;
-  const float* sink;
-  float scale_log2;          // scale * log2(e)
-  int nq, S, Nc, k, Ls, W, m;
-  int nsplit, chunks_per_split;
-  uint16_t* out;
-  float* lse;
-  float* part_o;             // [B*S, nsplit, H, c] fp32, unnormalised
-  float* part_ml;            // [B*S, nsplit, H, 2]: reference max (log2 units), sum
+// Workgroup shape for kParts channel parts per head group (4: quarters, 2: halves).
+template <int kParts>
+struct AttnShape {
+  static constexpr int kPart = kAC / kParts;        // channels per wave
+  static constexpr int kWGHG = kAttnWaves / kParts; // head groups per workgroup
+  static constexpr int kUnits = kNHG / kWGHG;       // workgroups per (query, split)
 };
+// channel halves once a call has this many queries
+constexpr int kHalvesMinQueries = 64;
+constexpr int kRing = 3;                            // chunks resident in LDS
+constexpr int kSxBytes = kAttnWaves * kWave * 8 * 4;  // one buffer of S^T shares
+constexpr int kValidSlots = 4;                      // row-mask slots (kRing, padded)
+constexpr int kAttnLdsFixed = kRing * kChunkBytes + 2 * kSxBytes + kValidSlots * kAttnWaves * 4;
+constexpr int kAttnLdsMax = kAttnLdsFixed + kMaxSplitChunks * kRows * 8;
+static_assert(kAttnLdsMax <= 160 * 1024, "LDS of one compute unit");
 
-// Window rows of query s: [w_lo, w_hi] of the sequence's swa tensor.
-__device__ __forceinline__ void window_rows(int s, int S, int Ls, int W, int& w_lo, int& n_swa) {
-  const int w_hi = s + Ls - S;
-  w_lo = max(0, w_hi - W + 1);
-  n_swa = w_hi - w_lo + 1;
-}
+// Source of the rows that are absent (index -1, padding, chunks past a split's end):
+// every chunk is the same loads per wave, so the compiler's count of loads in flight is
+// the same on every path.  Many zero rows, so that these reads spread over the L2
+// channels (all workgroups reading one line serialise on one channel); the low address
+// bit marks an absent row in the row table.
+constexpr int kZeroRows = 64;
+__device__ __attribute__((aligned(1024))) uint16_t g_zero_rows[kZeroRows * kAC];
 
-template <bool kDense>
+template <bool kDense, int kParts>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
+  using Sh = AttnShape<kParts>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* ring = smem;
-  float* sx = reinterpret_cast<float*>(smem + kRing * kChunkBytes);        // [wave][lane][8]
-  int* validw = reinterpret_cast<int*>(sx + kAttnWaves * kWave * 8);       // [ring slot][wave]: row masks
-  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kRing * kAttnWaves);   // this split's row addresses
+  uint8_t* ring = smem;                                                          // [slot][32 rows]
+  float* sx = reinterpret_cast<float*>(smem + kRing * kChunkBytes);              // [buffer][wave][lane][8]
+  int* validw = reinterpret_cast<int*>(smem + kRing * kChunkBytes + 2 * kSxBytes);   // [slot][wave]: row masks
+  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kValidSlots * kAttnWaves);  // the split's row addresses
 
-  // ---- workgroup -> (query, head group, split); one query's workgroups share an XCD
-  const int units = kNPair * a.nsplit;
-  const int xcd = blockIdx.x & 7, t8 = blockIdx.x >> 3;
-  const int u = t8 % units;
-  const int qi = (t8 / units) * 8 + xcd;
-  if (qi >= a.nq) return;
-  const int hp = u % kNPair, split = u / kNPair;
+  // ---- workgroup -> (query, head groups, split)
+  int qi, u;
+  if (!attn_unit(a.nq, Sh::kUnits * a.nsplit, qi, u)) return;
+  const int hp = u % Sh::kUnits, split = u / Sh::kUnits;
   const int b = qi / a.S, s = qi % a.S;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-  const int hg = kWGHG * hp + (wave >> 2);            // this wave's head group
-  const int quarter = wave & 3;                       // this wave's channel quarter
+  const int hg = Sh::kWGHG * hp + wave / kParts;      // this wave's head group
+  const int part = wave % kParts;                     // this wave's channel part
   const int l = static_cast<int>(lane_id());
   const int g = l >> 4;
 
   int w_lo, n_swa;
-  window_rows(s, a.S, a.Ls, a.W, w_lo, n_swa);
+  window_rows(s, a.S, a.Ls, a.W, last_position(a.q_pos, b, a.S), w_lo, n_swa);
   const int n_rem = kDense ? static_cast<int>(min(static_cast<int64_t>(a.Nc), (a.q_pos[qi] + 1) / a.m)) : a.k;
   const int n_slots = n_swa + n_rem;
   const int n_chunks = cdiv(n_slots, kRows);
@@ -132,45 +108,46 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
   const int32_t* idxq = kDense ? nullptr : a.idx + static_cast<size_t>(qi) * a.k;
 
-  // Q quarter of the 16 heads as the B operand: lane l holds head 16*hg + l%16,
-  // channels 128*wave + 32*ks + 8*g .. +7
-  v8s qb[kQuarter / 32];
+  // Q part of the 16 heads as the B operand: lane l holds head 16*hg + l%16,
+  // channels kPart*part + 32*ks + 8*g .. +7.  These loads complete under the waits of
+  // the row table below (one memory latency for both).
+  v8s qb[Sh::kPart / 32];
   {
-    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + kQuarter * quarter;
+    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + Sh::kPart * part;
 #pragma unroll
-    for (int ks = 0; ks < kQuarter / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
+    for (int ks = 0; ks < Sh::kPart / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
   }
-  // Q complete before any row load: otherwise the compiler's wait for Q inside the loop
-  // (on a path where no row load follows) becomes a wait for all rows in flight
-  __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
 
-  // The address of every row of the split (window row, selected or visible entry, or
-  // the zero row for absent ones), computed once by all threads.
+  // The address of every row of the split (window row, selected or visible entry, or a
+  // zero row with the low bit set for absent ones), computed once by all threads.
+  const uint64_t zero_rows = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g_zero_rows));
   {
     const int nsl = (ch1 - ch0) * kRows;
     for (int e = static_cast<int>(threadIdx.x); e < nsl; e += kAttnThreads) {
       const int slot = ch0 * kRows + e;
-      const uint16_t* p = g_zero_row;
+      uint64_t p = (zero_rows + static_cast<uint64_t>(e % kZeroRows) * (kAC * 2)) | 1u;
       if (slot < n_swa) {
-        p = swab + static_cast<size_t>(w_lo + slot) * kAC;
+        p = reinterpret_cast<uint64_t>(swab + static_cast<size_t>(w_lo + slot) * kAC);
       } else if (slot < n_slots) {
         const int j = kDense ? slot - n_swa : idxq[slot - n_swa];
-        if (j >= 0 && j < a.Nc) p = kvb + static_cast<size_t>(j) * kAC;
+        if (j >= 0 && j < a.Nc) p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kAC);
       }
-      rowptr[e] = reinterpret_cast<uint64_t>(p);
+      rowptr[e] = p;
     }
+    // Q complete before any row load: otherwise the compiler's wait for Q inside the
+    // loop becomes a wait for all rows in flight
+    __builtin_amdgcn_s_waitcnt(0x0f70);               // vmcnt(0)
     __syncthreads();
   }
-  const uint64_t zero_row = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g_zero_row));
 
-  // The wave's 4 rows of chunk CH (the zero row for chunks past the split): addresses from
+  // The wave's 4 rows of chunk CH (zero rows for chunks past the split): addresses from
   // the table with two 16-byte LDS reads, then one 16-byte load per lane per row.
 #define CSA_ATT_LOAD1(ST, VM, R, PTR)                                                   \
   do {                                                                                 \
     const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
                         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(PTR)));   \
-    (VM) |= (p_ != zero_row ? 1u : 0u) << (R);                                         \
-    ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_)[l];     \
+    (VM) |= static_cast<uint32_t>(~p_ & 1u) << (R);                                    \
+    ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
   } while (0)
 #define CSA_ATT_LOAD(CH, ST, VM)                                                        \
   do {                                                                                 \
@@ -181,7 +158,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       const ulonglong2 b_ = reinterpret_cast<const ulonglong2*>(t_)[1];                 \
       q_[0] = a_.x; q_[1] = a_.y; q_[2] = b_.x; q_[3] = b_.y;                          \
     } else {                                                                           \
-      q_[0] = q_[1] = q_[2] = q_[3] = zero_row;                                        \
+      const uint64_t z_ = zero_rows | 1u;                                              \
+      const int r_ = ((CH) * kRows + kRowsPerWave * wave) & (kZeroRows - 1);           \
+      q_[0] = z_ + static_cast<uint64_t>(r_) * (kAC * 2);                              \
+      q_[1] = z_ + static_cast<uint64_t>(r_ + 1) * (kAC * 2);                          \
+      q_[2] = z_ + static_cast<uint64_t>(r_ + 2) * (kAC * 2);                          \
+      q_[3] = z_ + static_cast<uint64_t>(r_ + 3) * (kAC * 2);                          \
     }                                                                                  \
     (VM) = 0;                                                                          \
     CSA_ATT_LOAD1(ST, VM, 0, q_[0]); CSA_ATT_LOAD1(ST, VM, 1, q_[1]);                  \
@@ -189,44 +171,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   } while (0)
 #define CSA_ATT_STORE1(BUF, ST, R) \
   *reinterpret_cast<v4u*>((BUF) + (kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R
-#define CSA_ATT_STORE(CH, ST, VM)                                                       \
+#define CSA_ATT_STORE(SLOT, ST, VM)                                                     \
   do {                                                                                 \
-    uint8_t* buf_ = ring + ((CH) & 1) * kChunkBytes;                                   \
+    uint8_t* buf_ = ring + (SLOT) * kChunkBytes;                                       \
     CSA_ATT_STORE1(buf_, ST, 0); CSA_ATT_STORE1(buf_, ST, 1);                          \
     CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                          \
-    if (l == 0) validw[((CH) & 1) * kAttnWaves + wave] = static_cast<int>(VM);         \
+    if (l == 0) validw[(SLOT) * kAttnWaves + wave] = static_cast<int>(VM);             \
   } while (0)
 
-  v4f o[kQuarter / 16];
+  v4f o[Sh::kPart / 16];
 #pragma unroll
-  for (int t = 0; t < kQuarter / 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < Sh::kPart / 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY;   // per head l%16 (log2 units)
   float l_run = 0.0f;        // this lane's share of the per-head sum
-  float* sxw = sx + (wave * kWave + l) * 8;
 
-  // one chunk: S^T share, exchange, softmax, P.V (the chunk is in LDS slot ch & 1)
-  auto compute = [&](int ch) __attribute__((always_inline)) {
-    const uint8_t* buf = ring + (ch & 1) * kChunkBytes;
-    // ---- this wave's share of S^T (32 rows x 16 heads) over its channel quarter
+  // This wave's share of S^T (32 rows x 16 heads) over its channel part for the chunk in
+  // ring slot SL, written to exchange buffer XB.
+  auto s_part = [&](int sl, int xb) __attribute__((always_inline)) {
+    const uint8_t* buf = ring + sl * kChunkBytes;
     v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int ks = 0; ks < kQuarter / 32; ++ks) {
+    for (int ks = 0; ks < Sh::kPart / 32; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 2 * kQuarter * quarter +
+        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 2 * Sh::kPart * part +
                                                      64 * ks + 16 * g);
         st[rb] = mfma_bf16_16x16x32(av, qb[ks], st[rb]);
       }
     }
-    *reinterpret_cast<v4f*>(sxw) = st[0];
-    *reinterpret_cast<v4f*>(sxw + 4) = st[1];
-    barrier_lds();
+    float* w = sx + xb * (kSxBytes / 4) + (wave * kWave + l) * 8;
+    *reinterpret_cast<v4f*>(w) = st[0];
+    *reinterpret_cast<v4f*>(w + 4) = st[1];
+  };
+
+  // Chunk in ring slot SL whose S^T shares are in exchange buffer XB: online softmax and
+  // O_part += P . V.
+  auto softmax_pv = [&](int sl, int xb) __attribute__((always_inline)) {
+    const uint8_t* buf = ring + sl * kChunkBytes;
     float sv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) sv[j] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {                     // fixed order: identical sums in the group's waves
-      const float* src = sx + ((wave & ~3) + w) * kWave * 8 + l * 8;
+    for (int w = 0; w < kParts; ++w) {                // fixed order: identical sums in the group's waves
+      const float* src = sx + xb * (kSxBytes / 4) + ((wave & ~(kParts - 1)) + w) * kWave * 8 + l * 8;
       const v4f x0 = *reinterpret_cast<const v4f*>(src);
       const v4f x1 = *reinterpret_cast<const v4f*>(src + 4);
 #pragma unroll
@@ -238,8 +225,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     // ---- online softmax; slot j <-> chunk row 16*(j/4) + 4*g + j%4
     uint32_t vmask;
     {
-      const int4 v0 = *reinterpret_cast<const int4*>(validw + (ch & 1) * kAttnWaves);
-      const int4 v1 = *reinterpret_cast<const int4*>(validw + (ch & 1) * kAttnWaves + 4);
+      const int4 v0 = *reinterpret_cast<const int4*>(validw + sl * kAttnWaves);
+      const int4 v1 = *reinterpret_cast<const int4*>(validw + sl * kAttnWaves + 4);
       vmask = static_cast<uint32_t>(v0.x) | (static_cast<uint32_t>(v0.y) << 4) | (static_cast<uint32_t>(v0.z) << 8) |
               (static_cast<uint32_t>(v0.w) << 12) | (static_cast<uint32_t>(v1.x) << 16) |
               (static_cast<uint32_t>(v1.y) << 20) | (static_cast<uint32_t>(v1.z) << 24) |
@@ -266,7 +253,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ah[i] = __shfl(alpha, 4 * g + i, kWave);
 #pragma unroll
-      for (int t = 0; t < kQuarter / 16; ++t)
+      for (int t = 0; t < Sh::kPart / 16; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[t][i] *= ah[i];
     }
@@ -291,10 +278,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
-    // ---- O_quarter += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
-    const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * kQuarter * quarter + 8 * (l & 3);
+    // ---- O_part += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
+    const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * Sh::kPart * part + 8 * (l & 3);
 #pragma unroll
-    for (int t = 0; t < kQuarter / 16; ++t) {
+    for (int t = 0; t < Sh::kPart / 16; ++t) {
       const v4s v0 = lds_read_tr16(vt + 32 * t);
       const v4s v1 = lds_read_tr16(vt + 32 * t + 16 * kRowStride);
       const v8s vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -303,27 +290,50 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     }
   };
 
+  // Pipeline over chunks c (ring slot c % 3, exchange buffer c % 2), two per loop trip (no
+  // exit between them, which keeps the compiler's load counts exact): iteration c forms the
+  // S^T share of chunk c+1, finishes chunk c (its shares were exchanged before the last
+  // barrier), moves chunk c+2 from registers into its slot and starts the loads of chunk
+  // c+4; one barrier per chunk.  Every iteration issues its four loads, also past the
+  // split's end (zero row), so the count of loads in flight is the same on every path
+  // and the compiler's waits before a store only cover the set being stored; stores past
+  // the end go to a slot no later step reads for a result.
   v4u stA0, stA1, stA2, stA3;
   v4u stB0, stB1, stB2, stB3;
   uint32_t vA = 0, vB = 0;
-  // Every chunk step issues its eight loads, also past the split's end (zero row), so the
-  // count of loads in flight is the same on every path and the compiler's waits before
-  // each store only cover the set being stored.
   CSA_ATT_LOAD(ch0, stA, vA);
   CSA_ATT_LOAD(ch0 + 1, stB, vB);
-  if (ch0 < ch1) CSA_ATT_STORE(ch0, stA, vA);
+  int sl = ch0 % kRing;                               // slot of chunk ch
+  const int sl1 = sl == kRing - 1 ? 0 : sl + 1;
+  CSA_ATT_STORE(sl, stA, vA);
   CSA_ATT_LOAD(ch0 + 2, stA, vA);
+  barrier_lds();
+  s_part(sl, ch0 & 1);
+  CSA_ATT_STORE(sl1, stB, vB);
+  CSA_ATT_LOAD(ch0 + 3, stB, vB);
+  barrier_lds();
 #pragma unroll 1
   for (int ch = ch0; ch < ch1; ch += 2) {
-    barrier_lds();                                  // chunk ch in slot ch&1; slot of ch-1 free
-    compute(ch);
-    if (ch + 1 < ch1) CSA_ATT_STORE(ch + 1, stB, vB);
-    CSA_ATT_LOAD(ch + 3, stB, vB);
-    if (ch + 1 >= ch1) break;
-    barrier_lds();
-    compute(ch + 1);
-    if (ch + 2 < ch1) CSA_ATT_STORE(ch + 2, stA, vA);
-    CSA_ATT_LOAD(ch + 4, stA, vA);
+    {
+      const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of ch + 1
+      const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of ch + 2
+      s_part(sn, (ch + 1) & 1);                         // past the split's end: unused
+      softmax_pv(sl, ch & 1);
+      CSA_ATT_STORE(s2, stA, vA);
+      CSA_ATT_LOAD(ch + 4, stA, vA);
+      barrier_lds();
+      sl = sn;
+    }
+    {                                                   // past ch1 (odd count): rows all absent, adds 0
+      const int sn = sl == kRing - 1 ? 0 : sl + 1;
+      const int s2 = sn == kRing - 1 ? 0 : sn + 1;
+      s_part(sn, ch & 1);
+      softmax_pv(sl, (ch + 1) & 1);
+      CSA_ATT_STORE(s2, stB, vB);
+      CSA_ATT_LOAD(ch + 5, stB, vB);
+      barrier_lds();
+      sl = sn;
+    }
   }
 #undef CSA_ATT_LOAD1
 #undef CSA_ATT_LOAD
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   float l_tot = l_run + wave_xor(l_run, 16);
   l_tot += wave_xor(l_tot, 32);
   const int head_l = kHG * hg + (l & 15);             // head whose statistics this lane holds
-  const int col0 = kQuarter * quarter + (l & 15);
+  const int col0 = Sh::kPart * part + (l & 15);
   if (a.nsplit == 1) {
     const float sink2 = a.sink[head_l] * kLog2e;
     const float M = fmaxf(m_ref, sink2);
@@ -348,26 +358,124 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       f = den > 0.0f ? em / den : 0.0f;
       lse2 = M + log2f(den);
     }
-    if (a.lse && quarter == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
+    if (a.lse && part == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
     float fh[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
     uint16_t* ob = a.out + (static_cast<size_t>(qi) * kAH + kHG * hg) * kAC;
 #pragma unroll
-    for (int t = 0; t < kQuarter / 16; ++t)
+    for (int t = 0; t < Sh::kPart / 16; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(o[t][i] * fh[i]);
   } else {
     const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
-    if (quarter == 0 && g == 0) {
+    if (part == 0 && g == 0) {
       a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_ref;
       a.part_ml[(pbase * kAH + head_l) * 2 + 1] = l_tot;
     }
-    float* po = a.part_o + (pbase * kAH + kHG * hg) * kAC;
+    // the partial in register order: [head group][16-channel tile][lane][4 heads], 16
+    // bytes per lane per store
+    float* po = a.part_o + ((pbase * kNHG + hg) * (kAC / 16) + Sh::kPart / 16 * part) * (kWave * 4) + 4 * l;
 #pragma unroll
-    for (int t = 0; t < kQuarter / 16; ++t)
+    for (int t = 0; t < Sh::kPart / 16; ++t) *reinterpret_cast<v4f*>(po + t * (kWave * 4)) = o[t];
+  }
+}
+
+// Combines the split partials of the bf16 kernel (register-order layout) with the sink.
+// One wave per (query, head group, 16-channel tile): lane l holds heads 16*hg + 4*(l/16)
+// + i and channel 16*ct + l%16, as the kernel's waves wrote them.  Blocks of 4 waves, 32
+// per query, numbered like the attention's workgroups so that a query's partials are
+// read on the XCD whose L2 received them.  Grid: ceil(B*S / 8) * 8 * 32 blocks.
+__global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict__ part_o,
+                                                        const float* __restrict__ part_ml,
+                                                        const float* __restrict__ sink, int nsplit, int nq,
+                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kBlocksPerQuery = kNHG * (kAC / 16) / 4;
+  int q, ub;
+  if (!attn_unit(nq, kBlocksPerQuery, q, ub)) return;
+  const size_t qi = q;
+  const int unit = 4 * ub + (threadIdx.x >> 6);
+  const int ct = unit % (kAC / 16);
+  const int hg = unit / (kAC / 16);
+  const int l = static_cast<int>(lane_id());
+  const int h0 = kHG * hg + 4 * (l >> 4);
+  float M[4], den[4], acc[4];
+  float sk[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) po[(4 * g + i) * kAC + col0 + 16 * t] = o[t][i];
+  for (int i = 0; i < 4; ++i) {
+    sk[i] = sink[h0 + i];
+    M[i] = sk[i] * kLog2e;
+    acc[i] = 0.0f;
+  }
+  // (m, l) of the lane's 4 heads: 32 contiguous bytes per split
+  auto ml_of = [&](int sp, v4f& a, v4f& b) __attribute__((always_inline)) {
+    const v4f* p = reinterpret_cast<const v4f*>(part_ml + ((qi * nsplit + sp) * kAH + h0) * 2);
+    a = p[0];                                                 // m0 l0 m1 l1
+    b = p[1];                                                 // m2 l2 m3 l3
+  };
+  auto po_of = [&](int sp) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v4f*>(part_o + (((qi * nsplit + sp) * kNHG + hg) * (kAC / 16) + ct) *
+                                                      (kWave * 4) + 4 * l);
+  };
+  if (nsplit <= 8) {
+    // every load in flight at once
+    v4f ma[8], mb[8], x[8];
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      if (sp < nsplit) {
+        ml_of(sp, ma[sp], mb[sp]);
+        x[sp] = po_of(sp);
+      }
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      if (sp < nsplit) {
+        M[0] = fmaxf(M[0], ma[sp][0]); M[1] = fmaxf(M[1], ma[sp][2]);
+        M[2] = fmaxf(M[2], mb[sp][0]); M[3] = fmaxf(M[3], mb[sp][2]);
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
+      if (sp < nsplit) {
+        const float mi[4] = {ma[sp][0], ma[sp][2], mb[sp][0], mb[sp][2]};
+        const float li[4] = {ma[sp][1], ma[sp][3], mb[sp][1], mb[sp][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
+          den[i] = fmaf(wgt, li[i], den[i]);
+          acc[i] = fmaf(wgt, x[sp][i], acc[i]);
+        }
+      }
+  } else {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      v4f a, b;
+      ml_of(sp, a, b);
+      M[0] = fmaxf(M[0], a[0]); M[1] = fmaxf(M[1], a[2]);
+      M[2] = fmaxf(M[2], b[0]); M[3] = fmaxf(M[3], b[2]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      v4f a, b;
+      ml_of(sp, a, b);
+      const v4f x = po_of(sp);
+      const float mi[4] = {a[0], a[2], b[0], b[2]};
+      const float li[4] = {a[1], a[3], b[1], b[3]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
+        den[i] = fmaf(wgt, li[i], den[i]);
+        acc[i] = fmaf(wgt, x[i], acc[i]);
+      }
+    }
+  }
+  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct + (l & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[i * kAC] = f32_to_bf16(den[i] > 0.0f ? acc[i] / den[i] : 0.0f);
+  if (lse && ct == 0 && (l & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
   }
 }
 
@@ -469,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
 // ------------------------------------------------------------------------------------
 // fp32 path (small shapes): one workgroup per (query, head); 256 slots per step, each
 // thread one slot's logit, then each thread accumulates channels.  Writes partials in
-// the same format as the bf16 kernel so attn_merge finishes it.
+// [query][head][channel] order, which attn_merge finishes.
 // ------------------------------------------------------------------------------------
 template <bool kDense>
 __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, const float* __restrict__ kv,
@@ -484,7 +592,7 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   const int qi = blockIdx.y, h = blockIdx.x;
   const int b = qi / S, s = qi % S;
   int w_lo, n_swa;
-  window_rows(s, S, Ls, W, w_lo, n_swa);
+  window_rows(s, S, Ls, W, last_position(q_pos, b, S), w_lo, n_swa);
   const int n_rem = kDense ? static_cast<int>(min(static_cast<int64_t>(Nc), (q_pos[qi] + 1) / m)) : k;
   const int n_slots = n_swa + n_rem;
   for (int i = threadIdx.x; i < c; i += 256) qv[i] = q[(static_cast<size_t>(qi) * H + h) * c + i];
@@ -547,14 +655,21 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
 }
 
-// Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (2 head-group
-// pairs x splits per query) to give every compute unit one, but every split keeps >= 4
-// chunks (128 rows): a split's partial result (32 heads x 512 fp32 = 64 KiB) must stay
-// small next to the rows it reads (1 KiB each).
+// Channel parts of the bf16 path for a call with nq queries.
+static int attn_parts(int nq) { return nq >= kHalvesMinQueries ? 2 : 4; }
+
+// Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (units per
+// query x splits) to give every compute unit one, but every split keeps >= 4 chunks (128
+// rows) per 32 heads it covers: a split's partial result (heads x 512 fp32, 2 KiB per
+// head) must stay small next to the rows it reads (1 KiB each).  The row table of a
+// split fits in LDS.
 int attn_nsplit(int nq, int max_rows) {
-  const int by_fill = cdiv(256, kNPair * nq);
-  const int by_rows = cdiv(max_rows, kRows) / 4;
-  const int by_lds = cdiv(cdiv(max_rows, kRows), kMaxSplitChunks);   // a split's row table fits LDS
+  const int units = nq >= kHalvesMinQueries ? AttnShape<2>::kUnits : AttnShape<4>::kUnits;
+  const int min_chunks = nq >= kHalvesMinQueries ? 8 : 4;
+  const int chunks = cdiv(max_rows, kRows);
+  const int by_fill = cdiv(256, units * nq);
+  const int by_rows = chunks / min_chunks;
+  const int by_lds = cdiv(chunks, kMaxSplitChunks);
   return std::max(by_lds, std::max(1, std::min(by_fill, by_rows)));
 }
 
@@ -563,6 +678,24 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
   const int ns = dtype == CSA_F32 ? 1 : attn_nsplit(static_cast<int>(nq), max_rows);
   if (dtype != CSA_F32 && ns == 1) return 0;
   return nq * ns * H * (static_cast<size_t>(c) + 2) * sizeof(float);
+}
+
+template <int kParts>
+static int launch_attn_bf16(bool dense, const AttnArgs& a, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
+    attr = true;
+  }
+  const dim3 grid(cdiv(a.nq, 8) * 8 * AttnShape<kParts>::kUnits * a.nsplit);
+  const int lds = kAttnLdsFixed + a.chunks_per_split * kRows * 8;
+  if (dense) hipLaunchKernelGGL((attn_bf16<true, kParts>), grid, dim3(kAttnThreads), lds, st, a);
+  else hipLaunchKernelGGL((attn_bf16<false, kParts>), grid, dim3(kAttnThreads), lds, st, a);
+  CSA_LAUNCH_CHECK();
+  return CSA_OK;
 }
 
 int launch_attention(bool dense, const void* q, const void* kv, const int32_t* idx, const int64_t* q_pos, int m,
@@ -584,28 +717,17 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     a.scale_log2 = scale_log2;
     a.nq = nq; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
     a.nsplit = ns;
-    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
+    a.chunks_per_split = 2 * cdiv(cdiv(max_rows, kRows), 2 * ns);   // even: the kernel steps two chunks
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     float* wsf = static_cast<float*>(ws);
     a.part_o = wsf;
     a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * H * c : nullptr;
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
-      attr = true;
-    }
-    const dim3 grid(cdiv(nq, 8) * 8 * kNPair * ns);
-    const int lds = kAttnLdsFixed + a.chunks_per_split * kRows * 8;
-    if (dense) hipLaunchKernelGGL(attn_bf16<true>, grid, dim3(kAttnThreads), lds, st, a);
-    else hipLaunchKernelGGL(attn_bf16<false>, grid, dim3(kAttnThreads), lds, st, a);
-    CSA_LAUNCH_CHECK();
+    const int rc = attn_parts(nq) == 2 ? launch_attn_bf16<2>(dense, a, st) : launch_attn_bf16<4>(dense, a, st);
+    if (rc != CSA_OK) return rc;
     if (ns > 1) {
-      hipLaunchKernelGGL(attn_merge<uint16_t>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, a.part_o, a.part_ml, sink,
-                         ns, H, c, nq * H, static_cast<uint16_t*>(out), lse);
+      hipLaunchKernelGGL(attn_merge_tiles, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st, a.part_o,
+                         a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
       CSA_LAUNCH_CHECK();
     }
     return CSA_OK;

@@ -21,7 +21,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     only enqueue work; they never synchronise and never allocate device memory.
  *     Scratch memory comes from the caller's `ws` buffer, sized by the matching
- *     *_workspace_size() query; ws may be NULL when that size is 0.
+ *     *_workspace_size() query and 16-byte aligned (hipMalloc gives 256); ws may
+ *     be NULL when that size is 0.
  *   - The library keeps no state between calls: calls on different streams with
  *     different buffers may run concurrently.  Two calls that share a workspace
  *     buffer must be ordered by the caller.
@@ -179,9 +180,13 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
  *
  *   q      [B,S,H,c]   dtype (CSA_BF16: H = 64, c = 512;  CSA_F32: H <= 64, c <= 512)
  *   kv_comp[B,Nc,c]    dtype;   idx [B,S,k] int32 in [-1, Nc), no duplicates.
+ *   q_pos  [B,S] int64 positions (consecutive within a sequence), or NULL.  Only the
+ *          window uses it: row r of swa holds position q_pos[b,S-1] - Ls + 1 + r, and
+ *          rows of negative positions (a sequence shorter than Ls) are left out.  NULL:
+ *          every row of swa is a real position.
  *   swa    [B,Ls,c]    dtype: raw KV of the Ls positions ending at the last query.
  *          Query s (of S consecutive queries) uses rows
- *          max(0, s+Ls-S-W+1) .. s+Ls-S  (positions t-W+1 .. t); requires Ls >= S.
+ *          max(0, s+Ls-S-W+1) .. s+Ls-S  (positions t-W+1 .. t, t >= 0); requires Ls >= S.
  *   sink   [H] fp32;  scale > 0 (normally 1/sqrt(c)).
  *   out    [B,S,H,c]   dtype;  lse [B,S,H] fp32 natural log, or NULL.
  *   ws >= csa_attn_workspace_size(...) bytes (split partial results).
@@ -189,7 +194,7 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
 size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dtype);
 
 int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
-                    const void* swa, const float* sink, int dtype, float scale,
+                    const int64_t* q_pos, const void* swa, const float* sink, int dtype, float scale,
                     int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
@@ -200,7 +205,7 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
  *
  * Same as csa_sparse_attn with the remote set of query (b,s) being the entries
  * j < min(Nc, floor((q_pos[b,s] + 1) / m)).  q_pos [B,S] int64, consecutive
- * positions within a sequence.  The workspace query takes max_rows = W + Nc.
+ * positions within a sequence (required; it also bounds the window as above).  The workspace query takes max_rows = W + Nc.
  * ------------------------------------------------------------------------------ */
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m,
                    const void* swa, const float* sink, int dtype, float scale,

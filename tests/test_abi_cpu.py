@@ -73,9 +73,9 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0,
                             fake, 8, None) == 3
     # attention: Ls < S, unsupported bf16 shape, non-positive scale
-    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
                                fake, None, None, 0, None) == 1
-    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128,
                                fake, None, None, 0, None) == 2
     assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128,
                               fake, None, None, 0, None) == 1

@@ -140,7 +140,7 @@ def test_topk_exact(lib, rows, Nc, k, kind, algo):
 # Stage 4: bf16 attention (CSA sparse and HCA dense)
 # ---------------------------------------------------------------------------------------
 
-def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=None):
+def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=None, pass_pos=False):
     Ls = S + W - 1
     a = I.attention_inputs(seed, B, S, Nc, Ls)
     if q_pos is None:
@@ -155,7 +155,7 @@ def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=Non
     else:
         idx = I.random_selection(seed, B, S, Nc, k, n_valid)
         lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(idx), dev_bf16(a["swa_bf16"]),
-                            dev(a["sink"]), W=W, out=out, lse=lse)
+                            dev(a["sink"]), W=W, out=out, lse=lse, q_pos=dev(q_pos) if pass_pos else None)
         o_ref, l_ref = O.sparse_attention(q_f, kv_f, idx, swa_f, a["sink"], 1 / math.sqrt(512), q_pos, W)
     torch.cuda.synchronize()
     assert_bf16_output(bf16_f64(host_bits(out)), o_ref, "attention output")
@@ -174,6 +174,36 @@ def test_sparse_attn_prefill_windows(lib):
 
 def test_sparse_attn_many_queries_single_split(lib):
     _attn_case(lib, B=8, S=64, Nc=600, k=96, W=128, seed=3, n_valid=90)
+
+
+def test_sparse_attn_full_channel_splits(lib):
+    # 64 queries: full-channel workgroups, 4 splits per query (merge); padded selections,
+    # one query with nothing selected (window rows and sink only)
+    n_valid = np.linspace(2048, 0, 64).astype(np.int64)[:, None]
+    _attn_case(lib, B=64, S=1, Nc=5000, k=2048, W=128, seed=7, n_valid=n_valid)
+
+
+def test_hca_dense_attn_full_channel_splits(lib):
+    # 64 queries over 2100 entries: full-channel workgroups, 4 splits; causal bounds from
+    # every entry down to none (query 63 sees window rows only)
+    q_pos = (128 * (2100 - 33 * np.arange(64)) - 1).astype(np.int64)[:, None]
+    q_pos[63, 0] = 100
+    _attn_case(lib, B=64, S=1, Nc=2100, k=0, W=128, seed=8, n_valid=0, dense=True, q_pos=q_pos)
+
+
+def test_sparse_attn_short_sequences(lib):
+    # sequences shorter than the window tensor (positions 0 .. t only): rows of negative
+    # positions are left out when q_pos is given; a sequence at position 0 sees one row
+    q_pos = np.array([[0], [50], [126], [127], [10 ** 6]], np.int64)
+    _attn_case(lib, B=5, S=1, Nc=300, k=64, W=128, seed=9, n_valid=np.array([[0], [3], [64], [64], [64]]),
+               q_pos=q_pos, pass_pos=True)
+
+
+def test_sparse_attn_short_prefill(lib):
+    # 70 consecutive queries from position 0: full-channel kernel, windows cut at position 0
+    q_pos = np.arange(70, dtype=np.int64)[None]
+    _attn_case(lib, B=1, S=70, Nc=40, k=16, W=128, seed=10, n_valid=np.minimum(np.arange(70) // 4, 16)[None],
+               q_pos=q_pos, pass_pos=True)
 
 
 def test_hca_dense_attn(lib):
