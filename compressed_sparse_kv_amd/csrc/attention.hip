@@ -205,8 +205,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   };
 
   // Chunk in ring slot SL whose S^T shares are in exchange buffer XB: online softmax and
-  // O_part += P . V.
-  auto softmax_pv = [&](int sl, int xb) __attribute__((always_inline)) {
+  // O_part += P . V; the S^T share of the next chunk (slot SN, buffer XN) is formed
+  // between the two, in the same basic block as the exponentials and P . V, so that its
+  // MFMAs can overlap them.
+  auto softmax_pv = [&](int sl, int xb, int sn, int xn) __attribute__((always_inline)) {
     const uint8_t* buf = ring + sl * kChunkBytes;
     float sv[8];
 #pragma unroll
@@ -278,6 +280,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
+    s_part(sn, xn);
     // ---- O_part += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
     const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * Sh::kPart * part + 8 * (l & 3);
 #pragma unroll
@@ -291,9 +294,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   };
 
   // Pipeline over chunks c (ring slot c % 3, exchange buffer c % 2), two per loop trip (no
-  // exit between them, which keeps the compiler's load counts exact): iteration c forms the
-  // S^T share of chunk c+1, finishes chunk c (its shares were exchanged before the last
-  // barrier), moves chunk c+2 from registers into its slot and starts the loads of chunk
+  // exit between them, which keeps the compiler's load counts exact): iteration c finishes
+  // chunk c (its shares were exchanged before the last barrier) and forms the S^T share of
+  // chunk c+1, moves chunk c+2 from registers into its slot and starts the loads of chunk
   // c+4; one barrier per chunk.  Every iteration issues its four loads, also past the
   // split's end (zero row), so the count of loads in flight is the same on every path
   // and the compiler's waits before a store only cover the set being stored; stores past
@@ -317,8 +320,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     {
       const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of ch + 1
       const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of ch + 2
-      s_part(sn, (ch + 1) & 1);                         // past the split's end: unused
-      softmax_pv(sl, ch & 1);
+      softmax_pv(sl, ch & 1, sn, (ch + 1) & 1);        // past the split's end: S^T unused
       CSA_ATT_STORE(s2, stA, vA);
       CSA_ATT_LOAD(ch + 4, stA, vA);
       barrier_lds();
@@ -327,8 +329,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     {                                                   // past ch1 (odd count): rows all absent, adds 0
       const int sn = sl == kRing - 1 ? 0 : sl + 1;
       const int s2 = sn == kRing - 1 ? 0 : sn + 1;
-      s_part(sn, ch & 1);
-      softmax_pv(sl, (ch + 1) & 1);
+      softmax_pv(sl, (ch + 1) & 1, sn, ch & 1);
       CSA_ATT_STORE(s2, stB, vB);
       CSA_ATT_LOAD(ch + 5, stB, vB);
       barrier_lds();
