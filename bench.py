@@ -103,8 +103,8 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
     copy_w = max(pick(wv, "copyBuffer"))
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
-    idx_f = pick(fv, "index_score_fp8_decode")
-    idx_w = pick(wv, "index_score_fp8_decode")
+    idx_f = pick(fv, "index_score_fp8_decode<false>")
+    idx_w = pick(wv, "index_score_fp8_decode<false>")
     fetch = sum(idx_f) / len(idx_f) * 1024.0 * f_scale
     write = sum(idx_w) / len(idx_w) * 1024.0 * w_scale
     src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", "index_score.hip")
@@ -129,7 +129,7 @@ def main():
     args = parse()
     if args.summarize_counters:
         base = "rocprofv3 --pmc {} --output-format csv -d <dir> -o run -- python3 bench.py --steps 5 --warmup 2 " \
-               "--no-prefill --no-cpu-baseline --calibrate-copy"
+               "--no-prefill --no-other --no-cpu-baseline --calibrate-copy"
         summarize_counters(*args.summarize_counters, base.format("FETCH_SIZE"), base.format("WRITE_SIZE"))
         return
     if args.gpus != 1:
@@ -167,23 +167,36 @@ def main():
     idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
     out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
     tk_ws = torch.empty(L.topk_workspace_size(B, Nc, k), dtype=torch.uint8, device=dev)
+    it_ws = torch.empty(L.index_topk_workspace_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
     at_ws_n = L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)
     at_ws = torch.empty(max(at_ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def step(i):
+        # one library call per stage: scores, top-k, attention
         s = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record(stream)
         L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
-        if ev is not None:
-            ev[1].record(stream)
         L.csa_topk(scores, k, idx, ws=tk_ws)
-        if ev is not None:
-            ev[2].record(stream)
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
-        if ev is not None:
-            ev[3].record(stream)
+
+    def step_fused(i):
+        # scores and top-k in one call (csa_index_topk), then the attention
+        s = sets[i % len(sets)]
+        L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+
+    def stage_step(i, ev):
+        # the same step as one call per stage, with events between the stages
+        s = sets[i % len(sets)]
+        ev[0].record(stream)
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        ev[1].record(stream)
+        L.csa_topk(scores, k, idx, ws=tk_ws)
+        ev[2].record(stream)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+        ev[3].record(stream)
+        L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
+        ev[4].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -204,6 +217,17 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / args.steps
+
+    # the same step with scores and top-k fused (informational; not `value`)
+    for i in range(args.warmup):
+        step_fused(i)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step_fused(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_fused = t0.elapsed_time(t1) / args.steps
 
     # graph: each input set's step captured once (same calls, same buffers) and replayed;
     # again exactly K steps between two synchronisations (reported beside the eager time)
@@ -226,12 +250,12 @@ def main():
         ms_graph = t0.elapsed_time(t1) / args.steps
     ms_per_step = ms_eager
 
-    # per-kernel durations (separate pass with events between the stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-stage durations (separate pass with events between the stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(i, evs[i])
+        stage_step(i, evs[i])
     torch.cuda.synchronize()
-    dur = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])
     us = dur.mean(axis=0) * 1e3
 
     # dominant kernel alone: back-to-back launches (rotating input sets) between two
@@ -260,6 +284,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "timing": "eager launches, one library call per stage",
+        "ms_per_step_fused_index_topk": ms_fused,
         "ms_per_step_graph": ms_graph,
         "higher_is_better": True,
         "scaling": "weak",
@@ -271,7 +296,8 @@ def main():
                    "indexer_dim": sh.d_I, "window": sh.W, "input_sets": args.sets},
         "hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
-        "stages_us": {"csa_index_score": us[0], "csa_topk": us[1], "csa_sparse_attn": us[2]},
+        "stages_us": {"csa_index_score": us[0], "csa_topk": us[1], "csa_sparse_attn": us[2],
+                      "csa_index_topk": us[3]},
         "roofline": {"kernel": "index_score_fp8_decode", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
@@ -336,17 +362,15 @@ def bench_csa_decode(torch, L, I, dev, sh, n_sets=2, reps=20):
                      "q8": up(a["qI_fp8"]), "qs": up(a["qI_scale"]), "w": up(a["w"])})
         del a
     B, Nc, k = sh.B, sh.n_c, sh.k
-    scores = torch.empty(B, 1, Nc, device=dev)
     idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
     out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
-    tk_ws = torch.empty(max(1, L.topk_workspace_size(B, Nc, k)), dtype=torch.uint8, device=dev)
+    it_ws = torch.empty(max(1, L.index_topk_workspace_size(B, 1, Nc, k)), dtype=torch.uint8, device=dev)
     at_ws = torch.empty(max(1, L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)), dtype=torch.uint8,
                         device=dev)
 
     def step(i):
         s = sets[i % len(sets)]
-        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
-        L.csa_topk(scores, k, idx, ws=tk_ws)
+        L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
 
     ms = _timed(torch, step, reps)

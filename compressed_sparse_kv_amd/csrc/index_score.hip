@@ -117,13 +117,19 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 // then written only when `scores` is not null.
 // ------------------------------------------------------------------------------------
 constexpr int kDecGroups = 8;                         // 64-entry groups per wave
-constexpr int kDecEntWG = 4 * 64 * kDecGroups;        // entries per workgroup
+// Waves per workgroup: 4 for scores alone (more workgroups for small grids), 8 with the
+// top-k epilogue (4096-entry segments: half the candidates for the row merge).
+template <bool kTopk> constexpr int dec_waves() { return kTopk ? 8 : 4; }
+template <bool kTopk> constexpr int dec_entries() { return dec_waves<kTopk>() * 64 * kDecGroups; }
 
 template <bool kTopk>
-__global__ __launch_bounds__(256) void index_score_fp8_decode(
+__global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decode(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
     int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand) {
+  constexpr int kDecWaves = dec_waves<kTopk>();
+  constexpr int kDecThreads = kDecWaves * 64;
+  constexpr int kDecEntWG = dec_entries<kTopk>();
   const size_t row = blockIdx.y;
   const int b = static_cast<int>(row / S);
   const int l = static_cast<int>(lane_id());
@@ -135,10 +141,10 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
   float* out = scores ? scores + row * Nc : nullptr;
 
-  // group gi of this wave covers entries base + 64*(gi*4 + wave) .. +63; the keys of
+  // group gi of this wave covers entries base + 64*(gi*kDecWaves + wave) .. +63; the keys of
   // the next two groups are in flight while a group is multiplied
   const int base = blockIdx.x * kDecEntWG;
-  auto group_e0 = [&](int gi) { return base + 64 * (gi * 4 + wave); };
+  auto group_e0 = [&](int gi) { return base + 64 * (gi * kDecWaves + wave); };
   auto group_live = [&](int gi) { const int e0 = group_e0(gi); return e0 < Nc && e0 < nvis; };
   v8i ring[3][4];
   float sring[3];            // row scale of entry e0 + l, fetched with the group's keys
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
     } else if (out && e < Nc) {
       out[e] = -INFINITY;
     }
-    if (kTopk) kst[64 * (gi * 4 + wave) + l] = key;
+    if (kTopk) kst[64 * (gi * kDecWaves + wave) + l] = key;
   }
 #undef CSA_DEC_LOAD
   if (kTopk) {
@@ -190,13 +196,14 @@ __global__ __launch_bounds__(256) void index_score_fp8_decode(
     for (int s2 = 0; s2 < 8; ++s2) key[0][s2] = kst[8 * threadIdx.x + s2];
     uint64_t taken;
     int obase[1];
-    const int kk = select_regs<256, 8, 1>(sh, key, ktop, taken, obase);
+    static_assert(kDecThreads * 8 == kDecEntWG, "8 keys per thread");
+    const int kk = select_regs<kDecThreads, 8, 1>(sh, key, ktop, taken, obase);
     uint2* dst = cand + (row * gridDim.x + blockIdx.x) * static_cast<size_t>(ktop);
     int o = obase[0];
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
       if ((taken >> s2) & 1ull) dst[o++] = make_uint2(key[0][s2], static_cast<uint32_t>(base + 8 * threadIdx.x + s2));
-    for (int p = kk + static_cast<int>(threadIdx.x); p < ktop; p += 256) dst[p] = make_uint2(0u, 0u);
+    for (int p = kk + static_cast<int>(threadIdx.x); p < ktop; p += kDecThreads) dst[p] = make_uint2(0u, 0u);
   }
 }
 
@@ -342,8 +349,8 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
                        int H_I, int d_I, int Nc, int m, float* scores, hipStream_t st) {
   if (dtype == CSA_FP8_E4M3) {
     if (S <= 4) {
-      dim3 grid(cdiv(Nc, kDecEntWG), B * S);
-      hipLaunchKernelGGL(index_score_fp8_decode<false>, grid, dim3(256), 0, st,
+      dim3 grid(cdiv(Nc, dec_entries<false>()), B * S);
+      hipLaunchKernelGGL(index_score_fp8_decode<false>, grid, dim3(dec_waves<false>() * 64), 0, st,
                          static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k),
                          k_scale, q_pos, S, Nc, m, scores, 0, nullptr);
     } else {
@@ -367,10 +374,10 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
 int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st);
 int topk_merge_supported(int G, int k);
 
-int index_topk_segments(int Nc) { return cdiv(Nc, kDecEntWG); }
+int index_topk_segments(int Nc) { return cdiv(Nc, dec_entries<true>()); }
 
 bool index_topk_fused_ok(int S, int Nc, int k) {
-  return S <= 4 && k <= kDecEntWG && topk_merge_supported(index_topk_segments(Nc), k);
+  return S <= 4 && k <= dec_entries<true>() && topk_merge_supported(index_topk_segments(Nc), k);
 }
 
 int launch_index_topk(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
@@ -379,7 +386,7 @@ int launch_index_topk(const void* q, const float* q_scale, const float* w, const
   const int G = index_topk_segments(Nc);
   uint2* cand = static_cast<uint2*>(ws);
   dim3 grid(G, B * S);
-  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(256), 0, st, static_cast<const uint8_t*>(q), q_scale,
+  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(dec_waves<true>() * 64), 0, st, static_cast<const uint8_t*>(q), q_scale,
                      w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc, m, scores, ktop, cand);
   CSA_LAUNCH_CHECK();
   return launch_topk_merge(cand, B * S, G, ktop, idx, st);

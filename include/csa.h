@@ -124,8 +124,8 @@ int csa_index_score(const void* q, const float* q_scale, const float* w,
 /* ------------------------------------------------------------------------------
  * Stages 2 and 3 in one call (FP8 inputs, H_I = 64, d_I = 128): the index scores of
  * csa_index_score and the selection of csa_topk, identical results.  For decode shapes
- * (S <= 4, ceil(Nc / 2048) * k <= 36864) the scoring pass also selects the top-k of each
- * 2048-entry segment while the scores are in registers, and one merge pass finishes the
+ * (S <= 4, ceil(Nc / 4096) * k <= 36864) the scoring pass also selects the top-k of each
+ * 4096-entry segment while the scores are in registers, and one merge pass finishes the
  * rows ([KV-COMP] section 9.4: the union of segment top-k sets holds the row's top-k);
  * other shapes run the two stages back to back.
  *   Arguments as csa_index_score and csa_topk (k = top-k, 1 <= k <= 2048);
