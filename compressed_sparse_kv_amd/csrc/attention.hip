@@ -42,6 +42,7 @@
 // of one query land on the same XCD (consecutive workgroup ids go round-robin over the
 // 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
+#include <type_traits>
 
 #include "attention_common.hpp"
 
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   // Chunk in ring slot SL whose S^T shares are in exchange buffer XB: online softmax and
   // O_part += P . V; the S^T share of the next chunk (slot SN, buffer XN) is formed
   // between the two, in the same basic block as the exponentials and P . V, so that its
-  // MFMAs can overlap them.
-  auto softmax_pv = [&](int sl, int xb, int sn, int xn) __attribute__((always_inline)) {
+  // MFMAs can overlap them (NEXT false: no next chunk).
+  auto softmax_pv = [&](int sl, int xb, int sn, int xn, auto next) __attribute__((always_inline)) {
     const uint8_t* buf = ring + sl * kChunkBytes;
     float sv[8];
 #pragma unroll
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
-    s_part(sn, xn);
+    if constexpr (decltype(next)::value) s_part(sn, xn);
     // ---- O_part += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
     const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * Sh::kPart * part + 8 * (l & 3);
 #pragma unroll
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   };
 
   // Pipeline over chunks c (ring slot c % 3, exchange buffer c % 2), two per loop trip (no
-  // exit between them, which keeps the compiler's load counts exact): iteration c finishes
+  // exit between them, which keeps the compiler's load counts exact; an odd last chunk is
+  // finished after the loop from what is already in LDS): iteration c finishes
   // chunk c (its shares were exchanged before the last barrier) and forms the S^T share of
   // chunk c+1, moves chunk c+2 from registers into its slot and starts the loads of chunk
   // c+4; one barrier per chunk.  Every iteration issues its four loads, also past the
@@ -315,27 +317,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   CSA_ATT_STORE(sl1, stB, vB);
   CSA_ATT_LOAD(ch0 + 3, stB, vB);
   barrier_lds();
+  int ch = ch0;
 #pragma unroll 1
-  for (int ch = ch0; ch < ch1; ch += 2) {
+  for (; ch + 1 < ch1; ch += 2) {
     {
       const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of ch + 1
       const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of ch + 2
-      softmax_pv(sl, ch & 1, sn, (ch + 1) & 1);        // past the split's end: S^T unused
+      softmax_pv(sl, ch & 1, sn, (ch + 1) & 1, std::true_type{});
       CSA_ATT_STORE(s2, stA, vA);
       CSA_ATT_LOAD(ch + 4, stA, vA);
       barrier_lds();
       sl = sn;
     }
-    {                                                   // past ch1 (odd count): rows all absent, adds 0
+    {
       const int sn = sl == kRing - 1 ? 0 : sl + 1;
       const int s2 = sn == kRing - 1 ? 0 : sn + 1;
-      softmax_pv(sl, (ch + 1) & 1, sn, ch & 1);
+      softmax_pv(sl, (ch + 1) & 1, sn, ch & 1, std::true_type{});   // past the split's end: S^T unused
       CSA_ATT_STORE(s2, stB, vB);
       CSA_ATT_LOAD(ch + 5, stB, vB);
       barrier_lds();
       sl = sn;
     }
   }
+  if (ch < ch1) softmax_pv(sl, ch & 1, sl, ch & 1, std::false_type{});
 #undef CSA_ATT_LOAD1
 #undef CSA_ATT_LOAD
 #undef CSA_ATT_STORE1
@@ -718,7 +722,7 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     a.scale_log2 = scale_log2;
     a.nq = nq; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
     a.nsplit = ns;
-    a.chunks_per_split = 2 * cdiv(cdiv(max_rows, kRows), 2 * ns);   // even: the kernel steps two chunks
+    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     float* wsf = static_cast<float*>(ws);
