@@ -62,6 +62,16 @@ def index_score_bytes(B, S, Nc, H_I, d_I):
     return B * S * per_query
 
 
+SEGMENT = 4096   # entries per segment of the scoring pass that also selects (csa_index_score_segments)
+
+
+def index_segments_bytes(B, S, Nc, H_I, d_I, k):
+    """Algorithmic HBM bytes of one scoring pass that keeps its scores on chip and writes
+    every segment's top-k: keys + scales, q + scale + w, position, (key, entry) pairs."""
+    per_query = Nc * (d_I + 4) + H_I * (d_I + 4 + 4) + 8 + -(-Nc // SEGMENT) * k * 8
+    return B * S * per_query
+
+
 def decode_step_bytes(sh):
     """Compulsory bytes of one decode step (the score/index round trip between stages excluded)."""
     B = sh.B
@@ -76,7 +86,7 @@ COPY_BYTES = 256 << 20
 
 
 def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
-    """Writes profiles/index_score_fp8_decode_flash_decode_b32_traffic.txt from the counter
+    """Writes profiles/index_score_segments_flash_decode_b32_traffic.txt from the counter
     CSVs: each counter of the indexer is scaled by what the same counter reads for the
     plain device copy of COPY_BYTES (read and written once)."""
     import csv
@@ -103,15 +113,16 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
     copy_w = max(pick(wv, "copyBuffer"))
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
-    idx_f = pick(fv, "index_score_fp8_decode<false>")
-    idx_w = pick(wv, "index_score_fp8_decode<false>")
+    idx_f = pick(fv, "index_score_fp8_decode<true>")
+    idx_w = pick(wv, "index_score_fp8_decode<true>")
     fetch = sum(idx_f) / len(idx_f) * 1024.0 * f_scale
     write = sum(idx_w) / len(idx_w) * 1024.0 * w_scale
     src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", "index_score.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    out = os.path.join(ROOT, "profiles", "index_score_fp8_decode_flash_decode_b32_traffic.txt")
+    out = os.path.join(ROOT, "profiles", "index_score_segments_flash_decode_b32_traffic.txt")
     with open(out, "w") as fo:
-        fo.write("# HBM traffic of index_score_fp8_decode, V4-Flash decode (B=32, 32768 entries), from\n")
+        fo.write("# HBM traffic of index_score_fp8_decode<true> (csa_index_score_segments), V4-Flash decode\n")
+        fo.write("# (B=32, 32768 entries, k=512, scores kept on chip), from\n")
         fo.write("# rocprofv3 counters; each counter scaled by its reading for a plain 256 MiB device copy.\n")
         fo.write(f"# fetch run: {cmd_fetch}\n# write run: {cmd_write}\n")
         fo.write(f"copy_fetch_kib = {copy_f:.1f}\ncopy_write_kib = {copy_w:.1f}\n")
@@ -120,7 +131,7 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
         fo.write(f"index_write_kib_per_dispatch = {sum(idx_w) / len(idx_w):.1f}  (n={len(idx_w)})\n")
         fo.write(f"traffic_fetch_bytes = {fetch:.0f}\ntraffic_write_bytes = {write:.0f}\n")
         fo.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
-        fo.write(f"algorithmic_bytes_per_launch = {index_score_bytes(32, 1, 32768, 64, 128)}\n")
+        fo.write(f"algorithmic_bytes_per_launch = {index_segments_bytes(32, 1, 32768, 64, 128, 512)}\n")
         fo.write(f"source_sha256 = {sha}\n")
     print(open(out).read())
 
@@ -172,31 +183,39 @@ def main():
     at_ws = torch.empty(max(at_ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    cand = torch.empty(L.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
+
+    def score_segments(s):
+        L.csa_index_score_segments(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, cand=cand)
+
     def step(i):
-        # one library call per stage: scores, top-k, attention
+        # scores with each 4096-entry segment's top-k, the per-row merge, the attention
+        s = sets[i % len(sets)]
+        score_segments(s)
+        L.csa_topk_merge(cand, B, 1, Nc, k, idx)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+
+    def step_separate(i):
+        # the same step with the scores written out and csa_topk over them
         s = sets[i % len(sets)]
         L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
         L.csa_topk(scores, k, idx, ws=tk_ws)
-        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
-
-    def step_fused(i):
-        # scores and top-k in one call (csa_index_topk), then the attention
-        s = sets[i % len(sets)]
-        L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
 
     def stage_step(i, ev):
-        # the same step as one call per stage, with events between the stages
+        # the step's calls with events between them, then the separate-stage calls
         s = sets[i % len(sets)]
         ev[0].record(stream)
-        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        score_segments(s)
         ev[1].record(stream)
-        L.csa_topk(scores, k, idx, ws=tk_ws)
+        L.csa_topk_merge(cand, B, 1, Nc, k, idx)
         ev[2].record(stream)
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
         ev[3].record(stream)
-        L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
         ev[4].record(stream)
+        L.csa_topk(scores, k, idx, ws=tk_ws)
+        ev[5].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -218,16 +237,16 @@ def main():
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / args.steps
 
-    # the same step with scores and top-k fused (informational; not `value`)
+    # the same step through csa_index_score + csa_topk (informational; not `value`)
     for i in range(args.warmup):
-        step_fused(i)
+        step_separate(i)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step_fused(i)
+        step_separate(i)
     t1.record(stream)
     torch.cuda.synchronize()
-    ms_fused = t0.elapsed_time(t1) / args.steps
+    ms_separate = t0.elapsed_time(t1) / args.steps
 
     # graph: each input set's step captured once (same calls, same buffers) and replayed;
     # again exactly K steps between two synchronisations (reported beside the eager time)
@@ -251,11 +270,11 @@ def main():
     ms_per_step = ms_eager
 
     # per-stage durations (separate pass with events between the stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for i in range(args.steps):
         stage_step(i, evs[i])
     torch.cuda.synchronize()
-    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])
+    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])
     us = dur.mean(axis=0) * 1e3
 
     # dominant kernel alone: back-to-back launches (rotating input sets) between two
@@ -266,13 +285,12 @@ def main():
     torch.cuda.synchronize()
     r0.record(stream)
     for i in range(n_rl):
-        s = sets[i % len(sets)]
-        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        score_segments(sets[i % len(sets)])
     r1.record(stream)
     torch.cuda.synchronize()
     is_us = r0.elapsed_time(r1) / n_rl * 1e3
 
-    isb = index_score_bytes(B, 1, Nc, sh.H_I, sh.d_I)
+    isb = index_segments_bytes(B, 1, Nc, sh.H_I, sh.d_I, k)
     achieved = isb / (is_us * 1e-6) / 1e9
     step_bytes = decode_step_bytes(sh)
     result = {
@@ -283,8 +301,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "timing": "eager launches, one library call per stage",
-        "ms_per_step_fused_index_topk": ms_fused,
+        "timing": "eager launches: csa_index_score_segments, csa_topk_merge, csa_sparse_attn",
+        "ms_per_step_separate_stages": ms_separate,
         "ms_per_step_graph": ms_graph,
         "higher_is_better": True,
         "scaling": "weak",
@@ -296,12 +314,12 @@ def main():
                    "indexer_dim": sh.d_I, "window": sh.W, "input_sets": args.sets},
         "hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
-        "stages_us": {"csa_index_score": us[0], "csa_topk": us[1], "csa_sparse_attn": us[2],
-                      "csa_index_topk": us[3]},
-        "roofline": {"kernel": "index_score_fp8_decode", "bound": "hbm", "achieved": achieved,
+        "stages_us": {"csa_index_score_segments": us[0], "csa_topk_merge": us[1], "csa_sparse_attn": us[2],
+                      "csa_index_score": us[3], "csa_topk": us[4]},
+        "roofline": {"kernel": "index_score_fp8_decode<true>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
-                     "traffic": measured_traffic("index_score.hip", "index_score_fp8_decode")},
+                     "traffic": measured_traffic("index_score.hip", "index_score_segments")},
         "input_generation_s": t_gen,
     }
 

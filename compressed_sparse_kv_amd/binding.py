@@ -27,6 +27,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "C
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
+           "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "hca_dense_attn")
 
@@ -52,6 +53,9 @@ def _load() -> ctypes.CDLL:
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
         "csa_index_topk_workspace_size": ([i, i, i, i], sz),
         "csa_index_topk": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "csa_index_segments_size": ([i, i, i, i], sz),
+        "csa_index_score_segments": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
+        "csa_topk_merge": ([vp, i, i, i, i, vp, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
@@ -173,6 +177,30 @@ def csa_index_topk(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, k: int, id
     _check("csa_index_topk", _lib.csa_index_topk(
         _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores), _p(idx),
         _p(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return idx
+
+
+def index_segments_size(B, S, Nc, k) -> int:
+    return int(_lib.csa_index_segments_size(B, S, Nc, k))
+
+
+def csa_index_score_segments(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, k: int, cand, scores=None,
+                             stream=None):
+    """Decode shapes: scores (when given) and every 4096-entry segment's top-k as (key, entry)
+    uint32 pairs in cand (a uint8 tensor of index_segments_size bytes)."""
+    _dev(q, q_scale, w, k_codes, k_scale, q_pos, cand, scores)
+    B, S, H, D = q.shape
+    Nc = k_codes.shape[1]
+    _check("csa_index_score_segments", _lib.csa_index_score_segments(
+        _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores),
+        _p(cand), cand.numel() * cand.element_size(), _stream(stream)))
+    return cand
+
+
+def csa_topk_merge(cand, B, S, Nc, k, idx, stream=None):
+    """idx [B,S,k] int32 = the k best of each row's segment candidates, as csa_topk returns them."""
+    _dev(cand, idx)
+    _check("csa_topk_merge", _lib.csa_topk_merge(_p(cand), B, S, Nc, k, _p(idx), _stream(stream)))
     return idx
 
 

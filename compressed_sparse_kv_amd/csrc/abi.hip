@@ -20,6 +20,9 @@ bool index_topk_fused_ok(int, int, int);
 int index_topk_segments(int);
 int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
                       int, int, int, float*, int32_t*, void*, hipStream_t);
+int launch_index_segments(const void*, const float*, const float*, const void*, const float*, const int64_t*, int,
+                          int, int, int, int, float*, uint2*, hipStream_t);
+int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
 }  // namespace csa
 
 using namespace csa;
@@ -130,6 +133,35 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w, const vo
   if (st != CSA_OK) return st;
   return launch_topk(sc, static_cast<int>(rows), Nc, k, idx, tk_bytes ? wsb : nullptr, tk_bytes, 0,
                      as_stream(stream));
+}
+
+size_t csa_index_segments_size(int B, int S, int Nc, int k) {
+  if (B <= 0 || S <= 0 || Nc <= 0 || k <= 0 || !index_topk_fused_ok(S, Nc, k)) return 0;
+  return static_cast<size_t>(B) * S * index_topk_segments(Nc) * k * sizeof(uint2);
+}
+
+int csa_index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
+                             const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
+                             int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream) {
+  CSA_REQUIRE(q && q_scale && w && k_codes && k_scale && q_pos && cand);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0 && k >= 1 && k <= 2048);
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
+  CSA_REQUIRE(aligned16(cand));
+  if (H_I != 64 || d_I != 128 || !index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
+  if (cand_bytes < csa_index_segments_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
+  return launch_index_segments(q, q_scale, w, k_codes, k_scale, q_pos, B, S, Nc, m, k, scores,
+                               static_cast<uint2*>(cand), as_stream(stream));
+}
+
+int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream) {
+  CSA_REQUIRE(cand && idx);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && k >= 1 && k <= 2048);
+  CSA_REQUIRE(static_cast<int64_t>(B) * S < (int64_t{1} << 31));
+  CSA_REQUIRE(aligned16(cand));
+  if (!index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
+  return launch_topk_merge(static_cast<const uint2*>(cand), B * S, index_topk_segments(Nc), k, idx,
+                           as_stream(stream));
 }
 
 // ---- stage 3 ------------------------------------------------------------------------

@@ -380,16 +380,25 @@ bool index_topk_fused_ok(int S, int Nc, int k) {
   return S <= 4 && k <= dec_entries<true>() && topk_merge_supported(index_topk_segments(Nc), k);
 }
 
+// Scores (optional) and every segment's top-k as (key, entry) pairs in cand[rows][G][k].
+int launch_index_segments(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
+                          const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, uint2* cand,
+                          hipStream_t st) {
+  dim3 grid(index_topk_segments(Nc), B * S);
+  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(dec_waves<true>() * 64), 0, st,
+                     static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc,
+                     m, scores, ktop, cand);
+  CSA_LAUNCH_CHECK();
+  return CSA_OK;
+}
+
 int launch_index_topk(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
                       const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, int32_t* idx,
                       void* ws, hipStream_t st) {
-  const int G = index_topk_segments(Nc);
   uint2* cand = static_cast<uint2*>(ws);
-  dim3 grid(G, B * S);
-  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(dec_waves<true>() * 64), 0, st, static_cast<const uint8_t*>(q), q_scale,
-                     w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc, m, scores, ktop, cand);
-  CSA_LAUNCH_CHECK();
-  return launch_topk_merge(cand, B * S, G, ktop, idx, st);
+  const int rc = launch_index_segments(q, q_scale, w, k, k_scale, q_pos, B, S, Nc, m, ktop, scores, cand, st);
+  if (rc != CSA_OK) return rc;
+  return launch_topk_merge(cand, B * S, index_topk_segments(Nc), ktop, idx, st);
 }
 
 }  // namespace csa

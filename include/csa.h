@@ -141,6 +141,30 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w,
                    float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * The fused path of csa_index_topk as two calls (decode shapes only: S <= 4,
+ * ceil(Nc / 4096) * k <= 36864, FP8, H_I = 64, d_I = 128; other shapes return
+ * CSA_ERR_UNSUPPORTED).  [KV-COMP] section 9.4: the row's top-k lies in the union of
+ * the top-k sets of its segments.
+ *
+ * csa_index_score_segments: the scores of csa_index_score (written when `scores` is not
+ *   NULL) and, for every 4096-entry segment g of row r, the k best entries of the
+ *   segment as pairs cand[r][g][j] = (key, entry) of two uint32: key = an
+ *   order-preserving image of the score (0 = empty slot: fewer than k candidates),
+ *   entries in ascending order.  cand: caller device memory of at least
+ *   csa_index_segments_size(B, S, Nc, k) bytes, 16-byte aligned.
+ * csa_topk_merge: idx [B,S,k] = the k best candidates of each row (key descending, then
+ *   lower entry), ascending, padded with -1: exactly csa_topk of the same scores.
+ * ------------------------------------------------------------------------------ */
+size_t csa_index_segments_size(int B, int S, int Nc, int k);
+
+int csa_index_score_segments(const void* q, const float* q_scale, const float* w,
+                             const void* k_codes, const float* k_scale, const int64_t* q_pos,
+                             int B, int S, int H_I, int d_I, int Nc, int m, int k,
+                             float* scores, void* cand, size_t cand_bytes, void* stream);
+
+int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 3: top-k selection.  [KV-COMP] sections 9.4 (S_t = TopK_k of the scores)
  * and 9.8 (invisible entries carry -inf and come out as -1).
  *

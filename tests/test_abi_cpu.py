@@ -72,6 +72,14 @@ def test_invalid_arguments_are_rejected_before_launch():
     # compressor workspace too small
     assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0,
                             fake, 8, None) == 3
+    # segment candidates: shape outside the decode path, candidate buffer too small, null idx
+    assert lib.csa_index_score_segments(fake, fake, fake, fake, fake, fake, 1, 8, 64, 128, 3000, 4, 128, None,
+                                        fake, 1 << 30, None) == 2
+    assert lib.csa_index_score_segments(fake, fake, fake, fake, fake, fake, 32, 1, 64, 128, 32768, 4, 512, None,
+                                        fake, 1024, None) == 3
+    assert lib.csa_topk_merge(fake, 32, 1, 32768, 512, None, None) == 1
+    assert lib.csa_index_segments_size(32, 1, 32768, 512) == 32 * 8 * 512 * 8
+    assert lib.csa_index_segments_size(1, 8, 3000, 128) == 0
     # attention: Ls < S, unsupported bf16 shape, non-positive scale
     assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
                                fake, None, None, 0, None) == 1

@@ -314,6 +314,8 @@ def test_decode_chain_graph_replay(lib):
     (1, 1, 3000, 2048, 4 * 3000 - 1, True),        # k above the visible count
     (2, 8, 3000, 128, 4 * 3000 + 40, True),        # prefill shape: the two stages back to back
     (1, 1, 262144, 1024, 4 * 262144 - 1, False),   # Pro shape: too many segment candidates, back to back
+    (32, 1, 32768, 512, 4 * 32768 - 1, False),     # V4-Flash decode batch
+    (2, 1, 20000, 512, 4 * 20000 - 1, True),       # five segments, the last ragged
 ])
 def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     a = I.indexer_inputs(B * 1000 + Nc + k, B, S, Nc)
@@ -330,6 +332,18 @@ def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     assert torch.equal(idx, idx_ref), "fused top-k differs from csa_index_score + csa_topk"
     if with_scores:
         assert torch.equal(sc, sc_ref), "fused scores differ from csa_index_score"
+    # the same path as two calls (segment candidates, then the merge), where it applies
+    nbytes = lib.index_segments_size(B, S, Nc, k)
+    if nbytes:
+        cand = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        sc2 = torch.empty(B, S, Nc, device="cuda") if with_scores else None
+        lib.csa_index_score_segments(*args, m=4, k=k, cand=cand, scores=sc2)
+        idx2 = torch.empty(B, S, k, dtype=torch.int32, device="cuda")
+        lib.csa_topk_merge(cand, B, S, Nc, k, idx2)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx_ref), "segments + merge differ from csa_index_score + csa_topk"
+        if with_scores:
+            assert torch.equal(sc2, sc_ref), "segment pass scores differ from csa_index_score"
     # and against the oracle, on the first query
     qI = O.dequant_rows(a["qI_fp8"][:1, :1], a["qI_scale"][:1, :1])
     KI = O.dequant_rows(a["kI_fp8"][:1], a["kI_scale"][:1])
