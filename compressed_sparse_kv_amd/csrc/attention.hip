@@ -423,13 +423,23 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
                                                       (kWave * 4) + 4 * l);
   };
   if (nsplit <= 8) {
-    // every load in flight at once
+    // every partial load in flight at once; the (m, l) of the block's 16 heads are read
+    // once per block into LDS (the 4 waves share the head group)
+    __shared__ v4f sml[8][kHG / 2];
     v4f ma[8], mb[8], x[8];
 #pragma unroll
     for (int sp = 0; sp < 8; ++sp)
+      if (sp < nsplit) x[sp] = po_of(sp);
+    if (static_cast<int>(threadIdx.x) < nsplit * (kHG / 2)) {
+      const int sp = threadIdx.x / (kHG / 2), j = threadIdx.x % (kHG / 2);
+      sml[sp][j] = *reinterpret_cast<const v4f*>(part_ml + ((qi * nsplit + sp) * kAH + kHG * hg) * 2 + 4 * j);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sp = 0; sp < 8; ++sp)
       if (sp < nsplit) {
-        ml_of(sp, ma[sp], mb[sp]);
-        x[sp] = po_of(sp);
+        ma[sp] = sml[sp][2 * (l >> 4)];
+        mb[sp] = sml[sp][2 * (l >> 4) + 1];
       }
 #pragma unroll
     for (int sp = 0; sp < 8; ++sp)

@@ -100,16 +100,19 @@ __global__ __launch_bounds__(kTkThreads) void topk_segments(const float* __restr
     int o = obase[u];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      if ((taken >> (4 * u + s)) & 1ull) {      // the key is read again (cached) to keep registers low
+      if ((taken >> (4 * u + s)) & 1ull) {
         const int p = kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s;
-        out[o++] = make_uint2(score_key(sr[p]), static_cast<uint32_t>(j0 + p));
+        // the largest register set reads its key again (cached) to stay within 128 VGPRs
+        const uint32_t kv = NU <= 4 ? key[u][s] : score_key(sr[p]);
+        out[o++] = make_uint2(kv, static_cast<uint32_t>(j0 + p));
       }
   }
   for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = make_uint2(0u, 0u);
 }
 
-// One workgroup per row over the n = G*k pairs of its segments (n <= NU * 4096).  Only
-// the keys are held in registers; the indices of the taken pairs are read again.
+// One workgroup per row over the n = G*k pairs of its segments (n <= NU * 4096).  The keys
+// and (up to four register chunks) their entry indices stay in registers from the one read
+// of the pairs; the largest set reads the indices of the taken pairs again.
 template <int NU>
 __global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict__ cand, int n, int k,
                                                          int32_t* __restrict__ idx) {
@@ -117,20 +120,23 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict
   const size_t row = blockIdx.x;
   const uint2* c = cand + row * static_cast<size_t>(n);
   const bool vec = (reinterpret_cast<uintptr_t>(c) & 15u) == 0;
-  uint32_t key[NU][4];
+  constexpr int NE = NU <= 4 ? NU : 1;                 // register chunks of entry indices
+  uint32_t key[NU][4], ent[NE][4];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     const int p = kTkChunk * u + 4 * static_cast<int>(threadIdx.x);
     if (vec && p + 3 < n) {
       const uint4 a = *reinterpret_cast<const uint4*>(c + p);
       const uint4 b = *reinterpret_cast<const uint4*>(c + p + 2);
-      key[u][0] = a.x;
-      key[u][1] = a.z;
-      key[u][2] = b.x;
-      key[u][3] = b.z;
+      key[u][0] = a.x; key[u][1] = a.z; key[u][2] = b.x; key[u][3] = b.z;
+      if (NU <= 4) { ent[u % NE][0] = a.y; ent[u % NE][1] = a.w; ent[u % NE][2] = b.y; ent[u % NE][3] = b.w; }
     } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) key[u][s] = p + s < n ? c[p + s].x : 0u;
+      for (int s = 0; s < 4; ++s) {
+        const uint2 v = p + s < n ? c[p + s] : make_uint2(0u, 0u);
+        key[u][s] = v.x;
+        if (NU <= 4) ent[u % NE][s] = v.y;
+      }
     }
   }
   uint64_t taken;
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       if ((taken >> (4 * u + s)) & 1ull)
-        out[o++] = static_cast<int32_t>(c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s].y);
+        out[o++] = static_cast<int32_t>(NU <= 4 ? ent[u % NE][s] : c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s].y);
   }
   for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
 }
