@@ -329,6 +329,7 @@ def main():
         result["pro_decode"] = bench_csa_decode(torch, L, I, dev, I.PRO_DECODE, n_sets=2)
         result["hca_decode"] = bench_hca_decode(torch, L, I, dev)
         result["prefill_compressor"] = bench_prefill_compressor(torch, L, I, dev)
+        result["prefill_attention"] = bench_prefill_attention(torch, L, I, dev)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_sets, sh)
@@ -414,6 +415,33 @@ def bench_hca_decode(torch, L, I, dev, reps=20):
     return {"workload": sh.name, "tokens_per_s": sh.B / (ms * 1e-3), "ms_per_step": ms, "bytes": byts,
             "hbm_gbs": byts / (ms * 1e-3) / 1e9, "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def bench_prefill_attention(torch, L, I, dev, reps=5):
+    """CSA attention over one prefill chunk: 8192 queries, each its 128-token window and
+    512 selected entries of the 32768 context entries (a seeded random selection)."""
+    sh = I.PREFILL
+    n_ctx = sh.ctx // sh.m
+    Ls = sh.S + sh.W - 1
+    a = I.attention_inputs(sh.seed + 7, 1, sh.S, n_ctx, Ls)
+    upb = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q, kv, swa, sink = upb(a["q_bf16"]), upb(a["kv_comp_bf16"]), upb(a["swa_bf16"]), up(a["sink"])
+    del a
+    g = torch.Generator(device=dev)
+    g.manual_seed(sh.seed + 8)
+    r = torch.rand(sh.S, n_ctx, generator=g, device=dev)
+    idx = r.topk(sh.k, dim=1).indices.sort(dim=1).values.to(torch.int32).view(1, sh.S, sh.k).contiguous()
+    del r
+    out = torch.empty(1, sh.S, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, L.attn_workspace_size(1, sh.S, sh.H, sh.c, sh.W + sh.k, L.CSA_BF16)), dtype=torch.uint8,
+                     device=dev)
+    ms = _timed(torch, lambda i: L.csa_sparse_attn(q, kv, idx, swa, sink, W=sh.W, out=out, ws=ws), reps)
+    flops = 4.0 * sh.S * sh.H * (sh.W + sh.k) * sh.c          # q.k and p.v over every row
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": "csa_prefill_chunk8192_attention_k512_w128", "ms": ms, "flops": flops,
+            "tflops": tflops, "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS,
+            "note": "P enters P.V as bf16 hi + lo: the MFMA work is 1.5x these flops"}
 
 
 def bench_prefill_compressor(torch, L, I, dev, reps=5):
