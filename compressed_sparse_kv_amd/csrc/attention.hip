@@ -387,30 +387,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
 }
 
 // Combines the split partials of the bf16 kernel (register-order layout) with the sink.
-// One wave per (query, head group, 16-channel tile): lane l holds heads 16*hg + 4*(l/16)
-// + i and channel 16*ct + l%16, as the kernel's waves wrote them.  Blocks of 4 waves, 32
-// per query, numbered like the attention's workgroups so that a query's partials are
-// read on the XCD whose L2 received them.  Grid: ceil(B*S / 8) * 8 * 32 blocks.
+// One wave per (query, head group, KT consecutive 16-channel tiles): lane l holds heads
+// 16*hg + 4*(l/16) + i and channel 16*ct + l%16 of each tile, as the kernel's waves wrote
+// them.  KT = 4 (few splits: every load of the wave in flight at once) or 1.  Blocks of 4
+// waves, numbered like the attention's workgroups so that a query's partials are read on
+// the XCD whose L2 received them.  Grid: ceil(B*S / 8) * 8 * (128 / KT / 4) blocks.
+template <int KT>
 __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         const float* __restrict__ sink, int nsplit, int nq,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int kBlocksPerQuery = kNHG * (kAC / 16) / 4;
+  constexpr int kTiles = kAC / 16;
+  constexpr int kBlocksPerQuery = kNHG * kTiles / KT / 4;
+  constexpr int kMaxFast = KT == 1 ? 8 : 4;             // splits held in registers at once
   int q, ub;
   if (!attn_unit(nq, kBlocksPerQuery, q, ub)) return;
   const size_t qi = q;
   const int unit = 4 * ub + (threadIdx.x >> 6);
-  const int ct = unit % (kAC / 16);
-  const int hg = unit / (kAC / 16);
+  const int ct0 = KT * (unit % (kTiles / KT));
+  const int hg = unit / (kTiles / KT);
   const int l = static_cast<int>(lane_id());
   const int h0 = kHG * hg + 4 * (l >> 4);
-  float M[4], den[4], acc[4];
+  float M[4], den[4], acc[KT][4];
   float sk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sk[i] = sink[h0 + i];
     M[i] = sk[i] * kLog2e;
-    acc[i] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) acc[t][i] = 0.0f;
   }
   // (m, l) of the lane's 4 heads: 32 contiguous bytes per split
   auto ml_of = [&](int sp, v4f& a, v4f& b) __attribute__((always_inline)) {
@@ -418,31 +423,33 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
     a = p[0];                                                 // m0 l0 m1 l1
     b = p[1];                                                 // m2 l2 m3 l3
   };
-  auto po_of = [&](int sp) __attribute__((always_inline)) {
-    return *reinterpret_cast<const v4f*>(part_o + (((qi * nsplit + sp) * kNHG + hg) * (kAC / 16) + ct) *
-                                                      (kWave * 4) + 4 * l);
+  auto po_of = [&](int sp, int ct) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v4f*>(part_o + (((qi * nsplit + sp) * kNHG + hg) * kTiles + ct) * (kWave * 4) +
+                                         4 * l);
   };
-  if (nsplit <= 8) {
+  if (nsplit <= kMaxFast) {
     // every partial load in flight at once; the (m, l) of the block's 16 heads are read
     // once per block into LDS (the 4 waves share the head group)
-    __shared__ v4f sml[8][kHG / 2];
-    v4f ma[8], mb[8], x[8];
+    __shared__ v4f sml[kMaxFast][kHG / 2];
+    v4f ma[kMaxFast], mb[kMaxFast], x[kMaxFast][KT];
 #pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
-      if (sp < nsplit) x[sp] = po_of(sp);
+    for (int sp = 0; sp < kMaxFast; ++sp)
+      if (sp < nsplit)
+#pragma unroll
+        for (int t = 0; t < KT; ++t) x[sp][t] = po_of(sp, ct0 + t);
     if (static_cast<int>(threadIdx.x) < nsplit * (kHG / 2)) {
       const int sp = threadIdx.x / (kHG / 2), j = threadIdx.x % (kHG / 2);
       sml[sp][j] = *reinterpret_cast<const v4f*>(part_ml + ((qi * nsplit + sp) * kAH + kHG * hg) * 2 + 4 * j);
     }
     __syncthreads();
 #pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
+    for (int sp = 0; sp < kMaxFast; ++sp)
       if (sp < nsplit) {
         ma[sp] = sml[sp][2 * (l >> 4)];
         mb[sp] = sml[sp][2 * (l >> 4) + 1];
       }
 #pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
+    for (int sp = 0; sp < kMaxFast; ++sp)
       if (sp < nsplit) {
         M[0] = fmaxf(M[0], ma[sp][0]); M[1] = fmaxf(M[1], ma[sp][2]);
         M[2] = fmaxf(M[2], mb[sp][0]); M[3] = fmaxf(M[3], mb[sp][2]);
@@ -450,7 +457,7 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
 #pragma unroll
-    for (int sp = 0; sp < 8; ++sp)
+    for (int sp = 0; sp < kMaxFast; ++sp)
       if (sp < nsplit) {
         const float mi[4] = {ma[sp][0], ma[sp][2], mb[sp][0], mb[sp][2]};
         const float li[4] = {ma[sp][1], ma[sp][3], mb[sp][1], mb[sp][3]};
@@ -458,7 +465,8 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
         for (int i = 0; i < 4; ++i) {
           const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
           den[i] = fmaf(wgt, li[i], den[i]);
-          acc[i] = fmaf(wgt, x[sp][i], acc[i]);
+#pragma unroll
+          for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[sp][t][i], acc[t][i]);
         }
       }
   } else {
@@ -473,21 +481,26 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
     for (int sp = 0; sp < nsplit; ++sp) {
       v4f a, b;
       ml_of(sp, a, b);
-      const v4f x = po_of(sp);
+      v4f x[KT];
+#pragma unroll
+      for (int t = 0; t < KT; ++t) x[t] = po_of(sp, ct0 + t);
       const float mi[4] = {a[0], a[2], b[0], b[2]};
       const float li[4] = {a[1], a[3], b[1], b[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
         den[i] = fmaf(wgt, li[i], den[i]);
-        acc[i] = fmaf(wgt, x[i], acc[i]);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[t][i], acc[t][i]);
       }
     }
   }
-  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct + (l & 15);
+  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct0 + (l & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i * kAC] = f32_to_bf16(den[i] > 0.0f ? acc[i] / den[i] : 0.0f);
-  if (lse && ct == 0 && (l & 15) == 0) {
+  for (int t = 0; t < KT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f);
+  if (lse && ct0 == 0 && (l & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
@@ -741,8 +754,12 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     const int rc = attn_parts(nq) == 2 ? launch_attn_bf16<2>(dense, a, st) : launch_attn_bf16<4>(dense, a, st);
     if (rc != CSA_OK) return rc;
     if (ns > 1) {
-      hipLaunchKernelGGL(attn_merge_tiles, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st, a.part_o,
-                         a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
+      if (ns <= 4)
+        hipLaunchKernelGGL(attn_merge_tiles<4>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 16)), dim3(256), 0, st,
+                           a.part_o, a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
+      else
+        hipLaunchKernelGGL(attn_merge_tiles<1>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st,
+                           a.part_o, a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
       CSA_LAUNCH_CHECK();
     }
     return CSA_OK;

@@ -280,27 +280,37 @@ def test_decode_chain_graph_replay(lib):
     at_ws = torch.empty(max(1, lib.attn_workspace_size(B, 1, 64, 512, W + k, lib.CSA_BF16)), dtype=torch.uint8,
                         device="cuda")
 
+    cand = torch.empty(lib.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device="cuda")
+
     def step():
         lib.csa_index_score(q8, qs, w, k8, ks, qpos, m=m, scores=scores)
         lib.csa_topk(scores, k, idx, ws=tk_ws)
         lib.csa_sparse_attn(q, kv, idx, swa, sink, W=W, out=out, ws=at_ws)
 
+    def step_segments():
+        lib.csa_index_score_segments(q8, qs, w, k8, ks, qpos, m=m, k=k, cand=cand, scores=scores)
+        lib.csa_topk_merge(cand, B, 1, Nc, k, idx)
+        lib.csa_sparse_attn(q, kv, idx, swa, sink, W=W, out=out, ws=at_ws)
+
     step()
     torch.cuda.synchronize()
     ref = (scores.clone(), idx.clone(), out.clone())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
-    for r in range(3):
-        scores.fill_(7.0)
-        idx.fill_(-7)
-        out.zero_()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(scores, ref[0]), f"scores differ on replay {r}"
-        assert torch.equal(idx, ref[1]), f"indices differ on replay {r}"
-        assert torch.equal(out, ref[2]), f"attention differs on replay {r}"
+    for fn in (step, step_segments):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for r in range(3):
+            scores.fill_(7.0)
+            idx.fill_(-7)
+            out.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(scores, ref[0]), f"{fn.__name__}: scores differ on replay {r}"
+            assert torch.equal(idx, ref[1]), f"{fn.__name__}: indices differ on replay {r}"
+            assert torch.equal(out, ref[2]), f"{fn.__name__}: attention differs on replay {r}"
+            fn()                                   # eager work between the replays
+            torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------------------------------
