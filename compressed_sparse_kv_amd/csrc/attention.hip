@@ -48,26 +48,35 @@
 
 namespace csa {
 
-constexpr int kAttnWaves = 8;
-constexpr int kAttnThreads = kAttnWaves * 64;
-constexpr int kRowsPerWave = 32 / kAttnWaves;       // rows of a chunk each wave loads
-static_assert(kRowsPerWave == 4, "the row staging macros move 4 rows per wave");
-
-// Workgroup shape for kParts channel parts per head group (4: quarters, 2: halves).
-template <int kParts>
-struct AttnShape {
-  static constexpr int kPart = kAC / kParts;        // channels per wave
-  static constexpr int kWGHG = kAttnWaves / kParts; // head groups per workgroup
-  static constexpr int kUnits = kNHG / kWGHG;       // workgroups per (query, split)
-};
-// channel halves once a call has this many queries
-constexpr int kHalvesMinQueries = 64;
 constexpr int kRing = 3;                            // chunks resident in LDS
-constexpr int kSxBytes = kAttnWaves * kWave * 8 * 4;  // one buffer of S^T shares
 constexpr int kValidSlots = 4;                      // row-mask slots (kRing, padded)
-constexpr int kAttnLdsFixed = kRing * kChunkBytes + 2 * kSxBytes + kValidSlots * kAttnWaves * 4;
-constexpr int kAttnLdsMax = kAttnLdsFixed + kMaxSplitChunks * kRows * 8;
-static_assert(kAttnLdsMax <= 160 * 1024, "LDS of one compute unit");
+
+// Workgroup shape: kWaves waves = (head group, channel part) pairs with kParts channel
+// parts per head group (4: quarters, 2: halves).
+template <int kParts, int kWaves>
+struct AttnShape {
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kRowsPerWave = kRows / kWaves;   // rows of a chunk each wave loads
+  static constexpr int kPart = kAC / kParts;            // channels per wave
+  static constexpr int kWGHG = kWaves / kParts;         // head groups per workgroup
+  static constexpr int kUnits = kNHG / kWGHG;           // workgroups per (query, split)
+  // S^T share buffers: two (shares of chunk c+1 formed while chunk c's are read, one
+  // barrier per chunk) when they fit next to the ring, else one and a second barrier
+  static constexpr int kSxBytes = kWaves * kWave * 8 * 4;
+  static constexpr int kSxBufs = kWaves <= 8 ? 2 : 1;
+  static constexpr int kLdsFixed = kRing * kChunkBytes + kSxBufs * kSxBytes + kValidSlots * kWaves * 4;
+  static constexpr int kLdsMax = kLdsFixed + kMaxSplitChunks * kRows * 8;
+  static_assert(kLdsMax <= 160 * 1024, "LDS of one compute unit");
+  static_assert(kRowsPerWave == 4 || kRowsPerWave == 2, "the row staging moves 4 or 2 rows per wave");
+  static_assert(kWGHG >= 1 && kWGHG <= kNHG, "head groups per workgroup");
+};
+// the 64-head shape (all head groups in one workgroup) once a call has this many queries:
+// 8 waves = 4 head groups x channel halves.  (16 waves x channel quarters fits 128 VGPRs
+// for 4 waves per SIMD, but the 4-way share exchange, the second barrier and spills made
+// HCA decode 1.3x slower.)
+constexpr int kWideMinQueries = 64;
+constexpr int kWideParts = 2;
+constexpr int kWideWaves = 8;
 
 // Source of the rows that are absent (index -1, padding, chunks past a split's end):
 // every chunk is the same loads per wave, so the compiler's count of loads in flight is
@@ -77,14 +86,14 @@ static_assert(kAttnLdsMax <= 160 * 1024, "LDS of one compute unit");
 constexpr int kZeroRows = 64;
 __device__ __attribute__((aligned(1024))) uint16_t g_zero_rows[kZeroRows * kAC];
 
-template <bool kDense, int kParts>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
-  using Sh = AttnShape<kParts>;
+template <bool kDense, int kParts, int kWaves>
+__global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
+  using Sh = AttnShape<kParts, kWaves>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* ring = smem;                                                          // [slot][32 rows]
   float* sx = reinterpret_cast<float*>(smem + kRing * kChunkBytes);              // [buffer][wave][lane][8]
-  int* validw = reinterpret_cast<int*>(smem + kRing * kChunkBytes + 2 * kSxBytes);   // [slot][wave]: row masks
-  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kValidSlots * kAttnWaves);  // the split's row addresses
+  int* validw = reinterpret_cast<int*>(smem + kRing * kChunkBytes + Sh::kSxBufs * Sh::kSxBytes);  // [slot][wave]
+  uint64_t* rowptr = reinterpret_cast<uint64_t*>(validw + kValidSlots * kWaves);  // the split's row addresses
 
   // ---- workgroup -> (query, head groups, split)
   int qi, u;
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   const uint64_t zero_rows = reinterpret_cast<uint64_t>(static_cast<const uint16_t*>(g_zero_rows));
   {
     const int nsl = (ch1 - ch0) * kRows;
-    for (int e = static_cast<int>(threadIdx.x); e < nsl; e += kAttnThreads) {
+    for (int e = static_cast<int>(threadIdx.x); e < nsl; e += Sh::kThreads) {
       const int slot = ch0 * kRows + e;
       uint64_t p = (zero_rows + static_cast<uint64_t>(e % kZeroRows) * (kAC * 2)) | 1u;
       if (slot < n_swa) {
@@ -141,8 +150,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     __syncthreads();
   }
 
-  // The wave's 4 rows of chunk CH (zero rows for chunks past the split): addresses from
-  // the table with two 16-byte LDS reads, then one 16-byte load per lane per row.
+  // The wave's 4 (or 2) rows of chunk CH (zero rows for chunks past the split): addresses
+  // from the table with 16-byte LDS reads, then one 16-byte load per lane per row.
 #define CSA_ATT_LOAD1(ST, VM, R, PTR)                                                   \
   do {                                                                                 \
     const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
@@ -154,13 +163,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
   do {                                                                                 \
     uint64_t q_[4];                                                                    \
     if ((CH) < ch1) {                                                                  \
-      const uint64_t* t_ = rowptr + ((CH) - ch0) * kRows + kRowsPerWave * wave;        \
+      const uint64_t* t_ = rowptr + ((CH) - ch0) * kRows + Sh::kRowsPerWave * wave;    \
       const ulonglong2 a_ = reinterpret_cast<const ulonglong2*>(t_)[0];                 \
-      const ulonglong2 b_ = reinterpret_cast<const ulonglong2*>(t_)[1];                 \
-      q_[0] = a_.x; q_[1] = a_.y; q_[2] = b_.x; q_[3] = b_.y;                          \
+      q_[0] = a_.x; q_[1] = a_.y;                                                      \
+      if constexpr (Sh::kRowsPerWave == 4) {                                           \
+        const ulonglong2 b_ = reinterpret_cast<const ulonglong2*>(t_)[1];               \
+        q_[2] = b_.x; q_[3] = b_.y;                                                    \
+      }                                                                                \
     } else {                                                                           \
       const uint64_t z_ = zero_rows | 1u;                                              \
-      const int r_ = ((CH) * kRows + kRowsPerWave * wave) & (kZeroRows - 1);           \
+      const int r_ = ((CH) * kRows + Sh::kRowsPerWave * wave) & (kZeroRows - 1);       \
       q_[0] = z_ + static_cast<uint64_t>(r_) * (kAC * 2);                              \
       q_[1] = z_ + static_cast<uint64_t>(r_ + 1) * (kAC * 2);                          \
       q_[2] = z_ + static_cast<uint64_t>(r_ + 2) * (kAC * 2);                          \
@@ -168,16 +180,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     }                                                                                  \
     (VM) = 0;                                                                          \
     CSA_ATT_LOAD1(ST, VM, 0, q_[0]); CSA_ATT_LOAD1(ST, VM, 1, q_[1]);                  \
-    CSA_ATT_LOAD1(ST, VM, 2, q_[2]); CSA_ATT_LOAD1(ST, VM, 3, q_[3]);                  \
+    if constexpr (Sh::kRowsPerWave == 4) {                                             \
+      CSA_ATT_LOAD1(ST, VM, 2, q_[2]); CSA_ATT_LOAD1(ST, VM, 3, q_[3]);                \
+    }                                                                                  \
   } while (0)
 #define CSA_ATT_STORE1(BUF, ST, R) \
-  *reinterpret_cast<v4u*>((BUF) + (kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R
+  *reinterpret_cast<v4u*>((BUF) + (Sh::kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R
 #define CSA_ATT_STORE(SLOT, ST, VM)                                                     \
   do {                                                                                 \
     uint8_t* buf_ = ring + (SLOT) * kChunkBytes;                                       \
     CSA_ATT_STORE1(buf_, ST, 0); CSA_ATT_STORE1(buf_, ST, 1);                          \
-    CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                          \
-    if (l == 0) validw[(SLOT) * kAttnWaves + wave] = static_cast<int>(VM);             \
+    if constexpr (Sh::kRowsPerWave == 4) {                                             \
+      CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                        \
+    }                                                                                  \
+    if (l == 0) validw[(SLOT) * kWaves + wave] = static_cast<int>(VM);                 \
   } while (0)
 
   v4f o[Sh::kPart / 16];
@@ -200,7 +216,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
         st[rb] = mfma_bf16_16x16x32(av, qb[ks], st[rb]);
       }
     }
-    float* w = sx + xb * (kSxBytes / 4) + (wave * kWave + l) * 8;
+    float* w = sx + (xb & (Sh::kSxBufs - 1)) * (Sh::kSxBytes / 4) + (wave * kWave + l) * 8;
     *reinterpret_cast<v4f*>(w) = st[0];
     *reinterpret_cast<v4f*>(w + 4) = st[1];
   };
@@ -216,7 +232,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
     for (int j = 0; j < 8; ++j) sv[j] = 0.0f;
 #pragma unroll
     for (int w = 0; w < kParts; ++w) {                // fixed order: identical sums in the group's waves
-      const float* src = sx + xb * (kSxBytes / 4) + ((wave & ~(kParts - 1)) + w) * kWave * 8 + l * 8;
+      const float* src = sx + (xb & (Sh::kSxBufs - 1)) * (Sh::kSxBytes / 4) + ((wave & ~(kParts - 1)) + w) * kWave * 8 +
+                         l * 8;
       const v4f x0 = *reinterpret_cast<const v4f*>(src);
       const v4f x1 = *reinterpret_cast<const v4f*>(src + 4);
 #pragma unroll
@@ -226,14 +243,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       }
     }
     // ---- online softmax; slot j <-> chunk row 16*(j/4) + 4*g + j%4
-    uint32_t vmask;
-    {
-      const int4 v0 = *reinterpret_cast<const int4*>(validw + sl * kAttnWaves);
-      const int4 v1 = *reinterpret_cast<const int4*>(validw + sl * kAttnWaves + 4);
-      vmask = static_cast<uint32_t>(v0.x) | (static_cast<uint32_t>(v0.y) << 4) | (static_cast<uint32_t>(v0.z) << 8) |
-              (static_cast<uint32_t>(v0.w) << 12) | (static_cast<uint32_t>(v1.x) << 16) |
-              (static_cast<uint32_t>(v1.y) << 20) | (static_cast<uint32_t>(v1.z) << 24) |
-              (static_cast<uint32_t>(v1.w) << 28);
+    uint32_t vmask = 0;
+#pragma unroll
+    for (int w4 = 0; w4 < kWaves / 4; ++w4) {               // the waves' row masks, in row order
+      constexpr int R = Sh::kRowsPerWave;
+      const int4 v = *reinterpret_cast<const int4*>(validw + sl * kWaves + 4 * w4);
+      vmask |= (static_cast<uint32_t>(v.x) << (R * (4 * w4))) | (static_cast<uint32_t>(v.y) << (R * (4 * w4 + 1))) |
+               (static_cast<uint32_t>(v.z) << (R * (4 * w4 + 2))) | (static_cast<uint32_t>(v.w) << (R * (4 * w4 + 3)));
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -281,7 +297,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16(AttnArgs a) {
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
-    if constexpr (decltype(next)::value) s_part(sn, xn);
+    if constexpr (decltype(next)::value) {
+      if constexpr (Sh::kSxBufs == 1) barrier_lds();     // every wave has read the one share buffer
+      s_part(sn, xn);
+    }
     // ---- O_part += P . V; lane (g, i) reads row 4g + i/4 (and 16 + ...) at columns 4*(i%4) ..
     const uint8_t* vt = buf + (4 * g + ((l & 15) >> 2)) * kRowStride + 2 * Sh::kPart * part + 8 * (l & 3);
 #pragma unroll
@@ -683,8 +702,12 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
   }
 }
 
-// Channel parts of the bf16 path for a call with nq queries.
-static int attn_parts(int nq) { return nq >= kHalvesMinQueries ? 2 : 4; }
+// The two shapes of the bf16 path: few queries -> 8 waves over 2 head groups x channel
+// quarters (two workgroups per query: more workgroups); many queries -> all 64 heads in one
+// workgroup (every row read serves 64 heads).
+using NarrowShape = AttnShape<4, 8>;
+using WideShape = AttnShape<kWideParts, kWideWaves>;
+static bool attn_wide(int nq) { return nq >= kWideMinQueries; }
 
 // Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (units per
 // query x splits) to give every compute unit one, but every split keeps >= 4 chunks (128
@@ -692,8 +715,8 @@ static int attn_parts(int nq) { return nq >= kHalvesMinQueries ? 2 : 4; }
 // head) must stay small next to the rows it reads (1 KiB each).  The row table of a
 // split fits in LDS.
 int attn_nsplit(int nq, int max_rows) {
-  const int units = nq >= kHalvesMinQueries ? AttnShape<2>::kUnits : AttnShape<4>::kUnits;
-  const int min_chunks = nq >= kHalvesMinQueries ? 8 : 4;
+  const int units = attn_wide(nq) ? WideShape::kUnits : NarrowShape::kUnits;
+  const int min_chunks = attn_wide(nq) ? 8 : 4;
   const int chunks = cdiv(max_rows, kRows);
   const int by_fill = cdiv(256, units * nq);
   const int by_rows = chunks / min_chunks;
@@ -708,20 +731,21 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
   return nq * ns * H * (static_cast<size_t>(c) + 2) * sizeof(float);
 }
 
-template <int kParts>
+template <int kParts, int kWaves>
 static int launch_attn_bf16(bool dense, const AttnArgs& a, hipStream_t st) {
+  using Sh = AttnShape<kParts, kWaves>;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kAttnLdsMax);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts, kWaves>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts, kWaves>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax);
     attr = true;
   }
-  const dim3 grid(cdiv(a.nq, 8) * 8 * AttnShape<kParts>::kUnits * a.nsplit);
-  const int lds = kAttnLdsFixed + a.chunks_per_split * kRows * 8;
-  if (dense) hipLaunchKernelGGL((attn_bf16<true, kParts>), grid, dim3(kAttnThreads), lds, st, a);
-  else hipLaunchKernelGGL((attn_bf16<false, kParts>), grid, dim3(kAttnThreads), lds, st, a);
+  const dim3 grid(cdiv(a.nq, 8) * 8 * Sh::kUnits * a.nsplit);
+  const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;
+  if (dense) hipLaunchKernelGGL((attn_bf16<true, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  else hipLaunchKernelGGL((attn_bf16<false, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }
@@ -751,7 +775,8 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
     float* wsf = static_cast<float*>(ws);
     a.part_o = wsf;
     a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * H * c : nullptr;
-    const int rc = attn_parts(nq) == 2 ? launch_attn_bf16<2>(dense, a, st) : launch_attn_bf16<4>(dense, a, st);
+    const int rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(dense, a, st)
+                                 : launch_attn_bf16<4, 8>(dense, a, st);
     if (rc != CSA_OK) return rc;
     if (ns > 1) {
       if (ns <= 4)
