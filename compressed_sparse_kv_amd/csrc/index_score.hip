@@ -108,7 +108,11 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 // Decode: few queries per sequence.  Each wave streams 64-entry groups of its sequence's
 // K straight from HBM into registers (one 128-byte row = one cache line, read by 4 lanes
 // x 32 bytes), converts them and multiplies; the keys (and row scales) of the next two
-// groups are in flight while a group is multiplied.  Grid: (ceil(Nc / kDecEntWG), B*S).
+// groups are in flight while a group is multiplied.  The unrolled group loop has no
+// branches (loads clamped to the last entry, results past the visible range masked), so
+// the compiler schedules one group's epilogue against the next group's MFMAs; entries
+// past a query's visible range cost compute but never memory outside K.
+// Grid: (ceil(Nc / kDecEntWG), B*S).
 //
 // kTopk: the workgroup also selects the top-k of its kDecEntWG scores (select_regs over
 // the scores' order-preserving keys, [KV-COMP] section 9.4) and writes them as (key,
@@ -145,7 +149,6 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
   // the next two groups are in flight while a group is multiplied
   const int base = blockIdx.x * kDecEntWG;
   auto group_e0 = [&](int gi) { return base + 64 * (gi * kDecWaves + wave); };
-  auto group_live = [&](int gi) { const int e0 = group_e0(gi); return e0 < Nc && e0 < nvis; };
   v8i ring[3][4];
   float sring[3];            // row scale of entry e0 + l, fetched with the group's keys
 #define CSA_DEC_LOAD(gi_)                                                                           \
@@ -156,8 +159,8 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     }                                                                                               \
     sring[(gi_) % 3] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                         \
   } while (0)
-  if (group_live(0)) CSA_DEC_LOAD(0);
-  if (group_live(1)) CSA_DEC_LOAD(1);
+  CSA_DEC_LOAD(0);
+  CSA_DEC_LOAD(1);
 
   v8s a[4][4];
   float wv[16];
@@ -167,24 +170,19 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
 #pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
     const int e0 = group_e0(gi);
-    if (!kTopk && e0 >= Nc) break;
-    if (gi + 2 < kDecGroups && group_live(gi + 2)) CSA_DEC_LOAD(gi + 2);
+    if (gi + 2 < kDecGroups) CSA_DEC_LOAD(gi + 2);
     const int e = e0 + l;
-    uint32_t key = 0u;
-    if (e0 < nvis) {
-      float p[4];
+    float p[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        v8s bk[4];
-        e4m3x32_to_bf16(ring[gi % 3][nb], bk);
-        p[nb] = head_sum1(a, bk, wv);
-      }
-      const float v = reduce_scatter4(p) * sring[gi % 3];
-      if (out && e < Nc) out[e] = e < nvis ? v : -INFINITY;
-      if (e < nvis) key = score_key(v);
-    } else if (out && e < Nc) {
-      out[e] = -INFINITY;
+    for (int nb = 0; nb < 4; ++nb) {
+      v8s bk[4];
+      e4m3x32_to_bf16(ring[gi % 3][nb], bk);
+      p[nb] = head_sum1(a, bk, wv);
     }
+    const float v = reduce_scatter4(p) * sring[gi % 3];
+    const bool vis = e < nvis;
+    if (out && e < Nc) out[e] = vis ? v : -INFINITY;
+    const uint32_t key = vis ? score_key(v) : 0u;
     if (kTopk) kst[64 * (gi * kDecWaves + wave) + l] = key;
   }
 #undef CSA_DEC_LOAD
