@@ -42,6 +42,7 @@
 // of one query land on the same XCD (consecutive workgroup ids go round-robin over the
 // 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "attention_common.hpp"
@@ -734,13 +735,18 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
 template <int kParts, int kWaves>
 static int launch_attn_bf16(bool dense, const AttnArgs& a, hipStream_t st) {
   using Sh = AttnShape<kParts, kWaves>;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts, kWaves>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts, kWaves>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax);
-    attr = true;
+  // the dynamic-LDS limit of both kernels, raised once per device (any thread may call)
+  static std::atomic<uint64_t> raised{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
+  const uint64_t bit = uint64_t{1} << (dev & 63);
+  if (!(raised.load(std::memory_order_acquire) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts, kWaves>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts, kWaves>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess)
+      return CSA_ERR_HIP;
+    raised.fetch_or(bit, std::memory_order_release);
   }
   const dim3 grid(cdiv(a.nq, 8) * 8 * Sh::kUnits * a.nsplit);
   const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;

@@ -206,6 +206,20 @@ def test_sparse_attn_short_prefill(lib):
                q_pos=q_pos, pass_pos=True)
 
 
+def test_hca_dense_attn_many_splits_narrow(lib):
+    # 2 queries over 20736 entries: 64 splits per query (merge over more than 8 partials)
+    q_pos = np.array([[128 * 20736 - 1], [128 * 20000 + 5]], np.int64)
+    _attn_case(lib, B=2, S=1, Nc=20736, k=0, W=128, seed=11, n_valid=0, dense=True, q_pos=q_pos)
+
+
+def test_hca_dense_attn_many_splits_wide(lib):
+    # 64 consecutive queries over 20736 entries: the 64-head shape, 10 splits (row tables
+    # of at most 72 chunks), merge over more than 8 partials
+    S = 64
+    q_pos = (128 * 20736 - S + np.arange(S, dtype=np.int64))[None]
+    _attn_case(lib, B=1, S=S, Nc=20736, k=0, W=128, seed=12, n_valid=0, dense=True, q_pos=q_pos)
+
+
 def test_hca_dense_attn(lib):
     # sequence 0 sees all 300 entries, sequence 1 only the first 200 (causal bound)
     q_pos = np.array([[128 * 300 - 1], [128 * 200 + 126]], np.int64)
