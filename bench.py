@@ -189,11 +189,11 @@ def main():
         L.csa_index_score_segments(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, cand=cand)
 
     def step(i):
-        # scores with each 4096-entry segment's top-k, the per-row merge, the attention
+        # scores with each 4096-entry segment's top-k, then the attention over the k best
+        # of each row's candidates (selection and attention in one call)
         s = sets[i % len(sets)]
         score_segments(s)
-        L.csa_topk_merge(cand, B, 1, Nc, k, idx)
-        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+        L.csa_topk_sparse_attn(s["q"], s["kv"], cand, s["swa"], s["sink"], k=k, W=sh.W, out=out, ws=at_ws)
 
     def step_separate(i):
         # the same step with the scores written out and csa_topk over them
@@ -203,19 +203,22 @@ def main():
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
 
     def stage_step(i, ev):
-        # the step's calls with events between them, then the separate-stage calls
+        # the step's calls with events between them, the same stages as three calls
+        # (merge, attention over idx), then the separate-stage calls
         s = sets[i % len(sets)]
         ev[0].record(stream)
         score_segments(s)
         ev[1].record(stream)
-        L.csa_topk_merge(cand, B, 1, Nc, k, idx)
+        L.csa_topk_sparse_attn(s["q"], s["kv"], cand, s["swa"], s["sink"], k=k, W=sh.W, out=out, ws=at_ws)
         ev[2].record(stream)
-        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
+        L.csa_topk_merge(cand, B, 1, Nc, k, idx)
         ev[3].record(stream)
-        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
+        L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
         ev[4].record(stream)
-        L.csa_topk(scores, k, idx, ws=tk_ws)
+        L.csa_index_score(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, scores=scores)
         ev[5].record(stream)
+        L.csa_topk(scores, k, idx, ws=tk_ws)
+        ev[6].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -270,11 +273,11 @@ def main():
     ms_per_step = ms_eager
 
     # per-stage durations (separate pass with events between the stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for i in range(args.steps):
         stage_step(i, evs[i])
     torch.cuda.synchronize()
-    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])
+    dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs])
     us = dur.mean(axis=0) * 1e3
 
     # dominant kernel alone: back-to-back launches (rotating input sets) between two
@@ -301,7 +304,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "timing": "eager launches: csa_index_score_segments, csa_topk_merge, csa_sparse_attn",
+        "timing": "eager launches: csa_index_score_segments, csa_topk_sparse_attn",
         "ms_per_step_separate_stages": ms_separate,
         "ms_per_step_graph": ms_graph,
         "higher_is_better": True,
@@ -314,8 +317,8 @@ def main():
                    "indexer_dim": sh.d_I, "window": sh.W, "input_sets": args.sets},
         "hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
-        "stages_us": {"csa_index_score_segments": us[0], "csa_topk_merge": us[1], "csa_sparse_attn": us[2],
-                      "csa_index_score": us[3], "csa_topk": us[4]},
+        "stages_us": {"csa_index_score_segments": us[0], "csa_topk_sparse_attn": us[1], "csa_topk_merge": us[2],
+                      "csa_sparse_attn": us[3], "csa_index_score": us[4], "csa_topk": us[5]},
         "roofline": {"kernel": "index_score_fp8_decode<true>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": isb, "avg_launch_us": is_us,

@@ -29,7 +29,7 @@ EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "c
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
-           "csa_attn_workspace_size", "csa_sparse_attn", "hca_dense_attn")
+           "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn")
 
 
 class CSAError(RuntimeError):
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
         "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "csa_topk_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp], i),
         "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
     }
     for name, (args, res) in sig.items():
@@ -243,6 +244,22 @@ def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=
     _check("csa_sparse_attn", _lib.csa_sparse_attn(
         _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
         _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+    return out
+
+
+def csa_topk_sparse_attn(q, kv_comp, cand, swa, sink, *, k: int, W: int, out, q_pos=None, lse=None, idx=None,
+                         scale=None, ws=None, stream=None):
+    """The k best of each query's segment candidates (cand from csa_index_score_segments),
+    then csa_sparse_attn over them; idx [B,S,k] int32 (optional) receives the selection."""
+    _dev(q, kv_comp, cand, swa, sink, out, lse, idx, ws, q_pos)
+    B, S, H, c = q.shape
+    Nc, Ls = kv_comp.shape[1], swa.shape[1]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    dt = _dtype(q)
+    ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
+    _check("csa_topk_sparse_attn", _lib.csa_topk_sparse_attn(
+        _p(q), _p(kv_comp), _p(cand), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
+        _p(out), _p(lse), _p(idx), _p(ws), wsb, _stream(stream)))
     return out
 
 

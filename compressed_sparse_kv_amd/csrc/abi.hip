@@ -23,6 +23,8 @@ int launch_index_topk(const void*, const float*, const float*, const void*, cons
 int launch_index_segments(const void*, const float*, const float*, const void*, const float*, const int64_t*, int,
                           int, int, int, int, float*, uint2*, hipStream_t);
 int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
+int launch_topk_attention(const void*, const void*, const uint2*, int, const int64_t*, const void*, const float*, float,
+                          int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t, hipStream_t);
 }  // namespace csa
 
 using namespace csa;
@@ -220,6 +222,21 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, cons
   CSA_REQUIRE(aligned16(ws));
   return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
                           lse, ws, ws_bytes, as_stream(stream));
+}
+
+int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand, const int64_t* q_pos,
+                         const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
+                         int Nc, int k, int Ls, int W, void* out, float* lse, int32_t* idx, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(cand && k >= 1 && k <= 2048);
+  CSA_REQUIRE(aligned16(cand) && aligned16(ws));
+  if (dtype != CSA_BF16 || !index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
+  const long long n_cand = static_cast<long long>(index_topk_segments(Nc)) * k;
+  if (n_cand > 4096) return CSA_ERR_UNSUPPORTED;
+  return launch_topk_attention(q, kv_comp, static_cast<const uint2*>(cand), static_cast<int>(n_cand), q_pos, swa,
+                               sink, scale, B, S, Nc, k, Ls, W, out, lse, idx, ws, ws_bytes, as_stream(stream));
 }
 
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m, const void* swa, const float* sink,

@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "attention_common.hpp"
+#include "select.hpp"
 
 namespace csa {
 
@@ -68,6 +69,9 @@ struct AttnShape {
   static constexpr int kLdsFixed = kRing * kChunkBytes + kSxBufs * kSxBytes + kValidSlots * kWaves * 4;
   static constexpr int kLdsMax = kLdsFixed + kMaxSplitChunks * kRows * 8;
   static_assert(kLdsMax <= 160 * 1024, "LDS of one compute unit");
+  // candidate selection (8 keys per thread) and its result sit in the ring before it is used
+  static constexpr int kMaxCand = 8 * kThreads;
+  static_assert(sizeof(TkShared) + 4 * kMaxCand <= kRing * kChunkBytes, "selection fits the ring");
   static_assert(kRowsPerWave == 4 || kRowsPerWave == 2, "the row staging moves 4 or 2 rows per wave");
   static_assert(kWGHG >= 1 && kWGHG <= kNHG, "head groups per workgroup");
 };
@@ -87,8 +91,14 @@ constexpr int kWideWaves = 8;
 constexpr int kZeroRows = 64;
 __device__ __attribute__((aligned(1024))) uint16_t g_zero_rows[kZeroRows * kAC];
 
-template <bool kDense, int kParts, int kWaves>
+// Where the remote rows of a query come from.
+constexpr int kSrcIdx = 0;     // idx[q][0..k): selected entries, -1 = none
+constexpr int kSrcDense = 1;   // every visible entry (HCA)
+constexpr int kSrcCand = 2;    // the k best of the query's segment candidates, selected here
+
+template <int kSrc, int kParts, int kWaves>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
+  constexpr bool kDense = kSrc == kSrcDense;
   using Sh = AttnShape<kParts, kWaves>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* ring = smem;                                                          // [slot][32 rows]
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
 
   const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
-  const int32_t* idxq = kDense ? nullptr : a.idx + static_cast<size_t>(qi) * a.k;
+  const int32_t* idxq = kSrc == kSrcIdx ? a.idx + static_cast<size_t>(qi) * a.k : nullptr;
 
   // Q part of the 16 heads as the B operand: lane l holds head 16*hg + l%16,
   // channels kPart*part + 32*ks + 8*g .. +7.  These loads complete under the waits of
@@ -127,6 +137,50 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
     const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC + Sh::kPart * part;
 #pragma unroll
     for (int ks = 0; ks < Sh::kPart / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
+  }
+
+  // Selection from candidates: the query's n_cand (key, entry) pairs (segment-major, each
+  // segment in entry order, key 0 = empty) -> the k best in entry order, as the top-k
+  // stage returns them, in LDS (sel) for the row table; the first workgroup of the
+  // query also writes them to idx_out.  Every workgroup of the query selects for itself
+  // (the same result); the ring is free until the pipeline starts.
+  int32_t* sel = reinterpret_cast<int32_t*>(ring + sizeof(TkShared));
+  if constexpr (kSrc == kSrcCand) {
+    TkShared& tsh = *reinterpret_cast<TkShared*>(ring);
+    const uint2* cq = a.cand + static_cast<size_t>(qi) * a.n_cand;
+    const int p0 = 8 * static_cast<int>(threadIdx.x);
+    uint32_t key[1][8], ent[8];
+    if ((a.n_cand & 1) == 0 && p0 + 7 < a.n_cand) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 v = reinterpret_cast<const uint4*>(cq + p0)[j];
+        key[0][2 * j] = v.x; ent[2 * j] = v.y;
+        key[0][2 * j + 1] = v.z; ent[2 * j + 1] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint2 v = p0 + j < a.n_cand ? cq[p0 + j] : make_uint2(0u, 0u);
+        key[0][j] = v.x; ent[j] = v.y;
+      }
+    }
+    uint64_t taken;
+    int obase[1];
+    const int kk = select_regs<Sh::kThreads, 8, 1>(tsh, key, a.k, taken, obase);
+    int32_t* io = a.idx_out && split == 0 && hp == 0 ? a.idx_out + static_cast<size_t>(qi) * a.k : nullptr;
+    int o = obase[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((taken >> j) & 1ull) {
+        sel[o] = static_cast<int32_t>(ent[j]);
+        if (io) io[o] = static_cast<int32_t>(ent[j]);
+        ++o;
+      }
+    for (int p = kk + static_cast<int>(threadIdx.x); p < a.k; p += Sh::kThreads) {
+      sel[p] = -1;
+      if (io) io[p] = -1;
+    }
+    __syncthreads();
   }
 
   // The address of every row of the split (window row, selected or visible entry, or a
@@ -140,7 +194,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
       if (slot < n_swa) {
         p = reinterpret_cast<uint64_t>(swab + static_cast<size_t>(w_lo + slot) * kAC);
       } else if (slot < n_slots) {
-        const int j = kDense ? slot - n_swa : idxq[slot - n_swa];
+        const int j = kDense ? slot - n_swa : kSrc == kSrcCand ? sel[slot - n_swa] : idxq[slot - n_swa];
         if (j >= 0 && j < a.Nc) p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kAC);
       }
       rowptr[e] = p;
@@ -733,27 +787,88 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
 }
 
 template <int kParts, int kWaves>
-static int launch_attn_bf16(bool dense, const AttnArgs& a, hipStream_t st) {
+static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
   using Sh = AttnShape<kParts, kWaves>;
-  // the dynamic-LDS limit of both kernels, raised once per device (any thread may call)
+  // the dynamic-LDS limit of every source's kernel, raised once per device (any thread may call)
   static std::atomic<uint64_t> raised{0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
   const uint64_t bit = uint64_t{1} << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<true, kParts, kWaves>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcIdx, kParts, kWaves>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<false, kParts, kWaves>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess)
       return CSA_ERR_HIP;
     raised.fetch_or(bit, std::memory_order_release);
   }
   const dim3 grid(cdiv(a.nq, 8) * 8 * Sh::kUnits * a.nsplit);
   const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;
-  if (dense) hipLaunchKernelGGL((attn_bf16<true, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
-  else hipLaunchKernelGGL((attn_bf16<false, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
+}
+
+// The bf16 path for row source SRC: splits of the row set, the attention kernel, then the
+// merge of split partials.  A carries everything but the split plan and the partials.
+static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream_t st) {
+  const int nq = a.nq;
+  const int ns = attn_nsplit(nq, max_rows);
+  a.nsplit = ns;
+  a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
+  float* wsf = static_cast<float*>(ws);
+  a.part_o = wsf;
+  a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * kAH * kAC : nullptr;
+  const int rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(src, a, st)
+                               : launch_attn_bf16<4, 8>(src, a, st);
+  if (rc != CSA_OK) return rc;
+  if (ns > 1) {
+    if (ns <= 4)
+      hipLaunchKernelGGL(attn_merge_tiles<4>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 16)), dim3(256), 0, st,
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse);
+    else
+      hipLaunchKernelGGL(attn_merge_tiles<1>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st,
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse);
+    CSA_LAUNCH_CHECK();
+  }
+  return CSA_OK;
+}
+
+static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, int m, const void* swa,
+                          const float* sink, float scale, int B, int S, int Nc, int k, int Ls, int W, void* out,
+                          float* lse) {
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv);
+  a.q_pos = q_pos;
+  a.swa = static_cast<const uint16_t*>(swa);
+  a.sink = sink;
+  a.scale_log2 = scale * kLog2e;
+  a.nq = B * S; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return a;
+}
+
+// Top-k selection from segment candidates fused with the bf16 attention: cand holds
+// n_cand = G*k (key, entry) pairs per query (n_cand <= 4096); idx_out (optional) receives
+// the selection.  The caller has checked shapes and the workspace.
+int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int n_cand, const int64_t* q_pos,
+                          const void* swa, const float* sink, float scale, int B, int S, int Nc, int k, int Ls,
+                          int W, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+                          hipStream_t st) {
+  const int max_rows = std::min(W, Ls) + k;
+  if (ws_bytes < attn_workspace_bytes(B, S, kAH, kAC, max_rows, CSA_BF16)) return CSA_ERR_WORKSPACE;
+  if (n_cand > NarrowShape::kMaxCand || n_cand > WideShape::kMaxCand || k > n_cand) return CSA_ERR_UNSUPPORTED;
+  AttnArgs a = attn_args(q, kv, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, out, lse);
+  a.cand = cand;
+  a.n_cand = n_cand;
+  a.idx_out = idx_out;
+  return run_attn_bf16(kSrcCand, a, max_rows, ws, st);
 }
 
 int launch_attention(bool dense, const void* q, const void* kv, const int32_t* idx, const int64_t* q_pos, int m,
@@ -764,36 +879,9 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
   if (ws_bytes < attn_workspace_bytes(B, S, H, c, max_rows, dtype)) return CSA_ERR_WORKSPACE;
   const float scale_log2 = scale * kLog2e;
   if (dtype == CSA_BF16) {
-    const int ns = attn_nsplit(nq, max_rows);
-    AttnArgs a;
-    a.q = static_cast<const uint16_t*>(q);
-    a.kv = static_cast<const uint16_t*>(kv);
+    AttnArgs a = attn_args(q, kv, q_pos, m, swa, sink, scale, B, S, Nc, k, Ls, W, out, lse);
     a.idx = idx;
-    a.q_pos = q_pos;
-    a.swa = static_cast<const uint16_t*>(swa);
-    a.sink = sink;
-    a.scale_log2 = scale_log2;
-    a.nq = nq; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
-    a.nsplit = ns;
-    a.chunks_per_split = cdiv(cdiv(max_rows, kRows), ns);
-    a.out = static_cast<uint16_t*>(out);
-    a.lse = lse;
-    float* wsf = static_cast<float*>(ws);
-    a.part_o = wsf;
-    a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * H * c : nullptr;
-    const int rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(dense, a, st)
-                                 : launch_attn_bf16<4, 8>(dense, a, st);
-    if (rc != CSA_OK) return rc;
-    if (ns > 1) {
-      if (ns <= 4)
-        hipLaunchKernelGGL(attn_merge_tiles<4>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 16)), dim3(256), 0, st,
-                           a.part_o, a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
-      else
-        hipLaunchKernelGGL(attn_merge_tiles<1>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st,
-                           a.part_o, a.part_ml, sink, ns, nq, static_cast<uint16_t*>(out), lse);
-      CSA_LAUNCH_CHECK();
-    }
-    return CSA_OK;
+    return run_attn_bf16(dense ? kSrcDense : kSrcIdx, a, max_rows, ws, st);
   }
   float* wsf = static_cast<float*>(ws);
   float* part_o = wsf;

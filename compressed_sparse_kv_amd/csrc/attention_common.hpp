@@ -39,6 +39,9 @@ struct AttnArgs {
   float* lse;
   float* part_o;             // [B*S, nsplit, H, c] fp32, unnormalised
   float* part_ml;            // [B*S, nsplit, H, 2]: reference max (log2 units), sum
+  const uint2* cand;         // [B*S, n_cand] (key, entry) pairs of the segment top-k sets
+  int n_cand;
+  int32_t* idx_out;          // [B*S, k] the selection made from cand, or null
 };
 
 // Window rows of query s: rows w_lo .. w_lo + n_swa - 1 of the sequence's swa tensor,

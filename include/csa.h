@@ -223,6 +223,25 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * Stages 3 and 4a in one call (decode shapes): csa_topk_merge of the segment
+ * candidates written by csa_index_score_segments, then csa_sparse_attn over the
+ * selected entries.  [KV-COMP] section 9.4 (the row's top-k lies in the union of its
+ * segments' top-k sets) and sections 9.5-9.6 (attention over window || selection).
+ * Results identical to csa_topk_merge followed by csa_sparse_attn.
+ *
+ *   cand: the pairs of csa_index_score_segments for the same B, S, Nc and k.
+ *   Supported: dtype CSA_BF16 (H = 64, c = 512), the shapes csa_index_score_segments
+ *   accepts, and ceil(Nc / 4096) * k <= 4096; otherwise CSA_ERR_UNSUPPORTED.
+ *   idx [B,S,k] int32: receives the selection (as csa_topk_merge writes it), or NULL.
+ *   Other arguments and the workspace (max_rows = min(W, Ls) + k) as csa_sparse_attn.
+ * ------------------------------------------------------------------------------ */
+int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand,
+                         const int64_t* q_pos, const void* swa, const float* sink, int dtype,
+                         float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                         void* out, float* lse, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 4b: HCA core attention.  [HCA-CSA] "HCA：重压缩 + 全量" (no indexer: every
  * completed, visible compressed entry plus the window and the sink); [KV-COMP]
  * section 9.8 (entry j visible iff t >= m*j + m - 1).

@@ -306,10 +306,14 @@ def test_decode_chain_graph_replay(lib):
         lib.csa_topk_merge(cand, B, 1, Nc, k, idx)
         lib.csa_sparse_attn(q, kv, idx, swa, sink, W=W, out=out, ws=at_ws)
 
+    def step_fused():
+        lib.csa_index_score_segments(q8, qs, w, k8, ks, qpos, m=m, k=k, cand=cand, scores=scores)
+        lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out, idx=idx, ws=at_ws)
+
     step()
     torch.cuda.synchronize()
     ref = (scores.clone(), idx.clone(), out.clone())
-    for fn in (step, step_segments):
+    for fn in (step, step_segments, step_fused):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
@@ -373,3 +377,56 @@ def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     KI = O.dequant_rows(a["kI_fp8"][:1], a["kI_scale"][:1])
     sc_o = O.index_scores(qI, a["w"][:1, :1], KI, pos[:1, :1], 4)
     assert_topk_equal(idx[:1, :1].cpu().numpy(), O.topk_indices(sc_o, k), sc_o, k, "fused top-k vs oracle")
+
+
+# ---------------------------------------------------------------------------------------
+# Stages 3 + 4a in one call: identical to csa_topk_merge followed by csa_sparse_attn
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,Nc,k,t", [
+    (3, 1, 32768, 512, 4 * 32768 - 1),     # decode: 8 segments, 4096 candidates per query
+    (2, 1, 5000, 256, 4 * 5000 + 7),       # ragged last segment
+    (2, 2, 9000, 301, 4 * 2500 + 2),       # causal limit inside the row; odd candidate count
+    (1, 1, 1500, 2048, 4 * 1500 - 1),      # k above the visible count: -1 padding
+    (2, 4, 6000, 512, 4 * 6000 - 1),       # four queries per sequence
+    (64, 1, 4096, 512, 4 * 4096 - 1),      # many queries: the 64-head workgroup shape
+])
+def test_topk_sparse_attn_fused(lib, B, S, Nc, k, t):
+    a = I.indexer_inputs(7000 + B + Nc + k, B, S, Nc)
+    W = 128
+    Ls = S + W - 1
+    at = I.attention_inputs(8000 + B + Nc, B, S, Nc, Ls)
+    pos = (t - S + 1 + np.arange(S, dtype=np.int64))[None].repeat(B, 0)
+    qpos = dev(pos)
+    cand = torch.empty(lib.index_segments_size(B, S, Nc, k), dtype=torch.uint8, device="cuda")
+    lib.csa_index_score_segments(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]),
+                                 dev(a["kI_scale"]), qpos, m=4, k=k, cand=cand)
+    q, kv, swa, sink = dev_bf16(at["q_bf16"]), dev_bf16(at["kv_comp_bf16"]), dev_bf16(at["swa_bf16"]), dev(at["sink"])
+    idx_ref = torch.empty(B, S, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_merge(cand, B, S, Nc, k, idx_ref)
+    out_ref = torch.empty(B, S, 64, 512, dtype=torch.bfloat16, device="cuda")
+    lse_ref = torch.empty(B, S, 64, device="cuda")
+    lib.csa_sparse_attn(q, kv, idx_ref, swa, sink, W=W, out=out_ref, lse=lse_ref, q_pos=qpos)
+    out = torch.full_like(out_ref, 7.0)
+    lse = torch.full_like(lse_ref, 7.0)
+    idx = torch.full_like(idx_ref, -7)
+    lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out, lse=lse, idx=idx, q_pos=qpos)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref), "fused selection differs from csa_topk_merge"
+    assert torch.equal(out, out_ref), "fused attention differs from csa_sparse_attn"
+    assert torch.equal(lse, lse_ref), "fused lse differs from csa_sparse_attn"
+    # without the index output, the same attention
+    out2 = torch.zeros_like(out_ref)
+    lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out2, q_pos=qpos)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out_ref), "fused attention without idx output differs"
+    # and the first query against the oracle: its own scores, top-k and attention
+    qI = O.dequant_rows(a["qI_fp8"][:1, :1], a["qI_scale"][:1, :1])
+    KI = O.dequant_rows(a["kI_fp8"][:1], a["kI_scale"][:1])
+    sc_o = O.index_scores(qI, a["w"][:1, :1], KI, pos[:1, :1], 4)
+    assert_topk_equal(idx[:1, :1].cpu().numpy(), O.topk_indices(sc_o, k), sc_o, k, "fused selection vs oracle")
+    o_ref, l_ref = O.sparse_attention(bf16_f64(at["q_bf16"][:1]), bf16_f64(at["kv_comp_bf16"][:1]),
+                                      idx[:1].cpu().numpy(), bf16_f64(at["swa_bf16"][:1]), at["sink"],
+                                      1 / math.sqrt(512), pos[:1], W)
+    assert_bf16_output(bf16_f64(host_bits(out[:1])), o_ref, "fused attention vs oracle")
+    assert_close(lse[:1].cpu().numpy(), l_ref, TOL_F32, "fused lse vs oracle")
