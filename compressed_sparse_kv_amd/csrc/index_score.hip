@@ -53,16 +53,17 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const v8i& c, v8s out[4]) {
 
 // p[nb] = partial head-sum of entry (lane&15) of block nb over this lane's heads.
 // Returns, in lane l, the full sum for entry 16*(l>>4) + (l&15) = l of the 4 blocks.
+// Two reduce-scatter steps on the gfx950 lane swaps, no LDS: v_permlane32_swap(x, y)
+// leaves x = [x.lo, y.lo] and y = [x.hi, y.hi] (32-lane halves), so x + y is, in the low
+// half, x + the high half's x and, in the high half, y + the low half's y; 16-lane rows
+// pair up the same way under v_permlane16_swap.
 __device__ __forceinline__ float reduce_scatter4(const float p[4]) {
-  const int g = static_cast<int>(lane_id()) >> 4;
-  const bool lo = g < 2;
-  const float s0 = lo ? p[2] : p[0], s1 = lo ? p[3] : p[1];
-  const float k0 = lo ? p[0] : p[2], k1 = lo ? p[1] : p[3];
-  const float q0 = k0 + wave_xor(s0, 32);
-  const float q1 = k1 + wave_xor(s1, 32);
-  const bool odd = g & 1;
-  const float send = odd ? q0 : q1, keep = odd ? q1 : q0;
-  return keep + wave_xor(send, 16);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
+  const float q0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // blocks 0 (low half), 2 (high half)
+  const float q1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // blocks 1, 3
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // ReLU as one instruction: med3(x, 0, 3e38) (fmaxf would also emit a NaN-quieting max).

@@ -81,13 +81,17 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // Histograms have 64 * PB bins stored with 4 padding words after every PB bins, so
 // that 64 lanes reading PB consecutive bins each hit distinct LDS banks.
 template <int PB>
-__device__ __forceinline__ int hist_slot(int bin) { return bin + 4 * (bin / PB); }
+__device__ __forceinline__ int hist_slot(int bin) {
+  const unsigned u = static_cast<unsigned>(bin);      // bins are >= 0
+  return static_cast<int>(u + 4u * (u / PB));
+}
 
 // Threshold search run by every wave on its own over the complete histogram (no
 // barrier): with 1 <= remain <= total, returns the bin b with
-// (#keys in bins > b) < remain <= (#keys in bins >= b) and sets above = #keys in bins > b.
+// (#keys in bins > b) < remain <= (#keys in bins >= b) and sets above = #keys in bins > b
+// and count = #keys in bin b.
 template <int PB>
-__device__ __forceinline__ int wave_threshold_bin(const uint32_t* hist, int remain, int& above) {
+__device__ __forceinline__ int wave_threshold_bin(const uint32_t* hist, int remain, int& above, int& count) {
   constexpr int nbins = kWave * PB;
   const int l = static_cast<int>(lane_id());
   // lane l sums group l counted from the top: bins nbins - PB*(l+1) .. nbins - 1 - PB*l
@@ -106,6 +110,7 @@ __device__ __forceinline__ int wave_threshold_bin(const uint32_t* hist, int rema
   const int incl2 = wave_incl_scan(c);
   const int J = __ffsll(static_cast<long long>(__ballot(l < PB && before + incl2 >= remain))) - 1;
   above = before + __builtin_amdgcn_readlane(incl2 - c, J);
+  count = __builtin_amdgcn_readlane(c, J);
   return nbins - 1 - (PB * L + J);
 }
 
@@ -166,7 +171,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
     }
     if (l == 0) sh.cell_nz[u * W + w] = cnt;
   }
-  for (int i = tid; i < kTkHistWords; i += NT) sh.hist[i] = 0;
+  for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid == 0) sh.ncand = 0;
   kmax = wave_max_u32(kmax);
   kmin = ~wave_max_u32(~kmin);
@@ -200,24 +205,34 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
   if (kk < total) {
     const float lo = key_value(kmin);
     const float range = key_value(kmax) - lo;
-    const float scale = static_cast<float>(kTkBins) / range;
+    // any positive scale keeps the bins monotone in the value; the reciprocal is enough
+    const float scale = static_cast<float>(kTkBins) * __builtin_amdgcn_rcpf(range);
     bool ok = range > 0.0f && range <= 3.0e38f && scale <= 3.0e38f;
     int b = 0, remain = 0;
+    // small register sets keep each key's bin from the histogram pass for the next one
+    constexpr bool kKeepBins = NU * KPT <= 16;
+    int bins[kKeepBins ? NU : 1][kKeepBins ? KPT : 1];
+    auto bin_of = [&](uint32_t kv) __attribute__((always_inline)) {
+      return kv != 0u ? min(kTkBins - 1, static_cast<int>((key_value(kv) - lo) * scale)) : -1;
+    };
     if (ok) {
-      // ---- 2. histogram over equal-width bins of [min, max]
+      // ---- 2. histogram over equal-width bins of [min, max]; a key that is not a
+      // candidate adds to a padding word of its lane's bin group (never read), so the
+      // pass has no branches
+      const int junk = hist_slot<kTkPB>(kTkPB * l) + kTkPB;
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
-        for (int s = 0; s < KPT; ++s)
-          if (key[u][s] != 0u) {
-            const int bn = min(kTkBins - 1, static_cast<int>((key_value(key[u][s]) - lo) * scale));
-            atomicAdd(&sh.hist[hist_slot<kTkPB>(bn)], 1u);
-          }
+        for (int s = 0; s < KPT; ++s) {
+          const int bn = bin_of(key[u][s]);
+          if constexpr (kKeepBins) bins[u][s] = bn;
+          atomicAdd(&sh.hist[bn >= 0 ? hist_slot<kTkPB>(bn) : junk], 1u);
+        }
       __syncthreads();                                                // barrier 2
-      int above;
-      b = wave_threshold_bin<kTkPB>(sh.hist, kk, above);
+      int above, cnt_b;
+      b = wave_threshold_bin<kTkPB>(sh.hist, kk, above, cnt_b);
       remain = kk - above;
-      ok = static_cast<int>(sh.hist[hist_slot<kTkPB>(b)]) <= kTkCandCap;
+      ok = cnt_b <= kTkCandCap;
     }
     if (ok) {
       // ---- 3. higher bins are taken (counted per cell); bin b goes to the list
@@ -227,7 +242,9 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
 #pragma unroll
         for (int s = 0; s < KPT; ++s) {
           const uint32_t kv = key[u][s];
-          const int bn = kv != 0u ? min(kTkBins - 1, static_cast<int>((key_value(kv) - lo) * scale)) : -1;
+          int bn;
+          if constexpr (kKeepBins) bn = bins[u][s];
+          else bn = bin_of(kv);
           g += __popcll(__ballot(bn > b));
           const uint64_t m = __ballot(bn == b);
           if (m != 0) {
@@ -288,7 +305,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
       for (int pass = 0; pass < 3; ++pass) {
         const int shift = digit_shift(pass), nbins = digit_bins(pass);
         __syncthreads();
-        for (int i = tid; i < kTkHistWords; i += NT) sh.hist[i] = 0;
+        for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < NU; ++u)
@@ -301,9 +318,9 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
             }
           }
         __syncthreads();
-        int above, bb;
-        if (nbins == 2048) bb = wave_threshold_bin<32>(sh.hist, rem, above);
-        else bb = wave_threshold_bin<16>(sh.hist, rem, above);
+        int above, bb, cnt_unused;
+        if (nbins == 2048) bb = wave_threshold_bin<32>(sh.hist, rem, above, cnt_unused);
+        else bb = wave_threshold_bin<16>(sh.hist, rem, above, cnt_unused);
         prefix |= static_cast<uint32_t>(bb) << shift;
         mask |= static_cast<uint32_t>(nbins - 1) << shift;
         rem -= above;
