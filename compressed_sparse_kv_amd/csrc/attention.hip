@@ -37,6 +37,10 @@
 //      4*(l/16)+i and 16+4*(l/16)+i) is the A-operand layout of P under the matching
 //      k-slot order, so P never leaves registers.  P enters as a bf16 hi + lo pair (two
 //      MFMAs on one V operand) so it keeps ~16 bits.
+// The remote rows come from idx (CSA), from every visible entry (HCA), or from a
+// selection each workgroup makes itself from the segment top-k candidates of the indexer
+// pass (the k best of G*k (key, entry) pairs, with the selection core of select.hpp), so
+// that selection and attention are one launch.
 // A row set split over several workgroups writes (m, l, O) partials that attn_merge_tiles
 // combines with the sink (LSE merge).  Workgroups are numbered so that all workgroups
 // of one query land on the same XCD (consecutive workgroup ids go round-robin over the

@@ -1,5 +1,6 @@
 // Selection of the k largest keys of a set held in registers by one workgroup: the core of
-// the top-k stage (see topk.hip), also run by the fused indexer epilogue.
+// the top-k stage (see topk.hip), also run by the fused indexer epilogue (segment top-k)
+// and by the attention kernel that selects from segment candidates.
 //
 // Keys are order-preserving images of the scores (score_key); the order is (key
 // descending, position ascending), a total order, and positions follow index order, so

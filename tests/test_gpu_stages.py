@@ -390,6 +390,7 @@ def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     (1, 1, 1500, 2048, 4 * 1500 - 1),      # k above the visible count: -1 padding
     (2, 4, 6000, 512, 4 * 6000 - 1),       # four queries per sequence
     (64, 1, 4096, 512, 4 * 4096 - 1),      # many queries: the 64-head workgroup shape
+    (1, 1, 8192, 2048, 4 * 8192 - 1),      # the largest selection: 2 x 2048 candidates, k = 2048
 ])
 def test_topk_sparse_attn_fused(lib, B, S, Nc, k, t):
     a = I.indexer_inputs(7000 + B + Nc + k, B, S, Nc)
@@ -420,6 +421,13 @@ def test_topk_sparse_attn_fused(lib, B, S, Nc, k, t):
     lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out2, q_pos=qpos)
     torch.cuda.synchronize()
     assert torch.equal(out2, out_ref), "fused attention without idx output differs"
+    # without q_pos (every window row a real position), as csa_sparse_attn without it
+    out3 = torch.zeros_like(out_ref)
+    out3_ref = torch.zeros_like(out_ref)
+    lib.csa_sparse_attn(q, kv, idx_ref, swa, sink, W=W, out=out3_ref)
+    lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out3)
+    torch.cuda.synchronize()
+    assert torch.equal(out3, out3_ref), "fused attention without q_pos differs"
     # and the first query against the oracle: its own scores, top-k and attention
     qI = O.dequant_rows(a["qI_fp8"][:1, :1], a["qI_scale"][:1, :1])
     KI = O.dequant_rows(a["kI_fp8"][:1], a["kI_scale"][:1])
