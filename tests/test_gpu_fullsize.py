@@ -54,11 +54,33 @@ def _check_decode(sh, a, scores, idx, out, lse, sample):
         assert_close(lse[sl], lse_o, TOL_F32, f"lse, sequence {b}")
 
 
+def _decode_step_fused(lib, sh, a):
+    """The decode step as the bench times it: scores with each segment's top-k, then the
+    selection and the sparse attention in one call."""
+    B, Nc, k = sh.B, sh.n_c, sh.k
+    cand = torch.empty(lib.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device="cuda")
+    lib.csa_index_score_segments(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]),
+                                 dev(a["kI_scale"]), dev(a["q_pos"]), m=sh.m, k=k, cand=cand)
+    idx = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, 1, sh.H, device="cuda")
+    lib.csa_topk_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), cand, dev_bf16(a["swa_bf16"]),
+                             dev(a["sink"]), k=k, W=sh.W, out=out, lse=lse, idx=idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), out, lse.cpu().numpy()
+
+
 def test_flash_decode_full(lib):
     sh = I.FLASH_DECODE
     a = I.decode_inputs(sh).arrays
     scores, idx, out, lse = _decode_chain(lib, sh, a)
     _check_decode(sh, a, scores, idx, out, lse, sample=[0, 13, 31])
+    # the bench's two-call step on the same inputs: the same selection on every row, and
+    # the same attention output bit for bit (same kernels on the same rows in the same order)
+    idx2, out2, lse2 = _decode_step_fused(lib, sh, a)
+    assert np.array_equal(idx2, idx), "segment top-k + fused selection differ from csa_topk (full batch)"
+    assert torch.equal(out2, out), "fused selection + attention differs from csa_sparse_attn (full batch)"
+    assert np.array_equal(lse2, lse), "fused lse differs (full batch)"
 
 
 def test_pro_decode_full(lib):
