@@ -23,6 +23,7 @@ int launch_index_topk(const void*, const float*, const float*, const void*, cons
 int launch_index_segments(const void*, const float*, const float*, const void*, const float*, const int64_t*, int,
                           int, int, int, int, float*, uint2*, hipStream_t);
 int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
+size_t topk_merge_pairs_per_row(int, int);
 int launch_topk_attention(const void*, const void*, const uint2*, int, const int64_t*, const void*, const float*, float,
                           int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t, hipStream_t);
 }  // namespace csa
@@ -106,7 +107,7 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 size_t csa_index_topk_workspace_size(int B, int S, int Nc, int k) {
   if (B <= 0 || S <= 0 || Nc <= 0 || k <= 0) return 0;
   const size_t rows = static_cast<size_t>(B) * S;
-  if (index_topk_fused_ok(S, Nc, k)) return rows * index_topk_segments(Nc) * k * sizeof(uint2);
+  if (index_topk_fused_ok(S, Nc, k)) return rows * topk_merge_pairs_per_row(index_topk_segments(Nc), k) * sizeof(uint2);
   return align256(rows * Nc * sizeof(float)) + topk_workspace_bytes(static_cast<int>(rows), Nc, k);
 }
 
@@ -139,7 +140,7 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w, const vo
 
 size_t csa_index_segments_size(int B, int S, int Nc, int k) {
   if (B <= 0 || S <= 0 || Nc <= 0 || k <= 0 || !index_topk_fused_ok(S, Nc, k)) return 0;
-  return static_cast<size_t>(B) * S * index_topk_segments(Nc) * k * sizeof(uint2);
+  return static_cast<size_t>(B) * S * topk_merge_pairs_per_row(index_topk_segments(Nc), k) * sizeof(uint2);
 }
 
 int csa_index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,

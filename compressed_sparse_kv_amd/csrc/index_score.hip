@@ -117,9 +117,10 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 //
 // kTopk: the workgroup also selects the top-k of its kDecEntWG scores (select_regs over
 // the scores' order-preserving keys, [KV-COMP] section 9.4) and writes them as (key,
-// entry) pairs in entry order to cand[row][blockIdx.x][k] (key 0 = empty slot); the union
-// of these local selections holds the row's top-k, which topk_merge finishes.  Scores are
-// then written only when `scores` is not null.
+// entry) pairs in entry order to cand + row * cand_stride + blockIdx.x * k (key 0 = empty
+// slot); the union of these local selections holds the row's top-k, which topk_merge
+// finishes (rows are cand_stride pairs apart: room for the merge's first level when there
+// are many segments).  Scores are then written only when `scores` is not null.
 // ------------------------------------------------------------------------------------
 constexpr int kDecGroups = 8;                         // 64-entry groups per wave
 // Waves per workgroup: 4 for scores alone (more workgroups for small grids), 8 with the
@@ -131,7 +132,7 @@ template <bool kTopk>
 __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decode(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
-    int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand) {
+    int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand, size_t cand_stride) {
   constexpr int kDecWaves = dec_waves<kTopk>();
   constexpr int kDecThreads = kDecWaves * 64;
   constexpr int kDecEntWG = dec_entries<kTopk>();
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     int obase[1];
     static_assert(kDecThreads * 8 == kDecEntWG, "8 keys per thread");
     const int kk = select_regs<kDecThreads, 8, 1>(sh, key, ktop, taken, obase);
-    uint2* dst = cand + (row * gridDim.x + blockIdx.x) * static_cast<size_t>(ktop);
+    uint2* dst = cand + row * cand_stride + blockIdx.x * static_cast<size_t>(ktop);
     int o = obase[0];
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
@@ -351,7 +352,7 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
       dim3 grid(cdiv(Nc, dec_entries<false>()), B * S);
       hipLaunchKernelGGL(index_score_fp8_decode<false>, grid, dim3(dec_waves<false>() * 64), 0, st,
                          static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k),
-                         k_scale, q_pos, S, Nc, m, scores, 0, nullptr);
+                         k_scale, q_pos, S, Nc, m, scores, 0, nullptr, size_t{0});
     } else {
       dim3 grid(cdiv(S, kPfQ), B);
       hipLaunchKernelGGL(index_score_fp8_prefill, grid, dim3(kPfThreads), 0, st,
@@ -372,6 +373,7 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
 // the per-row merge: idx = the k largest of each row, as csa_topk would return.
 int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st);
 int topk_merge_supported(int G, int k);
+size_t topk_merge_pairs_per_row(int G, int k);
 
 int index_topk_segments(int Nc) { return cdiv(Nc, dec_entries<true>()); }
 
@@ -386,7 +388,7 @@ int launch_index_segments(const void* q, const float* q_scale, const float* w, c
   dim3 grid(index_topk_segments(Nc), B * S);
   hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(dec_waves<true>() * 64), 0, st,
                      static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc,
-                     m, scores, ktop, cand);
+                     m, scores, ktop, cand, topk_merge_pairs_per_row(index_topk_segments(Nc), ktop));
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

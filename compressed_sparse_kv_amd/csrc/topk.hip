@@ -110,15 +110,24 @@ __global__ __launch_bounds__(kTkThreads) void topk_segments(const float* __restr
   for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = make_uint2(0u, 0u);
 }
 
-// One workgroup per row over the n = G*k pairs of its segments (n <= NU * 4096).  The keys
-// and (up to four register chunks) their entry indices stay in registers from the one read
-// of the pairs; the largest set reads the indices of the taken pairs again.
-template <int NU>
-__global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict__ cand, int n, int k,
-                                                         int32_t* __restrict__ idx) {
+// One workgroup per (row, group) over the pairs [grp * n_grp, min(n_row, (grp+1) * n_grp))
+// of the row's n_row pairs at cand + row * row_stride (n_grp <= NU * 4096); gridDim.y
+// groups per row.  The keys and
+// (up to four register chunks) their entry indices stay in registers from the one read of
+// the pairs; the largest set reads the indices of the taken pairs again.  kPairs: the k
+// best are written as (key, entry) pairs in entry order to pairs_out[row][grp][k] (key 0
+// = empty) at pairs_out + row * out_stride + grp * k, the input of a second merge; else as
+// indices to idx[row][k] (one group).
+// Groups of consecutive segments keep the pairs of a row in entry order at every level.
+template <int NU, bool kPairs>
+__global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict__ cand, size_t row_stride, int n_row,
+                                                         int n_grp, int k, int32_t* __restrict__ idx,
+                                                         uint2* __restrict__ pairs_out, size_t out_stride) {
   __shared__ TkShared sh;
   const size_t row = blockIdx.x;
-  const uint2* c = cand + row * static_cast<size_t>(n);
+  const int grp = blockIdx.y;
+  const uint2* c = cand + row * row_stride + static_cast<size_t>(grp) * n_grp;
+  const int n = min(n_grp, n_row - grp * n_grp);
   const bool vec = (reinterpret_cast<uintptr_t>(c) & 15u) == 0;
   constexpr int NE = NU <= 4 ? NU : 1;                 // register chunks of entry indices
   uint32_t key[NU][4], ent[NE][4];
@@ -142,16 +151,29 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge(const uint2* __restrict
   uint64_t taken;
   int obase[NU];
   const int kk = select_regs<kTkThreads, 4, NU>(sh, key, k, taken, obase);
-  int32_t* out = idx + row * k;
+  if constexpr (kPairs) {
+    uint2* out = pairs_out + row * out_stride + static_cast<size_t>(grp) * k;
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    int o = obase[u];
+    for (int u = 0; u < NU; ++u) {
+      int o = obase[u];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      if ((taken >> (4 * u + s)) & 1ull)
-        out[o++] = static_cast<int32_t>(NU <= 4 ? ent[u % NE][s] : c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s].y);
+      for (int s = 0; s < 4; ++s)
+        if ((taken >> (4 * u + s)) & 1ull)
+          out[o++] = NU <= 4 ? make_uint2(key[u][s], ent[u % NE][s]) : c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s];
+    }
+    for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = make_uint2(0u, 0u);
+  } else {
+    int32_t* out = idx + row * k;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      int o = obase[u];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if ((taken >> (4 * u + s)) & 1ull)
+          out[o++] = static_cast<int32_t>(NU <= 4 ? ent[u % NE][s] : c[kTkChunk * u + 4 * static_cast<int>(threadIdx.x) + s].y);
+    }
+    for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
   }
-  for (int p = kk + threadIdx.x; p < k; p += kTkThreads) out[p] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -199,7 +221,8 @@ static void launch_segments(const float* scores, int rows, int G, int Nc, int k,
 }
 template <int NU>
 static void launch_merge(const uint2* cand, int rows, int n, int k, int32_t* idx, hipStream_t st) {
-  hipLaunchKernelGGL(topk_merge<NU>, dim3(rows), dim3(kTkThreads), 0, st, cand, n, k, idx);
+  hipLaunchKernelGGL((topk_merge<NU, false>), dim3(rows), dim3(kTkThreads), 0, st, cand, static_cast<size_t>(n), n, n,
+                     k, idx, nullptr, size_t{0});
 }
 
 // algo: 0 = automatic, 1 = one workgroup per row, 2 = segments + merge.  The caller has
@@ -244,17 +267,59 @@ int launch_topk(const float* scores, int rows, int Nc, int k, int32_t* idx, void
 }
 
 // Merge of G per-segment candidate lists (G*k (key, index) pairs per row, each list in
-// index order, key 0 = empty) into the row's top-k.
-int topk_merge_supported(int G, int k) { return G >= 1 && k >= 1 && static_cast<long long>(G) * k <= kTkMaxSet; }
+// index order, key 0 = empty) into the row's top-k.  When the G*k pairs of a row exceed one
+// workgroup's set, a first level merges groups of M consecutive lists into k pairs each
+// (in entry order, after the rows' G*k pairs in the same buffer), and the second level
+// merges the ceil(G/M) group results.  M ~ sqrt(G) balances the two levels.
+// Returns M, 0 for a single level, or -1 when two levels do not suffice.
+int topk_merge_group(int G, int k) {
+  if (G < 1 || k < 1 || k > kTkMaxSet) return -1;
+  if (static_cast<long long>(G) * k <= kTkMaxSet) return 0;
+  const int M = std::max(2, std::min(kTkMaxSet / k, static_cast<int>(std::lround(std::sqrt(static_cast<double>(G))))));
+  return static_cast<long long>(cdiv(G, M)) * k <= kTkMaxSet ? M : -1;
+}
 
-int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st) {
-  const int n = G * k;
-  switch (chunks_for(n)) {
-    case 1: launch_merge<1>(cand, rows, n, k, idx, st); break;
-    case 2: launch_merge<2>(cand, rows, n, k, idx, st); break;
-    case 4: launch_merge<4>(cand, rows, n, k, idx, st); break;
-    default: launch_merge<kTkMaxChunks>(cand, rows, n, k, idx, st); break;
+int topk_merge_supported(int G, int k) { return topk_merge_group(G, k) >= 0; }
+
+// Pairs per row of the candidate buffer: the G*k segment pairs and the first level's.
+size_t topk_merge_pairs_per_row(int G, int k) {
+  const int M = topk_merge_group(G, k);
+  return static_cast<size_t>(G) * k + (M > 0 ? static_cast<size_t>(cdiv(G, M)) * k : 0);
+}
+
+template <bool kPairs>
+static void launch_merge_level(const uint2* cand, size_t row_stride, int rows, int groups, int n_row, int n_grp,
+                               int k, int32_t* idx, uint2* out, hipStream_t st) {
+  const dim3 grid(rows, groups), block(kTkThreads);
+#define CSA_MERGE_LAUNCH(NU_)                                                                                  \
+  hipLaunchKernelGGL((topk_merge<NU_, kPairs>), grid, block, 0, st, cand, row_stride, n_row, n_grp, k, idx, out, \
+                     row_stride)
+  switch (chunks_for(n_grp)) {
+    case 1: CSA_MERGE_LAUNCH(1); break;
+    case 2: CSA_MERGE_LAUNCH(2); break;
+    case 4: CSA_MERGE_LAUNCH(4); break;
+    default: CSA_MERGE_LAUNCH(kTkMaxChunks); break;
   }
+#undef CSA_MERGE_LAUNCH
+}
+
+// cand: rows x topk_merge_pairs_per_row(G, k) pairs (the first G*k of a row are the input).
+int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st) {
+  const int M = topk_merge_group(G, k);
+  if (M < 0) return CSA_ERR_UNSUPPORTED;
+  const size_t per_row = topk_merge_pairs_per_row(G, k);
+  if (M == 0) {
+    launch_merge_level<false>(cand, per_row, rows, 1, G * k, G * k, k, idx, nullptr, st);
+    CSA_LAUNCH_CHECK();
+    return CSA_OK;
+  }
+  // rows are per_row pairs apart: the first level reads row r's G*k pairs at
+  // cand + r * per_row and writes its G1 * k pairs right after them
+  const int G1 = cdiv(G, M);
+  uint2* lvl = const_cast<uint2*>(cand) + static_cast<size_t>(G) * k;
+  launch_merge_level<true>(cand, per_row, rows, G1, G * k, M * k, k, nullptr, lvl, st);
+  CSA_LAUNCH_CHECK();
+  launch_merge_level<false>(lvl, per_row, rows, 1, G1 * k, G1 * k, k, idx, nullptr, st);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

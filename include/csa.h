@@ -124,10 +124,11 @@ int csa_index_score(const void* q, const float* q_scale, const float* w,
 /* ------------------------------------------------------------------------------
  * Stages 2 and 3 in one call (FP8 inputs, H_I = 64, d_I = 128): the index scores of
  * csa_index_score and the selection of csa_topk, identical results.  For decode shapes
- * (S <= 4, ceil(Nc / 4096) * k <= 36864) the scoring pass also selects the top-k of each
- * 4096-entry segment while the scores are in registers, and one merge pass finishes the
- * rows ([KV-COMP] section 9.4: the union of segment top-k sets holds the row's top-k);
- * other shapes run the two stages back to back.
+ * (S <= 4 and G = ceil(Nc / 4096) segments whose G*k candidates merge in one or two
+ * levels, below) the scoring pass also selects the top-k of each 4096-entry segment while
+ * the scores are in registers, and the merge passes finish the rows ([KV-COMP] section
+ * 9.4: the union of segment top-k sets holds the row's top-k); other shapes run the two
+ * stages back to back.
  *   Arguments as csa_index_score and csa_topk (k = top-k, 1 <= k <= 2048);
  *   scores [B,S,Nc] fp32 or NULL (then not written, except in the workspace);
  *   idx [B,S,k] int32 output;
@@ -141,19 +142,25 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w,
                    float* scores, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
- * The fused path of csa_index_topk as two calls (decode shapes only: S <= 4,
- * ceil(Nc / 4096) * k <= 36864, FP8, H_I = 64, d_I = 128; other shapes return
- * CSA_ERR_UNSUPPORTED).  [KV-COMP] section 9.4: the row's top-k lies in the union of
- * the top-k sets of its segments.
+ * The fused path of csa_index_topk as two calls (decode shapes only: S <= 4, FP8,
+ * H_I = 64, d_I = 128, and G = ceil(Nc / 4096) segment lists of k candidates that merge
+ * in one level (G*k <= 36864) or in two (groups of M = clamp(round(sqrt(G)), 2,
+ * floor(36864 / k)) lists first, then ceil(G / M) * k <= 36864 pairs); other shapes
+ * return CSA_ERR_UNSUPPORTED).  [KV-COMP] section 9.4: the row's top-k lies in the union
+ * of the top-k sets of its segments (and of groups of segments).
  *
  * csa_index_score_segments: the scores of csa_index_score (written when `scores` is not
  *   NULL) and, for every 4096-entry segment g of row r, the k best entries of the
- *   segment as pairs cand[r][g][j] = (key, entry) of two uint32: key = an
- *   order-preserving image of the score (0 = empty slot: fewer than k candidates),
- *   entries in ascending order.  cand: caller device memory of at least
- *   csa_index_segments_size(B, S, Nc, k) bytes, 16-byte aligned.
+ *   segment as pairs (key, entry) of two uint32: key = an order-preserving image of the
+ *   score (0 = empty slot: fewer than k candidates), entries in ascending order.  cand:
+ *   caller device memory of at least csa_index_segments_size(B, S, Nc, k) bytes,
+ *   16-byte aligned, one equal share per row r = b*S + s; pair j of segment g is
+ *   element g*k + j of row r's share (with one merge level the shares are exactly G*k
+ *   pairs: cand[r][g][j]).
  * csa_topk_merge: idx [B,S,k] = the k best candidates of each row (key descending, then
- *   lower entry), ascending, padded with -1: exactly csa_topk of the same scores.
+ *   lower entry), ascending, padded with -1: exactly csa_topk of the same scores.  With two
+ *   levels it writes the first level's pairs into the rest of each row's share of cand
+ *   (the segment pairs stay intact).
  * ------------------------------------------------------------------------------ */
 size_t csa_index_segments_size(int B, int S, int Nc, int k);
 

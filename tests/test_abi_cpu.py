@@ -80,6 +80,8 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.csa_topk_merge(fake, 32, 1, 32768, 512, None, None) == 1
     assert lib.csa_index_segments_size(32, 1, 32768, 512) == 32 * 8 * 512 * 8
     assert lib.csa_index_segments_size(1, 8, 3000, 128) == 0
+    # Pro shape: 64 segment lists of 1024 merge in two levels (groups of 8): room for both
+    assert lib.csa_index_segments_size(4, 1, 262144, 1024) == 4 * (64 + 8) * 1024 * 8
     # attention: Ls < S, unsupported bf16 shape, non-positive scale
     assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
                                fake, None, None, 0, None) == 1

@@ -88,6 +88,13 @@ def test_pro_decode_full(lib):
     a = I.decode_inputs(sh).arrays
     scores, idx, out, lse = _decode_chain(lib, sh, a)
     _check_decode(sh, a, scores, idx, out, lse, sample=[0, 3])
+    # the bench's scoring + top-k call (segment top-k, two merge levels): the same selection
+    idx2 = torch.empty(sh.B, 1, sh.k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lib.index_topk_workspace_size(sh.B, 1, sh.n_c, sh.k), dtype=torch.uint8, device="cuda")
+    lib.csa_index_topk(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]), dev(a["kI_scale"]),
+                       dev(a["q_pos"]), m=sh.m, k=sh.k, idx=idx2, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), idx), "fused scoring + top-k differs from the stage chain (Pro)"
 
 
 def test_hca_decode_full(lib):

@@ -341,7 +341,9 @@ def test_decode_chain_graph_replay(lib):
     (2, 2, 9000, 300, 4 * 2500 + 2, True),         # causal limit inside the row, 2 queries
     (1, 1, 3000, 2048, 4 * 3000 - 1, True),        # k above the visible count
     (2, 8, 3000, 128, 4 * 3000 + 40, True),        # prefill shape: the two stages back to back
-    (1, 1, 262144, 1024, 4 * 262144 - 1, False),   # Pro shape: too many segment candidates, back to back
+    (1, 1, 262144, 1024, 4 * 262144 - 1, False),   # Pro shape: 64 x 1024 candidates, two merge levels
+    (2, 1, 86000, 2048, 4 * 86000 - 1, True),      # two levels, the last group of segments ragged
+    (1, 1, 150000, 1024, 4 * 100000 + 1, False),   # two levels, segments past the causal limit empty
     (32, 1, 32768, 512, 4 * 32768 - 1, False),     # V4-Flash decode batch
     (2, 1, 20000, 512, 4 * 20000 - 1, True),       # five segments, the last ragged
 ])
