@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_DIR", "BENCH_LOG"),
+                   help="write the prefill indexer's MFMA counter summary into profiles/")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) made "
                         "with --calibrate-copy into the committed traffic summary")
@@ -136,8 +138,52 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print(open(out).read())
 
 
+MFMA_CMD = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+            "--kernel-include-regex index_score_fp8_prefill --output-format csv -d <dir> -o run -- "
+            "python3 bench.py --steps 2 --warmup 1 --no-other --no-cpu-baseline --eager")
+
+
+def summarize_mfma(counter_dir, bench_log):
+    """Writes profiles/index_score_prefill_chunk8192_mfma.txt: MFMA utilisation and MFMA
+    flops of the prefill indexer from rocprofv3 counters (MfmaUtil = busy MFMA cycles over
+    all SIMDs / (active GPU cycles x SIMDs)), beside the same run's event-timed duration."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if "index_score_fp8_prefill" in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no index_score_fp8_prefill dispatch in the counter files")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    n = len(vals.get("MfmaUtil", []))
+    line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
+    pf = json.loads(line)["prefill_indexer"]
+    flops = mean["MfmaFlopsBF16"]
+    out = os.path.join(ROOT, "profiles", "index_score_prefill_chunk8192_mfma.txt")
+    with open(out, "w") as fo:
+        fo.write("# MFMA use of index_score_fp8_prefill, CSA prefill chunk (8192 queries x 34816 entries,\n")
+        fo.write("# 64 heads x 128, FP8 codes contracted on bf16 MFMA), from rocprofv3 counters; the\n")
+        fo.write("# duration is the same run's event timing of the prefill sub-benchmark.\n")
+        fo.write(f"# command: cd /tmp && {MFMA_CMD}\n")
+        fo.write(f"dispatches = {n}\n")
+        fo.write(f"mfma_util_percent = {mean['MfmaUtil']:.1f}\n")
+        fo.write(f"mfma_busy_cycles_all_simds = {mean['SQ_VALU_MFMA_BUSY_CYCLES']:.4g}\n")
+        fo.write(f"grbm_gui_active = {mean['GRBM_GUI_ACTIVE']:.4g}\n")
+        fo.write(f"mfma_flops_bf16_per_dispatch = {flops:.4g}\n")
+        fo.write(f"algorithmic_flops_causal = {pf['causal_flops']:.4g}\n")
+        fo.write(f"event_ms = {pf['ms']:.4f}\n")
+        fo.write(f"counter_tflops = {flops / (pf['ms'] * 1e-3) / 1e12:.1f}  (peak bf16 {BF16_PEAK_TFLOPS:.0f})\n")
+        fo.write(f"algorithmic_tflops = {pf['tflops']:.1f}\n")
+    print(open(out).read())
+
+
 def main():
     args = parse()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_counters:
         base = "rocprofv3 --pmc {} --output-format csv -d <dir> -o run -- python3 bench.py --steps 5 --warmup 2 " \
                "--no-prefill --no-other --no-cpu-baseline --calibrate-copy"
