@@ -143,6 +143,32 @@ MFMA_CMD = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRB
             "python3 bench.py --steps 2 --warmup 1 --no-other --no-cpu-baseline --eager")
 
 
+def device_info(torch, dev):
+    """The GPU the run used and a practical HBM rate: a 1 GiB device-to-device copy (read +
+    write), timed with events, best of 5."""
+    props = torch.cuda.get_device_properties(dev)
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(5):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del a, b
+    info = {"name": props.name, "compute_units": props.multi_processor_count,
+            "memory_gib": round(props.total_memory / (1 << 30), 1),
+            "copy_1gib_gbs": 2 * n / (best * 1e-3) / 1e9}
+    for key in ("gcnArchName", "clock_rate", "L2_cache_size"):
+        if hasattr(props, key):
+            info[key] = getattr(props, key)
+    return info
+
+
 def summarize_mfma(counter_dir, bench_log):
     """Writes profiles/index_score_prefill_chunk8192_mfma.txt: MFMA utilisation and MFMA
     flops of the prefill indexer from rocprofv3 counters (MfmaUtil = busy MFMA cycles over
@@ -370,6 +396,7 @@ def main():
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
                      "traffic": measured_traffic("index_score.hip", "index_score_segments")},
         "input_generation_s": t_gen,
+        "device": device_info(torch, dev),
     }
 
     if not args.no_prefill:
