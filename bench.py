@@ -400,7 +400,9 @@ def main():
     }
 
     if not args.no_prefill:
-        result["prefill_indexer"] = bench_prefill_indexer(torch, L, I, dev)
+        result["prefill_indexer"], pf_scores = bench_prefill_indexer(torch, L, I, dev)
+        result["prefill_topk"] = bench_prefill_topk(torch, L, pf_scores, I.PREFILL.k)
+        del pf_scores
     if not args.no_other:
         result["pro_decode"] = bench_csa_decode(torch, L, I, dev, I.PRO_DECODE, n_sets=2)
         result["hca_decode"] = bench_hca_decode(torch, L, I, dev)
@@ -570,10 +572,31 @@ def bench_prefill_indexer(torch, L, I, dev, reps=10):
     nvis = np.minimum(n, (pos[0] + 1) // sh.m)
     flops = float(np.sum(nvis)) * sh.H_I * sh.d_I * 2
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": "csa_prefill_chunk8192_ctx128k_indexer", "ms": ms, "causal_flops": flops,
-            "tflops": tflops, "frac_fp8_peak": tflops / FP8_PEAK_TFLOPS,
-            "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS,
-            "note": "contraction on bf16 MFMA (exact e4m3->bf16); FP8 MFMA accumulation misses the 1e-5 bound"}
+    res = {"workload": "csa_prefill_chunk8192_ctx128k_indexer", "ms": ms, "causal_flops": flops,
+           "tflops": tflops, "frac_fp8_peak": tflops / FP8_PEAK_TFLOPS,
+           "frac_bf16_peak": tflops / BF16_PEAK_TFLOPS,
+           "note": "contraction on bf16 MFMA (exact e4m3->bf16); FP8 MFMA accumulation misses the 1e-5 bound"}
+    return res, scores
+
+
+def bench_prefill_topk(torch, L, scores, k, reps=5):
+    """Top-k of the prefill chunk: the indexer's 8192 x 34816 scores (causal -inf tails) ->
+    8192 x 512 indices; every score is read once (the HBM bound)."""
+    rows, n = scores.shape[1], scores.shape[2]
+    idx = torch.empty(1, rows, k, dtype=torch.int32, device=scores.device)
+    ws = torch.empty(max(1, L.topk_workspace_size(rows, n, k)), dtype=torch.uint8, device=scores.device)
+    L.csa_topk(scores, k, idx, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.csa_topk(scores, k, idx, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    byts = scores.numel() * 4 + idx.numel() * 4
+    return {"workload": "csa_prefill_chunk8192_topk512", "ms": ms, "rows": rows, "entries": n,
+            "bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9, "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def cpu_baseline(host_sets, sh):
