@@ -210,9 +210,14 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
     const float scale = static_cast<float>(kTkBins) * __builtin_amdgcn_rcpf(range);
     bool ok = range > 0.0f && range <= 3.0e38f && scale <= 3.0e38f;
     int b = 0, remain = 0;
-    // small register sets keep each key's bin from the histogram pass for the next one
+    // each key's bin is kept from the histogram pass for the next one: as ints for small
+    // register sets, two per register (bin + 1 in 16 bits, 0 = no candidate) for large ones
     constexpr bool kKeepBins = NU * KPT <= 16;
+    constexpr int kPacked = kKeepBins ? 1 : (NU * KPT + 1) / 2;
     int bins[kKeepBins ? NU : 1][kKeepBins ? KPT : 1];
+    uint32_t pbins[kPacked];
+#pragma unroll
+    for (int i = 0; i < kPacked; ++i) pbins[i] = 0u;
     auto bin_of = [&](uint32_t kv) __attribute__((always_inline)) {
       return kv != 0u ? min(kTkBins - 1, static_cast<int>((key_value(kv) - lo) * scale)) : -1;
     };
@@ -226,7 +231,12 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
 #pragma unroll
         for (int s = 0; s < KPT; ++s) {
           const int bn = bin_of(key[u][s]);
-          if constexpr (kKeepBins) bins[u][s] = bn;
+          if constexpr (kKeepBins) {
+            bins[u][s] = bn;
+          } else {
+            const int i = KPT * u + s;
+            pbins[i >> 1] |= static_cast<uint32_t>(bn + 1) << (16 * (i & 1));
+          }
           atomicAdd(&sh.hist[bn >= 0 ? hist_slot<kTkPB>(bn) : junk], 1u);
         }
       __syncthreads();                                                // barrier 2
@@ -244,8 +254,12 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
         for (int s = 0; s < KPT; ++s) {
           const uint32_t kv = key[u][s];
           int bn;
-          if constexpr (kKeepBins) bn = bins[u][s];
-          else bn = bin_of(kv);
+          if constexpr (kKeepBins) {
+            bn = bins[u][s];
+          } else {
+            const int i = KPT * u + s;
+            bn = static_cast<int>((pbins[i >> 1] >> (16 * (i & 1))) & 0xffffu) - 1;
+          }
           g += __popcll(__ballot(bn > b));
           const uint64_t m = __ballot(bn == b);
           if (m != 0) {
@@ -364,6 +378,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
         if (kv == T) t = r++ < need_eq;
         if (t) { taken |= 1ull << (KPT * u + s); ++c; }
       }
+      obase[u] = base[u] + sel_before[u] + wave_incl_scan(c) - c;
     } else {
 #pragma unroll
       for (int s = 0; s < KPT; ++s) {
@@ -371,8 +386,24 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
         const int pos = kChunk * u + KPT * tid + s;
         if (kv > T || (kv == T && pos <= posT)) { taken |= 1ull << (KPT * u + s); ++c; }
       }
+      obase[u] = c;                      // this lane's count for now; prefixes below
     }
-    obase[u] = base[u] + sel_before[u] + wave_incl_scan(c) - c;
+  }
+  if (!exact) {
+    // lane prefixes of three chunks' counts per scan: a lane's count is <= KPT, so a
+    // chunk's wave total (<= 64 * KPT <= 1023) fits a 10-bit field without carries
+    static_assert(64 * KPT < 1024, "10-bit count fields");
+#pragma unroll
+    for (int u0 = 0; u0 < NU; u0 += 3) {
+      int packed = 0;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (u0 + j < NU) packed |= obase[u0 + j] << (10 * j);
+      const int excl = wave_incl_scan(packed) - packed;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (u0 + j < NU) obase[u0 + j] = base[u0 + j] + sel_before[u0 + j] + ((excl >> (10 * j)) & 1023);
+    }
   }
   return kk;
 }
