@@ -93,7 +93,6 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
     plain device copy of COPY_BYTES (read and written once)."""
     import csv
     import glob
-    import hashlib
 
     def per_kernel(d, counter):
         vals = {}
@@ -119,8 +118,7 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
     idx_w = pick(wv, "index_score_fp8_decode<true>")
     fetch = sum(idx_f) / len(idx_f) * 1024.0 * f_scale
     write = sum(idx_w) / len(idx_w) * 1024.0 * w_scale
-    src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", "index_score.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = sources_sha256(INDEXER_SOURCES)
     out = os.path.join(ROOT, "profiles", "index_score_segments_flash_decode_b32_traffic.txt")
     with open(out, "w") as fo:
         fo.write("# HBM traffic of index_score_fp8_decode<true> (csa_index_score_segments), V4-Flash decode\n")
@@ -134,7 +132,8 @@ def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
         fo.write(f"traffic_fetch_bytes = {fetch:.0f}\ntraffic_write_bytes = {write:.0f}\n")
         fo.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
         fo.write(f"algorithmic_bytes_per_launch = {index_segments_bytes(32, 1, 32768, 64, 128, 512)}\n")
-        fo.write(f"source_sha256 = {sha}\n")
+        fo.write(f"sources = {' + '.join(INDEXER_SOURCES)}\n")
+        fo.write(f"sources_sha256 = {sha}\n")
     print(open(out).read())
 
 
@@ -394,7 +393,7 @@ def main():
         "roofline": {"kernel": "index_score_fp8_decode<true>", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
-                     "traffic": measured_traffic("index_score.hip", "index_score_segments")},
+                     "traffic": measured_traffic(INDEXER_SOURCES, "index_score_segments")},
         "input_generation_s": t_gen,
         "device": device_info(torch, dev),
     }
@@ -415,22 +414,31 @@ def main():
     print(json.dumps(result))
 
 
-def measured_traffic(source, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
-    kernel's source has changed since the counters were taken (the summary records the
-    sha256 of the source file it measured)."""
+# Sources compiled into the indexer kernel: its counter summary is valid only for them.
+INDEXER_SOURCES = ("index_score.hip", "select.hpp", "common.hpp")
+
+
+def sources_sha256(names):
     import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", n), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(sources, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when a
+    source of the kernel has changed since the counters were taken (the summary records
+    the sha256 of the sources it measured)."""
     summary = os.path.join(ROOT, "profiles", f"{kernel}_flash_decode_b32_traffic.txt")
-    src = os.path.join(ROOT, "compressed_sparse_kv_amd", "csrc", source)
-    if not (os.path.exists(summary) and os.path.exists(src)):
+    if not os.path.exists(summary):
         return None
     fields = {}
     for line in open(summary):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("sources_sha256") != sources_sha256(sources) or "traffic_bytes_per_launch" not in fields:
         return None
     return float(fields["traffic_bytes_per_launch"])
 
