@@ -395,7 +395,8 @@ def main():
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
                      "traffic": measured_traffic(INDEXER_SOURCES, "index_score_segments")},
         "input_generation_s": t_gen,
-        "device": device_info(torch, dev),
+        # (not under --calibrate-copy: its copy must stay the only large one of a counter run)
+        "device": None if args.calibrate_copy else device_info(torch, dev),
     }
 
     if not args.no_prefill:
