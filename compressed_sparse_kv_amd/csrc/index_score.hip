@@ -161,12 +161,46 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     }                                                                                               \
     sring[(gi_) % 3] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                         \
   } while (0)
+  // The query (64 x 128 codes, 8 KiB), its head weights and scales are read once per
+  // workgroup, ahead of the keys, and shared through LDS: loads complete in order, so a
+  // query each wave read behind its first key groups would wait for all of them, and
+  // every wave reading the whole query multiplies the start burst by the waves.
+  constexpr int kQv = kIH * kID / 16 / kDecThreads;   // 16-byte pieces per thread
+  __shared__ v4u qlds[kIH * kID / 16];
+  __shared__ float wlds[2 * kIH];                    // w, then qs
+  v4u qv[kQv];
+  float wq = 0.0f;
+  {
+    const v4u* qsrc = reinterpret_cast<const v4u*>(q8 + row * (kIH * kID));
+#pragma unroll
+    for (int i = 0; i < kQv; ++i) qv[i] = qsrc[threadIdx.x + i * kDecThreads];
+    if (threadIdx.x < 2 * kIH) wq = threadIdx.x < kIH ? w[row * kIH + threadIdx.x] : qs[row * kIH + threadIdx.x - kIH];
+  }
   CSA_DEC_LOAD(0);
   CSA_DEC_LOAD(1);
+  __builtin_amdgcn_sched_barrier(0);      // every load above the query's staging
+#pragma unroll
+  for (int i = 0; i < kQv; ++i) qlds[threadIdx.x + i * kDecThreads] = qv[i];
+  if (threadIdx.x < 2 * kIH) wlds[threadIdx.x] = wq;
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): this wave's LDS writes done; key loads stay in flight
+  __builtin_amdgcn_s_barrier();
 
+  // A operand: lane l, head block hb: head 16*hb + l%16, codes 32*(l/16) .. +31
   v8s a[4][4];
   float wv[16];
-  load_query(q8, qs, w, row, a, wv);
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int p = ((16 * hb + (l & 15)) * kID + 32 * (l >> 4)) / 16;
+    const v4u lo = qlds[p], hi = qlds[p + 1];
+    e4m3x32_to_bf16(v8i{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]), static_cast<int>(lo[3]),
+                        static_cast<int>(hi[0]), static_cast<int>(hi[1]), static_cast<int>(hi[2]), static_cast<int>(hi[3])},
+                    a[hb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * hb + 4 * (l >> 4) + i;
+      wv[hb * 4 + i] = wlds[h] * wlds[kIH + h];
+    }
+  }
 
   __shared__ uint32_t kst[kTopk ? kDecEntWG : 1];       // keys of the workgroup's entries
 #pragma unroll
