@@ -474,15 +474,26 @@ def bench_csa_decode(torch, L, I, dev, sh, n_sets=2, reps=20):
     at_ws = torch.empty(max(1, L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)), dtype=torch.uint8,
                         device=dev)
 
+    cand = torch.empty(L.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
+
     def step(i):
         s = sets[i % len(sets)]
         L.csa_index_topk(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, idx=idx, ws=it_ws)
         L.csa_sparse_attn(s["q"], s["kv"], idx, s["swa"], s["sink"], W=sh.W, out=out, ws=at_ws)
 
+    def step_fused(i):
+        # the headline step's two calls: scores with segment top-k, then (first merge
+        # level,) selection and attention in one call
+        s = sets[i % len(sets)]
+        L.csa_index_score_segments(s["q8"], s["qs"], s["w"], s["k8"], s["ks"], s["pos"], m=sh.m, k=k, cand=cand)
+        L.csa_topk_sparse_attn(s["q"], s["kv"], cand, s["swa"], s["sink"], k=k, W=sh.W, out=out, ws=at_ws)
+
     ms = _timed(torch, step, reps)
+    ms_fused = _timed(torch, step_fused, reps)
     byts = decode_step_bytes(sh)
     return {"workload": sh.name, "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms, "step_bytes": byts,
-            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "input_sets": n_sets}
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "input_sets": n_sets,
+            "ms_per_step_segments_then_fused_attention": ms_fused}
 
 
 def bench_hca_decode(torch, L, I, dev, reps=20):

@@ -24,8 +24,12 @@ int launch_index_segments(const void*, const float*, const float*, const void*, 
                           int, int, int, int, float*, uint2*, hipStream_t);
 int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
 size_t topk_merge_pairs_per_row(int, int);
-int launch_topk_attention(const void*, const void*, const uint2*, int, const int64_t*, const void*, const float*, float,
-                          int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t, hipStream_t);
+int launch_topk_attention(const void*, const void*, const uint2*, int, size_t, const int64_t*, const void*,
+                          const float*, float, int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t,
+                          hipStream_t);
+int topk_attention_max_cand();
+int topk_merge_group(int, int);
+int launch_topk_merge_first(const uint2*, int, int, int, size_t&, hipStream_t);
 }  // namespace csa
 
 using namespace csa;
@@ -234,10 +238,22 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand, c
   CSA_REQUIRE(cand && k >= 1 && k <= 2048);
   CSA_REQUIRE(aligned16(cand) && aligned16(ws));
   if (dtype != CSA_BF16 || !index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
-  const long long n_cand = static_cast<long long>(index_topk_segments(Nc)) * k;
-  if (n_cand > 4096) return CSA_ERR_UNSUPPORTED;
-  return launch_topk_attention(q, kv_comp, static_cast<const uint2*>(cand), static_cast<int>(n_cand), q_pos, swa,
-                               sink, scale, B, S, Nc, k, Ls, W, out, lse, idx, ws, ws_bytes, as_stream(stream));
+  // the set the attention selects from: the segment pairs, or the first merge level's
+  // when the segments hold more pairs than one workgroup selects from at once
+  const int G = index_topk_segments(Nc);
+  const int M = topk_merge_group(G, k);
+  if (M < 0) return CSA_ERR_UNSUPPORTED;
+  const long long n_sel = M == 0 ? static_cast<long long>(G) * k : static_cast<long long>((G + M - 1) / M) * k;
+  if (n_sel > topk_attention_max_cand()) return CSA_ERR_UNSUPPORTED;
+  // every check before the first level is enqueued
+  if (ws_bytes < attn_workspace_bytes(B, S, H, c, std::min(W, Ls) + k, dtype)) return CSA_ERR_WORKSPACE;
+  const int rows = B * S;
+  const uint2* pairs = static_cast<const uint2*>(cand);
+  size_t offset = 0;
+  const int n_cand = launch_topk_merge_first(pairs, rows, G, k, offset, as_stream(stream));
+  if (n_cand < 0) return CSA_ERR_HIP;
+  return launch_topk_attention(q, kv_comp, pairs + offset, n_cand, topk_merge_pairs_per_row(G, k), q_pos, swa, sink,
+                               scale, B, S, Nc, k, Ls, W, out, lse, idx, ws, ws_bytes, as_stream(stream));
 }
 
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m, const void* swa, const float* sink,

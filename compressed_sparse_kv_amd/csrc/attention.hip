@@ -73,9 +73,10 @@ struct AttnShape {
   static constexpr int kLdsFixed = kRing * kChunkBytes + kSxBufs * kSxBytes + kValidSlots * kWaves * 4;
   static constexpr int kLdsMax = kLdsFixed + kMaxSplitChunks * kRows * 8;
   static_assert(kLdsMax <= 160 * 1024, "LDS of one compute unit");
-  // candidate selection (8 keys per thread) and its result sit in the ring before it is used
+  // candidate selection (8 or 16 keys per thread) and its result sit in the ring before it is used
   static constexpr int kMaxCand = 8 * kThreads;
-  static_assert(sizeof(TkShared) + 4 * kMaxCand <= kRing * kChunkBytes, "selection fits the ring");
+  static constexpr int kMaxCand2 = 16 * kThreads;
+  static_assert(sizeof(TkShared) + 4 * kMaxCand2 <= kRing * kChunkBytes, "selection fits the ring");
   static_assert(kRowsPerWave == 4 || kRowsPerWave == 2, "the row staging moves 4 or 2 rows per wave");
   static_assert(kWGHG >= 1 && kWGHG <= kNHG, "head groups per workgroup");
 };
@@ -99,10 +100,13 @@ __device__ __attribute__((aligned(1024))) uint16_t g_zero_rows[kZeroRows * kAC];
 constexpr int kSrcIdx = 0;     // idx[q][0..k): selected entries, -1 = none
 constexpr int kSrcDense = 1;   // every visible entry (HCA)
 constexpr int kSrcCand = 2;    // the k best of the query's segment candidates, selected here
+constexpr int kSrcCand2 = 3;   // the same from up to twice as many candidates (16 per thread)
 
 template <int kSrc, int kParts, int kWaves>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   constexpr bool kDense = kSrc == kSrcDense;
+  constexpr bool kCand = kSrc == kSrcCand || kSrc == kSrcCand2;
+  constexpr int kCandChunks = kSrc == kSrcCand2 ? 2 : 1;   // 8 candidates per thread per chunk
   using Sh = AttnShape<kParts, kWaves>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* ring = smem;                                                          // [slot][32 rows]
@@ -144,42 +148,49 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   }
 
   // Selection from candidates: the query's n_cand (key, entry) pairs (segment-major, each
-  // segment in entry order, key 0 = empty) -> the k best in entry order, as the top-k
-  // stage returns them, in LDS (sel) for the row table; the first workgroup of the
-  // query also writes them to idx_out.  Every workgroup of the query selects for itself
-  // (the same result); the ring is free until the pipeline starts.
+  // segment in entry order, key 0 = empty; rows cand_stride pairs apart) -> the k best in
+  // entry order, as the top-k stage returns them, in LDS (sel) for the row table; the
+  // first workgroup of the query also writes them to idx_out.  Every workgroup of the
+  // query selects for itself (the same result); the ring is free until the pipeline starts.
   int32_t* sel = reinterpret_cast<int32_t*>(ring + sizeof(TkShared));
-  if constexpr (kSrc == kSrcCand) {
+  if constexpr (kCand) {
+    constexpr int NU = kCandChunks;
     TkShared& tsh = *reinterpret_cast<TkShared*>(ring);
-    const uint2* cq = a.cand + static_cast<size_t>(qi) * a.n_cand;
-    const int p0 = 8 * static_cast<int>(threadIdx.x);
-    uint32_t key[1][8], ent[8];
-    if ((a.n_cand & 1) == 0 && p0 + 7 < a.n_cand) {
+    const uint2* cq = a.cand + static_cast<size_t>(qi) * a.cand_stride;
+    uint32_t key[NU][8], ent[NU][8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 v = reinterpret_cast<const uint4*>(cq + p0)[j];
-        key[0][2 * j] = v.x; ent[2 * j] = v.y;
-        key[0][2 * j + 1] = v.z; ent[2 * j + 1] = v.w;
-      }
-    } else {
+    for (int u = 0; u < NU; ++u) {
+      const int p0 = 8 * (static_cast<int>(threadIdx.x) + u * Sh::kThreads);
+      if ((a.n_cand & 1) == 0 && p0 + 7 < a.n_cand) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint2 v = p0 + j < a.n_cand ? cq[p0 + j] : make_uint2(0u, 0u);
-        key[0][j] = v.x; ent[j] = v.y;
+        for (int j = 0; j < 4; ++j) {
+          const uint4 v = reinterpret_cast<const uint4*>(cq + p0)[j];
+          key[u][2 * j] = v.x; ent[u][2 * j] = v.y;
+          key[u][2 * j + 1] = v.z; ent[u][2 * j + 1] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint2 v = p0 + j < a.n_cand ? cq[p0 + j] : make_uint2(0u, 0u);
+          key[u][j] = v.x; ent[u][j] = v.y;
+        }
       }
     }
     uint64_t taken;
-    int obase[1];
-    const int kk = select_regs<Sh::kThreads, 8, 1>(tsh, key, a.k, taken, obase);
+    int obase[NU];
+    const int kk = select_regs<Sh::kThreads, 8, NU>(tsh, key, a.k, taken, obase);
     int32_t* io = a.idx_out && split == 0 && hp == 0 ? a.idx_out + static_cast<size_t>(qi) * a.k : nullptr;
-    int o = obase[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((taken >> j) & 1ull) {
-        sel[o] = static_cast<int32_t>(ent[j]);
-        if (io) io[o] = static_cast<int32_t>(ent[j]);
-        ++o;
-      }
+    for (int u = 0; u < NU; ++u) {
+      int o = obase[u];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((taken >> (8 * u + j)) & 1ull) {
+          sel[o] = static_cast<int32_t>(ent[u][j]);
+          if (io) io[o] = static_cast<int32_t>(ent[u][j]);
+          ++o;
+        }
+    }
     for (int p = kk + static_cast<int>(threadIdx.x); p < a.k; p += Sh::kThreads) {
       sel[p] = -1;
       if (io) io[p] = -1;
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
       if (slot < n_swa) {
         p = reinterpret_cast<uint64_t>(swab + static_cast<size_t>(w_lo + slot) * kAC);
       } else if (slot < n_slots) {
-        const int j = kDense ? slot - n_swa : kSrc == kSrcCand ? sel[slot - n_swa] : idxq[slot - n_swa];
+        const int j = kDense ? slot - n_swa : kCand ? sel[slot - n_swa] : idxq[slot - n_swa];
         if (j >= 0 && j < a.Nc) p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kAC);
       }
       rowptr[e] = p;
@@ -804,6 +815,8 @@ static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
         hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
         hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand2, kParts, kWaves>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess)
       return CSA_ERR_HIP;
     raised.fetch_or(bit, std::memory_order_release);
@@ -812,6 +825,7 @@ static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
   const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;
   if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
   else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  else if (src == kSrcCand2) hipLaunchKernelGGL((attn_bf16<kSrcCand2, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
   else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
@@ -858,22 +872,31 @@ static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, i
   return a;
 }
 
-// Top-k selection from segment candidates fused with the bf16 attention: cand holds
-// n_cand = G*k (key, entry) pairs per query (n_cand <= 4096); idx_out (optional) receives
-// the selection.  The caller has checked shapes and the workspace.
-int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int n_cand, const int64_t* q_pos,
-                          const void* swa, const float* sink, float scale, int B, int S, int Nc, int k, int Ls,
-                          int W, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
+// Largest candidate set per row the fused selection takes (16 per thread).
+int topk_attention_max_cand() { return std::min(NarrowShape::kMaxCand2, WideShape::kMaxCand2); }
+
+// Top-k selection from candidates fused with the bf16 attention: row r's n_cand (key,
+// entry) pairs start at cand + r * cand_stride (the segment pairs, or a first merge
+// level's; 8 per thread up to kMaxCand, else 16); idx_out (optional) receives the
+// selection.  The caller has checked shapes and the workspace.
+
+int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int n_cand, size_t cand_stride,
+                          const int64_t* q_pos, const void* swa, const float* sink, float scale, int B, int S, int Nc,
+                          int k, int Ls, int W, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
                           hipStream_t st) {
   const int max_rows = std::min(W, Ls) + k;
   if (ws_bytes < attn_workspace_bytes(B, S, kAH, kAC, max_rows, CSA_BF16)) return CSA_ERR_WORKSPACE;
-  if (n_cand > NarrowShape::kMaxCand || n_cand > WideShape::kMaxCand || k > n_cand) return CSA_ERR_UNSUPPORTED;
+  if (n_cand > topk_attention_max_cand() || k > n_cand || cand_stride < static_cast<size_t>(n_cand))
+    return CSA_ERR_UNSUPPORTED;
   AttnArgs a = attn_args(q, kv, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, out, lse);
   a.cand = cand;
   a.n_cand = n_cand;
+  a.cand_stride = cand_stride;
   a.idx_out = idx_out;
-  return run_attn_bf16(kSrcCand, a, max_rows, ws, st);
+  const bool one = n_cand <= NarrowShape::kMaxCand && n_cand <= WideShape::kMaxCand;
+  return run_attn_bf16(one ? kSrcCand : kSrcCand2, a, max_rows, ws, st);
 }
+
 
 int launch_attention(bool dense, const void* q, const void* kv, const int32_t* idx, const int64_t* q_pos, int m,
                      const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc,

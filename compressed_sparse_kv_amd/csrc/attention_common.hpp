@@ -39,8 +39,9 @@ struct AttnArgs {
   float* lse;
   float* part_o;             // [B*S, nsplit, H, c] fp32, unnormalised
   float* part_ml;            // [B*S, nsplit, H, 2]: reference max (log2 units), sum
-  const uint2* cand;         // [B*S, n_cand] (key, entry) pairs of the segment top-k sets
+  const uint2* cand;         // (key, entry) pairs of the segment top-k sets, n_cand per row
   int n_cand;
+  size_t cand_stride;        // pairs from one row of cand to the next
   int32_t* idx_out;          // [B*S, k] the selection made from cand, or null
 };
 

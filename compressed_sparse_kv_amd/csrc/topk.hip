@@ -324,4 +324,22 @@ int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, h
   return CSA_OK;
 }
 
+// The first merge level alone (for the fused selection + attention, which finishes the
+// selection itself): writes the cdiv(G, M) * k level-one pairs of each row after its G * k
+// segment pairs.  Returns the number of candidate pairs per row the caller selects from
+// (G * k when one level is enough, nothing launched) and where they start, or < 0.
+int launch_topk_merge_first(const uint2* cand, int rows, int G, int k, size_t& offset, hipStream_t st) {
+  const int M = topk_merge_group(G, k);
+  if (M < 0) return -1;
+  offset = 0;
+  if (M == 0) return G * k;
+  const size_t per_row = topk_merge_pairs_per_row(G, k);
+  const int G1 = cdiv(G, M);
+  uint2* lvl = const_cast<uint2*>(cand) + static_cast<size_t>(G) * k;
+  launch_merge_level<true>(cand, per_row, rows, G1, G * k, M * k, k, nullptr, lvl, st);
+  if (hipGetLastError() != hipSuccess) return -1;
+  offset = static_cast<size_t>(G) * k;
+  return G1 * k;
+}
+
 }  // namespace csa

@@ -236,9 +236,13 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
  * segments' top-k sets) and sections 9.5-9.6 (attention over window || selection).
  * Results identical to csa_topk_merge followed by csa_sparse_attn.
  *
- *   cand: the pairs of csa_index_score_segments for the same B, S, Nc and k.
+ *   cand: the pairs of csa_index_score_segments for the same B, S, Nc and k.  When
+ *   csa_topk_merge would take two levels, the first level runs here too and writes its
+ *   pairs into the rest of each row's share of cand, as csa_topk_merge does; the
+ *   attention workgroups then select from those.
  *   Supported: dtype CSA_BF16 (H = 64, c = 512), the shapes csa_index_score_segments
- *   accepts, and ceil(Nc / 4096) * k <= 4096; otherwise CSA_ERR_UNSUPPORTED.
+ *   accepts, and at most 8192 pairs per row to select from (the segment pairs, G*k, or
+ *   with two levels the first level's); otherwise CSA_ERR_UNSUPPORTED.
  *   idx [B,S,k] int32: receives the selection (as csa_topk_merge writes it), or NULL.
  *   Other arguments and the workspace (max_rows = min(W, Ls) + k) as csa_sparse_attn.
  * ------------------------------------------------------------------------------ */

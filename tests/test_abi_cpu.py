@@ -90,14 +90,16 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128,
                               fake, None, None, 0, None) == 1
     # fused selection + attention: null candidates, fp32 dtype, too many candidates per
-    # query (Pro: 64 segments x 1024), workspace too small for the split partials
+    # query after the first merge level (21 segments x 2048 -> 5 x 2048), workspace too
+    # small for the split partials (also with two merge levels: V4-Pro, 64 segments x 1024)
     fused = lambda cand, dt, Nc, k, ws_bytes: lib.csa_topk_sparse_attn(
         fake, fake, cand, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, fake, None, None, fake,
         ws_bytes, None)
     assert fused(None, 1, 32768, 512, 1 << 40) == 1
     assert fused(fake, 0, 32768, 512, 1 << 40) == 2
-    assert fused(fake, 1, 262144, 1024, 1 << 40) == 2
+    assert fused(fake, 1, 86000, 2048, 1 << 40) == 2
     assert fused(fake, 1, 32768, 512, 16) == 3
+    assert fused(fake, 1, 262144, 1024, 16) == 3
 
 
 def test_workspace_queries():

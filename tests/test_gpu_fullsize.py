@@ -95,6 +95,12 @@ def test_pro_decode_full(lib):
                        dev(a["q_pos"]), m=sh.m, k=sh.k, idx=idx2, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx2.cpu().numpy(), idx), "fused scoring + top-k differs from the stage chain (Pro)"
+    # the bench's Pro step: segment top-k, then the first merge level, the selection from
+    # its pairs and the attention in one call
+    idx3, out3, lse3 = _decode_step_fused(lib, sh, a)
+    assert np.array_equal(idx3, idx), "segment top-k + merge level + fused selection differ from csa_topk (Pro)"
+    assert torch.equal(out3, out), "fused selection + attention differs from csa_sparse_attn (Pro)"
+    assert np.array_equal(lse3, lse), "fused lse differs (Pro)"
 
 
 def test_hca_decode_full(lib):

@@ -393,6 +393,9 @@ def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     (2, 4, 6000, 512, 4 * 6000 - 1),       # four queries per sequence
     (64, 1, 4096, 512, 4 * 4096 - 1),      # many queries: the 64-head workgroup shape
     (1, 1, 8192, 2048, 4 * 8192 - 1),      # the largest selection: 2 x 2048 candidates, k = 2048
+    (2, 1, 65536, 512, 4 * 65536 - 1),     # 16 segments: 8192 candidates, 16 per thread, one level
+    (1, 1, 36000, 901, 4 * 36000 - 1),     # 9 segments x 901: an odd count of 16-per-thread candidates
+    (1, 1, 150000, 1024, 4 * 100000 + 1),  # 37 segments: first merge level (7 x 1024) in the call; empty tail
 ])
 def test_topk_sparse_attn_fused(lib, B, S, Nc, k, t):
     a = I.indexer_inputs(7000 + B + Nc + k, B, S, Nc)
