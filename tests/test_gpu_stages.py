@@ -443,3 +443,72 @@ def test_topk_sparse_attn_fused(lib, B, S, Nc, k, t):
                                       1 / math.sqrt(512), pos[:1], W)
     assert_bf16_output(bf16_f64(host_bits(out[:1])), o_ref, "fused attention vs oracle")
     assert_close(lse[:1].cpu().numpy(), l_ref, TOL_F32, "fused lse vs oracle")
+
+
+# ---------------------------------------------------------------------------------------
+# Stages 3 + 4a in one call on crafted candidate sets: equal keys (ties decided by the
+# lower entry), few distinct keys (the exact radix path of the selection core), and
+# segments with empty slots; 8 per thread, 16 per thread, and a first merge level
+# ---------------------------------------------------------------------------------------
+
+def _crafted_pairs(rng, rows, G, k, Nc, per_row, kind):
+    """rows x per_row (key, entry) uint32 pairs: segment g's k slots hold entries of
+    [4096 g, 4096 (g + 1)) in ascending order (key 0 = empty slot, entry 0)."""
+    pairs = np.zeros((rows, per_row, 2), np.uint32)
+    for r in range(rows):
+        for g in range(G):
+            lo, hi = 4096 * g, min(4096 * (g + 1), Nc)
+            n = min(k, hi - lo)
+            if kind == "sparse":
+                n = int(rng.integers(0, n + 1))
+            ent = np.sort(rng.choice(np.arange(lo, hi), size=n, replace=False)).astype(np.uint32)
+            if kind == "equal":
+                key = np.full(n, 0xBF800000, np.uint32)
+            elif kind == "few":
+                key = rng.choice(np.array([0xBF000000, 0xC0000000, 0xC0400000], np.uint32), size=n)
+            else:
+                key = rng.integers(1, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+            pairs[r, g * k:g * k + n, 0] = key
+            pairs[r, g * k:g * k + n, 1] = ent
+    return pairs
+
+
+def _select_pairs(pairs_row, k):
+    """The k best valid pairs (key descending, then lower entry), entries ascending, -1 padded."""
+    valid = pairs_row[pairs_row[:, 0] != 0]
+    order = np.lexsort((valid[:, 1], -valid[:, 0].astype(np.int64)))
+    sel = np.sort(valid[order[:k], 1].astype(np.int64))
+    return np.concatenate([sel, np.full(k - len(sel), -1, np.int64)])
+
+
+@pytest.mark.parametrize("B,G,k,kind", [
+    (2, 8, 512, "equal"), (2, 8, 512, "few"), (2, 8, 512, "sparse"),
+    (2, 16, 512, "equal"), (2, 16, 512, "few"), (2, 16, 512, "sparse"),
+    (1, 37, 1024, "few"), (1, 37, 1024, "sparse"),
+])
+def test_topk_sparse_attn_fused_crafted(lib, B, G, k, kind):
+    rng = np.random.default_rng(9100 + 7 * G + k + len(kind))
+    Nc = 4096 * G - 1000                    # ragged last segment
+    W, S = 128, 1
+    Ls = W
+    per_row = lib.index_segments_size(B, S, Nc, k) // (8 * B)
+    pairs = _crafted_pairs(rng, B * S, G, k, Nc, per_row, kind)
+    cand = torch.from_numpy(pairs.view(np.uint8).reshape(-1).copy()).cuda()
+    at = I.attention_inputs(9200 + G, B, S, Nc, Ls)
+    q, kv, swa, sink = dev_bf16(at["q_bf16"]), dev_bf16(at["kv_comp_bf16"]), dev_bf16(at["swa_bf16"]), dev(at["sink"])
+    idx_ref = torch.empty(B, S, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_merge(cand, B, S, Nc, k, idx_ref)
+    torch.cuda.synchronize()
+    want = np.stack([_select_pairs(pairs[r, :G * k], k) for r in range(B * S)]).reshape(B, S, k)
+    assert np.array_equal(idx_ref.cpu().numpy(), want), f"csa_topk_merge on {kind} candidates"
+    out_ref = torch.empty(B, S, 64, 512, dtype=torch.bfloat16, device="cuda")
+    lse_ref = torch.empty(B, S, 64, device="cuda")
+    lib.csa_sparse_attn(q, kv, idx_ref, swa, sink, W=W, out=out_ref, lse=lse_ref)
+    idx = torch.full_like(idx_ref, -7)
+    out = torch.full_like(out_ref, 7.0)
+    lse = torch.full_like(lse_ref, 7.0)
+    lib.csa_topk_sparse_attn(q, kv, cand, swa, sink, k=k, W=W, out=out, lse=lse, idx=idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref), f"fused selection on {kind} candidates"
+    assert torch.equal(out, out_ref), f"fused attention on {kind} candidates"
+    assert torch.equal(lse, lse_ref), f"fused lse on {kind} candidates"
