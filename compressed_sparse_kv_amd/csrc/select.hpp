@@ -39,7 +39,7 @@ struct alignas(16) TkShared {
   uint32_t hist[kTkHistWords];
   uint32_t ckey[kTkCandCap];
   int32_t cpos[kTkCandCap];
-  int cell_nz[kTkMaxChunks * kTkMaxWaves];   // candidates per (chunk, wave)
+  int cell_nz[kTkMaxChunks * kTkMaxWaves];   // candidates per wave
   int cell[kTkMaxChunks * kTkMaxWaves];      // taken elements per (chunk, wave) above bin b / > T
   int cell_eq[kTkMaxChunks * kTkMaxWaves];   // exact path: keys equal to T per (chunk, wave)
   uint32_t red_lo[kTkMaxWaves], red_hi[kTkMaxWaves];   // smallest and largest candidate key per wave
@@ -156,38 +156,36 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
   constexpr int kChunk = KPT * NT;              // positions per chunk
   const int tid = threadIdx.x, w = wave_index();
   const int l = static_cast<int>(lane_id());
-  // ---- 1. candidates per cell and the key range
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  // ---- 1. candidate count and key range, per thread and then per wave: no branches
+  // (key 0 is the smallest key, and key - 1 wraps it to the largest)
+  uint32_t kmin1 = 0xffffffffu, kmax = 0u;      // smallest candidate key - 1, largest key
+  int cnt = 0;
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    int cnt = 0;
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int s = 0; s < KPT; ++s) {
       const uint32_t kv = key[u][s];
-      cnt += __popcll(__ballot(kv != 0u));
-      if (kv != 0u) {
-        kmin = min(kmin, kv);
-        kmax = max(kmax, kv);
-      }
+      cnt += kv != 0u ? 1 : 0;
+      kmax = max(kmax, kv);
+      kmin1 = min(kmin1, kv - 1u);
     }
-    if (l == 0) sh.cell_nz[u * W + w] = cnt;
-  }
   for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid == 0) sh.ncand = 0;
   kmax = wave_max_u32(kmax);
-  kmin = ~wave_max_u32(~kmin);
-  if (l == 0) { sh.red_lo[w] = kmin; sh.red_hi[w] = kmax; }
+  kmin1 = ~wave_max_u32(~kmin1);
+  cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+  if (l == 0) { sh.red_lo[w] = kmin1; sh.red_hi[w] = kmax; sh.cell_nz[w] = cnt; }
   __syncthreads();                                                    // barrier 1
   int total = 0;
-  kmin = 0xffffffffu;
+  kmin1 = 0xffffffffu;
   kmax = 0u;
 #pragma unroll
   for (int i = 0; i < W; ++i) {
-    kmin = min(kmin, sh.red_lo[i]);
+    kmin1 = min(kmin1, sh.red_lo[i]);
     kmax = max(kmax, sh.red_hi[i]);
+    total += sh.cell_nz[i];
   }
-#pragma unroll
-  for (int i = 0; i < NU * W; ++i) total += sh.cell_nz[i];
+  const uint32_t kmin = kmin1 + 1u;             // used only when there are candidates
   const int kk = __builtin_amdgcn_readfirstlane(min(k, total));
   taken = 0;
 #pragma unroll
@@ -200,7 +198,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
   int eq_before[NU];             // exact path: keys == T before each of this wave's cells
   bool exact = false;
   int need_eq = 0;
-  const int* cells = sh.cell_nz;
+  const int* cells = sh.cell;
 #pragma unroll
   for (int u = 0; u < NU; ++u) { sel_before[u] = 0; eq_before[u] = 0; }
   if (kk < total) {
@@ -359,6 +357,16 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
 #pragma unroll
       for (int u = 0; u < NU; ++u) sel_before[u] = min(need_eq, eq_before[u]);
     }
+  } else {
+    // every candidate is taken: candidates per (chunk, wave) give the output slots
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      int c = 0;
+#pragma unroll
+      for (int s = 0; s < KPT; ++s) c += __popcll(__ballot(key[u][s] != 0u));
+      if (l == 0) sh.cell[u * W + w] = c;
+    }
+    __syncthreads();
   }
   // ---- 5. output slots: cells before this one, then lanes before this one
   int base[NU];
