@@ -481,17 +481,19 @@ def _select_pairs(pairs_row, k):
     return np.concatenate([sel, np.full(k - len(sel), -1, np.int64)])
 
 
-@pytest.mark.parametrize("B,G,k,kind", [
-    (2, 8, 512, "equal"), (2, 8, 512, "few"), (2, 8, 512, "sparse"),
-    (2, 16, 512, "equal"), (2, 16, 512, "few"), (2, 16, 512, "sparse"),
-    (1, 37, 1024, "few"), (1, 37, 1024, "sparse"),
+@pytest.mark.parametrize("B,S,G,k,kind", [
+    (2, 1, 8, 512, "equal"), (2, 1, 8, 512, "few"), (2, 1, 8, 512, "sparse"),
+    (2, 1, 16, 512, "equal"), (2, 1, 16, 512, "few"), (2, 1, 16, 512, "sparse"),
+    (1, 1, 37, 1024, "few"), (1, 1, 37, 1024, "sparse"),
+    (1, 3, 16, 512, "rand"),                # several queries per sequence, 16 per thread
+    (1, 2, 37, 1024, "equal"),              # several queries per sequence, first merge level
 ])
-def test_topk_sparse_attn_fused_crafted(lib, B, G, k, kind):
-    rng = np.random.default_rng(9100 + 7 * G + k + len(kind))
+def test_topk_sparse_attn_fused_crafted(lib, B, S, G, k, kind):
+    rng = np.random.default_rng(9100 + 7 * G + k + len(kind) + S)
     Nc = 4096 * G - 1000                    # ragged last segment
-    W, S = 128, 1
-    Ls = W
-    per_row = lib.index_segments_size(B, S, Nc, k) // (8 * B)
+    W = 128
+    Ls = W + S - 1
+    per_row = lib.index_segments_size(B, S, Nc, k) // (8 * B * S)
     pairs = _crafted_pairs(rng, B * S, G, k, Nc, per_row, kind)
     cand = torch.from_numpy(pairs.view(np.uint8).reshape(-1).copy()).cuda()
     at = I.attention_inputs(9200 + G, B, S, Nc, Ls)
