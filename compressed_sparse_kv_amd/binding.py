@@ -28,6 +28,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "C
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
+           "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn")
 
@@ -55,6 +56,9 @@ def _load() -> ctypes.CDLL:
         "csa_index_topk": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
         "csa_index_segments_size": ([i, i, i, i], sz),
         "csa_index_score_segments": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
+        "csa_index_keys_b16_size": ([i, i], sz),
+        "csa_index_keys_b16": ([vp, vp, i, i, vp], i),
+        "csa_index_score_segments_b16": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_merge": ([vp, i, i, i, i, vp, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
@@ -183,6 +187,34 @@ def csa_index_topk(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, k: int, id
 
 def index_segments_size(B, S, Nc, k) -> int:
     return int(_lib.csa_index_segments_size(B, S, Nc, k))
+
+
+def index_keys_b16_size(B, Nc) -> int:
+    return int(_lib.csa_index_keys_b16_size(B, Nc))
+
+
+def csa_index_keys_b16(k_codes, k_blocks, stream=None):
+    """k_blocks (uint8, index_keys_b16_size bytes) = k_codes [B,Nc,128] in 16-entry blocks."""
+    _dev(k_codes, k_blocks)
+    B, Nc, D = k_codes.shape
+    if k_blocks.numel() * k_blocks.element_size() < index_keys_b16_size(B, Nc):
+        raise ValueError("k_blocks smaller than index_keys_b16_size")
+    _check("csa_index_keys_b16", _lib.csa_index_keys_b16(_p(k_codes), _p(k_blocks), B, Nc, _stream(stream)))
+    return k_blocks
+
+
+def csa_index_score_segments_b16(q, q_scale, w, k_blocks, k_scale, q_pos, *, m: int, k: int, cand, scores=None,
+                                 stream=None):
+    """csa_index_score_segments with the keys in 16-entry blocks (csa_index_keys_b16)."""
+    _dev(q, q_scale, w, k_blocks, k_scale, q_pos, cand, scores)
+    B, S, H, D = q.shape
+    Nc = k_scale.shape[1]
+    if k_blocks.numel() * k_blocks.element_size() < index_keys_b16_size(B, Nc):
+        raise ValueError("k_blocks smaller than index_keys_b16_size")
+    _check("csa_index_score_segments_b16", _lib.csa_index_score_segments_b16(
+        _p(q), _p(q_scale), _p(w), _p(k_blocks), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores),
+        _p(cand), cand.numel() * cand.element_size(), _stream(stream)))
+    return cand
 
 
 def csa_index_score_segments(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, k: int, cand, scores=None,

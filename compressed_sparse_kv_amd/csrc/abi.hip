@@ -21,7 +21,9 @@ int index_topk_segments(int);
 int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
                       int, int, int, float*, int32_t*, void*, hipStream_t);
 int launch_index_segments(const void*, const float*, const float*, const void*, const float*, const int64_t*, int,
-                          int, int, int, int, float*, uint2*, hipStream_t);
+                          int, int, int, int, float*, uint2*, hipStream_t, bool);
+size_t index_keys_b16_bytes(int, int);
+int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
 int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
 size_t topk_merge_pairs_per_row(int, int);
 int launch_topk_attention(const void*, const void*, const uint2*, int, size_t, const int64_t*, const void*,
@@ -147,18 +149,44 @@ size_t csa_index_segments_size(int B, int S, int Nc, int k) {
   return static_cast<size_t>(B) * S * topk_merge_pairs_per_row(index_topk_segments(Nc), k) * sizeof(uint2);
 }
 
-int csa_index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
-                             const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
-                             int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream) {
+static int index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
+                                const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
+                                int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream, bool b16) {
   CSA_REQUIRE(q && q_scale && w && k_codes && k_scale && q_pos && cand);
   CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0 && k >= 1 && k <= 2048);
   const int64_t rows = static_cast<int64_t>(B) * S;
   CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
-  CSA_REQUIRE(aligned16(cand));
+  CSA_REQUIRE(aligned16(cand) && (!b16 || aligned16(k_codes)));
   if (H_I != 64 || d_I != 128 || !index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
   if (cand_bytes < csa_index_segments_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
   return launch_index_segments(q, q_scale, w, k_codes, k_scale, q_pos, B, S, Nc, m, k, scores,
-                               static_cast<uint2*>(cand), as_stream(stream));
+                               static_cast<uint2*>(cand), as_stream(stream), b16);
+}
+
+int csa_index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
+                             const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
+                             int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream) {
+  return index_score_segments(q, q_scale, w, k_codes, k_scale, q_pos, B, S, H_I, d_I, Nc, m, k, scores, cand,
+                              cand_bytes, stream, false);
+}
+
+int csa_index_score_segments_b16(const void* q, const float* q_scale, const float* w, const void* k_blocks,
+                                 const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
+                                 int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream) {
+  return index_score_segments(q, q_scale, w, k_blocks, k_scale, q_pos, B, S, H_I, d_I, Nc, m, k, scores, cand,
+                              cand_bytes, stream, true);
+}
+
+size_t csa_index_keys_b16_size(int B, int Nc) {
+  if (B <= 0 || Nc <= 0) return 0;
+  return index_keys_b16_bytes(B, Nc);
+}
+
+int csa_index_keys_b16(const void* k_codes, void* k_blocks, int B, int Nc, void* stream) {
+  CSA_REQUIRE(k_codes && k_blocks && B > 0 && Nc > 0);
+  CSA_REQUIRE(static_cast<int64_t>(B) * Nc < (int64_t{1} << 34));
+  CSA_REQUIRE(aligned16(k_codes) && aligned16(k_blocks));
+  return launch_index_keys_b16(k_codes, k_blocks, B, Nc, as_stream(stream));
 }
 
 int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream) {

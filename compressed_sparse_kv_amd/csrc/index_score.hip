@@ -128,7 +128,10 @@ constexpr int kDecGroups = 8;                         // 64-entry groups per wav
 template <bool kTopk> constexpr int dec_waves() { return kTopk ? 8 : 4; }
 template <bool kTopk> constexpr int dec_entries() { return dec_waves<kTopk>() * 64 * kDecGroups; }
 
-template <bool kTopk>
+// kB16: the keys are stored in blocks of 16 entries (index_keys_b16 below), so that each
+// quarter-wave's load is 512 contiguous bytes already in the MFMA layout; one group is
+// then kept in flight instead of two.
+template <bool kTopk, bool kB16 = false>
 __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decode(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
   const int64_t t = q_pos[row];
   const int nvis = static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m));
 
-  const uint8_t* kb = k8 + static_cast<size_t>(b) * Nc * kID;
+  const uint8_t* kb = k8 + static_cast<size_t>(b) * (kB16 ? cdiv(Nc, 16) * 16 : Nc) * kID;
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
   float* out = scores ? scores + row * Nc : nullptr;
 
@@ -151,15 +154,21 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
   // the next two groups are in flight while a group is multiplied
   const int base = blockIdx.x * kDecEntWG;
   auto group_e0 = [&](int gi) { return base + 64 * (gi * kDecWaves + wave); };
-  v8i ring[3][4];
-  float sring[3];            // row scale of entry e0 + l, fetched with the group's keys
+  constexpr int kRingD = kB16 ? 2 : 3;       // groups held: the one multiplied + those in flight
+  v8i ring[kRingD][4];
+  float sring[kRingD];       // row scale of entry e0 + l, fetched with the group's keys
+  // lane l's 32 bytes of entry e: bytes 32*(l/16) .. +31 of its row
+  auto key_off = [&](int e) -> size_t {
+    return kB16 ? static_cast<size_t>(e >> 4) * (16 * kID) + (l >> 4) * (16 * 32) + (e & 15) * 32
+                : static_cast<size_t>(e) * kID + 32 * (l >> 4);
+  };
 #define CSA_DEC_LOAD(gi_)                                                                           \
   do {                                                                                              \
     _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                              \
       const int e_ = min(group_e0(gi_) + 16 * nb + (l & 15), Nc - 1);                               \
-      ring[(gi_) % 3][nb] = *reinterpret_cast<const v8i*>(kb + static_cast<size_t>(e_) * kID + 32 * (l >> 4)); \
+      ring[(gi_) % kRingD][nb] = *reinterpret_cast<const v8i*>(kb + key_off(e_));                   \
     }                                                                                               \
-    sring[(gi_) % 3] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                         \
+    sring[(gi_) % kRingD] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                    \
   } while (0)
   // The query (64 x 128 codes, 8 KiB), its head weights and scales are read once per
   // workgroup, ahead of the keys, and shared through LDS: loads complete in order, so a
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     if (threadIdx.x < 2 * kIH) wq = threadIdx.x < kIH ? w[row * kIH + threadIdx.x] : qs[row * kIH + threadIdx.x - kIH];
   }
   CSA_DEC_LOAD(0);
-  CSA_DEC_LOAD(1);
+  if constexpr (kRingD == 3) CSA_DEC_LOAD(1);
   __builtin_amdgcn_sched_barrier(0);      // every load above the query's staging
 #pragma unroll
   for (int i = 0; i < kQv; ++i) qlds[threadIdx.x + i * kDecThreads] = qv[i];
@@ -206,16 +215,16 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
 #pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
     const int e0 = group_e0(gi);
-    if (gi + 2 < kDecGroups) CSA_DEC_LOAD(gi + 2);
+    if (gi + kRingD - 1 < kDecGroups) CSA_DEC_LOAD(gi + kRingD - 1);
     const int e = e0 + l;
     float p[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       v8s bk[4];
-      e4m3x32_to_bf16(ring[gi % 3][nb], bk);
+      e4m3x32_to_bf16(ring[gi % kRingD][nb], bk);
       p[nb] = head_sum1(a, bk, wv);
     }
-    const float v = reduce_scatter4(p) * sring[gi % 3];
+    const float v = reduce_scatter4(p) * sring[gi % kRingD];
     const bool vis = e < nvis;
     if (out && e < Nc) out[e] = vis ? v : -INFINITY;
     const uint32_t key = vis ? score_key(v) : 0u;
@@ -415,14 +424,46 @@ bool index_topk_fused_ok(int S, int Nc, int k) {
   return S <= 4 && k <= dec_entries<true>() && topk_merge_supported(index_topk_segments(Nc), k);
 }
 
-// Scores (optional) and every segment's top-k as (key, entry) pairs in cand[rows][G][k].
+// Scores (optional) and every segment's top-k as (key, entry) pairs in cand[rows][G][k];
+// b16: the keys in 16-entry blocks.
 int launch_index_segments(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
                           const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, uint2* cand,
-                          hipStream_t st) {
+                          hipStream_t st, bool b16) {
   dim3 grid(index_topk_segments(Nc), B * S);
-  hipLaunchKernelGGL(index_score_fp8_decode<true>, grid, dim3(dec_waves<true>() * 64), 0, st,
-                     static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S, Nc,
-                     m, scores, ktop, cand, topk_merge_pairs_per_row(index_topk_segments(Nc), ktop));
+  const size_t stride = topk_merge_pairs_per_row(index_topk_segments(Nc), ktop);
+  if (b16)
+    hipLaunchKernelGGL((index_score_fp8_decode<true, true>), grid, dim3(dec_waves<true>() * 64), 0, st,
+                       static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S,
+                       Nc, m, scores, ktop, cand, stride);
+  else
+    hipLaunchKernelGGL((index_score_fp8_decode<true, false>), grid, dim3(dec_waves<true>() * 64), 0, st,
+                       static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S,
+                       Nc, m, scores, ktop, cand, stride);
+  CSA_LAUNCH_CHECK();
+  return CSA_OK;
+}
+
+// Keys in 16-entry blocks: block j of a sequence holds entries 16j .. 16j+15 as four
+// 512-byte pieces; piece p holds bytes 32p .. 32p+31 of each of the 16 entries (32 bytes
+// per entry, entry order).  Entries past Nc in the last block are zero.  One workgroup of
+// 64 threads per block: thread t copies piece t/16 of entry t%16.
+__global__ __launch_bounds__(64) void index_keys_b16(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                     int Nc) {
+  const int nblk = static_cast<int>(gridDim.x), blk = static_cast<int>(blockIdx.x), b = static_cast<int>(blockIdx.y);
+  const int t = static_cast<int>(threadIdx.x), e = 16 * blk + (t & 15), pc = t >> 4;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (static_cast<size_t>(b) * Nc + min(e, Nc - 1)) * kID + 32 * pc);
+  uint4 lo = s[0], hi = s[1];
+  if (e >= Nc) lo = hi = make_uint4(0u, 0u, 0u, 0u);
+  uint4* d = reinterpret_cast<uint4*>(dst + (static_cast<size_t>(b) * nblk + blk) * (16 * kID) + pc * 512 + (t & 15) * 32);
+  d[0] = lo;
+  d[1] = hi;
+}
+
+size_t index_keys_b16_bytes(int B, int Nc) { return static_cast<size_t>(B) * cdiv(Nc, 16) * 16 * kID; }
+
+int launch_index_keys_b16(const void* src, void* dst, int B, int Nc, hipStream_t st) {
+  hipLaunchKernelGGL(index_keys_b16, dim3(cdiv(Nc, 16), B), dim3(64), 0, st, static_cast<const uint8_t*>(src),
+                     static_cast<uint8_t*>(dst), Nc);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }
@@ -431,7 +472,7 @@ int launch_index_topk(const void* q, const float* q_scale, const float* w, const
                       const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, int32_t* idx,
                       void* ws, hipStream_t st) {
   uint2* cand = static_cast<uint2*>(ws);
-  const int rc = launch_index_segments(q, q_scale, w, k, k_scale, q_pos, B, S, Nc, m, ktop, scores, cand, st);
+  const int rc = launch_index_segments(q, q_scale, w, k, k_scale, q_pos, B, S, Nc, m, ktop, scores, cand, st, false);
   if (rc != CSA_OK) return rc;
   return launch_topk_merge(cand, B * S, index_topk_segments(Nc), ktop, idx, st);
 }

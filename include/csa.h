@@ -172,6 +172,31 @@ int csa_index_score_segments(const void* q, const float* q_scale, const float* w
 int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * The indexer keys in 16-entry blocks (decode scoring).  Same codes, another order:
+ * block j of sequence b holds entries 16j .. 16j+15 as four 512-byte pieces, piece p
+ * holding bytes 32p .. 32p+31 of each of the 16 entries in entry order (32 bytes per
+ * entry), so that the 16 lanes of a quarter-wave that feed one matrix step read 512
+ * contiguous bytes.  Entries past Nc in the last block are zero.
+ *
+ * csa_index_keys_b16_size: bytes of the blocked copy, B * ceil(Nc/16) * 2048 (0 on bad
+ *   arguments).
+ * csa_index_keys_b16: k_blocks = the blocked copy of k_codes [B,Nc,128] (e4m3 codes); both
+ *   caller device memory, 16-byte aligned, not overlapping.  The copy is made once per key
+ *   cache update, not per step.
+ * csa_index_score_segments_b16: csa_index_score_segments with the keys in blocks
+ *   (k_blocks as written by csa_index_keys_b16 for the same B and Nc; k_scale unchanged);
+ *   the scores and candidate pairs are identical to csa_index_score_segments'.
+ * ------------------------------------------------------------------------------ */
+size_t csa_index_keys_b16_size(int B, int Nc);
+
+int csa_index_keys_b16(const void* k_codes, void* k_blocks, int B, int Nc, void* stream);
+
+int csa_index_score_segments_b16(const void* q, const float* q_scale, const float* w,
+                                 const void* k_blocks, const float* k_scale, const int64_t* q_pos,
+                                 int B, int S, int H_I, int d_I, int Nc, int m, int k,
+                                 float* scores, void* cand, size_t cand_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 3: top-k selection.  [KV-COMP] sections 9.4 (S_t = TopK_k of the scores)
  * and 9.8 (invisible entries carry -inf and come out as -1).
  *

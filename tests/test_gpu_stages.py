@@ -514,3 +514,46 @@ def test_topk_sparse_attn_fused_crafted(lib, B, S, G, k, kind):
     assert torch.equal(idx, idx_ref), f"fused selection on {kind} candidates"
     assert torch.equal(out, out_ref), f"fused attention on {kind} candidates"
     assert torch.equal(lse, lse_ref), f"fused lse on {kind} candidates"
+
+
+# ---------------------------------------------------------------------------------------
+# The indexer keys in 16-entry blocks: the copy against its definition, and the scores and
+# segment candidates identical to the row-major path's
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,S,Nc,k,t", [
+    (3, 1, 32768, 512, 4 * 32768 - 1),     # decode: 8 segments
+    (2, 1, 5000, 256, 4 * 5000 + 7),       # ragged last segment, Nc not a multiple of 16
+    (2, 2, 9001, 301, 4 * 2500 + 2),       # causal limit inside the row; odd Nc and k
+    (1, 1, 150000, 1024, 4 * 100000 + 1),  # 37 segments, empty tail
+])
+def test_index_segments_b16(lib, B, S, Nc, k, t):
+    a = I.indexer_inputs(7100 + B + Nc + k, B, S, Nc)
+    pos = dev((t - S + 1 + np.arange(S, dtype=np.int64))[None].repeat(B, 0))
+    k8 = dev(a["kI_fp8"])
+    blocks = torch.full((lib.index_keys_b16_size(B, Nc),), 0x5A, dtype=torch.uint8, device="cuda")
+    lib.csa_index_keys_b16(k8, blocks)
+    torch.cuda.synchronize()
+    # the blocked copy against its definition (numpy re-ordering of the same codes)
+    nblk = -(-Nc // 16)
+    rows = np.zeros((B, nblk * 16, 128), np.uint8)
+    rows[:, :Nc] = a["kI_fp8"].reshape(B, Nc, 128)
+    want = rows.reshape(B, nblk, 16, 4, 32).transpose(0, 1, 3, 2, 4).reshape(-1)
+    assert np.array_equal(blocks.cpu().numpy(), want), "csa_index_keys_b16 layout"
+    args = (dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]))
+    n = lib.index_segments_size(B, S, Nc, k)
+    cand = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    cand16 = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(B, S, Nc, device="cuda")
+    sc16 = torch.full_like(sc, 7.0)
+    lib.csa_index_score_segments(*args, k8, dev(a["kI_scale"]), pos, m=4, k=k, cand=cand, scores=sc)
+    lib.csa_index_score_segments_b16(*args, blocks, dev(a["kI_scale"]), pos, m=4, k=k, cand=cand16, scores=sc16)
+    torch.cuda.synchronize()
+    G = -(-Nc // 4096)
+    seg = B * S * G * k * 8                 # the segment pairs (the rest of each share is merge space)
+    per_row = n // (B * S)
+    c0 = cand.view(B * S, per_row)[:, :G * k * 8]
+    c1 = cand16.view(B * S, per_row)[:, :G * k * 8]
+    assert seg == c0.numel()
+    assert torch.equal(c0, c1), "blocked keys: segment candidates differ"
+    assert torch.equal(sc, sc16), "blocked keys: scores differ"
