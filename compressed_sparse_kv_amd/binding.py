@@ -59,13 +59,13 @@ def _load() -> ctypes.CDLL:
         "csa_index_keys_b16_size": ([i, i], sz),
         "csa_index_keys_b16": ([vp, vp, i, i, vp], i),
         "csa_index_score_segments_b16": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
-        "csa_topk_merge": ([vp, i, i, i, i, vp, vp], i),
+        "csa_topk_merge": ([vp, sz, i, i, i, i, vp, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
         "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
-        "csa_topk_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp], i),
+        "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp], i),
         "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
     }
     for name, (args, res) in sig.items():
@@ -233,7 +233,8 @@ def csa_index_score_segments(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, 
 def csa_topk_merge(cand, B, S, Nc, k, idx, stream=None):
     """idx [B,S,k] int32 = the k best of each row's segment candidates, as csa_topk returns them."""
     _dev(cand, idx)
-    _check("csa_topk_merge", _lib.csa_topk_merge(_p(cand), B, S, Nc, k, _p(idx), _stream(stream)))
+    _check("csa_topk_merge", _lib.csa_topk_merge(_p(cand), cand.numel() * cand.element_size(), B, S, Nc, k, _p(idx),
+                                                 _stream(stream)))
     return idx
 
 
@@ -290,8 +291,8 @@ def csa_topk_sparse_attn(q, kv_comp, cand, swa, sink, *, k: int, W: int, out, q_
     dt = _dtype(q)
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_topk_sparse_attn", _lib.csa_topk_sparse_attn(
-        _p(q), _p(kv_comp), _p(cand), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
-        _p(out), _p(lse), _p(idx), _p(ws), wsb, _stream(stream)))
+        _p(q), _p(kv_comp), _p(cand), cand.numel() * cand.element_size(), _p(q_pos), _p(swa), _p(sink), dt,
+        float(scale), B, S, H, c, Nc, k, Ls, W, _p(out), _p(lse), _p(idx), _p(ws), wsb, _stream(stream)))
     return out
 
 

@@ -24,14 +24,14 @@ int launch_index_segments(const void*, const float*, const float*, const void*, 
                           int, int, int, int, float*, uint2*, hipStream_t, bool);
 size_t index_keys_b16_bytes(int, int);
 int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
-int launch_topk_merge(const uint2*, int, int, int, int32_t*, hipStream_t);
+int launch_topk_merge(uint2*, int, int, int, int32_t*, hipStream_t);
 size_t topk_merge_pairs_per_row(int, int);
 int launch_topk_attention(const void*, const void*, const uint2*, int, size_t, const int64_t*, const void*,
                           const float*, float, int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t,
                           hipStream_t);
 int topk_attention_max_cand();
 int topk_merge_group(int, int);
-int launch_topk_merge_first(const uint2*, int, int, int, size_t&, hipStream_t);
+int launch_topk_merge_first(uint2*, int, int, int, size_t&, hipStream_t);
 }  // namespace csa
 
 using namespace csa;
@@ -57,7 +57,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_version(void) { return 100; }
+int csa_version(void) { return 200; }
 
 // ---- stage 1 ------------------------------------------------------------------------
 size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev) {
@@ -189,14 +189,14 @@ int csa_index_keys_b16(const void* k_codes, void* k_blocks, int B, int Nc, void*
   return launch_index_keys_b16(k_codes, k_blocks, B, Nc, as_stream(stream));
 }
 
-int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream) {
+int csa_topk_merge(void* cand, size_t cand_bytes, int B, int S, int Nc, int k, int32_t* idx, void* stream) {
   CSA_REQUIRE(cand && idx);
   CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && k >= 1 && k <= 2048);
   CSA_REQUIRE(static_cast<int64_t>(B) * S < (int64_t{1} << 31));
   CSA_REQUIRE(aligned16(cand));
   if (!index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
-  return launch_topk_merge(static_cast<const uint2*>(cand), B * S, index_topk_segments(Nc), k, idx,
-                           as_stream(stream));
+  if (cand_bytes < csa_index_segments_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
+  return launch_topk_merge(static_cast<uint2*>(cand), B * S, index_topk_segments(Nc), k, idx, as_stream(stream));
 }
 
 // ---- stage 3 ------------------------------------------------------------------------
@@ -257,7 +257,7 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, cons
                           lse, ws, ws_bytes, as_stream(stream));
 }
 
-int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand, const int64_t* q_pos,
+int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes, const int64_t* q_pos,
                          const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
                          int Nc, int k, int Ls, int W, void* out, float* lse, int32_t* idx, void* ws,
                          size_t ws_bytes, void* stream) {
@@ -273,10 +273,11 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand, c
   if (M < 0) return CSA_ERR_UNSUPPORTED;
   const long long n_sel = M == 0 ? static_cast<long long>(G) * k : static_cast<long long>((G + M - 1) / M) * k;
   if (n_sel > topk_attention_max_cand()) return CSA_ERR_UNSUPPORTED;
+  if (cand_bytes < csa_index_segments_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
   // every check before the first level is enqueued
   if (ws_bytes < attn_workspace_bytes(B, S, H, c, std::min(W, Ls) + k, dtype)) return CSA_ERR_WORKSPACE;
   const int rows = B * S;
-  const uint2* pairs = static_cast<const uint2*>(cand);
+  uint2* pairs = static_cast<uint2*>(cand);
   size_t offset = 0;
   const int n_cand = launch_topk_merge_first(pairs, rows, G, k, offset, as_stream(stream));
   if (n_cand < 0) return CSA_ERR_HIP;

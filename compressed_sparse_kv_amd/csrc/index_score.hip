@@ -414,7 +414,7 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
 
 // Scores and per-segment top-k in one pass (decode shapes, FP8, H_I = 64, d_I = 128), then
 // the per-row merge: idx = the k largest of each row, as csa_topk would return.
-int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st);
+int launch_topk_merge(uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st);
 int topk_merge_supported(int G, int k);
 size_t topk_merge_pairs_per_row(int G, int k);
 

@@ -304,7 +304,7 @@ static void launch_merge_level(const uint2* cand, size_t row_stride, int rows, i
 }
 
 // cand: rows x topk_merge_pairs_per_row(G, k) pairs (the first G*k of a row are the input).
-int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st) {
+int launch_topk_merge(uint2* cand, int rows, int G, int k, int32_t* idx, hipStream_t st) {
   const int M = topk_merge_group(G, k);
   if (M < 0) return CSA_ERR_UNSUPPORTED;
   const size_t per_row = topk_merge_pairs_per_row(G, k);
@@ -316,7 +316,7 @@ int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, h
   // rows are per_row pairs apart: the first level reads row r's G*k pairs at
   // cand + r * per_row and writes its G1 * k pairs right after them
   const int G1 = cdiv(G, M);
-  uint2* lvl = const_cast<uint2*>(cand) + static_cast<size_t>(G) * k;
+  uint2* lvl = cand + static_cast<size_t>(G) * k;
   launch_merge_level<true>(cand, per_row, rows, G1, G * k, M * k, k, nullptr, lvl, st);
   CSA_LAUNCH_CHECK();
   launch_merge_level<false>(lvl, per_row, rows, 1, G1 * k, G1 * k, k, idx, nullptr, st);
@@ -328,14 +328,14 @@ int launch_topk_merge(const uint2* cand, int rows, int G, int k, int32_t* idx, h
 // selection itself): writes the cdiv(G, M) * k level-one pairs of each row after its G * k
 // segment pairs.  Returns the number of candidate pairs per row the caller selects from
 // (G * k when one level is enough, nothing launched) and where they start, or < 0.
-int launch_topk_merge_first(const uint2* cand, int rows, int G, int k, size_t& offset, hipStream_t st) {
+int launch_topk_merge_first(uint2* cand, int rows, int G, int k, size_t& offset, hipStream_t st) {
   const int M = topk_merge_group(G, k);
   if (M < 0) return -1;
   offset = 0;
   if (M == 0) return G * k;
   const size_t per_row = topk_merge_pairs_per_row(G, k);
   const int G1 = cdiv(G, M);
-  uint2* lvl = const_cast<uint2*>(cand) + static_cast<size_t>(G) * k;
+  uint2* lvl = cand + static_cast<size_t>(G) * k;
   launch_merge_level<true>(cand, per_row, rows, G1, G * k, M * k, k, nullptr, lvl, st);
   if (hipGetLastError() != hipSuccess) return -1;
   offset = static_cast<size_t>(G) * k;

@@ -158,9 +158,11 @@ int csa_index_topk(const void* q, const float* q_scale, const float* w,
  *   element g*k + j of row r's share (with one merge level the shares are exactly G*k
  *   pairs: cand[r][g][j]).
  * csa_topk_merge: idx [B,S,k] = the k best candidates of each row (key descending, then
- *   lower entry), ascending, padded with -1: exactly csa_topk of the same scores.  With two
- *   levels it writes the first level's pairs into the rest of each row's share of cand
- *   (the segment pairs stay intact).
+ *   lower entry), ascending, padded with -1: exactly csa_topk of the same scores.  cand is
+ *   read and, with two levels, also written: the first level's pairs go into the rest of
+ *   each row's share (the segment pairs stay intact), so cand is not const and must not be
+ *   shared with a concurrent call.  cand_bytes < csa_index_segments_size(B, S, Nc, k):
+ *   CSA_ERR_WORKSPACE.
  * ------------------------------------------------------------------------------ */
 size_t csa_index_segments_size(int B, int S, int Nc, int k);
 
@@ -169,7 +171,7 @@ int csa_index_score_segments(const void* q, const float* q_scale, const float* w
                              int B, int S, int H_I, int d_I, int Nc, int m, int k,
                              float* scores, void* cand, size_t cand_bytes, void* stream);
 
-int csa_topk_merge(const void* cand, int B, int S, int Nc, int k, int32_t* idx, void* stream);
+int csa_topk_merge(void* cand, size_t cand_bytes, int B, int S, int Nc, int k, int32_t* idx, void* stream);
 
 /* ------------------------------------------------------------------------------
  * The indexer keys in 16-entry blocks (decode scoring).  Same codes, another order:
@@ -261,17 +263,18 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
  * segments' top-k sets) and sections 9.5-9.6 (attention over window || selection).
  * Results identical to csa_topk_merge followed by csa_sparse_attn.
  *
- *   cand: the pairs of csa_index_score_segments for the same B, S, Nc and k.  When
+ *   cand: the pairs of csa_index_score_segments for the same B, S, Nc and k, cand_bytes
+ *   its size (>= csa_index_segments_size(B, S, Nc, k), else CSA_ERR_WORKSPACE).  When
  *   csa_topk_merge would take two levels, the first level runs here too and writes its
- *   pairs into the rest of each row's share of cand, as csa_topk_merge does; the
- *   attention workgroups then select from those.
+ *   pairs into the rest of each row's share of cand, as csa_topk_merge does (cand is not
+ *   const); the attention workgroups then select from those.
  *   Supported: dtype CSA_BF16 (H = 64, c = 512), the shapes csa_index_score_segments
  *   accepts, and at most 8192 pairs per row to select from (the segment pairs, G*k, or
  *   with two levels the first level's); otherwise CSA_ERR_UNSUPPORTED.
  *   idx [B,S,k] int32: receives the selection (as csa_topk_merge writes it), or NULL.
  *   Other arguments and the workspace (max_rows = min(W, Ls) + k) as csa_sparse_attn.
  * ------------------------------------------------------------------------------ */
-int csa_topk_sparse_attn(const void* q, const void* kv_comp, const void* cand,
+int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes,
                          const int64_t* q_pos, const void* swa, const float* sink, int dtype,
                          float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                          void* out, float* lse, int32_t* idx, void* ws, size_t ws_bytes,

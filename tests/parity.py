@@ -1,8 +1,9 @@
 """Comparison rules between the HIP path and the oracle (test infrastructure).
 
 * fp32 outputs: max |gpu - oracle| <= 1e-5;  bf16 attention outputs: <= 2e-3, except
-  where the exact value has magnitude >= 0.5: there a bf16 number cannot be trusted to
-  lie within 2e-3 of it (the rounding step is 2^-8 .. ) and one bf16 step is allowed.
+  where no bf16 number lies within 2e-3 of the exact value (|o| >= 1, where half a
+  rounding step is >= 3.9e-3): there half a bf16 step (x (1 + 2^-10)) plus 1e-5 for the
+  kernel's fp32 value before its rounding.
 * bf16 compressed KV: within one bf16 spacing of the oracle's value (its rounding
   step, taken at the oracle's magnitude).
 * FP8 codes: the row scale within 1e-5 relative; every code decodes to within half an
@@ -46,10 +47,21 @@ def bf16_f64(bits: np.ndarray) -> np.ndarray:
 
 # ---- rules -----------------------------------------------------------------------------
 
-def assert_bf16_output(gpu, ref, what=""):
-    """bf16 outputs: |gpu - oracle| <= max(2e-3, one bf16 step at the oracle's value)."""
+def bf16_output_tolerance(ref):
+    """max(2e-3, half a bf16 step at the oracle's value x (1 + 2^-10) + 1e-5).
+
+    A correctly rounded bf16 output lies within half a step of the exact value; the
+    kernel rounds its own fp32 value, whose error before rounding (P carried as a bf16
+    hi + lo pair, about 2^-18 of the weighted row sum, fp32 accumulation) stays below
+    1e-5 at these magnitudes.  Below |o| = 1 the bound is the flat 2e-3."""
     ref = np.asarray(ref, np.float64)
-    tol = np.maximum(TOL_BF16_ATTN, np.where(np.abs(ref) >= 0.5, bf16_spacing(ref), 0.0))
+    return np.maximum(TOL_BF16_ATTN, 0.5 * bf16_spacing(ref) * (1.0 + 2.0 ** -10) + TOL_F32)
+
+
+def assert_bf16_output(gpu, ref, what=""):
+    """bf16 outputs: |gpu - oracle| <= bf16_output_tolerance(oracle)."""
+    ref = np.asarray(ref, np.float64)
+    tol = bf16_output_tolerance(ref)
     err = np.abs(np.asarray(gpu, np.float64) - ref)
     if np.any(err > tol):
         i = np.unravel_index(np.argmax(err / tol), err.shape)

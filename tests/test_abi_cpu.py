@@ -35,7 +35,7 @@ def test_binding_covers_every_declared_symbol():
 def test_status_strings_and_version():
     from compressed_sparse_kv_amd import binding
     lib = binding.lib()
-    assert lib.csa_version() >= 100
+    assert lib.csa_version() >= 200
     for st in range(5):
         assert lib.csa_status_string(st)
     assert b"unknown" in lib.csa_status_string(99)
@@ -77,7 +77,8 @@ def test_invalid_arguments_are_rejected_before_launch():
                                         fake, 1 << 30, None) == 2
     assert lib.csa_index_score_segments(fake, fake, fake, fake, fake, fake, 32, 1, 64, 128, 32768, 4, 512, None,
                                         fake, 1024, None) == 3
-    assert lib.csa_topk_merge(fake, 32, 1, 32768, 512, None, None) == 1
+    assert lib.csa_topk_merge(fake, 1 << 30, 32, 1, 32768, 512, None, None) == 1
+    assert lib.csa_topk_merge(fake, 1024, 32, 1, 32768, 512, fake, None) == 3     # cand smaller than its size query
     assert lib.csa_index_segments_size(32, 1, 32768, 512) == 32 * 8 * 512 * 8
     assert lib.csa_index_segments_size(1, 8, 3000, 128) == 0
     # Pro shape: 64 segment lists of 1024 merge in two levels (groups of 8): room for both
@@ -92,14 +93,15 @@ def test_invalid_arguments_are_rejected_before_launch():
     # fused selection + attention: null candidates, fp32 dtype, too many candidates per
     # query after the first merge level (21 segments x 2048 -> 5 x 2048), workspace too
     # small for the split partials (also with two merge levels: V4-Pro, 64 segments x 1024)
-    fused = lambda cand, dt, Nc, k, ws_bytes: lib.csa_topk_sparse_attn(
-        fake, fake, cand, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, fake, None, None, fake,
-        ws_bytes, None)
+    fused = lambda cand, dt, Nc, k, ws_bytes, cand_bytes=1 << 40: lib.csa_topk_sparse_attn(
+        fake, fake, cand, cand_bytes, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, fake, None, None,
+        fake, ws_bytes, None)
     assert fused(None, 1, 32768, 512, 1 << 40) == 1
     assert fused(fake, 0, 32768, 512, 1 << 40) == 2
     assert fused(fake, 1, 86000, 2048, 1 << 40) == 2
     assert fused(fake, 1, 32768, 512, 16) == 3
     assert fused(fake, 1, 262144, 1024, 16) == 3
+    assert fused(fake, 1, 32768, 512, 1 << 40, cand_bytes=1024) == 3     # cand smaller than its size query
 
 
 def test_workspace_queries():

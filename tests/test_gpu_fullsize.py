@@ -70,11 +70,36 @@ def _decode_step_fused(lib, sh, a):
     return idx.cpu().numpy(), out, lse.cpu().numpy()
 
 
+def _decode_step_bench(lib, sh, a):
+    """The bench's timed calls on the Flash batch: scoring over the keys in 16-entry blocks
+    with each segment's top-k (the scores written too, for the check), then the selection
+    and the sparse attention in one call."""
+    B, Nc, k = sh.B, sh.n_c, sh.k
+    k16 = lib.csa_index_keys_b16(dev(a["kI_fp8"]), torch.empty(lib.index_keys_b16_size(B, Nc), dtype=torch.uint8,
+                                                                 device="cuda"))
+    cand = torch.empty(lib.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device="cuda")
+    scores = torch.full((B, 1, Nc), 7.0, device="cuda")
+    lib.csa_index_score_segments_b16(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), k16, dev(a["kI_scale"]),
+                                     dev(a["q_pos"]), m=sh.m, k=k, cand=cand, scores=scores)
+    idx = torch.full((B, 1, k), -7, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, 1, sh.H, device="cuda")
+    lib.csa_topk_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), cand, dev_bf16(a["swa_bf16"]),
+                             dev(a["sink"]), k=k, W=sh.W, out=out, lse=lse, idx=idx)
+    torch.cuda.synchronize()
+    return scores.cpu().numpy(), idx.cpu().numpy(), out, lse.cpu().numpy()
+
+
 def test_flash_decode_full(lib):
     sh = I.FLASH_DECODE
     a = I.decode_inputs(sh).arrays
     scores, idx, out, lse = _decode_chain(lib, sh, a)
     _check_decode(sh, a, scores, idx, out, lse, sample=[0, 13, 31])
+    # the bench's exact calls on the full batch, against the oracle on sampled sequences
+    # (scores, selection bit-exact on every row over the GPU's scores, attention, lse)
+    sc_b, idx_b, out_b, lse_b = _decode_step_bench(lib, sh, a)
+    _check_decode(sh, a, sc_b, idx_b, out_b, lse_b, sample=[1, 8, 19, 26, 30])
+    assert np.array_equal(idx_b, idx), "the bench's step selects other entries than the stage chain"
     # the bench's two-call step on the same inputs: the same selection on every row, and
     # the same attention output bit for bit (same kernels on the same rows in the same order)
     idx2, out2, lse2 = _decode_step_fused(lib, sh, a)
@@ -154,40 +179,50 @@ def test_prefill_chunk_full(lib):
                         lse=lse)
     torch.cuda.synchronize()
 
-    # compressor: sampled entries of the chunk (entry i pools block i and block i-1)
+    # compressor: sampled entries of the chunk (entry i pools block i and block i-1): the
+    # first and last entries and a seeded sample in between
     hid_all = np.concatenate([a["hidden_prev_bf16"], a["hidden_bf16"]], axis=1)      # rows of blocks -1 .. S/m-1
     kv_new = host_bits(kv[:, n_ctx:])
     kI_codes, kI_sc = kI_new.cpu().numpy(), kIs_new.cpu().numpy()
-    for e in (0, 1, 777, n_new - 1):
+    rng = np.random.default_rng(sh.seed + 500)
+    ents = sorted({0, 1, 2, n_new - 2, n_new - 1, *rng.choice(np.arange(3, n_new - 2), 27, replace=False).tolist()})
+    W_main, W_idx = bf16_f64(a["W_main_bf16"]), bf16_f64(a["W_idx_bf16"])
+    for e in ents:
         blk = bf16_f64(hid_all[:, sh.m * (e + 1): sh.m * (e + 2)])
         blk_prev = bf16_f64(hid_all[:, sh.m * e: sh.m * (e + 1)])
         pos = sh.ctx + sh.m * e
         kw_e = dict(kw, p0=pos)
-        ref = O.csa_compress(blk, bf16_f64(a["W_main_bf16"]), a["B_main"], c=sh.c, hidden_prev=blk_prev, **kw_e)
+        ref = O.csa_compress(blk, W_main, a["B_main"], c=sh.c, hidden_prev=blk_prev, **kw_e)
         assert_bf16_within_one_step(kv_new[:, e:e + 1], ref, f"compressed KV, entry {n_ctx + e}")
-        ref_i = O.csa_compress(blk, bf16_f64(a["W_idx_bf16"]), a["B_idx"], c=sh.d_I, hidden_prev=blk_prev, **kw_e)
+        ref_i = O.csa_compress(blk, W_idx, a["B_idx"], c=sh.d_I, hidden_prev=blk_prev, **kw_e)
         assert_fp8_rows(kI_codes[:, e:e + 1], kI_sc[:, e:e + 1], ref_i, f"indexer K, entry {n_ctx + e}")
 
-    # scores / top-k / attention for sampled queries (on the GPU's K, which is checked above)
+    # scores / top-k / attention for 256 sampled queries (on the GPU's K, which is checked
+    # above): the first 64 and last 64 of the chunk (the first and last workgroups of the
+    # indexer, the causal tile limits at both ends) and 128 seeded ones in between
     sc = scores.cpu().numpy()
     idx_h = idx.cpu().numpy()
     out_bits, lse_h = host_bits(out), lse.cpu().numpy()
     KI = O.dequant_rows(kI.cpu().numpy(), kIs.cpu().numpy())
     kv_h = host_bits(kv)
-    for s in (0, 1, 4095, sh.S - 1):
-        ss = slice(s, s + 1)
-        qI = O.dequant_rows(a["qI_fp8"][:, ss], a["qI_scale"][:, ss])
-        sc_o = O.index_scores(qI, a["w"][:, ss], KI, a["q_pos"][:, ss], sh.m)
-        assert_close(sc[:, ss], sc_o, TOL_F32, f"prefill scores, query {s}")
-        assert_topk_equal(idx_h[:, ss], O.topk_indices(sc[:, ss], sh.k), sc[:, ss], sh.k,
-                          f"prefill top-k of GPU scores, query {s}", exact=True)
-        assert_topk_equal(idx_h[:, ss], O.topk_indices(sc_o, sh.k), sc_o, sh.k, f"prefill top-k, query {s}")
-        sel = idx_h[0, s]
-        rows = sorted({int(j) for j in sel if j >= 0})
-        kv_sel = np.zeros((1, Nc, sh.c))
-        kv_sel[0, rows] = bf16_f64(kv_h[0, rows])
-        o_o, lse_o = O.sparse_attention(bf16_f64(a["q_bf16"][:, ss]), kv_sel, idx_h[:, ss],
-                                        bf16_f64(a["swa_bf16"][:, s: s + sh.W]), a["sink"], 1 / math.sqrt(sh.c),
-                                        a["q_pos"][:, ss], sh.W)
-        assert_bf16_output(bf16_f64(out_bits[:, ss]), o_o, f"prefill attention, query {s}")
-        assert_close(lse_h[:, ss], lse_o, TOL_F32, f"prefill lse, query {s}")
+    mid = rng.choice(np.arange(64, sh.S - 64), 128, replace=False)
+    sample = np.concatenate([np.arange(64), np.sort(mid), np.arange(sh.S - 64, sh.S)])
+    for c0 in range(0, len(sample), 16):
+        qs = sample[c0:c0 + 16]
+        qI = O.dequant_rows(a["qI_fp8"][:, qs], a["qI_scale"][:, qs])
+        sc_o = O.index_scores(qI, a["w"][:, qs], KI, a["q_pos"][:, qs], sh.m)
+        assert_close(sc[:, qs], sc_o, TOL_F32, f"prefill scores, queries {qs.tolist()}")
+        assert_topk_equal(idx_h[:, qs], O.topk_indices(sc[:, qs], sh.k), sc[:, qs], sh.k,
+                          f"prefill top-k of GPU scores, queries {qs.tolist()}", exact=True)
+        assert_topk_equal(idx_h[:, qs], O.topk_indices(sc_o, sh.k), sc_o, sh.k, f"prefill top-k, queries {qs.tolist()}")
+        for s in qs:
+            ss = slice(s, s + 1)
+            sel = idx_h[0, s]
+            rows = sorted({int(j) for j in sel if j >= 0})
+            kv_sel = np.zeros((1, Nc, sh.c))
+            kv_sel[0, rows] = bf16_f64(kv_h[0, rows])
+            o_o, lse_o = O.sparse_attention(bf16_f64(a["q_bf16"][:, ss]), kv_sel, idx_h[:, ss],
+                                            bf16_f64(a["swa_bf16"][:, s: s + sh.W]), a["sink"], 1 / math.sqrt(sh.c),
+                                            a["q_pos"][:, ss], sh.W)
+            assert_bf16_output(bf16_f64(out_bits[:, ss]), o_o, f"prefill attention, query {s}")
+            assert_close(lse_h[:, ss], lse_o, TOL_F32, f"prefill lse, query {s}")

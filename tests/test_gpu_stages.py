@@ -54,9 +54,16 @@ def test_tiny_layer_chain_fp32(lib):
     assert_close(sc.cpu().numpy(), sc_o, TOL_F32, "index scores")
     assert_topk_equal(idx.cpu().numpy(), idx_o, sc_o, sh.k, "top-k")
     assert_close(out2.cpu().numpy(), o_o, TOL_F32, "attention (oracle indices)")
-    if np.array_equal(idx.cpu().numpy(), idx_o):
-        assert_close(out.cpu().numpy(), o_o, TOL_F32, "attention (end to end)")
-        assert_close(lse.cpu().numpy(), lse_o, TOL_F32, "lse")
+    # end to end, always: the oracle's attention over the GPU's own entries and selection
+    # (where the selections agree this is the oracle chain itself)
+    idx_g = idx.cpu().numpy()
+    o_g, lse_g = O.sparse_attention(a["q"], kv.cpu().numpy().astype(np.float64), idx_g, a["swa"], a["sink"],
+                                    1 / math.sqrt(sh.c), a["q_pos"], sh.W)
+    assert_close(out.cpu().numpy(), o_g, TOL_F32, "attention (end to end, GPU entries and selection)")
+    assert_close(lse.cpu().numpy(), lse_g, TOL_F32, "lse (end to end)")
+    if np.array_equal(idx_g, idx_o):
+        assert_close(out.cpu().numpy(), o_o, TOL_F32, "attention (end to end, oracle chain)")
+        assert_close(lse.cpu().numpy(), lse_o, TOL_F32, "lse (oracle chain)")
 
 
 # ---------------------------------------------------------------------------------------
@@ -250,9 +257,10 @@ def test_attention_sink_only_limit(lib):
     (True, 4, 128, 200, True, "fp8"),
     (True, 4, 512, 64, False, "bf16"),
     (False, 128, 512, 512, False, "bf16"),
+    (False, 128, 512, 8192, False, "bf16"),          # the HCA compressor over 8192 tokens: 64 entries
 ])
 def test_compress_bf16(lib, overlap, m, c, T, with_prev, out_kind):
-    B, d = 2, 256
+    B, d = (1, 256) if T >= 4096 else (2, 256)
     a = I.compressor_inputs(20 + m + c, B, T, d, m, c, overlap, 0.05, with_prev)
     p0 = 4096 if with_prev else 0
     kw = dict(overlap=overlap, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6, p0=p0)
