@@ -23,14 +23,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
-          4: "CSA_ERR_HIP"}
+          4: "CSA_ERR_HIP", 5: "CSA_ERR_SCRATCH"}
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
-           "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn")
+           "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn",
+           "csa_sparse_attn_noalloc_max_bytes", "csa_sparse_attn_noalloc")
 
 
 class CSAError(RuntimeError):
@@ -67,6 +68,8 @@ def _load() -> ctypes.CDLL:
         "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
         "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp], i),
         "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "csa_sparse_attn_noalloc_max_bytes": ([], sz),
+        "csa_sparse_attn_noalloc": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -277,6 +280,23 @@ def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=
     _check("csa_sparse_attn", _lib.csa_sparse_attn(
         _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
         _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+    return out
+
+
+def sparse_attn_noalloc_max_bytes() -> int:
+    return int(_lib.csa_sparse_attn_noalloc_max_bytes())
+
+
+def csa_sparse_attn_noalloc(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None,
+                            stream=None):
+    """csa_sparse_attn with the split partials in the library's fixed scratch (no workspace)."""
+    _dev(q, kv_comp, idx, swa, sink, out, lse, q_pos)
+    B, S, H, c = q.shape
+    Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
+    scale = 1.0 / math.sqrt(c) if scale is None else scale
+    _check("csa_sparse_attn_noalloc", _lib.csa_sparse_attn_noalloc(
+        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), _dtype(q), float(scale), B, S, H, c, Nc, k, Ls,
+        W, _p(out), _p(lse), _stream(stream)))
     return out
 
 

@@ -13,6 +13,8 @@ bool topk_supported(int, int, bool);
 int launch_attention(bool, const void*, const void*, const int32_t*, const int64_t*, int, const void*, const float*,
                      int, float, int, int, int, int, int, int, int, int, void*, float*, void*, size_t, hipStream_t);
 size_t attn_workspace_bytes(int, int, int, int, int, int);
+size_t attn_scratch_bytes();
+int attn_scratch(void**);
 int launch_compress(const void*, const void*, int, const void*, const float*, int, int, int, int, int, int, int,
                     float, float, int64_t, void*, float*, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
@@ -53,6 +55,8 @@ const char* csa_status_string(int status) {
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: no kernel for this dtype/shape combination";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace smaller than the size query returned";
     case CSA_ERR_HIP: return "CSA_ERR_HIP: the HIP runtime rejected a kernel launch";
+    case CSA_ERR_SCRATCH:
+      return "CSA_ERR_SCRATCH: the call needs more scratch than the library's fixed scratch array holds";
     default: return "unknown csa_status";
   }
 }
@@ -255,6 +259,25 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, cons
   CSA_REQUIRE(aligned16(ws));
   return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
                           lse, ws, ws_bytes, as_stream(stream));
+}
+
+size_t csa_sparse_attn_noalloc_max_bytes(void) { return attn_scratch_bytes(); }
+
+int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
+                            const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
+                            int Nc, int k, int Ls, int W, void* out, float* lse, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(idx && k >= 1 && k <= 65536);
+  const size_t need = attn_workspace_bytes(B, S, H, c, std::min(W, Ls) + k, dtype);
+  if (need > attn_scratch_bytes()) return CSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = attn_scratch(&ws);
+    if (rc != CSA_OK) return rc;
+  }
+  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
+                          lse, ws, need, as_stream(stream));
 }
 
 int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes, const int64_t* q_pos,

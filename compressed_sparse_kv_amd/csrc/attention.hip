@@ -47,6 +47,7 @@
 // 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "attention_common.hpp"
@@ -926,6 +927,37 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
   hipLaunchKernelGGL(attn_merge<float>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, part_o, part_ml, sink, 1, H, c,
                      nq * H, static_cast<float*>(out), lse);
   CSA_LAUNCH_CHECK();
+  return CSA_OK;
+}
+
+
+// ------------------------------------------------------------------------------------
+// Fixed scratch for callers that cannot allocate (csa_sparse_attn_noalloc): the split
+// partials live in this file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy, at its own device address, until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and only that address is handed to kernels.
+// ------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t{32} << 20;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+size_t attn_scratch_bytes() { return kScratchBytes; }
+
+// Device address of this device's scratch array (looked up on the first call per device).
+int attn_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CSA_ERR_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
   return CSA_OK;
 }
 

@@ -50,7 +50,8 @@ typedef enum {
   CSA_ERR_INVALID_ARG = 1,
   CSA_ERR_UNSUPPORTED = 2,
   CSA_ERR_WORKSPACE = 3,
-  CSA_ERR_HIP = 4
+  CSA_ERR_HIP = 4,
+  CSA_ERR_SCRATCH = 5
 } csa_status;
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
@@ -255,6 +256,28 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
                     const int64_t* q_pos, const void* swa, const float* sink, int dtype, float scale,
                     int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * csa_sparse_attn for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments and
+ * results as csa_sparse_attn (the same kernels, bit for bit), without a workspace: the
+ * split partials go to one fixed scratch array of csa_sparse_attn_noalloc_max_bytes()
+ * bytes (32 MiB) that the library holds on every GPU it runs on until the process ends.
+ * The call itself allocates nothing (no hipMalloc, no hipFree); its first call on a
+ * device looks up that device's scratch address.
+ *   A call whose partials (csa_attn_workspace_size with max_rows = min(W, Ls) + k) exceed
+ *   the scratch returns CSA_ERR_SCRATCH before anything is launched.
+ *   All calls on one GPU share that GPU's scratch and leave their partials in it: two
+ *   calls that may overlap on one GPU (different streams, not ordered) race and give
+ *   wrong results; order them.  Nothing in the scratch needs clearing between calls
+ *   (every partial a call reads, it has written).
+ * ------------------------------------------------------------------------------ */
+size_t csa_sparse_attn_noalloc_max_bytes(void);
+
+int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
+                            const void* swa, const float* sink, int dtype, float scale,
+                            int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                            void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Stages 3 and 4a in one call (decode shapes): csa_topk_merge of the segment
