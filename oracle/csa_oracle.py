@@ -370,3 +370,101 @@ def dense_attention(q, kv_comp, q_pos, m: int, swa, sink, scale, W: int):
         for s in range(S):
             idx[b, s, :nv[b, s]] = np.arange(nv[b, s])
     return sparse_attention(q, kv_comp, idx, swa, sink, scale, q_pos, W)
+
+
+# ---------------------------------------------------------------------------
+# Decode-time compressor: the (C, Z) ring and the block-boundary emission
+# ---------------------------------------------------------------------------
+
+def decode_compress(hidden, W, bias, *, overlap: bool, m: int, c: int, d_rope: int, rope_theta: float,
+                    rms_eps: float, p0: int, hidden_prev=None, online: bool = False):
+    """Token-by-token compressor of one sequence, as a decode loop runs it.
+
+    [HCA-CSA] section "KV cache：成品与原料" (a ring of FP32 (C, Z) rows of the last 2m
+    tokens for CSA, m for HCA; a compressed entry is produced only when a token completes
+    its block) and section "在 SGLang 里的落点" (the CSA emission reads 2m ring slots: the
+    current block's and the previous block's); [KV-COMP] section 9.3 (state until the
+    block boundary, then one pooled entry written to the cache).  The HCA "online"
+    variant keeps, per channel, only a running (max, sum, weighted sum) over the block.
+
+    hidden: [T, d] real values of the tokens at positions p0 .. p0+T-1 (p0 % m == 0);
+    hidden_prev: [m, d] the m tokens before p0 (with overlap their b-stream feeds the entry
+    of block p0/m), or None: no earlier block (entry 0's b-slots are -inf / 0 padding).
+    W, bias as csa_compress.  Returns {entry index i: float64 [c]} for every block that a
+    token of `hidden` completes, in the order emitted.
+
+    The pooling below is written for the ring (slot = position mod ring size) and for the
+    running (max, sum, acc) triple; it shares no step with compressor_entries beyond the
+    Norm and RoPE helpers.
+    """
+    hidden = np.asarray(hidden, np.float64)
+    W = np.asarray(W, np.float64)
+    bias = np.asarray(bias, np.float64)
+    assert p0 % m == 0
+    n_slots = 2 * m if overlap else m
+    ring = {}                                    # slot -> projection row of the token stored there
+    run = None                                   # online HCA: (mx, sm, acc) per channel
+    out = {}
+
+    def push(t, h):
+        nonlocal run
+        proj = h @ W                                            # this token's C and Z streams
+        ring[t % n_slots] = (t, proj)
+        if online:
+            r = t % m
+            z = proj[c:2 * c] + bias[0][r]
+            if r == 0:                                          # first token of a block
+                run = (z.copy(), np.ones(c), proj[:c].copy())
+            else:
+                mx, sm, acc = run
+                mn = np.maximum(mx, z)
+                a_old, a_new = np.exp(mx - mn), np.exp(z - mn)
+                run = (mn, sm * a_old + a_new, acc * a_old + a_new * proj[:c])
+
+    if hidden_prev is not None:
+        for r in range(m):
+            push(p0 - m + r, np.asarray(hidden_prev[r], np.float64))
+    for s in range(hidden.shape[0]):
+        t = p0 + s
+        push(t, hidden[s])
+        if (t + 1) % m != 0:
+            continue
+        i = t // m                                              # the block this token completes
+        if online:
+            mx, sm, acc = run
+            u = acc / sm
+        else:
+            logits, values = [], []
+            for r in range(m):                                  # a-slots: block i
+                tt, proj = ring[(m * i + r) % n_slots]
+                assert tt == m * i + r
+                if overlap:
+                    logits.append(proj[c:2 * c] + bias[0][r]); values.append(proj[:c])
+                else:
+                    logits.append(proj[c:2 * c] + bias[0][r]); values.append(proj[:c])
+            if overlap:                                         # b-slots: block i-1, if there is one
+                for r in range(m):
+                    pos_b = m * (i - 1) + r
+                    if pos_b < 0:
+                        logits.append(np.full(c, -np.inf)); values.append(np.zeros(c))
+                        continue
+                    tt, proj = ring[pos_b % n_slots]
+                    assert tt == pos_b, "the ring lacks the previous block"
+                    logits.append(proj[3 * c:4 * c] + bias[1][r]); values.append(proj[2 * c:3 * c])
+            L = np.stack(logits); V = np.stack(values)
+            e = np.exp(L - L.max(axis=0))
+            u = (e * V).sum(axis=0) / e.sum(axis=0)
+        out[i] = rope(rms_norm(u[None], rms_eps), m * i, d_rope, rope_theta)[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Inverse RoPE on the attention output
+# ---------------------------------------------------------------------------
+
+def inverse_rope(o, pos, d_rope: int, theta: float):
+    """The attention output rotated back by the query's own position: RoPE at -t on its
+    last d_rope channels, so that a row rotated at position p contributes a rotation by
+    p - t ([V4-CSA2] section 12.1 "Partial RoPE 与 inverse RoPE"; [ATTN-CMP] section
+    "CSA（DeepSeek-V4）": the last 64 output dimensions are rotated back by RoPE(-t))."""
+    return rope(o, -np.asarray(pos, dtype=np.float64), d_rope, theta)
