@@ -22,10 +22,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+CSA_LAYOUT_ROWS, CSA_LAYOUT_B16 = 0, 1
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
           4: "CSA_ERR_HIP", 5: "CSA_ERR_SCRATCH"}
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
+           "csa_compress_state_size", "csa_compress_decode_workspace_size", "csa_compress_decode",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
@@ -52,6 +54,9 @@ def _load() -> ctypes.CDLL:
         "csa_version": ([], i),
         "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
+        "csa_compress_state_size": ([i, i, i, i, i], sz),
+        "csa_compress_decode_workspace_size": ([i, i, i], sz),
+        "csa_compress_decode": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i, vp, vp, vp, i, i, i, vp, sz, vp], i),
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
         "csa_index_topk_workspace_size": ([i, i, i, i], sz),
         "csa_index_topk": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
@@ -65,11 +70,12 @@ def _load() -> ctypes.CDLL:
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
         "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
-        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
-        "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp, vp, sz, vp], i),
-        "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
+        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
+        "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp, sz,
+                                  vp], i),
+        "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
         "csa_sparse_attn_noalloc_max_bytes": ([], sz),
-        "csa_sparse_attn_noalloc": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, vp, vp, vp], i),
+        "csa_sparse_attn_noalloc": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -146,6 +152,38 @@ def csa_compress(hidden, hidden_prev, w_proj, bias, *, overlap: bool, m: int, c:
         d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale), _dtype(out),
         _p(ws), wsb, _stream(stream)))
     return out
+
+
+def compress_state_size(B, m, c, overlap, online=False) -> int:
+    return int(_lib.csa_compress_state_size(B, m, c, int(overlap), int(online)))
+
+
+def compress_decode_workspace_size(B, c, overlap) -> int:
+    return int(_lib.csa_compress_decode_workspace_size(B, c, int(overlap)))
+
+
+def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: bool, m: int, c: int, d_rope: int,
+                        rope_theta: float, rms_eps: float, online: bool = False, emit: bool = True,
+                        cache_scale=None, layout: int = CSA_LAYOUT_ROWS, Nc_max: int | None = None, ws=None,
+                        stream=None):
+    """One decode token per sequence: hidden [B,d], pos [B] int64, state (uint8 or fp32,
+    compress_state_size bytes); a completed block's entry goes to cache ([B,Nc_max,c] rows,
+    or the 16-entry blocked FP8 layout with layout=CSA_LAYOUT_B16, Nc_max given)."""
+    _dev(hidden, w_proj, bias, pos, state, cache, cache_scale)
+    B, d = hidden.shape
+    if Nc_max is None:
+        if layout != CSA_LAYOUT_ROWS:
+            raise ValueError("Nc_max is required for the blocked layout")
+        Nc_max = cache.shape[1]
+    if state.numel() * state.element_size() < compress_state_size(B, m, c, overlap, online):
+        raise ValueError("state smaller than compress_state_size")
+    ws, wsb = _ws(compress_decode_workspace_size(B, c, overlap), ws, hidden.device)
+    out_dt = CSA_FP8_E4M3 if layout == CSA_LAYOUT_B16 else _dtype(cache)
+    _check("csa_compress_decode", _lib.csa_compress_decode(
+        _p(hidden), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), int(online), B, d, m, c, d_rope,
+        float(rope_theta), float(rms_eps), _p(pos), int(emit), _p(state), _p(cache), _p(cache_scale), out_dt,
+        int(layout), int(Nc_max), _p(ws), wsb, _stream(stream)))
+    return cache
 
 
 # ---------------------------------------------------------------------------------------
@@ -268,9 +306,10 @@ def attn_workspace_size(B, S, H, c, max_rows, dtype) -> int:
 
 
 def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None, ws=None,
-                    stream=None):
+                    inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
     """q [B,S,H,c], kv_comp [B,Nc,c], idx [B,S,k] int32, swa [B,Ls,c], sink [H] fp32;
-    q_pos [B,S] int64 (optional) leaves out window rows of negative positions."""
+    q_pos [B,S] int64 (optional) leaves out window rows of negative positions; inv_rope_d > 0
+    (needs q_pos) rotates the output's last inv_rope_d channels back by the query position."""
     _dev(q, kv_comp, idx, swa, sink, out, lse, ws, q_pos)
     B, S, H, c = q.shape
     Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
@@ -279,7 +318,7 @@ def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_sparse_attn", _lib.csa_sparse_attn(
         _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
-        _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+        int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
     return out
 
 
@@ -288,7 +327,7 @@ def sparse_attn_noalloc_max_bytes() -> int:
 
 
 def csa_sparse_attn_noalloc(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None,
-                            stream=None):
+                            inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
     """csa_sparse_attn with the split partials in the library's fixed scratch (no workspace)."""
     _dev(q, kv_comp, idx, swa, sink, out, lse, q_pos)
     B, S, H, c = q.shape
@@ -296,12 +335,12 @@ def csa_sparse_attn_noalloc(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     _check("csa_sparse_attn_noalloc", _lib.csa_sparse_attn_noalloc(
         _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), _dtype(q), float(scale), B, S, H, c, Nc, k, Ls,
-        W, _p(out), _p(lse), _stream(stream)))
+        W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _stream(stream)))
     return out
 
 
 def csa_topk_sparse_attn(q, kv_comp, cand, swa, sink, *, k: int, W: int, out, q_pos=None, lse=None, idx=None,
-                         scale=None, ws=None, stream=None):
+                         scale=None, ws=None, inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
     """The k best of each query's segment candidates (cand from csa_index_score_segments),
     then csa_sparse_attn over them; idx [B,S,k] int32 (optional) receives the selection."""
     _dev(q, kv_comp, cand, swa, sink, out, lse, idx, ws, q_pos)
@@ -312,12 +351,13 @@ def csa_topk_sparse_attn(q, kv_comp, cand, swa, sink, *, k: int, W: int, out, q_
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_topk_sparse_attn", _lib.csa_topk_sparse_attn(
         _p(q), _p(kv_comp), _p(cand), cand.numel() * cand.element_size(), _p(q_pos), _p(swa), _p(sink), dt,
-        float(scale), B, S, H, c, Nc, k, Ls, W, _p(out), _p(lse), _p(idx), _p(ws), wsb, _stream(stream)))
+        float(scale), B, S, H, c, Nc, k, Ls, W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(idx), _p(ws),
+        wsb, _stream(stream)))
     return out
 
 
 def hca_dense_attn(q, kv_comp, q_pos, swa, sink, *, m: int, W: int, out, lse=None, scale=None, ws=None,
-                   stream=None):
+                   inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
     """q [B,S,H,c], kv_comp [B,Nc,c], q_pos [B,S] int64, swa [B,Ls,c], sink [H] fp32."""
     _dev(q, kv_comp, q_pos, swa, sink, out, lse, ws)
     B, S, H, c = q.shape
@@ -327,5 +367,5 @@ def hca_dense_attn(q, kv_comp, q_pos, swa, sink, *, m: int, W: int, out, lse=Non
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + Nc, dt), ws, q.device)
     _check("hca_dense_attn", _lib.hca_dense_attn(
         _p(q), _p(kv_comp), _p(q_pos), m, _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, Ls, W,
-        _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+        int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
     return out

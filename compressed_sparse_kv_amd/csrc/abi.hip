@@ -11,13 +11,18 @@ int launch_topk(const float*, int, int, int, int32_t*, void*, size_t, int, hipSt
 size_t topk_workspace_bytes(int, int, int);
 bool topk_supported(int, int, bool);
 int launch_attention(bool, const void*, const void*, const int32_t*, const int64_t*, int, const void*, const float*,
-                     int, float, int, int, int, int, int, int, int, int, void*, float*, void*, size_t, hipStream_t);
+                     int, float, int, int, int, int, int, int, int, int, int, float, void*, float*, void*, size_t,
+                     hipStream_t);
 size_t attn_workspace_bytes(int, int, int, int, int, int);
 size_t attn_scratch_bytes();
 int attn_scratch(void**);
 int launch_compress(const void*, const void*, int, const void*, const float*, int, int, int, int, int, int, int,
                     float, float, int64_t, void*, float*, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
+size_t compress_state_bytes(int, int, int, int, int);
+size_t compress_decode_workspace_bytes(int, int, int);
+int launch_compress_decode(const void*, int, const void*, const float*, int, int, int, int, int, int, int, float,
+                           float, const int64_t*, int, float*, void*, float*, int, int, int, void*, hipStream_t);
 bool index_topk_fused_ok(int, int, int);
 int index_topk_segments(int);
 int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
@@ -29,8 +34,8 @@ int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
 int launch_topk_merge(uint2*, int, int, int, int32_t*, hipStream_t);
 size_t topk_merge_pairs_per_row(int, int);
 int launch_topk_attention(const void*, const void*, const uint2*, int, size_t, const int64_t*, const void*,
-                          const float*, float, int, int, int, int, int, int, void*, float*, int32_t*, void*, size_t,
-                          hipStream_t);
+                          const float*, float, int, int, int, int, int, int, int, float, void*, float*, int32_t*, void*,
+                          size_t, hipStream_t);
 int topk_attention_max_cand();
 int topk_merge_group(int, int);
 int launch_topk_merge_first(uint2*, int, int, int, size_t&, hipStream_t);
@@ -89,6 +94,39 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, cons
   if (ws == nullptr || ws_bytes < compress_workspace_bytes(B, T, m, c, overlap, has_prev)) return CSA_ERR_WORKSPACE;
   return launch_compress(hidden, hidden_prev, in_dtype, w_proj, bias, overlap, B, T, d, m, c, d_rope, rope_theta,
                          rms_eps, p0, out, out_scale, out_dtype, ws, as_stream(stream));
+}
+
+size_t csa_compress_state_size(int B, int m, int c, int overlap, int online) {
+  if (B <= 0 || m <= 0 || c <= 0) return 0;
+  return compress_state_bytes(B, m, c, overlap, online);
+}
+
+size_t csa_compress_decode_workspace_size(int B, int c, int overlap) {
+  if (B <= 0 || c <= 0) return 0;
+  return compress_decode_workspace_bytes(B, c, overlap);
+}
+
+int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias, int overlap,
+                        int online, int B, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
+                        const int64_t* pos, int emit, float* state, void* cache, float* cache_scale, int out_dtype,
+                        int out_layout, int Nc_max, void* ws, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(hidden && w_proj && bias && pos && state && cache);
+  CSA_REQUIRE((overlap == 0 || overlap == 1) && (online == 0 || online == 1) && !(online && overlap));
+  CSA_REQUIRE(B > 0 && d > 0 && m > 0 && c > 0 && Nc_max > 0);
+  CSA_REQUIRE(c % 2 == 0 && c <= 1024 && d_rope >= 0 && d_rope <= c && d_rope % 2 == 0);
+  CSA_REQUIRE(rms_eps >= 0.0f && rope_theta > 0.0f);
+  CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
+  CSA_REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_FP8_E4M3);
+  CSA_REQUIRE(out_dtype != CSA_FP8_E4M3 || cache_scale != nullptr);
+  CSA_REQUIRE(out_layout == CSA_LAYOUT_ROWS || out_layout == CSA_LAYOUT_B16);
+  CSA_REQUIRE(static_cast<int64_t>(B) * Nc_max * c < (int64_t{1} << 40));
+  if (out_layout == CSA_LAYOUT_B16 && (out_dtype != CSA_FP8_E4M3 || c != 128)) return CSA_ERR_UNSUPPORTED;
+  if (in_dtype == CSA_BF16 && d % 128 != 0) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(ws) && aligned16(state) && aligned16(hidden) && aligned16(w_proj));
+  if (ws == nullptr || ws_bytes < compress_decode_workspace_bytes(B, c, overlap)) return CSA_ERR_WORKSPACE;
+  return launch_compress_decode(hidden, in_dtype, w_proj, bias, overlap, online, B, d, m, c, d_rope, rope_theta,
+                                rms_eps, pos, emit, state, cache, cache_scale, out_dtype, out_layout, Nc_max, ws,
+                                as_stream(stream));
 }
 
 // ---- stage 2 ------------------------------------------------------------------------
@@ -235,8 +273,11 @@ size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dty
 }
 
 static int check_attn(const void* q, const void* kv, const void* swa, const float* sink, int dtype, float scale,
-                      int B, int S, int H, int c, int Nc, int Ls, int W, const void* out) {
+                      int B, int S, int H, int c, int Nc, int Ls, int W, const void* out, int inv_rope_d,
+                      float rope_theta, const int64_t* q_pos) {
   CSA_REQUIRE(q && kv && swa && sink && out);
+  CSA_REQUIRE(inv_rope_d >= 0 && inv_rope_d % 2 == 0 && inv_rope_d <= c);
+  CSA_REQUIRE(inv_rope_d == 0 || (q_pos != nullptr && rope_theta > 0.0f));
   CSA_REQUIRE(B > 0 && S > 0 && H > 0 && c > 0 && Nc > 0 && W > 0 && Ls >= S);
   CSA_REQUIRE(scale > 0.0f);
   CSA_REQUIRE(static_cast<int64_t>(B) * S < (int64_t{1} << 31));
@@ -252,21 +293,24 @@ static int check_attn(const void* q, const void* kv, const void* swa, const floa
 
 int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos, const void* swa,
                     const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
-                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+                    int inv_rope_d, float rope_theta, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+                            q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(idx && k >= 1 && k <= 65536);
   CSA_REQUIRE(aligned16(ws));
-  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
-                          lse, ws, ws_bytes, as_stream(stream));
+  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
+                          inv_rope_d, rope_theta, out, lse, ws, ws_bytes, as_stream(stream));
 }
 
 size_t csa_sparse_attn_noalloc_max_bytes(void) { return attn_scratch_bytes(); }
 
 int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
                             const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
-                            int Nc, int k, int Ls, int W, void* out, float* lse, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+                            int Nc, int k, int Ls, int W, int inv_rope_d, float rope_theta, void* out, float* lse,
+                            void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+                            q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(idx && k >= 1 && k <= 65536);
   const size_t need = attn_workspace_bytes(B, S, H, c, std::min(W, Ls) + k, dtype);
@@ -276,15 +320,16 @@ int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* i
     const int rc = attn_scratch(&ws);
     if (rc != CSA_OK) return rc;
   }
-  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W, out,
-                          lse, ws, need, as_stream(stream));
+  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
+                          inv_rope_d, rope_theta, out, lse, ws, need, as_stream(stream));
 }
 
 int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes, const int64_t* q_pos,
                          const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
-                         int Nc, int k, int Ls, int W, void* out, float* lse, int32_t* idx, void* ws,
-                         size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+                         int Nc, int k, int Ls, int W, int inv_rope_d, float rope_theta, void* out, float* lse,
+                         int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+                            q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(cand && k >= 1 && k <= 2048);
   CSA_REQUIRE(aligned16(cand) && aligned16(ws));
@@ -305,18 +350,20 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t 
   const int n_cand = launch_topk_merge_first(pairs, rows, G, k, offset, as_stream(stream));
   if (n_cand < 0) return CSA_ERR_HIP;
   return launch_topk_attention(q, kv_comp, pairs + offset, n_cand, topk_merge_pairs_per_row(G, k), q_pos, swa, sink,
-                               scale, B, S, Nc, k, Ls, W, out, lse, idx, ws, ws_bytes, as_stream(stream));
+                               scale, B, S, Nc, k, Ls, W, inv_rope_d, rope_theta, out, lse, idx, ws, ws_bytes,
+                               as_stream(stream));
 }
 
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m, const void* swa, const float* sink,
-                   int dtype, float scale, int B, int S, int H, int c, int Nc, int Ls, int W, void* out, float* lse,
-                   void* ws, size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out);
+                   int dtype, float scale, int B, int S, int H, int c, int Nc, int Ls, int W, int inv_rope_d,
+                   float rope_theta, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+                            q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(q_pos && m > 0);
   CSA_REQUIRE(aligned16(ws));
-  return launch_attention(true, q, kv_comp, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W, out,
-                          lse, ws, ws_bytes, as_stream(stream));
+  return launch_attention(true, q, kv_comp, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W,
+                          inv_rope_d, rope_theta, out, lse, ws, ws_bytes, as_stream(stream));
 }
 
 }  // extern "C"

@@ -458,10 +458,23 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
     uint16_t* ob = a.out + (static_cast<size_t>(qi) * kAH + kHG * hg) * kAC;
+    const int64_t tq = a.rope_d > 0 ? a.q_pos[qi] : 0;
 #pragma unroll
-    for (int t = 0; t < Sh::kPart / 16; ++t)
+    for (int t = 0; t < Sh::kPart / 16; ++t) {
+      float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(o[t][i] * fh[i]);
+      for (int i = 0; i < 4; ++i) v[i] = o[t][i] * fh[i];
+      // inverse RoPE of the output (the tile's 16 columns: lane pairs hold channel pairs)
+      if (a.rope_d > 0 && Sh::kPart * part + 16 * t + 16 > kAC - a.rope_d) {
+        const int col = col0 + 16 * t;
+        float cs = 1.0f, sn = 0.0f;
+        if (col >= kAC - a.rope_d) rope_cs_sn(col, kAC, a.rope_d, a.rope_theta, tq, cs, sn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(v[i]);
+    }
   } else {
     const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
     if (part == 0 && g == 0) {
@@ -486,7 +499,9 @@ template <int KT>
 __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict__ part_o,
                                                         const float* __restrict__ part_ml,
                                                         const float* __restrict__ sink, int nsplit, int nq,
-                                                        uint16_t* __restrict__ out, float* __restrict__ lse) {
+                                                        uint16_t* __restrict__ out, float* __restrict__ lse,
+                                                        const int64_t* __restrict__ q_pos, int rope_d,
+                                                        float rope_theta) {
   constexpr int kTiles = kAC / 16;
   constexpr int kBlocksPerQuery = kNHG * kTiles / KT / 4;
   constexpr int kMaxFast = KT == 1 ? 8 : 4;             // splits held in registers at once
@@ -586,14 +601,42 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
     }
   }
   uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct0 + (l & 15);
+  const int64_t tq = rope_d > 0 ? q_pos[qi] : 0;
 #pragma unroll
-  for (int t = 0; t < KT; ++t)
+  for (int t = 0; t < KT; ++t) {
+    float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f);
+    for (int i = 0; i < 4; ++i) v[i] = den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f;
+    // inverse RoPE of the output (lane pairs hold channel pairs)
+    if (rope_d > 0 && 16 * (ct0 + t) + 16 > kAC - rope_d) {
+      const int col = 16 * (ct0 + t) + (l & 15);
+      float cs = 1.0f, sn = 0.0f;
+      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_theta, tq, cs, sn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(v[i]);
+  }
   if (lse && ct0 == 0 && (l & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
+  }
+}
+
+// Inverse RoPE of 8 consecutive output channels c0 .. c0+7 (c0 even: they hold whole pairs).
+__device__ __forceinline__ void rope_back8(float (&v)[8], int c0, int c, int d_rope, float theta, int64_t t) {
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const int col = c0 + j;
+    if (col >= c - d_rope && col + 1 < c) {
+      float cs, sn;
+      rope_cs_sn(col, c, d_rope, theta, t, cs, sn);
+      const float x = v[j], y = v[j + 1];
+      v[j] = rope_back(x, y, col, cs, sn);
+      v[j + 1] = rope_back(y, x, col + 1, cs, sn);
+    }
   }
 }
 
@@ -603,7 +646,8 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
 template <typename OutT>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                   const float* __restrict__ sink, int nsplit, int H, int c, int nqh,
-                                                  OutT* __restrict__ out, float* __restrict__ lse) {
+                                                  OutT* __restrict__ out, float* __restrict__ lse,
+                                                  const int64_t* __restrict__ q_pos, int rope_d, float rope_theta) {
   const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (qh >= nqh) return;
   const int lane = threadIdx.x & 63;
@@ -644,16 +688,18 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     OutT* dst = out + (qi * H + h) * kAC + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv;
+    if (rope_d > 0) rope_back8(acc, 8 * lane, kAC, rope_d, rope_theta, q_pos[qi]);
     if constexpr (sizeof(OutT) == 2) {
       uint32_t pk[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pk[j] = static_cast<uint32_t>(f32_to_bf16(acc[2 * j] * inv)) |
-                (static_cast<uint32_t>(f32_to_bf16(acc[2 * j + 1] * inv)) << 16);
+        pk[j] = static_cast<uint32_t>(f32_to_bf16(acc[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * j + 1])) << 16);
       *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = acc[j] * inv;
+      for (int j = 0; j < 8; ++j) dst[j] = acc[j];
     }
     if (lse && lane == 0) lse[qi * H + h] = (M == -INFINITY || den <= 0.0f) ? -INFINITY : (M + log2f(den)) * kLn2;
     return;
@@ -684,9 +730,12 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
       }
     }
     OutT* dst = out + (qi * H + h) * c + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] *= inv;
+    if (rope_d > 0) rope_back8(acc, c0, c, rope_d, rope_theta, q_pos[qi]);
     for (int j = 0; j < 8 && c0 + j < c; ++j) {
-      if constexpr (sizeof(OutT) == 2) dst[j] = f32_to_bf16(acc[j] * inv);
-      else dst[j] = acc[j] * inv;
+      if constexpr (sizeof(OutT) == 2) dst[j] = f32_to_bf16(acc[j]);
+      else dst[j] = acc[j];
     }
   }
   if (lse && lane == 0) lse[qi * H + h] = (M == -INFINITY || den <= 0.0f) ? -INFINITY : (M + log2f(den)) * kLn2;
@@ -848,18 +897,18 @@ static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream
   if (ns > 1) {
     if (ns <= 4)
       hipLaunchKernelGGL(attn_merge_tiles<4>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 16)), dim3(256), 0, st,
-                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse);
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_theta);
     else
       hipLaunchKernelGGL(attn_merge_tiles<1>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st,
-                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse);
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_theta);
     CSA_LAUNCH_CHECK();
   }
   return CSA_OK;
 }
 
 static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, int m, const void* swa,
-                          const float* sink, float scale, int B, int S, int Nc, int k, int Ls, int W, void* out,
-                          float* lse) {
+                          const float* sink, float scale, int B, int S, int Nc, int k, int Ls, int W, int rope_d,
+                          float rope_theta, void* out, float* lse) {
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint16_t*>(kv);
@@ -870,6 +919,8 @@ static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, i
   a.nq = B * S; a.S = S; a.Nc = Nc; a.k = k; a.Ls = Ls; a.W = W; a.m = m;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
+  a.rope_d = rope_d;
+  a.rope_theta = rope_theta;
   return a;
 }
 
@@ -883,13 +934,13 @@ int topk_attention_max_cand() { return std::min(NarrowShape::kMaxCand2, WideShap
 
 int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int n_cand, size_t cand_stride,
                           const int64_t* q_pos, const void* swa, const float* sink, float scale, int B, int S, int Nc,
-                          int k, int Ls, int W, void* out, float* lse, int32_t* idx_out, void* ws, size_t ws_bytes,
-                          hipStream_t st) {
+                          int k, int Ls, int W, int rope_d, float rope_theta, void* out, float* lse, int32_t* idx_out,
+                          void* ws, size_t ws_bytes, hipStream_t st) {
   const int max_rows = std::min(W, Ls) + k;
   if (ws_bytes < attn_workspace_bytes(B, S, kAH, kAC, max_rows, CSA_BF16)) return CSA_ERR_WORKSPACE;
   if (n_cand > topk_attention_max_cand() || k > n_cand || cand_stride < static_cast<size_t>(n_cand))
     return CSA_ERR_UNSUPPORTED;
-  AttnArgs a = attn_args(q, kv, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, out, lse);
+  AttnArgs a = attn_args(q, kv, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out, lse);
   a.cand = cand;
   a.n_cand = n_cand;
   a.cand_stride = cand_stride;
@@ -901,13 +952,14 @@ int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int 
 
 int launch_attention(bool dense, const void* q, const void* kv, const int32_t* idx, const int64_t* q_pos, int m,
                      const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc,
-                     int k, int Ls, int W, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+                     int k, int Ls, int W, int rope_d, float rope_theta, void* out, float* lse, void* ws,
+                     size_t ws_bytes, hipStream_t st) {
   const int nq = B * S;
   const int max_rows = std::min(W, Ls) + (dense ? Nc : k);
   if (ws_bytes < attn_workspace_bytes(B, S, H, c, max_rows, dtype)) return CSA_ERR_WORKSPACE;
   const float scale_log2 = scale * kLog2e;
   if (dtype == CSA_BF16) {
-    AttnArgs a = attn_args(q, kv, q_pos, m, swa, sink, scale, B, S, Nc, k, Ls, W, out, lse);
+    AttnArgs a = attn_args(q, kv, q_pos, m, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out, lse);
     a.idx = idx;
     return run_attn_bf16(dense ? kSrcDense : kSrcIdx, a, max_rows, ws, st);
   }
@@ -925,7 +977,7 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
                        Nc, k, Ls, W, m, part_o, part_ml);
   CSA_LAUNCH_CHECK();
   hipLaunchKernelGGL(attn_merge<float>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, part_o, part_ml, sink, 1, H, c,
-                     nq * H, static_cast<float*>(out), lse);
+                     nq * H, static_cast<float*>(out), lse, q_pos, rope_d, rope_theta);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

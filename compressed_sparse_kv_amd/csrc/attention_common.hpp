@@ -43,7 +43,30 @@ struct AttnArgs {
   int n_cand;
   size_t cand_stride;        // pairs from one row of cand to the next
   int32_t* idx_out;          // [B*S, k] the selection made from cand, or null
+  int rope_d;                // > 0: rotate the output's last rope_d channels back by the query position
+  float rope_theta;
 };
+
+// The value of channel `col` after the inverse RoPE of its query's output: pair
+// (2p, 2p+1) of the last d_rope of c channels rotated by -t * theta^(-2p/d_rope), the
+// angle formed in double (positions reach 2^20 and beyond).  cs/sn come from rope_cs_sn.
+__device__ __forceinline__ void rope_cs_sn(int col, int c, int d_rope, float theta, int64_t t, float& cs, float& sn) {
+  const int p = (col - (c - d_rope)) >> 1;
+  const double ang = static_cast<double>(t) * pow(static_cast<double>(theta), -2.0 * p / d_rope);
+  cs = static_cast<float>(cos(ang));
+  sn = static_cast<float>(sin(ang));
+}
+
+// x' = x cos + y sin (even channel), y' = y cos - x sin (odd channel); `partner` is the
+// other member of the pair.
+__device__ __forceinline__ float rope_back(float v, float partner, int col, float cs, float sn) {
+  return (col & 1) ? fmaf(-partner, sn, v * cs) : fmaf(partner, sn, v * cs);
+}
+
+// The value held by the lane whose index differs in bit 0 (DPP quad permutation 1,0,3,2).
+__device__ __forceinline__ float pair_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
 
 // Window rows of query s: rows w_lo .. w_lo + n_swa - 1 of the sequence's swa tensor,
 // whose last row holds the last query's position t_last.  Rows of negative positions

@@ -56,6 +56,10 @@ typedef enum {
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
 
+/* Cache layouts of compressed entries: row-major [B, Nc, c], or (indexer keys, c = 128,
+ * FP8 codes) the 16-entry blocks of csa_index_keys_b16. */
+typedef enum { CSA_LAYOUT_ROWS = 0, CSA_LAYOUT_B16 = 1 } csa_layout;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* csa_status_string(int status);
 
@@ -99,6 +103,48 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
                  float rms_eps, int64_t p0,
                  void* out, float* out_scale, int out_dtype,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Stage 1, decode form: one new token per sequence.
+ * [HCA-CSA] "KV cache：成品与原料" (an FP32 ring of the (C, Z) projections of the last 2m
+ * tokens for CSA, m for HCA; an entry is produced only by the token that completes its
+ * block; the HCA online state keeps one running (max, sum, weighted sum) per channel) and
+ * "在 SGLang 里的落点" (the CSA emission reads the current and the previous block's slots);
+ * [KV-COMP] section 9.3 (state until the block boundary, then one entry into the cache).
+ *
+ * For every sequence b, with t = pos[b] the position of its new token hidden[b]:
+ *   1. the token's projection (C^a, Z^a, C^b, Z^b) (overlap = 1) or (C, Z) (overlap = 0)
+ *      = w_proj . hidden[b] enters ring slot t mod 2m (overlap) or t mod m; with online = 1
+ *      (requires overlap = 0) it updates the running triple instead;
+ *   2. when emit != 0 and (t + 1) % m == 0, entry i = t / m is written to cache row i of
+ *      sequence b, exactly as csa_compress computes it over the block's tokens (entry 0
+ *      without a previous block: b-slots padded), i.e. RoPE(RMSNorm(pooled)) at position
+ *      m*i.  Rows i >= Nc_max are not written.  emit = 0 only fills the state (to prime
+ *      the ring with the last block of a prefill chunk before the first decode step).
+ *   Sequences with pos[b] < 0 are skipped.
+ * The state is valid for the entry of block i once the steps of block i (and, with
+ * overlap, block i-1) have run on it; the online triple restarts at each block's first
+ * token.  Nothing in it needs initialising.
+ *
+ *   hidden  [B, d] in_dtype (CSA_F32, or CSA_BF16 with d % 128 == 0)
+ *   w_proj, bias, m, c, d_rope, rope_theta, rms_eps: as csa_compress
+ *   pos     [B] int64 (device);  state: >= csa_compress_state_size(B, m, c, overlap, online)
+ *           bytes, fp32, 16-byte aligned, one share per sequence, kept by the caller across
+ *           calls.
+ *   cache   CSA_LAYOUT_ROWS: [B, Nc_max, c] in out_dtype (CSA_F32, CSA_BF16, or
+ *           CSA_FP8_E4M3 codes with cache_scale [B, Nc_max] = amax/448);
+ *           CSA_LAYOUT_B16: FP8 codes of c = 128 in 16-entry blocks
+ *           (csa_index_keys_b16_size(B, Nc_max) bytes) + cache_scale [B, Nc_max].
+ *   ws      >= csa_compress_decode_workspace_size(B, c, overlap) bytes.
+ * ------------------------------------------------------------------------------ */
+size_t csa_compress_state_size(int B, int m, int c, int overlap, int online);
+size_t csa_compress_decode_workspace_size(int B, int c, int overlap);
+
+int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias,
+                        int overlap, int online, int B, int d, int m, int c, int d_rope,
+                        float rope_theta, float rms_eps, const int64_t* pos, int emit, float* state,
+                        void* cache, float* cache_scale, int out_dtype, int out_layout, int Nc_max,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Stage 2: lightning-indexer scores.
@@ -247,6 +293,13 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
  *          Query s (of S consecutive queries) uses rows
  *          max(0, s+Ls-S-W+1) .. s+Ls-S  (positions t-W+1 .. t, t >= 0); requires Ls >= S.
  *   sink   [H] fp32;  scale > 0 (normally 1/sqrt(c)).
+ *   inv_rope_d, rope_theta: 0 = no epilogue; else the output of query (b,s) at position
+ *          t = q_pos[b,s] (q_pos required) has its last inv_rope_d channels rotated back by
+ *          its own position before the cast, pair (2p, 2p+1) by the angle
+ *          -t * rope_theta^(-2p/inv_rope_d) ([V4-CSA2] section 12.1 "Partial RoPE 与 inverse
+ *          RoPE": rows rotated at their positions then contribute by relative distance;
+ *          [ATTN-CMP] section "CSA（DeepSeek-V4）": the last 64 output dimensions rotated by
+ *          RoPE(-t)).  inv_rope_d even, <= c.  lse is unaffected.
  *   out    [B,S,H,c]   dtype;  lse [B,S,H] fp32 natural log, or NULL.
  *   ws >= csa_attn_workspace_size(...) bytes (split partial results).
  * ------------------------------------------------------------------------------ */
@@ -255,6 +308,7 @@ size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dty
 int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
                     const int64_t* q_pos, const void* swa, const float* sink, int dtype, float scale,
                     int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                    int inv_rope_d, float rope_theta,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
@@ -277,7 +331,7 @@ size_t csa_sparse_attn_noalloc_max_bytes(void);
 int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
                             const void* swa, const float* sink, int dtype, float scale,
                             int B, int S, int H, int c, int Nc, int k, int Ls, int W,
-                            void* out, float* lse, void* stream);
+                            int inv_rope_d, float rope_theta, void* out, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------------
  * Stages 3 and 4a in one call (decode shapes): csa_topk_merge of the segment
@@ -300,6 +354,7 @@ int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* i
 int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes,
                          const int64_t* q_pos, const void* swa, const float* sink, int dtype,
                          float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                         int inv_rope_d, float rope_theta,
                          void* out, float* lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
 
@@ -315,6 +370,7 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t 
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m,
                    const void* swa, const float* sink, int dtype, float scale,
                    int B, int S, int H, int c, int Nc, int Ls, int W,
+                   int inv_rope_d, float rope_theta,
                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -84,18 +84,39 @@ def test_invalid_arguments_are_rejected_before_launch():
     # Pro shape: 64 segment lists of 1024 merge in two levels (groups of 8): room for both
     assert lib.csa_index_segments_size(4, 1, 262144, 1024) == 4 * (64 + 8) * 1024 * 8
     # attention: Ls < S, unsupported bf16 shape, non-positive scale
-    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128, 0, 1e4,
                                fake, None, None, 0, None) == 1
-    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128, 0, 1e4,
                                fake, None, None, 0, None) == 2
-    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128,
+    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128, 0, 1e4,
                               fake, None, None, 0, None) == 1
+    # inverse RoPE of the output: needs the query positions, an even width <= c
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 64, 1e4,
+                               fake, None, None, 0, None) == 1
+    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 63, 1e4,
+                               fake, None, None, 0, None) == 1
+    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 128, 128, 1024, 1e4,
+                              fake, None, None, 0, None) == 1
+    # the decode compressor: online needs overlap 0; the blocked layout needs FP8 codes of c = 128
+    dec = lambda ov, on, c, dt, layout: lib.csa_compress_decode(
+        fake, 1, fake, fake, ov, on, 2, 256, 4, c, 64, 1e4, 1e-6, fake, 1, fake, fake, fake, dt, layout, 16, fake,
+        1 << 30, None)
+    assert dec(1, 1, 512, 1, 0) == 1
+    assert dec(1, 0, 512, 1, 1) == 2
+    assert dec(1, 0, 512, 2, 1) == 2
+    assert lib.csa_compress_decode(fake, 1, fake, fake, 1, 0, 2, 200, 4, 128, 64, 1e4, 1e-6, fake, 1, fake, fake, fake,
+                                   1, 0, 16, fake, 1 << 30, None) == 2       # bf16 hidden: d % 128 != 0
+    assert lib.csa_compress_decode(fake, 1, fake, fake, 1, 0, 2, 256, 4, 128, 64, 1e4, 1e-6, fake, 1, fake, fake, fake,
+                                   1, 0, 16, fake, 8, None) == 3             # workspace too small
+    assert lib.csa_compress_state_size(32, 4, 512, 1, 0) == 32 * 8 * 2048 * 4
+    assert lib.csa_compress_state_size(64, 128, 512, 0, 0) == 64 * 128 * 1024 * 4
+    assert lib.csa_compress_state_size(64, 128, 512, 0, 1) == 64 * 3 * 512 * 4
     # fused selection + attention: null candidates, fp32 dtype, too many candidates per
     # query after the first merge level (21 segments x 2048 -> 5 x 2048), workspace too
     # small for the split partials (also with two merge levels: V4-Pro, 64 segments x 1024)
     fused = lambda cand, dt, Nc, k, ws_bytes, cand_bytes=1 << 40: lib.csa_topk_sparse_attn(
-        fake, fake, cand, cand_bytes, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, fake, None, None,
-        fake, ws_bytes, None)
+        fake, fake, cand, cand_bytes, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, 0, 1e4, fake, None,
+        None, fake, ws_bytes, None)
     assert fused(None, 1, 32768, 512, 1 << 40) == 1
     assert fused(fake, 0, 32768, 512, 1 << 40) == 2
     assert fused(fake, 1, 86000, 2048, 1 << 40) == 2

@@ -1,0 +1,145 @@
+"""Decode-time compressor (csa_compress_decode) against the oracle's token-by-token
+compressor, through the C ABI: one call per decode step, every emitted entry checked
+(bf16 entries within one bf16 step + 1e-5, FP8 rows by the FP8 rule, fp32 at 1e-5), the
+16-entry blocked FP8 layout against csa_index_keys_b16 of the row-major result, the HCA ring
+and online states, priming the ring after a prefill chunk, and the skipped cases."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa_oracle as O
+from synthetic import inputs as I
+from tests.parity import (TOL_F32, assert_bf16_within_one_step, assert_close, assert_fp8_rows, bf16_f64, dev,
+                          dev_bf16, host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _steps(lib, a, kw, starts, T, Nc_max, out_dtype, layout=0, online=False, prime=None):
+    """Runs T decode steps of B sequences; sequence b's token s sits at position starts[b] + s.
+    prime: [B, m, d] tokens pushed (emit = 0) before the first step, at the m positions before."""
+    B = a["hidden_bf16"].shape[0]
+    m, c = kw["m"], kw["c"]
+    state = torch.empty(lib.compress_state_size(B, m, c, kw["overlap"], online), dtype=torch.uint8, device="cuda")
+    if layout == lib.CSA_LAYOUT_B16:
+        cache = torch.zeros(lib.index_keys_b16_size(B, Nc_max), dtype=torch.uint8, device="cuda")
+    elif out_dtype == "fp8":
+        cache = torch.zeros(B, Nc_max, c, dtype=torch.uint8, device="cuda")
+    else:
+        cache = torch.zeros(B, Nc_max, c, dtype=torch.bfloat16, device="cuda")
+    scale = torch.zeros(B, Nc_max, device="cuda") if out_dtype == "fp8" else None
+    W = dev_bf16(np.ascontiguousarray(a["W_bf16"].T))
+    bias = dev(a["bias"])
+    common = dict(overlap=kw["overlap"], m=m, c=c, d_rope=kw["d_rope"], rope_theta=kw["rope_theta"],
+                  rms_eps=kw["rms_eps"], online=online, cache_scale=scale, layout=layout, Nc_max=Nc_max)
+    starts = np.asarray(starts, np.int64)
+    if prime is not None:
+        for r in range(m):
+            lib.csa_compress_decode(dev_bf16(np.ascontiguousarray(prime[:, r])), W, bias, dev(starts - m + r), state,
+                                    cache, emit=False, **common)
+    for s in range(T):
+        lib.csa_compress_decode(dev_bf16(np.ascontiguousarray(a["hidden_bf16"][:, s])), W, bias, dev(starts + s),
+                                state, cache, **common)
+    torch.cuda.synchronize()
+    return cache, scale
+
+
+def _oracle(a, kw, b, start, online=False, prime=None):
+    return O.decode_compress(bf16_f64(a["hidden_bf16"][b]), bf16_f64(a["W_bf16"]), a["bias"], p0=start,
+                             hidden_prev=None if prime is None else bf16_f64(prime[b]), online=online, **kw)
+
+
+@pytest.mark.parametrize("c,T,starts", [(512, 24, [0, 8, 40]), (128, 20, [0, 4, 12])])
+def test_decode_compress_csa_bf16(lib, c, T, starts):
+    m, d, B = 4, 256, 3
+    a = I.compressor_inputs(300 + c, B, T, d, m, c, True, 0.05, False)
+    kw = dict(overlap=True, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    # each sequence starts at a block start; sequences that do not start at 0 have their
+    # previous block primed (emit = 0): the same seeded tokens for all, positions differ
+    prev = I.compressor_inputs(400 + c, B, m, d, m, c, True, 0.05, False)["hidden_bf16"]
+    Nc_max = 40
+    cache, _ = _steps(lib, a, kw, starts, T, Nc_max, "bf16", prime=prev)
+    got = host_bits(cache)
+    for b in range(B):
+        ref = _oracle(a, kw, b, starts[b], prime=prev if starts[b] > 0 else None)
+        assert sorted(ref) == list(range(starts[b] // m, (starts[b] + T) // m))
+        for i, v in ref.items():
+            assert_bf16_within_one_step(got[b, i], v, f"decode entry {i} of sequence {b}")
+        # rows no step emitted stay untouched
+        untouched = [i for i in range(Nc_max) if i not in ref]
+        assert np.all(got[b, untouched] == 0)
+
+
+def test_decode_compress_indexer_fp8_rows_and_blocks(lib):
+    m, d, B, c, T = 4, 256, 2, 128, 40
+    a = I.compressor_inputs(500, B, T, d, m, c, True, 0.05, False)
+    kw = dict(overlap=True, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    Nc_max = 37                                     # ragged last block of 16
+    rows, sc = _steps(lib, a, kw, [0, 0], T, Nc_max, "fp8")
+    blocks, sc16 = _steps(lib, a, kw, [0, 0], T, Nc_max, "fp8", layout=lib.CSA_LAYOUT_B16)
+    n = T // m
+    codes, scales = rows.cpu().numpy(), sc.cpu().numpy()
+    for b in range(B):
+        ref = _oracle(a, kw, b, 0)
+        v = np.stack([ref[i] for i in range(n)])[None]
+        assert_fp8_rows(codes[b:b + 1, :n], scales[b:b + 1, :n], v, f"decode indexer K, sequence {b}")
+    # the blocked layout holds the same codes: compare with the library's copy of the rows
+    want = lib.csa_index_keys_b16(rows, torch.empty(lib.index_keys_b16_size(B, Nc_max), dtype=torch.uint8,
+                                                    device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(blocks, want), "blocked decode output differs from the blocked copy of its rows"
+    assert torch.equal(sc16, sc), "row scales differ between the layouts"
+
+
+@pytest.mark.parametrize("online", [False, True])
+def test_decode_compress_hca(lib, online):
+    m, d, B, c, T = 128, 256, 2, 512, 256
+    a = I.compressor_inputs(600, B, T, d, m, c, False, 0.05, False)
+    a["bias"] = (a["bias"] * 40.0).astype(np.float32)      # gates far apart: the running max matters
+    kw = dict(overlap=False, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    cache, _ = _steps(lib, a, kw, [0, 0], T, 4, "bf16", online=online)
+    got = host_bits(cache)
+    for b in range(B):
+        ref = _oracle(a, kw, b, 0, online=online)
+        assert sorted(ref) == [0, 1]
+        for i, v in ref.items():
+            assert_bf16_within_one_step(got[b, i], v, f"HCA decode entry {i} ({'online' if online else 'ring'})")
+
+
+def test_decode_compress_fp32_tiny(lib):
+    sh = I.TINY
+    a = I.tiny_inputs()
+    h = a["hidden"][0]                                       # [1024, 256] fp32
+    kw = dict(overlap=True, m=sh.m, c=sh.c, d_rope=sh.d_rope, rope_theta=sh.rope_theta, rms_eps=1e-6)
+    T = 64
+    state = torch.empty(lib.compress_state_size(1, sh.m, sh.c, True), dtype=torch.uint8, device="cuda")
+    cache = torch.zeros(1, T // sh.m, sh.c, device="cuda")
+    W, bias = dev(np.ascontiguousarray(a["W_comp"].T)), dev(a["B_comp"])
+    for s in range(T):
+        lib.csa_compress_decode(dev(h[s:s + 1]), W, bias, dev(np.array([s], np.int64)), state, cache, **kw)
+    torch.cuda.synchronize()
+    ref = O.decode_compress(h[:T], a["W_comp"], a["B_comp"], p0=0, **kw)
+    prefill = O.csa_compress(h[None, :T], a["W_comp"], a["B_comp"], p0=0, **kw)[0]
+    got = cache.cpu().numpy()[0]
+    assert_close(got, np.stack([ref[i] for i in range(T // sh.m)]), TOL_F32, "fp32 decode compressor")
+    assert_close(got, prefill, TOL_F32, "fp32 decode compressor vs the prefill definition")
+
+
+def test_decode_compress_skips(lib):
+    # pos < 0: nothing happens to that sequence; an entry index >= Nc_max: not written
+    m, d, B, c = 4, 256, 2, 128
+    a = I.compressor_inputs(700, B, 8, d, m, c, True, 0.05, False)
+    kw = dict(overlap=True, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    state = torch.empty(lib.compress_state_size(B, m, c, True), dtype=torch.uint8, device="cuda")
+    cache = torch.zeros(B, 1, c, dtype=torch.bfloat16, device="cuda")
+    W, bias = dev_bf16(np.ascontiguousarray(a["W_bf16"].T)), dev(a["bias"])
+    for s in range(8):
+        pos = np.array([-1, s], np.int64)                    # sequence 0 inactive; sequence 1 emits entries 0, 1
+        lib.csa_compress_decode(dev_bf16(np.ascontiguousarray(a["hidden_bf16"][:, s])), W, bias, dev(pos), state,
+                                cache, Nc_max=1, **kw)
+    torch.cuda.synchronize()
+    got = host_bits(cache)
+    assert np.all(got[0] == 0), "an inactive sequence was written"
+    ref = _oracle(a, kw, 1, 0)
+    assert_bf16_within_one_step(got[1, 0], ref[0], "entry 0 of sequence 1")

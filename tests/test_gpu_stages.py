@@ -147,7 +147,8 @@ def test_topk_exact(lib, rows, Nc, k, kind, algo):
 # Stage 4: bf16 attention (CSA sparse and HCA dense)
 # ---------------------------------------------------------------------------------------
 
-def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=None, pass_pos=False):
+def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=None, pass_pos=False, inv_rope_d=0,
+               rope_theta=1e4):
     Ls = S + W - 1
     a = I.attention_inputs(seed, B, S, Nc, Ls)
     if q_pos is None:
@@ -155,15 +156,19 @@ def _attn_case(lib, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, q_pos=Non
     q_f = bf16_f64(a["q_bf16"]); kv_f = bf16_f64(a["kv_comp_bf16"]); swa_f = bf16_f64(a["swa_bf16"])
     out = torch.empty(B, S, 64, 512, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, S, 64, device="cuda")
+    rope = dict(inv_rope_d=inv_rope_d, rope_theta=rope_theta)
     if dense:
         lib.hca_dense_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(q_pos), dev_bf16(a["swa_bf16"]),
-                           dev(a["sink"]), m=m, W=W, out=out, lse=lse)
+                           dev(a["sink"]), m=m, W=W, out=out, lse=lse, **rope)
         o_ref, l_ref = O.dense_attention(q_f, kv_f, q_pos, m, swa_f, a["sink"], 1 / math.sqrt(512), W)
     else:
         idx = I.random_selection(seed, B, S, Nc, k, n_valid)
         lib.csa_sparse_attn(dev_bf16(a["q_bf16"]), dev_bf16(a["kv_comp_bf16"]), dev(idx), dev_bf16(a["swa_bf16"]),
-                            dev(a["sink"]), W=W, out=out, lse=lse, q_pos=dev(q_pos) if pass_pos else None)
+                            dev(a["sink"]), W=W, out=out, lse=lse, q_pos=dev(q_pos) if pass_pos or inv_rope_d else None,
+                            **rope)
         o_ref, l_ref = O.sparse_attention(q_f, kv_f, idx, swa_f, a["sink"], 1 / math.sqrt(512), q_pos, W)
+    if inv_rope_d:
+        o_ref = O.inverse_rope(o_ref, q_pos[..., None], inv_rope_d, rope_theta)
     torch.cuda.synchronize()
     assert_bf16_output(bf16_f64(host_bits(out)), o_ref, "attention output")
     assert_close(lse.cpu().numpy(), l_ref, TOL_F32, "lse")
@@ -237,6 +242,63 @@ def test_hca_dense_attn_prefill_rows(lib):
     S = 24
     q_pos = np.tile(128 * 40 - S + np.arange(S), (1, 1)).astype(np.int64)   # crosses an entry boundary
     _attn_case(lib, B=1, S=S, Nc=64, k=0, W=128, seed=5, n_valid=0, dense=True, q_pos=q_pos)
+
+
+# inverse RoPE of the output, fused with the cast in each place an output is written: the
+# attention kernel itself (one split), the tiled merge (several splits; 64-head and
+# 32-head shapes) and the fp32 path
+@pytest.mark.parametrize("case", ["single_split", "merge_narrow", "merge_wide", "hca_merge"])
+def test_attention_inverse_rope(lib, case):
+    if case == "single_split":
+        _attn_case(lib, B=8, S=64, Nc=600, k=96, W=128, seed=31, n_valid=90, inv_rope_d=64)
+    elif case == "merge_narrow":
+        _attn_case(lib, B=3, S=1, Nc=2000, k=512, W=128, seed=32, n_valid=512, inv_rope_d=64, rope_theta=1.6e5)
+    elif case == "merge_wide":
+        _attn_case(lib, B=64, S=1, Nc=3000, k=1024, W=128, seed=33, n_valid=1024, inv_rope_d=128)
+    else:
+        # 2 queries over 3000 entries: more than four splits (the one-tile merge)
+        q_pos = np.array([[128 * 3000 - 1], [128 * 2000 + 126]], np.int64)
+        _attn_case(lib, B=2, S=1, Nc=3000, k=0, W=128, seed=34, n_valid=0, dense=True, q_pos=q_pos, inv_rope_d=64)
+
+
+def test_attention_inverse_rope_fp32_and_fused(lib):
+    # fp32 kernel (tiny shape) against the oracle
+    rng = np.random.default_rng(35)
+    B, Nc, k, H, c, W = 2, 200, 32, 8, 64, 128
+    q = rng.standard_normal((B, 1, H, c)).astype(np.float32)
+    kv = rng.standard_normal((B, Nc, c)).astype(np.float32)
+    swa = rng.standard_normal((B, W, c)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    idx = np.sort(np.stack([rng.choice(Nc, k, replace=False) for _ in range(B)]), axis=1)[:, None].astype(np.int32)
+    pos = np.array([[1023], [70000]], np.int64)
+    out = torch.empty(B, 1, H, c, device="cuda")
+    lib.csa_sparse_attn(dev(q), dev(kv), dev(idx), dev(swa), dev(sink), W=W, out=out, q_pos=dev(pos), inv_rope_d=16)
+    o_ref, _ = O.sparse_attention(q, kv, idx, swa, sink, 1 / math.sqrt(c), pos, W)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.inverse_rope(o_ref, pos[..., None], 16, 1e4), TOL_F32, "fp32 inverse RoPE")
+    # the fused selection + attention applies the same epilogue as csa_sparse_attn, bit for bit
+    B, Nc, k = 3, 9000, 512
+    t = 4 * Nc - 1
+    a = I.indexer_inputs(36, B, 1, Nc)
+    at = I.attention_inputs(37, B, 1, Nc, W)
+    qpos = dev(np.full((B, 1), t, np.int64))
+    cand = torch.empty(lib.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device="cuda")
+    lib.csa_index_score_segments(dev(a["qI_fp8"]), dev(a["qI_scale"]), dev(a["w"]), dev(a["kI_fp8"]),
+                                 dev(a["kI_scale"]), qpos, m=4, k=k, cand=cand)
+    args = (dev_bf16(at["q_bf16"]), dev_bf16(at["kv_comp_bf16"]))
+    idx_ref = torch.empty(B, 1, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk_merge(cand, B, 1, Nc, k, idx_ref)
+    o1 = torch.empty(B, 1, 64, 512, dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    lib.csa_sparse_attn(*args, idx_ref, dev_bf16(at["swa_bf16"]), dev(at["sink"]), W=W, out=o1, q_pos=qpos,
+                        inv_rope_d=64)
+    lib.csa_topk_sparse_attn(*args, cand, dev_bf16(at["swa_bf16"]), dev(at["sink"]), k=k, W=W, out=o2, q_pos=qpos,
+                             inv_rope_d=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "fused selection + attention: inverse RoPE epilogue differs"
+    o_ref, _ = O.sparse_attention(bf16_f64(at["q_bf16"]), bf16_f64(at["kv_comp_bf16"]), idx_ref.cpu().numpy(),
+                                  bf16_f64(at["swa_bf16"]), at["sink"], 1 / math.sqrt(512), np.full((B, 1), t), W)
+    assert_bf16_output(bf16_f64(host_bits(o2)), O.inverse_rope(o_ref, t, 64, 1e4), "fused attention, inverse RoPE")
 
 
 def test_attention_sink_only_limit(lib):
