@@ -1,22 +1,23 @@
-"""Throughput of the CSA decode hot path on one MI355X (plus the prefill indexer).
+"""Throughput of the CSA decode hot path on one MI355X (plus the prefill stages).
 
 One step = one CSA decode step of the V4-Flash-shaped workload (batch 32, 128K
 context, 32768 compressed entries per sequence, 64 indexer heads x 128 FP8, top-512,
-64 query heads x 512 bf16, 128-token window, per-head sink): lightning-indexer scores
--> top-k -> sparse shared-KV attention, all through the C ABI.  Inputs are resident in
-HBM before timing; the step rotates over several independent input sets (together
-larger than the 256 MB Infinity Cache) so the indexer keys stream from HBM.
+64 query heads x 512 bf16, 128-token window, per-head sink): lightning-indexer scores with
+each 4096-entry segment's top-k (keys in the 16-entry blocked layout the decode-time
+compressor appends to), then the selection of each query's top-k and the sparse
+attention in one call.  Inputs are resident in HBM before timing; the step rotates over
+several independent input sets (together larger than the 256 MB Infinity Cache) so the
+indexer keys stream from HBM.
 
-`value` times K eagerly launched steps (one library call per stage);
-`ms_per_step_graph` times the same K steps replayed from HIP graphs captured once per
-input set (torch.cuda.CUDAGraph).
+`value` times K eagerly launched steps; `ms_per_step_graph` the same K steps replayed
+from HIP graphs.  `roofline` is for the dominant kernel (the scoring pass), its duration
+timed with HIP events around each of its launches inside K more steps, on its stream.
+`decode_layer` adds the decode-time compressor (main KV + indexer key append for the new
+token) and the inverse-RoPE epilogue: the whole CSA layer step after the dense
+projections.  `cpu_baseline` is the CPU oracle on a bounded sample of the same workload.
 
-Prints one JSON line (see the keys below).  `roofline` is for the dominant kernel
-(the indexer), timed with HIP events on the stream it runs on.  `cpu_baseline` is the
-CPU oracle on a bounded sample of the same workload.  `prefill_indexer` times the
-indexer over a prefill chunk (8192 queries x 34816 entries) against the matrix peaks.
-
-    python bench.py [--steps K] [--warmup W] [--sets N] [--eager] [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--steps K] [--warmup W] [--sets N] [--eager] [--no-cpu-baseline]
+                    [--subs prefill,pro,hca,compressor,prefill_attention,decode_layer]
 """
 
 from __future__ import annotations
@@ -36,6 +37,8 @@ METRIC = "CSA decode tokens/s + HBM GB/s @128K ctx; prefill indexer TFLOPS (% ro
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA
+ALL_SUBS = ("prefill", "pro", "hca", "compressor", "prefill_attention", "decode_layer")
+ROOFLINE_KERNEL = "index_score_fp8_decode<true, true>"
 
 
 def parse():
@@ -45,8 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--no-other", action="store_true", help="skip the Pro / HCA decode and compressor lines")
+    p.add_argument("--subs", default=",".join(ALL_SUBS),
+                   help="comma-separated sub-benchmarks to run (empty: none): " + ",".join(ALL_SUBS))
     p.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one 256 MiB device copy (reference kernel for HBM byte counters)")
@@ -54,7 +57,10 @@ def parse():
                    help="write the prefill indexer's MFMA counter summary into profiles/")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) made "
-                        "with --calibrate-copy into the committed traffic summary")
+                        "with --calibrate-copy into the committed traffic summaries")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                   help="no GPU work: turn a rocprofv3 --kernel-trace --stats run of the default bench into "
+                        "the committed kernel-trace summary")
     return p.parse_args()
 
 
@@ -87,59 +93,195 @@ def decode_step_bytes(sh):
 COPY_BYTES = 256 << 20
 
 
-def summarize_counters(fetch_dir, write_dir, cmd_fetch, cmd_write):
-    """Writes profiles/index_score_segments_flash_decode_b32_traffic.txt from the counter
-    CSVs: each counter of the indexer is scaled by what the same counter reads for the
-    plain device copy of COPY_BYTES (read and written once)."""
+# Kernels whose HBM traffic the counter runs summarise: (summary name, kernel name, total
+# work-items of the dispatches meant (None: every dispatch), sources compiled into it,
+# algorithmic bytes per launch, what those bytes are).  The counter runs use
+# COUNTER_BENCH_ARGS: the default step (Flash decode, B = 32) and the HCA sub-benchmark.
+ATTN_SOURCES = ("attention.hip", "attention_common.hpp", "select.hpp", "common.hpp")
+
+
+def counter_kernels():
+    from synthetic import inputs as I
+    f, h = I.FLASH_DECODE, I.HCA_DECODE
+    fl_rows = f.B * ((f.W + f.k) * f.c * 2 + f.H * f.c * 2 + -(-f.n_c // SEGMENT) * f.k * 8)
+    hca_rows = h.B * ((h.W + h.n_c) * h.c * 2 + h.H * h.c * 2)
+    return [
+        ("index_score_segments_flash_decode_b32", ROOFLINE_KERNEL, None, INDEXER_SOURCES,
+         index_segments_bytes(f.B, 1, f.n_c, f.H_I, f.d_I, f.k),
+         "keys + scales (132 B per entry), q codes + scales + w, positions, 8 x 512 candidate pairs per query"),
+        ("attn_select_flash_decode_b32", "attn_bf16<2, 4, 8>", None, ATTN_SOURCES, fl_rows,
+         "candidate pairs, window + selected rows (1 KiB each), q (the split partials it writes are not counted)"),
+        ("attn_merge_flash_decode_b32", "attn_merge_tiles<4>", 32 * 8 * 8 * 256, ATTN_SOURCES,
+         f.B * f.H * f.c * 2, "the bf16 output (the split partials it reads are not counted)"),
+        ("attn_hca_decode_b64", "attn_bf16<1, 2, 8>", None, ATTN_SOURCES, hca_rows,
+         "window + every visible entry (1 KiB each), q (the split partials it writes are not counted)"),
+    ]
+
+
+COUNTER_BENCH_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy --eager --subs hca"
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """Writes profiles/<name>_traffic.txt for every kernel of counter_kernels() from the two
+    counter runs: each counter is scaled by what it reads for the plain device copy of
+    COPY_BYTES (read and written once) in the same run."""
     import csv
     import glob
 
-    def per_kernel(d, counter):
-        vals = {}
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] != counter:
-                    continue
-                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+    def rows_of(d, counter):
+        out = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(fn)):
+                if r["Counter_Name"] == counter:
+                    out.append(r)
+        return out
 
-    def pick(vals, key):
-        rows = [v for k, v in vals.items() if key in k]
-        if not rows:
-            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
-        return rows[0]
+    def pick(rows, key, grid=None):
+        v = [float(r["Counter_Value"]) for r in rows
+             if key in r["Kernel_Name"] and (grid is None or int(float(r.get("Grid_Size", -1))) == grid)]
+        if not v:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r} (grid {grid})")
+        return v
 
-    fv, wv = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
-    copy_f = max(pick(fv, "copyBuffer"))            # KiB, the one large copy
-    copy_w = max(pick(wv, "copyBuffer"))
-    f_scale = COPY_BYTES / (copy_f * 1024.0)
-    w_scale = COPY_BYTES / (copy_w * 1024.0)
-    idx_f = pick(fv, "index_score_fp8_decode<true, true>")
-    idx_w = pick(wv, "index_score_fp8_decode<true, true>")
-    fetch = sum(idx_f) / len(idx_f) * 1024.0 * f_scale
-    write = sum(idx_w) / len(idx_w) * 1024.0 * w_scale
-    sha = sources_sha256(INDEXER_SOURCES)
-    out = os.path.join(ROOT, "profiles", "index_score_segments_flash_decode_b32_traffic.txt")
+    fr, wr = rows_of(fetch_dir, "FETCH_SIZE"), rows_of(write_dir, "WRITE_SIZE")
+    copy_f, copy_w = max(pick(fr, "copyBuffer")), max(pick(wr, "copyBuffer"))      # KiB, the one large copy
+    f_scale, w_scale = COPY_BYTES / (copy_f * 1024.0), COPY_BYTES / (copy_w * 1024.0)
+    base = "cd /tmp && rocprofv3 --pmc {} --output-format csv -d <dir> -o run -- python3 <repo>/bench.py " + \
+        COUNTER_BENCH_ARGS
+    for name, kern, grid, sources, alg, what in counter_kernels():
+        kf, kw = pick(fr, kern, grid), pick(wr, kern, grid)
+        fetch = sum(kf) / len(kf) * 1024.0 * f_scale
+        write = sum(kw) / len(kw) * 1024.0 * w_scale
+        out = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+        with open(out, "w") as fo:
+            fo.write(f"# HBM traffic of {kern} ({name}), from rocprofv3 counters; each counter scaled by\n")
+            fo.write("# its reading for a plain 256 MiB device copy in the same run.\n")
+            fo.write(f"# fetch run: {base.format('FETCH_SIZE')}\n# write run: {base.format('WRITE_SIZE')}\n")
+            if grid is not None:
+                fo.write(f"# dispatches of {grid} work-items only\n")
+            fo.write(f"copy_fetch_kib = {copy_f:.1f}\ncopy_write_kib = {copy_w:.1f}\n")
+            fo.write(f"fetch_scale = {f_scale:.4f}\nwrite_scale = {w_scale:.4f}\n")
+            fo.write(f"fetch_kib_per_dispatch = {sum(kf) / len(kf):.1f}  (n={len(kf)})\n")
+            fo.write(f"write_kib_per_dispatch = {sum(kw) / len(kw):.1f}  (n={len(kw)})\n")
+            fo.write(f"traffic_fetch_bytes = {fetch:.0f}\ntraffic_write_bytes = {write:.0f}\n")
+            fo.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
+            fo.write(f"algorithmic_bytes_per_launch = {alg}  ({what})\n")
+            fo.write(f"traffic_over_algorithmic = {(fetch + write) / alg:.3f}\n")
+            fo.write(f"sources = {' + '.join(sources)}\n")
+            fo.write(f"sources_sha256 = {sources_sha256(sources)}\n")
+        print(open(out).read())
+
+
+TRACE_CMD = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+             "python3 <repo>/bench.py")
+
+
+def summarize_trace(trace_dir, bench_log):
+    """Writes profiles/decode_flash_b32_ctx128k_kernel_stats.txt from a kernel trace of the
+    default bench command: per-kernel statistics over the whole run (as --stats gives them)
+    and, for the roofline kernel, its dispatches split by the phase of the run they belong
+    to (the bench line's dispatch_plan), so that the bench's event-timed duration and frac
+    can be checked against the trace's own durations of the same launches."""
+    import csv
+    import glob
+    rows = []
+    for fn in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    if not rows:
+        raise SystemExit("no kernel_trace.csv under " + trace_dir)
+    rows.sort()
+    line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
+    res = json.loads(line)
+    stats = {}
+    for t0, t1, name in rows:
+        short = name.split("(")[0].replace("void ", "")
+        stats.setdefault(short, []).append((t1 - t0) / 1e3)
+    total = sum(sum(v) for v in stats.values())
+    rl = [(t1 - t0) / 1e3 for t0, t1, name in rows if ROOFLINE_KERNEL in name]
+    plan = res["roofline"]["dispatch_plan"]
+    out = os.path.join(ROOT, "profiles", "decode_flash_b32_ctx128k_kernel_stats.txt")
     with open(out, "w") as fo:
-        fo.write("# HBM traffic of index_score_fp8_decode<true, true> (csa_index_score_segments_b16), V4-Flash decode\n")
-        fo.write("# (B=32, 32768 entries, k=512, scores kept on chip), from\n")
-        fo.write("# rocprofv3 counters; each counter scaled by its reading for a plain 256 MiB device copy.\n")
-        fo.write(f"# fetch run: {cmd_fetch}\n# write run: {cmd_write}\n")
-        fo.write(f"copy_fetch_kib = {copy_f:.1f}\ncopy_write_kib = {copy_w:.1f}\n")
-        fo.write(f"fetch_scale = {f_scale:.4f}\nwrite_scale = {w_scale:.4f}\n")
-        fo.write(f"index_fetch_kib_per_dispatch = {sum(idx_f) / len(idx_f):.1f}  (n={len(idx_f)})\n")
-        fo.write(f"index_write_kib_per_dispatch = {sum(idx_w) / len(idx_w):.1f}  (n={len(idx_w)})\n")
-        fo.write(f"traffic_fetch_bytes = {fetch:.0f}\ntraffic_write_bytes = {write:.0f}\n")
-        fo.write(f"traffic_bytes_per_launch = {fetch + write:.0f}\n")
-        fo.write(f"algorithmic_bytes_per_launch = {index_segments_bytes(32, 1, 32768, 64, 128, 512)}\n")
-        fo.write(f"sources = {' + '.join(INDEXER_SOURCES)}\n")
-        fo.write(f"sources_sha256 = {sha}\n")
+        fo.write("# rocprofv3 kernel trace of the default bench run on one MI355X\n")
+        fo.write(f"# command: {TRACE_CMD}\n")
+        fo.write("# workload: V4-Flash CSA decode step, B=32, 128K context (32768 entries), top-512, H=64 x c=512;\n")
+        fo.write(f"#   the timed step = {res['timing']}\n")
+        fo.write(f"# bench line of this run (under the tracer): value={res['value']:.0f} tokens/s, "
+                 f"ms_per_step={res['ms_per_step']:.4f}, roofline kernel avg_launch_us={res['roofline']['avg_launch_us']:.2f} "
+                 f"(in-step, events), frac={res['roofline']['frac']:.3f}\n")
+        fo.write(f"\n# {ROOFLINE_KERNEL}: the trace's durations of the same launches, by phase of the run\n")
+        i = 0
+        for phase, n in plan:
+            seg = rl[i:i + n]
+            i += n
+            if seg:
+                fo.write(f"phase {phase:<14} dispatches {len(seg):4d}  avg_us {np.mean(seg):8.2f}  "
+                         f"min_us {np.min(seg):8.2f}  max_us {np.max(seg):8.2f}\n")
+        if i != len(rl):
+            fo.write(f"# note: {len(rl)} dispatches in the trace, {i} in the plan\n")
+        ev = dict(plan)
+        j = 0
+        for phase, n in plan:
+            if phase == "event_pass":
+                seg = rl[j:j + n]
+                tr_us = float(np.mean(seg))
+                fo.write(f"event_pass_trace_avg_us = {tr_us:.2f}\n")
+                fo.write(f"event_pass_bench_us = {res['roofline']['avg_launch_us']:.2f}  (the bench's events around the "
+                         f"same launches)\n")
+                fo.write(f"bytes_per_launch = {res['roofline']['bytes_per_launch']}\n")
+                fo.write(f"frac_from_trace = {res['roofline']['bytes_per_launch'] / (tr_us * 1e-6) / 1e9 / HBM_PEAK_GBS:.3f}\n")
+            j += n
+        fo.write("\n# every kernel of the run\n")
+        fo.write(f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>7}\n")
+        for name, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+            fo.write(f"{name[:60]:<60} {len(v):6d} {np.mean(v):10.2f} {np.min(v):10.2f} {np.max(v):10.2f} "
+                     f"{100 * sum(v) / total:7.2f}\n")
     print(open(out).read())
 
 
 MFMA_CMD = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
             "--kernel-include-regex index_score_fp8_prefill --output-format csv -d <dir> -o run -- "
             "python3 bench.py --steps 2 --warmup 1 --no-other --no-cpu-baseline --eager")
+
+
+class TimingEvents:
+    """HIP events created with hipEventDisableSystemFence, recorded on a torch stream through
+    the HIP runtime torch has loaded (measurement plumbing: a default event's record adds a
+    system-scope release, whose cache write-back lands inside the interval it times)."""
+    FLAGS = 0x20000000                       # hipEventDisableSystemFence
+
+    def __init__(self, n):
+        import ctypes
+        path = None
+        for ln in open("/proc/self/maps"):
+            if "libamdhip64" in ln:
+                path = ln.split()[-1]
+                break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.FLAGS)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i, stream):
+        if self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i, j):
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 def device_info(torch, dev):
@@ -210,14 +352,19 @@ def main():
         summarize_mfma(*args.summarize_mfma)
         return
     if args.summarize_counters:
-        base = "rocprofv3 --pmc {} --output-format csv -d <dir> -o run -- python3 bench.py --steps 5 --warmup 2 " \
-               "--no-prefill --no-other --no-cpu-baseline --calibrate-copy"
-        summarize_counters(*args.summarize_counters, base.format("FETCH_SIZE"), base.format("WRITE_SIZE"))
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the CSA hot path here runs on one GPU; sharding over several GPUs "
                                    "is not launched", "n_gpus": args.gpus}))
         sys.exit(2)
+    subs = [x for x in args.subs.split(",") if x]
+    for x in subs:
+        if x not in ALL_SUBS:
+            raise SystemExit(f"unknown sub-benchmark {x!r}; choose from {','.join(ALL_SUBS)}")
     import torch
     from compressed_sparse_kv_amd import binding as L
     from synthetic import inputs as I
@@ -249,13 +396,14 @@ def main():
     idx = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
     out = torch.empty(B, 1, sh.H, sh.c, dtype=torch.bfloat16, device=dev)
     tk_ws = torch.empty(L.topk_workspace_size(B, Nc, k), dtype=torch.uint8, device=dev)
-    it_ws = torch.empty(L.index_topk_workspace_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
     at_ws_n = L.attn_workspace_size(B, 1, sh.H, sh.c, sh.W + k, L.CSA_BF16)
     at_ws = torch.empty(max(at_ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     cand = torch.empty(L.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
-    # the key cache in 16-entry blocks, made once per input set (a cache update, not a step)
+    # Each set's key cache in the 16-entry blocked layout.  A decode loop builds it entry by
+    # entry with csa_compress_decode (layout CSA_LAYOUT_B16), which writes the same bytes
+    # (tested); here the precompressed cache is laid out once per set before timing.
     for s in sets:
         s["k16"] = L.csa_index_keys_b16(s["k8"], torch.empty(L.index_keys_b16_size(B, Nc), dtype=torch.uint8,
                                                              device=dev))
@@ -297,15 +445,17 @@ def main():
         L.csa_topk(scores, k, idx, ws=tk_ws)
         ev[6].record(stream)
 
+    plan = []                                   # launches of the roofline kernel, by phase, in order
     for i in range(args.warmup):
         step(i)
+    plan.append(("warmup", args.warmup))
     torch.cuda.synchronize()
     if args.calibrate_copy:
-        a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        b.copy_(a)
+        a_ = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        b_ = torch.empty_like(a_)
+        b_.copy_(a_)
         torch.cuda.synchronize()
-        del a, b
+        del a_, b_
     # eager: exactly K steps between two synchronisations, one library call per stage
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -316,6 +466,7 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_eager = t0.elapsed_time(t1) / args.steps
+    plan.append(("timed", args.steps))
 
     # the same step through csa_index_score + csa_topk (informational; not `value`)
     for i in range(args.warmup):
@@ -347,7 +498,24 @@ def main():
         t1.record(stream)
         torch.cuda.synchronize()
         ms_graph = t0.elapsed_time(t1) / args.steps
+        plan.append(("graph", len(sets) + args.steps))
     ms_per_step = ms_eager
+
+    # the dominant kernel inside the step: K more steps with a pair of timing events around
+    # each of its launches, on its stream.  The events skip the system-scope fence a default
+    # event adds when it is recorded (a cache write-back that would be timed with the kernel).
+    hev = TimingEvents(2 * args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        hev.record(2 * i, stream)
+        score_segments(s)
+        hev.record(2 * i + 1, stream)
+        L.csa_topk_sparse_attn(s["q"], s["kv"], cand, s["swa"], s["sink"], k=k, W=sh.W, out=out, ws=at_ws)
+    torch.cuda.synchronize()
+    is_us = float(np.mean([hev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)])) * 1e3
+    hev.destroy()
+    plan.append(("event_pass", args.steps))
 
     # per-stage durations (separate pass with events between the stages)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
@@ -356,9 +524,10 @@ def main():
     torch.cuda.synchronize()
     dur = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(6)] for e in evs])
     us = dur.mean(axis=0) * 1e3
+    plan.append(("stage_pass", args.steps))
 
-    # dominant kernel alone: back-to-back launches (rotating input sets) between two
-    # events on its stream, so the average matches a kernel trace of the same run
+    # the dominant kernel alone, back to back (rotating input sets): no attention between
+    # its launches, so the chip runs it at the clock a continuous stream of it allows
     n_rl = max(args.steps, 20)
     r0 = torch.cuda.Event(enable_timing=True)
     r1 = torch.cuda.Event(enable_timing=True)
@@ -368,7 +537,8 @@ def main():
         score_segments(sets[i % len(sets)])
     r1.record(stream)
     torch.cuda.synchronize()
-    is_us = r0.elapsed_time(r1) / n_rl * 1e3
+    b2b_us = r0.elapsed_time(r1) / n_rl * 1e3
+    plan.append(("back_to_back", n_rl))
 
     isb = index_segments_bytes(B, 1, Nc, sh.H_I, sh.d_I, k)
     achieved = isb / (is_us * 1e-6) / 1e9
@@ -394,26 +564,37 @@ def main():
                    "indexer_dim": sh.d_I, "window": sh.W, "input_sets": args.sets},
         "hbm_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "step_bytes": step_bytes,
+        "step_frac_hbm_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "stages_us": {"csa_index_score_segments": us[0], "csa_topk_sparse_attn": us[1], "csa_topk_merge": us[2],
                       "csa_sparse_attn": us[3], "csa_index_score": us[4], "csa_topk": us[5]},
-        "roofline": {"kernel": "index_score_fp8_decode<true, true>", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": ROOFLINE_KERNEL, "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(INDEXER_SOURCES, "index_score_segments_flash_decode_b32"),
                      "bytes_per_launch": isb, "avg_launch_us": is_us,
-                     "traffic": measured_traffic(INDEXER_SOURCES, "index_score_segments")},
+                     "timing": "HIP events (no system-scope fence) around each launch inside K steps, on its stream",
+                     "avg_launch_us_back_to_back": b2b_us,
+                     "frac_back_to_back": isb / (b2b_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                     "dispatch_plan": plan},
         "input_generation_s": t_gen,
         # (not under --calibrate-copy: its copy must stay the only large one of a counter run)
         "device": None if args.calibrate_copy else device_info(torch, dev),
     }
 
-    if not args.no_prefill:
+    if "prefill" in subs:
         result["prefill_indexer"], pf_scores = bench_prefill_indexer(torch, L, I, dev)
         result["prefill_topk"] = bench_prefill_topk(torch, L, pf_scores, I.PREFILL.k)
         del pf_scores
-    if not args.no_other:
+    if "pro" in subs:
         result["pro_decode"] = bench_csa_decode(torch, L, I, dev, I.PRO_DECODE, n_sets=2)
+    if "hca" in subs:
         result["hca_decode"] = bench_hca_decode(torch, L, I, dev)
+    if "compressor" in subs:
         result["prefill_compressor"] = bench_prefill_compressor(torch, L, I, dev)
+    if "prefill_attention" in subs:
         result["prefill_attention"] = bench_prefill_attention(torch, L, I, dev)
+    if "decode_layer" in subs:
+        result["decode_layer"] = bench_decode_layer(torch, L, I, dev, sets, cand, at_ws)
+        plan.append(("decode_layer", 21))
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(host_sets, sh)
@@ -433,11 +614,11 @@ def sources_sha256(names):
     return h.hexdigest()
 
 
-def measured_traffic(sources, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None when a
-    source of the kernel has changed since the counters were taken (the summary records
-    the sha256 of the sources it measured)."""
-    summary = os.path.join(ROOT, "profiles", f"{kernel}_flash_decode_b32_traffic.txt")
+def measured_traffic(sources, name):
+    """HBM bytes per launch from the committed counter summary profiles/<name>_traffic.txt, or
+    None when a source of the kernel has changed since the counters were taken (the summary
+    records the sha256 of the sources it measured)."""
+    summary = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
     if not os.path.exists(summary):
         return None
     fields = {}
@@ -625,33 +806,121 @@ def bench_prefill_topk(torch, L, scores, k, reps=5):
             "bytes": byts, "hbm_gbs": byts / (ms * 1e-3) / 1e9, "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def bench_decode_layer(torch, L, I, dev, sets, cand, at_ws, reps=20):
+    """The whole CSA decode layer step after the dense projections (V4-Flash shapes, hidden
+    d = 5120): the new token's compressor step for the main KV (bf16 rows into the KV
+    cache) and for the indexer key (FP8 appended straight into the 16-entry blocked key
+    cache), the scores with each segment's top-k, and the selection + sparse attention with
+    the inverse-RoPE epilogue.  Position t = 131071 completes block 32767, so every step
+    emits one entry into each cache (entry 32767, which the query sees)."""
+    sh = I.FLASH_DECODE
+    B, Nc, k, m, c, dI, W = sh.B, sh.n_c, sh.k, sh.m, sh.c, sh.d_I, sh.W
+    d = I.PREFILL.d
+    a = I.decode_layer_inputs(sh.seed + 900, B, d, m, c, dI)
+    upb = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    hid, prime = upb(a["hidden_bf16"]), upb(a["prime_bf16"])
+    Wm, Bm, Wi, Bi = upb(a["W_main_t_bf16"]), up(a["B_main"]), upb(a["W_idx_t_bf16"]), up(a["B_idx"])
+    st_m = [torch.empty(L.compress_state_size(B, m, c, True), dtype=torch.uint8, device=dev) for _ in sets]
+    st_i = [torch.empty(L.compress_state_size(B, m, dI, True), dtype=torch.uint8, device=dev) for _ in sets]
+    ws_m = torch.empty(L.compress_decode_workspace_size(B, d, c, True), dtype=torch.uint8, device=dev)
+    ws_i = torch.empty(L.compress_decode_workspace_size(B, d, dI, True), dtype=torch.uint8, device=dev)
+    kw = dict(overlap=True, m=m, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    t = sh.t
+    pos_t = torch.full((B,), t, dtype=torch.int64, device=dev)
+
+    def compress(si, h, pos, emit=True):
+        s = sets[si]
+        L.csa_compress_decode(h, Wm, Bm, pos, st_m[si], s["kv"], c=c, emit=emit, ws=ws_m, **kw)
+        L.csa_compress_decode(h, Wi, Bi, pos, st_i[si], s["k16"], c=dI, cache_scale=s["ks"],
+                              layout=L.CSA_LAYOUT_B16, Nc_max=Nc, emit=emit, ws=ws_i, **kw)
+
+    # each set's rings hold the previous block and the first 2m - 1 - m tokens of this one
+    for si in range(len(sets)):
+        for r in range(2 * m - 1):
+            compress(si, prime[:, r].contiguous(), torch.full((B,), t - (2 * m - 1) + r, dtype=torch.int64,
+                                                               device=dev), emit=False)
+    torch.cuda.synchronize()
+
+    out = torch.empty_like(sets[0]["q"])
+
+    def step(i):
+        si = i % len(sets)
+        s = sets[si]
+        compress(si, hid, pos_t)
+        L.csa_index_score_segments_b16(s["q8"], s["qs"], s["w"], s["k16"], s["ks"], s["pos"], m=m, k=k, cand=cand)
+        L.csa_topk_sparse_attn(s["q"], s["kv"], cand, s["swa"], s["sink"], k=k, W=W, out=out, q_pos=s["pos"],
+                               inv_rope_d=64, ws=at_ws)
+
+    ms = _timed(torch, step, reps)
+    ms_c = _timed(torch, lambda i: compress(i % len(sets), hid, pos_t), reps)
+    w_bytes = (4 * c + 4 * dI) * d * 2
+    ring = B * (2 * m * 2 * c + 2 * c + 2 * m * 2 * dI + 2 * dI) * 4     # the 2m slots read, the new one written
+    comp_bytes = w_bytes + 2 * B * d * 2 + ring + B * (c * 2 + dI + 4)
+    byts = decode_step_bytes(sh) + comp_bytes
+    return {"workload": "v4flash_csa_decode_layer_b32_ctx128k_d5120",
+            "steps": "csa_compress_decode (main, bf16 rows) + csa_compress_decode (indexer, FP8, blocked layout) + "
+                     "csa_index_score_segments_b16 + csa_topk_sparse_attn (inverse RoPE 64)",
+            "tokens_per_s": B / (ms * 1e-3), "ms_per_step": ms, "step_bytes": byts,
+            "hbm_gbs": byts / (ms * 1e-3) / 1e9, "frac_hbm_peak": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "compressor_us": ms_c * 1e3, "compressor_bytes": comp_bytes,
+            "compressor_hbm_gbs": comp_bytes / (ms_c * 1e-3) / 1e9}
+
+
 def cpu_baseline(host_sets, sh):
-    """The CPU oracle, as it stands, on every query of the rotated input sets."""
+    """The CPU oracle, as it stands, on every query of the rotated input sets (all host
+    cores), and on 8 of them with one thread."""
     import math
+    import platform
     from oracle import csa_oracle as O
+
+    def one(a, b):
+        qI = O.dequant_rows(a["qI_fp8"][b:b + 1], a["qI_scale"][b:b + 1])
+        KI = O.dequant_rows(a["kI_fp8"][b:b + 1], a["kI_scale"][b:b + 1])
+        sc = O.index_scores(qI, a["w"][b:b + 1], KI, a["q_pos"][b:b + 1], sh.m)
+        idx = O.topk_indices(sc, sh.k)
+        O.sparse_attention(O.bf16_bits_to_f64(a["q_bf16"][b:b + 1]), O.bf16_bits_to_f64(a["kv_comp_bf16"][b:b + 1]),
+                           idx, O.bf16_bits_to_f64(a["swa_bf16"][b:b + 1]), a["sink"], 1 / math.sqrt(sh.c),
+                           a["q_pos"][b:b + 1], sh.W)
+
+    threads = None
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count()
+        threadpool_limits = None
     t = time.time()
     nq = 0
     for a in host_sets:
-        qI = O.dequant_rows(a["qI_fp8"], a["qI_scale"])
         for b in range(sh.B):
-            KI = O.dequant_rows(a["kI_fp8"][b:b + 1], a["kI_scale"][b:b + 1])
-            sc = O.index_scores(qI[b:b + 1], a["w"][b:b + 1], KI, a["q_pos"][b:b + 1], sh.m)
-            idx = O.topk_indices(sc, sh.k)
-            O.sparse_attention(O.bf16_bits_to_f64(a["q_bf16"][b:b + 1]),
-                               O.bf16_bits_to_f64(a["kv_comp_bf16"][b:b + 1]), idx,
-                               O.bf16_bits_to_f64(a["swa_bf16"][b:b + 1]), a["sink"], 1 / math.sqrt(sh.c),
-                               a["q_pos"][b:b + 1], sh.W)
+            one(a, b)
             nq += 1
     el = time.time() - t
-    return {"value": nq / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nq} decode queries ({len(host_sets)} input sets x batch {sh.B}): "
-                      f"scores over {sh.n_c} entries, top-{sh.k}, attention over {sh.k}+{sh.W} rows; "
-                      f"{el:.1f} s"}
+    res = {"value": nq / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{nq} decode queries ({len(host_sets)} input sets x batch {sh.B}): "
+                     f"scores over {sh.n_c} entries, top-{sh.k}, attention over {sh.k}+{sh.W} rows; {el:.1f} s"}
+    try:
+        res["nproc"] = len(os.sched_getaffinity(0))
+    except Exception:
+        res["nproc"] = os.cpu_count()
+    model = platform.processor()
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except Exception:
+        pass
+    res["cpu_model"] = model
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t = time.time()
+            for b in range(8):
+                one(host_sets[0], b)
+            el1 = time.time() - t
+        res["value_1thread"] = 8 / el1
+        res["sample_1thread"] = f"8 decode queries of input set 0 with one BLAS thread: {el1:.1f} s"
+    return res
 
 
 if __name__ == "__main__":

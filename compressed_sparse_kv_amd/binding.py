@@ -55,7 +55,7 @@ def _load() -> ctypes.CDLL:
         "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
         "csa_compress_state_size": ([i, i, i, i, i], sz),
-        "csa_compress_decode_workspace_size": ([i, i, i], sz),
+        "csa_compress_decode_workspace_size": ([i, i, i, i, i], sz),
         "csa_compress_decode": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i, vp, vp, vp, i, i, i, vp, sz, vp], i),
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
         "csa_index_topk_workspace_size": ([i, i, i, i], sz),
@@ -158,8 +158,8 @@ def compress_state_size(B, m, c, overlap, online=False) -> int:
     return int(_lib.csa_compress_state_size(B, m, c, int(overlap), int(online)))
 
 
-def compress_decode_workspace_size(B, c, overlap) -> int:
-    return int(_lib.csa_compress_decode_workspace_size(B, c, int(overlap)))
+def compress_decode_workspace_size(B, d, c, overlap, in_dtype=CSA_BF16) -> int:
+    return int(_lib.csa_compress_decode_workspace_size(B, d, c, int(overlap), int(in_dtype)))
 
 
 def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: bool, m: int, c: int, d_rope: int,
@@ -177,7 +177,7 @@ def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: boo
         Nc_max = cache.shape[1]
     if state.numel() * state.element_size() < compress_state_size(B, m, c, overlap, online):
         raise ValueError("state smaller than compress_state_size")
-    ws, wsb = _ws(compress_decode_workspace_size(B, c, overlap), ws, hidden.device)
+    ws, wsb = _ws(compress_decode_workspace_size(B, d, c, overlap, _dtype(hidden)), ws, hidden.device)
     out_dt = CSA_FP8_E4M3 if layout == CSA_LAYOUT_B16 else _dtype(cache)
     _check("csa_compress_decode", _lib.csa_compress_decode(
         _p(hidden), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), int(online), B, d, m, c, d_rope,

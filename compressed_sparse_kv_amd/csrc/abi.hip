@@ -20,7 +20,7 @@ int launch_compress(const void*, const void*, int, const void*, const float*, in
                     float, float, int64_t, void*, float*, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
 size_t compress_state_bytes(int, int, int, int, int);
-size_t compress_decode_workspace_bytes(int, int, int);
+size_t compress_decode_workspace_bytes(int, int, int, int, int);
 int launch_compress_decode(const void*, int, const void*, const float*, int, int, int, int, int, int, int, float,
                            float, const int64_t*, int, float*, void*, float*, int, int, int, void*, hipStream_t);
 bool index_topk_fused_ok(int, int, int);
@@ -101,9 +101,9 @@ size_t csa_compress_state_size(int B, int m, int c, int overlap, int online) {
   return compress_state_bytes(B, m, c, overlap, online);
 }
 
-size_t csa_compress_decode_workspace_size(int B, int c, int overlap) {
-  if (B <= 0 || c <= 0) return 0;
-  return compress_decode_workspace_bytes(B, c, overlap);
+size_t csa_compress_decode_workspace_size(int B, int d, int c, int overlap, int in_dtype) {
+  if (B <= 0 || d <= 0 || c <= 0) return 0;
+  return compress_decode_workspace_bytes(B, d, c, overlap, in_dtype);
 }
 
 int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias, int overlap,
@@ -123,7 +123,7 @@ int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, co
   if (out_layout == CSA_LAYOUT_B16 && (out_dtype != CSA_FP8_E4M3 || c != 128)) return CSA_ERR_UNSUPPORTED;
   if (in_dtype == CSA_BF16 && d % 128 != 0) return CSA_ERR_UNSUPPORTED;
   CSA_REQUIRE(aligned16(ws) && aligned16(state) && aligned16(hidden) && aligned16(w_proj));
-  if (ws == nullptr || ws_bytes < compress_decode_workspace_bytes(B, c, overlap)) return CSA_ERR_WORKSPACE;
+  if (ws == nullptr || ws_bytes < compress_decode_workspace_bytes(B, d, c, overlap, in_dtype)) return CSA_ERR_WORKSPACE;
   return launch_compress_decode(hidden, in_dtype, w_proj, bias, overlap, online, B, d, m, c, d_rope, rope_theta,
                                 rms_eps, pos, emit, state, cache, cache_scale, out_dtype, out_layout, Nc_max, ws,
                                 as_stream(stream));

@@ -468,7 +468,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
       if (a.rope_d > 0 && Sh::kPart * part + 16 * t + 16 > kAC - a.rope_d) {
         const int col = col0 + 16 * t;
         float cs = 1.0f, sn = 0.0f;
-        if (col >= kAC - a.rope_d) rope_cs_sn(col, kAC, a.rope_d, a.rope_theta, tq, cs, sn);
+        if (col >= kAC - a.rope_d) rope_cs_sn(col, kAC, a.rope_d, a.rope_r, tq, cs, sn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
       }
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
                                                         const float* __restrict__ sink, int nsplit, int nq,
                                                         uint16_t* __restrict__ out, float* __restrict__ lse,
                                                         const int64_t* __restrict__ q_pos, int rope_d,
-                                                        float rope_theta) {
+                                                        double rope_r) {
   constexpr int kTiles = kAC / 16;
   constexpr int kBlocksPerQuery = kNHG * kTiles / KT / 4;
   constexpr int kMaxFast = KT == 1 ? 8 : 4;             // splits held in registers at once
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
     if (rope_d > 0 && 16 * (ct0 + t) + 16 > kAC - rope_d) {
       const int col = 16 * (ct0 + t) + (l & 15);
       float cs = 1.0f, sn = 0.0f;
-      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_theta, tq, cs, sn);
+      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_r, tq, cs, sn);
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
     }
@@ -626,13 +626,13 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
 }
 
 // Inverse RoPE of 8 consecutive output channels c0 .. c0+7 (c0 even: they hold whole pairs).
-__device__ __forceinline__ void rope_back8(float (&v)[8], int c0, int c, int d_rope, float theta, int64_t t) {
+__device__ __forceinline__ void rope_back8(float (&v)[8], int c0, int c, int d_rope, double r, int64_t t) {
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
     const int col = c0 + j;
     if (col >= c - d_rope && col + 1 < c) {
       float cs, sn;
-      rope_cs_sn(col, c, d_rope, theta, t, cs, sn);
+      rope_cs_sn(col, c, d_rope, r, t, cs, sn);
       const float x = v[j], y = v[j + 1];
       v[j] = rope_back(x, y, col, cs, sn);
       v[j + 1] = rope_back(y, x, col + 1, cs, sn);
@@ -647,7 +647,7 @@ template <typename OutT>
 __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                   const float* __restrict__ sink, int nsplit, int H, int c, int nqh,
                                                   OutT* __restrict__ out, float* __restrict__ lse,
-                                                  const int64_t* __restrict__ q_pos, int rope_d, float rope_theta) {
+                                                  const int64_t* __restrict__ q_pos, int rope_d, double rope_r) {
   const int qh = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (qh >= nqh) return;
   const int lane = threadIdx.x & 63;
@@ -690,7 +690,7 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
     OutT* dst = out + (qi * H + h) * kAC + 8 * lane;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= inv;
-    if (rope_d > 0) rope_back8(acc, 8 * lane, kAC, rope_d, rope_theta, q_pos[qi]);
+    if (rope_d > 0) rope_back8(acc, 8 * lane, kAC, rope_d, rope_r, q_pos[qi]);
     if constexpr (sizeof(OutT) == 2) {
       uint32_t pk[4];
 #pragma unroll
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(256) void attn_merge(const float* __restrict__ part
     OutT* dst = out + (qi * H + h) * c + c0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] *= inv;
-    if (rope_d > 0) rope_back8(acc, c0, c, rope_d, rope_theta, q_pos[qi]);
+    if (rope_d > 0) rope_back8(acc, c0, c, rope_d, rope_r, q_pos[qi]);
     for (int j = 0; j < 8 && c0 + j < c; ++j) {
       if constexpr (sizeof(OutT) == 2) dst[j] = f32_to_bf16(acc[j]);
       else dst[j] = acc[j];
@@ -897,10 +897,10 @@ static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream
   if (ns > 1) {
     if (ns <= 4)
       hipLaunchKernelGGL(attn_merge_tiles<4>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 16)), dim3(256), 0, st,
-                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_theta);
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_r);
     else
       hipLaunchKernelGGL(attn_merge_tiles<1>, dim3(cdiv(nq, 8) * 8 * (kNHG * (kAC / 16) / 4)), dim3(256), 0, st,
-                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_theta);
+                         a.part_o, a.part_ml, a.sink, ns, nq, a.out, a.lse, a.q_pos, a.rope_d, a.rope_r);
     CSA_LAUNCH_CHECK();
   }
   return CSA_OK;
@@ -920,7 +920,7 @@ static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, i
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.rope_d = rope_d;
-  a.rope_theta = rope_theta;
+  a.rope_r = rope_ratio(rope_theta, rope_d);
   return a;
 }
 
@@ -977,7 +977,7 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
                        Nc, k, Ls, W, m, part_o, part_ml);
   CSA_LAUNCH_CHECK();
   hipLaunchKernelGGL(attn_merge<float>, dim3(cdiv(nq * H, 4)), dim3(256), 0, st, part_o, part_ml, sink, 1, H, c,
-                     nq * H, static_cast<float*>(out), lse, q_pos, rope_d, rope_theta);
+                     nq * H, static_cast<float*>(out), lse, q_pos, rope_d, rope_ratio(rope_theta, rope_d));
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

@@ -44,17 +44,14 @@ struct AttnArgs {
   size_t cand_stride;        // pairs from one row of cand to the next
   int32_t* idx_out;          // [B*S, k] the selection made from cand, or null
   int rope_d;                // > 0: rotate the output's last rope_d channels back by the query position
-  float rope_theta;
+  double rope_r;             // theta^(-2/rope_d)
 };
 
-// The value of channel `col` after the inverse RoPE of its query's output: pair
-// (2p, 2p+1) of the last d_rope of c channels rotated by -t * theta^(-2p/d_rope), the
-// angle formed in double (positions reach 2^20 and beyond).  cs/sn come from rope_cs_sn.
-__device__ __forceinline__ void rope_cs_sn(int col, int c, int d_rope, float theta, int64_t t, float& cs, float& sn) {
-  const int p = (col - (c - d_rope)) >> 1;
-  const double ang = static_cast<double>(t) * pow(static_cast<double>(theta), -2.0 * p / d_rope);
-  cs = static_cast<float>(cos(ang));
-  sn = static_cast<float>(sin(ang));
+// cos / sin of the inverse-RoPE angle of channel `col` (pair p of the last d_rope of c
+// channels): the rotation by -t * theta^(-2p/d_rope) uses cos(a) and sin(a) of
+// a = t * r^p (rope_cos_sin; r = theta^(-2/d_rope) from the host).
+__device__ __forceinline__ void rope_cs_sn(int col, int c, int d_rope, double r, int64_t t, float& cs, float& sn) {
+  rope_cos_sin(t, (col - (c - d_rope)) >> 1, r, cs, sn);
 }
 
 // x' = x cos + y sin (even channel), y' = y cos - x sin (odd channel); `partner` is the

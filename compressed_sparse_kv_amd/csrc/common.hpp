@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include "csa.h"
 
 namespace csa {
@@ -92,6 +94,27 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 
 __host__ __device__ constexpr inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---- RoPE angles -------------------------------------------------------------------
+// cos and sin of the angle pos * r^p for pair p, with r = theta^(-2/d_rope) formed once on
+// the host in double (rope_ratio).  r^p by square-and-multiply and the product with the
+// position in double (positions reach 2^20 and beyond, where an fp32 angle would be off by
+// tenths of a radian), the angle reduced to [-pi, pi] in double, then cos/sin in fp32.
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int p, double r, float& cs, float& sn) {
+  double f = 1.0, base = r;
+  for (int e = p; e != 0; e >>= 1) {
+    if (e & 1) f *= base;
+    base *= base;
+  }
+  const double ang = static_cast<double>(pos) * f;
+  const double turns = rint(ang * 0.15915494309189535);         // 1 / (2 pi)
+  const double red = fma(-turns, 6.283185307179586, ang);
+  sincosf(static_cast<float>(red), &sn, &cs);
+}
+
+inline double rope_ratio(float theta, int d_rope) {
+  return d_rope > 0 ? std::pow(static_cast<double>(theta), -2.0 / d_rope) : 1.0;
+}
 
 }  // namespace csa
 

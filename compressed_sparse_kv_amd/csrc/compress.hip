@@ -13,7 +13,7 @@
 //      per sequence as [previous block (m rows, when given) | chunk (T rows)];
 //   2. pooling: one workgroup per entry, one thread per channel pair (2p, 2p+1) so the
 //      RoPE pair is thread-local; softmax per channel, block-wide RMS, RoPE with the
-//      angle computed in double precision (positions reach 2^20 and beyond), output
+//      angle formed in double (positions reach 2^20 and beyond; rope_cos_sin), output
 //      in fp32 / bf16 / e4m3 with the row scale amax/448.
 #include <algorithm>
 
@@ -169,7 +169,8 @@ struct PoolArgs {
   const float* bias;         // [ns/2, m, c]
   int overlap, has_prev;
   int T, m, c, d_rope, rows_pb;
-  float rope_theta, rms_eps;
+  double rope_r;             // theta^(-2/d_rope)
+  float rms_eps;
   int64_t p0;
   int out_dtype;
   void* out;
@@ -235,12 +236,11 @@ __global__ __launch_bounds__(512) void compress_pool(PoolArgs a) {
   // RoPE on the last d_rope channels, pair p = pidx - (c - d_rope)/2, position p0 + m*i
   const int p = pidx - (a.c - a.d_rope) / 2;
   if (live && p >= 0) {
-    const double pos = static_cast<double>(a.p0 + static_cast<int64_t>(a.m) * i);
-    const double ang = pos * pow(static_cast<double>(a.rope_theta), -2.0 * p / a.d_rope);
-    const double cs = cos(ang), sn = sin(ang);
-    const double y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-    x0 = static_cast<float>(y0);
-    x1 = static_cast<float>(y1);
+    float cs, sn;
+    rope_cos_sin(a.p0 + static_cast<int64_t>(a.m) * i, p, a.rope_r, cs, sn);
+    const float y0 = fmaf(x0, cs, -x1 * sn), y1 = fmaf(x0, sn, x1 * cs);
+    x0 = y0;
+    x1 = y1;
   }
   const size_t orow = static_cast<size_t>(b) * (a.T / a.m) + i;
   if (a.out_dtype == CSA_F32) {
@@ -298,8 +298,8 @@ int launch_compress(const void* hidden, const void* hidden_prev, int in_dtype, c
                        N, P);
   }
   CSA_LAUNCH_CHECK();
-  PoolArgs pa{P, bias, overlap, has_prev, T, m, c, d_rope, rows_pb, rope_theta, rms_eps, p0, out_dtype, out,
-              out_scale};
+  PoolArgs pa{P, bias, overlap, has_prev, T, m, c, d_rope, rows_pb, rope_ratio(rope_theta, d_rope), rms_eps, p0,
+              out_dtype, out, out_scale};
   const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);
   hipLaunchKernelGGL(compress_pool, dim3(T / m, B), dim3(threads), 0, st, pa);
   CSA_LAUNCH_CHECK();

@@ -11,14 +11,17 @@
 // Two kernels per call:
 //   1. proj_token_bf16 / proj_token_f32: P[b, :] = W . h_b for the B new tokens (fp32, in
 //      the workspace).  bf16: v_mfma_f32_16x16x32_bf16 with M = the tokens (16 per tile),
-//      N = 16 output columns per workgroup, K = d split over the 4 waves of the workgroup;
-//      each lane streams 64 contiguous bytes of its W row per 128-wide K block (the same
-//      permutation of the K slots on both operands, so the pairing is exact).  The weights
-//      are read once per call: decode projection is bound by that stream.
-//   2. compress_step: one workgroup per sequence, one thread per channel pair.  The
-//      token's streams go into ring slot t mod 2m (or m), or update the online triple;
+//      N = 16 output columns per workgroup, K = d cut into 1024-wide slices (one per
+//      workgroup row of the grid; partial sums in the workspace) and each slice over the 4
+//      waves of the workgroup, 2 K blocks of 128 per wave with all loads issued first; each
+//      lane streams 64 contiguous bytes of its W row per block (the same permutation of the
+//      K slots on both operands, so the pairing is exact).  The weights are read once per
+//      call: decode projection is bound by that stream, so it is spread over many waves.
+//   2. compress_step: one workgroup per sequence, one thread per channel pair.  The K
+//      slices are summed (fixed order); the token's streams go into ring slot t mod 2m (or
+//      m), or update the online triple;
 //      when (t + 1) % m == 0 entry i = t / m is pooled (per-channel softmax over the slots,
-//      weighted sum), RMS-normalised, rotated (RoPE at position m*i, angle in double) and
+//      weighted sum), RMS-normalised, rotated (RoPE at position m*i, angle formed in double) and
 //      written as fp32 / bf16 / e4m3 (+ row scale amax/448), row-major or, for the indexer
 //      keys, straight into the 16-entry blocked layout the decode scoring pass reads.
 #include <algorithm>
@@ -29,41 +32,55 @@ namespace csa {
 
 constexpr int kPjK = 128;                   // K block: 4 MFMA steps of 32
 constexpr int kPjWaves = 4;
-constexpr int kPjMaxTiles = 8;              // token tiles of 16 per launch row (128 tokens)
+constexpr int kPjBlocksPerWave = 2;         // K blocks per wave: one K slice = 8 blocks = 1024 wide
+constexpr int kPjSlice = kPjWaves * kPjBlocksPerWave * kPjK;
+constexpr int kPjTilesSmall = 2;            // token tiles of 16 per workgroup: up to 32 tokens ...
+constexpr int kPjTilesLarge = 8;            // ... or 128 (more tokens: further workgroup rows)
 
-// P[b, n0 + (l & 15)] for the tokens b of tile group blockIdx.y; W [N, d] bf16 ("out x in").
+// Partial projection over K slice blockIdx.y: Pk[slice][b][n] for the tokens b of tile group
+// blockIdx.z (MT tiles of 16 tokens at most) and the 16 columns of blockIdx.x; W [N, d] bf16
+// ("out x in").  Every wave issues all its loads (two K blocks of its 16 W rows, 64
+// contiguous bytes per lane per block) before its first MFMA; the four waves' products are
+// summed in LDS in a fixed order.
+template <int MT>
 __global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t* __restrict__ hidden,
                                                                  const uint16_t* __restrict__ W, int B, int d, int N,
-                                                                 float* __restrict__ P) {
+                                                                 float* __restrict__ Pk) {
+  constexpr int kPjMaxTiles = MT;
   __shared__ v4f red[kPjWaves - 1][kPjMaxTiles][64];
   const int l = static_cast<int>(lane_id());
   const int wave = threadIdx.x >> 6;
   const int g = l >> 4;
   const int n0 = blockIdx.x * 16;
-  const int b0 = blockIdx.y * 16 * kPjMaxTiles;
+  const int slice = blockIdx.y;
+  const int b0 = blockIdx.z * 16 * kPjMaxTiles;
   const int ntiles = min(kPjMaxTiles, cdiv(B - b0, 16));
+  static_assert(MT >= 1 && MT <= 8, "token tiles per workgroup");
   const int nblk = d / kPjK;
+  const int j0 = slice * (kPjWaves * kPjBlocksPerWave) + wave * kPjBlocksPerWave;
   const uint16_t* wrow = W + static_cast<size_t>(min(n0 + (l & 15), N - 1)) * d + 32 * g;
+  v8s wb[kPjBlocksPerWave][4];
+#pragma unroll
+  for (int jj = 0; jj < kPjBlocksPerWave; ++jj) {
+    const int j = min(j0 + jj, nblk - 1);              // past the end: a block re-read, its product dropped
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) wb[jj][ks] = *reinterpret_cast<const v8s*>(wrow + static_cast<size_t>(j) * kPjK + 8 * ks);
+  }
   v4f acc[kPjMaxTiles];
 #pragma unroll
   for (int mt = 0; mt < kPjMaxTiles; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-  // hidden rows of this lane in every tile (clamped to the last token; extra rows unused)
-  const uint16_t* hrow[kPjMaxTiles];
 #pragma unroll
-  for (int mt = 0; mt < kPjMaxTiles; ++mt)
-    hrow[mt] = hidden + static_cast<size_t>(min(b0 + 16 * mt + (l & 15), B - 1)) * d + 32 * g;
-  for (int j = wave; j < nblk; j += kPjWaves) {
-    const size_t k0 = static_cast<size_t>(j) * kPjK;
-    v8s wb[4];
+  for (int mt = 0; mt < kPjMaxTiles; ++mt) {
+    if (mt < ntiles) {
+      const uint16_t* hrow = hidden + static_cast<size_t>(min(b0 + 16 * mt + (l & 15), B - 1)) * d + 32 * g;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wb[ks] = *reinterpret_cast<const v8s*>(wrow + k0 + 8 * ks);
+      for (int jj = 0; jj < kPjBlocksPerWave; ++jj) {
+        if (j0 + jj < nblk) {
 #pragma unroll
-    for (int mt = 0; mt < kPjMaxTiles; ++mt) {
-      if (mt < ntiles) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const v8s ha = *reinterpret_cast<const v8s*>(hrow[mt] + k0 + 8 * ks);
-          acc[mt] = mfma_bf16_16x16x32(ha, wb[ks], acc[mt]);
+          for (int ks = 0; ks < 4; ++ks) {
+            const v8s ha = *reinterpret_cast<const v8s*>(hrow + static_cast<size_t>(j0 + jj) * kPjK + 8 * ks);
+            acc[mt] = mfma_bf16_16x16x32(ha, wb[jj][ks], acc[mt]);
+          }
         }
       }
     }
@@ -78,6 +95,7 @@ __global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t*
   __syncthreads();
   if (wave != 0) return;
   const int n = n0 + (l & 15);
+  float* P = Pk + static_cast<size_t>(slice) * B * N;
 #pragma unroll
   for (int mt = 0; mt < kPjMaxTiles; ++mt) {
     if (mt >= ntiles) continue;
@@ -109,17 +127,22 @@ __global__ __launch_bounds__(256) void proj_token_f32(const float* __restrict__ 
 }
 
 struct StepArgs {
-  const float* P;            // [B, ns*c] this call's projections
+  const float* P;            // [n_slices, B, ns*c] partial projections of this call's tokens
+  int n_slices;
+  int B;
   const float* bias;         // [ns/2, m, c]
   const int64_t* pos;        // [B]
   float* state;              // ring [B, nslot, ns*c] or online [B, 3, c]
   int overlap, online, emit;
   int m, c, d_rope;
-  float rope_theta, rms_eps;
+  double rope_r;             // theta^(-2/d_rope)
+  float rms_eps;
   int out_dtype, out_layout, Nc_max;
   void* cache;
   float* cache_scale;
 };
+
+constexpr int kStepMaxSlots = 8;            // ring slots held in registers by the pooling (2m <= 8)
 
 __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   __shared__ float red[8];
@@ -132,71 +155,130 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   const int nslot = a.overlap ? 2 * m : m;
   const int p = threadIdx.x;                            // channel pair (2p, 2p+1)
   const bool live = p < c / 2;
-  const float* Pb = a.P + static_cast<size_t>(b) * N;
   const int r = static_cast<int>(t % m);                // slot of the token within its block
   const bool boundary = a.emit && r == m - 1;
+  // this token's streams for the pair: the sum of the K slices (fixed order)
+  float2 tok[4] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
+  if (live) {
+    for (int sl = 0; sl < a.n_slices; ++sl) {
+      const float* Pb = a.P + (static_cast<size_t>(sl) * a.B + b) * N;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < ns) {
+          const float2 v = *reinterpret_cast<const float2*>(Pb + s * c + 2 * p);
+          tok[s].x += v.x;
+          tok[s].y += v.y;
+        }
+    }
+  }
   float u[2] = {0.f, 0.f};
   if (a.online) {
     float* st = a.state + static_cast<size_t>(b) * 3 * c;
     if (live) {
+      const float2 bz = *reinterpret_cast<const float2*>(a.bias + r * c + 2 * p);
+      const float z[2] = {tok[1].x + bz.x, tok[1].y + bz.y}, cv[2] = {tok[0].x, tok[0].y};
+      float2 mo = make_float2(0.f, 0.f), so = mo, ao = mo;
+      if (r != 0) {
+        mo = *reinterpret_cast<const float2*>(st + 2 * p);
+        so = *reinterpret_cast<const float2*>(st + c + 2 * p);
+        ao = *reinterpret_cast<const float2*>(st + 2 * c + 2 * p);
+      }
+      const float mov[2] = {mo.x, mo.y}, sov[2] = {so.x, so.y}, aov[2] = {ao.x, ao.y};
+      float mx[2], sm[2], acc[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int ch = 2 * p + h;
-        const float z = Pb[c + ch] + a.bias[r * c + ch], cv = Pb[ch];
-        float mx, sm, acc;
         if (r == 0) {
-          mx = z; sm = 1.0f; acc = cv;
+          mx[h] = z[h]; sm[h] = 1.0f; acc[h] = cv[h];
         } else {
-          const float mo = st[ch], so = st[c + ch], ao = st[2 * c + ch];
-          mx = fmaxf(mo, z);
-          const float e_old = expf(mo - mx), e_new = expf(z - mx);
-          sm = so * e_old + e_new;
-          acc = fmaf(e_new, cv, ao * e_old);
+          mx[h] = fmaxf(mov[h], z[h]);
+          const float e_old = expf(mov[h] - mx[h]), e_new = expf(z[h] - mx[h]);
+          sm[h] = sov[h] * e_old + e_new;
+          acc[h] = fmaf(e_new, cv[h], aov[h] * e_old);
         }
-        st[ch] = mx; st[c + ch] = sm; st[2 * c + ch] = acc;
-        u[h] = acc / sm;
+        u[h] = acc[h] / sm[h];
       }
+      *reinterpret_cast<float2*>(st + 2 * p) = make_float2(mx[0], mx[1]);
+      *reinterpret_cast<float2*>(st + c + 2 * p) = make_float2(sm[0], sm[1]);
+      *reinterpret_cast<float2*>(st + 2 * c + 2 * p) = make_float2(acc[0], acc[1]);
     }
   } else {
     float* ring = a.state + static_cast<size_t>(b) * nslot * N;
-    float* slot = ring + static_cast<size_t>(t % nslot) * N;
-    if (live)
-      for (int s = 0; s < ns; ++s) {
-        slot[s * c + 2 * p] = Pb[s * c + 2 * p];
-        slot[s * c + 2 * p + 1] = Pb[s * c + 2 * p + 1];
-      }
+    const int my_slot = static_cast<int>(t % nslot);
+    if (live) {
+      float* slot = ring + static_cast<size_t>(my_slot) * N;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < ns) *reinterpret_cast<float2*>(slot + s * c + 2 * p) = tok[s];
+    }
     if (boundary && live) {
       const int64_t i = t / m;
       const bool bslots = a.overlap && i > 0;
+      // slots of block i (a-stream: C at stream 0, Z at stream 1) and, with overlap, of
+      // block i-1 (b-stream: C at stream 2, Z at stream 3); this thread wrote every slot of
+      // its channels, in this call or an earlier one.  Loaded first, then pooled.
+      const int nsl = bslots ? 2 * m : m;
+      float2 zc[2 * kStepMaxSlots][2];                  // [slot][logit, value]
+      if (m <= kStepMaxSlots / 2 || (!a.overlap && m <= kStepMaxSlots)) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ch = 2 * p + h;
-        // this thread wrote every slot of its channels (in this and earlier calls)
-        float mx = -INFINITY;
-        for (int j = 0; j < m; ++j) {
-          const float* s = ring + static_cast<size_t>((m * i + j) % nslot) * N;
-          mx = fmaxf(mx, s[c + ch] + a.bias[j * c + ch]);
-        }
-        if (bslots)
-          for (int j = 0; j < m; ++j) {
-            const float* s = ring + static_cast<size_t>((m * (i - 1) + j) % nslot) * N;
-            mx = fmaxf(mx, s[3 * c + ch] + a.bias[(m + j) * c + ch]);
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j) {
+          if (j < nsl) {
+            const bool bs = j >= m;
+            const int jr = bs ? j - m : j;
+            const int64_t pj = bs ? m * (i - 1) + jr : m * i + jr;
+            const int sj = static_cast<int>(pj % nslot);
+            const int sz = bs ? 3 : 1, sc = bs ? 2 : 0;
+            float2 zz, cc;
+            if (sj == my_slot) {
+              zz = bs ? tok[3] : tok[1];
+              cc = bs ? tok[2] : tok[0];
+            } else {
+              const float* s = ring + static_cast<size_t>(sj) * N;
+              zz = *reinterpret_cast<const float2*>(s + sz * c + 2 * p);
+              cc = *reinterpret_cast<const float2*>(s + sc * c + 2 * p);
+            }
+            const float2 bz = *reinterpret_cast<const float2*>(a.bias + ((bs ? m : 0) + jr) * c + 2 * p);
+            zc[j][0] = make_float2(zz.x + bz.x, zz.y + bz.y);
+            zc[j][1] = cc;
           }
-        float den = 0.f, num = 0.f;
-        for (int j = 0; j < m; ++j) {
-          const float* s = ring + static_cast<size_t>((m * i + j) % nslot) * N;
-          const float e = expf(s[c + ch] + a.bias[j * c + ch] - mx);
-          den += e;
-          num = fmaf(e, s[ch], num);
         }
-        if (bslots)
-          for (int j = 0; j < m; ++j) {
-            const float* s = ring + static_cast<size_t>((m * (i - 1) + j) % nslot) * N;
-            const float e = expf(s[3 * c + ch] + a.bias[(m + j) * c + ch] - mx);
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+          if (j < nsl) { mx0 = fmaxf(mx0, zc[j][0].x); mx1 = fmaxf(mx1, zc[j][0].y); }
+        float d0 = 0.f, d1 = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+          if (j < nsl) {
+            const float e0 = expf(zc[j][0].x - mx0), e1 = expf(zc[j][0].y - mx1);
+            d0 += e0; d1 += e1;
+            n0 = fmaf(e0, zc[j][1].x, n0);
+            n1 = fmaf(e1, zc[j][1].y, n1);
+          }
+        u[0] = n0 / d0;
+        u[1] = n1 / d1;
+      } else {
+        // long blocks (HCA ring, m > 8): two passes over the slots in memory
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 2 * p + h;
+          float mx = -INFINITY;
+          for (int j = 0; j < nsl; ++j) {
+            const bool bs = j >= m;
+            const int jr = bs ? j - m : j;
+            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
+            mx = fmaxf(mx, s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch]);
+          }
+          float den = 0.f, num = 0.f;
+          for (int j = 0; j < nsl; ++j) {
+            const bool bs = j >= m;
+            const int jr = bs ? j - m : j;
+            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
+            const float e = expf(s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch] - mx);
             den += e;
-            num = fmaf(e, s[2 * c + ch], num);
+            num = fmaf(e, s[(bs ? 2 : 0) * c + ch], num);
           }
-        u[h] = num / den;
+          u[h] = num / den;
+        }
       }
     }
   }
@@ -214,11 +296,11 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   const int64_t i = t / m;
   const int pr = p - (c - a.d_rope) / 2;                // RoPE pair index
   if (live && pr >= 0) {
-    const double ang = static_cast<double>(m * i) * pow(static_cast<double>(a.rope_theta), -2.0 * pr / a.d_rope);
-    const double cs = cos(ang), sn = sin(ang);
-    const double y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
-    x0 = static_cast<float>(y0);
-    x1 = static_cast<float>(y1);
+    float cs, sn;
+    rope_cos_sin(m * i, pr, a.rope_r, cs, sn);
+    const float y0 = fmaf(x0, cs, -x1 * sn), y1 = fmaf(x0, sn, x1 * cs);
+    x0 = y0;
+    x1 = y1;
   }
   const bool store = i < a.Nc_max;
   const size_t row = static_cast<size_t>(b) * a.Nc_max + static_cast<size_t>(i);
@@ -267,8 +349,11 @@ size_t compress_state_bytes(int B, int m, int c, int overlap, int online) {
   return static_cast<size_t>(B) * nslot * (overlap ? 4 : 2) * c * sizeof(float);
 }
 
-size_t compress_decode_workspace_bytes(int B, int c, int overlap) {
-  return static_cast<size_t>(B) * (overlap ? 4 : 2) * c * sizeof(float);
+// K slices of the bf16 projection (each summed by the step kernel); 1 for fp32 inputs.
+static int proj_slices(int d, int in_dtype) { return in_dtype == CSA_BF16 ? cdiv(d, kPjSlice) : 1; }
+
+size_t compress_decode_workspace_bytes(int B, int d, int c, int overlap, int in_dtype) {
+  return static_cast<size_t>(proj_slices(d, in_dtype)) * B * (overlap ? 4 : 2) * c * sizeof(float);
 }
 
 int launch_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias, int overlap,
@@ -277,17 +362,22 @@ int launch_compress_decode(const void* hidden, int in_dtype, const void* w_proj,
                            int out_dtype, int out_layout, int Nc_max, void* ws, hipStream_t st) {
   const int N = (overlap ? 4 : 2) * c;
   float* P = static_cast<float*>(ws);
+  const int n_slices = proj_slices(d, in_dtype);
   if (in_dtype == CSA_BF16) {
-    const dim3 grid(cdiv(N, 16), cdiv(B, 16 * kPjMaxTiles));
-    hipLaunchKernelGGL(proj_token_bf16, grid, dim3(kPjWaves * 64), 0, st, static_cast<const uint16_t*>(hidden),
-                       static_cast<const uint16_t*>(w_proj), B, d, N, P);
+    if (B <= 16 * kPjTilesSmall)
+      hipLaunchKernelGGL(proj_token_bf16<kPjTilesSmall>, dim3(cdiv(N, 16), n_slices, 1), dim3(kPjWaves * 64), 0, st,
+                         static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_proj), B, d, N, P);
+    else
+      hipLaunchKernelGGL(proj_token_bf16<kPjTilesLarge>, dim3(cdiv(N, 16), n_slices, cdiv(B, 16 * kPjTilesLarge)),
+                         dim3(kPjWaves * 64), 0, st, static_cast<const uint16_t*>(hidden),
+                         static_cast<const uint16_t*>(w_proj), B, d, N, P);
   } else {
     hipLaunchKernelGGL(proj_token_f32, dim3(cdiv(N, 256), B), dim3(256), 0, st, static_cast<const float*>(hidden),
                        static_cast<const float*>(w_proj), B, d, N, P);
   }
   CSA_LAUNCH_CHECK();
-  StepArgs a{P, bias, pos, state, overlap, online, emit, m, c, d_rope, rope_theta, rms_eps, out_dtype, out_layout,
-             Nc_max, cache, cache_scale};
+  StepArgs a{P, n_slices, B, bias, pos, state, overlap, online, emit, m, c, d_rope, rope_ratio(rope_theta, d_rope),
+             rms_eps, out_dtype, out_layout, Nc_max, cache, cache_scale};
   const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);
   hipLaunchKernelGGL(compress_step, dim3(B), dim3(threads), 0, st, a);
   CSA_LAUNCH_CHECK();

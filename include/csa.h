@@ -135,10 +135,11 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
  *           CSA_FP8_E4M3 codes with cache_scale [B, Nc_max] = amax/448);
  *           CSA_LAYOUT_B16: FP8 codes of c = 128 in 16-entry blocks
  *           (csa_index_keys_b16_size(B, Nc_max) bytes) + cache_scale [B, Nc_max].
- *   ws      >= csa_compress_decode_workspace_size(B, c, overlap) bytes.
+ *   ws      >= csa_compress_decode_workspace_size(B, d, c, overlap, in_dtype) bytes (the projection
+ *           of the B tokens, in partial sums over slices of the d inputs).
  * ------------------------------------------------------------------------------ */
 size_t csa_compress_state_size(int B, int m, int c, int overlap, int online);
-size_t csa_compress_decode_workspace_size(int B, int c, int overlap);
+size_t csa_compress_decode_workspace_size(int B, int d, int c, int overlap, int in_dtype);
 
 int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias,
                         int overlap, int online, int B, int d, int m, int c, int d_rope,

@@ -351,3 +351,19 @@ def compressor_inputs(seed: int, B: int, T: int, d: int, m: int, c: int, overlap
     a["W_bf16"] = to_bf16_bits(gaussian(rs[2], (d, ns * c), sigma_w))
     a["bias"] = gaussian(rs[3], (ns // 2, m, c), sigma_w)
     return a
+
+
+def decode_layer_inputs(seed: int, B: int, d: int, m: int, c: int, d_I: int, sigma_w: float = 0.02) -> dict:
+    """The compressor side of one CSA decode step: the new token's hidden state per sequence
+    (N(0,1) bf16), the 2m - 1 tokens before it (to fill the (C, Z) ring before the first
+    step), and the main / indexer compressor weights and biases (N(0, sigma_w); W in the
+    "out x in" layout the library takes, bf16)."""
+    rs = _streams(seed, 6)
+    return {
+        "hidden_bf16": to_bf16_bits(gaussian(rs[0], (B, d))),
+        "prime_bf16": to_bf16_bits(gaussian(rs[1], (B, 2 * m - 1, d))),
+        "W_main_t_bf16": to_bf16_bits(gaussian(rs[2], (4 * c, d), sigma_w)),
+        "B_main": gaussian(rs[3], (2, m, c), sigma_w),
+        "W_idx_t_bf16": to_bf16_bits(gaussian(rs[4], (4 * d_I, d), sigma_w)),
+        "B_idx": gaussian(rs[5], (2, m, d_I), sigma_w),
+    }
