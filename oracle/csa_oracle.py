@@ -468,3 +468,52 @@ def inverse_rope(o, pos, d_rope: int, theta: float):
     p - t ([V4-CSA2] section 12.1 "Partial RoPE 与 inverse RoPE"; [ATTN-CMP] section
     "CSA（DeepSeek-V4）": the last 64 output dimensions are rotated back by RoPE(-t))."""
     return rope(o, -np.asarray(pos, dtype=np.float64), d_rope, theta)
+
+
+# ---------------------------------------------------------------------------
+# CSA2 compressor: single stream, no position bias, indexer K projected from the main KV
+# ---------------------------------------------------------------------------
+
+def csa2_compress(hidden, W_kv, W_gate, W_k, *, m: int, d_rope: int, theta_kv: float, theta_k: float,
+                  rms_eps: float, p0: int):
+    """CSA2 main KV entries and indexer keys of each sequence of a chunk.
+
+    [V4-CSA2] sections 6.1 and 7.2 (one KV projection and one gate, each entry pooling only
+    its own m-token block, no position bias inside the compressor: per channel, a softmax
+    over the block's gate values weights the block's KV values), 7.5 and 15.1 (ratio 1:
+    no gate, the entry is the normalised projection), 6.2 (indexer K is a projection of the
+    main KV latent, not a second compressor) and 7.4 (the entry's RoPE position is its
+    block's first token); [ATTN-CMP] section on CSA2 (the latent before RoPE feeds the
+    indexer-K projection wk, then k_norm and RoPE with the indexer's own theta).
+
+    hidden [B, T, d] at positions p0 .. p0+T-1 (T % m == 0, p0 % m == 0); W_kv, W_gate [d, c]
+    (W_gate None when m == 1); W_k [c, d_I].  Returns (kv [B, T/m, c], kI [B, T/m, d_I]),
+    both float64:
+        latent_i = RMSNorm(sum_r softmax_r(Z_r) * C_r)  over the block's tokens r,
+        kv_i     = RoPE_{theta_kv}(latent_i, p0 + m*i),
+        kI_i     = RoPE_{theta_k}(RMSNorm(latent_i . W_k), p0 + m*i).
+    """
+    hidden = np.asarray(hidden, np.float64)
+    W_kv = np.asarray(W_kv, np.float64)
+    W_k = np.asarray(W_k, np.float64)
+    B, T, d = hidden.shape
+    assert T % m == 0 and p0 % m == 0
+    n = T // m
+    c = W_kv.shape[1]
+    kv = np.zeros((B, n, c))
+    kI = np.zeros((B, n, W_k.shape[1]))
+    for b in range(B):
+        C = hidden[b] @ W_kv
+        Z = None if W_gate is None else hidden[b] @ np.asarray(W_gate, np.float64)
+        for i in range(n):
+            if m == 1 and Z is None:
+                pooled = C[i]
+            else:
+                z = Z[m * i:m * i + m]                               # [m, c]
+                e = np.exp(z - z.max(axis=0))
+                pooled = (e * C[m * i:m * i + m]).sum(axis=0) / e.sum(axis=0)
+            latent = rms_norm(pooled[None], rms_eps)[0]
+            pos = p0 + m * i
+            kv[b, i] = rope(latent[None], pos, d_rope, theta_kv)[0]
+            kI[b, i] = rope(rms_norm((latent @ W_k)[None], rms_eps), pos, d_rope, theta_k)[0]
+    return kv, kI

@@ -1,10 +1,12 @@
-"""Pins of the oracle's decode-time compressor and inverse RoPE (CPU only).
+"""Pins of the oracle's decode-time compressor, inverse RoPE and CSA2 compressor (CPU only).
 
 The decode compressor is pinned to the prefill compressor (itself pinned by hand cases
 and invariants in test_oracle_pins.py), to the hand case H1 run token by token, and to the
 emission rule of the pages (an entry only when a token completes its block); the online
 HCA variant to the ring.  Inverse RoPE is pinned to a hand rotation, to RoPE itself, and to
-the relative-position property it exists for.
+the relative-position property it exists for.  The CSA2 compressor is pinned to the
+single-stream compressor with zero bias, to the ratio-1 closed form and a hand case, and its
+indexer key to the projection of the main latent recovered by inverse RoPE.
 """
 
 import math
@@ -120,3 +122,56 @@ def test_inverse_rope_makes_the_output_relative():
 
     assert np.allclose(out_at(0), out_at(977), atol=1e-10)
     assert np.allclose(out_at(0), out_at(-90), atol=1e-10)
+
+
+# ---------------------------------------------------------------------------
+# CSA2 compressor
+# ---------------------------------------------------------------------------
+
+def test_csa2_main_is_the_single_stream_compressor_without_bias():
+    # the CSA2 main latent is the HCA-style single stream with B = 0
+    rng = np.random.default_rng(30)
+    m, c, d, T, dI = 4, 8, 12, 24, 4
+    hidden = rng.normal(size=(2, T, d))
+    Wkv, Wg, Wk = rng.normal(size=(d, c)), rng.normal(size=(d, c)), rng.normal(size=(c, dI))
+    kv, _ = O.csa2_compress(hidden, Wkv, Wg, Wk, m=m, d_rope=4, theta_kv=1e4, theta_k=1.6e5, rms_eps=1e-6, p0=8)
+    ref = O.csa_compress(hidden, np.concatenate([Wkv, Wg], axis=1), np.zeros((1, m, c)), overlap=False, m=m, c=c,
+                         d_rope=4, rope_theta=1e4, rms_eps=1e-6, p0=8)
+    assert np.allclose(kv, ref, atol=1e-12)
+
+
+def test_csa2_ratio_one_and_hand_case():
+    rng = np.random.default_rng(31)
+    d, c, dI, T = 6, 4, 2, 5
+    hidden = rng.normal(size=(1, T, d))
+    Wkv, Wk = rng.normal(size=(d, c)), rng.normal(size=(c, dI))
+    kv, kI = O.csa2_compress(hidden, Wkv, None, Wk, m=1, d_rope=2, theta_kv=1e4, theta_k=1e4, rms_eps=0.0, p0=3)
+    for i in range(T):
+        C = hidden[0, i] @ Wkv
+        lat = C / math.sqrt(np.mean(C * C))
+        assert np.allclose(kv[0, i], O.rope(lat, 3 + i, 2, 1e4), atol=1e-12)
+    # hand case, m = 2, c = 2: gates (0, ln 3) on channel 0 -> weights 1/4, 3/4; equal on channel 1
+    hidden = np.eye(2)[None]                                  # token r projects to row r
+    Wkv = np.array([[4.0, 2.0], [8.0, -2.0]])
+    Wg = np.array([[0.0, 0.0], [math.log(3), 0.0]])
+    Wk = np.array([[1.0, 0.0], [0.0, 1.0]])                   # identity: K^I = RoPE(Norm(latent))
+    kv, kI = O.csa2_compress(hidden, Wkv, Wg, Wk, m=2, d_rope=0, theta_kv=1e4, theta_k=1e4, rms_eps=0.0, p0=0)
+    # pooled = (0.25*4 + 0.75*8, 0.5*2 - 0.5*2) = (7, 0): normalised (sqrt 2, 0)
+    assert np.allclose(kv[0, 0], [math.sqrt(2), 0.0])
+    assert np.allclose(kI[0, 0], [math.sqrt(2), 0.0])
+
+
+def test_csa2_indexer_key_is_projected_from_the_pre_rope_latent():
+    # K^I from the latent before RoPE: undo the main RoPE of kv, project, normalise, rotate
+    rng = np.random.default_rng(32)
+    m, c, d, T, dI = 2, 8, 10, 12, 6
+    hidden = rng.normal(size=(1, T, d))
+    Wkv, Wg, Wk = rng.normal(size=(d, c)), rng.normal(size=(d, c)), rng.normal(size=(c, dI))
+    kv, kI = O.csa2_compress(hidden, Wkv, Wg, Wk, m=m, d_rope=4, theta_kv=1e4, theta_k=1.6e5, rms_eps=1e-6, p0=100)
+    pos = 100 + m * np.arange(T // m)
+    latent = O.inverse_rope(kv[0], pos, 4, 1e4)
+    expect = O.rope(O.rms_norm(latent @ Wk, 1e-6), pos, 4, 1.6e5)
+    assert np.allclose(kI[0], expect, atol=1e-12)
+    # and not from the rotated one (the positions are large enough for the two to differ)
+    wrong = O.rope(O.rms_norm(kv[0] @ Wk, 1e-6), pos, 4, 1.6e5)
+    assert not np.allclose(kI[0], wrong, atol=1e-3)
