@@ -28,6 +28,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "C
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
            "csa_compress_state_size", "csa_compress_decode_workspace_size", "csa_compress_decode",
+           "csa2_compress_workspace_size", "csa2_compress",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
         "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
         "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
         "csa_compress_state_size": ([i, i, i, i, i], sz),
+        "csa2_compress_workspace_size": ([i, i, i, i], sz),
+        "csa2_compress": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, f, i64, vp, vp, i, vp, vp, i, vp, sz, vp], i),
         "csa_compress_decode_workspace_size": ([i, i, i, i, i], sz),
         "csa_compress_decode": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i, vp, vp, vp, i, i, i, vp, sz, vp], i),
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
@@ -152,6 +155,21 @@ def csa_compress(hidden, hidden_prev, w_proj, bias, *, overlap: bool, m: int, c:
         d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale), _dtype(out),
         _p(ws), wsb, _stream(stream)))
     return out
+
+
+def csa2_compress(hidden, w_proj, w_k, *, m: int, d_rope: int, theta_kv: float, theta_k: float, rms_eps: float,
+                  p0: int, kv_out, k_out, kv_scale=None, k_scale=None, ws=None, stream=None):
+    """CSA2 compressor: hidden [B,T,d], w_proj [(2 if m > 1 else 1)*c, d], w_k [d_I, c] ->
+    kv_out [B,T/m,c] and k_out [B,T/m,d_I] (fp32 / bf16 / uint8 codes with their scales)."""
+    _dev(hidden, w_proj, w_k, kv_out, k_out, kv_scale, k_scale, ws)
+    B, T, d = hidden.shape
+    c, dI = kv_out.shape[-1], k_out.shape[-1]
+    ws, wsb = _ws(int(_lib.csa2_compress_workspace_size(B, T, m, c)), ws, hidden.device)
+    _check("csa2_compress", _lib.csa2_compress(
+        _p(hidden), _dtype(hidden), _p(w_proj), _p(w_k), B, T, d, m, c, dI, d_rope, float(theta_kv), float(theta_k),
+        float(rms_eps), int(p0), _p(kv_out), _p(kv_scale), _dtype(kv_out), _p(k_out), _p(k_scale), _dtype(k_out),
+        _p(ws), wsb, _stream(stream)))
+    return kv_out, k_out
 
 
 def compress_state_size(B, m, c, overlap, online=False) -> int:

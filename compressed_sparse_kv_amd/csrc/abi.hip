@@ -20,6 +20,9 @@ int launch_compress(const void*, const void*, int, const void*, const float*, in
                     float, float, int64_t, void*, float*, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
 size_t compress_state_bytes(int, int, int, int, int);
+size_t csa2_workspace_bytes(int, int, int, int);
+int launch_csa2_compress(const void*, int, const void*, const void*, int, int, int, int, int, int, int, float, float,
+                         float, int64_t, void*, float*, int, void*, float*, int, void*, hipStream_t);
 size_t compress_decode_workspace_bytes(int, int, int, int, int);
 int launch_compress_decode(const void*, int, const void*, const float*, int, int, int, int, int, int, int, float,
                            float, const int64_t*, int, float*, void*, float*, int, int, int, void*, hipStream_t);
@@ -94,6 +97,34 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, cons
   if (ws == nullptr || ws_bytes < compress_workspace_bytes(B, T, m, c, overlap, has_prev)) return CSA_ERR_WORKSPACE;
   return launch_compress(hidden, hidden_prev, in_dtype, w_proj, bias, overlap, B, T, d, m, c, d_rope, rope_theta,
                          rms_eps, p0, out, out_scale, out_dtype, ws, as_stream(stream));
+}
+
+size_t csa2_compress_workspace_size(int B, int T, int m, int c) {
+  if (B <= 0 || T <= 0 || m <= 0 || c <= 0) return 0;
+  return csa2_workspace_bytes(B, T, m, c);
+}
+
+int csa2_compress(const void* hidden, int in_dtype, const void* w_proj, const void* w_k, int B, int T, int d, int m,
+                  int c, int d_I, int d_rope, float theta_kv, float theta_k, float rms_eps, int64_t p0, void* kv_out,
+                  float* kv_scale, int kv_dtype, void* k_out, float* k_scale, int k_dtype, void* ws, size_t ws_bytes,
+                  void* stream) {
+  CSA_REQUIRE(hidden && w_proj && w_k && kv_out && k_out);
+  CSA_REQUIRE(B > 0 && T > 0 && d > 0 && m > 0 && c > 0 && d_I > 0);
+  CSA_REQUIRE(T % m == 0 && p0 >= 0 && p0 % m == 0);
+  CSA_REQUIRE(c % 2 == 0 && c <= 1024 && d_I % 2 == 0 && d_I <= 256);
+  CSA_REQUIRE(d_rope >= 0 && d_rope % 2 == 0 && d_rope <= c && d_rope <= d_I);
+  CSA_REQUIRE(rms_eps >= 0.0f && theta_kv > 0.0f && theta_k > 0.0f);
+  CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
+  CSA_REQUIRE(kv_dtype == CSA_F32 || kv_dtype == CSA_BF16 || kv_dtype == CSA_FP8_E4M3);
+  CSA_REQUIRE(k_dtype == CSA_F32 || k_dtype == CSA_BF16 || k_dtype == CSA_FP8_E4M3);
+  CSA_REQUIRE(kv_dtype != CSA_FP8_E4M3 || kv_scale != nullptr);
+  CSA_REQUIRE(k_dtype != CSA_FP8_E4M3 || k_scale != nullptr);
+  if (in_dtype == CSA_BF16 && (d % 64 != 0 || c % 8 != 0)) return CSA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * T * 2 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(ws) && aligned16(w_k));
+  if (ws == nullptr || ws_bytes < csa2_workspace_bytes(B, T, m, c)) return CSA_ERR_WORKSPACE;
+  return launch_csa2_compress(hidden, in_dtype, w_proj, w_k, B, T, d, m, c, d_I, d_rope, theta_kv, theta_k, rms_eps,
+                              p0, kv_out, kv_scale, kv_dtype, k_out, k_scale, k_dtype, ws, as_stream(stream));
 }
 
 size_t csa_compress_state_size(int B, int m, int c, int overlap, int online) {

@@ -279,25 +279,35 @@ size_t compress_workspace_bytes(int B, int T, int m, int c, int overlap, int has
   return rows * (overlap ? 4 : 2) * static_cast<size_t>(c) * sizeof(float);
 }
 
+// P[B*rows_pb, N] = rows of (hidden_prev | hidden) . w^T: the projection GEMM alone (also
+// used by the CSA2 compressor).
+int launch_proj_gemm(const void* hidden, const void* hidden_prev, int in_dtype, const void* w, int B, int T, int m,
+                     int d, int N, float* P, hipStream_t st) {
+  const int has_prev = hidden_prev != nullptr;
+  const int rows_pb = T + (has_prev ? m : 0);
+  const int M = B * rows_pb;
+  if (in_dtype == CSA_BF16) {
+    GemmA A{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(hidden_prev), T, m, d, rows_pb};
+    dim3 grid(cdiv(N, kGT), cdiv(M, kGT));
+    hipLaunchKernelGGL(proj_gemm_bf16, grid, dim3(256), 0, st, A, static_cast<const uint16_t*>(w), M, N, P);
+  } else {
+    dim3 grid(cdiv(N, 16), cdiv(M, 16));
+    hipLaunchKernelGGL(proj_gemm_f32, grid, dim3(256), 0, st, static_cast<const float*>(hidden),
+                       static_cast<const float*>(hidden_prev), T, m, d, rows_pb, static_cast<const float*>(w), M, N, P);
+  }
+  CSA_LAUNCH_CHECK();
+  return CSA_OK;
+}
+
 int launch_compress(const void* hidden, const void* hidden_prev, int in_dtype, const void* w_proj, const float* bias,
                     int overlap, int B, int T, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
                     int64_t p0, void* out, float* out_scale, int out_dtype, void* ws, hipStream_t st) {
   const int has_prev = hidden_prev != nullptr;
   const int rows_pb = T + (has_prev ? m : 0);
-  const int M = B * rows_pb;
   const int N = (overlap ? 4 : 2) * c;
   float* P = static_cast<float*>(ws);
-  if (in_dtype == CSA_BF16) {
-    GemmA A{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(hidden_prev), T, m, d, rows_pb};
-    dim3 grid(cdiv(N, kGT), cdiv(M, kGT));
-    hipLaunchKernelGGL(proj_gemm_bf16, grid, dim3(256), 0, st, A, static_cast<const uint16_t*>(w_proj), M, N, P);
-  } else {
-    dim3 grid(cdiv(N, 16), cdiv(M, 16));
-    hipLaunchKernelGGL(proj_gemm_f32, grid, dim3(256), 0, st, static_cast<const float*>(hidden),
-                       static_cast<const float*>(hidden_prev), T, m, d, rows_pb, static_cast<const float*>(w_proj), M,
-                       N, P);
-  }
-  CSA_LAUNCH_CHECK();
+  const int rc = launch_proj_gemm(hidden, hidden_prev, in_dtype, w_proj, B, T, m, d, N, P, st);
+  if (rc != CSA_OK) return rc;
   PoolArgs pa{P, bias, overlap, has_prev, T, m, c, d_rope, rows_pb, rope_ratio(rope_theta, d_rope), rms_eps, p0,
               out_dtype, out, out_scale};
   const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);

@@ -105,6 +105,36 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
                  void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * Stage 1, CSA2 form (DeepSeek-V4.1): main KV entries and the indexer keys derived from
+ * them.  [V4-CSA2] sections 6.1, 7.2 (one KV projection and one gate; each entry pools only
+ * its own m-token block, per channel a softmax over the block's gate values, no position
+ * bias), 7.5 and 15.1 (ratio 1: no gate, the entry is the normalised projection), 6.2 (the
+ * indexer key is a projection of the main latent) and 7.4 (RoPE at the block's first
+ * token); [ATTN-CMP] section on CSA2 (wk applied to the latent before RoPE, then k_norm and
+ * RoPE with the indexer's own theta).
+ *
+ *   latent_i = RMSNorm(sum_r softmax_r(Z_r) * C_r)   (ratio 1: RMSNorm(C_i))
+ *   kv_i     = RoPE(latent_i) at position p0 + m*i, theta_kv, last d_rope channels
+ *   kI_i     = RoPE(RMSNorm(latent_i . W_k^T)) at the same position, theta_k, last d_rope
+ * RMSNorm has unit gain and rms_eps.
+ *
+ *   hidden [B, T, d] in_dtype (CSA_F32 or CSA_BF16 with d % 64 == 0, c % 8 == 0), positions
+ *          p0 .. p0+T-1;  T % m == 0, p0 % m == 0.
+ *   w_proj [S*c, d] in_dtype ("out x in"): S = 2 (C | Z) for m > 1, S = 1 (C) for m = 1.
+ *   w_k    [d_I, c] in_dtype ("out x in"), 16-byte aligned;  c <= 1024, d_I <= 256, even;
+ *          d_rope even, <= c and <= d_I.
+ *   kv_out [B, T/m, c] and k_out [B, T/m, d_I] in CSA_F32, CSA_BF16 or CSA_FP8_E4M3 (with
+ *          kv_scale / k_scale [B, T/m] = amax/448 of the row).
+ *   ws     >= csa2_compress_workspace_size(B, T, m, c) bytes (the projection).
+ * ------------------------------------------------------------------------------ */
+size_t csa2_compress_workspace_size(int B, int T, int m, int c);
+
+int csa2_compress(const void* hidden, int in_dtype, const void* w_proj, const void* w_k, int B, int T, int d,
+                  int m, int c, int d_I, int d_rope, float theta_kv, float theta_k, float rms_eps,
+                  int64_t p0, void* kv_out, float* kv_scale, int kv_dtype, void* k_out, float* k_scale,
+                  int k_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 1, decode form: one new token per sequence.
  * [HCA-CSA] "KV cache：成品与原料" (an FP32 ring of the (C, Z) projections of the last 2m
  * tokens for CSA, m for HCA; an entry is produced only by the token that completes its

@@ -517,3 +517,64 @@ def csa2_compress(hidden, W_kv, W_gate, W_k, *, m: int, d_rope: int, theta_kv: f
             kv[b, i] = rope(latent[None], pos, d_rope, theta_kv)[0]
             kI[b, i] = rope(rms_norm((latent @ W_k)[None], rms_eps), pos, d_rope, theta_k)[0]
     return kv, kI
+
+
+# ---------------------------------------------------------------------------
+# CSA2 hierarchical indexer: block candidates of the Full layer, Reindex over the pool
+# ---------------------------------------------------------------------------
+
+def block_scores(scores, block: int):
+    """Block score = the largest score among a block's positions ([V4-CSA2] section 11: a
+    block of 8 positions scores as its best position); -inf when no position of the block
+    is a candidate (all -inf).  scores [..., N] -> [..., ceil(N/block)]."""
+    s = np.asarray(scores, np.float64)
+    n = s.shape[-1]
+    nb = -(-n // block)
+    pad = np.full(s.shape[:-1] + (nb * block - n,), -np.inf)
+    return np.concatenate([s, pad], axis=-1).reshape(s.shape[:-1] + (nb, block)).max(axis=-1)
+
+
+def candidate_pool(scores, block: int, n_blocks: int):
+    """The Full layer's candidate pool ([V4-CSA2] sections 11 and 11.1): the n_blocks best
+    blocks (block score descending, lower block first on ties; blocks with no candidate
+    are never chosen) -> the candidate positions of those blocks, ascending, padded with -1
+    to n_blocks*block.  Returns (blocks [..., n_blocks] ascending, -1 padded, pool [...,
+    n_blocks*block])."""
+    s = np.asarray(scores, np.float64)
+    lead, n = s.shape[:-1], s.shape[-1]
+    blocks = topk_indices(block_scores(s, block), n_blocks)             # ascending block indices
+    flat_s = s.reshape(-1, n)
+    flat_b = blocks.reshape(-1, n_blocks)
+    pool = np.full((flat_s.shape[0], n_blocks * block), -1, np.int64)
+    for r in range(flat_s.shape[0]):
+        pos = [int(bk) * block + j for bk in flat_b[r] if bk >= 0 for j in range(block)
+               if int(bk) * block + j < n and flat_s[r, int(bk) * block + j] > -np.inf]
+        pool[r, :len(pos)] = pos
+    return blocks, pool.reshape(lead + (n_blocks * block,))
+
+
+def pool_scores(qI, w, KI, pool, q_pos, m: int):
+    """Reindex scores ([V4-CSA2] sections 11 and 15.2: gather the pool's keys, then score):
+    I[b,s,e] = sum_h w[b,s,h] * ReLU(qI[b,s,h] . KI[b, pool[b,s,e]]) for a visible pool
+    position, -inf for padding (-1) or positions the query may not see."""
+    qI = np.asarray(qI, np.float64); w = np.asarray(w, np.float64); KI = np.asarray(KI, np.float64)
+    pool = np.asarray(pool)
+    B, S = qI.shape[:2]
+    n_c = KI.shape[1]
+    out = np.full(pool.shape, -np.inf)
+    for b in range(B):
+        for s in range(S):
+            nv = int(visible_entries(np.asarray(q_pos)[b, s], m, n_c))
+            for e, p in enumerate(pool[b, s]):
+                if 0 <= p < nv:
+                    out[b, s, e] = float(np.dot(w[b, s], np.maximum(qI[b, s] @ KI[b, p], 0.0)))
+    return out
+
+
+def reindex_topk(qI, w, KI, pool, q_pos, m: int, k: int):
+    """A Reindex layer's selection: its own top-k over the pool (ties to the lower
+    position), returned as positions, ascending, -1 padded."""
+    sc = pool_scores(qI, w, KI, pool, q_pos, m)
+    sel = topk_indices(sc, k)                                          # indices into the pool
+    pool = np.asarray(pool)
+    return np.where(sel >= 0, np.take_along_axis(pool, np.maximum(sel, 0), axis=-1), -1)

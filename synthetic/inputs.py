@@ -367,3 +367,17 @@ def decode_layer_inputs(seed: int, B: int, d: int, m: int, c: int, d_I: int, sig
         "W_idx_t_bf16": to_bf16_bits(gaussian(rs[4], (4 * d_I, d), sigma_w)),
         "B_idx": gaussian(rs[5], (2, m, d_I), sigma_w),
     }
+
+
+def csa2_inputs(seed: int, B: int, T: int, d: int, m: int, c: int, d_I: int, sigma_w: float = 0.05,
+                bf16: bool = True) -> dict:
+    """CSA2 compressor inputs: hidden N(0,1), W_kv and W_gate [d, c] (no gate for m = 1) and
+    W_k [c, d_I], all N(0, sigma_w) with W_k scaled by sqrt(d / c) (it reads the unit-RMS
+    latent, not the hidden state); bf16 bit patterns, or fp32 with bf16=False."""
+    rs = _streams(seed, 4)
+    cast = to_bf16_bits if bf16 else (lambda x: np.ascontiguousarray(x, np.float32))
+    a = {"hidden": cast(gaussian(rs[0], (B, T, d))),
+         "W_kv": cast(gaussian(rs[1], (d, c), sigma_w)),
+         "W_gate": cast(gaussian(rs[2], (d, c), sigma_w)) if m > 1 else None,
+         "W_k": cast(gaussian(rs[3], (c, d_I), sigma_w * np.sqrt(d / c)))}
+    return a
