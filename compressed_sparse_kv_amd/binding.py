@@ -32,6 +32,7 @@ EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "c
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
+           "csa_index_score_segments_bmax", "csa_index_pool_segments_size", "csa_index_score_pool",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc_max_bytes", "csa_sparse_attn_noalloc")
@@ -69,6 +70,9 @@ def _load() -> ctypes.CDLL:
         "csa_index_keys_b16": ([vp, vp, i, i, vp], i),
         "csa_index_score_segments_b16": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_merge": ([vp, sz, i, i, i, i, vp, vp], i),
+        "csa_index_score_segments_bmax": ([vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp, vp], i),
+        "csa_index_pool_segments_size": ([i, i, i, i], sz),
+        "csa_index_score_pool": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
@@ -286,6 +290,35 @@ def csa_index_score_segments(q, q_scale, w, k_codes, k_scale, q_pos, *, m: int, 
     _check("csa_index_score_segments", _lib.csa_index_score_segments(
         _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores),
         _p(cand), cand.numel() * cand.element_size(), _stream(stream)))
+    return cand
+
+
+def csa_index_score_segments_bmax(q, q_scale, w, k_keys, k_scale, q_pos, *, m: int, k: int, cand, block_max,
+                                  Nc: int, layout: int = CSA_LAYOUT_ROWS, scores=None, stream=None):
+    """The Full layer of the hierarchical indexer: segment candidates (and scores) plus the
+    block-of-8 maxima block_max [B,S,ceil(Nc/8)] fp32."""
+    _dev(q, q_scale, w, k_keys, k_scale, q_pos, cand, block_max, scores)
+    B, S, H, D = q.shape
+    _check("csa_index_score_segments_bmax", _lib.csa_index_score_segments_bmax(
+        _p(q), _p(q_scale), _p(w), _p(k_keys), int(layout), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores),
+        _p(cand), cand.numel() * cand.element_size(), _p(block_max), _stream(stream)))
+    return cand
+
+
+def index_pool_segments_size(B, S, n_blocks, k) -> int:
+    return int(_lib.csa_index_pool_segments_size(B, S, n_blocks, k))
+
+
+def csa_index_score_pool(q, q_scale, w, k_codes, k_scale, q_pos, blocks, *, m: int, k: int, cand, scores=None,
+                         stream=None):
+    """A Reindex layer over the pool blocks [B,S,n_blocks] int32: segment candidates (key,
+    position) of the pool's 8*n_blocks entries (and their scores in pool order)."""
+    _dev(q, q_scale, w, k_codes, k_scale, q_pos, blocks, cand, scores)
+    B, S, H, D = q.shape
+    Nc, n_blocks = k_codes.shape[1], blocks.shape[-1]
+    _check("csa_index_score_pool", _lib.csa_index_score_pool(
+        _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), _p(q_pos), _p(blocks), n_blocks, B, S, H, D, Nc, m, k,
+        _p(scores), _p(cand), cand.numel() * cand.element_size(), _stream(stream)))
     return cand
 
 

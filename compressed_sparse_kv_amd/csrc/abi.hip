@@ -31,7 +31,9 @@ int index_topk_segments(int);
 int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
                       int, int, int, float*, int32_t*, void*, hipStream_t);
 int launch_index_segments(const void*, const float*, const float*, const void*, const float*, const int64_t*, int,
-                          int, int, int, int, float*, uint2*, hipStream_t, bool);
+                          int, int, int, int, float*, uint2*, hipStream_t, bool, float*);
+int launch_index_pool(const void*, const float*, const float*, const void*, const float*, const int64_t*,
+                      const int32_t*, int, int, int, int, int, int, float*, uint2*, hipStream_t);
 size_t index_keys_b16_bytes(int, int);
 int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
 int launch_topk_merge(uint2*, int, int, int, int32_t*, hipStream_t);
@@ -224,7 +226,8 @@ size_t csa_index_segments_size(int B, int S, int Nc, int k) {
 
 static int index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
                                 const float* k_scale, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc,
-                                int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream, bool b16) {
+                                int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream, bool b16,
+                                float* bmax = nullptr) {
   CSA_REQUIRE(q && q_scale && w && k_codes && k_scale && q_pos && cand);
   CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0 && k >= 1 && k <= 2048);
   const int64_t rows = static_cast<int64_t>(B) * S;
@@ -233,7 +236,7 @@ static int index_score_segments(const void* q, const float* q_scale, const float
   if (H_I != 64 || d_I != 128 || !index_topk_fused_ok(S, Nc, k)) return CSA_ERR_UNSUPPORTED;
   if (cand_bytes < csa_index_segments_size(B, S, Nc, k)) return CSA_ERR_WORKSPACE;
   return launch_index_segments(q, q_scale, w, k_codes, k_scale, q_pos, B, S, Nc, m, k, scores,
-                               static_cast<uint2*>(cand), as_stream(stream), b16);
+                               static_cast<uint2*>(cand), as_stream(stream), b16, bmax);
 }
 
 int csa_index_score_segments(const void* q, const float* q_scale, const float* w, const void* k_codes,
@@ -248,6 +251,35 @@ int csa_index_score_segments_b16(const void* q, const float* q_scale, const floa
                                  int m, int k, float* scores, void* cand, size_t cand_bytes, void* stream) {
   return index_score_segments(q, q_scale, w, k_blocks, k_scale, q_pos, B, S, H_I, d_I, Nc, m, k, scores, cand,
                               cand_bytes, stream, true);
+}
+
+int csa_index_score_segments_bmax(const void* q, const float* q_scale, const float* w, const void* k_keys,
+                                  int k_layout, const float* k_scale, const int64_t* q_pos, int B, int S, int H_I,
+                                  int d_I, int Nc, int m, int k, float* scores, void* cand, size_t cand_bytes,
+                                  float* block_max, void* stream) {
+  CSA_REQUIRE(block_max && (k_layout == CSA_LAYOUT_ROWS || k_layout == CSA_LAYOUT_B16));
+  return index_score_segments(q, q_scale, w, k_keys, k_scale, q_pos, B, S, H_I, d_I, Nc, m, k, scores, cand,
+                              cand_bytes, stream, k_layout == CSA_LAYOUT_B16, block_max);
+}
+
+size_t csa_index_pool_segments_size(int B, int S, int n_blocks, int k) {
+  if (n_blocks <= 0 || n_blocks > (1 << 26)) return 0;
+  return csa_index_segments_size(B, S, 8 * n_blocks, k);
+}
+
+int csa_index_score_pool(const void* q, const float* q_scale, const float* w, const void* k_codes,
+                         const float* k_scale, const int64_t* q_pos, const int32_t* blocks, int n_blocks, int B, int S,
+                         int H_I, int d_I, int Nc, int m, int k, float* scores, void* cand, size_t cand_bytes,
+                         void* stream) {
+  CSA_REQUIRE(q && q_scale && w && k_codes && k_scale && q_pos && blocks && cand);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0 && k >= 1 && k <= 2048 && n_blocks > 0 && n_blocks <= (1 << 26));
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * 8 * n_blocks < (int64_t{1} << 40));
+  CSA_REQUIRE(aligned16(cand));
+  if (H_I != 64 || d_I != 128 || !index_topk_fused_ok(S, 8 * n_blocks, k)) return CSA_ERR_UNSUPPORTED;
+  if (cand_bytes < csa_index_pool_segments_size(B, S, n_blocks, k)) return CSA_ERR_WORKSPACE;
+  return launch_index_pool(q, q_scale, w, k_codes, k_scale, q_pos, blocks, n_blocks, B, S, Nc, m, k, scores,
+                           static_cast<uint2*>(cand), as_stream(stream));
 }
 
 size_t csa_index_keys_b16_size(int B, int Nc) {

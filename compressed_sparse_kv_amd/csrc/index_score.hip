@@ -131,11 +131,21 @@ template <bool kTopk> constexpr int dec_entries() { return dec_waves<kTopk>() * 
 // kB16: the keys are stored in blocks of 16 entries (index_keys_b16 below), so that each
 // quarter-wave's load is 512 contiguous bytes already in the MFMA layout; one group is
 // then kept in flight instead of two.
-template <bool kTopk, bool kB16 = false>
+// kBmax: the maxima of the row's scores over blocks of 8 entries (-inf where a block has
+// no visible entry) also go to bmax [row][ceil(Nc/8)] (the Full layer of the hierarchical
+// indexer, [V4-CSA2] section 11); 8 consecutive lanes hold a block's scores.
+// kPool: the entries scanned are a candidate pool of 8 * n_blk positions, pool entry e
+// being position 8 * blk[row][e / 8] + e % 8 (blk = -1: no position); keys are gathered
+// from the row-major cache by position (gather, then score: a Reindex layer, [V4-CSA2]
+// sections 11 and 15.2).  Scores are written in pool order; candidate pairs carry the
+// position.
+template <bool kTopk, bool kB16 = false, bool kPool = false, bool kBmax = false>
 __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decode(
     const uint8_t* __restrict__ q8, const float* __restrict__ qs, const float* __restrict__ w,
     const uint8_t* __restrict__ k8, const float* __restrict__ ks, const int64_t* __restrict__ q_pos,
-    int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand, size_t cand_stride) {
+    int S, int Nc, int m, float* __restrict__ scores, int ktop, uint2* __restrict__ cand, size_t cand_stride,
+    float* __restrict__ bmax = nullptr, const int32_t* __restrict__ pool_blk = nullptr, int n_blk = 0) {
+  static_assert(!(kPool && kB16), "pool positions are gathered from the row-major cache");
   constexpr int kDecWaves = dec_waves<kTopk>();
   constexpr int kDecThreads = kDecWaves * 64;
   constexpr int kDecEntWG = dec_entries<kTopk>();
@@ -145,10 +155,23 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
   const int wave = threadIdx.x >> 6;
   const int64_t t = q_pos[row];
   const int nvis = static_cast<int>(min(static_cast<int64_t>(Nc), (t + 1) / m));
+  const int n_ent = kPool ? 8 * n_blk : Nc;          // entries of the row scanned
 
   const uint8_t* kb = k8 + static_cast<size_t>(b) * (kB16 ? cdiv(Nc, 16) * 16 : Nc) * kID;
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
-  float* out = scores ? scores + row * Nc : nullptr;
+  float* out = scores ? scores + row * n_ent : nullptr;
+  const int32_t* pb = kPool ? pool_blk + row * n_blk : nullptr;
+  // position of (pool) entry e, e < n_ent; -1 when the pool has no position there
+  auto pos_of = [&](int e) -> int {
+    if constexpr (kPool) {
+      const int bk = pb[e >> 3];
+      return bk >= 0 ? 8 * bk + (e & 7) : -1;
+    } else {
+      return e;
+    }
+  };
+  // the cache row a load of entry e reads (clamped: never outside the cache)
+  auto load_row = [&](int e) -> int { return min(max(pos_of(min(e, n_ent - 1)), 0), Nc - 1); };
 
   // group gi of this wave covers entries base + 64*(gi*kDecWaves + wave) .. +63; the keys of
   // the next two groups are in flight while a group is multiplied
@@ -165,10 +188,10 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
 #define CSA_DEC_LOAD(gi_)                                                                           \
   do {                                                                                              \
     _Pragma("unroll") for (int nb = 0; nb < 4; ++nb) {                                              \
-      const int e_ = min(group_e0(gi_) + 16 * nb + (l & 15), Nc - 1);                               \
+      const int e_ = load_row(group_e0(gi_) + 16 * nb + (l & 15));                                  \
       ring[(gi_) % kRingD][nb] = *reinterpret_cast<const v8i*>(kb + key_off(e_));                   \
     }                                                                                               \
-    sring[(gi_) % kRingD] = ksb[min(group_e0(gi_) + l, Nc - 1)];                                    \
+    sring[(gi_) % kRingD] = ksb[load_row(group_e0(gi_) + l)];                                       \
   } while (0)
   // The query (64 x 128 codes, 8 KiB), its head weights and scales are read once per
   // workgroup, ahead of the keys, and shared through LDS: loads complete in order, so a
@@ -225,10 +248,23 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
       p[nb] = head_sum1(a, bk, wv);
     }
     const float v = reduce_scatter4(p) * sring[gi % kRingD];
-    const bool vis = e < nvis;
-    if (out && e < Nc) out[e] = vis ? v : -INFINITY;
+    bool vis;
+    if constexpr (kPool) {
+      const int pe = e < n_ent ? pos_of(e) : -1;
+      vis = pe >= 0 && pe < nvis;
+    } else {
+      vis = e < nvis;
+    }
+    if (out && e < n_ent) out[e] = vis ? v : -INFINITY;
     const uint32_t key = vis ? score_key(v) : 0u;
     if (kTopk) kst[64 * (gi * kDecWaves + wave) + l] = key;
+    if constexpr (kBmax) {
+      float bm = vis ? v : -INFINITY;
+      bm = fmaxf(bm, __shfl_xor(bm, 1, kWave));
+      bm = fmaxf(bm, __shfl_xor(bm, 2, kWave));
+      bm = fmaxf(bm, __shfl_xor(bm, 4, kWave));
+      if ((l & 7) == 0 && e < Nc) bmax[row * static_cast<size_t>(cdiv(Nc, 8)) + (e >> 3)] = bm;
+    }
   }
 #undef CSA_DEC_LOAD
   if (kTopk) {
@@ -243,9 +279,14 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     const int kk = select_regs<kDecThreads, 8, 1>(sh, key, ktop, taken, obase);
     uint2* dst = cand + row * cand_stride + blockIdx.x * static_cast<size_t>(ktop);
     int o = obase[0];
+    // the entries 8*tid .. 8*tid+7 of the segment: one block of 8 (positions from the pool)
+    int e8 = base + 8 * static_cast<int>(threadIdx.x);
+    if constexpr (kPool) {
+      if (taken != 0ull) e8 = 8 * pb[min(e8, n_ent - 1) >> 3];
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
-      if ((taken >> s2) & 1ull) dst[o++] = make_uint2(key[0][s2], static_cast<uint32_t>(base + 8 * threadIdx.x + s2));
+      if ((taken >> s2) & 1ull) dst[o++] = make_uint2(key[0][s2], static_cast<uint32_t>(e8 + s2));
     for (int p = kk + static_cast<int>(threadIdx.x); p < ktop; p += kDecThreads) dst[p] = make_uint2(0u, 0u);
   }
 }
@@ -395,7 +436,7 @@ int launch_index_score(const void* q, const float* q_scale, const float* w, cons
       dim3 grid(cdiv(Nc, dec_entries<false>()), B * S);
       hipLaunchKernelGGL(index_score_fp8_decode<false>, grid, dim3(dec_waves<false>() * 64), 0, st,
                          static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k),
-                         k_scale, q_pos, S, Nc, m, scores, 0, nullptr, size_t{0});
+                         k_scale, q_pos, S, Nc, m, scores, 0, nullptr, size_t{0}, nullptr, nullptr, 0);
     } else {
       dim3 grid(cdiv(S, kPfQ), B);
       hipLaunchKernelGGL(index_score_fp8_prefill, grid, dim3(kPfThreads), 0, st,
@@ -425,20 +466,44 @@ bool index_topk_fused_ok(int S, int Nc, int k) {
 }
 
 // Scores (optional) and every segment's top-k as (key, entry) pairs in cand[rows][G][k];
-// b16: the keys in 16-entry blocks.
+// b16: the keys in 16-entry blocks; bmax (optional): the block-of-8 maxima of the scores.
 int launch_index_segments(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
                           const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, uint2* cand,
-                          hipStream_t st, bool b16) {
+                          hipStream_t st, bool b16, float* bmax) {
   dim3 grid(index_topk_segments(Nc), B * S);
   const size_t stride = topk_merge_pairs_per_row(index_topk_segments(Nc), ktop);
-  if (b16)
-    hipLaunchKernelGGL((index_score_fp8_decode<true, true>), grid, dim3(dec_waves<true>() * 64), 0, st,
-                       static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S,
-                       Nc, m, scores, ktop, cand, stride);
+  const uint8_t* q8 = static_cast<const uint8_t*>(q);
+  const uint8_t* k8 = static_cast<const uint8_t*>(k);
+  const dim3 block(dec_waves<true>() * 64);
+  if (b16 && bmax)
+    hipLaunchKernelGGL((index_score_fp8_decode<true, true, false, true>), grid, block, 0, st, q8, q_scale, w, k8,
+                       k_scale, q_pos, S, Nc, m, scores, ktop, cand, stride, bmax, nullptr, 0);
+  else if (bmax)
+    hipLaunchKernelGGL((index_score_fp8_decode<true, false, false, true>), grid, block, 0, st, q8, q_scale, w, k8,
+                       k_scale, q_pos, S, Nc, m, scores, ktop, cand, stride, bmax, nullptr, 0);
+  else if (b16)
+    hipLaunchKernelGGL((index_score_fp8_decode<true, true>), grid, block, 0, st, q8, q_scale, w, k8, k_scale, q_pos,
+                       S, Nc, m, scores, ktop, cand, stride, nullptr, nullptr, 0);
   else
-    hipLaunchKernelGGL((index_score_fp8_decode<true, false>), grid, dim3(dec_waves<true>() * 64), 0, st,
-                       static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S,
-                       Nc, m, scores, ktop, cand, stride);
+    hipLaunchKernelGGL((index_score_fp8_decode<true, false>), grid, block, 0, st, q8, q_scale, w, k8, k_scale, q_pos,
+                       S, Nc, m, scores, ktop, cand, stride, nullptr, nullptr, 0);
+  CSA_LAUNCH_CHECK();
+  return CSA_OK;
+}
+
+// Reindex over a candidate pool of 8 * n_blk positions (blocks [rows][n_blk] of 8
+// positions, -1 = none): scores of the pool (optional, pool order) and each 4096-entry
+// segment's top-k as (key, position) pairs, as launch_index_segments writes them for a row
+// of 8 * n_blk entries.
+int launch_index_pool(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
+                      const int64_t* q_pos, const int32_t* blocks, int n_blk, int B, int S, int Nc, int m, int ktop,
+                      float* scores, uint2* cand, hipStream_t st) {
+  const int P = 8 * n_blk;
+  dim3 grid(index_topk_segments(P), B * S);
+  const size_t stride = topk_merge_pairs_per_row(index_topk_segments(P), ktop);
+  hipLaunchKernelGGL((index_score_fp8_decode<true, false, true, false>), grid, dim3(dec_waves<true>() * 64), 0, st,
+                     static_cast<const uint8_t*>(q), q_scale, w, static_cast<const uint8_t*>(k), k_scale, q_pos, S,
+                     Nc, m, scores, ktop, cand, stride, nullptr, blocks, n_blk);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }
@@ -472,7 +537,8 @@ int launch_index_topk(const void* q, const float* q_scale, const float* w, const
                       const int64_t* q_pos, int B, int S, int Nc, int m, int ktop, float* scores, int32_t* idx,
                       void* ws, hipStream_t st) {
   uint2* cand = static_cast<uint2*>(ws);
-  const int rc = launch_index_segments(q, q_scale, w, k, k_scale, q_pos, B, S, Nc, m, ktop, scores, cand, st, false);
+  const int rc = launch_index_segments(q, q_scale, w, k, k_scale, q_pos, B, S, Nc, m, ktop, scores, cand, st, false,
+                                       nullptr);
   if (rc != CSA_OK) return rc;
   return launch_topk_merge(cand, B * S, index_topk_segments(Nc), ktop, idx, st);
 }

@@ -277,6 +277,42 @@ int csa_index_score_segments_b16(const void* q, const float* q_scale, const floa
                                  float* scores, void* cand, size_t cand_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * The CSA2 hierarchical indexer ([V4-CSA2] section 11): the Full layer scores every entry,
+ * keeps its own top-k, and scores blocks of 8 consecutive entries by their best entry; the
+ * 2048 best blocks form a candidate pool of at most 16384 positions (11.1: a recall set
+ * larger than top-k, so deeper layers can choose differently); each Reindex layer gathers
+ * the pool's keys and scores them with its own query (gather, then score: sections 11 and
+ * 15.2), and takes its own top-k.
+ *
+ * csa_index_score_segments_bmax: csa_index_score_segments (k_layout CSA_LAYOUT_ROWS, keys
+ *   [B,Nc,128]) or csa_index_score_segments_b16 (CSA_LAYOUT_B16), the same scores and
+ *   candidate pairs, and block_max [B,S,ceil(Nc/8)] fp32: the largest score of entries
+ *   8j .. 8j+7 that the query sees, -inf for a block with none.  The pool's blocks are then
+ *   csa_topk(block_max, k = n_blocks) (ascending block indices, -1 padded).
+ * csa_index_score_pool: for the pool of blocks [B,S,n_blocks] int32 (block j = entries
+ *   8j .. 8j+7; -1 = none) the pool's 8*n_blocks entries, pool entry e being position
+ *   8*blocks[e/8] + e%8, scored as csa_index_score scores that position (-inf for no
+ *   position or one the query does not see); scores [B,S,8*n_blocks] (pool order) or NULL;
+ *   cand: the pairs of csa_index_score_segments for a row of 8*n_blocks entries, each pair
+ *   carrying the POSITION (>= csa_index_pool_segments_size(B, S, n_blocks, k) bytes).
+ *   csa_topk_merge(cand, ..., Nc = 8*n_blocks, k) then gives the Reindex layer's top-k as
+ *   positions, ascending (ties to the lower position when the blocks are ascending).
+ *   Keys row-major [B,Nc,128] FP8; decode shapes as csa_index_score_segments.
+ * ------------------------------------------------------------------------------ */
+int csa_index_score_segments_bmax(const void* q, const float* q_scale, const float* w, const void* k_keys,
+                                  int k_layout, const float* k_scale, const int64_t* q_pos,
+                                  int B, int S, int H_I, int d_I, int Nc, int m, int k,
+                                  float* scores, void* cand, size_t cand_bytes, float* block_max,
+                                  void* stream);
+
+size_t csa_index_pool_segments_size(int B, int S, int n_blocks, int k);
+
+int csa_index_score_pool(const void* q, const float* q_scale, const float* w, const void* k_codes,
+                         const float* k_scale, const int64_t* q_pos, const int32_t* blocks,
+                         int n_blocks, int B, int S, int H_I, int d_I, int Nc, int m, int k,
+                         float* scores, void* cand, size_t cand_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 3: top-k selection.  [KV-COMP] sections 9.4 (S_t = TopK_k of the scores)
  * and 9.8 (invisible entries carry -inf and come out as -1).
  *
