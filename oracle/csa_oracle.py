@@ -578,3 +578,128 @@ def reindex_topk(qI, w, KI, pool, q_pos, m: int, k: int):
     sel = topk_indices(sc, k)                                          # indices into the pool
     pool = np.asarray(pool)
     return np.where(sel >= 0, np.take_along_axis(pool, np.maximum(sel, 0), axis=-1), -1)
+
+
+# ---------------------------------------------------------------------------
+# Low-precision cache formats: FP4 E2M1 with E8M0 (per 32) or E4M3 (per 16) scales,
+# FP8 entries with bf16 RoPE channels, bf16 index scores
+# ---------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+
+
+def e2m1_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP E2M1 (FP4) codes 0..15 -> values: 1 sign bit, 2 exponent bits (bias 1), 1
+    mantissa bit; exponent field 0 is subnormal (0 or 0.5).  Magnitudes 0, 0.5, 1, 1.5, 2,
+    3, 4, 6; no infinity or NaN."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e, mt = (c >> 1) & 0x3, (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, mt * 0.5, (1.0 + mt * 0.5) * np.exp2(e - 1.0))
+    return sign * mag
+
+
+def f64_to_e2m1(x: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (ties to the code with an even mantissa bit), saturating at 6,
+    by brute force over the 8 non-negative codes; zero keeps its sign."""
+    x = np.asarray(x, np.float64)
+    codes = np.arange(8)
+    vals = e2m1_to_f64(codes)
+    mag = np.minimum(np.abs(x), E2M1_MAX)
+    d = np.abs(mag[..., None] - vals)
+    tied = d == d.min(axis=-1, keepdims=True)
+    even = tied & (codes % 2 == 0)
+    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1))
+    return (codes[pick] | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def e8m0_to_f64(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> 2^(e - 127) (255 = NaN)."""
+    e = np.asarray(e).astype(np.float64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def quantize_mxfp4(x: np.ndarray, block: int = 32):
+    """MXFP4 quantisation of rows ([V4-CSA2] section 16.2: E2M1 values, one E8M0 scale per
+    32; the conversion follows the OCP microscaling format definition): per block, the
+    shared exponent is floor(log2(amax)) - 2 (2 = the largest E2M1 exponent), clamped to
+    the E8M0 range, and every value becomes the nearest E2M1 code of x / 2^exponent
+    (saturating).  An all-zero block gets the smallest scale and zero codes.  Returns
+    (codes [..., n] one code per value, scales [..., n/block] E8M0 bytes)."""
+    x = np.asarray(x, np.float64)
+    lead, n = x.shape[:-1], x.shape[-1]
+    xb = x.reshape(lead + (n // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2.0, -127.0)
+    ex = np.clip(ex, -127.0, 127.0)
+    codes = f64_to_e2m1(xb / np.exp2(ex)[..., None]).reshape(lead + (n,))
+    return codes, (ex + 127.0).astype(np.uint8)
+
+
+def dequant_mxfp4(codes, scales, block: int = 32):
+    v = e2m1_to_f64(codes)
+    n = v.shape[-1]
+    s = e8m0_to_f64(scales)
+    return (v.reshape(v.shape[:-1] + (n // block, block)) * s[..., None]).reshape(v.shape)
+
+
+def quantize_fp4_e4m3(x: np.ndarray, block: int = 16):
+    """FP4 main-KV quantisation ([V4-CSA2] section 16.1; [ATTN-CMP] section on CSA2: E2M1
+    values with one E4M3 scale per 16 channels): per block the scale is amax/6 (the largest
+    E2M1 magnitude) rounded to the nearest E4M3 code, and every value becomes the nearest
+    E2M1 code of x / scale (saturating).  A block whose scale rounds to 0 gets zero codes.
+    Returns (codes [..., n], scales [..., n/block] E4M3 bytes)."""
+    x = np.asarray(x, np.float64)
+    lead, n = x.shape[:-1], x.shape[-1]
+    xb = x.reshape(lead + (n // block, block))
+    sc = f64_to_e4m3fn(np.abs(xb).max(axis=-1) / E2M1_MAX)
+    s = e4m3fn_to_f64(sc)
+    safe = np.where(s > 0, s, 1.0)
+    codes = np.where(s[..., None] > 0, f64_to_e2m1(xb / safe[..., None]), 0).astype(np.uint8)
+    return codes.reshape(lead + (n,)), sc
+
+
+def dequant_fp4_e4m3(codes, scales, block: int = 16):
+    v = e2m1_to_f64(codes)
+    n = v.shape[-1]
+    s = e4m3fn_to_f64(scales)
+    return (v.reshape(v.shape[:-1] + (n // block, block)) * s[..., None]).reshape(v.shape)
+
+
+def quantize_fp8_rope_split(x: np.ndarray, d_rope: int):
+    """The split entry ([ATTN-CMP] section "CSA（DeepSeek-V4）": the c - d_rope channels
+    without RoPE in FP8, the d_rope RoPE channels in bf16): the FP8 part is quantised with
+    one power-of-two scale per entry, 2^ceil(log2(amax/448)) (the smallest that avoids
+    saturation), so that code * scale is exact in bf16; the RoPE part is rounded to bf16
+    (RNE).  Returns (codes [..., c - d_rope] e4m3, exponent [...] int, rope bf16 bit
+    patterns [..., d_rope])."""
+    x = np.asarray(x, np.float64)
+    c = x.shape[-1]
+    main, rp = x[..., :c - d_rope], x[..., c - d_rope:]
+    amax = np.abs(main).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        ex = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / E4M3_MAX)), -127.0)
+    codes = f64_to_e4m3fn(main / np.exp2(ex)[..., None])
+    # RoPE channels: the nearest bf16 (8 significant bits, ties to even), from the real value
+    mant, e2 = np.frexp(rp)
+    rq = np.ldexp(np.rint(mant * 256.0), e2 - 8)
+    rope_bits = (rq.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return codes, ex.astype(np.int64), rope_bits
+
+
+def dequant_fp8_rope_split(codes, ex, rope_bits):
+    return np.concatenate([e4m3fn_to_f64(codes) * np.exp2(np.asarray(ex, np.float64))[..., None],
+                           bf16_bits_to_f64(rope_bits)], axis=-1)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """An index score as the pages cast it ([KV-COMP] section 7: scores quantised from FP32
+    to BF16 before the top-k): the value as fp32 (nearest), then the nearest bf16 (ties to
+    even), back in float64; -inf stays -inf."""
+    x = np.asarray(x, np.float64)
+    fin = np.isfinite(x)
+    r32 = np.where(fin, x, 0.0).astype(np.float32)
+    u = r32.view(np.uint32).astype(np.uint64)
+    b = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+    return np.where(fin, b.view(np.float32).astype(np.float64), x)

@@ -1,0 +1,98 @@
+"""Pins of the oracle's low-precision formats (CPU only): the E2M1 and E8M0 tables of the OCP
+microscaling formats, round-to-nearest-even ties, the MX shared-exponent rule and its
+saturation bound, the E4M3-scaled FP4 blocks, the FP8 + bf16 split entry (exact round
+trip of values on its grid, no saturation) and the bf16 cast of scores (ties, and torch's
+own bfloat16 cast of the same fp32 values)."""
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import csa_oracle as O
+
+
+def test_e2m1_table_and_ties():
+    assert np.array_equal(O.e2m1_to_f64(np.arange(8)), [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    assert np.array_equal(O.e2m1_to_f64(np.arange(8, 16)), -np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6]))
+    # ties go to the even mantissa bit; beyond 6 saturates; the sign is kept
+    x = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 100.0, -0.75, -5.0])
+    want = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, 6.0, -1.0, -4.0])
+    assert np.array_equal(O.e2m1_to_f64(O.f64_to_e2m1(x)), want)
+    # every code round-trips
+    assert np.array_equal(O.f64_to_e2m1(O.e2m1_to_f64(np.arange(16)))[1:], np.arange(1, 16))
+
+
+def test_e8m0_scale_bytes():
+    assert np.array_equal(O.e8m0_to_f64(np.array([127, 128, 126, 0, 254])),
+                          [1.0, 2.0, 0.5, 2.0 ** -127, 2.0 ** 127])
+    assert math.isnan(O.e8m0_to_f64(np.array([255]))[0])
+
+
+def test_mxfp4_shared_exponent_and_error_bound():
+    # block amax 6 -> exponent floor(log2 6) - 2 = 0: values on the E2M1 grid stay exact
+    x = np.zeros(32); x[:8] = [6, 3, 0.5, -1.5, 4, 2, 1, -6]
+    codes, sc = O.quantize_mxfp4(x[None])
+    assert sc[0, 0] == 127 and np.array_equal(O.dequant_mxfp4(codes, sc)[0], x)
+    # amax in [2^e, 2^(e+1)) -> scale 2^(e-2); x / scale < 8, so saturation costs at most
+    # 2 * scale and everything else at most half a grid step (scale * 1 at the top binade)
+    rng = np.random.default_rng(50)
+    x = rng.normal(size=(200, 128)) * np.exp2(rng.integers(-8, 8, size=(200, 1)))
+    codes, sc = O.quantize_mxfp4(x)
+    s = O.e8m0_to_f64(sc)
+    amax = np.abs(x.reshape(200, 4, 32)).max(axis=-1)
+    assert np.all(s == np.exp2(np.floor(np.log2(amax)) - 2))
+    err = np.abs(O.dequant_mxfp4(codes, sc) - x).reshape(200, 4, 32)
+    assert np.all(err <= 2 * s[..., None] + 1e-300)
+    inside = np.abs(x.reshape(200, 4, 32)) <= 6 * s[..., None]
+    assert np.all(err[inside] <= (np.abs(x.reshape(200, 4, 32)) / 4 + 0.25 * s[..., None])[inside])
+    # an all-zero block
+    codes, sc = O.quantize_mxfp4(np.zeros((1, 32)))
+    assert np.all(codes == 0) and np.all(O.dequant_mxfp4(codes, sc) == 0)
+
+
+def test_fp4_e4m3_blocks():
+    # amax 3 -> scale 3/6 = 0.5 (an exact E4M3 value): values on the grid round-trip
+    x = np.zeros(16); x[:6] = [3.0, -1.5, 0.25, 2.0, -0.5, 1.0]
+    codes, sc = O.quantize_fp4_e4m3(x[None])
+    assert O.e4m3fn_to_f64(sc)[0, 0] == 0.5
+    assert np.array_equal(O.dequant_fp4_e4m3(codes, sc)[0], x)
+    # random rows: the scale is the E4M3 rounding of amax / 6 and no value exceeds its block's
+    # reach by more than the E4M3 rounding of the scale allows
+    rng = np.random.default_rng(51)
+    x = rng.normal(size=(100, 512))
+    codes, sc = O.quantize_fp4_e4m3(x)
+    assert np.array_equal(sc, O.f64_to_e4m3fn(np.abs(x.reshape(100, 32, 16)).max(axis=-1) / 6))
+    rel = np.abs(O.dequant_fp4_e4m3(codes, sc) - x).max() / np.abs(x).max()
+    assert rel < 0.2
+    # 288 bytes per 512-channel entry: 256 of codes, 32 of scales
+    assert codes.shape[-1] // 2 + sc.shape[-1] == 288
+
+
+def test_fp8_rope_split_entry():
+    rng = np.random.default_rng(52)
+    x = rng.normal(size=(50, 512))
+    codes, ex, rope = O.quantize_fp8_rope_split(x, 64)
+    # power-of-two scale: the smallest with no saturation
+    amax = np.abs(x[:, :448]).max(axis=-1)
+    assert np.all(amax / np.exp2(ex) <= 448) and np.all(amax / np.exp2(ex - 1) > 448)
+    y = O.dequant_fp8_rope_split(codes, ex, rope)
+    assert np.array_equal(y[:, 448:], O.bf16_bits_to_f64(rope))
+    assert np.abs(y[:, 448:] - x[:, 448:]).max() <= np.abs(x[:, 448:]).max() * 2 ** -8
+    # values already on the grid come back exactly, and the dequantised values are bf16 numbers
+    back = O.quantize_fp8_rope_split(y, 64)
+    assert np.array_equal(O.dequant_fp8_rope_split(*back), y)
+    assert np.array_equal(O.round_bf16(y), y)
+    # 576 bytes of payload per entry: 448 codes + 64 bf16 channels
+    assert codes.shape[-1] + 2 * rope.shape[-1] == 576
+
+
+def test_bf16_cast_of_scores():
+    one = 1.0
+    assert O.round_bf16(np.array([one + 2 ** -8]))[0] == 1.0                      # tie -> even
+    assert O.round_bf16(np.array([one + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6         # tie -> even
+    assert O.round_bf16(np.array([-np.inf]))[0] == -np.inf
+    rng = np.random.default_rng(53)
+    x = rng.normal(size=10000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
