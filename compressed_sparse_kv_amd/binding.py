@@ -21,7 +21,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
 CSA_LAYOUT_ROWS, CSA_LAYOUT_B16 = 0, 1
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
           4: "CSA_ERR_HIP", 5: "CSA_ERR_SCRATCH"}
@@ -33,6 +33,7 @@ EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "c
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
            "csa_index_keys_b16_size", "csa_index_keys_b16", "csa_index_score_segments_b16",
            "csa_index_score_segments_bmax", "csa_index_pool_segments_size", "csa_index_score_pool",
+           "csa_index_score_mx",
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc_max_bytes", "csa_sparse_attn_noalloc")
@@ -72,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "csa_topk_merge": ([vp, sz, i, i, i, i, vp, vp], i),
         "csa_index_score_segments_bmax": ([vp, vp, vp, vp, i, vp, vp, i, i, i, i, i, i, i, vp, vp, sz, vp, vp], i),
         "csa_index_pool_segments_size": ([i, i, i, i], sz),
+        "csa_index_score_mx": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, i, vp, i, vp, sz, vp], i),
         "csa_index_score_pool": ([vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_workspace_size": ([i, i, i], sz),
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
@@ -303,6 +305,21 @@ def csa_index_score_segments_bmax(q, q_scale, w, k_keys, k_scale, q_pos, *, m: i
         _p(q), _p(q_scale), _p(w), _p(k_keys), int(layout), _p(k_scale), _p(q_pos), B, S, H, D, Nc, m, k, _p(scores),
         _p(cand), cand.numel() * cand.element_size(), _p(block_max), _stream(stream)))
     return cand
+
+
+def csa_index_score_mx(q, q_scale, w, k_codes, k_scale, q_pos, *, fp4: bool, m: int, scores=None, k: int = 0,
+                       cand=None, score_bf16: bool = False, stream=None):
+    """Index scores over MX caches: q [B,S,64,64 (FP4) or 128 (FP8)] uint8, q_scale [B,S,64,4]
+    E8M0, w [B,S,64], k_codes [B,Nc,64 or 128], k_scale [B,Nc,4]; scores [B,S,Nc] and/or the
+    segment top-k pairs in cand (decode shapes)."""
+    _dev(q, q_scale, w, k_codes, k_scale, q_pos, scores, cand)
+    B, S, H = q.shape[:3]
+    Nc = k_codes.shape[1]
+    _check("csa_index_score_mx", _lib.csa_index_score_mx(
+        _p(q), _p(q_scale), _p(w), _p(k_codes), _p(k_scale), CSA_FP4_E2M1 if fp4 else CSA_FP8_E4M3, _p(q_pos), B, S,
+        H, 128, Nc, m, int(score_bf16), _p(scores), int(k), _p(cand),
+        0 if cand is None else cand.numel() * cand.element_size(), _stream(stream)))
+    return scores if cand is None else cand
 
 
 def index_pool_segments_size(B, S, n_blocks, k) -> int:

@@ -35,6 +35,7 @@ def sources() -> list[str]:
 # the output rows) read results with VALU instructions, which would otherwise need one
 # accvgpr move per value.
 PER_FILE = {"index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "index_mx.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
             "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

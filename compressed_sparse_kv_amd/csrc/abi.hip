@@ -34,6 +34,8 @@ int launch_index_segments(const void*, const float*, const float*, const void*, 
                           int, int, int, int, float*, uint2*, hipStream_t, bool, float*);
 int launch_index_pool(const void*, const float*, const float*, const void*, const float*, const int64_t*,
                       const int32_t*, int, int, int, int, int, int, float*, uint2*, hipStream_t);
+int launch_index_mx(const void*, const void*, const float*, const void*, const void*, int, const int64_t*, int, int,
+                    int, int, int, float*, int, uint2*, hipStream_t);
 size_t index_keys_b16_bytes(int, int);
 int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
 int launch_topk_merge(uint2*, int, int, int, int32_t*, hipStream_t);
@@ -260,6 +262,27 @@ int csa_index_score_segments_bmax(const void* q, const float* q_scale, const flo
   CSA_REQUIRE(block_max && (k_layout == CSA_LAYOUT_ROWS || k_layout == CSA_LAYOUT_B16));
   return index_score_segments(q, q_scale, w, k_keys, k_scale, q_pos, B, S, H_I, d_I, Nc, m, k, scores, cand,
                               cand_bytes, stream, k_layout == CSA_LAYOUT_B16, block_max);
+}
+
+int csa_index_score_mx(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
+                       int elem_dtype, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc, int m,
+                       int score_bf16, float* scores, int k_top, void* cand, size_t cand_bytes, void* stream) {
+  CSA_REQUIRE(q && q_scale && w && k && k_scale && q_pos);
+  CSA_REQUIRE(elem_dtype == CSA_FP4_E2M1 || elem_dtype == CSA_FP8_E4M3);
+  CSA_REQUIRE(B > 0 && S > 0 && Nc > 0 && m > 0);
+  const int64_t rows = static_cast<int64_t>(B) * S;
+  CSA_REQUIRE(rows < (int64_t{1} << 31) && rows * Nc < (int64_t{1} << 40));
+  if (H_I != 64 || d_I != 128) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(q) && aligned16(k));
+  if (cand == nullptr) {
+    CSA_REQUIRE(scores != nullptr);
+  } else {
+    CSA_REQUIRE(k_top >= 1 && k_top <= 2048 && aligned16(cand));
+    if (!index_topk_fused_ok(S, Nc, k_top)) return CSA_ERR_UNSUPPORTED;
+    if (cand_bytes < csa_index_segments_size(B, S, Nc, k_top)) return CSA_ERR_WORKSPACE;
+  }
+  return launch_index_mx(q, q_scale, w, k, k_scale, elem_dtype == CSA_FP4_E2M1, q_pos, B, S, Nc, m, score_bf16 != 0,
+                         scores, k_top, static_cast<uint2*>(cand), as_stream(stream));
 }
 
 size_t csa_index_pool_segments_size(int B, int S, int n_blocks, int k) {

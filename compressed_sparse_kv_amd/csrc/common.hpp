@@ -20,13 +20,6 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));        // 4 bf16 bit patterns
 typedef unsigned v4u __attribute__((ext_vector_type(4)));     // 16 raw bytes
 
-// D(16x16, fp32) += A(16x128 e4m3) * B(128x16 e4m3).  Lane l holds row/column l%16 of
-// A/B and one 32-byte group (l/16) of the reduction index in both operands, so the
-// product pairs the same k-slots on both sides whatever the hardware order inside a group.
-__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
-
 // D(16x16, fp32) += A(16x32 bf16) * B(32x16 bf16); lane l: row/col l%16, k-group l/16.
 __device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8s& a, const v8s& b, const v4f& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),

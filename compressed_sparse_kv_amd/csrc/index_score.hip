@@ -25,12 +25,10 @@
 // 4 entry blocks at once (a reduce-scatter leaving lane l with entry e0+l of a 64-entry
 // group, so stores are coalesced).
 #include "common.hpp"
+#include "index_common.hpp"
 #include "select.hpp"
 
 namespace csa {
-
-constexpr int kIH = 64;    // indexer heads handled by the FP8-input kernels
-constexpr int kID = 128;   // indexer head dim handled by the FP8-input kernels
 
 // 32 e4m3 codes (8 dwords) -> 32 bf16 (4 MFMA operands of 8 values each), exactly.
 __device__ __forceinline__ void e4m3x32_to_bf16(const v8i& c, v8s out[4]) {
@@ -50,24 +48,6 @@ __device__ __forceinline__ void e4m3x32_to_bf16(const v8i& c, v8s out[4]) {
     out[ks] = __builtin_bit_cast(v8s, w);
   }
 }
-
-// p[nb] = partial head-sum of entry (lane&15) of block nb over this lane's heads.
-// Returns, in lane l, the full sum for entry 16*(l>>4) + (l&15) = l of the 4 blocks.
-// Two reduce-scatter steps on the gfx950 lane swaps, no LDS: v_permlane32_swap(x, y)
-// leaves x = [x.lo, y.lo] and y = [x.hi, y.hi] (32-lane halves), so x + y is, in the low
-// half, x + the high half's x and, in the high half, y + the low half's y; 16-lane rows
-// pair up the same way under v_permlane16_swap.
-__device__ __forceinline__ float reduce_scatter4(const float p[4]) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[2]), false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[1]), __float_as_uint(p[3]), false, false);
-  const float q0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);   // blocks 0 (low half), 2 (high half)
-  const float q1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);   // blocks 1, 3
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-// ReLU as one instruction: med3(x, 0, 3e38) (fmaxf would also emit a NaN-quieting max).
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
 
 // Weighted ReLU head-sum of one 16-entry block against the 4 head blocks of one query.
 // Each head block is a chain of 4 MFMAs followed by its 16 VALU epilogue operations; the
@@ -122,12 +102,6 @@ __device__ __forceinline__ void load_query(const uint8_t* __restrict__ q8, const
 // finishes (rows are cand_stride pairs apart: room for the merge's first level when there
 // are many segments).  Scores are then written only when `scores` is not null.
 // ------------------------------------------------------------------------------------
-constexpr int kDecGroups = 8;                         // 64-entry groups per wave
-// Waves per workgroup: 4 for scores alone (more workgroups for small grids), 8 with the
-// top-k epilogue (4096-entry segments: half the candidates for the row merge).
-template <bool kTopk> constexpr int dec_waves() { return kTopk ? 8 : 4; }
-template <bool kTopk> constexpr int dec_entries() { return dec_waves<kTopk>() * 64 * kDecGroups; }
-
 // kB16: the keys are stored in blocks of 16 entries (index_keys_b16 below), so that each
 // quarter-wave's load is 512 contiguous bytes already in the MFMA layout; one group is
 // then kept in flight instead of two.

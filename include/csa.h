@@ -54,7 +54,7 @@ typedef enum {
   CSA_ERR_SCRATCH = 5
 } csa_status;
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 } csa_dtype;
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3 } csa_dtype;
 
 /* Cache layouts of compressed entries: row-major [B, Nc, c], or (indexer keys, c = 128,
  * FP8 codes) the 16-entry blocks of csa_index_keys_b16. */
@@ -275,6 +275,29 @@ int csa_index_score_segments_b16(const void* q, const float* q_scale, const floa
                                  const void* k_blocks, const float* k_scale, const int64_t* q_pos,
                                  int B, int S, int H_I, int d_I, int Nc, int m, int k,
                                  float* scores, void* cand, size_t cand_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
+ * Index scores over microscaled caches ([V4-CSA2] sections 16.2 and 11.2: indexer keys of
+ * 128 FP4 E2M1 values with one E8M0 scale per 32, 68 bytes; [ATTN-CMP] section on CSA2: the
+ * indexer query in FP4 too; [KV-COMP] section 7: scores cast from FP32 to BF16 before the
+ * top-k).  The score is csa_index_score's over the dequantised values,
+ *   I[b,s,j] = sum_h w[b,s,h] * ReLU(q[b,s,h] . K[b,j])   (j < n_vis, else -inf),
+ * each value being code * 2^(scale byte - 127) of its block of 32.
+ *   elem_dtype CSA_FP4_E2M1: q [B,S,64,64] bytes (two codes per byte, the even value in the
+ *     low nibble), k [B,Nc,64] bytes; CSA_FP8_E4M3: q [B,S,64,128], k [B,Nc,128] codes.
+ *   q_scale [B,S,64,4], k_scale [B,Nc,4]: E8M0 bytes (block j = values 32j .. 32j+31).
+ *   H_I = 64, d_I = 128.  FP4 block sums are exact in the matrix unit (products are
+ *   multiples of 1/4); FP8 ones are not, so the FP8 form misses the 1e-5 bound of the
+ *   e4m3 path of csa_index_score (kept for measuring that difference).
+ *   score_bf16 != 0: every score is rounded to bf16 (RNE) before it is written or selected.
+ *   cand NULL: scores [B,S,Nc] fp32 (required), any S.  cand not NULL: decode shapes as
+ *   csa_index_score_segments (segment top-k pairs for csa_topk_merge /
+ *   csa_topk_sparse_attn, >= csa_index_segments_size(B, S, Nc, k_top) bytes), scores
+ *   optional.
+ * ------------------------------------------------------------------------------ */
+int csa_index_score_mx(const void* q, const void* q_scale, const float* w, const void* k, const void* k_scale,
+                       int elem_dtype, const int64_t* q_pos, int B, int S, int H_I, int d_I, int Nc, int m,
+                       int score_bf16, float* scores, int k_top, void* cand, size_t cand_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
  * The CSA2 hierarchical indexer ([V4-CSA2] section 11): the Full layer scores every entry,
