@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
 CSA_LAYOUT_ROWS, CSA_LAYOUT_B16 = 0, 1
+CSA_KV_BF16, CSA_KV_FP4_E4M3, CSA_KV_FP8_ROPE_BF16 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
           4: "CSA_ERR_HIP", 5: "CSA_ERR_SCRATCH"}
 
@@ -79,12 +80,12 @@ def _load() -> ctypes.CDLL:
         "csa_topk": ([vp, i, i, i, i, vp, vp, sz, vp], i),
         "csa_topk_algo": ([vp, i, i, i, i, vp, vp, sz, i, vp], i),
         "csa_attn_workspace_size": ([i, i, i, i, i, i], sz),
-        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
-        "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp, sz,
+        "csa_sparse_attn": ([vp, vp, vp, vp, vp, vp, i, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
+        "csa_topk_sparse_attn": ([vp, vp, vp, sz, vp, vp, vp, i, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp, vp, sz,
                                   vp], i),
-        "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, f, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
+        "hca_dense_attn": ([vp, vp, vp, i, vp, vp, i, i, f, i, i, i, i, i, i, i, i, f, vp, vp, vp, sz, vp], i),
         "csa_sparse_attn_noalloc_max_bytes": ([], sz),
-        "csa_sparse_attn_noalloc": ([vp, vp, vp, vp, vp, vp, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp], i),
+        "csa_sparse_attn_noalloc": ([vp, vp, vp, vp, vp, vp, i, i, f, i, i, i, i, i, i, i, i, i, f, vp, vp, vp], i),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -373,20 +374,36 @@ def attn_workspace_size(B, S, H, c, max_rows, dtype) -> int:
     return int(_lib.csa_attn_workspace_size(B, S, H, c, max_rows, dtype))
 
 
+KV_ROW_BYTES = {CSA_KV_BF16: 1024, CSA_KV_FP4_E4M3: 288, CSA_KV_FP8_ROPE_BF16: 584}
+
+
+def _kv_entries(kv_comp, kv_format: int, c: int) -> int:
+    """Nc of a compressed cache: [B,Nc,c] in the query dtype, or for the packed formats
+    [B,Nc,row bytes] uint8 (c = 512)."""
+    if kv_format == CSA_KV_BF16:
+        return kv_comp.shape[1]
+    if kv_format not in KV_ROW_BYTES or c != 512:
+        raise CSAError("attention", 2, f"kv_format {kv_format} with c = {c} is not supported")
+    if kv_comp.dtype != torch.uint8 or kv_comp.dim() != 3 or kv_comp.shape[2] != KV_ROW_BYTES[kv_format]:
+        raise CSAError("attention", 1, f"kv_comp of kv_format {kv_format} must be uint8 [B,Nc,{KV_ROW_BYTES[kv_format]}]")
+    return kv_comp.shape[1]
+
+
 def csa_sparse_attn(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None, ws=None,
-                    inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
-    """q [B,S,H,c], kv_comp [B,Nc,c], idx [B,S,k] int32, swa [B,Ls,c], sink [H] fp32;
-    q_pos [B,S] int64 (optional) leaves out window rows of negative positions; inv_rope_d > 0
-    (needs q_pos) rotates the output's last inv_rope_d channels back by the query position."""
+                    inv_rope_d: int = 0, rope_theta: float = 1e4, kv_format: int = 0, stream=None):
+    """q [B,S,H,c], kv_comp [B,Nc,c] (or a packed cache of kv_format), idx [B,S,k] int32,
+    swa [B,Ls,c], sink [H] fp32; q_pos [B,S] int64 (optional) leaves out window rows of
+    negative positions; inv_rope_d > 0 (needs q_pos) rotates the output's last inv_rope_d
+    channels back by the query position."""
     _dev(q, kv_comp, idx, swa, sink, out, lse, ws, q_pos)
     B, S, H, c = q.shape
-    Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
+    Nc, Ls, k = _kv_entries(kv_comp, kv_format, c), swa.shape[1], idx.shape[-1]
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     dt = _dtype(q)
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_sparse_attn", _lib.csa_sparse_attn(
-        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, k, Ls, W,
-        int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
+        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), dt, int(kv_format), float(scale), B, S, H, c, Nc,
+        k, Ls, W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
     return out
 
 
@@ -395,45 +412,47 @@ def sparse_attn_noalloc_max_bytes() -> int:
 
 
 def csa_sparse_attn_noalloc(q, kv_comp, idx, swa, sink, *, W: int, out, lse=None, scale=None, q_pos=None,
-                            inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
+                            inv_rope_d: int = 0, rope_theta: float = 1e4, kv_format: int = 0, stream=None):
     """csa_sparse_attn with the split partials in the library's fixed scratch (no workspace)."""
     _dev(q, kv_comp, idx, swa, sink, out, lse, q_pos)
     B, S, H, c = q.shape
-    Nc, Ls, k = kv_comp.shape[1], swa.shape[1], idx.shape[-1]
+    Nc, Ls, k = _kv_entries(kv_comp, kv_format, c), swa.shape[1], idx.shape[-1]
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     _check("csa_sparse_attn_noalloc", _lib.csa_sparse_attn_noalloc(
-        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), _dtype(q), float(scale), B, S, H, c, Nc, k, Ls,
-        W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _stream(stream)))
+        _p(q), _p(kv_comp), _p(idx), _p(q_pos), _p(swa), _p(sink), _dtype(q), int(kv_format), float(scale), B, S, H,
+        c, Nc, k, Ls, W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _stream(stream)))
     return out
 
 
 def csa_topk_sparse_attn(q, kv_comp, cand, swa, sink, *, k: int, W: int, out, q_pos=None, lse=None, idx=None,
-                         scale=None, ws=None, inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
+                         scale=None, ws=None, inv_rope_d: int = 0, rope_theta: float = 1e4, kv_format: int = 0,
+                         stream=None):
     """The k best of each query's segment candidates (cand from csa_index_score_segments),
     then csa_sparse_attn over them; idx [B,S,k] int32 (optional) receives the selection."""
     _dev(q, kv_comp, cand, swa, sink, out, lse, idx, ws, q_pos)
     B, S, H, c = q.shape
-    Nc, Ls = kv_comp.shape[1], swa.shape[1]
+    Nc, Ls = _kv_entries(kv_comp, kv_format, c), swa.shape[1]
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     dt = _dtype(q)
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + k, dt), ws, q.device)
     _check("csa_topk_sparse_attn", _lib.csa_topk_sparse_attn(
         _p(q), _p(kv_comp), _p(cand), cand.numel() * cand.element_size(), _p(q_pos), _p(swa), _p(sink), dt,
-        float(scale), B, S, H, c, Nc, k, Ls, W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(idx), _p(ws),
+        int(kv_format), float(scale), B, S, H, c, Nc, k, Ls, W, int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(idx), _p(ws),
         wsb, _stream(stream)))
     return out
 
 
 def hca_dense_attn(q, kv_comp, q_pos, swa, sink, *, m: int, W: int, out, lse=None, scale=None, ws=None,
-                   inv_rope_d: int = 0, rope_theta: float = 1e4, stream=None):
-    """q [B,S,H,c], kv_comp [B,Nc,c], q_pos [B,S] int64, swa [B,Ls,c], sink [H] fp32."""
+                   inv_rope_d: int = 0, rope_theta: float = 1e4, kv_format: int = 0, stream=None):
+    """q [B,S,H,c], kv_comp [B,Nc,c] (or a packed cache of kv_format), q_pos [B,S] int64,
+    swa [B,Ls,c], sink [H] fp32."""
     _dev(q, kv_comp, q_pos, swa, sink, out, lse, ws)
     B, S, H, c = q.shape
-    Nc, Ls = kv_comp.shape[1], swa.shape[1]
+    Nc, Ls = _kv_entries(kv_comp, kv_format, c), swa.shape[1]
     scale = 1.0 / math.sqrt(c) if scale is None else scale
     dt = _dtype(q)
     ws, wsb = _ws(attn_workspace_size(B, S, H, c, min(W, Ls) + Nc, dt), ws, q.device)
     _check("hca_dense_attn", _lib.hca_dense_attn(
-        _p(q), _p(kv_comp), _p(q_pos), m, _p(swa), _p(sink), dt, float(scale), B, S, H, c, Nc, Ls, W,
+        _p(q), _p(kv_comp), _p(q_pos), m, _p(swa), _p(sink), dt, int(kv_format), float(scale), B, S, H, c, Nc, Ls, W,
         int(inv_rope_d), float(rope_theta), _p(out), _p(lse), _p(ws), wsb, _stream(stream)))
     return out

@@ -10,7 +10,7 @@ int launch_index_score(const void*, const float*, const float*, const void*, con
 int launch_topk(const float*, int, int, int, int32_t*, void*, size_t, int, hipStream_t);
 size_t topk_workspace_bytes(int, int, int);
 bool topk_supported(int, int, bool);
-int launch_attention(bool, const void*, const void*, const int32_t*, const int64_t*, int, const void*, const float*,
+int launch_attention(bool, const void*, const void*, int, const int32_t*, const int64_t*, int, const void*, const float*,
                      int, float, int, int, int, int, int, int, int, int, int, float, void*, float*, void*, size_t,
                      hipStream_t);
 size_t attn_workspace_bytes(int, int, int, int, int, int);
@@ -40,7 +40,7 @@ size_t index_keys_b16_bytes(int, int);
 int launch_index_keys_b16(const void*, void*, int, int, hipStream_t);
 int launch_topk_merge(uint2*, int, int, int, int32_t*, hipStream_t);
 size_t topk_merge_pairs_per_row(int, int);
-int launch_topk_attention(const void*, const void*, const uint2*, int, size_t, const int64_t*, const void*,
+int launch_topk_attention(const void*, const void*, int, const uint2*, int, size_t, const int64_t*, const void*,
                           const float*, float, int, int, int, int, int, int, int, float, void*, float*, int32_t*, void*,
                           size_t, hipStream_t);
 int topk_attention_max_cand();
@@ -73,7 +73,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_version(void) { return 200; }
+int csa_version(void) { return 300; }
 
 // ---- stage 1 ------------------------------------------------------------------------
 size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev) {
@@ -358,10 +358,13 @@ size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dty
   return attn_workspace_bytes(B, S, H, c, max_rows, dtype);
 }
 
-static int check_attn(const void* q, const void* kv, const void* swa, const float* sink, int dtype, float scale,
-                      int B, int S, int H, int c, int Nc, int Ls, int W, const void* out, int inv_rope_d,
+static int check_attn(const void* q, const void* kv, const void* swa, const float* sink, int dtype, int kv_format,
+                      float scale, int B, int S, int H, int c, int Nc, int Ls, int W, const void* out, int inv_rope_d,
                       float rope_theta, const int64_t* q_pos) {
   CSA_REQUIRE(q && kv && swa && sink && out);
+  CSA_REQUIRE(kv_format == CSA_KV_BF16 || kv_format == CSA_KV_FP4_E4M3 || kv_format == CSA_KV_FP8_ROPE_BF16);
+  if (kv_format != CSA_KV_BF16 && dtype != CSA_BF16) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(kv_format == CSA_KV_BF16 || aligned16(kv));
   CSA_REQUIRE(inv_rope_d >= 0 && inv_rope_d % 2 == 0 && inv_rope_d <= c);
   CSA_REQUIRE(inv_rope_d == 0 || (q_pos != nullptr && rope_theta > 0.0f));
   CSA_REQUIRE(B > 0 && S > 0 && H > 0 && c > 0 && Nc > 0 && W > 0 && Ls >= S);
@@ -378,24 +381,24 @@ static int check_attn(const void* q, const void* kv, const void* swa, const floa
 }
 
 int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos, const void* swa,
-                    const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                    const float* sink, int dtype, int kv_format, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                     int inv_rope_d, float rope_theta, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, kv_format, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
                             q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(idx && k >= 1 && k <= 65536);
   CSA_REQUIRE(aligned16(ws));
-  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
+  return launch_attention(false, q, kv_comp, kv_format, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
                           inv_rope_d, rope_theta, out, lse, ws, ws_bytes, as_stream(stream));
 }
 
 size_t csa_sparse_attn_noalloc_max_bytes(void) { return attn_scratch_bytes(); }
 
 int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
-                            const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
+                            const void* swa, const float* sink, int dtype, int kv_format, float scale, int B, int S, int H, int c,
                             int Nc, int k, int Ls, int W, int inv_rope_d, float rope_theta, void* out, float* lse,
                             void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, kv_format, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
                             q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(idx && k >= 1 && k <= 65536);
@@ -406,15 +409,15 @@ int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* i
     const int rc = attn_scratch(&ws);
     if (rc != CSA_OK) return rc;
   }
-  return launch_attention(false, q, kv_comp, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
+  return launch_attention(false, q, kv_comp, kv_format, idx, q_pos, 1, swa, sink, dtype, scale, B, S, H, c, Nc, k, Ls, W,
                           inv_rope_d, rope_theta, out, lse, ws, need, as_stream(stream));
 }
 
 int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes, const int64_t* q_pos,
-                         const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c,
-                         int Nc, int k, int Ls, int W, int inv_rope_d, float rope_theta, void* out, float* lse,
-                         int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+                         const void* swa, const float* sink, int dtype, int kv_format, float scale, int B, int S,
+                         int H, int c, int Nc, int k, int Ls, int W, int inv_rope_d, float rope_theta, void* out,
+                         float* lse, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, kv_format, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
                             q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(cand && k >= 1 && k <= 2048);
@@ -435,20 +438,20 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t 
   size_t offset = 0;
   const int n_cand = launch_topk_merge_first(pairs, rows, G, k, offset, as_stream(stream));
   if (n_cand < 0) return CSA_ERR_HIP;
-  return launch_topk_attention(q, kv_comp, pairs + offset, n_cand, topk_merge_pairs_per_row(G, k), q_pos, swa, sink,
+  return launch_topk_attention(q, kv_comp, kv_format, pairs + offset, n_cand, topk_merge_pairs_per_row(G, k), q_pos, swa, sink,
                                scale, B, S, Nc, k, Ls, W, inv_rope_d, rope_theta, out, lse, idx, ws, ws_bytes,
                                as_stream(stream));
 }
 
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m, const void* swa, const float* sink,
-                   int dtype, float scale, int B, int S, int H, int c, int Nc, int Ls, int W, int inv_rope_d,
+                   int dtype, int kv_format, float scale, int B, int S, int H, int c, int Nc, int Ls, int W, int inv_rope_d,
                    float rope_theta, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  const int st = check_attn(q, kv_comp, swa, sink, dtype, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
+  const int st = check_attn(q, kv_comp, swa, sink, dtype, kv_format, scale, B, S, H, c, Nc, Ls, W, out, inv_rope_d, rope_theta,
                             q_pos);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(q_pos && m > 0);
   CSA_REQUIRE(aligned16(ws));
-  return launch_attention(true, q, kv_comp, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W,
+  return launch_attention(true, q, kv_comp, kv_format, nullptr, q_pos, m, swa, sink, dtype, scale, B, S, H, c, Nc, 0, Ls, W,
                           inv_rope_d, rope_theta, out, lse, ws, ws_bytes, as_stream(stream));
 }
 

@@ -103,7 +103,7 @@ constexpr int kSrcDense = 1;   // every visible entry (HCA)
 constexpr int kSrcCand = 2;    // the k best of the query's segment candidates, selected here
 constexpr int kSrcCand2 = 3;   // the same from up to twice as many candidates (16 per thread)
 
-template <int kSrc, int kParts, int kWaves>
+template <int kSrc, int kParts, int kWaves, int kFmt = kFmtBf16>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   constexpr bool kDense = kSrc == kSrcDense;
   constexpr bool kCand = kSrc == kSrcCand || kSrc == kSrcCand2;
@@ -134,7 +134,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   const int ch0 = split * a.chunks_per_split;
   const int ch1 = min(n_chunks, ch0 + a.chunks_per_split);
 
-  const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
+  constexpr int kRowBytes = kv_row_bytes(kFmt);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + static_cast<size_t>(b) * a.Nc * kRowBytes;
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
   const int32_t* idxq = kSrc == kSrcIdx ? a.idx + static_cast<size_t>(qi) * a.k : nullptr;
 
@@ -211,7 +212,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
         p = reinterpret_cast<uint64_t>(swab + static_cast<size_t>(w_lo + slot) * kAC);
       } else if (slot < n_slots) {
         const int j = kDense ? slot - n_swa : kCand ? sel[slot - n_swa] : idxq[slot - n_swa];
-        if (j >= 0 && j < a.Nc) p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kAC);
+        // a compressed row of another format carries bit 1 (its address is a multiple of 8)
+        if (j >= 0 && j < a.Nc)
+          p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kRowBytes) | (kFmt != kFmtBf16 ? 2u : 0u);
       }
       rowptr[e] = p;
     }
@@ -228,7 +231,11 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
     const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
                         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(PTR)));   \
     (VM) |= static_cast<uint32_t>(~p_ & 1u) << (R);                                    \
-    ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
+    if (kFmt != kFmtBf16 && (p_ & 2u)) {             /* raw share, decoded at the store */ \
+      (VM) |= 1u << (8 + (R));                                                         \
+      ST##R = load_row8<kFmt>(p_ & ~static_cast<uint64_t>(3), l);                     \
+    } else                                                                             \
+      ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
   } while (0)
 #define CSA_ATT_LOAD(CH, ST, VM)                                                        \
   do {                                                                                 \
@@ -255,16 +262,19 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
       CSA_ATT_LOAD1(ST, VM, 2, q_[2]); CSA_ATT_LOAD1(ST, VM, 3, q_[3]);                \
     }                                                                                  \
   } while (0)
-#define CSA_ATT_STORE1(BUF, ST, R) \
-  *reinterpret_cast<v4u*>((BUF) + (Sh::kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R
+#define CSA_ATT_STORE1(BUF, ST, R, VM)                                                  \
+  do {                                                                                 \
+    if (kFmt != kFmtBf16 && (((VM) >> (8 + (R))) & 1u)) ST##R = decode_row8<kFmt>(ST##R, l); \
+    *reinterpret_cast<v4u*>((BUF) + (Sh::kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R; \
+  } while (0)
 #define CSA_ATT_STORE(SLOT, ST, VM)                                                     \
   do {                                                                                 \
     uint8_t* buf_ = ring + (SLOT) * kChunkBytes;                                       \
-    CSA_ATT_STORE1(buf_, ST, 0); CSA_ATT_STORE1(buf_, ST, 1);                          \
+    CSA_ATT_STORE1(buf_, ST, 0, VM); CSA_ATT_STORE1(buf_, ST, 1, VM);                  \
     if constexpr (Sh::kRowsPerWave == 4) {                                             \
-      CSA_ATT_STORE1(buf_, ST, 2); CSA_ATT_STORE1(buf_, ST, 3);                        \
+      CSA_ATT_STORE1(buf_, ST, 2, VM); CSA_ATT_STORE1(buf_, ST, 3, VM);                \
     }                                                                                  \
-    if (l == 0) validw[(SLOT) * kWaves + wave] = static_cast<int>(VM);                 \
+    if (l == 0) validw[(SLOT) * kWaves + wave] = static_cast<int>((VM) & 0xffu);       \
   } while (0)
 
   v4f o[Sh::kPart / 16];
@@ -851,8 +861,8 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
   return nq * ns * H * (static_cast<size_t>(c) + 2) * sizeof(float);
 }
 
-template <int kParts, int kWaves>
-static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
+template <int kParts, int kWaves, int kFmt>
+static int launch_attn_bf16_fmt(int src, const AttnArgs& a, hipStream_t st) {
   using Sh = AttnShape<kParts, kWaves>;
   // the dynamic-LDS limit of every source's kernel, raised once per device (any thread may call)
   static std::atomic<uint64_t> raised{0};
@@ -860,25 +870,33 @@ static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
   if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
   const uint64_t bit = uint64_t{1} << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcIdx, kParts, kWaves>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcIdx, kParts, kWaves, kFmt>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves, kFmt>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves, kFmt>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand2, kParts, kWaves>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand2, kParts, kWaves, kFmt>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess)
       return CSA_ERR_HIP;
     raised.fetch_or(bit, std::memory_order_release);
   }
   const dim3 grid(cdiv(a.nq, 8) * 8 * Sh::kUnits * a.nsplit);
   const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;
-  if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
-  else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
-  else if (src == kSrcCand2) hipLaunchKernelGGL((attn_bf16<kSrcCand2, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
-  else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves>), grid, dim3(Sh::kThreads), lds, st, a);
+  const dim3 block(Sh::kThreads);
+  if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves, kFmt>), grid, block, lds, st, a);
+  else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves, kFmt>), grid, block, lds, st, a);
+  else if (src == kSrcCand2) hipLaunchKernelGGL((attn_bf16<kSrcCand2, kParts, kWaves, kFmt>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves, kFmt>), grid, block, lds, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
+}
+
+template <int kParts, int kWaves>
+static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
+  if (a.kv_fmt == kFmtFp4) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp4>(src, a, st);
+  if (a.kv_fmt == kFmtFp8Rope) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp8Rope>(src, a, st);
+  return launch_attn_bf16_fmt<kParts, kWaves, kFmtBf16>(src, a, st);
 }
 
 // The bf16 path for row source SRC: splits of the row set, the attention kernel, then the
@@ -906,12 +924,13 @@ static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream
   return CSA_OK;
 }
 
-static AttnArgs attn_args(const void* q, const void* kv, const int64_t* q_pos, int m, const void* swa,
+static AttnArgs attn_args(const void* q, const void* kv, int kv_fmt, const int64_t* q_pos, int m, const void* swa,
                           const float* sink, float scale, int B, int S, int Nc, int k, int Ls, int W, int rope_d,
                           float rope_theta, void* out, float* lse) {
   AttnArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kv = static_cast<const uint16_t*>(kv);
+  a.kv_fmt = kv_fmt;
   a.q_pos = q_pos;
   a.swa = static_cast<const uint16_t*>(swa);
   a.sink = sink;
@@ -932,7 +951,7 @@ int topk_attention_max_cand() { return std::min(NarrowShape::kMaxCand2, WideShap
 // level's; 8 per thread up to kMaxCand, else 16); idx_out (optional) receives the
 // selection.  The caller has checked shapes and the workspace.
 
-int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int n_cand, size_t cand_stride,
+int launch_topk_attention(const void* q, const void* kv, int kv_fmt, const uint2* cand, int n_cand, size_t cand_stride,
                           const int64_t* q_pos, const void* swa, const float* sink, float scale, int B, int S, int Nc,
                           int k, int Ls, int W, int rope_d, float rope_theta, void* out, float* lse, int32_t* idx_out,
                           void* ws, size_t ws_bytes, hipStream_t st) {
@@ -940,7 +959,7 @@ int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int 
   if (ws_bytes < attn_workspace_bytes(B, S, kAH, kAC, max_rows, CSA_BF16)) return CSA_ERR_WORKSPACE;
   if (n_cand > topk_attention_max_cand() || k > n_cand || cand_stride < static_cast<size_t>(n_cand))
     return CSA_ERR_UNSUPPORTED;
-  AttnArgs a = attn_args(q, kv, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out, lse);
+  AttnArgs a = attn_args(q, kv, kv_fmt, q_pos, 1, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out, lse);
   a.cand = cand;
   a.n_cand = n_cand;
   a.cand_stride = cand_stride;
@@ -950,7 +969,8 @@ int launch_topk_attention(const void* q, const void* kv, const uint2* cand, int 
 }
 
 
-int launch_attention(bool dense, const void* q, const void* kv, const int32_t* idx, const int64_t* q_pos, int m,
+int launch_attention(bool dense, const void* q, const void* kv, int kv_fmt, const int32_t* idx, const int64_t* q_pos,
+                     int m,
                      const void* swa, const float* sink, int dtype, float scale, int B, int S, int H, int c, int Nc,
                      int k, int Ls, int W, int rope_d, float rope_theta, void* out, float* lse, void* ws,
                      size_t ws_bytes, hipStream_t st) {
@@ -959,7 +979,8 @@ int launch_attention(bool dense, const void* q, const void* kv, const int32_t* i
   if (ws_bytes < attn_workspace_bytes(B, S, H, c, max_rows, dtype)) return CSA_ERR_WORKSPACE;
   const float scale_log2 = scale * kLog2e;
   if (dtype == CSA_BF16) {
-    AttnArgs a = attn_args(q, kv, q_pos, m, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out, lse);
+    AttnArgs a = attn_args(q, kv, kv_fmt, q_pos, m, swa, sink, scale, B, S, Nc, k, Ls, W, rope_d, rope_theta, out,
+                           lse);
     a.idx = idx;
     return run_attn_bf16(dense ? kSrcDense : kSrcIdx, a, max_rows, ws, st);
   }

@@ -25,9 +25,84 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Formats of the compressed KV rows (the window rows are always bf16).
+constexpr int kFmtBf16 = 0;                         // 512 bf16 channels, 1024 bytes
+constexpr int kFmtFp4 = 1;                          // 512 E2M1 codes (256 B) + 32 E4M3 scales per 16: 288 bytes
+constexpr int kFmtFp8Rope = 2;                      // 448 e4m3 codes + 64 bf16 + E8M0 exponent + pad: 584 bytes
+constexpr int kFp8RopeCodes = 448;
+__host__ __device__ constexpr inline int kv_row_bytes(int fmt) {
+  return fmt == kFmtFp4 ? 288 : fmt == kFmtFp8Rope ? 584 : kAC * 2;
+}
+
+// Lane l's share of a compressed row (channels 8l .. 8l+7) is loaded raw and decoded only
+// when it is written to LDS, so that the loads of later chunks stay in flight meanwhile.
+// FP4: two codes per byte, the even channel in the low nibble, the E4M3 scale of channels
+// 16i .. 16i+15 in byte 256 + i.  FP8 + RoPE: channels below 448 are e4m3 codes times
+// 2^(e - 127) with e = byte 576, the last 64 channels bf16 at byte 448.
+template <int kFmt>
+__device__ __forceinline__ v4u load_row8(uint64_t row, int l) {
+  typedef const __attribute__((address_space(1))) uint8_t g8;
+  typedef const __attribute__((address_space(1))) uint32_t g32;
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  typedef const __attribute__((address_space(1))) u2 g64;
+  g8* r = reinterpret_cast<g8*>(row);
+  v4u v = {0u, 0u, 0u, 0u};
+  if constexpr (kFmt == kFmtFp4) {
+    v[0] = *reinterpret_cast<g32*>(r + 4 * l);              // codes of channels 8l .. 8l+7
+    v[1] = r[256 + (l >> 1)];                               // their block's scale
+  } else {
+    if (8 * l < kFp8RopeCodes) {
+      const u2 c = *reinterpret_cast<g64*>(r + 8 * l);
+      v[0] = c[0];
+      v[1] = c[1];
+      v[2] = r[kFp8RopeCodes + 128];
+    } else {                                                // 8-byte aligned: two 8-byte loads
+      g64* b = reinterpret_cast<g64*>(r + kFp8RopeCodes + 2 * (8 * l - kFp8RopeCodes));
+      const u2 lo = b[0], hi = b[1];
+      v = v4u{lo[0], lo[1], hi[0], hi[1]};
+    }
+  }
+  return v;
+}
+
+// The 8 bf16 values of a raw share from load_row8, exactly: an E2M1 value times an E4M3
+// scale has at most 6 significant bits, an e4m3 value times a power of two at most 4, so
+// both products are bf16 numbers and dropping the low half of the fp32 word is exact.
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+template <int kFmt>
+__device__ __forceinline__ v4u decode_row8(v4u v, int l) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v4u out;
+  if constexpr (kFmt == kFmtFp4) {
+    const uint32_t codes = v[0];
+    const float s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], 1.0f, false)[0];
+    v2f f;
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0); out[0] = pack_bf16_exact(f[0] * s, f[1] * s);
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1); out[1] = pack_bf16_exact(f[0] * s, f[1] * s);
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2); out[2] = pack_bf16_exact(f[0] * s, f[1] * s);
+    f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3); out[3] = pack_bf16_exact(f[0] * s, f[1] * s);
+  } else {
+    if (8 * l < kFp8RopeCodes) {
+      const float s = ldexpf(1.0f, static_cast<int>(v[2]) - 127);
+      v2f f;
+      f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], 1.0f, false); out[0] = pack_bf16_exact(f[0] * s, f[1] * s);
+      f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[0], 1.0f, true); out[1] = pack_bf16_exact(f[0] * s, f[1] * s);
+      f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], 1.0f, false); out[2] = pack_bf16_exact(f[0] * s, f[1] * s);
+      f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v[1], 1.0f, true); out[3] = pack_bf16_exact(f[0] * s, f[1] * s);
+    } else {
+      out = v;
+    }
+  }
+  return out;
+}
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kv;
+  int kv_fmt;                // kFmt* of the compressed rows
   const int32_t* idx;
   const int64_t* q_pos;
   const uint16_t* swa;

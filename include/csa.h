@@ -60,6 +60,20 @@ typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3 } c
  * FP8 codes) the 16-entry blocks of csa_index_keys_b16. */
 typedef enum { CSA_LAYOUT_ROWS = 0, CSA_LAYOUT_B16 = 1 } csa_layout;
 
+/* Storage formats of the compressed main-KV cache read by the attention calls (c = 512,
+ * one row per entry, rows of one batch element contiguous, [B, Nc, row bytes]):
+ *   CSA_KV_BF16           the row as c bf16 values (1024 bytes).
+ *   CSA_KV_FP4_E4M3       [V4-CSA2] section 16.1, [ATTN-CMP] section on CSA2: 512 E2M1
+ *                         codes, two per byte with the even channel in the low nibble
+ *                         (bytes 0..255), then one E4M3 scale per 16 channels (bytes
+ *                         256..287); channel i = E2M1(code i) * E4M3(scale i/16).  288 bytes.
+ *   CSA_KV_FP8_ROPE_BF16  [ATTN-CMP] section "CSA（DeepSeek-V4）": the 448 channels without
+ *                         RoPE as e4m3 codes (bytes 0..447) times one power-of-two scale
+ *                         2^(e - 127) per row, e = byte 576 (E8M0); the 64 RoPE channels as
+ *                         bf16 (bytes 448..575); bytes 577..583 unused.  584 bytes.
+ * Every value of these formats is a bf16 number, so the attention reads them exactly. */
+typedef enum { CSA_KV_BF16 = 0, CSA_KV_FP4_E4M3 = 1, CSA_KV_FP8_ROPE_BF16 = 2 } csa_kv_format;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* csa_status_string(int status);
 
@@ -374,7 +388,11 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
  * The sink enters the denominator only (unscaled).
  *
  *   q      [B,S,H,c]   dtype (CSA_BF16: H = 64, c = 512;  CSA_F32: H <= 64, c <= 512)
- *   kv_comp[B,Nc,c]    dtype;   idx [B,S,k] int32 in [-1, Nc), no duplicates.
+ *   kv_comp[B,Nc,c]    dtype, when kv_format = CSA_KV_BF16; with dtype CSA_BF16 it may also
+ *          be a cache of kv_format CSA_KV_FP4_E4M3 or CSA_KV_FP8_ROPE_BF16 (see csa_kv_format;
+ *          16-byte aligned), read and decoded in the kernel: the result equals the call on
+ *          the decoded bf16 rows.  Another format with CSA_F32: CSA_ERR_UNSUPPORTED.
+ *   idx    [B,S,k] int32 in [-1, Nc), no duplicates.
  *   q_pos  [B,S] int64 positions (consecutive within a sequence), or NULL.  Only the
  *          window uses it: row r of swa holds position q_pos[b,S-1] - Ls + 1 + r, and
  *          rows of negative positions (a sequence shorter than Ls) are left out.  NULL:
@@ -396,8 +414,8 @@ int csa_topk_algo(const float* scores, int B, int S, int Nc, int k, int32_t* idx
 size_t csa_attn_workspace_size(int B, int S, int H, int c, int max_rows, int dtype);
 
 int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
-                    const int64_t* q_pos, const void* swa, const float* sink, int dtype, float scale,
-                    int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                    const int64_t* q_pos, const void* swa, const float* sink, int dtype, int kv_format,
+                    float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                     int inv_rope_d, float rope_theta,
                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
@@ -419,7 +437,7 @@ int csa_sparse_attn(const void* q, const void* kv_comp, const int32_t* idx,
 size_t csa_sparse_attn_noalloc_max_bytes(void);
 
 int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* idx, const int64_t* q_pos,
-                            const void* swa, const float* sink, int dtype, float scale,
+                            const void* swa, const float* sink, int dtype, int kv_format, float scale,
                             int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                             int inv_rope_d, float rope_theta, void* out, float* lse, void* stream);
 
@@ -443,7 +461,7 @@ int csa_sparse_attn_noalloc(const void* q, const void* kv_comp, const int32_t* i
  * ------------------------------------------------------------------------------ */
 int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t cand_bytes,
                          const int64_t* q_pos, const void* swa, const float* sink, int dtype,
-                         float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
+                         int kv_format, float scale, int B, int S, int H, int c, int Nc, int k, int Ls, int W,
                          int inv_rope_d, float rope_theta,
                          void* out, float* lse, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream);
@@ -458,7 +476,7 @@ int csa_topk_sparse_attn(const void* q, const void* kv_comp, void* cand, size_t 
  * positions within a sequence (required; it also bounds the window as above).  The workspace query takes max_rows = W + Nc.
  * ------------------------------------------------------------------------------ */
 int hca_dense_attn(const void* q, const void* kv_comp, const int64_t* q_pos, int m,
-                   const void* swa, const float* sink, int dtype, float scale,
+                   const void* swa, const float* sink, int dtype, int kv_format, float scale,
                    int B, int S, int H, int c, int Nc, int Ls, int W,
                    int inv_rope_d, float rope_theta,
                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);

@@ -84,18 +84,25 @@ def test_invalid_arguments_are_rejected_before_launch():
     # Pro shape: 64 segment lists of 1024 merge in two levels (groups of 8): room for both
     assert lib.csa_index_segments_size(4, 1, 262144, 1024) == 4 * (64 + 8) * 1024 * 8
     # attention: Ls < S, unsupported bf16 shape, non-positive scale
-    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 4, 64, 512, 10, 8, 2, 128, 0, 1e4,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0, 0.1, 1, 4, 64, 512, 10, 8, 2, 128, 0, 1e4,
                                fake, None, None, 0, None) == 1
-    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 32, 512, 10, 8, 8, 128, 0, 1e4,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0, 0.1, 1, 1, 32, 512, 10, 8, 8, 128, 0, 1e4,
                                fake, None, None, 0, None) == 2
-    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.0, 1, 1, 64, 512, 10, 8, 128, 0, 1e4,
+    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0, 0.0, 1, 1, 64, 512, 10, 8, 128, 0, 1e4,
                               fake, None, None, 0, None) == 1
+    # packed main-KV formats: only with the bf16 kernel, a known format, a 16-byte aligned cache
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 0, 1, 0.1, 1, 1, 64, 512, 10, 8, 8, 128, 0, 1e4,
+                               fake, None, None, 0, None) == 2
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 3, 0.1, 1, 1, 64, 512, 10, 8, 8, 128, 0, 1e4,
+                               fake, None, None, 0, None) == 1
+    assert lib.hca_dense_attn(fake, ctypes.c_void_p(0x1008), fake, 128, fake, fake, 1, 2, 0.1, 1, 1, 64, 512, 10,
+                              128, 128, 0, 1e4, fake, None, None, 0, None) == 1
     # inverse RoPE of the output: needs the query positions, an even width <= c
-    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 64, 1e4,
+    assert lib.csa_sparse_attn(fake, fake, fake, None, fake, fake, 1, 0, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 64, 1e4,
                                fake, None, None, 0, None) == 1
-    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 63, 1e4,
+    assert lib.csa_sparse_attn(fake, fake, fake, fake, fake, fake, 1, 0, 0.1, 1, 1, 64, 512, 10, 8, 128, 128, 63, 1e4,
                                fake, None, None, 0, None) == 1
-    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0.1, 1, 1, 64, 512, 10, 128, 128, 1024, 1e4,
+    assert lib.hca_dense_attn(fake, fake, fake, 128, fake, fake, 1, 0, 0.1, 1, 1, 64, 512, 10, 128, 128, 1024, 1e4,
                               fake, None, None, 0, None) == 1
     # the decode compressor: online needs overlap 0; the blocked layout needs FP8 codes of c = 128
     dec = lambda ov, on, c, dt, layout: lib.csa_compress_decode(
@@ -115,7 +122,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     # query after the first merge level (21 segments x 2048 -> 5 x 2048), workspace too
     # small for the split partials (also with two merge levels: V4-Pro, 64 segments x 1024)
     fused = lambda cand, dt, Nc, k, ws_bytes, cand_bytes=1 << 40: lib.csa_topk_sparse_attn(
-        fake, fake, cand, cand_bytes, None, fake, fake, dt, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, 0, 1e4, fake, None,
+        fake, fake, cand, cand_bytes, None, fake, fake, dt, 0, 0.1, 32, 1, 64, 512, Nc, k, 128, 128, 0, 1e4, fake, None,
         None, fake, ws_bytes, None)
     assert fused(None, 1, 32768, 512, 1 << 40) == 1
     assert fused(fake, 0, 32768, 512, 1 << 40) == 2
