@@ -21,7 +21,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1, CSA_PACKED_FP4_E4M3, CSA_PACKED_FP8_ROPE = 0, 1, 2, 3, 4, 5
 CSA_LAYOUT_ROWS, CSA_LAYOUT_B16 = 0, 1
 CSA_KV_BF16, CSA_KV_FP4_E4M3, CSA_KV_FP8_ROPE_BF16 = 0, 1, 2
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_WORKSPACE",
@@ -151,31 +151,37 @@ def compress_workspace_size(B, T, m, c, overlap, has_prev) -> int:
 
 
 def csa_compress(hidden, hidden_prev, w_proj, bias, *, overlap: bool, m: int, c: int, d_rope: int,
-                 rope_theta: float, rms_eps: float, p0: int, out, out_scale=None, ws=None, stream=None):
+                 rope_theta: float, rms_eps: float, p0: int, out, out_scale=None, out_dtype: int | None = None,
+                 ws=None, stream=None):
     """hidden [B,T,d], hidden_prev [B,m,d] or None, w_proj [S*c, d], bias [S/2,m,c] fp32,
-    out [B,T/m,c] (fp32 / bf16 / uint8 codes with out_scale [B,T/m])."""
+    out [B,T/m,c] (fp32 / bf16 / uint8 codes with out_scale [B,T/m]); out_dtype (default:
+    from out's dtype) selects the low-precision types: CSA_FP4_E2M1 (codes [B,T/m,c/2],
+    out_scale uint8 [B,T/m,c/32]), CSA_PACKED_FP4_E4M3 / CSA_PACKED_FP8_ROPE (uint8 rows)."""
     _dev(hidden, hidden_prev, w_proj, bias, out, out_scale)
     B, T, d = hidden.shape
     ws, wsb = _ws(compress_workspace_size(B, T, m, c, overlap, hidden_prev is not None), ws, hidden.device)
     _check("csa_compress", _lib.csa_compress(
         _p(hidden), _p(hidden_prev), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), B, T, d, m, c,
-        d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale), _dtype(out),
-        _p(ws), wsb, _stream(stream)))
+        d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale),
+        _dtype(out) if out_dtype is None else int(out_dtype), _p(ws), wsb, _stream(stream)))
     return out
 
 
 def csa2_compress(hidden, w_proj, w_k, *, m: int, d_rope: int, theta_kv: float, theta_k: float, rms_eps: float,
-                  p0: int, kv_out, k_out, kv_scale=None, k_scale=None, ws=None, stream=None):
+                  p0: int, kv_out, k_out, kv_scale=None, k_scale=None, kv_dtype: int | None = None,
+                  k_dtype: int | None = None, ws=None, stream=None):
     """CSA2 compressor: hidden [B,T,d], w_proj [(2 if m > 1 else 1)*c, d], w_k [d_I, c] ->
-    kv_out [B,T/m,c] and k_out [B,T/m,d_I] (fp32 / bf16 / uint8 codes with their scales)."""
+    kv_out [B,T/m,c] and k_out [B,T/m,d_I] (fp32 / bf16 / uint8 codes with their scales);
+    kv_dtype / k_dtype (default: from the tensors) select the low-precision types as in
+    csa_compress (c = w_k.shape[1], d_I = w_k.shape[0])."""
     _dev(hidden, w_proj, w_k, kv_out, k_out, kv_scale, k_scale, ws)
     B, T, d = hidden.shape
-    c, dI = kv_out.shape[-1], k_out.shape[-1]
+    dI, c = w_k.shape
     ws, wsb = _ws(int(_lib.csa2_compress_workspace_size(B, T, m, c)), ws, hidden.device)
     _check("csa2_compress", _lib.csa2_compress(
         _p(hidden), _dtype(hidden), _p(w_proj), _p(w_k), B, T, d, m, c, dI, d_rope, float(theta_kv), float(theta_k),
-        float(rms_eps), int(p0), _p(kv_out), _p(kv_scale), _dtype(kv_out), _p(k_out), _p(k_scale), _dtype(k_out),
-        _p(ws), wsb, _stream(stream)))
+        float(rms_eps), int(p0), _p(kv_out), _p(kv_scale), _dtype(kv_out) if kv_dtype is None else int(kv_dtype),
+        _p(k_out), _p(k_scale), _dtype(k_out) if k_dtype is None else int(k_dtype), _p(ws), wsb, _stream(stream)))
     return kv_out, k_out
 
 
@@ -190,7 +196,7 @@ def compress_decode_workspace_size(B, d, c, overlap, in_dtype=CSA_BF16) -> int:
 def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: bool, m: int, c: int, d_rope: int,
                         rope_theta: float, rms_eps: float, online: bool = False, emit: bool = True,
                         cache_scale=None, layout: int = CSA_LAYOUT_ROWS, Nc_max: int | None = None, ws=None,
-                        stream=None):
+                        out_dtype: int | None = None, stream=None):
     """One decode token per sequence: hidden [B,d], pos [B] int64, state (uint8 or fp32,
     compress_state_size bytes); a completed block's entry goes to cache ([B,Nc_max,c] rows,
     or the 16-entry blocked FP8 layout with layout=CSA_LAYOUT_B16, Nc_max given)."""
@@ -203,7 +209,7 @@ def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: boo
     if state.numel() * state.element_size() < compress_state_size(B, m, c, overlap, online):
         raise ValueError("state smaller than compress_state_size")
     ws, wsb = _ws(compress_decode_workspace_size(B, d, c, overlap, _dtype(hidden)), ws, hidden.device)
-    out_dt = CSA_FP8_E4M3 if layout == CSA_LAYOUT_B16 else _dtype(cache)
+    out_dt = CSA_FP8_E4M3 if layout == CSA_LAYOUT_B16 else _dtype(cache) if out_dtype is None else int(out_dtype)
     _check("csa_compress_decode", _lib.csa_compress_decode(
         _p(hidden), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), int(online), B, d, m, c, d_rope,
         float(rope_theta), float(rms_eps), _p(pos), int(emit), _p(state), _p(cache), _p(cache_scale), out_dt,

@@ -81,6 +81,21 @@ size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int 
   return compress_workspace_bytes(B, T, m, c, overlap, has_prev);
 }
 
+// The entry types a compressor writes and what each needs (packed: the main-KV row formats).
+static int check_entry_dtype(int dt, const void* out, const void* scale, int c, int d_rope, bool packed_ok) {
+  if (dt == CSA_F32 || dt == CSA_BF16) return CSA_OK;
+  if (dt == CSA_FP8_E4M3) return scale != nullptr ? CSA_OK : CSA_ERR_INVALID_ARG;
+  if (dt == CSA_FP4_E2M1) {
+    if (scale == nullptr) return CSA_ERR_INVALID_ARG;
+    return c % 32 == 0 ? CSA_OK : CSA_ERR_UNSUPPORTED;
+  }
+  if (packed_ok && (dt == CSA_PACKED_FP4_E4M3 || dt == CSA_PACKED_FP8_ROPE)) {
+    if (!aligned16(out)) return CSA_ERR_INVALID_ARG;
+    return c == 512 && (dt == CSA_PACKED_FP4_E4M3 || d_rope == 64) ? CSA_OK : CSA_ERR_UNSUPPORTED;
+  }
+  return CSA_ERR_INVALID_ARG;
+}
+
 int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, const void* w_proj, const float* bias,
                  int overlap, int B, int T, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
                  int64_t p0, void* out, float* out_scale, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
@@ -92,8 +107,8 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, cons
   CSA_REQUIRE(rms_eps >= 0.0f && rope_theta > 0.0f);
   CSA_REQUIRE(!(overlap && p0 > 0 && hidden_prev == nullptr));
   CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
-  CSA_REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_FP8_E4M3);
-  CSA_REQUIRE(out_dtype != CSA_FP8_E4M3 || out_scale != nullptr);
+  const int ot = check_entry_dtype(out_dtype, out, out_scale, c, d_rope, true);
+  if (ot != CSA_OK) return ot;
   if (in_dtype == CSA_BF16 && d % 64 != 0) return CSA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * (T + m) * 4 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
   const int has_prev = hidden_prev != nullptr;
@@ -119,10 +134,10 @@ int csa2_compress(const void* hidden, int in_dtype, const void* w_proj, const vo
   CSA_REQUIRE(d_rope >= 0 && d_rope % 2 == 0 && d_rope <= c && d_rope <= d_I);
   CSA_REQUIRE(rms_eps >= 0.0f && theta_kv > 0.0f && theta_k > 0.0f);
   CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
-  CSA_REQUIRE(kv_dtype == CSA_F32 || kv_dtype == CSA_BF16 || kv_dtype == CSA_FP8_E4M3);
-  CSA_REQUIRE(k_dtype == CSA_F32 || k_dtype == CSA_BF16 || k_dtype == CSA_FP8_E4M3);
-  CSA_REQUIRE(kv_dtype != CSA_FP8_E4M3 || kv_scale != nullptr);
-  CSA_REQUIRE(k_dtype != CSA_FP8_E4M3 || k_scale != nullptr);
+  const int kvt = check_entry_dtype(kv_dtype, kv_out, kv_scale, c, d_rope, true);
+  if (kvt != CSA_OK) return kvt;
+  const int kt = check_entry_dtype(k_dtype, k_out, k_scale, d_I, d_rope, false);
+  if (kt != CSA_OK) return kt;
   if (in_dtype == CSA_BF16 && (d % 64 != 0 || c % 8 != 0)) return CSA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * T * 2 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
   CSA_REQUIRE(aligned16(ws) && aligned16(w_k));
@@ -151,8 +166,8 @@ int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, co
   CSA_REQUIRE(c % 2 == 0 && c <= 1024 && d_rope >= 0 && d_rope <= c && d_rope % 2 == 0);
   CSA_REQUIRE(rms_eps >= 0.0f && rope_theta > 0.0f);
   CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
-  CSA_REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_FP8_E4M3);
-  CSA_REQUIRE(out_dtype != CSA_FP8_E4M3 || cache_scale != nullptr);
+  const int ot = check_entry_dtype(out_dtype, cache, cache_scale, c, d_rope, true);
+  if (ot != CSA_OK) return ot;
   CSA_REQUIRE(out_layout == CSA_LAYOUT_ROWS || out_layout == CSA_LAYOUT_B16);
   CSA_REQUIRE(static_cast<int64_t>(B) * Nc_max * c < (int64_t{1} << 40));
   if (out_layout == CSA_LAYOUT_B16 && (out_dtype != CSA_FP8_E4M3 || c != 128)) return CSA_ERR_UNSUPPORTED;

@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "entry_store.hpp"
 
 namespace csa {
 
@@ -250,6 +251,8 @@ __global__ __launch_bounds__(512) void compress_pool(PoolArgs a) {
       const uint32_t v = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
       reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + orow * a.c)[pidx] = v;
     }
+  } else if (a.out_dtype != CSA_FP8_E4M3) {
+    store_entry_lowp(a.out_dtype, a.out, reinterpret_cast<uint8_t*>(a.out_scale), orow, a.c, pidx, live, x0, x1, red);
   } else {
     float am = live ? fmaxf(fabsf(x0), fabsf(x1)) : 0.f;
 #pragma unroll

@@ -27,6 +27,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "entry_store.hpp"
 
 namespace csa {
 
@@ -311,6 +312,9 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
       const uint32_t v = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
       reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.cache) + row * c)[p] = v;
     }
+  } else if (a.out_dtype != CSA_FP8_E4M3) {
+    store_entry_lowp(a.out_dtype, a.cache, reinterpret_cast<uint8_t*>(a.cache_scale), row, c, p, live && store, x0,
+                     x1, red);
   } else {
     float am = live ? fmaxf(fabsf(x0), fabsf(x1)) : 0.f;
 #pragma unroll

@@ -17,6 +17,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "entry_store.hpp"
 
 namespace csa {
 
@@ -62,8 +63,8 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return t;
 }
 
-// Stores the channel pair (2p, 2p+1) of row `row` (n channels) in dtype; FP8 needs the row's
-// amax (every thread of the workgroup calls this, live or not, for the block reduction).
+// Stores the channel pair (2p, 2p+1) of row `row` (n channels) in dtype; FP8 and the
+// low-precision types need reductions (every thread of the workgroup calls this, live or not).
 __device__ __forceinline__ void store_pair(void* out, float* out_scale, int dtype, size_t row, int n, int p, bool live,
                                            float x0, float x1, float* red) {
   if (dtype == CSA_F32) {
@@ -73,6 +74,8 @@ __device__ __forceinline__ void store_pair(void* out, float* out_scale, int dtyp
       const uint32_t v = static_cast<uint32_t>(f32_to_bf16(x0)) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16);
       reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row * n)[p] = v;
     }
+  } else if (dtype != CSA_FP8_E4M3) {
+    store_entry_lowp(dtype, out, reinterpret_cast<uint8_t*>(out_scale), row, n, p, live, x0, x1, red);
   } else {
     const float amax = block_max(live ? fmaxf(fabsf(x0), fabsf(x1)) : 0.f, red);
     const float scale = amax / 448.0f;

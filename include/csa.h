@@ -54,7 +54,15 @@ typedef enum {
   CSA_ERR_SCRATCH = 5
 } csa_status;
 
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3 } csa_dtype;
+/* Element types.  CSA_FP4_E2M1 as a compressor output means MXFP4 rows (E2M1 codes, two per
+ * byte with the even channel in the low nibble, and one E8M0 scale byte per 32 channels);
+ * CSA_PACKED_FP4_E4M3 and CSA_PACKED_FP8_ROPE are compressor outputs only: the packed
+ * main-KV rows that the attention calls read with kv_format CSA_KV_FP4_E4M3 and
+ * CSA_KV_FP8_ROPE_BF16 (csa_kv_format below). */
+typedef enum {
+  CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_FP4_E2M1 = 3,
+  CSA_PACKED_FP4_E4M3 = 4, CSA_PACKED_FP8_ROPE = 5
+} csa_dtype;
 
 /* Cache layouts of compressed entries: row-major [B, Nc, c], or (indexer keys, c = 128,
  * FP8 codes) the 16-entry blocks of csa_index_keys_b16. */
@@ -105,8 +113,16 @@ int csa_version(void);
  *   c <= 1024.
  *   out         [B, T/m, c]  out_dtype: CSA_F32 or CSA_BF16 (RNE), or CSA_FP8_E4M3 codes
  *               with out_scale [B, T/m] fp32 = amax/448 of the row (RNE, saturating;
- *               an all-zero row gets scale 0 and zero codes).  out_scale is ignored
- *               for the other output types.
+ *               an all-zero row gets scale 0 and zero codes).  Low-precision caches:
+ *               CSA_FP4_E2M1: MXFP4 codes [B, T/m, c/2] with out_scale taken as uint8
+ *               E8M0 bytes [B, T/m, c/32] (block exponent floor(log2 amax) - 2, clamped to
+ *               [-127, 127]; values to the nearest E2M1, ties to even, saturating; c % 32
+ *               == 0);  CSA_PACKED_FP4_E4M3 / CSA_PACKED_FP8_ROPE (c = 512; the FP8 one
+ *               with d_rope = 64): packed rows [B, T/m, 288] / [B, T/m, 584] as described
+ *               under csa_kv_format (E4M3 scale = amax/6 per 16 channels, RNE; FP8 row
+ *               exponent e = ceil(log2(amax/448)) over the 448 channels without RoPE, the
+ *               RoPE channels in bf16, RNE).  out_scale is ignored for the types without
+ *               a separate scale.
  *   ws          >= csa_compress_workspace_size(...) bytes (holds the projection).
  * ------------------------------------------------------------------------------ */
 size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev);
@@ -138,7 +154,10 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
  *   w_k    [d_I, c] in_dtype ("out x in"), 16-byte aligned;  c <= 1024, d_I <= 256, even;
  *          d_rope even, <= c and <= d_I.
  *   kv_out [B, T/m, c] and k_out [B, T/m, d_I] in CSA_F32, CSA_BF16 or CSA_FP8_E4M3 (with
- *          kv_scale / k_scale [B, T/m] = amax/448 of the row).
+ *          kv_scale / k_scale [B, T/m] = amax/448 of the row), or in the low-precision
+ *          types of csa_compress: CSA_FP4_E2M1 (MXFP4, scales as E8M0 bytes through
+ *          kv_scale / k_scale) for either, CSA_PACKED_FP4_E4M3 or CSA_PACKED_FP8_ROPE
+ *          (c = 512; d_rope = 64 for the FP8 one) for kv_out.
  *   ws     >= csa2_compress_workspace_size(B, T, m, c) bytes (the projection).
  * ------------------------------------------------------------------------------ */
 size_t csa2_compress_workspace_size(int B, int T, int m, int c);
@@ -176,7 +195,9 @@ int csa2_compress(const void* hidden, int in_dtype, const void* w_proj, const vo
  *           bytes, fp32, 16-byte aligned, one share per sequence, kept by the caller across
  *           calls.
  *   cache   CSA_LAYOUT_ROWS: [B, Nc_max, c] in out_dtype (CSA_F32, CSA_BF16, or
- *           CSA_FP8_E4M3 codes with cache_scale [B, Nc_max] = amax/448);
+ *           CSA_FP8_E4M3 codes with cache_scale [B, Nc_max] = amax/448), or one of the
+ *           low-precision types of csa_compress (CSA_FP4_E2M1 with E8M0 bytes
+ *           [B, Nc_max, c/32] through cache_scale; packed rows [B, Nc_max, 288 / 584]);
  *           CSA_LAYOUT_B16: FP8 codes of c = 128 in 16-entry blocks
  *           (csa_index_keys_b16_size(B, Nc_max) bytes) + cache_scale [B, Nc_max].
  *   ws      >= csa_compress_decode_workspace_size(B, d, c, overlap, in_dtype) bytes (the projection

@@ -148,3 +148,83 @@ def assert_topk_equal(idx_g: np.ndarray, idx_o: np.ndarray, scores_o: np.ndarray
         for j in sg ^ so:
             assert abs(sc[r, j] - kth) <= rel * abs(kth), \
                 f"{what} row {r}: entry {j} (score {sc[r, j]}) differs, k-th score {kth}"
+
+
+# ---------------------------------------------------------------------------------------
+# Low-precision entries written by the GPU from its own fp32 rows: the scales and codes must
+# be the oracle's quantisation of the oracle's rows, except where the oracle's value lies
+# so close to a rounding boundary that the fp32 rows may fall on the other side.
+# ---------------------------------------------------------------------------------------
+
+E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+NEAR = 1e-4                                   # relative distance to a boundary that may flip
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, np.uint8)
+    return np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+
+
+def _near_e2m1_mid(v):
+    a = np.abs(v)[..., None]
+    return (np.abs(a - E2M1_MIDS) <= NEAR * np.maximum(a, 0.25)).any(axis=-1)
+
+
+def _near_e4m3_mid(v):
+    a = np.abs(np.asarray(v, np.float64))
+    step = e4m3_step(a)
+    frac = a / step
+    return np.abs(frac - (np.floor(frac) + 0.5)) * step <= NEAR * np.maximum(a, 2.0 ** -9)
+
+
+def _check_codes(codes_g, codes_o, near, what):
+    diff = codes_g != codes_o
+    bad = diff & ~near
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes differ away from a rounding boundary"
+    return int(diff.sum())
+
+
+def assert_mxfp4_rows(codes_g, scales_g, ref, what=""):
+    """codes_g [..., n/2] packed E2M1, scales_g [..., n/32] E8M0 bytes, ref [..., n] oracle rows."""
+    ref = np.asarray(ref, np.float64)
+    n = ref.shape[-1]
+    _, sc_o = O.quantize_mxfp4(ref)
+    amax = np.abs(ref.reshape(ref.shape[:-1] + (n // 32, 32))).max(axis=-1)
+    frac = np.log2(np.maximum(amax, 1e-300))
+    near_pow2 = np.abs(frac - np.rint(frac)) <= NEAR
+    bad = (scales_g != sc_o) & ~near_pow2
+    assert not bad.any(), f"{what}: {int(bad.sum())} MX block exponents differ"
+    v = ref / np.repeat(O.e8m0_to_f64(scales_g), 32, axis=-1)
+    return _check_codes(unpack_nibbles(codes_g), O.f64_to_e2m1(v), _near_e2m1_mid(v), what)
+
+
+def assert_packed_fp4_rows(rows_g, ref, what=""):
+    """rows_g [..., 288] packed main-KV rows (E2M1 + E4M3 per 16), ref [..., 512]."""
+    ref = np.asarray(ref, np.float64)
+    codes_g, sc_g = unpack_nibbles(rows_g[..., :256]), rows_g[..., 256:288]
+    _, sc_o = O.quantize_fp4_e4m3(ref)
+    amax6 = np.abs(ref.reshape(ref.shape[:-1] + (32, 16))).max(axis=-1) / O.E2M1_MAX
+    bad = (sc_g != sc_o) & ~_near_e4m3_mid(amax6)
+    assert not bad.any(), f"{what}: {int(bad.sum())} E4M3 block scales differ"
+    s = np.repeat(O.e4m3fn_to_f64(sc_g), 16, axis=-1)
+    v = ref / np.where(s > 0, s, 1.0)
+    codes_o = np.where(s > 0, O.f64_to_e2m1(v), 0)
+    return _check_codes(codes_g, codes_o, _near_e2m1_mid(v) & (s > 0), what)
+
+
+def assert_packed_fp8_rope_rows(rows_g, ref, what=""):
+    """rows_g [..., 584] packed rows (e4m3 * 2^e over 448 channels, bf16 RoPE channels)."""
+    ref = np.asarray(ref, np.float64)
+    _, ex_o, _ = O.quantize_fp8_rope_split(ref, 64)
+    ex_g = rows_g[..., 576].astype(np.int64) - 127
+    amax = np.abs(ref[..., :448]).max(axis=-1) / O.E4M3_MAX
+    frac = np.log2(np.maximum(amax, 1e-300))
+    near_pow2 = np.abs(frac - np.rint(frac)) <= NEAR
+    bad = (ex_g != ex_o) & ~near_pow2
+    assert not bad.any(), f"{what}: {int(bad.sum())} row exponents differ"
+    assert not rows_g[..., 577:].any(), f"{what}: padding bytes not zero"
+    v = ref[..., :448] / np.exp2(ex_g.astype(np.float64))[..., None]
+    n_diff = _check_codes(rows_g[..., :448], O.f64_to_e4m3fn(v), _near_e4m3_mid(v), what)
+    assert_bf16_within_one_step(np.ascontiguousarray(rows_g[..., 448:576]).view("<u2"), ref[..., 448:],
+                                what + " (RoPE channels)")
+    return n_diff

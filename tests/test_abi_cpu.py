@@ -72,6 +72,15 @@ def test_invalid_arguments_are_rejected_before_launch():
     # compressor workspace too small
     assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0,
                             fake, 8, None) == 3
+    # low-precision entry types: packed rows need c = 512 (FP8 + RoPE also d_rope = 64), MXFP4
+    # needs its scale bytes and c % 32 == 0, unknown types are invalid
+    comp = lambda c, d_rope, dt, scale: lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, c, d_rope, 1e4,
+                                                         1e-6, 0, fake, scale, dt, fake, 1 << 30, None)
+    assert comp(256, 64, 4, None) == 2
+    assert comp(512, 32, 5, None) == 2
+    assert comp(128, 64, 3, None) == 1
+    assert comp(48, 16, 3, fake) == 2
+    assert comp(512, 64, 6, None) == 1
     # segment candidates: shape outside the decode path, candidate buffer too small, null idx
     assert lib.csa_index_score_segments(fake, fake, fake, fake, fake, fake, 1, 8, 64, 128, 3000, 4, 128, None,
                                         fake, 1 << 30, None) == 2

@@ -96,3 +96,36 @@ def test_bf16_cast_of_scores():
     x = rng.normal(size=10000).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
     assert np.array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_lowp_row_checks_accept_the_oracle_rows_and_catch_layout_mistakes():
+    # the GPU-side row checks (tests/parity.py) applied to the oracle's own quantisation laid
+    # out as the library documents, and to the same rows with a plausible layout mistake
+    import pytest
+    from tests.parity import assert_mxfp4_rows, assert_packed_fp4_rows, assert_packed_fp8_rope_rows
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((3, 512))
+    x /= np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+
+    def nib(c):
+        return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+    c4, s4 = O.quantize_fp4_e4m3(x)
+    rows = np.concatenate([nib(c4), s4], axis=-1)
+    assert assert_packed_fp4_rows(rows, x) == 0
+    swapped = np.concatenate([(c4[..., 1::2] | (c4[..., 0::2] << 4)).astype(np.uint8), s4], axis=-1)
+    with pytest.raises(AssertionError):
+        assert_packed_fp4_rows(swapped, x)                    # nibble order
+    cm, sm = O.quantize_mxfp4(x[:, :128])
+    assert assert_mxfp4_rows(nib(cm), sm, x[:, :128]) == 0
+    with pytest.raises(AssertionError):
+        assert_mxfp4_rows(nib(cm), sm + 1, x[:, :128])        # exponent off by one
+    c8, ex, rb = O.quantize_fp8_rope_split(x, 64)
+    tail = np.zeros((3, 8), np.uint8)
+    tail[:, 0] = ex + 127
+    r8 = np.concatenate([c8, rb.astype("<u2").view(np.uint8), tail], axis=-1)
+    assert assert_packed_fp8_rope_rows(r8, x) == 0
+    bad = r8.copy()
+    bad[:, 448:576] = np.roll(bad[:, 448:576], 2, axis=-1)    # RoPE channels shifted by one
+    with pytest.raises(AssertionError):
+        assert_packed_fp8_rope_rows(bad, x)
