@@ -42,7 +42,8 @@
 // pass (the k best of G*k (key, entry) pairs, with the selection core of select.hpp), so
 // that selection and attention are one launch.
 // A row set split over several workgroups writes (m, l, O) partials that attn_merge_tiles
-// combines with the sink (LSE merge).  Workgroups are numbered so that all workgroups
+// combines with the sink (LSE merge).  (Merging in the last workgroup of a query instead
+// measured far slower: its device-scope release writes back the XCD's whole L2.)  Workgroups are numbered so that all workgroups
 // of one query land on the same XCD (consecutive workgroup ids go round-robin over the
 // 8 XCDs) and share its L2 for the rows they all read.
 #include <algorithm>
@@ -64,6 +65,9 @@ template <int kParts, int kWaves>
 struct AttnShape {
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRowsPerWave = kRows / kWaves;   // rows of a chunk each wave loads
+  // chunks of row loads in flight (register sets of kRowsPerWave rows).  (4 measured
+  // slower for decode splits of 5 chunks: the loads past a split's end double.)
+  static constexpr int kDepth = 2;
   static constexpr int kPart = kAC / kParts;            // channels per wave
   static constexpr int kWGHG = kWaves / kParts;         // head groups per workgroup
   static constexpr int kUnits = kNHG / kWGHG;           // workgroups per (query, split)
@@ -102,6 +106,131 @@ constexpr int kSrcIdx = 0;     // idx[q][0..k): selected entries, -1 = none
 constexpr int kSrcDense = 1;   // every visible entry (HCA)
 constexpr int kSrcCand = 2;    // the k best of the query's segment candidates, selected here
 constexpr int kSrcCand2 = 3;   // the same from up to twice as many candidates (16 per thread)
+
+// ---- merge of split partials (attn_merge_tiles, and the last workgroup of a query in
+// attn_bf16).  The partials are in register order: for (query qi, head group hg,
+// 16-channel tile ct), lane l holds heads 16*hg + 4*(l/16) + i and channel 16*ct + l%16.
+
+// One wave's KT tiles from the merged numerators acc, denominators den and reference
+// maxima M (log2 units) of the lane's 4 heads: division, inverse RoPE, bf16 cast; the wave
+// holding tile 0 writes the lse of its heads.
+template <int KT>
+__device__ __forceinline__ void merge_store(const float (&acc)[KT][4], const float (&den)[4], const float (&M)[4],
+                                            size_t qi, int h0, int ct0, int l, uint16_t* __restrict__ out,
+                                            float* __restrict__ lse, const int64_t* __restrict__ q_pos, int rope_d,
+                                            double rope_r) {
+  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct0 + (l & 15);
+  const int64_t tq = rope_d > 0 ? q_pos[qi] : 0;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f;
+    // inverse RoPE of the output (lane pairs hold channel pairs)
+    if (rope_d > 0 && 16 * (ct0 + t) + 16 > kAC - rope_d) {
+      const int col = 16 * (ct0 + t) + (l & 15);
+      float cs = 1.0f, sn = 0.0f;
+      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_r, tq, cs, sn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(v[i]);
+  }
+  if (lse && ct0 == 0 && (l & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
+  }
+}
+
+// Merges the nsplit partials of one wave's KT tiles with the sink and stores them (every
+// load in flight at once for up to 4 splits, else one split's at a time).
+template <int KT>
+__device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                                             const float* __restrict__ sink, int nsplit, size_t qi, int hg, int ct0,
+                                             uint16_t* __restrict__ out, float* __restrict__ lse,
+                                             const int64_t* __restrict__ q_pos, int rope_d, double rope_r) {
+  constexpr int kTiles = kAC / 16;
+  const int l = static_cast<int>(lane_id());
+  const int h0 = kHG * hg + 4 * (l >> 4);
+  float M[4], den[4], acc[KT][4], sk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sk[i] = sink[h0 + i];
+    M[i] = sk[i] * kLog2e;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) acc[t][i] = 0.0f;
+  }
+  auto ml_of = [&](int sp, v4f& a, v4f& b) __attribute__((always_inline)) {
+    const v4f* p = reinterpret_cast<const v4f*>(part_ml + ((qi * nsplit + sp) * kAH + h0) * 2);
+    a = p[0];                                                 // m0 l0 m1 l1
+    b = p[1];                                                 // m2 l2 m3 l3
+  };
+  auto po_of = [&](int sp, int ct) __attribute__((always_inline)) {
+    return *reinterpret_cast<const v4f*>(part_o + (((qi * nsplit + sp) * kNHG + hg) * kTiles + ct) * (kWave * 4) +
+                                         4 * l);
+  };
+  if (nsplit <= 4) {
+    // every load of the wave in flight at once
+    v4f ma[4], mb[4], x[4][KT];
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+      if (sp < nsplit) {
+        ml_of(sp, ma[sp], mb[sp]);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) x[sp][t] = po_of(sp, ct0 + t);
+      }
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+      if (sp < nsplit) {
+        M[0] = fmaxf(M[0], ma[sp][0]); M[1] = fmaxf(M[1], ma[sp][2]);
+        M[2] = fmaxf(M[2], mb[sp][0]); M[3] = fmaxf(M[3], mb[sp][2]);
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+      if (sp < nsplit) {
+        const float mi[4] = {ma[sp][0], ma[sp][2], mb[sp][0], mb[sp][2]};
+        const float li[4] = {ma[sp][1], ma[sp][3], mb[sp][1], mb[sp][3]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
+          den[i] = fmaf(wgt, li[i], den[i]);
+#pragma unroll
+          for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[sp][t][i], acc[t][i]);
+        }
+      }
+    merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
+    return;
+  }
+  for (int sp = 0; sp < nsplit; ++sp) {
+    v4f a, b;
+    ml_of(sp, a, b);
+    M[0] = fmaxf(M[0], a[0]); M[1] = fmaxf(M[1], a[2]);
+    M[2] = fmaxf(M[2], b[0]); M[3] = fmaxf(M[3], b[2]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
+  for (int sp = 0; sp < nsplit; ++sp) {
+    v4f a, b;
+    ml_of(sp, a, b);
+    v4f x[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) x[t] = po_of(sp, ct0 + t);
+    const float mi[4] = {a[0], a[2], b[0], b[2]};
+    const float li[4] = {a[1], a[3], b[1], b[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
+      den[i] = fmaf(wgt, li[i], den[i]);
+#pragma unroll
+      for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[t][i], acc[t][i]);
+    }
+  }
+  merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
+}
 
 template <int kSrc, int kParts, int kWaves, int kFmt = kFmtBf16>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
@@ -233,9 +362,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
     (VM) |= static_cast<uint32_t>(~p_ & 1u) << (R);                                    \
     if (kFmt != kFmtBf16 && (p_ & 2u)) {             /* raw share, decoded at the store */ \
       (VM) |= 1u << (8 + (R));                                                         \
-      ST##R = load_row8<kFmt>(p_ & ~static_cast<uint64_t>(3), l);                     \
+      (ST)[R] = load_row8<kFmt>(p_ & ~static_cast<uint64_t>(3), l);                   \
     } else                                                                             \
-      ST##R = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
+      (ST)[R] = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
   } while (0)
 #define CSA_ATT_LOAD(CH, ST, VM)                                                        \
   do {                                                                                 \
@@ -264,8 +393,8 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   } while (0)
 #define CSA_ATT_STORE1(BUF, ST, R, VM)                                                  \
   do {                                                                                 \
-    if (kFmt != kFmtBf16 && (((VM) >> (8 + (R))) & 1u)) ST##R = decode_row8<kFmt>(ST##R, l); \
-    *reinterpret_cast<v4u*>((BUF) + (Sh::kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = ST##R; \
+    if (kFmt != kFmtBf16 && (((VM) >> (8 + (R))) & 1u)) (ST)[R] = decode_row8<kFmt>((ST)[R], l); \
+    *reinterpret_cast<v4u*>((BUF) + (Sh::kRowsPerWave * wave + (R)) * kRowStride + 16 * l) = (ST)[R]; \
   } while (0)
 #define CSA_ATT_STORE(SLOT, ST, VM)                                                     \
   do {                                                                                 \
@@ -394,52 +523,62 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
     }
   };
 
-  // Pipeline over chunks c (ring slot c % 3, exchange buffer c % 2), two per loop trip (no
-  // exit between them, which keeps the compiler's load counts exact; an odd last chunk is
-  // finished after the loop from what is already in LDS): iteration c finishes
-  // chunk c (its shares were exchanged before the last barrier) and forms the S^T share of
-  // chunk c+1, moves chunk c+2 from registers into its slot and starts the loads of chunk
-  // c+4; one barrier per chunk.  Every iteration issues its four loads, also past the
-  // split's end (zero row), so the count of loads in flight is the same on every path
-  // and the compiler's waits before a store only cover the set being stored; stores past
-  // the end go to a slot no later step reads for a result.
-  v4u stA0, stA1, stA2, stA3;
-  v4u stB0, stB1, stB2, stB3;
-  uint32_t vA = 0, vB = 0;
-  CSA_ATT_LOAD(ch0, stA, vA);
-  CSA_ATT_LOAD(ch0 + 1, stB, vB);
+  // Pipeline over chunks c (ring slot c % 3, exchange buffer c % 2) with kDepth register
+  // sets of row loads in flight, kDepth chunks per loop trip (no exit between them, which
+  // keeps the compiler's load counts exact; the last ch1 - ch < kDepth chunks are finished
+  // after the loop): step c finishes chunk c (its shares were exchanged before the last
+  // barrier) and forms the S^T share of chunk c+1, moves chunk c+2 from registers into its
+  // slot and starts the loads of chunk c+2+kDepth into the set it freed; one barrier per
+  // chunk.  Chunk x lives in set (x - ch0) % kDepth.  Every step issues its loads, also
+  // past the split's end (zero rows), so the count of loads in flight is the same on every
+  // path and the compiler's waits before a store only cover the set being stored; stores
+  // past the end go to a slot no later step reads for a result.
+  constexpr int kDepth = Sh::kDepth;
+  v4u st[kDepth][4];
+  uint32_t vm[kDepth];
+#pragma unroll
+  for (int i = 0; i < kDepth; ++i) CSA_ATT_LOAD(ch0 + i, st[i], vm[i]);
   int sl = ch0 % kRing;                               // slot of chunk ch
   const int sl1 = sl == kRing - 1 ? 0 : sl + 1;
-  CSA_ATT_STORE(sl, stA, vA);
-  CSA_ATT_LOAD(ch0 + 2, stA, vA);
+  CSA_ATT_STORE(sl, st[0], vm[0]);
+  CSA_ATT_LOAD(ch0 + kDepth, st[0], vm[0]);
   barrier_lds();
   s_part(sl, ch0 & 1);
-  CSA_ATT_STORE(sl1, stB, vB);
-  CSA_ATT_LOAD(ch0 + 3, stB, vB);
+  CSA_ATT_STORE(sl1, st[1], vm[1]);
+  CSA_ATT_LOAD(ch0 + kDepth + 1, st[1], vm[1]);
   barrier_lds();
   int ch = ch0;
 #pragma unroll 1
-  for (; ch + 1 < ch1; ch += 2) {
-    {
-      const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of ch + 1
-      const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of ch + 2
-      softmax_pv(sl, ch & 1, sn, (ch + 1) & 1, std::true_type{});
-      CSA_ATT_STORE(s2, stA, vA);
-      CSA_ATT_LOAD(ch + 4, stA, vA);
-      barrier_lds();
-      sl = sn;
-    }
-    {
-      const int sn = sl == kRing - 1 ? 0 : sl + 1;
-      const int s2 = sn == kRing - 1 ? 0 : sn + 1;
-      softmax_pv(sl, (ch + 1) & 1, sn, ch & 1, std::true_type{});   // past the split's end: S^T unused
-      CSA_ATT_STORE(s2, stB, vB);
-      CSA_ATT_LOAD(ch + 5, stB, vB);
+  for (; ch + kDepth - 1 < ch1; ch += kDepth) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) {
+      const int c = ch + i;
+      const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of c + 1
+      const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of c + 2
+      softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});   // past the split's end: S^T unused
+      CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
+      CSA_ATT_LOAD(c + 2 + kDepth, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
       barrier_lds();
       sl = sn;
     }
   }
-  if (ch < ch1) softmax_pv(sl, ch & 1, sl, ch & 1, std::false_type{});
+  // the last chunks: ch and ch + 1 are in their slots, the later ones in their sets
+#pragma unroll
+  for (int i = 0; i < kDepth - 1; ++i) {
+    const int c = ch + i;
+    if (c < ch1) {
+      const int sn = sl == kRing - 1 ? 0 : sl + 1;
+      const int s2 = sn == kRing - 1 ? 0 : sn + 1;
+      if (c + 1 < ch1) {
+        softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});
+        if (c + 2 < ch1) CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
+        barrier_lds();
+      } else {
+        softmax_pv(sl, c & 1, sl, c & 1, std::false_type{});
+      }
+      sl = sn;
+    }
+  }
 #undef CSA_ATT_LOAD1
 #undef CSA_ATT_LOAD
 #undef CSA_ATT_STORE1
@@ -532,12 +671,6 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
 #pragma unroll
     for (int t = 0; t < KT; ++t) acc[t][i] = 0.0f;
   }
-  // (m, l) of the lane's 4 heads: 32 contiguous bytes per split
-  auto ml_of = [&](int sp, v4f& a, v4f& b) __attribute__((always_inline)) {
-    const v4f* p = reinterpret_cast<const v4f*>(part_ml + ((qi * nsplit + sp) * kAH + h0) * 2);
-    a = p[0];                                                 // m0 l0 m1 l1
-    b = p[1];                                                 // m2 l2 m3 l3
-  };
   auto po_of = [&](int sp, int ct) __attribute__((always_inline)) {
     return *reinterpret_cast<const v4f*>(part_o + (((qi * nsplit + sp) * kNHG + hg) * kTiles + ct) * (kWave * 4) +
                                          4 * l);
@@ -584,54 +717,9 @@ __global__ __launch_bounds__(256) void attn_merge_tiles(const float* __restrict_
           for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[sp][t][i], acc[t][i]);
         }
       }
+    merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
   } else {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      v4f a, b;
-      ml_of(sp, a, b);
-      M[0] = fmaxf(M[0], a[0]); M[1] = fmaxf(M[1], a[2]);
-      M[2] = fmaxf(M[2], b[0]); M[3] = fmaxf(M[3], b[2]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
-    for (int sp = 0; sp < nsplit; ++sp) {
-      v4f a, b;
-      ml_of(sp, a, b);
-      v4f x[KT];
-#pragma unroll
-      for (int t = 0; t < KT; ++t) x[t] = po_of(sp, ct0 + t);
-      const float mi[4] = {a[0], a[2], b[0], b[2]};
-      const float li[4] = {a[1], a[3], b[1], b[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
-        den[i] = fmaf(wgt, li[i], den[i]);
-#pragma unroll
-        for (int t = 0; t < KT; ++t) acc[t][i] = fmaf(wgt, x[t][i], acc[t][i]);
-      }
-    }
-  }
-  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct0 + (l & 15);
-  const int64_t tq = rope_d > 0 ? q_pos[qi] : 0;
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f;
-    // inverse RoPE of the output (lane pairs hold channel pairs)
-    if (rope_d > 0 && 16 * (ct0 + t) + 16 > kAC - rope_d) {
-      const int col = 16 * (ct0 + t) + (l & 15);
-      float cs = 1.0f, sn = 0.0f;
-      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_r, tq, cs, sn);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(v[i]);
-  }
-  if (lse && ct0 == 0 && (l & 15) == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
+    merge_splits<KT>(part_o, part_ml, sink, nsplit, qi, hg, ct0, out, lse, q_pos, rope_d, rope_r);
   }
 }
 
