@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense MFMA
 BF16_PEAK_TFLOPS = 2500.0      # dense MFMA
 ALL_SUBS = ("prefill", "pro", "hca", "compressor", "prefill_attention", "decode_layer")
-ROOFLINE_KERNEL = "index_score_fp8_decode<true, true>"
+ROOFLINE_KERNEL = "index_score_fp8_decode<true, true, false, false>"
 
 
 def parse():
@@ -109,11 +109,11 @@ def counter_kernels():
         ("index_score_segments_flash_decode_b32", ROOFLINE_KERNEL, None, INDEXER_SOURCES,
          index_segments_bytes(f.B, 1, f.n_c, f.H_I, f.d_I, f.k),
          "keys + scales (132 B per entry), q codes + scales + w, positions, 8 x 512 candidate pairs per query"),
-        ("attn_select_flash_decode_b32", "attn_bf16<2, 4, 8>", None, ATTN_SOURCES, fl_rows,
+        ("attn_select_flash_decode_b32", "attn_bf16<2, 4, 8, 0>", None, ATTN_SOURCES, fl_rows,
          "candidate pairs, window + selected rows (1 KiB each), q (the split partials it writes are not counted)"),
-        ("attn_merge_flash_decode_b32", "attn_merge_tiles<4>", 32 * 8 * 8 * 256, ATTN_SOURCES,
+        ("attn_merge_flash_decode_b32", "attn_merge_tiles<4>", 32 * 8 * 256, ATTN_SOURCES,
          f.B * f.H * f.c * 2, "the bf16 output (the split partials it reads are not counted)"),
-        ("attn_hca_decode_b64", "attn_bf16<1, 2, 8>", None, ATTN_SOURCES, hca_rows,
+        ("attn_hca_decode_b64", "attn_bf16<1, 2, 8, 0>", None, ATTN_SOURCES, hca_rows,
          "window + every visible entry (1 KiB each), q (the split partials it writes are not counted)"),
     ]
 
@@ -241,7 +241,7 @@ def summarize_trace(trace_dir, bench_log):
 
 MFMA_CMD = ("rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
             "--kernel-include-regex index_score_fp8_prefill --output-format csv -d <dir> -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-other --no-cpu-baseline --eager")
+            "python3 <repo>/bench.py --steps 2 --warmup 1 --subs prefill --no-cpu-baseline --eager")
 
 
 class TimingEvents:

@@ -15,6 +15,12 @@ constexpr int kRowStride = kAC * 2 + 32;            // bytes
 constexpr int kChunkBytes = kRows * kRowStride;
 constexpr int kMaxSplitChunks = 72;                 // chunks of row addresses tabled per workgroup
 constexpr float kLazy = 8.0f;                       // log2 units
+
+// Where the remote rows of a query come from.
+constexpr int kSrcIdx = 0;     // idx[q][0..k): selected entries, -1 = none
+constexpr int kSrcDense = 1;   // every visible entry (HCA)
+constexpr int kSrcCand = 2;    // the k best of the query's segment candidates, selected in the kernel
+constexpr int kSrcCand2 = 3;   // the same from up to twice as many candidates
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -164,6 +170,39 @@ __device__ __forceinline__ bool attn_unit(int nq, int units, int& qi, int& u) {
   u = t8 % units;
   qi = (t8 / units) * 8 + xcd;
   return qi < nq;
+}
+
+// One wave's KT tiles from the merged numerators acc, denominators den and reference
+// maxima M (log2 units) of the lane's 4 heads: division, inverse RoPE, bf16 cast; the wave
+// holding tile 0 writes the lse of its heads.
+template <int KT>
+__device__ __forceinline__ void merge_store(const float (&acc)[KT][4], const float (&den)[4], const float (&M)[4],
+                                            size_t qi, int h0, int ct0, int l, uint16_t* __restrict__ out,
+                                            float* __restrict__ lse, const int64_t* __restrict__ q_pos, int rope_d,
+                                            double rope_r) {
+  uint16_t* dst = out + (qi * kAH + h0) * kAC + 16 * ct0 + (l & 15);
+  const int64_t tq = rope_d > 0 ? q_pos[qi] : 0;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = den[i] > 0.0f ? acc[t][i] / den[i] : 0.0f;
+    // inverse RoPE of the output (lane pairs hold channel pairs)
+    if (rope_d > 0 && 16 * (ct0 + t) + 16 > kAC - rope_d) {
+      const int col = 16 * (ct0 + t) + (l & 15);
+      float cs = 1.0f, sn = 0.0f;
+      if (col >= kAC - rope_d) rope_cs_sn(col, kAC, rope_d, rope_r, tq, cs, sn);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i * kAC + 16 * t] = f32_to_bf16(v[i]);
+  }
+  if (lse && ct0 == 0 && (l & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lse[qi * kAH + h0 + i] = (M[i] == -INFINITY || den[i] <= 0.0f) ? -INFINITY : (M[i] + log2f(den[i])) * kLn2;
+  }
 }
 
 }  // namespace csa
