@@ -729,7 +729,7 @@ def bench_prefill_attention(torch, L, I, dev, reps=5):
             "note": "P enters P.V as bf16 hi + lo: the MFMA work is 1.5x these flops"}
 
 
-def bench_prefill_compressor(torch, L, I, dev, reps=5):
+def bench_prefill_compressor(torch, L, I, dev, reps=20):
     """Compressor over one prefill chunk: 8192 new tokens (+4 from the previous block), d = 5120,
     main KV (c = 512, bf16 out) and indexer K (c = 128, FP8 out)."""
     sh = I.PREFILL
@@ -749,8 +749,8 @@ def bench_prefill_compressor(torch, L, I, dev, reps=5):
     ms_m = _timed(torch, lambda i: L.csa_compress(hid, prev, Wm, Bm, c=sh.c, out=kv, ws=ws, **kw), reps)
     ms_i = _timed(torch, lambda i: L.csa_compress(hid, prev, Wi, Bi, c=sh.d_I, out=kI, out_scale=kIs, ws=ws, **kw),
                   reps)
-    rows = sh.S + sh.m
-    f_m, f_i = 2.0 * rows * sh.d * 4 * sh.c, 2.0 * rows * sh.d * 4 * sh.d_I
+    # each entry pools 2m slots of (C, Z): 4c projected values per token of the chunk
+    f_m, f_i = 2.0 * sh.S * sh.d * 4 * sh.c, 2.0 * sh.S * sh.d * 4 * sh.d_I
     return {"workload": "csa_prefill_chunk8192_d5120_compressor", "main_ms": ms_m, "indexer_ms": ms_i,
             "main_tflops": f_m / (ms_m * 1e-3) / 1e12, "indexer_tflops": f_i / (ms_i * 1e-3) / 1e12,
             "main_frac_bf16_peak": f_m / (ms_m * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,

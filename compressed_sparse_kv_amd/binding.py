@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
         "csa_status_string": ([i], ctypes.c_char_p),
         "csa_version": ([], i),
         "csa_compress_workspace_size": ([i, i, i, i, i, i], sz),
-        "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, vp, sz, vp], i),
+        "csa_compress": ([vp, vp, i, vp, vp, i, i, i, i, i, i, i, f, f, i64, vp, vp, i, i, i, vp, sz, vp], i),
         "csa_compress_state_size": ([i, i, i, i, i], sz),
         "csa2_compress_workspace_size": ([i, i, i, i], sz),
         "csa2_compress": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, f, i64, vp, vp, i, vp, vp, i, vp, sz, vp], i),
@@ -152,18 +152,25 @@ def compress_workspace_size(B, T, m, c, overlap, has_prev) -> int:
 
 def csa_compress(hidden, hidden_prev, w_proj, bias, *, overlap: bool, m: int, c: int, d_rope: int,
                  rope_theta: float, rms_eps: float, p0: int, out, out_scale=None, out_dtype: int | None = None,
-                 ws=None, stream=None):
+                 layout: int = CSA_LAYOUT_ROWS, Nc_max: int | None = None, ws=None, stream=None):
     """hidden [B,T,d], hidden_prev [B,m,d] or None, w_proj [S*c, d], bias [S/2,m,c] fp32,
     out [B,T/m,c] (fp32 / bf16 / uint8 codes with out_scale [B,T/m]); out_dtype (default:
     from out's dtype) selects the low-precision types: CSA_FP4_E2M1 (codes [B,T/m,c/2],
-    out_scale uint8 [B,T/m,c/32]), CSA_PACKED_FP4_E4M3 / CSA_PACKED_FP8_ROPE (uint8 rows)."""
+    out_scale uint8 [B,T/m,c/32]), CSA_PACKED_FP4_E4M3 / CSA_PACKED_FP8_ROPE (uint8 rows).
+    layout=CSA_LAYOUT_B16 (FP8, c = 128): out is the 16-entry blocked cache of Nc_max
+    entries per sequence and out_scale [B,Nc_max]; the chunk's entries land at p0/m on."""
     _dev(hidden, hidden_prev, w_proj, bias, out, out_scale)
     B, T, d = hidden.shape
+    if layout != CSA_LAYOUT_ROWS:
+        if Nc_max is None:
+            raise ValueError("Nc_max is required for the blocked layout")
+        out_dtype = CSA_FP8_E4M3
     ws, wsb = _ws(compress_workspace_size(B, T, m, c, overlap, hidden_prev is not None), ws, hidden.device)
     _check("csa_compress", _lib.csa_compress(
         _p(hidden), _p(hidden_prev), _dtype(hidden), _p(w_proj), _p(bias), int(overlap), B, T, d, m, c,
         d_rope, float(rope_theta), float(rms_eps), int(p0), _p(out), _p(out_scale),
-        _dtype(out) if out_dtype is None else int(out_dtype), _p(ws), wsb, _stream(stream)))
+        _dtype(out) if out_dtype is None else int(out_dtype), int(layout), int(Nc_max or 0), _p(ws), wsb,
+        _stream(stream)))
     return out
 
 

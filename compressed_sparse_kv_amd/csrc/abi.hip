@@ -17,7 +17,7 @@ size_t attn_workspace_bytes(int, int, int, int, int, int);
 size_t attn_scratch_bytes();
 int attn_scratch(void**);
 int launch_compress(const void*, const void*, int, const void*, const float*, int, int, int, int, int, int, int,
-                    float, float, int64_t, void*, float*, int, void*, hipStream_t);
+                    float, float, int64_t, void*, float*, int, int, int, void*, hipStream_t);
 size_t compress_workspace_bytes(int, int, int, int, int, int);
 size_t compress_state_bytes(int, int, int, int, int);
 size_t csa2_workspace_bytes(int, int, int, int);
@@ -73,7 +73,7 @@ const char* csa_status_string(int status) {
   }
 }
 
-int csa_version(void) { return 300; }
+int csa_version(void) { return 400; }
 
 // ---- stage 1 ------------------------------------------------------------------------
 size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev) {
@@ -98,8 +98,10 @@ static int check_entry_dtype(int dt, const void* out, const void* scale, int c, 
 
 int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, const void* w_proj, const float* bias,
                  int overlap, int B, int T, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
-                 int64_t p0, void* out, float* out_scale, int out_dtype, void* ws, size_t ws_bytes, void* stream) {
+                 int64_t p0, void* out, float* out_scale, int out_dtype, int out_layout, int Nc_max, void* ws,
+                 size_t ws_bytes, void* stream) {
   CSA_REQUIRE(hidden && w_proj && bias && out);
+  CSA_REQUIRE(out_layout == CSA_LAYOUT_ROWS || out_layout == CSA_LAYOUT_B16);
   CSA_REQUIRE(overlap == 0 || overlap == 1);
   CSA_REQUIRE(B > 0 && T > 0 && d > 0 && m > 0 && c > 0);
   CSA_REQUIRE(T % m == 0 && p0 >= 0 && p0 % m == 0);
@@ -111,11 +113,16 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype, cons
   if (ot != CSA_OK) return ot;
   if (in_dtype == CSA_BF16 && d % 64 != 0) return CSA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(B) * (T + m) * 4 * c > (int64_t{1} << 40)) return CSA_ERR_UNSUPPORTED;
+  if (out_layout == CSA_LAYOUT_B16) {
+    // the chunk's entries p0/m .. p0/m + T/m - 1 must lie inside the cache of Nc_max entries
+    if (out_dtype != CSA_FP8_E4M3 || c != 128) return CSA_ERR_UNSUPPORTED;
+    CSA_REQUIRE(Nc_max > 0 && p0 / m + T / m <= Nc_max && static_cast<int64_t>(B) * Nc_max * c < (int64_t{1} << 40));
+  }
   const int has_prev = hidden_prev != nullptr;
   CSA_REQUIRE(aligned16(ws));
   if (ws == nullptr || ws_bytes < compress_workspace_bytes(B, T, m, c, overlap, has_prev)) return CSA_ERR_WORKSPACE;
   return launch_compress(hidden, hidden_prev, in_dtype, w_proj, bias, overlap, B, T, d, m, c, d_rope, rope_theta,
-                         rms_eps, p0, out, out_scale, out_dtype, ws, as_stream(stream));
+                         rms_eps, p0, out, out_scale, out_dtype, out_layout, Nc_max, ws, as_stream(stream));
 }
 
 size_t csa2_compress_workspace_size(int B, int T, int m, int c) {

@@ -123,7 +123,17 @@ int csa_version(void);
  *               exponent e = ceil(log2(amax/448)) over the 448 channels without RoPE, the
  *               RoPE channels in bf16, RNE).  out_scale is ignored for the types without
  *               a separate scale.
- *   ws          >= csa_compress_workspace_size(...) bytes (holds the projection).
+ *   out_layout  CSA_LAYOUT_ROWS: out as above (the chunk's entries only; Nc_max unused).
+ *               CSA_LAYOUT_B16 (CSA_FP8_E4M3 with c = 128): out is the sequence caches of
+ *               Nc_max entries in the 16-entry blocks of csa_index_keys_b16
+ *               (csa_index_keys_b16_size(B, Nc_max) bytes) and out_scale [B, Nc_max]; entry i
+ *               of the chunk is cache entry p0/m + i (p0/m + T/m <= Nc_max); other entries
+ *               are left as they are.  The bytes equal csa_index_keys_b16 of the rows.
+ *   ws          >= csa_compress_workspace_size(...) bytes (the projection, or for bf16
+ *               inputs with overlap and m = 4 the pooled vectors, which need less).
+ * The bf16 overlapping compressor with m = 4 and c % 64 == 0 runs the projection and the
+ * pooling in one kernel; other shapes project first, then pool.  Results agree within
+ * fp32 rounding order.
  * ------------------------------------------------------------------------------ */
 size_t csa_compress_workspace_size(int B, int T, int m, int c, int overlap, int has_prev);
 
@@ -131,7 +141,7 @@ int csa_compress(const void* hidden, const void* hidden_prev, int in_dtype,
                  const void* w_proj, const float* bias, int overlap,
                  int B, int T, int d, int m, int c, int d_rope, float rope_theta,
                  float rms_eps, int64_t p0,
-                 void* out, float* out_scale, int out_dtype,
+                 void* out, float* out_scale, int out_dtype, int out_layout, int Nc_max,
                  void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------

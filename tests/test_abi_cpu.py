@@ -65,22 +65,31 @@ def test_invalid_arguments_are_rejected_before_launch():
     args = dict(hidden=fake, prev=None, dt=0, w=fake, bias=fake, ov=1, B=1, T=10, d=64, m=4, c=8, dr=4)
     call = lambda **kw: lib.csa_compress(kw["hidden"], kw["prev"], kw["dt"], kw["w"], kw["bias"], kw["ov"],
                                          kw["B"], kw["T"], kw["d"], kw["m"], kw["c"], kw["dr"], 1e4, 1e-6,
-                                         kw.get("p0", 0), fake, None, 0, fake, 1 << 30, None)
+                                         kw.get("p0", 0), fake, None, 0, 0, 0, fake, 1 << 30, None)
     assert call(**args) == 1
     assert call(**{**args, "T": 8, "p0": 4}) == 1
     assert call(**{**args, "T": 8, "dt": 1, "d": 96}) == 2
     # compressor workspace too small
-    assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0,
+    assert lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, 8, 4, 1e4, 1e-6, 0, fake, None, 0, 0, 0,
                             fake, 8, None) == 3
     # low-precision entry types: packed rows need c = 512 (FP8 + RoPE also d_rope = 64), MXFP4
     # needs its scale bytes and c % 32 == 0, unknown types are invalid
     comp = lambda c, d_rope, dt, scale: lib.csa_compress(fake, None, 0, fake, fake, 1, 1, 8, 64, 4, c, d_rope, 1e4,
-                                                         1e-6, 0, fake, scale, dt, fake, 1 << 30, None)
+                                                         1e-6, 0, fake, scale, dt, 0, 0, fake, 1 << 30, None)
     assert comp(256, 64, 4, None) == 2
     assert comp(512, 32, 5, None) == 2
     assert comp(128, 64, 3, None) == 1
     assert comp(48, 16, 3, fake) == 2
     assert comp(512, 64, 6, None) == 1
+    # the blocked key layout: FP8 codes of c = 128 only, a cache that holds the chunk's entries
+    blk = lambda c, dt, p0, Nc_max, layout=1: lib.csa_compress(fake, fake, 1, fake, fake, 1, 1, 64, 64, 4, c, 64, 1e4,
+                                                               1e-6, p0, fake, fake, dt, layout, Nc_max, fake, 1 << 30,
+                                                               None)
+    assert blk(128, 2, 0, 16, layout=2) == 1
+    assert blk(512, 2, 0, 16) == 2
+    assert blk(128, 1, 0, 16) == 2
+    assert blk(128, 2, 16, 19) == 1                                   # entries 4 .. 19 do not fit 19
+    assert blk(128, 2, 0, 0) == 1
     # segment candidates: shape outside the decode path, candidate buffer too small, null idx
     assert lib.csa_index_score_segments(fake, fake, fake, fake, fake, fake, 1, 8, 64, 128, 3000, 4, 128, None,
                                         fake, 1 << 30, None) == 2

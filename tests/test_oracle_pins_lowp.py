@@ -129,3 +129,35 @@ def test_lowp_row_checks_accept_the_oracle_rows_and_catch_layout_mistakes():
     bad[:, 448:576] = np.roll(bad[:, 448:576], 2, axis=-1)    # RoPE channels shifted by one
     with pytest.raises(AssertionError):
         assert_packed_fp8_rope_rows(bad, x)
+
+
+def test_fp8_row_check_accepts_the_oracle_rows_and_catches_mistakes():
+    # the GPU-side FP8 row check (tests/parity.py) on the oracle's own quantisation, on values
+    # moved by less than the fp32 tolerance, and on rows with a plausible mistake
+    import pytest
+    from tests.parity import assert_fp8_rows
+    rng = np.random.default_rng(78)
+    x = rng.standard_normal((4, 128))
+    codes, sc = O.quantize_rows_e4m3(x)
+    assert assert_fp8_rows(codes, sc, x) == 0
+    # a value 5e-6 past a rounding midpoint may take either code
+    v = x / sc[:, None].astype(np.float64)
+    mid = np.array([1.0625, -2.125])                       # midpoints between e4m3 codes
+    y = x.copy()
+    y[0, :2] = mid * sc[0]
+    y[0, :2] += np.sign(mid) * 5e-6
+    c2, s2 = O.quantize_rows_e4m3(y)
+    flipped = c2.copy()
+    flipped[0, :2] = O.f64_to_e4m3fn(np.array([1.0, -2.0]))   # the other side of the midpoint
+    assert assert_fp8_rows(flipped, s2, y) == 2
+    bad = codes.copy()                                    # the row maximum (448) one code lower
+    j = int(np.argmax(np.abs(v[1])))
+    bad[1, j] = O.f64_to_e4m3fn(np.array([v[1, j] * 416.0 / 448.0]))[0]
+    with pytest.raises(AssertionError):
+        assert_fp8_rows(bad, sc, x)
+    with pytest.raises(AssertionError):                   # two channels swapped
+        sw = codes.copy()
+        sw[2, [3, 40]] = sw[2, [40, 3]]
+        if sw[2, 3] == codes[2, 3]:
+            sw[2, 3] ^= 0x08
+        assert_fp8_rows(sw, sc, x)
