@@ -401,9 +401,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     cand = torch.empty(L.index_segments_size(B, 1, Nc, k), dtype=torch.uint8, device=dev)
-    # Each set's key cache in the 16-entry blocked layout.  A decode loop builds it entry by
-    # entry with csa_compress_decode (layout CSA_LAYOUT_B16), which writes the same bytes
-    # (tested); here the precompressed cache is laid out once per set before timing.
+    # Each set's key cache in the 16-entry blocked layout.  The compressors write this layout
+    # themselves: csa_compress (prefill chunks) and csa_compress_decode (one entry per block
+    # boundary) with CSA_LAYOUT_B16, the same bytes as this re-layout (tested); the
+    # synthetic precompressed cache here is laid out once per set before timing.
     for s in sets:
         s["k16"] = L.csa_index_keys_b16(s["k8"], torch.empty(L.index_keys_b16_size(B, Nc), dtype=torch.uint8,
                                                              device=dev))

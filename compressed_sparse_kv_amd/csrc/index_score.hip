@@ -276,7 +276,8 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfQ = kPfWaves;            // one query per wave
-constexpr int kPfTile = 64;               // entries per LDS tile
+constexpr int kPfSub = 1;                // 64-entry parts per LDS tile (2: one barrier per 128 entries, measured slower: 4 more VGPRs spill)
+constexpr int kPfTile = 64 * kPfSub;      // entries per LDS tile
 constexpr int kPfStride = 2 * kID + 16;   // LDS row stride in bytes (bf16 rows)
 
 __global__ __launch_bounds__(kPfThreads, 4) void index_score_fp8_prefill(
@@ -310,63 +311,66 @@ __global__ __launch_bounds__(kPfThreads, 4) void index_score_fp8_prefill(
   const float* ksb = ks + static_cast<size_t>(b) * Nc;
   float* out = scores + qrow * Nc;
   const int ntiles_vis = cdiv(wg_vis, kPfTile);
-  const int ntiles = cdiv(Nc, kPfTile);
 
-  // cooperative tile load: thread t converts codes 16*(t%8) .. +15 of entry t/8
+  // cooperative tile load: thread t converts codes 16*(t%8) .. +15 of entry t/8 of each
+  // 64-entry part of the tile
   const int le = tid >> 3, lb = 16 * (tid & 7);
-  uint4 raw;
-#define CSA_PF_GLOAD(ti)                                                                    \
-  do {                                                                                      \
-    const int e_ = min((ti) * kPfTile + le, Nc - 1);                                        \
-    raw = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(e_) * kID + lb);         \
-  } while (0)
-#define CSA_PF_SWRITE(buf)                                                                  \
-  do {                                                                                      \
-    const unsigned wd_[4] = {raw.x, raw.y, raw.z, raw.w};                                   \
-    unsigned cv_[8];                                                                        \
-    _Pragma("unroll") for (int q_ = 0; q_ < 4; ++q_) {                                      \
-      cv_[2 * q_] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd_[q_], 1.0f, false)); \
-      cv_[2 * q_ + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd_[q_], 1.0f, true)); \
-    }                                                                                       \
-    uint4* dst_ = reinterpret_cast<uint4*>(&tile[buf][le * kPfStride + 2 * lb]);            \
-    dst_[0] = make_uint4(cv_[0], cv_[1], cv_[2], cv_[3]);                                   \
-    dst_[1] = make_uint4(cv_[4], cv_[5], cv_[6], cv_[7]);                                   \
-  } while (0)
+  uint4 raw[kPfSub];
+  auto gload = [&](int ti) {
+#pragma unroll
+    for (int j = 0; j < kPfSub; ++j) {
+      const int e = min(ti * kPfTile + 64 * j + le, Nc - 1);
+      raw[j] = *reinterpret_cast<const uint4*>(kb + static_cast<size_t>(e) * kID + lb);
+    }
+  };
+  auto swrite = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < kPfSub; ++j) {
+      const unsigned wd[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      unsigned cv[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cv[2 * q] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.0f, false));
+        cv[2 * q + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[q], 1.0f, true));
+      }
+      uint4* dst = reinterpret_cast<uint4*>(&tile[buf][(64 * j + le) * kPfStride + 2 * lb]);
+      dst[0] = make_uint4(cv[0], cv[1], cv[2], cv[3]);
+      dst[1] = make_uint4(cv[4], cv[5], cv[6], cv[7]);
+    }
+  };
 
-  // row scales travel one tile ahead of their use, like the codes
-  float sk_next = 0.0f;
   if (ntiles_vis > 0) {
-    CSA_PF_GLOAD(0);
-    sk_next = ksb[min(l, Nc - 1)];
-    CSA_PF_SWRITE(0);
+    gload(0);
+    swrite(0);
   }
   __syncthreads();
 #pragma unroll 1
   for (int ti = 0; ti < ntiles_vis; ++ti) {
     const int buf = ti & 1;
     const bool more = ti + 1 < ntiles_vis;
-    const float sk = sk_next;
-    if (more) {
-      CSA_PF_GLOAD(ti + 1);
-      sk_next = ksb[min((ti + 1) * kPfTile + l, Nc - 1)];
-    }
-    const int e = ti * kPfTile + l;
-    float p[4];
+    // the row scales of this tile, used after its MFMAs (their latency hides behind them)
+    float sk[kPfSub];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      v8s bk[4];
+    for (int j = 0; j < kPfSub; ++j) sk[j] = ksb[min(ti * kPfTile + 64 * j + l, Nc - 1)];
+    if (more) gload(ti + 1);
 #pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4)
-        bk[k4] = *reinterpret_cast<const v8s*>(&tile[buf][(16 * nb + (l & 15)) * kPfStride + 64 * g + 16 * k4]);
-      p[nb] = head_sum1(a, bk, wv);
+    for (int j = 0; j < kPfSub; ++j) {
+      const int e = ti * kPfTile + 64 * j + l;
+      float p[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        v8s bk[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+          bk[k4] = *reinterpret_cast<const v8s*>(&tile[buf][(64 * j + 16 * nb + (l & 15)) * kPfStride + 64 * g + 16 * k4]);
+        p[nb] = head_sum1(a, bk, wv);
+      }
+      const float v = reduce_scatter4(p);
+      if (qlive && e < Nc) out[e] = e < nvis ? v * sk[j] : -INFINITY;
     }
-    const float v = reduce_scatter4(p);
-    if (qlive && e < Nc) out[e] = e < nvis ? v * sk : -INFINITY;
-    if (more) CSA_PF_SWRITE(buf ^ 1);
+    if (more) swrite(buf ^ 1);
     __syncthreads();
   }
-#undef CSA_PF_GLOAD
-#undef CSA_PF_SWRITE
   // tiles no query of this workgroup can see
   if (qlive)
     for (int e = ntiles_vis * kPfTile + l; e < Nc; e += 64) out[e] = -INFINITY;
