@@ -115,10 +115,26 @@ def counter_kernels():
          f.B * f.H * f.c * 2, "the bf16 output (the split partials it reads are not counted)"),
         ("attn_hca_decode_b64", "attn_bf16<1, 2, 8, 0>", None, ATTN_SOURCES, hca_rows,
          "window + every visible entry (1 KiB each), q (the split partials it writes are not counted)"),
+        ("compress_fused_prefill_chunk8192_main", COMPRESS_MAIN_KERNEL, None, COMPRESS_SOURCES,
+         compress_main_bytes(), "hidden rows of the chunk + the 4 before it, w_proj, bias, pooled vectors written"),
     ]
 
 
-COUNTER_BENCH_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy --eager --subs hca"
+# The fused compressor kernels of the prefill chunk (main: 256-token tiles; indexer: 64-token tiles)
+COMPRESS_MAIN_KERNEL = "compress_fused<csa::FusedShape<4, 2, 4, 2, 64, 2>"
+COMPRESS_IDX_KERNEL = "compress_fused<csa::FusedShape<1, 1, 4, 2, 64, 2>"
+COMPRESS_SOURCES = ("compress.hip", "entry_store.hpp", "common.hpp")
+
+
+def compress_main_bytes():
+    """Algorithmic bytes of the main compressor's fused kernel on the prefill chunk: bf16
+    hidden rows (T + m), bf16 w_proj [4c, d], the fp32 bias, the fp32 pooled vectors."""
+    from synthetic import inputs as I
+    sh = I.PREFILL
+    return (sh.S + sh.m) * sh.d * 2 + 4 * sh.c * sh.d * 2 + 2 * sh.m * sh.c * 4 + (sh.S // sh.m) * sh.c * 4
+
+
+COUNTER_BENCH_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --calibrate-copy --eager --subs hca,compressor"
 
 
 def summarize_counters(fetch_dir, write_dir):
@@ -236,6 +252,39 @@ def summarize_trace(trace_dir, bench_log):
         for name, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
             fo.write(f"{name[:60]:<60} {len(v):6d} {np.mean(v):10.2f} {np.min(v):10.2f} {np.max(v):10.2f} "
                      f"{100 * sum(v) / total:7.2f}\n")
+    print(open(out).read())
+    if "prefill_compressor" in res:
+        summarize_compressor_trace(rows, res)
+
+
+def summarize_compressor_trace(rows, res):
+    """profiles/compress_prefill_chunk8192_kernel_stats.txt: the prefill compressor's kernels in
+    the same trace, with the fraction of the bf16 peak from the trace's own durations."""
+    from synthetic import inputs as I
+    sh = I.PREFILL
+    f_main, f_idx = 2.0 * sh.S * sh.d * 4 * sh.c, 2.0 * sh.S * sh.d * 4 * sh.d_I
+    out = os.path.join(ROOT, "profiles", "compress_prefill_chunk8192_kernel_stats.txt")
+    with open(out, "w") as fo:
+        fo.write("# rocprofv3 kernel trace of the default bench run: the prefill compressor sub-benchmark\n")
+        fo.write(f"# command: {TRACE_CMD}\n")
+        fo.write(f"# workload: one prefill chunk, T = {sh.S} tokens (+{sh.m} before it), d = {sh.d}, overlap, m = {sh.m};\n")
+        fo.write(f"#   main KV c = {sh.c} (bf16 rows), indexer K c = {sh.d_I} (FP8 rows + scale)\n")
+        pc = res["prefill_compressor"]
+        fo.write(f"# bench (events, whole csa_compress call, under the tracer): main_ms={pc['main_ms']:.4f} "
+                 f"indexer_ms={pc['indexer_ms']:.4f}\n")
+        fo.write("# algorithmic flops: 2 * T * d * 4c (each entry pools 2m slots of (C, Z))\n\n")
+        for label, key, fl in (("main", COMPRESS_MAIN_KERNEL, f_main), ("indexer", COMPRESS_IDX_KERNEL, f_idx),
+                               ("finish (both)", "compress_pool<true>", None)):
+            v = [(t1 - t0) / 1e3 for t0, t1, name in rows if key in name]
+            if not v:
+                continue
+            fo.write(f"{label:<14} {key:<52} calls {len(v):4d}  avg_us {np.mean(v):8.2f}  min_us {np.min(v):8.2f}  "
+                     f"max_us {np.max(v):8.2f}\n")
+            if fl is not None:
+                tf = fl / (np.mean(v) * 1e-6) / 1e12
+                fo.write(f"{'':<14} flops_per_launch = {fl:.4e}  tflops_from_trace_avg = {tf:.1f}  "
+                         f"frac_bf16_peak = {tf / BF16_PEAK_TFLOPS:.3f}\n")
+        fo.write(f"sources = {' + '.join(COMPRESS_SOURCES)}\nsources_sha256 = {sources_sha256(COMPRESS_SOURCES)}\n")
     print(open(out).read())
 
 
