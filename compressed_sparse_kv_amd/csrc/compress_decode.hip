@@ -10,20 +10,22 @@
 //
 // Two kernels per call:
 //   1. proj_token_bf16 / proj_token_f32: P[b, :] = W . h_b for the B new tokens (fp32, in
-//      the workspace).  bf16: v_mfma_f32_16x16x32_bf16 with M = the tokens (16 per tile),
-//      N = 16 output columns per workgroup, K = d cut into 1024-wide slices (one per
-//      workgroup row of the grid; partial sums in the workspace) and each slice over the 4
-//      waves of the workgroup, 2 K blocks of 128 per wave with all loads issued first; each
-//      lane streams 64 contiguous bytes of its W row per block (the same permutation of the
-//      K slots on both operands, so the pairing is exact).  The weights are read once per
-//      call: decode projection is bound by that stream, so it is spread over many waves.
+//      the workspace).  bf16: v_mfma_f32_16x16x32_bf16, a workgroup per (64 output columns,
+//      512-wide K slice, 32 tokens): the slice of the tokens' hidden vectors is staged once
+//      in LDS and shared by the 4 waves, each wave holding its 16 W rows of the slice in
+//      registers; partial sums per slice in the workspace.  The weights are read once per
+//      call and spread over many workgroups: decode projection is bound by that stream.
+//      (A single pass with full-K dot products per workgroup, the pooling in its epilogue,
+//      measured slower: every workgroup then pulls all the tokens' hidden vectors, 320 KB
+//      for 32 tokens, and a compute unit streams only about 20 GB/s of such loads.)
 //   2. compress_step: one workgroup per sequence, one thread per channel pair.  The K
-//      slices are summed (fixed order); the token's streams go into ring slot t mod 2m (or
-//      m), or update the online triple;
+//      slices are summed (fixed order, loaded in groups); the token's streams go into ring
+//      slot t mod 2m (or m), or update the online triple;
 //      when (t + 1) % m == 0 entry i = t / m is pooled (per-channel softmax over the slots,
-//      weighted sum), RMS-normalised, rotated (RoPE at position m*i, angle formed in double) and
-//      written as fp32 / bf16 / e4m3 (+ row scale amax/448), row-major or, for the indexer
-//      keys, straight into the 16-entry blocked layout the decode scoring pass reads.
+//      weighted sum; the other slots are loaded before the slices), RMS-normalised, rotated
+//      (RoPE at position m*i, angle formed in double) and written as fp32 / bf16 / e4m3
+//      (+ row scale amax/448), row-major or, for the indexer keys, straight into the
+//      16-entry blocked layout the decode scoring pass reads.
 #include <algorithm>
 
 #include "common.hpp"
@@ -32,85 +34,63 @@
 namespace csa {
 
 constexpr int kPjK = 128;                   // K block: 4 MFMA steps of 32
+constexpr int kPjSlice = 512;               // K per workgroup (4 blocks); one partial sum per slice
 constexpr int kPjWaves = 4;
-constexpr int kPjBlocksPerWave = 2;         // K blocks per wave: one K slice = 8 blocks = 1024 wide
-constexpr int kPjSlice = kPjWaves * kPjBlocksPerWave * kPjK;
-constexpr int kPjTilesSmall = 2;            // token tiles of 16 per workgroup: up to 32 tokens ...
-constexpr int kPjTilesLarge = 8;            // ... or 128 (more tokens: further workgroup rows)
+constexpr int kPjCols = 16 * kPjWaves;      // output columns per workgroup, 16 per wave
+constexpr int kPjTok = 32;                  // tokens per workgroup (2 MFMA tiles)
+constexpr int kPjStride = 2 * kPjSlice + 16;   // LDS bytes per token row (8 rows in 8 bank groups)
 
-// Partial projection over K slice blockIdx.y: Pk[slice][b][n] for the tokens b of tile group
-// blockIdx.z (MT tiles of 16 tokens at most) and the 16 columns of blockIdx.x; W [N, d] bf16
-// ("out x in").  Every wave issues all its loads (two K blocks of its 16 W rows, 64
-// contiguous bytes per lane per block) before its first MFMA; the four waves' products are
-// summed in LDS in a fixed order.
-template <int MT>
+// Partial projection over K slice blockIdx.y: Pk[slice][b][n] for the up to 32 tokens of
+// blockIdx.z and the 64 columns of blockIdx.x; W [N, d] bf16 ("out x in").  The slice of
+// the tokens' hidden vectors is read once into LDS and shared by the 4 waves; each wave
+// holds its 16 W rows of the slice in registers (A operand: rows = output columns,
+// B operand: the tokens), so a lane ends with 4 consecutive columns of one token.
 __global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t* __restrict__ hidden,
                                                                  const uint16_t* __restrict__ W, int B, int d, int N,
                                                                  float* __restrict__ Pk) {
-  constexpr int kPjMaxTiles = MT;
-  __shared__ v4f red[kPjWaves - 1][kPjMaxTiles][64];
-  const int l = static_cast<int>(lane_id());
-  const int wave = threadIdx.x >> 6;
-  const int g = l >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int slice = blockIdx.y;
-  const int b0 = blockIdx.z * 16 * kPjMaxTiles;
-  const int ntiles = min(kPjMaxTiles, cdiv(B - b0, 16));
-  static_assert(MT >= 1 && MT <= 8, "token tiles per workgroup");
-  const int nblk = d / kPjK;
-  const int j0 = slice * (kPjWaves * kPjBlocksPerWave) + wave * kPjBlocksPerWave;
-  const uint16_t* wrow = W + static_cast<size_t>(min(n0 + (l & 15), N - 1)) * d + 32 * g;
-  v8s wb[kPjBlocksPerWave][4];
+  __shared__ __attribute__((aligned(16))) uint8_t hs[kPjTok * kPjStride];
+  const int tid = threadIdx.x, l = static_cast<int>(lane_id()), wave = tid >> 6, g = l >> 4;
+  const int n0 = blockIdx.x * kPjCols + 16 * wave;
+  const int slice = blockIdx.y, k0 = slice * kPjSlice;
+  const int b0 = blockIdx.z * kPjTok;
+  const int nblk = min(kPjSlice, d - k0) / kPjK;        // blocks of this slice (d % 128 == 0)
+  // this wave's W rows: 4 blocks x 4 MFMA steps, 16 bytes per lane each (issued first)
+  const uint16_t* wrow = W + static_cast<size_t>(min(n0 + (l & 15), N - 1)) * d + k0 + 8 * g;
+  v8s wa[kPjSlice / kPjK][4];
 #pragma unroll
-  for (int jj = 0; jj < kPjBlocksPerWave; ++jj) {
-    const int j = min(j0 + jj, nblk - 1);              // past the end: a block re-read, its product dropped
+  for (int jb = 0; jb < kPjSlice / kPjK; ++jb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wb[jj][ks] = *reinterpret_cast<const v8s*>(wrow + static_cast<size_t>(j) * kPjK + 8 * ks);
-  }
-  v4f acc[kPjMaxTiles];
+    for (int ks = 0; ks < 4; ++ks)
+      wa[jb][ks] = jb < nblk ? *reinterpret_cast<const v8s*>(wrow + jb * kPjK + 32 * ks) : v8s{};
+  // the tokens' slice: 32 rows x 64 pieces of 16 bytes, 8 per thread
 #pragma unroll
-  for (int mt = 0; mt < kPjMaxTiles; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int mt = 0; mt < kPjMaxTiles; ++mt) {
-    if (mt < ntiles) {
-      const uint16_t* hrow = hidden + static_cast<size_t>(min(b0 + 16 * mt + (l & 15), B - 1)) * d + 32 * g;
-#pragma unroll
-      for (int jj = 0; jj < kPjBlocksPerWave; ++jj) {
-        if (j0 + jj < nblk) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const v8s ha = *reinterpret_cast<const v8s*>(hrow + static_cast<size_t>(j0 + jj) * kPjK + 8 * ks);
-            acc[mt] = mfma_bf16_16x16x32(ha, wb[jj][ks], acc[mt]);
-          }
-        }
-      }
+  for (int i = 0; i < kPjTok * 64 / (kPjWaves * 64); ++i) {
+    const int q = tid + kPjWaves * 64 * i, tok = q >> 6, piece = q & 63;
+    if (8 * piece < nblk * kPjK) {
+      const uint4 v = *reinterpret_cast<const uint4*>(hidden + static_cast<size_t>(min(b0 + tok, B - 1)) * d + k0 +
+                                                      8 * piece);
+      *reinterpret_cast<uint4*>(&hs[tok * kPjStride + 16 * piece]) = v;
     }
-  }
-  // sum the waves' partial products (fixed order) and store: lane l holds tokens
-  // 16*mt + 4*g + i of column n0 + (l & 15)
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < kPjMaxTiles; ++mt)
-      if (mt < ntiles) red[wave - 1][mt][l] = acc[mt];
   }
   __syncthreads();
-  if (wave != 0) return;
-  const int n = n0 + (l & 15);
+  v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int jb = 0; jb < kPjSlice / kPjK; ++jb)
+    if (jb < nblk)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const v8s hb = *reinterpret_cast<const v8s*>(&hs[(16 * tt + (l & 15)) * kPjStride +
+                                                           2 * (jb * kPjK + 32 * ks + 8 * g)]);
+          acc[tt] = mfma_bf16_16x16x32(wa[jb][ks], hb, acc[tt]);
+        }
+  // lane l: columns n0 + 4g .. +3 of token b0 + 16*tt + (l & 15)
   float* P = Pk + static_cast<size_t>(slice) * B * N;
 #pragma unroll
-  for (int mt = 0; mt < kPjMaxTiles; ++mt) {
-    if (mt >= ntiles) continue;
-    v4f s = acc[mt];
-#pragma unroll
-    for (int w = 0; w < kPjWaves - 1; ++w) {
-      const v4f x = red[w][mt][l];
-      s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = b0 + 16 * mt + 4 * g + i;
-      if (b < B && n < N) P[static_cast<size_t>(b) * N + n] = s[i];
-    }
+  for (int tt = 0; tt < 2; ++tt) {
+    const int b = b0 + 16 * tt + (l & 15), n = n0 + 4 * g;
+    if (b < B && n < N) *reinterpret_cast<v4f*>(P + static_cast<size_t>(b) * N + n) = acc[tt];
   }
 }
 
@@ -144,146 +124,14 @@ struct StepArgs {
 };
 
 constexpr int kStepMaxSlots = 8;            // ring slots held in registers by the pooling (2m <= 8)
+constexpr int kStepSliceGroup = 8;          // K-slice partials loaded together (16: no faster)
 
-__global__ __launch_bounds__(512) void compress_step(StepArgs a) {
-  __shared__ float red[8];
-  const int b = blockIdx.x;
-  const int64_t t = a.pos[b];
-  if (t < 0) return;
+// Entry i of sequence b from its pooled pair (u0, u1) of thread p = threadIdx.x: RMSNorm over
+// the c channels, RoPE at position m*i, the store (every thread of the workgroup calls it).
+__device__ void emit_entry(const StepArgs& a, int b, int64_t i, float u0, float u1, bool live, float* red) {
   const int c = a.c, m = a.m;
-  const int ns = a.overlap ? 4 : 2;
-  const int N = ns * c;
-  const int nslot = a.overlap ? 2 * m : m;
-  const int p = threadIdx.x;                            // channel pair (2p, 2p+1)
-  const bool live = p < c / 2;
-  const int r = static_cast<int>(t % m);                // slot of the token within its block
-  const bool boundary = a.emit && r == m - 1;
-  // this token's streams for the pair: the sum of the K slices (fixed order)
-  float2 tok[4] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
-  if (live) {
-    for (int sl = 0; sl < a.n_slices; ++sl) {
-      const float* Pb = a.P + (static_cast<size_t>(sl) * a.B + b) * N;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < ns) {
-          const float2 v = *reinterpret_cast<const float2*>(Pb + s * c + 2 * p);
-          tok[s].x += v.x;
-          tok[s].y += v.y;
-        }
-    }
-  }
-  float u[2] = {0.f, 0.f};
-  if (a.online) {
-    float* st = a.state + static_cast<size_t>(b) * 3 * c;
-    if (live) {
-      const float2 bz = *reinterpret_cast<const float2*>(a.bias + r * c + 2 * p);
-      const float z[2] = {tok[1].x + bz.x, tok[1].y + bz.y}, cv[2] = {tok[0].x, tok[0].y};
-      float2 mo = make_float2(0.f, 0.f), so = mo, ao = mo;
-      if (r != 0) {
-        mo = *reinterpret_cast<const float2*>(st + 2 * p);
-        so = *reinterpret_cast<const float2*>(st + c + 2 * p);
-        ao = *reinterpret_cast<const float2*>(st + 2 * c + 2 * p);
-      }
-      const float mov[2] = {mo.x, mo.y}, sov[2] = {so.x, so.y}, aov[2] = {ao.x, ao.y};
-      float mx[2], sm[2], acc[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (r == 0) {
-          mx[h] = z[h]; sm[h] = 1.0f; acc[h] = cv[h];
-        } else {
-          mx[h] = fmaxf(mov[h], z[h]);
-          const float e_old = expf(mov[h] - mx[h]), e_new = expf(z[h] - mx[h]);
-          sm[h] = sov[h] * e_old + e_new;
-          acc[h] = fmaf(e_new, cv[h], aov[h] * e_old);
-        }
-        u[h] = acc[h] / sm[h];
-      }
-      *reinterpret_cast<float2*>(st + 2 * p) = make_float2(mx[0], mx[1]);
-      *reinterpret_cast<float2*>(st + c + 2 * p) = make_float2(sm[0], sm[1]);
-      *reinterpret_cast<float2*>(st + 2 * c + 2 * p) = make_float2(acc[0], acc[1]);
-    }
-  } else {
-    float* ring = a.state + static_cast<size_t>(b) * nslot * N;
-    const int my_slot = static_cast<int>(t % nslot);
-    if (live) {
-      float* slot = ring + static_cast<size_t>(my_slot) * N;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (s < ns) *reinterpret_cast<float2*>(slot + s * c + 2 * p) = tok[s];
-    }
-    if (boundary && live) {
-      const int64_t i = t / m;
-      const bool bslots = a.overlap && i > 0;
-      // slots of block i (a-stream: C at stream 0, Z at stream 1) and, with overlap, of
-      // block i-1 (b-stream: C at stream 2, Z at stream 3); this thread wrote every slot of
-      // its channels, in this call or an earlier one.  Loaded first, then pooled.
-      const int nsl = bslots ? 2 * m : m;
-      float2 zc[2 * kStepMaxSlots][2];                  // [slot][logit, value]
-      if (m <= kStepMaxSlots / 2 || (!a.overlap && m <= kStepMaxSlots)) {
-#pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j) {
-          if (j < nsl) {
-            const bool bs = j >= m;
-            const int jr = bs ? j - m : j;
-            const int64_t pj = bs ? m * (i - 1) + jr : m * i + jr;
-            const int sj = static_cast<int>(pj % nslot);
-            const int sz = bs ? 3 : 1, sc = bs ? 2 : 0;
-            float2 zz, cc;
-            if (sj == my_slot) {
-              zz = bs ? tok[3] : tok[1];
-              cc = bs ? tok[2] : tok[0];
-            } else {
-              const float* s = ring + static_cast<size_t>(sj) * N;
-              zz = *reinterpret_cast<const float2*>(s + sz * c + 2 * p);
-              cc = *reinterpret_cast<const float2*>(s + sc * c + 2 * p);
-            }
-            const float2 bz = *reinterpret_cast<const float2*>(a.bias + ((bs ? m : 0) + jr) * c + 2 * p);
-            zc[j][0] = make_float2(zz.x + bz.x, zz.y + bz.y);
-            zc[j][1] = cc;
-          }
-        }
-        float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
-          if (j < nsl) { mx0 = fmaxf(mx0, zc[j][0].x); mx1 = fmaxf(mx1, zc[j][0].y); }
-        float d0 = 0.f, d1 = 0.f, n0 = 0.f, n1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
-          if (j < nsl) {
-            const float e0 = expf(zc[j][0].x - mx0), e1 = expf(zc[j][0].y - mx1);
-            d0 += e0; d1 += e1;
-            n0 = fmaf(e0, zc[j][1].x, n0);
-            n1 = fmaf(e1, zc[j][1].y, n1);
-          }
-        u[0] = n0 / d0;
-        u[1] = n1 / d1;
-      } else {
-        // long blocks (HCA ring, m > 8): two passes over the slots in memory
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ch = 2 * p + h;
-          float mx = -INFINITY;
-          for (int j = 0; j < nsl; ++j) {
-            const bool bs = j >= m;
-            const int jr = bs ? j - m : j;
-            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
-            mx = fmaxf(mx, s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch]);
-          }
-          float den = 0.f, num = 0.f;
-          for (int j = 0; j < nsl; ++j) {
-            const bool bs = j >= m;
-            const int jr = bs ? j - m : j;
-            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
-            const float e = expf(s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch] - mx);
-            den += e;
-            num = fmaf(e, s[(bs ? 2 : 0) * c + ch], num);
-          }
-          u[h] = num / den;
-        }
-      }
-    }
-  }
-  if (!boundary) return;                                // uniform over the workgroup
+  const int p = threadIdx.x;
+  float u[2] = {u0, u1};
   // RMSNorm over the c channels
   float ss = live ? u[0] * u[0] + u[1] * u[1] : 0.f;
 #pragma unroll
@@ -294,7 +142,6 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(c) + a.rms_eps);
   float x0 = u[0] * inv, x1 = u[1] * inv;
-  const int64_t i = t / m;
   const int pr = p - (c - a.d_rope) / 2;                // RoPE pair index
   if (live && pr >= 0) {
     float cs, sn;
@@ -347,6 +194,171 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   }
 }
 
+__global__ __launch_bounds__(512) void compress_step(StepArgs a) {
+  __shared__ float red[8];
+  const int b = blockIdx.x;
+  const int64_t t = a.pos[b];
+  if (t < 0) return;
+  const int c = a.c, m = a.m;
+  const int ns = a.overlap ? 4 : 2;
+  const int N = ns * c;
+  const int nslot = a.overlap ? 2 * m : m;
+  const int p = threadIdx.x;                            // channel pair (2p, 2p+1)
+  const bool live = p < c / 2;
+  const int r = static_cast<int>(t % m);                // slot of the token within its block
+  const bool boundary = a.emit && r == m - 1;
+  // Ring path at a block boundary with the slots held in registers: the entry's other slots
+  // (never the slot this token writes: an a-slot before it or a b-slot of the previous
+  // block) and the biases do not depend on this token, so they are loaded before the K
+  // slices and the two sets of loads overlap.
+  const bool reg_pool = !a.online && (m <= kStepMaxSlots / 2 || (!a.overlap && m <= kStepMaxSlots));
+  const int64_t i_e = t / m;
+  const bool bslots_e = a.overlap && i_e > 0;
+  const int nsl_e = bslots_e ? 2 * m : m;
+  float2 zc[2 * kStepMaxSlots][2];                        // [slot][logit, value]
+  if (!a.online && boundary && live && reg_pool) {
+    const float* ring = a.state + static_cast<size_t>(b) * nslot * N;
+#pragma unroll
+    for (int j = 0; j < 2 * kStepMaxSlots; ++j) {
+      if (j < nsl_e) {
+        const bool bs = j >= m;
+        const int jr = bs ? j - m : j;
+        const float2 bz = *reinterpret_cast<const float2*>(a.bias + ((bs ? m : 0) + jr) * c + 2 * p);
+        if (!bs && jr == m - 1) {
+          zc[j][0] = bz;                                  // this token's logit is added below
+          zc[j][1] = make_float2(0.f, 0.f);
+        } else {
+          const int64_t pj = bs ? m * (i_e - 1) + jr : m * i_e + jr;
+          const float* sl = ring + static_cast<size_t>(pj % nslot) * N;
+          const float2 zz = *reinterpret_cast<const float2*>(sl + (bs ? 3 : 1) * c + 2 * p);
+          zc[j][0] = make_float2(zz.x + bz.x, zz.y + bz.y);
+          zc[j][1] = *reinterpret_cast<const float2*>(sl + (bs ? 2 : 0) * c + 2 * p);
+        }
+      }
+    }
+  }
+  // this token's streams for the pair: the sum of the K slices (fixed order)
+  float2 tok[4] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
+  if (live) {
+    // slices in groups of kStepSliceGroup with all their loads issued together (a loop over
+    // single slices would wait for each one in turn); summed in slice order
+    for (int s0 = 0; s0 < a.n_slices; s0 += kStepSliceGroup) {
+      float2 v[kStepSliceGroup][4];
+#pragma unroll
+      for (int k = 0; k < kStepSliceGroup; ++k) {
+        const float* Pb = a.P + (static_cast<size_t>(min(s0 + k, a.n_slices - 1)) * a.B + b) * N;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[k][s] = s < ns ? *reinterpret_cast<const float2*>(Pb + s * c + 2 * p) : float2{};
+      }
+#pragma unroll
+      for (int k = 0; k < kStepSliceGroup; ++k)
+        if (s0 + k < a.n_slices)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            tok[s].x += v[k][s].x;
+            tok[s].y += v[k][s].y;
+          }
+    }
+  }
+  float u[2] = {0.f, 0.f};
+  if (a.online) {
+    float* st = a.state + static_cast<size_t>(b) * 3 * c;
+    if (live) {
+      const float2 bz = *reinterpret_cast<const float2*>(a.bias + r * c + 2 * p);
+      const float z[2] = {tok[1].x + bz.x, tok[1].y + bz.y}, cv[2] = {tok[0].x, tok[0].y};
+      float2 mo = make_float2(0.f, 0.f), so = mo, ao = mo;
+      if (r != 0) {
+        mo = *reinterpret_cast<const float2*>(st + 2 * p);
+        so = *reinterpret_cast<const float2*>(st + c + 2 * p);
+        ao = *reinterpret_cast<const float2*>(st + 2 * c + 2 * p);
+      }
+      const float mov[2] = {mo.x, mo.y}, sov[2] = {so.x, so.y}, aov[2] = {ao.x, ao.y};
+      float mx[2], sm[2], acc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (r == 0) {
+          mx[h] = z[h]; sm[h] = 1.0f; acc[h] = cv[h];
+        } else {
+          mx[h] = fmaxf(mov[h], z[h]);
+          const float e_old = expf(mov[h] - mx[h]), e_new = expf(z[h] - mx[h]);
+          sm[h] = sov[h] * e_old + e_new;
+          acc[h] = fmaf(e_new, cv[h], aov[h] * e_old);
+        }
+        u[h] = acc[h] / sm[h];
+      }
+      *reinterpret_cast<float2*>(st + 2 * p) = make_float2(mx[0], mx[1]);
+      *reinterpret_cast<float2*>(st + c + 2 * p) = make_float2(sm[0], sm[1]);
+      *reinterpret_cast<float2*>(st + 2 * c + 2 * p) = make_float2(acc[0], acc[1]);
+    }
+  } else {
+    float* ring = a.state + static_cast<size_t>(b) * nslot * N;
+    const int my_slot = static_cast<int>(t % nslot);
+    if (live) {
+      float* slot = ring + static_cast<size_t>(my_slot) * N;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < ns) *reinterpret_cast<float2*>(slot + s * c + 2 * p) = tok[s];
+    }
+    if (boundary && live) {
+      const int64_t i = t / m;
+      const bool bslots = a.overlap && i > 0;
+      // slots of block i (a-stream: C at stream 0, Z at stream 1) and, with overlap, of
+      // block i-1 (b-stream: C at stream 2, Z at stream 3); this thread wrote every slot of
+      // its channels, in this call or an earlier one.  Loaded first, then pooled.
+      const int nsl = bslots ? 2 * m : m;
+      if (reg_pool) {
+        // the token's own slot (a-slot m - 1) joins the slots loaded at the start
+#pragma unroll
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+          if (j == m - 1) {
+            zc[j][0] = make_float2(tok[1].x + zc[j][0].x, tok[1].y + zc[j][0].y);
+            zc[j][1] = tok[0];
+          }
+        float mx0 = -INFINITY, mx1 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+          if (j < nsl) { mx0 = fmaxf(mx0, zc[j][0].x); mx1 = fmaxf(mx1, zc[j][0].y); }
+        float d0 = 0.f, d1 = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+          if (j < nsl) {
+            const float e0 = expf(zc[j][0].x - mx0), e1 = expf(zc[j][0].y - mx1);
+            d0 += e0; d1 += e1;
+            n0 = fmaf(e0, zc[j][1].x, n0);
+            n1 = fmaf(e1, zc[j][1].y, n1);
+          }
+        u[0] = n0 / d0;
+        u[1] = n1 / d1;
+      } else {
+        // long blocks (HCA ring, m > 8): two passes over the slots in memory
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 2 * p + h;
+          float mx = -INFINITY;
+          for (int j = 0; j < nsl; ++j) {
+            const bool bs = j >= m;
+            const int jr = bs ? j - m : j;
+            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
+            mx = fmaxf(mx, s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch]);
+          }
+          float den = 0.f, num = 0.f;
+          for (int j = 0; j < nsl; ++j) {
+            const bool bs = j >= m;
+            const int jr = bs ? j - m : j;
+            const float* s = ring + static_cast<size_t>(((bs ? m * (i - 1) : m * i) + jr) % nslot) * N;
+            const float e = expf(s[(bs ? 3 : 1) * c + ch] + a.bias[((bs ? m : 0) + jr) * c + ch] - mx);
+            den += e;
+            num = fmaf(e, s[(bs ? 2 : 0) * c + ch], num);
+          }
+          u[h] = num / den;
+        }
+      }
+    }
+  }
+  if (!boundary) return;                                // uniform over the workgroup
+  emit_entry(a, b, t / m, u[0], u[1], live, red);
+}
+
 size_t compress_state_bytes(int B, int m, int c, int overlap, int online) {
   if (online) return static_cast<size_t>(B) * 3 * c * sizeof(float);
   const size_t nslot = overlap ? 2 * static_cast<size_t>(m) : static_cast<size_t>(m);
@@ -366,15 +378,11 @@ int launch_compress_decode(const void* hidden, int in_dtype, const void* w_proj,
                            int out_dtype, int out_layout, int Nc_max, void* ws, hipStream_t st) {
   const int N = (overlap ? 4 : 2) * c;
   float* P = static_cast<float*>(ws);
+  const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);
   const int n_slices = proj_slices(d, in_dtype);
   if (in_dtype == CSA_BF16) {
-    if (B <= 16 * kPjTilesSmall)
-      hipLaunchKernelGGL(proj_token_bf16<kPjTilesSmall>, dim3(cdiv(N, 16), n_slices, 1), dim3(kPjWaves * 64), 0, st,
-                         static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_proj), B, d, N, P);
-    else
-      hipLaunchKernelGGL(proj_token_bf16<kPjTilesLarge>, dim3(cdiv(N, 16), n_slices, cdiv(B, 16 * kPjTilesLarge)),
-                         dim3(kPjWaves * 64), 0, st, static_cast<const uint16_t*>(hidden),
-                         static_cast<const uint16_t*>(w_proj), B, d, N, P);
+    hipLaunchKernelGGL(proj_token_bf16, dim3(cdiv(N, kPjCols), n_slices, cdiv(B, kPjTok)), dim3(kPjWaves * 64), 0, st,
+                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_proj), B, d, N, P);
   } else {
     hipLaunchKernelGGL(proj_token_f32, dim3(cdiv(N, 256), B), dim3(256), 0, st, static_cast<const float*>(hidden),
                        static_cast<const float*>(w_proj), B, d, N, P);
@@ -382,7 +390,6 @@ int launch_compress_decode(const void* hidden, int in_dtype, const void* w_proj,
   CSA_LAUNCH_CHECK();
   StepArgs a{P, n_slices, B, bias, pos, state, overlap, online, emit, m, c, d_rope, rope_ratio(rope_theta, d_rope),
              rms_eps, out_dtype, out_layout, Nc_max, cache, cache_scale};
-  const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);
   hipLaunchKernelGGL(compress_step, dim3(B), dim3(threads), 0, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;

@@ -143,3 +143,36 @@ def test_decode_compress_skips(lib):
     assert np.all(got[0] == 0), "an inactive sequence was written"
     ref = _oracle(a, kw, 1, 0)
     assert_bf16_within_one_step(got[1, 0], ref[0], "entry 0 of sequence 1")
+
+
+def test_decode_compress_many_sequences_f32(lib):
+    """20 sequences (two token tiles of the fused step, the second partial) at different
+    block starts, one of them inactive (position -1): every emitted fp32 entry at 1e-5, the
+    inactive sequence untouched."""
+    m, d, B, c, T = 4, 256, 20, 128, 12
+    a = I.compressor_inputs(800, B, T, d, m, c, True, 0.05, False)
+    kw = dict(overlap=True, m=m, c=c, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+    prev = I.compressor_inputs(801, B, m, d, m, c, True, 0.05, False)["hidden_bf16"]
+    starts = np.array([4 * (b % 5) for b in range(B)], np.int64)
+    Nc_max = 8
+    state = torch.empty(lib.compress_state_size(B, m, c, True), dtype=torch.uint8, device="cuda")
+    cache = torch.zeros(B, Nc_max, c, device="cuda")
+    W, bias = dev_bf16(np.ascontiguousarray(a["W_bf16"].T)), dev(a["bias"])
+    live = np.arange(B) != 7
+    for r in range(m):
+        pos = np.where(live, starts - m + r, -1)
+        lib.csa_compress_decode(dev_bf16(np.ascontiguousarray(prev[:, r])), W, bias, dev(pos), state, cache,
+                                emit=False, **kw)
+    for s in range(T):
+        pos = np.where(live, starts + s, -1)
+        lib.csa_compress_decode(dev_bf16(np.ascontiguousarray(a["hidden_bf16"][:, s])), W, bias, dev(pos), state,
+                                cache, **kw)
+    torch.cuda.synchronize()
+    got = cache.cpu().numpy()
+    assert np.all(got[7] == 0), "the inactive sequence was written"
+    for b in np.flatnonzero(live):
+        ref = _oracle(a, kw, b, starts[b], prime=prev if starts[b] > 0 else None)
+        for i, v in ref.items():
+            assert_close(got[b, i], v, TOL_F32, f"decode entry {i} of sequence {b}")
+        untouched = [i for i in range(Nc_max) if i not in ref]
+        assert np.all(got[b, untouched] == 0)
