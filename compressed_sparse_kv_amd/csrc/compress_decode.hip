@@ -194,48 +194,87 @@ __device__ void emit_entry(const StepArgs& a, int b, int64_t i, float u0, float 
   }
 }
 
+// The 2m-slot softmax of a CSA entry from the ring in registers: ra = the ring half of this
+// block (its a-streams; slot m - 1 is the token itself, in tok), rb = the previous block's
+// half (its b-streams, pooled when bslots); slots in order a then b.
+template <int kH>
+__device__ __forceinline__ void pool_csa_ring(const float2 (&ra)[kH][4], const float2 (&rb)[kH][4],
+                                              const float2 (&bza)[kH], const float2 (&bzb)[kH], const float2 (&tok)[4],
+                                              int m, bool bslots, float (&u)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float za[kH], va[kH], zb[kH], vb[kH];
+#pragma unroll
+    for (int jr = 0; jr < kH; ++jr) {
+      const float2 z2 = jr == m - 1 ? tok[1] : ra[jr][1], v2 = jr == m - 1 ? tok[0] : ra[jr][0];
+      za[jr] = (h ? z2.y : z2.x) + (h ? bza[jr].y : bza[jr].x);
+      va[jr] = h ? v2.y : v2.x;
+      zb[jr] = (h ? rb[jr][3].y : rb[jr][3].x) + (h ? bzb[jr].y : bzb[jr].x);
+      vb[jr] = h ? rb[jr][2].y : rb[jr][2].x;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jr = 0; jr < kH; ++jr)
+      if (jr < m) mx = fmaxf(mx, za[jr]);
+    if (bslots)
+#pragma unroll
+      for (int jr = 0; jr < kH; ++jr)
+        if (jr < m) mx = fmaxf(mx, zb[jr]);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int jr = 0; jr < kH; ++jr)
+      if (jr < m) {
+        const float e = expf(za[jr] - mx);
+        den += e;
+        num = fmaf(e, va[jr], num);
+      }
+    if (bslots)
+#pragma unroll
+      for (int jr = 0; jr < kH; ++jr)
+        if (jr < m) {
+          const float e = expf(zb[jr] - mx);
+          den += e;
+          num = fmaf(e, vb[jr], num);
+        }
+    u[h] = num / den;
+  }
+}
+
 __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   __shared__ float red[8];
   const int b = blockIdx.x;
-  const int64_t t = a.pos[b];
-  if (t < 0) return;
   const int c = a.c, m = a.m;
   const int ns = a.overlap ? 4 : 2;
   const int N = ns * c;
   const int nslot = a.overlap ? 2 * m : m;
   const int p = threadIdx.x;                            // channel pair (2p, 2p+1)
   const bool live = p < c / 2;
-  const int r = static_cast<int>(t % m);                // slot of the token within its block
-  const bool boundary = a.emit && r == m - 1;
-  // Ring path at a block boundary with the slots held in registers: the entry's other slots
-  // (never the slot this token writes: an a-slot before it or a b-slot of the previous
-  // block) and the biases do not depend on this token, so they are loaded before the K
-  // slices and the two sets of loads overlap.
-  const bool reg_pool = !a.online && (m <= kStepMaxSlots / 2 || (!a.overlap && m <= kStepMaxSlots));
-  const int64_t i_e = t / m;
-  const bool bslots_e = a.overlap && i_e > 0;
-  const int nsl_e = bslots_e ? 2 * m : m;
-  float2 zc[2 * kStepMaxSlots][2];                        // [slot][logit, value]
-  if (!a.online && boundary && live && reg_pool) {
+  const int64_t t = a.pos[b];
+  // Everything that does not depend on the token's position is loaded before the position
+  // is used, so one memory latency covers the position, the K-slice partials, the biases
+  // and, for the CSA ring (overlap, m <= 4), the whole ring: at a block boundary the entry
+  // pools every slot but the token's own (this block in one half of the ring, the previous
+  // block in the other; which half follows from t mod 2m).
+  const bool csa_ring = !a.online && a.overlap && m <= kStepMaxSlots / 2;
+  constexpr int kH = kStepMaxSlots / 2;
+  float2 rs0[kH][4], rs1[kH][4];                        // ring halves: [slot][stream]
+  float2 bza[kH], bzb[kH];                              // logit biases of the a- and b-slots
+  if (csa_ring && a.emit && live) {
     const float* ring = a.state + static_cast<size_t>(b) * nslot * N;
 #pragma unroll
-    for (int j = 0; j < 2 * kStepMaxSlots; ++j) {
-      if (j < nsl_e) {
-        const bool bs = j >= m;
-        const int jr = bs ? j - m : j;
-        const float2 bz = *reinterpret_cast<const float2*>(a.bias + ((bs ? m : 0) + jr) * c + 2 * p);
-        if (!bs && jr == m - 1) {
-          zc[j][0] = bz;                                  // this token's logit is added below
-          zc[j][1] = make_float2(0.f, 0.f);
-        } else {
-          const int64_t pj = bs ? m * (i_e - 1) + jr : m * i_e + jr;
-          const float* sl = ring + static_cast<size_t>(pj % nslot) * N;
-          const float2 zz = *reinterpret_cast<const float2*>(sl + (bs ? 3 : 1) * c + 2 * p);
-          zc[j][0] = make_float2(zz.x + bz.x, zz.y + bz.y);
-          zc[j][1] = *reinterpret_cast<const float2*>(sl + (bs ? 2 : 0) * c + 2 * p);
+    for (int jr = 0; jr < kH; ++jr)
+      if (jr < m)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          rs0[jr][st] = *reinterpret_cast<const float2*>(ring + static_cast<size_t>(jr) * N + st * c + 2 * p);
+          rs1[jr][st] = *reinterpret_cast<const float2*>(ring + static_cast<size_t>(m + jr) * N + st * c + 2 * p);
         }
+#pragma unroll
+    for (int jr = 0; jr < kH; ++jr)
+      if (jr < m) {
+        bza[jr] = *reinterpret_cast<const float2*>(a.bias + jr * c + 2 * p);
+        bzb[jr] = *reinterpret_cast<const float2*>(a.bias + (m + jr) * c + 2 * p);
       }
-    }
   }
   // this token's streams for the pair: the sum of the K slices (fixed order)
   float2 tok[4] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
@@ -258,6 +297,32 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
             tok[s].x += v[k][s].x;
             tok[s].y += v[k][s].y;
           }
+    }
+  }
+  if (t < 0) return;
+  const int r = static_cast<int>(t % m);                // slot of the token within its block
+  const bool boundary = a.emit && r == m - 1;
+  // The HCA ring (no overlap, m <= 8) at a boundary: the block's other slots and the biases,
+  // loaded before this token's slot is written (never the same slot).
+  const bool reg_pool = !a.online && (m <= kStepMaxSlots / 2 || (!a.overlap && m <= kStepMaxSlots));
+  const int64_t i_e = t / m;
+  float2 zc[kStepMaxSlots][2];                          // [slot][logit, value]
+  if (!a.online && !a.overlap && boundary && live && reg_pool) {
+    const float* ring = a.state + static_cast<size_t>(b) * nslot * N;
+#pragma unroll
+    for (int j = 0; j < kStepMaxSlots; ++j) {
+      if (j < m) {
+        const float2 bz = *reinterpret_cast<const float2*>(a.bias + j * c + 2 * p);
+        if (j == m - 1) {
+          zc[j][0] = bz;                                  // this token's logit is added below
+          zc[j][1] = make_float2(0.f, 0.f);
+        } else {
+          const float* sl = ring + static_cast<size_t>((m * i_e + j) % nslot) * N;
+          const float2 zz = *reinterpret_cast<const float2*>(sl + c + 2 * p);
+          zc[j][0] = make_float2(zz.x + bz.x, zz.y + bz.y);
+          zc[j][1] = *reinterpret_cast<const float2*>(sl + 2 * p);
+        }
+      }
     }
   }
   float u[2] = {0.f, 0.f};
@@ -306,21 +371,26 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
       // block i-1 (b-stream: C at stream 2, Z at stream 3); this thread wrote every slot of
       // its channels, in this call or an earlier one.  Loaded first, then pooled.
       const int nsl = bslots ? 2 * m : m;
-      if (reg_pool) {
-        // the token's own slot (a-slot m - 1) joins the slots loaded at the start
+      if (csa_ring) {
+        // this block's slots are the upper ring half when t mod 2m >= m (the same for the
+        // whole workgroup: a branch, so that each arm reads its halves at fixed indices)
+        if ((t % nslot) >= m) pool_csa_ring(rs1, rs0, bza, bzb, tok, m, bslots, u);
+        else pool_csa_ring(rs0, rs1, bza, bzb, tok, m, bslots, u);
+      } else if (reg_pool) {
+        // the token's own slot (slot m - 1) joins the slots loaded at the start
 #pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+        for (int j = 0; j < kStepMaxSlots; ++j)
           if (j == m - 1) {
             zc[j][0] = make_float2(tok[1].x + zc[j][0].x, tok[1].y + zc[j][0].y);
             zc[j][1] = tok[0];
           }
         float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+        for (int j = 0; j < kStepMaxSlots; ++j)
           if (j < nsl) { mx0 = fmaxf(mx0, zc[j][0].x); mx1 = fmaxf(mx1, zc[j][0].y); }
         float d0 = 0.f, d1 = 0.f, n0 = 0.f, n1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 2 * kStepMaxSlots; ++j)
+        for (int j = 0; j < kStepMaxSlots; ++j)
           if (j < nsl) {
             const float e0 = expf(zc[j][0].x - mx0), e1 = expf(zc[j][0].y - mx1);
             d0 += e0; d1 += e1;
