@@ -194,6 +194,68 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, c
   merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
 }
 
+// One wave's result (head group hg, channels kPart*part .. +kPart-1; O unnormalised, its
+// reference maximum m_ref in log2 units, l_run this lane's share of the per-head sums):
+// with one split the output (sink in the denominator, inverse RoPE, bf16) and the lse,
+// else the split's partial in register order for attn_merge_tiles.
+template <int kPart>
+__device__ __forceinline__ void attn_finish(const AttnArgs& a, const v4f (&o)[kPart / 16], float m_ref, float l_run,
+                                            int qi, int split, int hg, int part) {
+  const int l = static_cast<int>(lane_id());
+  const int g = l >> 4;
+  float l_tot = l_run + wave_xor(l_run, 16);
+  l_tot += wave_xor(l_tot, 32);
+  const int head_l = kHG * hg + (l & 15);             // head whose statistics this lane holds
+  const int col0 = kPart * part + (l & 15);
+  if (a.nsplit == 1) {
+    const float sink2 = a.sink[head_l] * kLog2e;
+    const float M = fmaxf(m_ref, sink2);
+    float f, lse2;
+    if (M == -INFINITY) {
+      f = 0.0f;
+      lse2 = -INFINITY;
+    } else {
+      const float em = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - M);
+      const float den = l_tot * em + exp2f(sink2 - M);
+      f = den > 0.0f ? em / den : 0.0f;
+      lse2 = M + log2f(den);
+    }
+    if (a.lse && part == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
+    float fh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
+    uint16_t* ob = a.out + (static_cast<size_t>(qi) * kAH + kHG * hg) * kAC;
+    const int64_t tq = a.rope_d > 0 ? a.q_pos[qi] : 0;
+#pragma unroll
+    for (int t = 0; t < kPart / 16; ++t) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = o[t][i] * fh[i];
+      // inverse RoPE of the output (the tile's 16 columns: lane pairs hold channel pairs)
+      if (a.rope_d > 0 && kPart * part + 16 * t + 16 > kAC - a.rope_d) {
+        const int col = col0 + 16 * t;
+        float cs = 1.0f, sn = 0.0f;
+        if (col >= kAC - a.rope_d) rope_cs_sn(col, kAC, a.rope_d, a.rope_r, tq, cs, sn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(v[i]);
+    }
+  } else {
+    const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
+    if (part == 0 && g == 0) {
+      a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_ref;
+      a.part_ml[(pbase * kAH + head_l) * 2 + 1] = l_tot;
+    }
+    // the partial in register order: [head group][16-channel tile][lane][4 heads], 16
+    // bytes per lane per store
+    float* po = a.part_o + ((pbase * kNHG + hg) * (kAC / 16) + kPart / 16 * part) * (kWave * 4) + 4 * l;
+#pragma unroll
+    for (int t = 0; t < kPart / 16; ++t) *reinterpret_cast<v4f*>(po + t * (kWave * 4)) = o[t];
+  }
+}
+
 template <int kSrc, int kParts, int kWaves, int kFmt = kFmtBf16>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   constexpr bool kDense = kSrc == kSrcDense;
@@ -546,58 +608,248 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
 #undef CSA_ATT_STORE1
 #undef CSA_ATT_STORE
 
-  // ---- finish: per-head totals
-  float l_tot = l_run + wave_xor(l_run, 16);
-  l_tot += wave_xor(l_tot, 32);
-  const int head_l = kHG * hg + (l & 15);             // head whose statistics this lane holds
-  const int col0 = Sh::kPart * part + (l & 15);
-  if (a.nsplit == 1) {
-    const float sink2 = a.sink[head_l] * kLog2e;
-    const float M = fmaxf(m_ref, sink2);
-    float f, lse2;
-    if (M == -INFINITY) {
-      f = 0.0f;
-      lse2 = -INFINITY;
-    } else {
-      const float em = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - M);
-      const float den = l_tot * em + exp2f(sink2 - M);
-      f = den > 0.0f ? em / den : 0.0f;
-      lse2 = M + log2f(den);
-    }
-    if (a.lse && part == 0 && g == 0) a.lse[static_cast<size_t>(qi) * kAH + head_l] = lse2 * kLn2;
-    float fh[4];
+  attn_finish<Sh::kPart>(a, o, m_ref, l_run, qi, split, hg, part);
+}
+
+// ------------------------------------------------------------------------------------
+// Dense bf16 rows (HCA: the window, then every visible entry; each a contiguous 1 KiB
+// row), 64 heads per workgroup.  The 8 waves form two sets of 4, one wave of each set
+// per SIMD; wave w owns head group w % 4 over all 512 channels (its Q part 64 VGPRs, its
+// O 128), so S^T needs no exchange between waves.  Set s takes the split's chunks of
+// parity s, and every chunk passes two half-phases: S^T + online softmax (32 MFMAs, P
+// kept in registers), then O += P . V (64 MFMAs, P as bf16 hi + lo).  The sets run one
+// half-phase apart, so at every barrier one wave of a SIMD starts the S^T of a chunk while
+// the other starts the P . V of the previous one: the matrix unit stays fed while the
+// other wave reads LDS or exponentiates.  Rows go straight from HBM into a 4-slot LDS
+// ring (global_load_lds_dwordx4: one row per wave instruction, no staging registers),
+// two chunks ahead; one barrier per half-phase.  At the end set 1 hands its (m, l, O) to
+// set 0 through the ring and set 0 writes the result as attn_bf16 does.
+// [HCA-CSA] "HCA：重压缩 + 全量" (dense attention over all compressed entries with the
+// window and the sink); the softmax is the one of the kernel above.
+// ------------------------------------------------------------------------------------
+constexpr int kDnSlots = 4;
+constexpr int kDnWaves = 8;
+constexpr int kDnRowsPerWave = kRows / kDnWaves;
+
+// One 1 KiB row from global memory (row, wave-uniform) into LDS at dst (wave-uniform):
+// lane l moves bytes voff = 16 * l .. +15.  Written as an instruction of its own so that
+// the compiler, which cannot see that it writes LDS, does not wait for it before every
+// LDS read: the code waits for these loads itself (dn_wait_vmcnt, then a barrier) before
+// a slot is read, and the ring never reads a slot a load in flight writes.  It has no
+// result register; M0 (the LDS address) is an input, set at least one wait state ahead.
+__device__ __forceinline__ void dn_dma_row(const void* row, uint8_t* dst, int voff) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(row), "{m0}"(lds)
+               : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void dn_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+__global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kDnSlots * kChunkBytes];
+  int qi, split;
+  if (!attn_unit(a.nq, a.nsplit, qi, split)) return;
+  const int b = qi / a.S, s = qi % a.S;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int set = wave >> 2, hg = wave & 3;
+  const int l = static_cast<int>(lane_id());
+  const int g = l >> 4;
+
+  int w_lo, n_swa;
+  window_rows(s, a.S, a.Ls, a.W, last_position(a.q_pos, b, a.S), w_lo, n_swa);
+  const int n_rem = static_cast<int>(min(static_cast<int64_t>(a.Nc), (a.q_pos[qi] + 1) / a.m));
+  const int n_slots = n_swa + n_rem;
+  const int ch0 = split * a.chunks_per_split;
+  const int n = max(0, min(cdiv(n_slots, kRows), ch0 + a.chunks_per_split) - ch0);   // chunks of the split
+  const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
+  const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
+
+  // Q part of head group hg as the B operand: lane l holds head 16*hg + l%16, channels
+  // 32*ks + 8*g .. +7 (loaded before the first rows, so the first wait covers both)
+  v8s qb[kAC / 32];
+  {
+    const uint16_t* qh = a.q + (static_cast<size_t>(qi) * kAH + kHG * hg + (l & 15)) * kAC;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fh[i] = __shfl(f, 4 * g + i, kWave);
-    uint16_t* ob = a.out + (static_cast<size_t>(qi) * kAH + kHG * hg) * kAC;
-    const int64_t tq = a.rope_d > 0 ? a.q_pos[qi] : 0;
-#pragma unroll
-    for (int t = 0; t < Sh::kPart / 16; ++t) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = o[t][i] * fh[i];
-      // inverse RoPE of the output (the tile's 16 columns: lane pairs hold channel pairs)
-      if (a.rope_d > 0 && Sh::kPart * part + 16 * t + 16 > kAC - a.rope_d) {
-        const int col = col0 + 16 * t;
-        float cs = 1.0f, sn = 0.0f;
-        if (col >= kAC - a.rope_d) rope_cs_sn(col, kAC, a.rope_d, a.rope_r, tq, cs, sn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = rope_back(v[i], pair_lane(v[i]), col, cs, sn);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ob[(4 * g + i) * kAC + col0 + 16 * t] = f32_to_bf16(v[i]);
-    }
-  } else {
-    const size_t pbase = static_cast<size_t>(qi) * a.nsplit + split;
-    if (part == 0 && g == 0) {
-      a.part_ml[(pbase * kAH + head_l) * 2 + 0] = m_ref;
-      a.part_ml[(pbase * kAH + head_l) * 2 + 1] = l_tot;
-    }
-    // the partial in register order: [head group][16-channel tile][lane][4 heads], 16
-    // bytes per lane per store
-    float* po = a.part_o + ((pbase * kNHG + hg) * (kAC / 16) + Sh::kPart / 16 * part) * (kWave * 4) + 4 * l;
-#pragma unroll
-    for (int t = 0; t < Sh::kPart / 16; ++t) *reinterpret_cast<v4f*>(po + t * (kWave * 4)) = o[t];
+    for (int ks = 0; ks < kAC / 32; ++ks) qb[ks] = *reinterpret_cast<const v8s*>(qh + 32 * ks + 8 * g);
   }
+
+  // Chunk c of the split (c >= n: zero rows) into ring slot S = c % kDnSlots: this wave's
+  // kDnRowsPerWave rows, one instruction each; rows past the row set read zero rows.
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    uint8_t* slot = ring + (c % kDnSlots) * kChunkBytes;
+#pragma unroll
+    for (int i = 0; i < kDnRowsPerWave; ++i) {
+      const int r = kDnRowsPerWave * wave + i;
+      const int e = (ch0 + c) * kRows + r;              // slot of the query's row set
+      const bool win = c < n && e < n_swa, ent = c < n && e >= n_swa && e < n_slots;
+      const uint16_t* src = win ? swab + static_cast<size_t>(w_lo + e) * kAC
+                          : ent ? kvb + static_cast<size_t>(e - n_swa) * kAC
+                                : g_zero_rows + static_cast<size_t>(e & (kZeroRows - 1)) * kAC;
+      dn_dma_row(src, slot + r * kRowStride, 16 * l);
+    }
+  };
+
+  v4f o[kAC / 16];
+#pragma unroll
+  for (int t = 0; t < kAC / 16; ++t) o[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;   // per head l%16 (log2 units)
+  float l_run = 0.0f;        // this lane's share of the per-head sum
+  v8s pa, pb;                // P of the chunk between its two half-phases (bf16 hi, lo)
+
+  // S^T of chunk c (32 rows x 16 heads, all channels) and its online softmax; P -> pa, pb.
+  auto step_s = [&](int c) __attribute__((always_inline)) {
+    const uint8_t* buf = ring + (c % kDnSlots) * kChunkBytes;
+    v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < kAC / 32; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const v8s av = *reinterpret_cast<const v8s*>(buf + (16 * rb + (l & 15)) * kRowStride + 64 * ks + 16 * g);
+        st[rb] = mfma_bf16_16x16x32(av, qb[ks], st[rb]);
+      }
+    // fragment reads two steps ahead of their MFMAs (bounds the registers they hold)
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < kAC / 16 - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // slot j <-> chunk row 16*(j/4) + 4*g + j%4; rows past the row set are masked
+    const int e0 = (ch0 + c) * kRows;
+    float sv[8];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 16 * (j >> 2) + 4 * g + (j & 3);
+      sv[j] = c < n && e0 + row < n_slots ? st[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
+      lmax = fmaxf(lmax, sv[j]);
+    }
+    if (__ballot(lmax > m_ref + kLazy)) {
+      float cmax = fmaxf(lmax, wave_xor(lmax, 16));
+      cmax = fmaxf(cmax, wave_xor(cmax, 32));
+      const bool move = cmax > m_ref + kLazy;
+      const float m_new = move ? cmax : m_ref;
+      const float alpha = move ? exp2f(m_ref - m_new) : 1.0f;      // 0 when m_ref = -inf
+      l_run *= alpha;
+      m_ref = m_new;
+      float ah[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ah[i] = __shfl(alpha, 4 * g + i, kWave);
+#pragma unroll
+      for (int t = 0; t < kAC / 16; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[t][i] *= ah[i];
+    }
+    const float m_use = m_ref == -INFINITY ? 0.0f : m_ref;
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+      typedef float v2f __attribute__((ext_vector_type(2)));
+      const v2f p = {__builtin_amdgcn_exp2f(sv[j] - m_use), __builtin_amdgcn_exp2f(sv[j + 1] - m_use)};
+      psum += p[0] + p[1];
+      const v2bf hi = __builtin_convertvector(p, v2bf);
+      const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+      const v2f r = {p[0] - __uint_as_float(hb << 16), p[1] - __uint_as_float(hb & 0xffff0000u)};
+      const uint32_t lb = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, v2bf));
+      pa[j] = static_cast<short>(hb & 0xffffu);
+      pa[j + 1] = static_cast<short>(hb >> 16);
+      pb[j] = static_cast<short>(lb & 0xffffu);
+      pb[j + 1] = static_cast<short>(lb >> 16);
+    }
+    l_run += psum;
+  };
+
+  // O += P . V for chunk c (V rows read transposed from the same LDS rows).
+  auto step_pv = [&](int c) __attribute__((always_inline)) {
+    const uint8_t* vt = ring + (c % kDnSlots) * kChunkBytes + (4 * g + ((l & 15) >> 2)) * kRowStride + 8 * (l & 3);
+#pragma unroll
+    for (int t = 0; t < kAC / 16; ++t) {
+      const v4s v0 = lds_read_tr16(vt + 32 * t);
+      const v4s v1 = lds_read_tr16(vt + 32 * t + 16 * kRowStride);
+      const v8s vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      o[t] = mfma_bf16_16x16x32(pa, vb, o[t]);
+      o[t] = mfma_bf16_16x16x32(pb, vb, o[t]);
+    }
+    // V reads four tiles ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int t = 0; t < kAC / 16 - 4; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+
+  // Half-phase h: set h%2 forms S^T of chunk h, the other set finishes chunk h-1.  Before
+  // it: chunk h has landed (this wave's own rows: at most chunk h+1's still in flight; the
+  // barrier: every wave's), chunk h-2 is no longer read (its slot takes chunk h+2).  Each
+  // wave runs its two half-phase kinds in one straight loop (set 1 starting one half-phase
+  // later); every wave passes the n + 1 barriers and issues the same loads.
+  auto top = [&](int h) __attribute__((always_inline)) {
+    dn_wait_vmcnt<kDnRowsPerWave>();
+    __builtin_amdgcn_s_barrier();
+    issue(h + 2);
+  };
+  issue(0);
+  issue(1);
+  // Q and both chunks complete before the loop (the compiler's own count of the Q loads
+  // would otherwise put a full wait inside it)
+  dn_wait_vmcnt<0>();
+  int h = set;
+  if (set == 1) top(0);
+#pragma unroll 1
+  while (h <= n) {
+    top(h);
+    step_s(h);                                          // all rows masked when h = n
+    if (h == n) break;
+    top(h + 1);
+    step_pv(h);
+    h += 2;
+  }
+
+  // set 1 hands (m, l, O) to set 0 through the ring: [head group][tile][lane][4] + (m, l)
+  dn_wait_vmcnt<0>();
+  __syncthreads();
+  static_assert((kAC / 16 * kWave * 4 + 2 * kWave) * 4 <= kChunkBytes, "a head group's (O, m, l) fits one slot");
+  float* xo = reinterpret_cast<float*>(ring + hg * kChunkBytes);
+  if (set == 1) {
+#pragma unroll
+    for (int t = 0; t < kAC / 16; ++t) *reinterpret_cast<v4f*>(xo + (t * kWave + l) * 4) = o[t];
+    xo[kAC / 16 * kWave * 4 + 2 * l] = m_ref;
+    xo[kAC / 16 * kWave * 4 + 2 * l + 1] = l_run;
+  }
+  __syncthreads();
+  if (set == 1) return;
+  {
+    const float mb = xo[kAC / 16 * kWave * 4 + 2 * l], lb = xo[kAC / 16 * kWave * 4 + 2 * l + 1];
+    const float M = fmaxf(m_ref, mb);
+    const float ea = m_ref == -INFINITY ? 0.0f : exp2f(m_ref - M);
+    const float eb = mb == -INFINITY ? 0.0f : exp2f(mb - M);
+    l_run = l_run * ea + lb * eb;
+    m_ref = M;
+    float ah[4], bh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = __shfl(ea, 4 * g + i, kWave);
+      bh[i] = __shfl(eb, 4 * g + i, kWave);
+    }
+#pragma unroll
+    for (int t = 0; t < kAC / 16; ++t) {
+      const v4f x = *reinterpret_cast<const v4f*>(xo + (t * kWave + l) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[t][i] = o[t][i] * ah[i] + x[i] * bh[i];
+    }
+  }
+  attn_finish<kAC>(a, o, m_ref, l_run, qi, split, hg, 0);
 }
 
 // Combines the split partials of the bf16 kernel (register-order layout) with the sink.
@@ -887,6 +1139,7 @@ __global__ __launch_bounds__(256) void attn_f32(const float* __restrict__ q, con
 // workgroup (every row read serves 64 heads).
 using NarrowShape = AttnShape<4, 8>;
 using WideShape = AttnShape<kWideParts, kWideWaves>;
+static_assert(WideShape::kUnits == 1, "the dense kernel takes the wide shape's splits: one workgroup per (query, split)");
 static bool attn_wide(int nq) { return nq >= kWideMinQueries; }
 
 // Splits of one query's rows over workgroups (bf16 kernel): enough workgroups (units per
@@ -959,8 +1212,15 @@ static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream
   float* wsf = static_cast<float*>(ws);
   a.part_o = wsf;
   a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * kAH * kAC : nullptr;
-  const int rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(src, a, st)
-                               : launch_attn_bf16<4, 8>(src, a, st);
+  int rc = CSA_OK;
+  if (src == kSrcDense && a.kv_fmt == kFmtBf16 && attn_wide(nq)) {
+    // bf16 rows read whole and in order: the two-set dense kernel (same splits, one
+    // workgroup per (query, split))
+    hipLaunchKernelGGL(attn_dense_bf16, dim3(cdiv(nq, 8) * 8 * ns), dim3(kDnWaves * kWave), 0, st, a);
+    CSA_LAUNCH_CHECK();
+  } else {
+    rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(src, a, st) : launch_attn_bf16<4, 8>(src, a, st);
+  }
   if (rc != CSA_OK) return rc;
   if (ns > 1) {
     if (ns <= 4)
