@@ -705,6 +705,9 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs 
 
   // S^T of chunk c (32 rows x 16 heads, all channels) and its online softmax; P -> pa, pb.
   auto step_s = [&](int c) __attribute__((always_inline)) {
+    // the S^T chain and the softmax are the latency-bound half: issued ahead of the other
+    // set's P . V on the same SIMD (which fills the matrix unit's gaps)
+    __builtin_amdgcn_s_setprio(1);
     const uint8_t* buf = ring + (c % kDnSlots) * kChunkBytes;
     v4f st[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -766,25 +769,35 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs 
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // O += P . V for chunk c (V rows read transposed from the same LDS rows).
+  // O += P . V for chunk c (V rows read transposed from the same LDS rows), tiles in pairs:
+  // the P_hi products of both, then their P_lo products, so that no MFMA waits for the
+  // result of the one just before it; V reads run four tiles ahead.
   auto step_pv = [&](int c) __attribute__((always_inline)) {
     const uint8_t* vt = ring + (c % kDnSlots) * kChunkBytes + (4 * g + ((l & 15) >> 2)) * kRowStride + 8 * (l & 3);
 #pragma unroll
-    for (int t = 0; t < kAC / 16; ++t) {
-      const v4s v0 = lds_read_tr16(vt + 32 * t);
-      const v4s v1 = lds_read_tr16(vt + 32 * t + 16 * kRowStride);
-      const v8s vb = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      o[t] = mfma_bf16_16x16x32(pa, vb, o[t]);
-      o[t] = mfma_bf16_16x16x32(pb, vb, o[t]);
+    for (int t = 0; t < kAC / 16; t += 2) {
+      v8s vb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v4s v0 = lds_read_tr16(vt + 32 * (t + j));
+        const v4s v1 = lds_read_tr16(vt + 32 * (t + j) + 16 * kRowStride);
+        vb[j] = v8s{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      }
+      o[t] = mfma_bf16_16x16x32(pa, vb[0], o[t]);
+      o[t + 1] = mfma_bf16_16x16x32(pa, vb[1], o[t + 1]);
+      o[t] = mfma_bf16_16x16x32(pb, vb[0], o[t]);
+      o[t + 1] = mfma_bf16_16x16x32(pb, vb[1], o[t + 1]);
     }
-    // V reads four tiles ahead of their MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int t = 0; t < kAC / 16 - 4; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int k = 0; k < kAC / 16 - 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
