@@ -612,20 +612,22 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Dense bf16 rows (HCA: the window, then every visible entry; each a contiguous 1 KiB
-// row), 64 heads per workgroup.  The 8 waves form two sets of 4, one wave of each set
-// per SIMD; wave w owns head group w % 4 over all 512 channels (its Q part 64 VGPRs, its
-// O 128), so S^T needs no exchange between waves.  Set s takes the split's chunks of
-// parity s, and every chunk passes two half-phases: S^T + online softmax (32 MFMAs, P
-// kept in registers), then O += P . V (64 MFMAs, P as bf16 hi + lo).  The sets run one
-// half-phase apart, so at every barrier one wave of a SIMD starts the S^T of a chunk while
-// the other starts the P . V of the previous one: the matrix unit stays fed while the
-// other wave reads LDS or exponentiates.  Rows go straight from HBM into a 4-slot LDS
-// ring (global_load_lds_dwordx4: one row per wave instruction, no staging registers),
-// two chunks ahead; one barrier per half-phase.  At the end set 1 hands its (m, l, O) to
-// set 0 through the ring and set 0 writes the result as attn_bf16 does.
-// [HCA-CSA] "HCA：重压缩 + 全量" (dense attention over all compressed entries with the
-// window and the sink); the softmax is the one of the kernel above.
+// Two-set bf16 kernel for 64+ queries whose rows are bf16: the window, then every visible
+// entry (HCA, kSrcDense: addresses by arithmetic) or the selected entries (kSrcIdx: a row
+// table built once in LDS); 64 heads per workgroup.  The 8 waves form two sets of 4, one
+// wave of each set per SIMD; wave w owns head group w % 4 over all 512 channels (its Q
+// part 64 VGPRs, its O 128), so S^T needs no exchange between waves.  Set s takes the
+// split's chunks of parity s, and every chunk passes two half-phases: S^T + online
+// softmax (32 MFMAs, P kept in registers), then O += P . V (64 MFMAs, P as bf16 hi + lo).
+// The sets run one half-phase apart, so at every barrier one wave of a SIMD starts the
+// S^T of a chunk while the other starts the P . V of the previous one: the matrix unit
+// stays fed while the other wave reads LDS or exponentiates.  Rows go straight from
+// memory into a 4-slot LDS ring (global_load_lds_dwordx4: one row per wave instruction,
+// no staging registers), two chunks ahead; one barrier per half-phase.  At the end set 1
+// hands its (m, l, O) to set 0 through the ring and set 0 writes the result as attn_bf16
+// does.  [HCA-CSA] "HCA：重压缩 + 全量" (dense attention over all compressed entries with
+// the window and the sink); [KV-COMP] sections 9.5-9.6 (the selected rows); the softmax is
+// the one of the kernel above.
 // ------------------------------------------------------------------------------------
 constexpr int kDnSlots = 4;
 constexpr int kDnWaves = 8;
@@ -636,10 +638,12 @@ constexpr int kDnRowsPerWave = kRows / kDnWaves;
 // the compiler, which cannot see that it writes LDS, does not wait for it before every
 // LDS read: the code waits for these loads itself (dn_wait_vmcnt, then a barrier) before
 // a slot is read, and the ring never reads a slot a load in flight writes.  It has no
-// result register; M0 (the LDS address) is an input, set at least one wait state ahead.
+// result register.  The compiler does not see the load inside, so the asm provides the
+// wait states the load's scalar inputs need: 5 after a VALU instruction wrote the address
+// SGPRs (v_readfirstlane of a table entry), which also covers the 1 after M0 is written.
 __device__ __forceinline__ void dn_dma_row(const void* row, uint8_t* dst, int voff) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(row), "{m0}"(lds)
                : "memory");
@@ -652,8 +656,15 @@ __device__ __forceinline__ void dn_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-__global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs a) {
+template <int kSrc>
+__global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a) {
+  constexpr bool kDense = kSrc == kSrcDense;
+  constexpr bool kCand = kSrc == kSrcCand || kSrc == kSrcCand2;
   __shared__ __attribute__((aligned(16))) uint8_t ring[kDnSlots * kChunkBytes];
+  // selected rows (kSrcIdx): the split's row addresses (low bit: absent, a zero row) and
+  // each chunk's mask of present rows, built once
+  __shared__ uint64_t rowtab[kDense ? 1 : kMaxSplitChunks * kRows];
+  __shared__ uint32_t rowmask[kDense ? 1 : kMaxSplitChunks];
   int qi, split;
   if (!attn_unit(a.nq, a.nsplit, qi, split)) return;
   const int b = qi / a.S, s = qi % a.S;
@@ -664,12 +675,87 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs 
 
   int w_lo, n_swa;
   window_rows(s, a.S, a.Ls, a.W, last_position(a.q_pos, b, a.S), w_lo, n_swa);
-  const int n_rem = static_cast<int>(min(static_cast<int64_t>(a.Nc), (a.q_pos[qi] + 1) / a.m));
+  const int n_rem = kDense ? static_cast<int>(min(static_cast<int64_t>(a.Nc), (a.q_pos[qi] + 1) / a.m)) : a.k;
   const int n_slots = n_swa + n_rem;
   const int ch0 = split * a.chunks_per_split;
   const int n = max(0, min(cdiv(n_slots, kRows), ch0 + a.chunks_per_split) - ch0);   // chunks of the split
   const uint16_t* kvb = a.kv + static_cast<size_t>(b) * a.Nc * kAC;
   const uint16_t* swab = a.swa + static_cast<size_t>(b) * a.Ls * kAC;
+  if constexpr (!kDense) {
+    // Selection from candidates (kSrcCand, kSrcCand2), as attn_bf16 makes it: the query's
+    // n_cand (key, entry) pairs -> the k best in entry order, in the ring (free until the
+    // rows are loaded); the first split of the query also writes them to idx_out.
+    constexpr int kT = kDnWaves * kWave;
+    int32_t* sel = reinterpret_cast<int32_t*>(ring + sizeof(TkShared));
+    if constexpr (kCand) {
+      constexpr int NU = kSrc == kSrcCand2 ? 2 : 1;
+      static_assert(sizeof(TkShared) + 4 * 8 * NU * kT <= kDnSlots * kChunkBytes, "selection fits the ring");
+      TkShared& tsh = *reinterpret_cast<TkShared*>(ring);
+      const uint2* cq = a.cand + static_cast<size_t>(qi) * a.cand_stride;
+      uint32_t key[NU][8], ent[NU][8];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int p0 = 8 * (static_cast<int>(threadIdx.x) + u * kT);
+        if ((a.n_cand & 1) == 0 && p0 + 7 < a.n_cand) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint4 v = reinterpret_cast<const uint4*>(cq + p0)[j];
+            key[u][2 * j] = v.x; ent[u][2 * j] = v.y;
+            key[u][2 * j + 1] = v.z; ent[u][2 * j + 1] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint2 v = p0 + j < a.n_cand ? cq[p0 + j] : make_uint2(0u, 0u);
+            key[u][j] = v.x; ent[u][j] = v.y;
+          }
+        }
+      }
+      uint64_t taken;
+      int obase[NU];
+      const int kk = select_regs<kT, 8, NU>(tsh, key, a.k, taken, obase);
+      int32_t* io = a.idx_out && split == 0 ? a.idx_out + static_cast<size_t>(qi) * a.k : nullptr;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int o = obase[u];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((taken >> (8 * u + j)) & 1ull) {
+            sel[o] = static_cast<int32_t>(ent[u][j]);
+            if (io) io[o] = static_cast<int32_t>(ent[u][j]);
+            ++o;
+          }
+      }
+      for (int p = kk + static_cast<int>(threadIdx.x); p < a.k; p += kT) {
+        sel[p] = -1;
+        if (io) io[p] = -1;
+      }
+      __syncthreads();
+    }
+    // row e of the split: a window row, the selected entry (idx or sel; -1 or out of
+    // range: absent), or past the row set; each wave's ballot covers two chunks' masks
+    const int32_t* idxq = kCand ? sel : a.idx + static_cast<size_t>(qi) * a.k;
+    for (int e0 = 0; e0 < n * kRows; e0 += kT) {
+      const int e = e0 + static_cast<int>(threadIdx.x);
+      const int slot = ch0 * kRows + e;
+      uint64_t p = reinterpret_cast<uint64_t>(g_zero_rows + static_cast<size_t>(e & (kZeroRows - 1)) * kAC) | 1u;
+      if (e < n * kRows) {
+        if (slot < n_swa) {
+          p = reinterpret_cast<uint64_t>(swab + static_cast<size_t>(w_lo + slot) * kAC);
+        } else if (slot < n_slots) {
+          const int j = idxq[slot - n_swa];
+          if (j >= 0 && j < a.Nc) p = reinterpret_cast<uint64_t>(kvb + static_cast<size_t>(j) * kAC);
+        }
+        rowtab[e] = p;
+      }
+      const uint64_t present = __ballot(e < n * kRows && !(p & 1u));
+      if (l == 0 && e < n * kRows) {
+        rowmask[e >> 5] = static_cast<uint32_t>(present);
+        if ((e >> 5) + 1 < n) rowmask[(e >> 5) + 1] = static_cast<uint32_t>(present >> 32);
+      }
+    }
+    __syncthreads();
+  }
 
   // Q part of head group hg as the B operand: lane l holds head 16*hg + l%16, channels
   // 32*ks + 8*g .. +7 (loaded before the first rows, so the first wait covers both)
@@ -688,10 +774,19 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs 
     for (int i = 0; i < kDnRowsPerWave; ++i) {
       const int r = kDnRowsPerWave * wave + i;
       const int e = (ch0 + c) * kRows + r;              // slot of the query's row set
-      const bool win = c < n && e < n_swa, ent = c < n && e >= n_swa && e < n_slots;
-      const uint16_t* src = win ? swab + static_cast<size_t>(w_lo + e) * kAC
-                          : ent ? kvb + static_cast<size_t>(e - n_swa) * kAC
-                                : g_zero_rows + static_cast<size_t>(e & (kZeroRows - 1)) * kAC;
+      const uint16_t* src;
+      if constexpr (kDense) {
+        const bool win = c < n && e < n_swa, ent = c < n && e >= n_swa && e < n_slots;
+        src = win ? swab + static_cast<size_t>(w_lo + e) * kAC
+            : ent ? kvb + static_cast<size_t>(e - n_swa) * kAC
+                  : g_zero_rows + static_cast<size_t>(e & (kZeroRows - 1)) * kAC;
+      } else {
+        const uint64_t v = c < n ? rowtab[c * kRows + r] : reinterpret_cast<uint64_t>(g_zero_rows);
+        // the same entry in every lane: a scalar address
+        const uint64_t p = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+        src = reinterpret_cast<const uint16_t*>(p & ~static_cast<uint64_t>(1));
+      }
       dn_dma_row(src, slot + r * kRowStride, 16 * l);
     }
   };
@@ -727,12 +822,15 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_dense_bf16(AttnArgs 
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // slot j <-> chunk row 16*(j/4) + 4*g + j%4; rows past the row set are masked
     const int e0 = (ch0 + c) * kRows;
+    uint32_t present = 0;
+    if constexpr (!kDense) present = c < n ? rowmask[c] : 0u;
     float sv[8];
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 16 * (j >> 2) + 4 * g + (j & 3);
-      sv[j] = c < n && e0 + row < n_slots ? st[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
+      const bool ok = kDense ? c < n && e0 + row < n_slots : ((present >> row) & 1u) != 0;
+      sv[j] = ok ? st[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
       lmax = fmaxf(lmax, sv[j]);
     }
     if (__ballot(lmax > m_ref + kLazy)) {
@@ -1226,10 +1324,13 @@ static int run_attn_bf16(int src, AttnArgs& a, int max_rows, void* ws, hipStream
   a.part_o = wsf;
   a.part_ml = wsf ? wsf + static_cast<size_t>(nq) * ns * kAH * kAC : nullptr;
   int rc = CSA_OK;
-  if (src == kSrcDense && a.kv_fmt == kFmtBf16 && attn_wide(nq)) {
-    // bf16 rows read whole and in order: the two-set dense kernel (same splits, one
-    // workgroup per (query, split))
-    hipLaunchKernelGGL(attn_dense_bf16, dim3(cdiv(nq, 8) * 8 * ns), dim3(kDnWaves * kWave), 0, st, a);
+  if (a.kv_fmt == kFmtBf16 && attn_wide(nq)) {
+    // bf16 rows, 64+ queries: the two-set kernel (same splits, one workgroup per (query, split))
+    const dim3 grid(cdiv(nq, 8) * 8 * ns), block(kDnWaves * kWave);
+    if (src == kSrcDense) hipLaunchKernelGGL(attn_rows_bf16<kSrcDense>, grid, block, 0, st, a);
+    else if (src == kSrcCand) hipLaunchKernelGGL(attn_rows_bf16<kSrcCand>, grid, block, 0, st, a);
+    else if (src == kSrcCand2) hipLaunchKernelGGL(attn_rows_bf16<kSrcCand2>, grid, block, 0, st, a);
+    else hipLaunchKernelGGL(attn_rows_bf16<kSrcIdx>, grid, block, 0, st, a);
     CSA_LAUNCH_CHECK();
   } else {
     rc = attn_wide(nq) ? launch_attn_bf16<kWideParts, kWideWaves>(src, a, st) : launch_attn_bf16<4, 8>(src, a, st);
