@@ -902,13 +902,13 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
 
   // Half-phase h: set h%2 forms S^T of chunk h, the other set finishes chunk h-1.  Before
   // it: chunk h has landed (this wave's own rows: at most chunk h+1's still in flight; the
-  // barrier: every wave's), chunk h-2 is no longer read (its slot takes chunk h+2).  Each
-  // wave runs its two half-phase kinds in one straight loop (set 1 starting one half-phase
-  // later); every wave passes the n + 1 barriers and issues the same loads.
+  // barrier: every wave's), chunk h-2 is no longer read; after its step each wave issues
+  // its rows of chunk h+2 into that slot (no wave reads it again before the next barrier).
+  // Each wave runs its two half-phase kinds in one straight loop (set 1 starting one
+  // half-phase later); every wave passes the n + 1 barriers and issues the same loads.
   auto top = [&](int h) __attribute__((always_inline)) {
     dn_wait_vmcnt<kDnRowsPerWave>();
     __builtin_amdgcn_s_barrier();
-    issue(h + 2);
   };
   issue(0);
   issue(1);
@@ -916,14 +916,19 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
   // would otherwise put a full wait inside it)
   dn_wait_vmcnt<0>();
   int h = set;
-  if (set == 1) top(0);
+  if (set == 1) {
+    top(0);
+    issue(2);
+  }
 #pragma unroll 1
   while (h <= n) {
     top(h);
     step_s(h);                                          // all rows masked when h = n
+    issue(h + 2);
     if (h == n) break;
     top(h + 1);
     step_pv(h);
+    issue(h + 3);
     h += 2;
   }
 
