@@ -113,7 +113,7 @@ def counter_kernels():
          "candidate pairs, window + selected rows (1 KiB each), q (the split partials it writes are not counted)"),
         ("attn_merge_flash_decode_b32", "attn_merge_tiles<4>", 32 * 8 * 256, ATTN_SOURCES,
          f.B * f.H * f.c * 2, "the bf16 output (the split partials it reads are not counted)"),
-        ("attn_hca_decode_b64", "attn_dense_bf16", None, ATTN_SOURCES, hca_rows,
+        ("attn_hca_decode_b64", "attn_rows_bf16<1>", None, ATTN_SOURCES, hca_rows,
          "window + every visible entry (1 KiB each), q (the split partials it writes are not counted)"),
         ("compress_fused_prefill_chunk8192_main", COMPRESS_MAIN_KERNEL, None, COMPRESS_SOURCES,
          compress_main_bytes(), "hidden rows of the chunk + the 4 before it, w_proj, bias, pooled vectors written"),

@@ -170,7 +170,14 @@ def _fmt_attn_case(lib, fmt, B, S, Nc, k, W, seed, n_valid, dense=False, m=128, 
     torch.cuda.synchronize()
     assert_bf16_output(bf16_f64(host_bits(out)), o_ref, f"attention over packed rows (format {fmt})")
     assert_close(lse.cpu().numpy(), l_ref, TOL_F32, f"lse over packed rows (format {fmt})")
-    assert torch.equal(out, out_b) and torch.equal(lse, lse_b), "packed rows differ from their bf16 decode"
+    if B * S < 64:
+        # the same kernel reads both (packed rows decoded exactly while staged): bit-equal
+        assert torch.equal(out, out_b) and torch.equal(lse, lse_b), "packed rows differ from their bf16 decode"
+    else:
+        # 64+ queries: bf16 rows go to the two-set kernel, packed rows to the staging one
+        # (another summation order); the bf16 decode meets the same bound
+        assert_bf16_output(bf16_f64(host_bits(out_b)), o_ref, "attention over the bf16 decode")
+        assert_close(lse_b.cpu().numpy(), l_ref, TOL_F32, "lse over the bf16 decode")
 
 
 @pytest.mark.parametrize("fmt", [FMT_FP4, FMT_FP8_ROPE])
