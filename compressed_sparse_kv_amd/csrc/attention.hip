@@ -641,12 +641,14 @@ constexpr int kDnRowsPerWave = kRows / kDnWaves;
 // result register.  The compiler does not see the load inside, so the asm provides the
 // wait states the load's scalar inputs need: 5 after a VALU instruction wrote the address
 // SGPRs (v_readfirstlane of a table entry), which also covers the 1 after M0 is written.
+// kStream: the row is read once (nt: streamed past the caches' retention).
+template <bool kStream>
 __device__ __forceinline__ void dn_dma_row(const void* row, uint8_t* dst, int voff) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(row), "{m0}"(lds)
-               : "memory");
+  if constexpr (kStream)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(row), "{m0}"(lds) : "memory");
+  else
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(row), "{m0}"(lds) : "memory");
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -787,7 +789,8 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
                            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
         src = reinterpret_cast<const uint16_t*>(p & ~static_cast<uint64_t>(1));
       }
-      dn_dma_row(src, slot + r * kRowStride, 16 * l);
+      // HCA's rows are read by one workgroup once; selected entries may serve other queries
+      dn_dma_row<kDense>(src, slot + r * kRowStride, 16 * l);
     }
   };
 
