@@ -771,6 +771,7 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
   // Chunk c of the split (c >= n: zero rows) into ring slot S = c % kDnSlots: this wave's
   // kDnRowsPerWave rows, one instruction each; rows past the row set read zero rows.
   auto issue = [&](int c) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
     uint8_t* slot = ring + (c % kDnSlots) * kChunkBytes;
 #pragma unroll
     for (int i = 0; i < kDnRowsPerWave; ++i) {
@@ -825,14 +826,16 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     // slot j <-> chunk row 16*(j/4) + 4*g + j%4; rows past the row set are masked
     const int e0 = (ch0 + c) * kRows;
+    // the chunk's present rows, shifted by this lane's 4g: the remaining bit positions
+    // (16 * (j / 4) + j % 4) are constants (no per-lane masks live through the loop)
     uint32_t present = 0;
-    if constexpr (!kDense) present = c < n ? rowmask[c] : 0u;
+    if constexpr (!kDense) present = (c < n ? rowmask[c] : 0u) >> (4 * g);
     float sv[8];
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int row = 16 * (j >> 2) + 4 * g + (j & 3);
-      const bool ok = kDense ? c < n && e0 + row < n_slots : ((present >> row) & 1u) != 0;
+      const bool ok = kDense ? c < n && e0 + row < n_slots : ((present >> (16 * (j >> 2) + (j & 3))) & 1u) != 0;
       sv[j] = ok ? st[j >> 2][j & 3] * a.scale_log2 : -INFINITY;
       lmax = fmaxf(lmax, sv[j]);
     }
@@ -870,6 +873,9 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
       pb[j + 1] = static_cast<short>(lb >> 16);
     }
     l_run += psum;
+    // P complete here: otherwise its exponentials sink past the row loads and the barrier
+    // into the P . V step, whose V reads then find no registers to run ahead in
+    asm volatile("" : : "v"(pa), "v"(pb));
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -912,11 +918,18 @@ __global__ __launch_bounds__(kDnWaves * kWave, 1) void attn_rows_bf16(AttnArgs a
   auto top = [&](int h) __attribute__((always_inline)) {
     dn_wait_vmcnt<kDnRowsPerWave>();
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);                // each step scheduled on its own
   };
   issue(0);
   issue(1);
   // Q and both chunks complete before the loop (the compiler's own count of the Q loads
-  // would otherwise put a full wait inside it)
+  // would otherwise put a full wait inside it); so are the scalar loads of arguments only
+  // the finish reads (a scalar load in flight, which may return out of order, would make
+  // every LDS wait in the loop a wait for all of them)
+  {
+    const double rope_r = a.rope_r;
+    asm volatile("" : : "s"(rope_r));
+  }
   dn_wait_vmcnt<0>();
   int h = set;
   if (set == 1) {
