@@ -462,6 +462,7 @@ def test_index_topk_fused(lib, B, S, Nc, k, t, with_scores):
     (1, 1, 1500, 2048, 4 * 1500 - 1),      # k above the visible count: -1 padding
     (2, 4, 6000, 512, 4 * 6000 - 1),       # four queries per sequence
     (64, 1, 4096, 512, 4 * 4096 - 1),      # many queries: the 64-head workgroup shape
+    (16, 4, 17000, 1024, 4 * 17000 - 1),   # 64 queries, 5 x 1024 candidates: 16 per thread, 64-head shape
     (1, 1, 8192, 2048, 4 * 8192 - 1),      # the largest selection: 2 x 2048 candidates, k = 2048
     (2, 1, 65536, 512, 4 * 65536 - 1),     # 16 segments: 8192 candidates, 16 per thread, one level
     (1, 1, 36000, 901, 4 * 36000 - 1),     # 9 segments x 901: an odd count of 16-per-thread candidates
