@@ -109,7 +109,7 @@ def counter_kernels():
         ("index_score_segments_flash_decode_b32", ROOFLINE_KERNEL, None, INDEXER_SOURCES,
          index_segments_bytes(f.B, 1, f.n_c, f.H_I, f.d_I, f.k),
          "keys + scales (132 B per entry), q codes + scales + w, positions, 8 x 512 candidate pairs per query"),
-        ("attn_select_flash_decode_b32", "attn_bf16<2, 4, 8, 0>", None, ATTN_SOURCES, fl_rows,
+        ("attn_select_flash_decode_b32", "attn_bf16<2, 4, 8, 0, false>", None, ATTN_SOURCES, fl_rows,
          "candidate pairs, window + selected rows (1 KiB each), q (the split partials it writes are not counted)"),
         ("attn_merge_flash_decode_b32", "attn_merge_tiles<4>", 32 * 8 * 256, ATTN_SOURCES,
          f.B * f.H * f.c * 2, "the bf16 output (the split partials it reads are not counted)"),

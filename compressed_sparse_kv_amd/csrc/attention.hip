@@ -68,6 +68,9 @@ struct AttnShape {
   // chunks of row loads in flight (register sets of kRowsPerWave rows).  (4 measured
   // slower for decode splits of 5 chunks: the loads past a split's end double.)
   static constexpr int kDepth = 2;
+  // splits of at most this many chunks may load all of them at once (the quarter-channel
+  // shape, whose registers have room for them)
+  static constexpr int kAllChunks = kParts == 4 ? 4 : 0;
   static constexpr int kPart = kAC / kParts;            // channels per wave
   static constexpr int kWGHG = kWaves / kParts;         // head groups per workgroup
   static constexpr int kUnits = kNHG / kWGHG;           // workgroups per (query, split)
@@ -256,7 +259,7 @@ __device__ __forceinline__ void attn_finish(const AttnArgs& a, const v4f (&o)[kP
   }
 }
 
-template <int kSrc, int kParts, int kWaves, int kFmt = kFmtBf16>
+template <int kSrc, int kParts, int kWaves, int kFmt = kFmtBf16, bool kShort = false>
 __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   constexpr bool kDense = kSrc == kSrcDense;
   constexpr bool kCand = kSrc == kSrcCand || kSrc == kSrcCand2;
@@ -557,50 +560,84 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   // past the split's end (zero rows), so the count of loads in flight is the same on every
   // path and the compiler's waits before a store only cover the set being stored; stores
   // past the end go to a slot no later step reads for a result.
-  constexpr int kDepth = Sh::kDepth;
-  v4u st[kDepth][4];
-  uint32_t vm[kDepth];
+  // kShort (splits of at most kAllChunks chunks, e.g. long-context decode) loads every
+  // chunk at once, so the split waits for one memory latency instead of one per kDepth
+  // chunks; chunks past the split's end are zero rows, loaded but neither stored nor
+  // computed.  All loads are issued before the first store, so the compiler's count of
+  // loads in flight is exact on every path.  (A separate instantiation: compiled into the
+  // pipelined kernel, this path's registers slowed that kernel down.)
+  const int n_loc = ch1 - ch0;
+  if constexpr (kShort) {
+    static_assert(Sh::kAllChunks > 0, "short splits need the quarter-channel shape");
+    constexpr int kA = Sh::kAllChunks;
+    v4u sa[kA][4];
+    uint32_t va[kA];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i) CSA_ATT_LOAD(ch0 + i, st[i], vm[i]);
-  int sl = ch0 % kRing;                               // slot of chunk ch
-  const int sl1 = sl == kRing - 1 ? 0 : sl + 1;
-  CSA_ATT_STORE(sl, st[0], vm[0]);
-  CSA_ATT_LOAD(ch0 + kDepth, st[0], vm[0]);
-  barrier_lds();
-  s_part(sl, ch0 & 1);
-  CSA_ATT_STORE(sl1, st[1], vm[1]);
-  CSA_ATT_LOAD(ch0 + kDepth + 1, st[1], vm[1]);
-  barrier_lds();
-  int ch = ch0;
-#pragma unroll 1
-  for (; ch + kDepth - 1 < ch1; ch += kDepth) {
+    for (int i = 0; i < kA; ++i) CSA_ATT_LOAD(ch0 + i, sa[i], va[i]);
+    CSA_ATT_STORE(0, sa[0], va[0]);
+    barrier_lds();
+    s_part(0, 0);
+    if (n_loc > 1) CSA_ATT_STORE(1, sa[1], va[1]);
+    barrier_lds();
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) {
-      const int c = ch + i;
-      const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of c + 1
-      const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of c + 2
-      softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});   // past the split's end: S^T unused
-      CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
-      CSA_ATT_LOAD(c + 2 + kDepth, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
-      barrier_lds();
-      sl = sn;
-    }
-  }
-  // the last chunks: ch and ch + 1 are in their slots, the later ones in their sets
-#pragma unroll
-  for (int i = 0; i < kDepth - 1; ++i) {
-    const int c = ch + i;
-    if (c < ch1) {
-      const int sn = sl == kRing - 1 ? 0 : sl + 1;
-      const int s2 = sn == kRing - 1 ? 0 : sn + 1;
-      if (c + 1 < ch1) {
-        softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});
-        if (c + 2 < ch1) CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
-        barrier_lds();
-      } else {
-        softmax_pv(sl, c & 1, sl, c & 1, std::false_type{});
+    for (int j = 0; j < kA; ++j) {
+      if (j < n_loc) {                                  // uniform over the workgroup
+        const int s0 = j % kRing, s1 = (j + 1) % kRing, s2 = (j + 2) % kRing;
+        if (j + 1 < n_loc) {
+          softmax_pv(s0, j & 1, s1, (j + 1) & 1, std::true_type{});
+          if (j + 2 < kA && j + 2 < n_loc) CSA_ATT_STORE(s2, sa[j + 2], va[j + 2]);
+          barrier_lds();
+        } else {
+          softmax_pv(s0, j & 1, s0, j & 1, std::false_type{});
+        }
       }
-      sl = sn;
+    }
+  } else {
+    constexpr int kDepth = Sh::kDepth;
+    v4u st[kDepth][4];
+    uint32_t vm[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) CSA_ATT_LOAD(ch0 + i, st[i], vm[i]);
+    int sl = ch0 % kRing;                               // slot of chunk ch
+    const int sl1 = sl == kRing - 1 ? 0 : sl + 1;
+    CSA_ATT_STORE(sl, st[0], vm[0]);
+    CSA_ATT_LOAD(ch0 + kDepth, st[0], vm[0]);
+    barrier_lds();
+    s_part(sl, ch0 & 1);
+    CSA_ATT_STORE(sl1, st[1], vm[1]);
+    CSA_ATT_LOAD(ch0 + kDepth + 1, st[1], vm[1]);
+    barrier_lds();
+    int ch = ch0;
+#pragma unroll 1
+    for (; ch + kDepth - 1 < ch1; ch += kDepth) {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        const int c = ch + i;
+        const int sn = sl == kRing - 1 ? 0 : sl + 1;     // slot of c + 1
+        const int s2 = sn == kRing - 1 ? 0 : sn + 1;     // slot of c + 2
+        softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});   // past the split's end: S^T unused
+        CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
+        CSA_ATT_LOAD(c + 2 + kDepth, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
+        barrier_lds();
+        sl = sn;
+      }
+    }
+    // the last chunks: ch and ch + 1 are in their slots, the later ones in their sets
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) {
+      const int c = ch + i;
+      if (c < ch1) {
+        const int sn = sl == kRing - 1 ? 0 : sl + 1;
+        const int s2 = sn == kRing - 1 ? 0 : sn + 1;
+        if (c + 1 < ch1) {
+          softmax_pv(sl, c & 1, sn, (c + 1) & 1, std::true_type{});
+          if (c + 2 < ch1) CSA_ATT_STORE(s2, st[(i + 2) % kDepth], vm[(i + 2) % kDepth]);
+          barrier_lds();
+        } else {
+          softmax_pv(sl, c & 1, sl, c & 1, std::false_type{});
+        }
+        sl = sn;
+      }
     }
   }
 #undef CSA_ATT_LOAD1
@@ -1296,7 +1333,7 @@ size_t attn_workspace_bytes(int B, int S, int H, int c, int max_rows, int dtype)
   return nq * ns * H * (static_cast<size_t>(c) + 2) * sizeof(float);
 }
 
-template <int kParts, int kWaves, int kFmt>
+template <int kParts, int kWaves, int kFmt, bool kShort>
 static int launch_attn_bf16_fmt(int src, const AttnArgs& a, hipStream_t st) {
   using Sh = AttnShape<kParts, kWaves>;
   // the dynamic-LDS limit of every source's kernel, raised once per device (any thread may call)
@@ -1305,13 +1342,13 @@ static int launch_attn_bf16_fmt(int src, const AttnArgs& a, hipStream_t st) {
   if (hipGetDevice(&dev) != hipSuccess) return CSA_ERR_HIP;
   const uint64_t bit = uint64_t{1} << (dev & 63);
   if (!(raised.load(std::memory_order_acquire) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcIdx, kParts, kWaves, kFmt>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcIdx, kParts, kWaves, kFmt, kShort>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves, kFmt>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcDense, kParts, kWaves, kFmt, kShort>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves, kFmt>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand, kParts, kWaves, kFmt, kShort>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand2, kParts, kWaves, kFmt>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16<kSrcCand2, kParts, kWaves, kFmt, kShort>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, Sh::kLdsMax) != hipSuccess)
       return CSA_ERR_HIP;
     raised.fetch_or(bit, std::memory_order_release);
@@ -1319,19 +1356,27 @@ static int launch_attn_bf16_fmt(int src, const AttnArgs& a, hipStream_t st) {
   const dim3 grid(cdiv(a.nq, 8) * 8 * Sh::kUnits * a.nsplit);
   const int lds = Sh::kLdsFixed + a.chunks_per_split * kRows * 8;
   const dim3 block(Sh::kThreads);
-  if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves, kFmt>), grid, block, lds, st, a);
-  else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves, kFmt>), grid, block, lds, st, a);
-  else if (src == kSrcCand2) hipLaunchKernelGGL((attn_bf16<kSrcCand2, kParts, kWaves, kFmt>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves, kFmt>), grid, block, lds, st, a);
+  if (src == kSrcDense) hipLaunchKernelGGL((attn_bf16<kSrcDense, kParts, kWaves, kFmt, kShort>), grid, block, lds, st, a);
+  else if (src == kSrcCand) hipLaunchKernelGGL((attn_bf16<kSrcCand, kParts, kWaves, kFmt, kShort>), grid, block, lds, st, a);
+  else if (src == kSrcCand2) hipLaunchKernelGGL((attn_bf16<kSrcCand2, kParts, kWaves, kFmt, kShort>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((attn_bf16<kSrcIdx, kParts, kWaves, kFmt, kShort>), grid, block, lds, st, a);
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }
 
+template <int kParts, int kWaves, bool kShort>
+static int launch_attn_bf16_short(int src, const AttnArgs& a, hipStream_t st) {
+  if (a.kv_fmt == kFmtFp4) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp4, kShort>(src, a, st);
+  if (a.kv_fmt == kFmtFp8Rope) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp8Rope, kShort>(src, a, st);
+  return launch_attn_bf16_fmt<kParts, kWaves, kFmtBf16, kShort>(src, a, st);
+}
+
 template <int kParts, int kWaves>
 static int launch_attn_bf16(int src, const AttnArgs& a, hipStream_t st) {
-  if (a.kv_fmt == kFmtFp4) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp4>(src, a, st);
-  if (a.kv_fmt == kFmtFp8Rope) return launch_attn_bf16_fmt<kParts, kWaves, kFmtFp8Rope>(src, a, st);
-  return launch_attn_bf16_fmt<kParts, kWaves, kFmtBf16>(src, a, st);
+  if constexpr (AttnShape<kParts, kWaves>::kAllChunks > 0)
+    if (a.chunks_per_split <= AttnShape<kParts, kWaves>::kAllChunks)
+      return launch_attn_bf16_short<kParts, kWaves, true>(src, a, st);
+  return launch_attn_bf16_short<kParts, kWaves, false>(src, a, st);
 }
 
 // The bf16 path for row source SRC: splits of the row set, the attention kernel, then the
