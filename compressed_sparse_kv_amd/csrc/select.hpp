@@ -9,11 +9,14 @@
 //   2. histogram over 1024 equal-width bins of [min, max] of the candidate values (bin =
 //      trunc((x-min)*scale), monotone in x because every rounding step is);
 //   3. every wave finds the bin b holding the kk-th element from the padded histogram;
-//      higher bins are taken, bin b goes to an LDS candidate list;
+//      elements of higher bins are taken (a bit per element in registers), bin b goes to
+//      an LDS candidate list;
 //   4. the candidates are ranked in the total order (by readlane within one wave when
-//      there are at most 64), giving the pivot (T, posT), the kk-th element;
-//   5. an element is taken iff it precedes or equals the pivot; an ordered compaction
-//      (per-(chunk, wave) counts, one scan) gives every taken element its output slot.
+//      there are at most 64), giving the pivot (T, posT), the kk-th element; the list's
+//      taken elements are marked in an LDS bitmap over positions;
+//   5. an element is taken iff it precedes or equals the pivot: its bit from step 3 or
+//      the bitmap; an ordered compaction (per-(chunk, wave) counts, one scan) gives every
+//      taken element its output slot.
 // Degenerate value ranges (all equal, infinities, or more than kTkCandCap keys in bin b)
 // take an exact radix select over the three key digits (11, 11, 10 bits) and a tie rank
 // among keys equal to T.
@@ -30,6 +33,7 @@ constexpr int kTkBins = 1024;                  // equal-width bins of the fast p
 constexpr int kTkPB = kTkBins / kWave;
 constexpr int kTkHistWords = 2048 + 4 * 64;    // largest padded histogram (11-bit digit)
 constexpr int kTkCandCap = 1024;
+constexpr int kTkSelWords = kTkMaxChunks * 4096 / 32;   // bitmap of taken list elements
 
 // radix digits, most significant first: bits 31..21, 20..10, 9..0
 __host__ __device__ constexpr inline int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
@@ -38,13 +42,13 @@ __host__ __device__ constexpr inline int digit_bins(int pass) { return pass < 2 
 struct alignas(16) TkShared {
   uint32_t hist[kTkHistWords];
   uint32_t ckey[kTkCandCap];
+  uint32_t selbits[kTkSelWords];             // bit p: list element at position p taken
   int32_t cpos[kTkCandCap];
   int cell_nz[kTkMaxChunks * kTkMaxWaves];   // candidates per wave
   int cell[kTkMaxChunks * kTkMaxWaves];      // taken elements per (chunk, wave) above bin b / > T
   int cell_eq[kTkMaxChunks * kTkMaxWaves];   // exact path: keys equal to T per (chunk, wave)
   uint32_t red_lo[kTkMaxWaves], red_hi[kTkMaxWaves];   // smallest and largest candidate key per wave
-  int ncand, posT;
-  uint32_t T;
+  int ncand;
 };
 
 // Wave64 inclusive prefix sum by DPP: row shifts 1, 2, 4, 8 scan each 16-lane row, then
@@ -152,6 +156,7 @@ __device__ __forceinline__ void cells_before(const int* cells, int w, int (&out)
 template <int NT, int KPT, int NU>
 __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, uint64_t& taken, int (&obase)[NU]) {
   static_assert(NT % kWave == 0 && kWave % (NT / kWave) == 0 && NU * KPT <= 64, "select_regs shape");
+  static_assert(NU * KPT * NT <= 32 * kTkSelWords && 32 % KPT == 0, "taken-element bitmap");
   constexpr int W = NT / kWave;                 // waves
   constexpr int kChunk = KPT * NT;              // positions per chunk
   const int tid = threadIdx.x, w = wave_index();
@@ -170,6 +175,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
       kmin1 = min(kmin1, kv - 1u);
     }
   for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < NU * KPT * NT / 128; i += NT) reinterpret_cast<uint4*>(sh.selbits)[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid == 0) sh.ncand = 0;
   kmax = wave_max_u32(kmax);
   kmin1 = ~wave_max_u32(~kmin1);
@@ -192,8 +198,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
   for (int u = 0; u < NU; ++u) obase[u] = 0;
   if (kk == 0) return 0;
 
-  uint32_t T = 0u;
-  int posT = -1;                 // pivot; (0, -1) takes every candidate
+  uint32_t T = 0u;               // exact path: the kk-th key
   int sel_before[NU];            // taken candidates of bin b before each of this wave's cells
   int eq_before[NU];             // exact path: keys == T before each of this wave's cells
   bool exact = false;
@@ -258,7 +263,9 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
             const int i = KPT * u + s;
             bn = static_cast<int>((pbins[i >> 1] >> (16 * (i & 1))) & 0xffffu) - 1;
           }
-          g += __popcll(__ballot(bn > b));
+          const bool above = bn > b;
+          g += __popcll(__ballot(above));
+          if (above) taken |= 1ull << (KPT * u + s);
           const uint64_t m = __ballot(bn == b);
           if (m != 0) {
             int base = 0;
@@ -276,7 +283,7 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
       }
       __syncthreads();                                                // barrier 3
       cells = sh.cell;
-      // ---- 4. rank the candidates; the remain-th is the pivot
+      // ---- 4. rank the candidates; the first remain of them are taken
       const int nc = __builtin_amdgcn_readfirstlane(sh.ncand);
       if (nc <= kWave) {
         // every wave ranks the list itself: candidate l in lane l, the others by readlane
@@ -289,12 +296,12 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
           r += (kj > ki || (kj == ki && pj < pi)) ? 1 : 0;
         }
         const bool sel = l < nc && r < remain;
-        const int lp = __ffsll(static_cast<long long>(__ballot(l < nc && r == remain - 1))) - 1;
-        T = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), lp));
-        posT = __builtin_amdgcn_readlane(pi, lp);
 #pragma unroll
         for (int u = 0; u < NU; ++u)
           sel_before[u] = __popcll(__ballot(sel && pi < kChunk * u + KPT * kWave * w));
+        // every wave marks the taken list elements among its own positions (the only
+        // bitmap words it reads), so no barrier is needed
+        if (sel && (pi % kChunk) / (KPT * kWave) == w) atomicOr(&sh.selbits[pi >> 5], 1u << (pi & 31));
       } else {
         for (int i = tid; i < nc; i += NT) {
           const uint32_t ki = sh.ckey[i];
@@ -304,12 +311,12 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
             const uint32_t kj = sh.ckey[j];
             r += (kj > ki || (kj == ki && sh.cpos[j] < pi)) ? 1 : 0;
           }
-          if (r < remain) atomicAdd(&sh.cell[cell_of<NT, KPT>(pi)], 1);
-          if (r == remain - 1) { sh.T = ki; sh.posT = pi; }
+          if (r < remain) {
+            atomicAdd(&sh.cell[cell_of<NT, KPT>(pi)], 1);
+            atomicOr(&sh.selbits[pi >> 5], 1u << (pi & 31));
+          }
         }
         __syncthreads();
-        T = sh.T;
-        posT = sh.posT;
       }
     } else {
       // ---- exact radix select over the three key digits
@@ -363,7 +370,10 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
     for (int u = 0; u < NU; ++u) {
       int c = 0;
 #pragma unroll
-      for (int s = 0; s < KPT; ++s) c += __popcll(__ballot(key[u][s] != 0u));
+      for (int s = 0; s < KPT; ++s) {
+        c += __popcll(__ballot(key[u][s] != 0u));
+        if (key[u][s] != 0u) taken |= 1ull << (KPT * u + s);
+      }
       if (l == 0) sh.cell[u * W + w] = c;
     }
     __syncthreads();
@@ -388,13 +398,12 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
       }
       obase[u] = base[u] + sel_before[u] + wave_incl_scan(c) - c;
     } else {
-#pragma unroll
-      for (int s = 0; s < KPT; ++s) {
-        const uint32_t kv = key[u][s];
-        const int pos = kChunk * u + KPT * tid + s;
-        if (kv > T || (kv == T && pos <= posT)) { taken |= 1ull << (KPT * u + s); ++c; }
-      }
-      obase[u] = c;                      // this lane's count for now; prefixes below
+      // taken: the bits of step 3 (higher bins; every candidate when all are taken) and
+      // the list elements marked in the bitmap (KPT consecutive positions in one word)
+      const int p0 = kChunk * u + KPT * tid;
+      const uint32_t lb = (sh.selbits[p0 >> 5] >> (p0 & 31)) & ((1u << KPT) - 1u);
+      taken |= static_cast<uint64_t>(lb) << (KPT * u);
+      obase[u] = __popc(static_cast<uint32_t>(taken >> (KPT * u)) & ((1u << KPT) - 1u));   // this lane's count for now
     }
   }
   if (!exact) {
