@@ -77,6 +77,89 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
+// Long rows (the largest register set), persistent: workgroup g takes rows g, g + G, ...
+// (G = gridDim.x, one workgroup per compute unit).  While it selects over one row, the
+// next row's scores stream into LDS (global_load_lds: one 1 KiB wave instruction per 256
+// scores), so a row's memory time hides under the previous row's selection instead of
+// adding to it.  The first kTkPfFloats scores of a row (whole 1 KiB pieces) take this
+// path; the rest (rows longer than the buffer) are read directly.  Needs rows of a
+// multiple of 4 scores at a 16-byte aligned base.
+// ---------------------------------------------------------------------------------------
+constexpr int kTkPfFloats = 34816;               // 139264 B: what LDS holds next to TkShared
+
+// One 1 KiB piece from global memory (src, wave-uniform) into LDS at dst (wave-uniform):
+// lane l moves bytes 16 l .. 16 l + 15.  Written as an instruction of its own so that the
+// compiler, which cannot see that it writes LDS, does not wait for it at every LDS access
+// or barrier of the selection: the kernel waits for these loads itself (vmcnt(0) and a
+// barrier) before the buffer is read, and issues the next ones only after every wave has
+// read it.  The asm provides the 5 wait states between a VALU write of the address SGPRs
+// and the load (and the 1 after M0 is written).  nt: each score is read once.
+__device__ __forceinline__ void tk_dma_piece(const void* src, void* dst, int voff) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(src), "{m0}"(lds) : "memory");
+}
+
+template <int NU>
+__global__ __launch_bounds__(kTkThreads) void topk_rows_pf(const float* __restrict__ scores, int rows, int Nc, int k,
+                                                           int32_t* __restrict__ idx) {
+  static_assert(NU * kTkChunk >= kTkPfFloats, "the staged prefix lies inside the register set");
+  __shared__ TkShared sh;
+  __shared__ __attribute__((aligned(16))) float buf[kTkPfFloats];
+  const int tid = static_cast<int>(threadIdx.x);
+  const int w = wave_index();
+  const int n_pc = min(Nc, kTkPfFloats) / 256;       // whole pieces staged through LDS
+  const int p_lds = 256 * n_pc;                       // positions [0, p_lds) come from LDS
+  auto issue = [&](int r) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(scores + static_cast<size_t>(r) * Nc);
+    for (int j = w; j < n_pc; j += kTkThreads / kWave) tk_dma_piece(src + 1024 * j, buf + 256 * j, 16 * static_cast<int>(lane_id()));
+  };
+  int row = blockIdx.x;
+  if (row < rows) issue(row);
+  for (; row < rows; row += gridDim.x) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0): this wave's pieces landed
+    __syncthreads();                                  // and every other wave's
+    const float* sr = scores + static_cast<size_t>(row) * Nc;
+    uint32_t key[NU][4];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int p = kTkChunk * u + 4 * tid;           // 4 scores, all below p_lds or none
+      float4 v;
+      if (p < p_lds) {
+        v = *reinterpret_cast<const float4*>(buf + p);
+      } else if (p + 3 < Nc) {
+        v = *reinterpret_cast<const float4*>(sr + p);
+      } else {
+        v.x = p < Nc ? sr[p] : -INFINITY;
+        v.y = p + 1 < Nc ? sr[p + 1] : -INFINITY;
+        v.z = p + 2 < Nc ? sr[p + 2] : -INFINITY;
+        v.w = p + 3 < Nc ? sr[p + 3] : -INFINITY;
+      }
+      key[u][0] = score_key(v.x);
+      key[u][1] = score_key(v.y);
+      key[u][2] = score_key(v.z);
+      key[u][3] = score_key(v.w);
+    }
+    // direct reads complete before the next pieces are issued (the compiler does not count
+    // the pieces, so a later wait of its own for these reads would cover them too)
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();                                  // every wave has read the buffer
+    if (row + static_cast<int>(gridDim.x) < rows) issue(row + gridDim.x);
+    uint64_t taken;
+    int obase[NU];
+    const int kk = select_regs<kTkThreads, 4, NU>(sh, key, k, taken, obase);
+    int32_t* out = idx + static_cast<size_t>(row) * k;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      int o = obase[u];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if ((taken >> (4 * u + s)) & 1ull) out[o++] = kTkChunk * u + 4 * tid + s;
+    }
+    for (int p = kk + tid; p < k; p += kTkThreads) out[p] = -1;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Segmented schedule.  Workspace cand[rows][G][k] of (key, index) pairs, key 0 = empty,
 // each segment's pairs in ascending index order.  Grid (rows, G).
 // ---------------------------------------------------------------------------------------
@@ -212,6 +295,23 @@ bool topk_supported(int Nc, int k, bool with_ws) {
 
 template <int NU>
 static void launch_rows(const float* scores, int rows, int Nc, int k, int32_t* idx, hipStream_t st) {
+  if constexpr (NU == kTkMaxChunks) {
+    // rows long enough to stage: the persistent kernel, one workgroup per compute unit
+    static int n_cu[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && Nc % 4 == 0 &&
+        (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && rows > 1) {
+      if (n_cu[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu[dev] = v;
+      }
+      if (n_cu[dev] > 0) {
+        hipLaunchKernelGGL(topk_rows_pf<NU>, dim3(std::min(rows, n_cu[dev])), dim3(kTkThreads), 0, st, scores, rows,
+                           Nc, k, idx);
+        return;
+      }
+    }
+  }
   hipLaunchKernelGGL(topk_rows<NU>, dim3(rows), dim3(kTkThreads), 0, st, scores, Nc, k, idx);
 }
 template <int NU>
