@@ -1,8 +1,8 @@
-"""The attention's row loads are written as inline asm (global_load_lds_dwordx4), which
-the compiler's hazard recognizer does not see into.  The hardware needs 5 wait states
+"""The attention's row loads and the long-row top-k's score pieces are written as inline
+asm (global_load_lds_dwordx4), which the compiler's hazard recognizer does not see into.  The hardware needs 5 wait states
 between a VALU write of an SGPR (v_readfirstlane of a row-table entry) and a vector-memory
 instruction that reads it as its address, and 1 between a write of M0 and a load into LDS
-that uses it.  This compiles attention.hip to gfx950 assembly exactly as the build does
+that uses it.  This compiles both sources to gfx950 assembly exactly as the build does
 and checks both distances before every such load (a load issued too early reads a stale
 address word).  CPU only: hipcc cross-compiles."""
 
@@ -16,12 +16,12 @@ import pytest
 from compressed_sparse_kv_amd import build as B
 
 
-def _asm(tmp_path):
+def _asm(tmp_path, name):
     if not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None:
         pytest.skip("hipcc not available")
-    src = os.path.join(B.CSRC, "attention.hip")
-    out = tmp_path / "attention.s"
-    cmd = [B.HIPCC, *B.COMMON, *B.DEVICE_FLAGS, *B.PER_FILE.get("attention.hip", []), "--cuda-device-only", "-S",
+    src = os.path.join(B.CSRC, name)
+    out = tmp_path / name.replace(".hip", ".s")
+    cmd = [B.HIPCC, *B.COMMON, *B.DEVICE_FLAGS, *B.PER_FILE.get(name, []), "--cuda-device-only", "-S",
            src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
@@ -47,8 +47,9 @@ def _wait_states_before(lines, k, writes):
     return ws
 
 
-def test_row_loads_have_their_wait_states(tmp_path):
-    text = _asm(tmp_path)
+@pytest.mark.parametrize("name", ["attention.hip", "topk.hip"])
+def test_row_loads_have_their_wait_states(tmp_path, name):
+    text = _asm(tmp_path, name)
     lines = [ln.strip() for ln in text.splitlines()]
     lines = [ln for ln in lines if ln and not ln.startswith(";") and not ln.startswith(".")
              or re.match(r"^\.LBB\S+:$", ln or "")]
@@ -69,4 +70,4 @@ def test_row_loads_have_their_wait_states(tmp_path):
         assert ws is None or ws >= 5, f"row load {n_loads}: {ws} wait states after a VALU write of its address"
         ws_m0 = _wait_states_before(lines, k, lambda x: re.match(r"s_\w+ m0,", x) is not None)
         assert ws_m0 is None or ws_m0 >= 1, f"row load {n_loads}: M0 written right before it"
-    assert n_loads > 0, "no row loads found in the attention kernels"
+    assert n_loads > 0, f"no global_load_lds_dwordx4 found in {name}"
