@@ -381,7 +381,9 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
   }
 
   // The wave's 4 (or 2) rows of chunk CH (zero rows for chunks past the split): addresses
-  // from the table with 16-byte LDS reads, then one 16-byte load per lane per row.
+  // from the table with 16-byte LDS reads, then one 16-byte load per lane per row,
+  // non-temporal, so that the rows streaming through L2 evict less of the split partials
+  // the merge reads back (Flash decode call 25.1 -> 24.1 us).
 #define CSA_ATT_LOAD1(ST, VM, R, PTR)                                                   \
   do {                                                                                 \
     const uint64_t p_ = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>((PTR) >> 32))) << 32) | \
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(kWaves * kWave, 1) void attn_bf16(AttnArgs a) {
       (VM) |= 1u << (8 + (R));                                                         \
       (ST)[R] = load_row8<kFmt>(p_ & ~static_cast<uint64_t>(3), l);                   \
     } else                                                                             \
-      (ST)[R] = reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1))[l];  \
+      (ST)[R] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) v4u*>(p_ & ~static_cast<uint64_t>(1)) + l);  \
   } while (0)
 #define CSA_ATT_LOAD(CH, ST, VM)                                                        \
   do {                                                                                 \
