@@ -16,6 +16,7 @@
 //     among the G*k pairs.  The union of the local top-k sets holds the global top-k
 //     (same total order), so the result is identical.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "common.hpp"
@@ -297,17 +298,17 @@ template <int NU>
 static void launch_rows(const float* scores, int rows, int Nc, int k, int32_t* idx, hipStream_t st) {
   if constexpr (NU == kTkMaxChunks) {
     // rows long enough to stage: the persistent kernel, one workgroup per compute unit
-    static int n_cu[64] = {};
+    // (the count is cached per device; any host thread may call)
+    static std::atomic<int> n_cu[64];
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && Nc % 4 == 0 &&
         (reinterpret_cast<uintptr_t>(scores) & 15u) == 0 && rows > 1) {
-      if (n_cu[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu[dev] = v;
-      }
-      if (n_cu[dev] > 0) {
-        hipLaunchKernelGGL(topk_rows_pf<NU>, dim3(std::min(rows, n_cu[dev])), dim3(kTkThreads), 0, st, scores, rows,
-                           Nc, k, idx);
+      int cu = n_cu[dev].load(std::memory_order_relaxed);
+      if (cu == 0 && hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+        n_cu[dev].store(cu, std::memory_order_relaxed);
+      if (cu > 0) {
+        hipLaunchKernelGGL(topk_rows_pf<NU>, dim3(std::min(rows, cu)), dim3(kTkThreads), 0, st, scores, rows, Nc, k,
+                           idx);
         return;
       }
     }
