@@ -29,6 +29,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "C
 
 EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "csa_compress",
            "csa_compress_state_size", "csa_compress_decode_workspace_size", "csa_compress_decode",
+           "csa_compress_decode_many_workspace_size", "csa_compress_decode_many",
            "csa2_compress_workspace_size", "csa2_compress",
            "csa_index_score", "csa_index_topk_workspace_size", "csa_index_topk",
            "csa_index_segments_size", "csa_index_score_segments", "csa_topk_merge",
@@ -38,6 +39,15 @@ EXPORTS = ("csa_status_string", "csa_version", "csa_compress_workspace_size", "c
            "csa_topk_workspace_size", "csa_topk", "csa_topk_algo",
            "csa_attn_workspace_size", "csa_sparse_attn", "csa_topk_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_noalloc_max_bytes", "csa_sparse_attn_noalloc")
+
+
+class DecodeCompressor(ctypes.Structure):
+    """csa_decode_compressor: the per-compressor arguments of csa_compress_decode_many."""
+    _fields_ = [("w_proj", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("overlap", ctypes.c_int),
+                ("online", ctypes.c_int), ("m", ctypes.c_int), ("c", ctypes.c_int), ("d_rope", ctypes.c_int),
+                ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("state", ctypes.c_void_p),
+                ("cache", ctypes.c_void_p), ("cache_scale", ctypes.c_void_p), ("out_dtype", ctypes.c_int),
+                ("out_layout", ctypes.c_int), ("Nc_max", ctypes.c_int)]
 
 
 class CSAError(RuntimeError):
@@ -63,6 +73,8 @@ def _load() -> ctypes.CDLL:
         "csa2_compress": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, f, i64, vp, vp, i, vp, vp, i, vp, sz, vp], i),
         "csa_compress_decode_workspace_size": ([i, i, i, i, i], sz),
         "csa_compress_decode": ([vp, i, vp, vp, i, i, i, i, i, i, i, f, f, vp, i, vp, vp, vp, i, i, i, vp, sz, vp], i),
+        "csa_compress_decode_many_workspace_size": ([i, i, i, i, ctypes.POINTER(DecodeCompressor)], sz),
+        "csa_compress_decode_many": ([vp, i, i, i, vp, i, i, ctypes.POINTER(DecodeCompressor), vp, sz, vp], i),
         "csa_index_score": ([vp, vp, vp, vp, vp, i, vp, i, i, i, i, i, i, vp, vp], i),
         "csa_index_topk_workspace_size": ([i, i, i, i], sz),
         "csa_index_topk": ([vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, vp, sz, vp], i),
@@ -222,6 +234,50 @@ def csa_compress_decode(hidden, w_proj, bias, pos, state, cache, *, overlap: boo
         float(rope_theta), float(rms_eps), _p(pos), int(emit), _p(state), _p(cache), _p(cache_scale), out_dt,
         int(layout), int(Nc_max), _p(ws), wsb, _stream(stream)))
     return cache
+
+
+def _decode_comp(B, w_proj, bias, state, cache, *, overlap: bool, m: int, c: int, d_rope: int, rope_theta: float,
+                 rms_eps: float, online: bool = False, cache_scale=None, layout: int = CSA_LAYOUT_ROWS,
+                 Nc_max: int | None = None, out_dtype: int | None = None) -> DecodeCompressor:
+    _dev(w_proj, bias, state, cache, cache_scale)
+    if Nc_max is None:
+        if layout != CSA_LAYOUT_ROWS:
+            raise ValueError("Nc_max is required for the blocked layout")
+        Nc_max = cache.shape[1]
+    if state.numel() * state.element_size() < compress_state_size(B, m, c, overlap, online):
+        raise ValueError("state smaller than compress_state_size")
+    out_dt = CSA_FP8_E4M3 if layout == CSA_LAYOUT_B16 else _dtype(cache) if out_dtype is None else int(out_dtype)
+    return DecodeCompressor(_p(w_proj), _p(bias), int(overlap), int(online), m, c, d_rope, float(rope_theta),
+                            float(rms_eps), _p(state), _p(cache), _p(cache_scale), out_dt, int(layout), int(Nc_max))
+
+
+def decode_compressors(B, comps):
+    """The csa_decode_compressor array for comps (dicts of csa_compress_decode's
+    per-compressor keywords), to build once and pass to csa_compress_decode_many on every
+    step; the caller keeps the tensors it points to alive."""
+    if isinstance(comps, ctypes.Array):
+        return comps
+    structs = [_decode_comp(B, **k) for k in comps]
+    return (DecodeCompressor * len(structs))(*structs)
+
+
+def compress_decode_many_workspace_size(B, d, in_dtype, comps) -> int:
+    arr = decode_compressors(B, comps)
+    return int(_lib.csa_compress_decode_many_workspace_size(B, d, int(in_dtype), len(arr), arr))
+
+
+def csa_compress_decode_many(hidden, pos, comps, *, emit: bool = True, ws=None, stream=None):
+    """The decode step of 1 or 2 compressors over the same new tokens (hidden [B,d], pos [B]
+    int64): comps are dicts of csa_compress_decode's per-compressor keywords (w_proj, bias,
+    state, cache, overlap, m, c, d_rope, rope_theta, rms_eps, and optionally online,
+    cache_scale, layout, Nc_max, out_dtype), or the array decode_compressors made of them.
+    Same results as one csa_compress_decode per compressor, in order."""
+    _dev(hidden, pos)
+    B, d = hidden.shape
+    arr = decode_compressors(B, comps)
+    ws, wsb = _ws(compress_decode_many_workspace_size(B, d, _dtype(hidden), arr), ws, hidden.device)
+    _check("csa_compress_decode_many", _lib.csa_compress_decode_many(
+        _p(hidden), _dtype(hidden), B, d, _p(pos), int(emit), len(arr), arr, _p(ws), wsb, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------------------

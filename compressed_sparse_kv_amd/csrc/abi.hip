@@ -24,8 +24,9 @@ size_t csa2_workspace_bytes(int, int, int, int);
 int launch_csa2_compress(const void*, int, const void*, const void*, int, int, int, int, int, int, int, float, float,
                          float, int64_t, void*, float*, int, void*, float*, int, void*, hipStream_t);
 size_t compress_decode_workspace_bytes(int, int, int, int, int);
-int launch_compress_decode(const void*, int, const void*, const float*, int, int, int, int, int, int, int, float,
-                           float, const int64_t*, int, float*, void*, float*, int, int, int, void*, hipStream_t);
+size_t compress_decode_many_workspace_bytes(int, int, int, int, const csa_decode_compressor*);
+int launch_compress_decode_many(const void*, int, int, int, const int64_t*, int, int, const csa_decode_compressor*,
+                                void*, hipStream_t);
 bool index_topk_fused_ok(int, int, int);
 int index_topk_segments(int);
 int launch_index_topk(const void*, const float*, const float*, const void*, const float*, const int64_t*, int, int,
@@ -163,27 +164,51 @@ size_t csa_compress_decode_workspace_size(int B, int d, int c, int overlap, int 
   return compress_decode_workspace_bytes(B, d, c, overlap, in_dtype);
 }
 
+// The checks of one decode compressor's arguments (every one before anything is enqueued).
+static int check_decode_comp(int in_dtype, int B, int d, const csa_decode_compressor& k) {
+  CSA_REQUIRE(k.w_proj && k.bias && k.state && k.cache);
+  CSA_REQUIRE((k.overlap == 0 || k.overlap == 1) && (k.online == 0 || k.online == 1) && !(k.online && k.overlap));
+  CSA_REQUIRE(B > 0 && d > 0 && k.m > 0 && k.c > 0 && k.Nc_max > 0);
+  CSA_REQUIRE(k.c % 2 == 0 && k.c <= 1024 && k.d_rope >= 0 && k.d_rope <= k.c && k.d_rope % 2 == 0);
+  CSA_REQUIRE(k.rms_eps >= 0.0f && k.rope_theta > 0.0f);
+  CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
+  const int ot = check_entry_dtype(k.out_dtype, k.cache, k.cache_scale, k.c, k.d_rope, true);
+  if (ot != CSA_OK) return ot;
+  CSA_REQUIRE(k.out_layout == CSA_LAYOUT_ROWS || k.out_layout == CSA_LAYOUT_B16);
+  CSA_REQUIRE(static_cast<int64_t>(B) * k.Nc_max * k.c < (int64_t{1} << 40));
+  if (k.out_layout == CSA_LAYOUT_B16 && (k.out_dtype != CSA_FP8_E4M3 || k.c != 128)) return CSA_ERR_UNSUPPORTED;
+  if (in_dtype == CSA_BF16 && d % 128 != 0) return CSA_ERR_UNSUPPORTED;
+  CSA_REQUIRE(aligned16(k.state) && aligned16(k.w_proj));
+  return CSA_OK;
+}
+
 int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias, int overlap,
                         int online, int B, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
                         const int64_t* pos, int emit, float* state, void* cache, float* cache_scale, int out_dtype,
                         int out_layout, int Nc_max, void* ws, size_t ws_bytes, void* stream) {
-  CSA_REQUIRE(hidden && w_proj && bias && pos && state && cache);
-  CSA_REQUIRE((overlap == 0 || overlap == 1) && (online == 0 || online == 1) && !(online && overlap));
-  CSA_REQUIRE(B > 0 && d > 0 && m > 0 && c > 0 && Nc_max > 0);
-  CSA_REQUIRE(c % 2 == 0 && c <= 1024 && d_rope >= 0 && d_rope <= c && d_rope % 2 == 0);
-  CSA_REQUIRE(rms_eps >= 0.0f && rope_theta > 0.0f);
-  CSA_REQUIRE(in_dtype == CSA_F32 || in_dtype == CSA_BF16);
-  const int ot = check_entry_dtype(out_dtype, cache, cache_scale, c, d_rope, true);
-  if (ot != CSA_OK) return ot;
-  CSA_REQUIRE(out_layout == CSA_LAYOUT_ROWS || out_layout == CSA_LAYOUT_B16);
-  CSA_REQUIRE(static_cast<int64_t>(B) * Nc_max * c < (int64_t{1} << 40));
-  if (out_layout == CSA_LAYOUT_B16 && (out_dtype != CSA_FP8_E4M3 || c != 128)) return CSA_ERR_UNSUPPORTED;
-  if (in_dtype == CSA_BF16 && d % 128 != 0) return CSA_ERR_UNSUPPORTED;
-  CSA_REQUIRE(aligned16(ws) && aligned16(state) && aligned16(hidden) && aligned16(w_proj));
-  if (ws == nullptr || ws_bytes < compress_decode_workspace_bytes(B, d, c, overlap, in_dtype)) return CSA_ERR_WORKSPACE;
-  return launch_compress_decode(hidden, in_dtype, w_proj, bias, overlap, online, B, d, m, c, d_rope, rope_theta,
-                                rms_eps, pos, emit, state, cache, cache_scale, out_dtype, out_layout, Nc_max, ws,
-                                as_stream(stream));
+  const csa_decode_compressor k{w_proj, bias, overlap, online, m, c, d_rope, rope_theta, rms_eps, state, cache,
+                                cache_scale, out_dtype, out_layout, Nc_max};
+  return csa_compress_decode_many(hidden, in_dtype, B, d, pos, emit, 1, &k, ws, ws_bytes, stream);
+}
+
+size_t csa_compress_decode_many_workspace_size(int B, int d, int in_dtype, int n, const csa_decode_compressor* comps) {
+  if (B <= 0 || d <= 0 || n < 1 || n > 2 || comps == nullptr) return 0;
+  for (int i = 0; i < n; ++i)
+    if (comps[i].c <= 0) return 0;
+  return compress_decode_many_workspace_bytes(B, d, in_dtype, n, comps);
+}
+
+int csa_compress_decode_many(const void* hidden, int in_dtype, int B, int d, const int64_t* pos, int emit, int n,
+                             const csa_decode_compressor* comps, void* ws, size_t ws_bytes, void* stream) {
+  CSA_REQUIRE(hidden && pos && comps && n >= 1 && n <= 2);
+  for (int i = 0; i < n; ++i) {
+    const int rc = check_decode_comp(in_dtype, B, d, comps[i]);
+    if (rc != CSA_OK) return rc;
+  }
+  CSA_REQUIRE(aligned16(ws) && aligned16(hidden));
+  if (ws == nullptr || ws_bytes < compress_decode_many_workspace_bytes(B, d, in_dtype, n, comps))
+    return CSA_ERR_WORKSPACE;
+  return launch_compress_decode_many(hidden, in_dtype, B, d, pos, emit, n, comps, ws, as_stream(stream));
 }
 
 // ---- stage 2 ------------------------------------------------------------------------

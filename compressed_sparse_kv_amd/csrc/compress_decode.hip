@@ -41,16 +41,14 @@ constexpr int kPjTok = 32;                  // tokens per workgroup (2 MFMA tile
 constexpr int kPjStride = 2 * kPjSlice + 16;   // LDS bytes per token row (8 rows in 8 bank groups)
 
 // Partial projection over K slice blockIdx.y: Pk[slice][b][n] for the up to 32 tokens of
-// blockIdx.z and the 64 columns of blockIdx.x; W [N, d] bf16 ("out x in").  The slice of
-// the tokens' hidden vectors is read once into LDS and shared by the 4 waves; each wave
-// holds its 16 W rows of the slice in registers (A operand: rows = output columns,
+// blockIdx.z and the 64 columns of column block xb; W [N, d] bf16 ("out x in").  The slice
+// of the tokens' hidden vectors is read once into LDS (hs) and shared by the 4 waves; each
+// wave holds its 16 W rows of the slice in registers (A operand: rows = output columns,
 // B operand: the tokens), so a lane ends with 4 consecutive columns of one token.
-__global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t* __restrict__ hidden,
-                                                                 const uint16_t* __restrict__ W, int B, int d, int N,
-                                                                 float* __restrict__ Pk) {
-  __shared__ __attribute__((aligned(16))) uint8_t hs[kPjTok * kPjStride];
+__device__ __forceinline__ void proj_token_body(const uint16_t* __restrict__ hidden, const uint16_t* __restrict__ W,
+                                                int B, int d, int N, float* __restrict__ Pk, int xb, uint8_t* hs) {
   const int tid = threadIdx.x, l = static_cast<int>(lane_id()), wave = tid >> 6, g = l >> 4;
-  const int n0 = blockIdx.x * kPjCols + 16 * wave;
+  const int n0 = xb * kPjCols + 16 * wave;
   const int slice = blockIdx.y, k0 = slice * kPjSlice;
   const int b0 = blockIdx.z * kPjTok;
   const int nblk = min(kPjSlice, d - k0) / kPjK;        // blocks of this slice (d % 128 == 0)
@@ -92,6 +90,25 @@ __global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t*
     const int b = b0 + 16 * tt + (l & 15), n = n0 + 4 * g;
     if (b < B && n < N) *reinterpret_cast<v4f*>(P + static_cast<size_t>(b) * N + n) = acc[tt];
   }
+}
+
+// The projections of up to two compressors that read the same tokens (a CSA layer's main
+// and indexer compressors), in one launch: column blocks [0, xb1) are job 0's, the rest
+// job 1's.
+struct ProjJobs {
+  const uint16_t* W0;
+  const uint16_t* W1;
+  float* P0;
+  float* P1;
+  int N0, N1, xb1;
+};
+
+__global__ __launch_bounds__(kPjWaves * 64) void proj_token_bf16(const uint16_t* __restrict__ hidden, ProjJobs j,
+                                                                 int B, int d) {
+  __shared__ __attribute__((aligned(16))) uint8_t hs[kPjTok * kPjStride];
+  const int xb = static_cast<int>(blockIdx.x);
+  if (xb < j.xb1) proj_token_body(hidden, j.W0, B, d, j.N0, j.P0, xb, hs);
+  else proj_token_body(hidden, j.W1, B, d, j.N1, j.P1, xb - j.xb1, hs);
 }
 
 // fp32 inputs (small shapes): one thread per (token, column).
@@ -240,9 +257,7 @@ __device__ __forceinline__ void pool_csa_ring(const float2 (&ra)[kH][4], const f
   }
 }
 
-__global__ __launch_bounds__(512) void compress_step(StepArgs a) {
-  __shared__ float red[8];
-  const int b = blockIdx.x;
+__device__ __forceinline__ void compress_step_body(const StepArgs& a, int b, float* red) {
   const int c = a.c, m = a.m;
   const int ns = a.overlap ? 4 : 2;
   const int N = ns * c;
@@ -429,6 +444,21 @@ __global__ __launch_bounds__(512) void compress_step(StepArgs a) {
   emit_entry(a, b, t / m, u[0], u[1], live, red);
 }
 
+// One workgroup per (compressor, sequence): workgroups [0, B0) run job 0, the rest job 1
+// (a CSA layer's two compressors in one launch; threads beyond a job's c/2 only join its
+// reductions).
+struct StepJobs {
+  StepArgs a0, a1;
+  int B0;
+};
+
+__global__ __launch_bounds__(512) void compress_step(StepJobs j) {
+  __shared__ float red[8];
+  const int wg = static_cast<int>(blockIdx.x);
+  if (wg < j.B0) compress_step_body(j.a0, wg, red);
+  else compress_step_body(j.a1, wg - j.B0, red);
+}
+
 size_t compress_state_bytes(int B, int m, int c, int overlap, int online) {
   if (online) return static_cast<size_t>(B) * 3 * c * sizeof(float);
   const size_t nslot = overlap ? 2 * static_cast<size_t>(m) : static_cast<size_t>(m);
@@ -442,25 +472,62 @@ size_t compress_decode_workspace_bytes(int B, int d, int c, int overlap, int in_
   return static_cast<size_t>(proj_slices(d, in_dtype)) * B * (overlap ? 4 : 2) * c * sizeof(float);
 }
 
-int launch_compress_decode(const void* hidden, int in_dtype, const void* w_proj, const float* bias, int overlap,
-                           int online, int B, int d, int m, int c, int d_rope, float rope_theta, float rms_eps,
-                           const int64_t* pos, int emit, float* state, void* cache, float* cache_scale,
-                           int out_dtype, int out_layout, int Nc_max, void* ws, hipStream_t st) {
-  const int N = (overlap ? 4 : 2) * c;
-  float* P = static_cast<float*>(ws);
-  const int threads = std::max(kWave, cdiv(c / 2, kWave) * kWave);
-  const int n_slices = proj_slices(d, in_dtype);
-  if (in_dtype == CSA_BF16) {
-    hipLaunchKernelGGL(proj_token_bf16, dim3(cdiv(N, kPjCols), n_slices, cdiv(B, kPjTok)), dim3(kPjWaves * 64), 0, st,
-                       static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_proj), B, d, N, P);
-  } else {
-    hipLaunchKernelGGL(proj_token_f32, dim3(cdiv(N, 256), B), dim3(256), 0, st, static_cast<const float*>(hidden),
-                       static_cast<const float*>(w_proj), B, d, N, P);
+using DecodeComp = csa_decode_compressor;
+
+// One compressor's step arguments.
+static StepArgs step_args(const DecodeComp& k, const float* P, int n_slices, int B, const int64_t* pos, int emit) {
+  return StepArgs{P, n_slices, B, k.bias, pos, k.state, k.overlap, k.online, emit, k.m, k.c, k.d_rope,
+                  rope_ratio(k.rope_theta, k.d_rope), k.rms_eps, k.out_dtype, k.out_layout, k.Nc_max, k.cache,
+                  k.cache_scale};
+}
+
+// Compressor i's partial projections start at the 256-aligned end of those before it; the
+// last one's size is exact (one compressor needs what csa_compress_decode_workspace_size says).
+size_t compress_decode_many_workspace_bytes(int B, int d, int in_dtype, int n, const DecodeComp* comps) {
+  size_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const size_t sz = compress_decode_workspace_bytes(B, d, comps[i].c, comps[i].overlap, in_dtype);
+    total += i + 1 < n ? (sz + 255) / 256 * 256 : sz;
   }
+  return total;
+}
+
+// n = 1 or 2 compressors over the same B tokens: bf16 inputs take one projection launch and
+// one step launch for all of them; fp32 inputs run the compressors one after the other.
+int launch_compress_decode_many(const void* hidden, int in_dtype, int B, int d, const int64_t* pos, int emit, int n,
+                                const DecodeComp* comps, void* ws, hipStream_t st) {
+  const int n_slices = proj_slices(d, in_dtype);
+  float* P[2] = {nullptr, nullptr};
+  int N[2] = {0, 0}, threads = kWave;
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    P[i] = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + off);
+    off += (compress_decode_workspace_bytes(B, d, comps[i].c, comps[i].overlap, in_dtype) + 255) / 256 * 256;
+    N[i] = (comps[i].overlap ? 4 : 2) * comps[i].c;
+    threads = std::max(threads, cdiv(comps[i].c / 2, kWave) * kWave);
+  }
+  if (in_dtype != CSA_BF16) {
+    for (int i = 0; i < n; ++i) {
+      hipLaunchKernelGGL(proj_token_f32, dim3(cdiv(N[i], 256), B), dim3(256), 0, st, static_cast<const float*>(hidden),
+                         static_cast<const float*>(comps[i].w_proj), B, d, N[i], P[i]);
+      CSA_LAUNCH_CHECK();
+      const StepArgs a = step_args(comps[i], P[i], n_slices, B, pos, emit);
+      hipLaunchKernelGGL(compress_step, dim3(B), dim3(std::max(kWave, cdiv(comps[i].c / 2, kWave) * kWave)), 0, st,
+                         StepJobs{a, a, B});
+      CSA_LAUNCH_CHECK();
+    }
+    return CSA_OK;
+  }
+  const int xb0 = cdiv(N[0], kPjCols), xb_all = xb0 + (n > 1 ? cdiv(N[1], kPjCols) : 0);
+  const ProjJobs pj{static_cast<const uint16_t*>(comps[0].w_proj),
+                    static_cast<const uint16_t*>(comps[n > 1 ? 1 : 0].w_proj), P[0], P[n > 1 ? 1 : 0], N[0],
+                    N[n > 1 ? 1 : 0], xb0};
+  hipLaunchKernelGGL(proj_token_bf16, dim3(xb_all, n_slices, cdiv(B, kPjTok)), dim3(kPjWaves * 64), 0, st,
+                     static_cast<const uint16_t*>(hidden), pj, B, d);
   CSA_LAUNCH_CHECK();
-  StepArgs a{P, n_slices, B, bias, pos, state, overlap, online, emit, m, c, d_rope, rope_ratio(rope_theta, d_rope),
-             rms_eps, out_dtype, out_layout, Nc_max, cache, cache_scale};
-  hipLaunchKernelGGL(compress_step, dim3(B), dim3(threads), 0, st, a);
+  const StepArgs a0 = step_args(comps[0], P[0], n_slices, B, pos, emit);
+  const StepArgs a1 = n > 1 ? step_args(comps[1], P[1], n_slices, B, pos, emit) : a0;
+  hipLaunchKernelGGL(compress_step, dim3(n * B), dim3(threads), 0, st, StepJobs{a0, a1, B});
   CSA_LAUNCH_CHECK();
   return CSA_OK;
 }

@@ -223,6 +223,40 @@ int csa_compress_decode(const void* hidden, int in_dtype, const void* w_proj, co
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * The decode step of several compressors that read the same new tokens: a CSA layer's
+ * main KV compressor and its indexer-key compressor, which both compress the layer's
+ * hidden states ([HCA-CSA] "CSA：轻压缩 + 稀疏选择"; [KV-COMP] section 9.3).  The result
+ * is exactly that of csa_compress_decode called once per compressor, in order, with the
+ * same hidden, in_dtype, B, d, pos and emit; with bf16 inputs the compressors share one
+ * projection launch and one step launch.
+ *
+ *   comps   n (1 or 2) compressors in host memory, read during the call.  Each holds the
+ *           per-compressor arguments of csa_compress_decode, with the same meaning, layout
+ *           and constraints.  The compressors' state, cache and cache_scale buffers must
+ *           not overlap one another.
+ *   ws      >= csa_compress_decode_many_workspace_size(B, d, in_dtype, n, comps) bytes,
+ *           16-byte aligned (the projections of the B tokens for every compressor).
+ * The arguments of every compressor are checked before anything is enqueued; the first
+ * error found is returned.
+ * ------------------------------------------------------------------------------ */
+typedef struct csa_decode_compressor {
+  const void* w_proj;
+  const float* bias;
+  int overlap, online, m, c, d_rope;
+  float rope_theta, rms_eps;
+  float* state;
+  void* cache;
+  float* cache_scale;
+  int out_dtype, out_layout, Nc_max;
+} csa_decode_compressor;
+
+size_t csa_compress_decode_many_workspace_size(int B, int d, int in_dtype, int n,
+                                               const csa_decode_compressor* comps);
+int csa_compress_decode_many(const void* hidden, int in_dtype, int B, int d, const int64_t* pos,
+                             int emit, int n, const csa_decode_compressor* comps, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Stage 2: lightning-indexer scores.
  * [HCA-CSA] "CSA：轻压缩 + 稀疏选择" (indexer equations); [KV-COMP] sections 9.4, 9.8.
  *

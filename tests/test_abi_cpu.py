@@ -157,3 +157,36 @@ def test_workspace_queries():
     assert b.topk_workspace_size(32, 32768, 512) > 0
     assert b.attn_workspace_size(32, 1, 64, 512, 640, 1) > 0           # split rows need partials
     assert b.attn_workspace_size(1, 1, 8, 64, 160, 0) == 8 * 66 * 4    # fp32 path: one partial
+
+
+def test_compress_decode_many_checks_and_workspace():
+    """csa_compress_decode_many: arguments of every compressor are checked before anything
+    is enqueued, and its workspace is the single call's for one compressor, the 256-aligned
+    first share plus the second for two."""
+    from compressed_sparse_kv_amd import binding as b
+    lib = b.lib()
+    fake = 0x1000                         # 16-byte aligned, never dereferenced: checks fail first
+    D = b.DecodeCompressor
+    main = D(fake, fake, 1, 0, 4, 512, 64, 1e4, 1e-6, fake, fake, None, b.CSA_BF16, b.CSA_LAYOUT_ROWS, 64)
+    idx = D(fake, fake, 1, 0, 4, 128, 64, 1e4, 1e-6, fake, fake, fake, b.CSA_FP8_E4M3, b.CSA_LAYOUT_B16, 64)
+    two = (D * 2)(main, idx)
+    single_main = lib.csa_compress_decode_workspace_size(32, 5120, 512, 1, b.CSA_BF16)
+    single_idx = lib.csa_compress_decode_workspace_size(32, 5120, 128, 1, b.CSA_BF16)
+    assert lib.csa_compress_decode_many_workspace_size(32, 5120, b.CSA_BF16, 1, two) == single_main
+    assert lib.csa_compress_decode_many_workspace_size(32, 5120, b.CSA_BF16, 2, two) == \
+        (single_main + 255) // 256 * 256 + single_idx
+    assert lib.csa_compress_decode_many_workspace_size(32, 5120, b.CSA_BF16, 3, two) == 0
+    ws_ok = (single_main + 255) // 256 * 256 + single_idx
+    # n out of range, no compressors
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 0, two, fake, ws_ok, None) == 1
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 3, two, fake, ws_ok, None) == 1
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 2, None, fake, ws_ok, None) == 1
+    # the second compressor's blocked layout needs FP8 codes of c = 128
+    bad = (D * 2)(main, D(fake, fake, 1, 0, 4, 256, 64, 1e4, 1e-6, fake, fake, fake, b.CSA_FP8_E4M3,
+                          b.CSA_LAYOUT_B16, 64))
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 2, bad, fake, ws_ok, None) == 2
+    # odd c in the second compressor; workspace one byte short
+    bad2 = (D * 2)(main, D(fake, fake, 1, 0, 4, 127, 64, 1e4, 1e-6, fake, fake, fake, b.CSA_FP8_E4M3,
+                           b.CSA_LAYOUT_ROWS, 64))
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 2, bad2, fake, ws_ok, None) == 1
+    assert lib.csa_compress_decode_many(fake, b.CSA_BF16, 32, 5120, fake, 1, 2, two, fake, ws_ok - 1, None) == 3

@@ -176,3 +176,46 @@ def test_decode_compress_many_sequences_f32(lib):
             assert_close(got[b, i], v, TOL_F32, f"decode entry {i} of sequence {b}")
         untouched = [i for i in range(Nc_max) if i not in ref]
         assert np.all(got[b, untouched] == 0)
+
+
+@pytest.mark.parametrize("B,d", [(33, 5120), (3, 1024)])
+def test_decode_compress_many_equals_single_calls(lib, B, d):
+    """A CSA layer's main (c = 512, bf16 rows) and indexer (c = 128, FP8 in 16-entry blocks)
+    compressors through one csa_compress_decode_many call per token, against one
+    csa_compress_decode per compressor: caches, scales and ring states bit-identical after
+    every token.  Sequences sit at different phases of their blocks (boundary and
+    non-boundary steps in the same call), one is skipped (pos -1), and the ring is primed
+    with emit = 0 first; B = 33 spans two token tiles of the projection."""
+    m, c, dI, Nc = 4, 512, 128, 64
+    a = I.decode_layer_inputs(700 + B, B, d, m, c, dI)
+    Wm, Bm = dev_bf16(a["W_main_t_bf16"]), dev(a["B_main"])
+    Wi, Bi = dev_bf16(a["W_idx_t_bf16"]), dev(a["B_idx"])
+    kw = dict(overlap=True, m=m, d_rope=64, rope_theta=1e4, rms_eps=1e-6)
+
+    def buffers():
+        z = lambda n: torch.zeros(n, dtype=torch.uint8, device="cuda")
+        return {"kv": torch.zeros(B, Nc, c, dtype=torch.bfloat16, device="cuda"),
+                "k16": z(lib.index_keys_b16_size(B, Nc)), "ks": torch.zeros(B, Nc, device="cuda"),
+                "st_m": z(lib.compress_state_size(B, m, c, True)), "st_i": z(lib.compress_state_size(B, m, dI, True))}
+
+    one, many = buffers(), buffers()
+    tokens = [a["prime_bf16"][:, r] for r in range(2 * m - 1)] + [a["hidden_bf16"]] + \
+        [a["prime_bf16"][:, r] for r in range(2 * m - 1)]
+    base = np.int64(4 * 40 - (2 * m - 1))
+    for r, hid in enumerate(tokens):
+        h = dev_bf16(np.ascontiguousarray(hid))
+        pos_h = base + r + (np.arange(B, dtype=np.int64) % 3)
+        pos_h[B // 2] = -1
+        pos = dev(pos_h)
+        emit = r >= 2 * m - 1
+        lib.csa_compress_decode(h, Wm, Bm, pos, one["st_m"], one["kv"], c=c, emit=emit, **kw)
+        lib.csa_compress_decode(h, Wi, Bi, pos, one["st_i"], one["k16"], c=dI, cache_scale=one["ks"],
+                                layout=lib.CSA_LAYOUT_B16, Nc_max=Nc, emit=emit, **kw)
+        lib.csa_compress_decode_many(h, pos, [
+            dict(w_proj=Wm, bias=Bm, state=many["st_m"], cache=many["kv"], c=c, **kw),
+            dict(w_proj=Wi, bias=Bi, state=many["st_i"], cache=many["k16"], c=dI, cache_scale=many["ks"],
+                 layout=lib.CSA_LAYOUT_B16, Nc_max=Nc, **kw)], emit=emit)
+        torch.cuda.synchronize()
+        for name in one:
+            assert torch.equal(one[name], many[name]), f"token {r}: {name} differs between the two paths"
+    assert int((many["ks"] > 0).sum()) > 0, "no entry was emitted"
