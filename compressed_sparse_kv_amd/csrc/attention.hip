@@ -110,7 +110,9 @@ __device__ __attribute__((aligned(1024))) uint16_t g_zero_rows[kZeroRows * kAC];
 // 16-channel tile ct), lane l holds heads 16*hg + 4*(l/16) + i and channel 16*ct + l%16.
 
 // Merges the nsplit partials of one wave's KT tiles with the sink and stores them (every
-// load in flight at once for up to 4 splits, else one split's at a time).
+// load in flight at once for up to 4 splits, or up to kMergeAllSplits with one tile, else
+// one split's at a time).
+constexpr int kMergeAllSplits = 16;
 template <int KT>
 __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                              const float* __restrict__ sink, int nsplit, size_t qi, int hg, int ct0,
@@ -169,6 +171,41 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ part_o, c
       }
     merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
     return;
+  }
+  if constexpr (KT == 1) {
+    if (nsplit <= kMergeAllSplits) {
+      // one tile: every split's loads in flight at once (a loop over the splits would
+      // wait for each one in turn); the same arithmetic in the same split order
+      v4f ma[kMergeAllSplits], mb[kMergeAllSplits], x[kMergeAllSplits];
+#pragma unroll
+      for (int sp = 0; sp < kMergeAllSplits; ++sp)
+        if (sp < nsplit) {
+          ml_of(sp, ma[sp], mb[sp]);
+          x[sp] = po_of(sp, ct0);
+        }
+#pragma unroll
+      for (int sp = 0; sp < kMergeAllSplits; ++sp)
+        if (sp < nsplit) {
+          M[0] = fmaxf(M[0], ma[sp][0]); M[1] = fmaxf(M[1], ma[sp][2]);
+          M[2] = fmaxf(M[2], mb[sp][0]); M[3] = fmaxf(M[3], mb[sp][2]);
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) den[i] = M[i] == -INFINITY ? 0.0f : exp2f(sk[i] * kLog2e - M[i]);
+#pragma unroll
+      for (int sp = 0; sp < kMergeAllSplits; ++sp)
+        if (sp < nsplit) {
+          const float mi[4] = {ma[sp][0], ma[sp][2], mb[sp][0], mb[sp][2]};
+          const float li[4] = {ma[sp][1], ma[sp][3], mb[sp][1], mb[sp][3]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float wgt = mi[i] == -INFINITY ? 0.0f : exp2f(mi[i] - M[i]);
+            den[i] = fmaf(wgt, li[i], den[i]);
+            acc[0][i] = fmaf(wgt, x[sp][i], acc[0][i]);
+          }
+        }
+      merge_store<KT>(acc, den, M, qi, h0, ct0, l, out, lse, q_pos, rope_d, rope_r);
+      return;
+    }
   }
   for (int sp = 0; sp < nsplit; ++sp) {
     v4f a, b;
