@@ -219,3 +219,52 @@ def test_decode_compress_many_equals_single_calls(lib, B, d):
         for name in one:
             assert torch.equal(one[name], many[name]), f"token {r}: {name} differs between the two paths"
     assert int((many["ks"] > 0).sum()) > 0, "no entry was emitted"
+
+
+@pytest.mark.parametrize("bf16_in", [True, False])
+def test_decode_compress_many_mixed_compressors(lib, bf16_in):
+    """Two unlike compressors in one csa_compress_decode_many call: a CSA ring (overlap,
+    m = 4, c = 64, bf16 rows) and an HCA online state (m = 8, c = 32, fp32 rows, no RoPE
+    part), over bf16 inputs (one projection launch) or fp32 inputs (one compressor after
+    the other): bit-identical to one csa_compress_decode per compressor after every token,
+    over 20 tokens (boundaries of both block sizes)."""
+    rng = np.random.default_rng(4242 + int(bf16_in))
+    B, d, Nc = 5, 256, 8
+    specs = [dict(overlap=True, online=False, m=4, c=64, d_rope=16, out=torch.bfloat16),
+             dict(overlap=False, online=True, m=8, c=32, d_rope=0, out=torch.float32)]
+
+    def to_dev(x):
+        if bf16_in:
+            return dev_bf16(I.to_bf16_bits(x))
+        return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+
+    weights = []
+    for sp in specs:
+        ns = 4 if sp["overlap"] else 2
+        W = to_dev(rng.normal(0.0, 0.05, (ns * sp["c"], d)))
+        bias = dev(rng.normal(0.0, 0.05, (ns // 2, sp["m"], sp["c"])).astype(np.float32))
+        weights.append((W, bias))
+
+    def buffers():
+        out = []
+        for sp in specs:
+            st = torch.zeros(lib.compress_state_size(B, sp["m"], sp["c"], sp["overlap"], sp["online"]),
+                             dtype=torch.uint8, device="cuda")
+            out.append((st, torch.zeros(B, Nc, sp["c"], dtype=sp["out"], device="cuda")))
+        return out
+
+    one, many = buffers(), buffers()
+    kw = lambda sp: dict(overlap=sp["overlap"], online=sp["online"], m=sp["m"], c=sp["c"], d_rope=sp["d_rope"],
+                         rope_theta=1e4, rms_eps=1e-6)
+    for r in range(20):
+        h = to_dev(rng.normal(0.0, 1.0, (B, d)))
+        pos = dev((8 + r + np.arange(B) % 3).astype(np.int64))
+        for i, sp in enumerate(specs):
+            lib.csa_compress_decode(h, weights[i][0], weights[i][1], pos, one[i][0], one[i][1], **kw(sp))
+        lib.csa_compress_decode_many(h, pos, [dict(w_proj=weights[i][0], bias=weights[i][1], state=many[i][0],
+                                                   cache=many[i][1], **kw(sp)) for i, sp in enumerate(specs)])
+        torch.cuda.synchronize()
+        for i in range(len(specs)):
+            assert torch.equal(one[i][0], many[i][0]), f"token {r}: state of compressor {i} differs"
+            assert torch.equal(one[i][1], many[i][1]), f"token {r}: cache of compressor {i} differs"
+    assert bool((many[0][1] != 0).any()) and bool((many[1][1] != 0).any()), "no entries emitted"
