@@ -633,3 +633,25 @@ def test_index_segments_b16(lib, B, S, Nc, k, t):
     assert seg == c0.numel()
     assert torch.equal(c0, c1), "blocked keys: segment candidates differ"
     assert torch.equal(sc, sc16), "blocked keys: scores differ"
+
+
+def test_topk_long_rows_unaligned_base(lib):
+    """Scores whose base is 4- but not 16-byte aligned take the one-workgroup-per-row kernel
+    (the persistent long-row kernel streams 16-byte pieces): the same selection as from an
+    aligned copy, and the oracle's on sampled rows."""
+    rows, Nc, k = 300, 20000, 256
+    rng = np.random.default_rng(77)
+    s = I.score_rows(rows + Nc + k, rows, Nc, "ties", rng.integers(Nc // 2, Nc + 1, rows))
+    flat = torch.empty(rows * Nc + 4, device="cuda")
+    flat[1:1 + rows * Nc] = torch.from_numpy(s.reshape(-1)).cuda()
+    view = flat[1:1 + rows * Nc].view(1, rows, Nc)
+    assert view.data_ptr() % 16 == 4
+    idx_u = torch.empty(1, rows, k, dtype=torch.int32, device="cuda")
+    idx_a = torch.empty(1, rows, k, dtype=torch.int32, device="cuda")
+    lib.csa_topk(view, k, idx_u, algo=1)
+    lib.csa_topk(dev(s[None]), k, idx_a, algo=1)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_u, idx_a), "unaligned scores select differently"
+    sample = [0, 1, 150, rows - 1]
+    ref = O.topk_indices(s[sample], k)
+    assert_topk_equal(idx_u[0, sample].cpu().numpy(), ref, s[sample], k, "top-k, unaligned base", exact=True)
