@@ -268,3 +268,60 @@ def test_decode_compress_many_mixed_compressors(lib, bf16_in):
             assert torch.equal(one[i][0], many[i][0]), f"token {r}: state of compressor {i} differs"
             assert torch.equal(one[i][1], many[i][1]), f"token {r}: cache of compressor {i} differs"
     assert bool((many[0][1] != 0).any()) and bool((many[1][1] != 0).any()), "no entries emitted"
+
+
+def test_decode_compress_many_graph_replay(lib):
+    """Both compressors' decode step (csa_compress_decode_many, bf16, a block boundary) captured
+    in a HIP graph: from the same primed state, every replay writes the eager call's entries
+    and state, with eager calls between the replays."""
+    B, d, m, c, dI, Nc = 4, 512, 4, 64, 32, 16
+    a = I.decode_layer_inputs(99, B, d, m, c, dI)
+    Wm, Bm = dev_bf16(a["W_main_t_bf16"]), dev(a["B_main"])
+    Wi, Bi = dev_bf16(a["W_idx_t_bf16"]), dev(a["B_idx"])
+    kw = dict(overlap=True, m=m, d_rope=16, rope_theta=1e4, rms_eps=1e-6)
+    st_m = torch.zeros(lib.compress_state_size(B, m, c, True), dtype=torch.uint8, device="cuda")
+    st_i = torch.zeros(lib.compress_state_size(B, m, dI, True), dtype=torch.uint8, device="cuda")
+    kv = torch.zeros(B, Nc, c, dtype=torch.bfloat16, device="cuda")
+    kk = torch.zeros(B, Nc, dI, dtype=torch.uint8, device="cuda")
+    ks = torch.zeros(B, Nc, device="cuda")
+    comps = lib.decode_compressors(B, [dict(w_proj=Wm, bias=Bm, state=st_m, cache=kv, c=c, **kw),
+                                       dict(w_proj=Wi, bias=Bi, state=st_i, cache=kk, c=dI, cache_scale=ks,
+                                            out_dtype=lib.CSA_FP8_E4M3, **kw)])
+    ws = torch.empty(lib.compress_decode_many_workspace_size(B, d, lib.CSA_BF16, comps), dtype=torch.uint8,
+                     device="cuda")
+    t = 4 * 10 + 3                                   # completes block 10
+    for r in range(2 * m - 1):
+        lib.csa_compress_decode_many(dev_bf16(np.ascontiguousarray(a["prime_bf16"][:, r])),
+                                     dev(np.full(B, t - (2 * m - 1) + r, np.int64)), comps, emit=False, ws=ws)
+    torch.cuda.synchronize()
+    primed = (st_m.clone(), st_i.clone())
+    h, pos = dev_bf16(a["hidden_bf16"]), dev(np.full(B, t, np.int64))
+
+    def reset():
+        st_m.copy_(primed[0]); st_i.copy_(primed[1])
+        kv.zero_(); kk.zero_(); ks.zero_()
+
+    def step():
+        lib.csa_compress_decode_many(h, pos, comps, ws=ws)
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (st_m, st_i, kv, kk, ks)]
+    assert bool((ks > 0).any()), "no entry emitted"
+    g = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        reset()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y, name in zip((st_m, st_i, kv, kk, ks), ref, ("main state", "indexer state", "KV entries",
+                                                                  "key codes", "key scales")):
+            assert torch.equal(x, y), f"{name} differ on replay {r}"
+        reset()
+        step()                                       # eager work between the replays
+        torch.cuda.synchronize()
