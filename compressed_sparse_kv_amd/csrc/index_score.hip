@@ -209,6 +209,9 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
   }
 
   __shared__ uint32_t kst[kTopk ? kDecEntWG : 1];       // keys of the workgroup's entries
+  // the selection's step 1 (candidate count, key range), kept per lane during the scoring
+  uint32_t sel_min1 = 0xffffffffu, sel_max = 0u;
+  int sel_cnt = 0;
 #pragma unroll
   for (int gi = 0; gi < kDecGroups; ++gi) {
     const int e0 = group_e0(gi);
@@ -231,7 +234,12 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     }
     if (out && e < n_ent) out[e] = vis ? v : -INFINITY;
     const uint32_t key = vis ? score_key(v) : 0u;
-    if (kTopk) kst[64 * (gi * kDecWaves + wave) + l] = key;
+    if (kTopk) {
+      kst[64 * (gi * kDecWaves + wave) + l] = key;
+      sel_cnt += key != 0u ? 1 : 0;
+      sel_max = max(sel_max, key);
+      sel_min1 = min(sel_min1, key - 1u);
+    }
     if constexpr (kBmax) {
       float bm = vis ? v : -INFINITY;
       bm = fmaxf(bm, __shfl_xor(bm, 1, kWave));
@@ -243,6 +251,8 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
 #undef CSA_DEC_LOAD
   if (kTopk) {
     __shared__ TkShared sh;
+    sel_clear<kDecThreads, kDecEntWG>(sh);
+    sel_wave_range(sh, wave, l, sel_min1, sel_max, sel_cnt);
     __syncthreads();
     uint32_t key[1][8];
 #pragma unroll
@@ -250,7 +260,7 @@ __global__ __launch_bounds__(dec_waves<kTopk>() * 64) void index_score_fp8_decod
     uint64_t taken;
     int obase[1];
     static_assert(kDecThreads * 8 == kDecEntWG, "8 keys per thread");
-    const int kk = select_regs<kDecThreads, 8, 1>(sh, key, ktop, taken, obase);
+    const int kk = select_regs<kDecThreads, 8, 1, true>(sh, key, ktop, taken, obase);
     uint2* dst = cand + row * cand_stride + blockIdx.x * static_cast<size_t>(ktop);
     int o = obase[0];
     // the entries 8*tid .. 8*tid+7 of the segment: one block of 8 (positions from the pool)

@@ -150,10 +150,32 @@ __device__ __forceinline__ void cells_before(const int* cells, int w, int (&out)
 
 // Selection over the keys of one set held in registers by a workgroup of NT threads:
 // key[u][s] is the key of position KPT*NT*u + KPT*threadIdx.x + s (0 = not a candidate).
+// kPre: the caller has done step 1 itself, before a barrier: every wave w wrote its
+// smallest candidate key - 1, largest key and candidate count to sh.red_lo[w],
+// sh.red_hi[w], sh.cell_nz[w] (any partition of the set over the waves), and the
+// histogram, the taken-element bitmap and sh.ncand were cleared (sel_clear).
 // Returns kk = min(k, #candidates); sets bit KPT*u+s of `taken` for the taken elements and
 // obase[u] to the output slot of this thread's first taken element of chunk u (taken
 // elements fill slots 0..kk-1 in position order).
-template <int NT, int KPT, int NU>
+// Step 1's clears: the histogram, the first NPOS bits of the taken-element bitmap, the list.
+template <int NT, int NPOS>
+__device__ __forceinline__ void sel_clear(TkShared& sh) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < NPOS / 128; i += NT) reinterpret_cast<uint4*>(sh.selbits)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) sh.ncand = 0;
+}
+
+// Step 1's per-wave partials (this lane's smallest candidate key - 1, largest key and
+// candidate count, reduced over the wave) into wave w's LDS slots.
+__device__ __forceinline__ void sel_wave_range(TkShared& sh, int w, int l, uint32_t kmin1, uint32_t kmax, int cnt) {
+  kmax = wave_max_u32(kmax);
+  kmin1 = ~wave_max_u32(~kmin1);
+  cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+  if (l == 0) { sh.red_lo[w] = kmin1; sh.red_hi[w] = kmax; sh.cell_nz[w] = cnt; }
+}
+
+template <int NT, int KPT, int NU, bool kPre = false>
 __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, uint64_t& taken, int (&obase)[NU]) {
   static_assert(NT % kWave == 0 && kWave % (NT / kWave) == 0 && NU * KPT <= 64, "select_regs shape");
   static_assert(NU * KPT * NT <= 32 * kTkSelWords && 32 % KPT == 0, "taken-element bitmap");
@@ -164,24 +186,21 @@ __device__ int select_regs(TkShared& sh, const uint32_t (&key)[NU][KPT], int k, 
   // ---- 1. candidate count and key range, per thread and then per wave: no branches
   // (key 0 is the smallest key, and key - 1 wraps it to the largest)
   uint32_t kmin1 = 0xffffffffu, kmax = 0u;      // smallest candidate key - 1, largest key
-  int cnt = 0;
+  if constexpr (!kPre) {
+    int cnt = 0;
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int s = 0; s < KPT; ++s) {
-      const uint32_t kv = key[u][s];
-      cnt += kv != 0u ? 1 : 0;
-      kmax = max(kmax, kv);
-      kmin1 = min(kmin1, kv - 1u);
-    }
-  for (int i = tid; i < kTkHistWords / 4; i += NT) reinterpret_cast<uint4*>(sh.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = tid; i < NU * KPT * NT / 128; i += NT) reinterpret_cast<uint4*>(sh.selbits)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (tid == 0) sh.ncand = 0;
-  kmax = wave_max_u32(kmax);
-  kmin1 = ~wave_max_u32(~kmin1);
-  cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
-  if (l == 0) { sh.red_lo[w] = kmin1; sh.red_hi[w] = kmax; sh.cell_nz[w] = cnt; }
-  __syncthreads();                                                    // barrier 1
+      for (int s = 0; s < KPT; ++s) {
+        const uint32_t kv = key[u][s];
+        cnt += kv != 0u ? 1 : 0;
+        kmax = max(kmax, kv);
+        kmin1 = min(kmin1, kv - 1u);
+      }
+    sel_clear<NT, NU * KPT * NT>(sh);
+    sel_wave_range(sh, w, l, kmin1, kmax, cnt);
+    __syncthreads();                                                  // barrier 1
+  }
   int total = 0;
   kmin1 = 0xffffffffu;
   kmax = 0u;
